@@ -1,0 +1,265 @@
+/*
+ * iqlher.h -- C ABI of the MI355X (gfx950) IQL + HER auxiliary-trainer step.
+ *
+ * One training step of an Implicit Q-Learning value trainer fed by Hindsight
+ * Experience Replay, as described on these pages:
+ *   [P1] "GPU IQL + HER Porting Plan"
+ *   [P2] "DQN Backward-Path NaN Audit -- SP1 Phase A"
+ *   [P3] "Phase 2: Multi-Stream Graph Parallelism"
+ *   [P5] "Gradient Stability -- Proper Multi-Task Gradient Isolation +
+ *        Full Spectral Norm"
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named d_* or documented "device" are HIP device pointers (any
+ *     allocation visible to the current device); "host" pointers are read
+ *     during the call only.  No entry point keeps a caller pointer.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call that takes a stream only enqueues work on it: no host
+ *     synchronisation, no allocation, no memset node -- all of them may be
+ *     captured into a HIP graph and replayed.
+ *   - Return value: IQLH_OK or a negative iqlh_status.  Argument errors are
+ *     detected on the host before any HIP call; iqlh_last_error() then holds a
+ *     message (thread-local).  Errors the device detects (non-finite gradient,
+ *     an index outside the buffer) are recorded in a sticky device flag word
+ *     and reported by iql_status().
+ *   - Floating-point tensors are IEEE binary32 unless the config selects
+ *     IQLH_BF16 for the GEMM operand `states` (bfloat16, stored as uint16).
+ *   - Row-major layouts throughout; weights are [out, in].
+ */
+#ifndef IQLHER_H
+#define IQLHER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    IQLH_OK = 0,
+    IQLH_EINVAL = -1,     /* null pointer, bad size or hyper-parameter       */
+    IQLH_ESHAPE = -2,     /* shape the library has no kernel for             */
+    IQLH_ENOMEM = -3,     /* device allocation failed (iql_create only)      */
+    IQLH_EHIP = -4,       /* a HIP runtime call failed                       */
+    IQLH_ENONFINITE = -5  /* iql_status: the device saw a non-finite value   */
+} iqlh_status;
+
+typedef enum { IQLH_F32 = 0, IQLH_BF16 = 1 } iqlh_dtype;
+
+/* Sticky device flag bits (iql_status, her_out.d_flags, iqlh_adam.d_flags). */
+#define IQLH_FLAG_NONFINITE_GRAD 0x1  /* Adam saw a non-finite clipped grad  */
+#define IQLH_FLAG_BAD_INDEX      0x2  /* HER source/donor outside the buffer */
+#define IQLH_FLAG_NONFINITE_LOSS 0x4  /* non-finite expectile loss term      */
+
+/* ------------------------------------------------------------------------
+ * IQL value trainer ([P1] "Current State / IQL (CPU)", "CUDA Kernel:
+ * iql_value_kernel.cu", "Rust Integration: gpu_iql_trainer.rs"; grouped
+ * high/low trainers: [P3] "2C. Grouped GEMM for IQL").
+ *
+ * V(s) = w3 . relu(W2 relu(W1 s + b1) + b2) + b3, W1 [hidden, state_dim],
+ * W2 [hidden, hidden], w3 [hidden], b3 scalar.  Flat parameter order per
+ * group: w1, b1, w2, b2, w3, b3 (iql_num_params elements).
+ * ---------------------------------------------------------------------- */
+typedef struct iqlh_config {
+    int32_t state_dim;      /* S >= 1                                          */
+    int32_t hidden;         /* H: width of both hidden layers                  */
+    int32_t max_batch;      /* largest B passed to iql_train_step              */
+    int32_t num_groups;     /* 1 or 2 trainers sharing states and q_taken      */
+    int32_t compute_dtype;  /* iqlh_dtype of `states` and of the GEMM operands */
+    int32_t reserved0;
+    int64_t states_ld;      /* row stride of `states`, elements, >= state_dim  */
+    float tau[2];           /* expectile tau per group, in [0, 1]              */
+    float lr, beta1, beta2, eps, weight_decay, max_grad_norm;
+    float weight_clamp_max_abs;  /* post-update |p| bound, 0 = off ([P2] Mech 9) */
+} iqlh_config;
+
+typedef struct iql_trainer* iql_handle;
+
+/* Parameters per group: S*H + H + H*H + H + H + 1.  Host only. */
+int iql_num_params(int32_t state_dim, int32_t hidden, int64_t* out_count);
+
+/* Creates a trainer on the current device.  `init_params_host` holds
+ * num_groups * iql_num_params floats (group-major) and is copied; Adam
+ * moments start at zero and the step counter t at 0.  The handle owns the
+ * fp32 master weights, Adam moments, gradients, the GEMM-operand shadows of
+ * the weights and the per-workgroup partial buffers sized for max_batch.
+ * Returns IQLH_ESHAPE when no kernel is built for (dtype, state_dim, hidden). */
+int iql_create(const iqlh_config* cfg, const float* init_params_host, iql_handle* out);
+int iql_destroy(iql_handle h);
+
+/* One IQL step for every group, enqueued on `stream`:
+ *   V(s) forward, expectile loss on diff = q_taken - V with weight tau where
+ *   diff >= 0 and 1 - tau elsewhere, loss = mean over the B rows ([P1] "Current
+ *   State / IQL (CPU)"); backward through the MLP (q_taken is a stop-gradient
+ *   target, [P1] "IQL GPU Porting"); global L2 norm of the flat gradient; clip
+ *   by max_grad_norm / norm when norm > max_grad_norm; Adam with bias
+ *   correction, t incremented before use, non-finite elements skipped and the
+ *   gradient zeroed after use ([P2] section on iqn_adam_kernel).
+ *   states   device [B, states_ld] of compute_dtype (only the first state_dim
+ *            columns are read).
+ *   q_taken  device [B] f32, Q(s, a_taken).
+ *   out_v    device [num_groups, B] f32, V(s) before the update, or NULL.
+ *   out_loss device [num_groups] f32, or NULL.
+ *   out_grad_norm device [num_groups] f32, pre-clip norm, or NULL.
+ * 1 <= B <= max_batch.  Also increments the device step counter. */
+int iql_train_step(iql_handle h, const void* states, const float* q_taken, int32_t batch,
+                   float* out_v, float* out_loss, float* out_grad_norm, void* stream);
+
+/* The two halves of iql_train_step, for callers that time or schedule them
+ * separately ([P1] "CUDA Kernel: iql_value_kernel.cu" fuses forward, loss and
+ * backward into one launch; the norm and Adam follow as separate phases):
+ *   iql_compute_gradients: V(s) into out_v (or NULL) and the expectile-loss
+ *     gradient of every group into the handle's per-workgroup partial
+ *     buffers (overwritten, not accumulated).  Parameters are not changed.
+ *   iql_apply_gradients: sums those partials in a fixed order, writes the
+ *     mean loss and the pre-clip norm, clips, applies Adam and increments t
+ *     and the step counter.  `batch` must equal the preceding
+ *     iql_compute_gradients call's batch. */
+int iql_compute_gradients(iql_handle h, const void* states, const float* q_taken, int32_t batch,
+                          float* out_v, void* stream);
+int iql_apply_gradients(iql_handle h, int32_t batch, float* out_loss, float* out_grad_norm,
+                        void* stream);
+
+/* Measurement aid: launches the iql_compute_gradients kernel `reps` times,
+ * each bracketed by HIP events that the dispatch itself records, waits for
+ * each, and writes the mean kernel duration in microseconds.  Synchronous and
+ * not capturable; the partial buffers are overwritten, parameters unchanged. */
+int iql_time_compute_gradients(iql_handle h, const void* states, const float* q_taken,
+                               int32_t batch, int32_t reps, float* out_avg_us, void* stream);
+
+/* Copies one group's state to / from device buffers of iql_num_params floats
+ * (params, m, v) and one int32 (t).  set_state also refreshes the shadows. */
+int iql_get_state(iql_handle h, int32_t group, float* d_params, float* d_m, float* d_v,
+                  int32_t* d_t, void* stream);
+int iql_set_state(iql_handle h, int32_t group, const float* d_params, const float* d_m,
+                  const float* d_v, const int32_t* d_t, void* stream);
+
+/* Device int64 step counter owned by the handle (0 before the first step);
+ * pass it to her_relabel as d_step so a replayed graph draws new donors. */
+const int64_t* iql_step_counter(iql_handle h);
+/* Device int32 sticky flag word owned by the handle (IQLH_FLAG_*). */
+int32_t* iql_flags(iql_handle h);
+/* Synchronises the device, copies the flag word to *flags_host (may be NULL)
+ * and returns IQLH_ENONFINITE if a non-finite flag is set, IQLH_ESHAPE if a
+ * bad-index flag is set, else IQLH_OK.  Never call it inside a timed loop. */
+int iql_status(iql_handle h, int32_t* flags_host);
+
+/* ------------------------------------------------------------------------
+ * Advantage-weighted policy ([P1] "Current State / IQL (CPU)", item
+ * "Advantage-weighted action selection"):
+ *   pi[g, b, a] = softmax_a(beta * clamp(q[b, a] - v[g, b], -10, 10)),
+ * with the row maximum subtracted before exponentiation.
+ *   q  device [B, A] f32;  v device [G, B] f32;  out_pi device [G, B, A] f32.
+ * 1 <= A <= 64.  NaN gaps clamp to the bound (fminf/fmaxf semantics). */
+int iql_aw_policy(const float* q, const float* v, int32_t num_groups, int32_t batch,
+                  int32_t num_actions, float beta, float* out_pi, void* stream);
+
+/* ------------------------------------------------------------------------
+ * HER relabelling ([P1] "CUDA Kernel: her_relabel_kernel.cu", "Donor Index
+ * Generation", "How HER Interacts with GPU PER").
+ *
+ * For each row i < n with src = source_idx[i] and donor chosen by strategy:
+ *   FINAL  donor = end - 1, end = exclusive end of src's episode;
+ *   FUTURE donor uniform in [src + 1, end), or src when that range is empty;
+ *   RANDOM donor uniform in [0, buffer_size).
+ * Uniform draws: word 0 of Philox4x64-10 (Salmon et al., SC'11) with key
+ * (seed, 0x484552646F6E6F72) and counter (i, *d_step, 0, 0), mapped to
+ * lo + floor(word * span / 2^64).
+ *   out.states[i]      = states[src] with entries [0, goal_dim) replaced by
+ *                        next_states[donor][0, goal_dim)  (f32 or bf16 RNE)
+ *   out.next_states[i] = next_states[src], same goal replacement (f32)
+ *   out.actions[i] = actions[src], out.dones[i] = dones[src]
+ *   out.rewards[i] = reward_hit if sqrt(sum_d (next_states[src][d] -
+ *                    next_states[donor][d])^2) < goal_threshold else
+ *                    reward_miss, summed in goal order in binary32 without
+ *                    fused multiply-add, correctly rounded sqrt.
+ * Writing out.states = X + (B - n) * ld appends the relabelled rows to a
+ * merged batch X without a copy (normal rows first). */
+typedef enum { HER_FINAL = 0, HER_FUTURE = 1, HER_RANDOM = 2 } her_strategy;
+
+typedef struct her_config {
+    int32_t state_dim;       /* S                                         */
+    int32_t goal_dim;        /* G, 0 <= G <= S                             */
+    int32_t strategy;        /* her_strategy                               */
+    int32_t reserved0;
+    float goal_threshold;    /* 0.01 on the pages                          */
+    float reward_hit;        /* +1.0                                       */
+    float reward_miss;       /* -0.01                                      */
+    float reserved1;
+} her_config;
+
+typedef struct her_buffer {
+    const float* states;        /* device [capacity, state_dim] f32        */
+    const float* next_states;   /* device [capacity, state_dim] f32        */
+    const int32_t* actions;     /* device [capacity]                       */
+    const float* rewards;       /* device [capacity]; not read (the reward is
+                                   recomputed), may be NULL               */
+    const float* dones;         /* device [capacity]                       */
+    const int32_t* episode_ends;/* device [num_episodes], exclusive ends,
+                                   ascending; episode e = [ends[e-1], ends[e]) */
+    int64_t capacity;           /* rows allocated                          */
+    int64_t buffer_size;        /* rows filled, <= capacity, <= ends[last] */
+    int32_t num_episodes;       /* >= 1                                    */
+    int32_t reserved0;
+} her_buffer;
+
+typedef struct her_out {
+    int32_t* donor_idx;         /* device [n] or NULL                      */
+    void* states;               /* device [n, states_ld], states_dtype     */
+    int32_t states_dtype;       /* iqlh_dtype                              */
+    int32_t reserved0;
+    int64_t states_ld;          /* >= state_dim                            */
+    float* next_states;         /* device [n, state_dim] f32 or NULL       */
+    int32_t* actions;           /* device [n] or NULL                      */
+    float* rewards;             /* device [n]                              */
+    float* dones;               /* device [n] or NULL                      */
+    int32_t* d_flags;           /* device sticky flag word or NULL         */
+} her_out;
+
+/* n >= 0 rows (n == 0 is a no-op).  d_step: device int64 counter (NULL = 0).
+ * A source index outside [0, buffer_size) or a donor outside it (malformed
+ * episode_ends) sets IQLH_FLAG_BAD_INDEX; that row's outputs are zeroed and
+ * its donor_idx is -1. */
+int her_relabel(const her_config* cfg, const her_buffer* buf, const int32_t* source_idx,
+                int32_t n, uint64_t seed, const int64_t* d_step, const her_out* out,
+                void* stream);
+
+/* ------------------------------------------------------------------------
+ * Budgeted clipped-SAXPY accumulation ([P5] "Design -- Why the current
+ * per-component clipping is wrong" / "Proper design", "Task 1", "Task 2"):
+ *   n_k = ||s_k||,  c_k = f_k*mgn / n_k if n_k > f_k*mgn and n_k > 0 else 1,
+ *   grad = sum_k alpha_k * c_k * s_k  (k = 0 is the primary source),
+ * then optionally Adam on the parameters with the safety clip at mgn.
+ *   grad_buf     device [n] f32 output; may alias sources[0] (in place).
+ *   sources      host array of k device pointers [n] f32.
+ *   fractions, alphas  host [k] f32.
+ *   out_norms    device [k + 1] f32: n_0 .. n_{k-1}, then ||grad||; or NULL.
+ *   adam         NULL, or Adam state for the parameters grad belongs to; when
+ *                given, grad_buf is consumed and left zeroed.
+ *   workspace    device, >= grad_budget_workspace_bytes(n, k) bytes, no
+ *                initial contents required.
+ * 1 <= k <= 8, n >= 1. */
+typedef struct iqlh_adam {
+    float* params;              /* device [n] */
+    float* m;                   /* device [n] */
+    float* v;                   /* device [n] */
+    int32_t* t;                 /* device step counter, incremented before use */
+    int32_t* d_flags;           /* device sticky flag word or NULL */
+    float lr, beta1, beta2, eps, weight_decay, max_grad_norm, weight_clamp_max_abs;
+    float reserved0;
+} iqlh_adam;
+
+int grad_budget_workspace_bytes(int64_t n, int32_t num_sources, size_t* bytes);
+int grad_budget_accumulate(float* grad_buf, const float* const* sources, const float* fractions,
+                           const float* alphas, int32_t num_sources, int64_t n,
+                           float max_grad_norm, float* out_norms, const iqlh_adam* adam,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Thread-local text of the last error returned on this thread ("" if none). */
+const char* iqlh_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* IQLHER_H */

@@ -1,0 +1,373 @@
+// C ABI of the IQL + HER step (include/iqlher.h): argument validation, the
+// trainer handle and its device buffers, and kernel dispatch.  Every check
+// that can fail on the host runs before the first HIP call.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/iqlher.h"
+#include "launch.hpp"
+
+using namespace iqlh;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(IQLH_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool finite_pos(float x) { return std::isfinite(x) && x > 0.f; }
+
+}  // namespace
+
+struct iql_trainer {
+    iqlh_config cfg;
+    IqlDims dims;
+    IqlBuffers buf;
+    int device;
+    std::vector<void*> allocs;
+};
+
+extern "C" {
+
+const char* iqlh_last_error(void) { return g_err; }
+
+int iql_num_params(int32_t state_dim, int32_t hidden, int64_t* out_count) {
+    if (!out_count) return fail(IQLH_EINVAL, "iql_num_params: out_count is NULL");
+    if (state_dim < 1 || hidden < 1) return fail(IQLH_EINVAL, "iql_num_params: dims must be >= 1");
+    const int64_t S = state_dim, H = hidden;
+    *out_count = S * H + H + H * H + H + H + 1;
+    return IQLH_OK;
+}
+
+static int check_config(const iqlh_config* c) {
+    if (!c) return fail(IQLH_EINVAL, "config is NULL");
+    if (c->state_dim < 1 || c->hidden < 1) return fail(IQLH_EINVAL, "state_dim and hidden must be >= 1");
+    if (c->max_batch < 1) return fail(IQLH_EINVAL, "max_batch must be >= 1");
+    if (c->num_groups < 1 || c->num_groups > 2) return fail(IQLH_EINVAL, "num_groups must be 1 or 2");
+    if (c->compute_dtype != IQLH_F32 && c->compute_dtype != IQLH_BF16)
+        return fail(IQLH_EINVAL, "compute_dtype must be IQLH_F32 or IQLH_BF16");
+    if (c->states_ld < c->state_dim) return fail(IQLH_EINVAL, "states_ld < state_dim");
+    for (int g = 0; g < c->num_groups; ++g)
+        if (!(c->tau[g] >= 0.f && c->tau[g] <= 1.f)) return fail(IQLH_EINVAL, "tau[%d] outside [0, 1]", g);
+    if (!(c->lr >= 0.f) || !std::isfinite(c->lr)) return fail(IQLH_EINVAL, "lr must be finite and >= 0");
+    if (!(c->beta1 >= 0.f && c->beta1 < 1.f) || !(c->beta2 >= 0.f && c->beta2 < 1.f))
+        return fail(IQLH_EINVAL, "beta1 and beta2 must be in [0, 1)");
+    if (!finite_pos(c->eps)) return fail(IQLH_EINVAL, "eps must be finite and > 0");
+    if (!(c->weight_decay >= 0.f) || !std::isfinite(c->weight_decay))
+        return fail(IQLH_EINVAL, "weight_decay must be finite and >= 0");
+    if (!(c->max_grad_norm > 0.f)) return fail(IQLH_EINVAL, "max_grad_norm must be > 0");
+    if (!(c->weight_clamp_max_abs >= 0.f)) return fail(IQLH_EINVAL, "weight_clamp_max_abs must be >= 0");
+    if (!iql_supported(c->compute_dtype, c->state_dim, c->hidden))
+        return fail(IQLH_ESHAPE, "no kernel for dtype=%d state_dim=%d hidden=%d", c->compute_dtype,
+                    c->state_dim, c->hidden);
+    return IQLH_OK;
+}
+
+static void free_all(iql_trainer* t) {
+    for (void* p : t->allocs) (void)hipFree(p);
+    t->allocs.clear();
+}
+
+static int dev_alloc(iql_trainer* t, void** p, size_t bytes) {
+    hipError_t e = hipMalloc(p, bytes < 256 ? 256 : bytes);
+    if (e != hipSuccess) return fail(IQLH_ENOMEM, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
+    t->allocs.push_back(*p);
+    e = hipMemset(*p, 0, bytes < 256 ? 256 : bytes);
+    if (e != hipSuccess) return hip_fail(e, "hipMemset");
+    return IQLH_OK;
+}
+
+int iql_create(const iqlh_config* cfg, const float* init_params_host, iql_handle* out) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (!init_params_host) return fail(IQLH_EINVAL, "init_params_host is NULL");
+    if (!out) return fail(IQLH_EINVAL, "out is NULL");
+    *out = nullptr;
+    iql_trainer* t = new (std::nothrow) iql_trainer();
+    if (!t) return fail(IQLH_ENOMEM, "host allocation failed");
+    t->cfg = *cfg;
+    hipError_t e = hipGetDevice(&t->device);
+    if (e != hipSuccess) { delete t; return hip_fail(e, "hipGetDevice"); }
+    const int G = cfg->num_groups, S = cfg->state_dim, H = cfg->hidden;
+    int64_t P = 0;
+    iql_num_params(S, H, &P);
+    IqlDims& d = t->dims;
+    d.S = S; d.H = H; d.G = G; d.dtype = cfg->compute_dtype;
+    d.S_pad = iql_s_pad(d.dtype, S, H);
+    d.P = P;
+    const int BT = iql_tile_samples(d.dtype, S, H);
+    const int max_wg = (cfg->max_batch + BT - 1) / BT;
+    const int rb = iql_reduce_blocks(P);
+    const size_t esz = d.dtype == IQLH_BF16 ? 2 : 4;
+    IqlBuffers& b = t->buf;
+    b.max_wg = max_wg;
+    b.max_rb = rb;
+    struct { void** p; size_t bytes; } plan[] = {
+        {(void**)&b.params, sizeof(float) * G * P},
+        {(void**)&b.m, sizeof(float) * G * P},
+        {(void**)&b.v, sizeof(float) * G * P},
+        {(void**)&b.grad, sizeof(float) * G * P},
+        {(void**)&b.t, sizeof(int32_t) * G},
+        {(void**)&b.step, sizeof(int64_t)},
+        {(void**)&b.flags, sizeof(int32_t)},
+        {(void**)&b.w1s, esz * G * H * d.S_pad},
+        {(void**)&b.w2s, esz * G * H * H},
+        {(void**)&b.w2ts, esz * G * H * H},
+        {(void**)&b.part, sizeof(float) * G * (size_t)max_wg * P},
+        {(void**)&b.loss_part, sizeof(float) * G * (size_t)max_wg},
+        {(void**)&b.sq_part, sizeof(float) * G * (size_t)rb},
+    };
+    for (auto& a : plan) {
+        rc = dev_alloc(t, a.p, a.bytes);
+        if (rc) { free_all(t); delete t; return rc; }
+    }
+    e = hipMemcpy(b.params, init_params_host, sizeof(float) * G * P, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = launch_iql_refresh_shadows(d, b, nullptr);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) { free_all(t); delete t; return hip_fail(e, "iql_create upload"); }
+    *out = t;
+    return IQLH_OK;
+}
+
+int iql_destroy(iql_handle h) {
+    if (!h) return fail(IQLH_EINVAL, "handle is NULL");
+    (void)hipDeviceSynchronize();
+    free_all(h);
+    delete h;
+    return IQLH_OK;
+}
+
+static int check_step_args(iql_handle h, const void* states, const float* q_taken, int32_t batch) {
+    if (!h) return fail(IQLH_EINVAL, "handle is NULL");
+    if (!states || !q_taken) return fail(IQLH_EINVAL, "states and q_taken must be non-NULL");
+    if (batch < 1 || batch > h->cfg.max_batch)
+        return fail(IQLH_EINVAL, "batch %d outside [1, max_batch=%d]", batch, h->cfg.max_batch);
+    return IQLH_OK;
+}
+
+static AdamHyper adam_hyper(const iqlh_config& c) {
+    return AdamHyper{c.lr, c.beta1, c.beta2, c.eps, c.weight_decay, c.max_grad_norm, c.weight_clamp_max_abs};
+}
+
+int iql_compute_gradients(iql_handle h, const void* states, const float* q_taken, int32_t batch,
+                          float* out_v, void* stream) {
+    int rc = check_step_args(h, states, q_taken, batch);
+    if (rc) return rc;
+    hipError_t e = launch_iql_fwd_bwd(h->dims, h->buf, h->cfg.tau, states, h->cfg.states_ld, q_taken, batch,
+                                      out_v, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "iql_compute_gradients launch");
+    return IQLH_OK;
+}
+
+int iql_time_compute_gradients(iql_handle h, const void* states, const float* q_taken, int32_t batch,
+                               int32_t reps, float* out_avg_us, void* stream) {
+    int rc = check_step_args(h, states, q_taken, batch);
+    if (rc) return rc;
+    if (reps < 1 || !out_avg_us) return fail(IQLH_EINVAL, "reps must be >= 1 and out_avg_us non-NULL");
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    hipError_t e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    double total_ms = 0.0;
+    for (int r = 0; r < reps && e == hipSuccess; ++r) {
+        e = launch_iql_fwd_bwd(h->dims, h->buf, h->cfg.tau, states, h->cfg.states_ld, q_taken, batch,
+                               nullptr, (hipStream_t)stream, e0, e1);
+        if (e == hipSuccess) e = hipEventSynchronize(e1);
+        float ms = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+        total_ms += ms;
+    }
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (e != hipSuccess) return hip_fail(e, "iql_time_compute_gradients");
+    *out_avg_us = (float)(total_ms * 1000.0 / reps);
+    return IQLH_OK;
+}
+
+int iql_apply_gradients(iql_handle h, int32_t batch, float* out_loss, float* out_grad_norm, void* stream) {
+    if (!h) return fail(IQLH_EINVAL, "handle is NULL");
+    if (batch < 1 || batch > h->cfg.max_batch)
+        return fail(IQLH_EINVAL, "batch %d outside [1, max_batch=%d]", batch, h->cfg.max_batch);
+    hipError_t e = launch_iql_update(h->dims, h->buf, adam_hyper(h->cfg), batch, out_loss, out_grad_norm,
+                                     (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "iql_apply_gradients launch");
+    return IQLH_OK;
+}
+
+int iql_train_step(iql_handle h, const void* states, const float* q_taken, int32_t batch,
+                   float* out_v, float* out_loss, float* out_grad_norm, void* stream) {
+    int rc = iql_compute_gradients(h, states, q_taken, batch, out_v, stream);
+    if (rc) return rc;
+    return iql_apply_gradients(h, batch, out_loss, out_grad_norm, stream);
+}
+
+int iql_get_state(iql_handle h, int32_t group, float* d_params, float* d_m, float* d_v, int32_t* d_t,
+                  void* stream) {
+    if (!h) return fail(IQLH_EINVAL, "handle is NULL");
+    if (group < 0 || group >= h->dims.G) return fail(IQLH_EINVAL, "group %d out of range", group);
+    const int64_t P = h->dims.P;
+    hipStream_t s = (hipStream_t)stream;
+    const size_t bytes = sizeof(float) * P;
+    hipError_t e = hipSuccess;
+    if (d_params) e = hipMemcpyAsync(d_params, h->buf.params + group * P, bytes, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess && d_m) e = hipMemcpyAsync(d_m, h->buf.m + group * P, bytes, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess && d_v) e = hipMemcpyAsync(d_v, h->buf.v + group * P, bytes, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess && d_t)
+        e = hipMemcpyAsync(d_t, h->buf.t + group, sizeof(int32_t), hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "iql_get_state");
+    return IQLH_OK;
+}
+
+int iql_set_state(iql_handle h, int32_t group, const float* d_params, const float* d_m, const float* d_v,
+                  const int32_t* d_t, void* stream) {
+    if (!h) return fail(IQLH_EINVAL, "handle is NULL");
+    if (group < 0 || group >= h->dims.G) return fail(IQLH_EINVAL, "group %d out of range", group);
+    if (!d_params || !d_m || !d_v || !d_t) return fail(IQLH_EINVAL, "set_state needs params, m, v and t");
+    const int64_t P = h->dims.P;
+    hipStream_t s = (hipStream_t)stream;
+    const size_t bytes = sizeof(float) * P;
+    hipError_t e = hipMemcpyAsync(h->buf.params + group * P, d_params, bytes, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(h->buf.m + group * P, d_m, bytes, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(h->buf.v + group * P, d_v, bytes, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(h->buf.t + group, d_t, sizeof(int32_t), hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = launch_iql_refresh_shadows(h->dims, h->buf, s);
+    if (e != hipSuccess) return hip_fail(e, "iql_set_state");
+    return IQLH_OK;
+}
+
+const int64_t* iql_step_counter(iql_handle h) { return h ? h->buf.step : nullptr; }
+int32_t* iql_flags(iql_handle h) { return h ? h->buf.flags : nullptr; }
+
+int iql_status(iql_handle h, int32_t* flags_host) {
+    if (!h) return fail(IQLH_EINVAL, "handle is NULL");
+    int32_t f = 0;
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemcpy(&f, h->buf.flags, sizeof(int32_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "iql_status");
+    if (flags_host) *flags_host = f;
+    if (f & (IQLH_FLAG_NONFINITE_GRAD | IQLH_FLAG_NONFINITE_LOSS))
+        return fail(IQLH_ENONFINITE, "device flagged a non-finite value (flags=0x%x)", f);
+    if (f & IQLH_FLAG_BAD_INDEX) return fail(IQLH_ESHAPE, "device flagged an index outside the buffer");
+    return IQLH_OK;
+}
+
+int iql_aw_policy(const float* q, const float* v, int32_t num_groups, int32_t batch, int32_t num_actions,
+                  float beta, float* out_pi, void* stream) {
+    if (!q || !v || !out_pi) return fail(IQLH_EINVAL, "iql_aw_policy: NULL pointer");
+    if (num_groups < 1 || batch < 1) return fail(IQLH_EINVAL, "iql_aw_policy: num_groups and batch must be >= 1");
+    if (num_actions < 1 || num_actions > 64) return fail(IQLH_EINVAL, "iql_aw_policy: num_actions must be in [1, 64]");
+    if (!std::isfinite(beta)) return fail(IQLH_EINVAL, "iql_aw_policy: beta must be finite");
+    hipError_t e = launch_aw_policy(q, v, num_groups, batch, num_actions, beta, out_pi, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "iql_aw_policy launch");
+    return IQLH_OK;
+}
+
+int her_relabel(const her_config* cfg, const her_buffer* buf, const int32_t* source_idx, int32_t n,
+                uint64_t seed, const int64_t* d_step, const her_out* out, void* stream) {
+    if (!cfg || !buf || !out) return fail(IQLH_EINVAL, "her_relabel: NULL argument struct");
+    if (n < 0) return fail(IQLH_EINVAL, "her_relabel: n < 0");
+    if (cfg->state_dim < 1) return fail(IQLH_EINVAL, "her_relabel: state_dim < 1");
+    if (cfg->goal_dim < 0 || cfg->goal_dim > cfg->state_dim)
+        return fail(IQLH_EINVAL, "her_relabel: goal_dim outside [0, state_dim]");
+    if (cfg->strategy < HER_FINAL || cfg->strategy > HER_RANDOM)
+        return fail(IQLH_EINVAL, "her_relabel: unknown strategy %d", cfg->strategy);
+    if (!std::isfinite(cfg->goal_threshold)) return fail(IQLH_EINVAL, "her_relabel: threshold not finite");
+    if (buf->capacity < 1 || buf->buffer_size < 1 || buf->buffer_size > buf->capacity)
+        return fail(IQLH_EINVAL, "her_relabel: need 1 <= buffer_size <= capacity");
+    if (buf->buffer_size > 0x7FFFFFFFLL) return fail(IQLH_EINVAL, "her_relabel: buffer_size exceeds int32 indices");
+    if (cfg->strategy != HER_RANDOM && (buf->num_episodes < 1 || !buf->episode_ends))
+        return fail(IQLH_EINVAL, "her_relabel: final/future need episode_ends");
+    if (out->states_dtype != IQLH_F32 && out->states_dtype != IQLH_BF16)
+        return fail(IQLH_EINVAL, "her_relabel: bad out.states_dtype");
+    if (out->states_ld < cfg->state_dim) return fail(IQLH_EINVAL, "her_relabel: out.states_ld < state_dim");
+    if (n == 0) return IQLH_OK;
+    if (!buf->states || !buf->next_states || !source_idx || !out->states || !out->rewards)
+        return fail(IQLH_EINVAL, "her_relabel: NULL device pointer");
+    if ((out->actions && !buf->actions) || (out->dones && !buf->dones))
+        return fail(IQLH_EINVAL, "her_relabel: out.actions/out.dones need buf.actions/buf.dones");
+    HerArgs a;
+    a.states = buf->states; a.next_states = buf->next_states; a.actions = buf->actions; a.dones = buf->dones;
+    a.episode_ends = buf->episode_ends; a.source_idx = source_idx; a.d_step = d_step;
+    a.donor_out = out->donor_idx; a.out_states = out->states; a.out_next_states = out->next_states;
+    a.out_actions = out->actions; a.out_rewards = out->rewards; a.out_dones = out->dones; a.flags = out->d_flags;
+    a.buffer_size = buf->buffer_size; a.out_ld = out->states_ld; a.seed = seed;
+    a.num_episodes = buf->num_episodes; a.n = n;
+    a.S = cfg->state_dim; a.G = cfg->goal_dim; a.strategy = cfg->strategy;
+    a.out_bf16 = out->states_dtype == IQLH_BF16;
+    a.threshold = cfg->goal_threshold; a.reward_hit = cfg->reward_hit; a.reward_miss = cfg->reward_miss;
+    hipError_t e = launch_her_relabel(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "her_relabel launch");
+    return IQLH_OK;
+}
+
+int grad_budget_workspace_bytes(int64_t n, int32_t num_sources, size_t* bytes) {
+    if (!bytes) return fail(IQLH_EINVAL, "bytes is NULL");
+    if (n < 1) return fail(IQLH_EINVAL, "n must be >= 1");
+    if (num_sources < 1 || num_sources > kMaxSources)
+        return fail(IQLH_EINVAL, "num_sources must be in [1, %d]", kMaxSources);
+    const int nb = budget_num_blocks(n);
+    *bytes = sizeof(float) * (size_t)(num_sources + 1) * nb;
+    return IQLH_OK;
+}
+
+int grad_budget_accumulate(float* grad_buf, const float* const* sources, const float* fractions,
+                           const float* alphas, int32_t num_sources, int64_t n, float max_grad_norm,
+                           float* out_norms, const iqlh_adam* adam, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    size_t need = 0;
+    int rc = grad_budget_workspace_bytes(n, num_sources, &need);
+    if (rc) return rc;
+    if (!grad_buf || !sources || !fractions || !alphas || !workspace)
+        return fail(IQLH_EINVAL, "grad_budget_accumulate: NULL argument");
+    if (workspace_bytes < need) return fail(IQLH_EINVAL, "workspace too small: %zu < %zu", workspace_bytes, need);
+    if (!(max_grad_norm > 0.f) || !std::isfinite(max_grad_norm))
+        return fail(IQLH_EINVAL, "max_grad_norm must be finite and > 0");
+    SourceSet s;
+    std::memset(&s, 0, sizeof(s));
+    s.k = num_sources;
+    for (int j = 0; j < num_sources; ++j) {
+        if (!sources[j]) return fail(IQLH_EINVAL, "sources[%d] is NULL", j);
+        if (!(fractions[j] >= 0.f) || !std::isfinite(fractions[j]))
+            return fail(IQLH_EINVAL, "fractions[%d] must be finite and >= 0", j);
+        if (!std::isfinite(alphas[j])) return fail(IQLH_EINVAL, "alphas[%d] must be finite", j);
+        s.ptr[j] = sources[j];
+        s.frac[j] = fractions[j];
+        s.alpha[j] = alphas[j];
+    }
+    AdamHyper hp{};
+    if (adam) {
+        if (!adam->params || !adam->m || !adam->v || !adam->t)
+            return fail(IQLH_EINVAL, "adam: params, m, v and t must be non-NULL");
+        if (!(adam->beta1 >= 0.f && adam->beta1 < 1.f) || !(adam->beta2 >= 0.f && adam->beta2 < 1.f))
+            return fail(IQLH_EINVAL, "adam: beta1 and beta2 must be in [0, 1)");
+        if (!finite_pos(adam->eps) || !std::isfinite(adam->lr) || !(adam->lr >= 0.f))
+            return fail(IQLH_EINVAL, "adam: bad eps or lr");
+        if (!(adam->max_grad_norm > 0.f)) return fail(IQLH_EINVAL, "adam: max_grad_norm must be > 0");
+        hp = AdamHyper{adam->lr, adam->beta1, adam->beta2, adam->eps, adam->weight_decay, adam->max_grad_norm,
+                       adam->weight_clamp_max_abs};
+    }
+    hipError_t e = launch_budget(grad_buf, s, n, max_grad_norm, out_norms, adam ? adam->params : nullptr,
+                                 adam ? adam->m : nullptr, adam ? adam->v : nullptr, adam ? adam->t : nullptr,
+                                 adam ? adam->d_flags : nullptr, adam ? &hp : nullptr, (float*)workspace,
+                                 (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "grad_budget_accumulate launch");
+    return IQLH_OK;
+}
+
+}  // extern "C"

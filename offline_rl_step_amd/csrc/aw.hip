@@ -1,0 +1,82 @@
+// Advantage-weighted policy pi = softmax(beta * clamp(Q - V, -10, 10)), gfx950.
+//
+// Follows "GPU IQL + HER Porting Plan", section "Current State / IQL (CPU)",
+// item "Advantage-weighted action selection": per-action advantage Q - V,
+// clamp to [-10, 10], scale by the temperature beta, softmax over actions with
+// the row maximum subtracted.
+//
+// HBM-bound.  A workgroup owns 256 consecutive rows: the [256, A] slab of Q is
+// read once with coalesced loads into LDS (padded to an odd row stride so the
+// per-row reads are bank-conflict free), every group's policy is computed from
+// that one copy, and each result slab is written back with coalesced stores.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace iqlh {
+
+constexpr int kAwRows = 256;
+
+__global__ __launch_bounds__(256) void aw_policy_kernel(const float* __restrict__ q,
+                                                         const float* __restrict__ v, int G, int B,
+                                                         int A, float beta, float* __restrict__ pi) {
+    extern __shared__ float lds[];
+    const int AP = A | 1;  // odd stride
+    float* sq = lds;                  // [kAwRows][AP]
+    float* sp = lds + kAwRows * AP;   // [kAwRows][AP]
+    const int64_t row0 = (int64_t)blockIdx.x * kAwRows;
+    const int rows = (int)min<int64_t>(kAwRows, (int64_t)B - row0);
+    const int cnt = rows * A;
+    const float* qs = q + row0 * A;
+    for (int idx = threadIdx.x; idx < cnt; idx += 256) {
+        const int r = idx / A, c = idx - r * A;
+        sq[r * AP + c] = qs[idx];
+    }
+    __syncthreads();
+    const int r = threadIdx.x;
+    for (int g = 0; g < G; ++g) {
+        if (r < rows) {
+            const float vv = v[(int64_t)g * B + row0 + r];
+            const float* qr = sq + r * AP;
+            float* pr = sp + r * AP;
+            float mx = -INFINITY;
+            for (int c = 0; c < A; ++c) {
+                const float x = beta * fminf(fmaxf(qr[c] - vv, -10.f), 10.f);
+                pr[c] = x;
+                mx = fmaxf(mx, x);
+            }
+            float s = 0.f;
+            for (int c = 0; c < A; ++c) {
+                const float e = expf(pr[c] - mx);
+                pr[c] = e;
+                s += e;
+            }
+            for (int c = 0; c < A; ++c) pr[c] = pr[c] / s;
+        }
+        __syncthreads();
+        float* ps = pi + ((int64_t)g * B + row0) * A;
+        for (int idx = threadIdx.x; idx < cnt; idx += 256) {
+            const int rr = idx / A, c = idx - rr * A;
+            ps[idx] = sp[rr * AP + c];
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_aw_policy(const float* q, const float* v, int G, int B, int A, float beta,
+                            float* pi, hipStream_t stream) {
+    if (B <= 0) return hipSuccess;
+    const unsigned blocks = (unsigned)((B + kAwRows - 1) / kAwRows);
+    const size_t lds = (size_t)2 * kAwRows * (A | 1) * sizeof(float);
+    static bool attr_set = false;
+    if (lds > 64 * 1024 && !attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)aw_policy_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)(2 * kAwRows * 65 * sizeof(float)));
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(aw_policy_kernel, dim3(blocks), dim3(256), lds, stream, q, v, G, B, A, beta, pi);
+    return hipGetLastError();
+}
+
+}  // namespace iqlh

@@ -1,0 +1,79 @@
+// Device helpers shared by the IQL + HER kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define IQLH_DEV __device__ __forceinline__
+
+namespace iqlh {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bfloat16
+// Round-to-nearest-even float -> bfloat16 bits; NaN becomes 0x7FC0.
+IQLH_DEV uint16_t f2bf(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+IQLH_DEV float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+IQLH_DEV uint32_t pack_bf2(float lo, float hi) {
+    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// ---------------------------------------------------------------- Philox
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+// Easy as 1, 2, 3", SC'11): ten rounds of two 64x64->128 multiplies with the
+// key bumped by two Weyl constants between rounds.
+struct u64x4 { uint64_t x, y, z, w; };
+
+IQLH_DEV u64x4 philox4x64_10(u64x4 c, uint64_t k0, uint64_t k1) {
+    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) { k0 += W0; k1 += W1; }
+        const uint64_t hi0 = __umul64hi(M0, c.x), lo0 = M0 * c.x;
+        const uint64_t hi1 = __umul64hi(M1, c.z), lo1 = M1 * c.z;
+        c = u64x4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+    }
+    return c;
+}
+
+// lo + floor(r * span / 2^64); exact, span >= 1.
+IQLH_DEV int64_t uniform_index(uint64_t r, int64_t lo, uint64_t span) {
+    return lo + (int64_t)__umul64hi(r, span);
+}
+
+// ---------------------------------------------------------------- reductions
+IQLH_DEV float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+IQLH_DEV float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// Block sum in a fixed order (deterministic).  `red` holds >= NT/64 floats.
+template <int NT>
+IQLH_DEV float block_sum(float v, float* red) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    __syncthreads();
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NT / kWave; ++i) s += red[i];
+    return s;
+}
+
+IQLH_DEV void set_flag(int32_t* flags, int32_t bit) {
+    if (flags) atomicOr(flags, bit);
+}
+
+}  // namespace iqlh

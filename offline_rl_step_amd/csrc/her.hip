@@ -1,0 +1,131 @@
+// HER goal relabelling with sparse-reward recomputation, gfx950.
+//
+// Follows "GPU IQL + HER Porting Plan": section "CUDA Kernel:
+// her_relabel_kernel.cu" (copy s and s' of the source, overwrite the goal
+// entries of both with the donor's next-state goal, copy action and done,
+// reward from the Euclidean goal distance against the threshold) and section
+// "Donor Index Generation" (final / future / random donors).
+//
+// MI355X layout: one wave64 per relabelled row.  The wave finds the source's
+// episode with a 64-ary search (each lane probes one position, a ballot picks
+// the segment), so a 16k-episode table takes three dependent loads instead of
+// fourteen; the row copy is a coalesced 64-lane sweep; the relabelled state is
+// written straight into the caller's merged batch (bf16 or f32), which removes
+// the page's staging buffers and the D2D concatenation.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace iqlh {
+
+constexpr uint64_t kHerKey1 = 0x484552646F6E6F72ull;
+
+// First e in [0, E) with ends[e] > src, or -1.  All 64 lanes call it with the
+// same arguments; every branch is wave-uniform.
+IQLH_DEV int find_episode(const int32_t* __restrict__ ends, int E, int64_t src, int lane) {
+    if ((int64_t)ends[E - 1] <= src) return -1;
+    int lo = 0, hi = E - 1;  // answer in [lo, hi] and ends[hi] > src
+    for (int it = 0; it < 64 && lo < hi; ++it) {
+        const int64_t span = (int64_t)(hi - lo) + 1;
+        const int p = lo + (int)((span * lane) >> 6);
+        const bool pred = (int64_t)ends[p] > src;
+        const uint64_t m = __ballot(pred);
+        const int c = 64 - __popcll(m);  // lanes whose probe is still <= src
+        if (c == 0) {
+            hi = lo;
+        } else {
+            const int nlo = lo + (int)((span * (c - 1)) >> 6) + 1;
+            if (c < 64) hi = lo + (int)((span * c) >> 6);
+            lo = nlo;
+        }
+    }
+    if (lo >= E || (int64_t)ends[lo] <= src || (lo > 0 && (int64_t)ends[lo - 1] > src)) return -1;
+    return lo;
+}
+
+__global__ __launch_bounds__(256) void her_relabel_kernel(HerArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (i >= a.n) return;  // wave-uniform
+    const int S = a.S, G = a.G;
+    const uint64_t step = a.d_step ? (uint64_t)(*a.d_step) : 0ull;
+    const int64_t src = a.source_idx[i];
+    bool ok = src >= 0 && src < a.buffer_size;
+    int64_t donor = -1;
+    if (ok) {
+        uint64_t r = 0;
+        if (a.strategy != 0) {  // future and random draw one word
+            u64x4 c = philox4x64_10(u64x4{(uint64_t)i, step, 0ull, 0ull}, a.seed, kHerKey1);
+            r = c.x;
+        }
+        if (a.strategy == 2) {
+            donor = uniform_index(r, 0, (uint64_t)a.buffer_size);
+        } else {
+            const int e = find_episode(a.episode_ends, a.num_episodes, src, lane);
+            if (e < 0) {
+                ok = false;
+            } else {
+                const int64_t end = a.episode_ends[e];
+                if (a.strategy == 0) {
+                    donor = end - 1;
+                } else {
+                    const int64_t span = end - src - 1;
+                    donor = span > 0 ? uniform_index(r, src + 1, (uint64_t)span) : src;
+                }
+            }
+        }
+        if (donor < 0 || donor >= a.buffer_size) ok = false;
+    }
+
+    const int64_t ld = a.out_ld;
+    if (!ok) {
+        for (int d = lane; d < S; d += 64) {
+            if (a.out_bf16) ((uint16_t*)a.out_states)[i * ld + d] = 0;
+            else ((float*)a.out_states)[i * ld + d] = 0.f;
+            if (a.out_next_states) a.out_next_states[i * S + d] = 0.f;
+        }
+        if (lane == 0) {
+            if (a.donor_out) a.donor_out[i] = -1;
+            if (a.out_actions) a.out_actions[i] = 0;
+            if (a.out_dones) a.out_dones[i] = 0.f;
+            a.out_rewards[i] = 0.f;
+            set_flag(a.flags, 0x2);
+        }
+        return;
+    }
+
+    const float* __restrict__ s_src = a.states + src * S;
+    const float* __restrict__ n_src = a.next_states + src * S;
+    const float* __restrict__ n_don = a.next_states + donor * S;
+    for (int d = lane; d < S; d += 64) {
+        const bool goal = d < G;
+        const float gv = goal ? n_don[d] : 0.f;
+        const float vs = goal ? gv : s_src[d];
+        const float vn = goal ? gv : n_src[d];
+        if (a.out_bf16) ((uint16_t*)a.out_states)[i * ld + d] = f2bf(vs);
+        else ((float*)a.out_states)[i * ld + d] = vs;
+        if (a.out_next_states) a.out_next_states[i * S + d] = vn;
+    }
+    if (lane == 0) {
+        // Binary32 sum of squares in goal order, no contraction, correctly
+        // rounded square root, strict comparison.
+        float acc = 0.f;
+        for (int d = 0; d < G; ++d) {
+            const float diff = __fsub_rn(n_src[d], n_don[d]);
+            acc = __fadd_rn(acc, __fmul_rn(diff, diff));
+        }
+        const float dist = __fsqrt_rn(acc);
+        a.out_rewards[i] = dist < a.threshold ? a.reward_hit : a.reward_miss;
+        if (a.donor_out) a.donor_out[i] = (int32_t)donor;
+        if (a.out_actions) a.out_actions[i] = a.actions[src];
+        if (a.out_dones) a.out_dones[i] = a.dones[src];
+    }
+}
+
+hipError_t launch_her_relabel(const HerArgs& a, hipStream_t stream) {
+    if (a.n <= 0) return hipSuccess;
+    const unsigned blocks = (unsigned)((a.n + 3) / 4);
+    hipLaunchKernelGGL(her_relabel_kernel, dim3(blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace iqlh

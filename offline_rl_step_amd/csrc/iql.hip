@@ -1,0 +1,654 @@
+// IQL value-network step: fused V(s) forward + expectile loss + backward,
+// fixed-order gradient reduction, clipped Adam.  gfx950 MFMA.
+//
+// What is computed ("GPU IQL + HER Porting Plan", sections "Current State /
+// IQL (CPU)" and "CUDA Kernel: iql_value_kernel.cu"):
+//   z1 = W1 s + b1, h1 = relu(z1), z2 = W2 h1 + b2, h2 = relu(z2),
+//   v = w3 . h2 + b3, diff = q - v, w = tau (diff >= 0) or 1 - tau,
+//   loss = mean(w diff^2), dv = -2 w diff / B, and the gradients of the six
+//   parameter tensors; then the global-norm clip and Adam of "DQN
+//   Backward-Path NaN Audit -- SP1 Phase A" (section on iqn_adam_kernel).
+// The high/low trainers of "Phase 2: Multi-Stream Graph Parallelism" (section
+// "2C. Grouped GEMM for IQL") run as one grouped launch: blockIdx.y = group.
+//
+// MI355X design (not the pages' warp-per-sample kernel nor a chain of library
+// GEMMs):
+//   * One workgroup = NW wave64s = BT = 32*NW samples of one group.  Each wave
+//     owns 32 samples and computes every hidden feature for them with
+//     v_mfma_f32_32x32x16_bf16 (bf16 operands, fp32 accumulate) or
+//     v_mfma_f32_32x32x2f32, in the feature-major orientation
+//     D[feature][sample] = W[feature][k] * act[sample][k].
+//   * The accumulator layout of one layer (lane = sample, registers = four
+//     runs of four features) is fed back, rounded to the operand type, as the
+//     B operand of the next layer; the weight operand is read from LDS with
+//     its k columns permuted to the same order.  h1 never leaves registers for
+//     layer 2, nor dz2 for the dh1 = W2^T dz2 product.
+//   * The weight gradients reduce over samples (K = batch); their operands are
+//     written to LDS transposed ([feature][sample], padded rows) once, and the
+//     products dW2 = dz2^T h1 and dW1 = dz1^T s run from LDS.  Bias gradients
+//     and dw3 are row sums of the same LDS tiles.
+//   * W1, W2 and W2^T come from operand-typed shadows written by the Adam
+//     kernel, so no conversion or transpose happens in the hot kernel.
+//   * Gradients leave the workgroup as fp32 partials; a second kernel sums
+//     them in workgroup order (no float atomics: bitwise reproducible) and a
+//     third applies the clip and Adam and refreshes the shadows.
+#include <hip/hip_ext.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace iqlh {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- operands
+template <typename T> struct Op;
+
+template <> struct Op<uint16_t> {  // bfloat16 storage
+    static constexpr int KS = 16;   // k per MFMA
+    static constexpr int KPL = 8;   // k per lane (lane half h holds 8h .. 8h+7)
+    static constexpr int PAD = 8;   // LDS row padding, elements (16 bytes)
+    typedef bf16x8 frag;
+    static IQLH_DEV f32x16 mma(frag a, frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    static IQLH_DEV frag zero() { return __builtin_bit_cast(frag, u32x4{0u, 0u, 0u, 0u}); }
+    // KPL consecutive elements (16-byte aligned)
+    static IQLH_DEV frag load(const uint16_t* p) {
+        return __builtin_bit_cast(frag, *(const u32x4*)p);
+    }
+    // chained-k fragment of k step u for lane half h: two runs of four
+    static IQLH_DEV frag load_chain(const uint16_t* row, int u, int h) {
+        const int c0 = 16 * u + 4 * h;
+        const u32x2 lo = *(const u32x2*)(row + c0);
+        const u32x2 hi = *(const u32x2*)(row + c0 + 8);
+        return __builtin_bit_cast(frag, u32x4{lo.x, lo.y, hi.x, hi.y});
+    }
+    // B operand of k step u from a layer's accumulators
+    template <int NT>
+    static IQLH_DEV frag from_acc(const f32x16 (&acc)[NT], int u) {
+        const f32x16& a = acc[u >> 1];
+        const int r = 8 * (u & 1);
+        return __builtin_bit_cast(frag, u32x4{pack_bf2(a[r + 0], a[r + 1]), pack_bf2(a[r + 2], a[r + 3]),
+                                             pack_bf2(a[r + 4], a[r + 5]), pack_bf2(a[r + 6], a[r + 7])});
+    }
+    static IQLH_DEV frag make(const uint16_t* t) {
+        return __builtin_bit_cast(frag, u32x4{(uint32_t)t[0] | ((uint32_t)t[1] << 16),
+                                             (uint32_t)t[2] | ((uint32_t)t[3] << 16),
+                                             (uint32_t)t[4] | ((uint32_t)t[5] << 16),
+                                             (uint32_t)t[6] | ((uint32_t)t[7] << 16)});
+    }
+    static IQLH_DEV uint16_t cvt(float x) { return f2bf(x); }
+    static IQLH_DEV float tof(uint16_t x) { return bf2f(x); }
+    static IQLH_DEV void elems(frag f, float* out) {
+        const u32x4 u = __builtin_bit_cast(u32x4, f);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = bf2f((uint16_t)(u[i] & 0xFFFFu));
+            out[2 * i + 1] = bf2f((uint16_t)(u[i] >> 16));
+        }
+    }
+    static IQLH_DEV bool chain_positive(frag f, int e) {
+        const u32x4 u = __builtin_bit_cast(u32x4, f);
+        const uint32_t w = u[e >> 1];
+        const uint16_t b = (e & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xFFFFu);
+        return b != 0;  // relu outputs are +0 or positive
+    }
+};
+
+template <> struct Op<float> {
+    static constexpr int KS = 2;
+    static constexpr int KPL = 1;
+    static constexpr int PAD = 4;
+    typedef float frag;
+    static IQLH_DEV f32x16 mma(frag a, frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+    static IQLH_DEV frag zero() { return 0.f; }
+    static IQLH_DEV frag load(const float* p) { return *p; }
+    static IQLH_DEV frag load_chain(const float* row, int u, int h) {
+        return row[32 * (u >> 4) + 8 * ((u & 15) >> 2) + 4 * h + (u & 3)];
+    }
+    template <int NT>
+    static IQLH_DEV frag from_acc(const f32x16 (&acc)[NT], int u) {
+        return acc[u >> 4][u & 15];
+    }
+    static IQLH_DEV frag make(const float* t) { return t[0]; }
+    static IQLH_DEV float cvt(float x) { return x; }
+    static IQLH_DEV float tof(float x) { return x; }
+    static IQLH_DEV void elems(frag f, float* out) { out[0] = f; }
+    static IQLH_DEV bool chain_positive(frag f, int) { return f > 0.f; }
+};
+
+// Parameter offsets inside one group's flat vector.
+struct POff {
+    int64_t w1, b1, w2, b2, w3, b3;
+    IQLH_DEV POff(int S, int H) {
+        w1 = 0; b1 = (int64_t)H * S; w2 = b1 + H; b2 = w2 + (int64_t)H * H; w3 = b2 + H; b3 = w3 + H;
+    }
+};
+
+struct FusedArgs {
+    const void* states;
+    int64_t ld;
+    const float* q;
+    const float* params;  // [G][P] fp32 master (biases, w3)
+    const void* w1s;      // [G][H][SP]
+    const void* w2s;      // [G][H][H]
+    const void* w2ts;     // [G][H][H]
+    float* part;          // [G][nwg][P]
+    float* loss_part;     // [G][nwg]
+    float* out_v;         // [G][B] or null
+    float tau0, tau1, invB;
+    int B, S, nwg;
+    int64_t P;
+    int32_t* flags;
+};
+
+template <typename T, int SP, int H, int NW>
+struct FusedCfg {
+    static constexpr int BT = 32 * NW;
+    static constexpr int NT = H / 32;
+    static constexpr int PAD = Op<T>::PAD;
+    static constexpr int LDA = BT + PAD;       // activation tiles [rows][LDA]
+    static constexpr int LDW1 = SP + PAD;      // W1 [H][LDW1]
+    static constexpr int LDW2 = H + PAD;       // W2, W2^T [H][LDW2]
+    static constexpr int R0 = (H * LDW1 > H * LDA) ? H * LDW1 : H * LDA;
+    static constexpr int R1 = H * LDW2;
+    static constexpr int R2 = H * LDA;
+    static constexpr int R3 = (SP * LDA > H * LDA) ? SP * LDA : H * LDA;
+    static constexpr size_t BYTES_T = (size_t)(R0 + R1 + R2 + R3) * sizeof(T);
+    static constexpr size_t BYTES = BYTES_T + (size_t)(3 * H + 2 * NW) * sizeof(float);
+    static_assert(SP % 32 == 0 && H % 32 == 0, "tile shape");
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+};
+
+// Row sums of a [rows][ld] LDS tile over its first BT columns, into dst[row].
+template <typename T, int BT, int NTHR>
+IQLH_DEV void row_sums(const T* tile, int rows, int ld, float* dst) {
+    for (int r = threadIdx.x; r < rows; r += NTHR) {
+        const T* p = tile + (int64_t)r * ld;
+        float s = 0.f;
+        for (int c = 0; c < BT; c += Op<T>::KPL) {
+            float e[Op<T>::KPL];
+            Op<T>::elems(Op<T>::load(p + c), e);
+#pragma unroll
+            for (int i = 0; i < Op<T>::KPL; ++i) s += e[i];
+        }
+        dst[r] = s;
+    }
+}
+
+// out[i][j] += sum_k A[i][k] * B[j][k] over K = BT columns of two LDS tiles,
+// for 32x32 output tiles [t0, t1) (row-major over NCT column tiles); stores
+// fp32 results to dst[i * ldo + j] for j < ncols.
+template <typename T, int BT, int MAXT>
+IQLH_DEV void lds_gemm_store(const T* A, const T* Bm, int lda, int NCT, int t0, int t1,
+                             float* dst, int ldo, int ncols) {
+    typedef Op<T> O;
+    const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
+    for (int tb = t0; tb < t1; tb += MAXT) {
+        const int nb = min(MAXT, t1 - tb);
+        f32x16 acc[MAXT];
+#pragma unroll
+        for (int q = 0; q < MAXT; ++q) acc[q] = f32x16{};
+        for (int u = 0; u < BT / O::KS; ++u) {
+            const int k0 = O::KS * u + O::KPL * h;
+            int last_row = -1;
+            typename O::frag a = O::zero();
+#pragma unroll
+            for (int q = 0; q < MAXT; ++q) {
+                if (q < nb) {
+                    const int tau = tb + q, rt = tau / NCT, ct = tau - rt * NCT;
+                    if (rt != last_row) {
+                        a = O::load(A + (int64_t)(32 * rt + l32) * lda + k0);
+                        last_row = rt;
+                    }
+                    const typename O::frag b = O::load(Bm + (int64_t)(32 * ct + l32) * lda + k0);
+                    acc[q] = O::mma(a, b, acc[q]);
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < MAXT; ++q) {
+            if (q < nb) {
+                const int tau = tb + q, rt = tau / NCT, ct = tau - rt * NCT;
+                const int j = 32 * ct + l32;
+                if (j < ncols) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int i = 32 * rt + 8 * (r >> 2) + 4 * h + (r & 3);
+                        dst[(int64_t)i * ldo + j] = acc[q][r];
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <typename T, int SP, int H, int NW>
+__global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
+    typedef Op<T> O;
+    typedef FusedCfg<T, SP, H, NW> C;
+    constexpr int BT = C::BT, NT = C::NT, NTHR = 64 * NW;
+    constexpr int KU1 = SP / O::KS;   // k steps of layer 1
+    constexpr int KUH = H / O::KS;    // k steps over hidden
+    extern __shared__ __align__(16) unsigned char smem[];
+    T* R0 = (T*)smem;
+    T* R1 = R0 + C::R0;
+    T* R2 = R1 + C::R1;
+    T* R3 = R2 + C::R2;
+    float* sb1 = (float*)(R3 + C::R3);
+    float* sb2 = sb1 + H;
+    float* sw3 = sb2 + H;
+    float* sred = sw3 + H;  // [2][NW]
+
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5, wv = tid >> 6;
+    const int g = blockIdx.y, wg = blockIdx.x;
+    const int S = a.S, B = a.B;
+    const POff po(S, H);
+    const float* prm = a.params + (int64_t)g * a.P;
+    const T* w1s = (const T*)a.w1s + (int64_t)g * H * SP;
+    const T* w2s = (const T*)a.w2s + (int64_t)g * H * H;
+    const T* w2ts = (const T*)a.w2ts + (int64_t)g * H * H;
+    float* part = a.part + ((int64_t)g * a.nwg + wg) * a.P;
+    const float tau = g == 0 ? a.tau0 : a.tau1;
+
+    // ---- S0: weights to LDS, biases and w3 to LDS, X fragments to registers
+    for (int idx = tid * O::KPL; idx < H * SP; idx += NTHR * O::KPL) {
+        const int r = idx / SP, c = idx - r * SP;
+        *(typename O::frag*)(R0 + r * C::LDW1 + c) = O::load(w1s + idx);
+    }
+    for (int idx = tid * O::KPL; idx < H * H; idx += NTHR * O::KPL) {
+        const int r = idx / H, c = idx - r * H;
+        *(typename O::frag*)(R1 + r * C::LDW2 + c) = O::load(w2s + idx);
+    }
+    for (int i = tid; i < H; i += NTHR) {
+        sb1[i] = prm[po.b1 + i];
+        sb2[i] = prm[po.b2 + i];
+        sw3[i] = prm[po.w3 + i];
+    }
+    const int bl = 32 * wv + l32;              // sample within the tile
+    const int b = wg * BT + bl;                // sample in the batch
+    const bool valid = b < B;
+    typename O::frag xf[KU1];
+    {
+        const T* xr = (const T*)a.states + (int64_t)b * a.ld;
+        const bool vec = (S == SP) && ((a.ld % O::KPL) == 0);
+#pragma unroll
+        for (int u = 0; u < KU1; ++u) {
+            const int k0 = O::KS * u + O::KPL * h;
+            if (valid && vec) {
+                xf[u] = O::load(xr + k0);
+            } else {
+                T tmp[O::KPL];
+#pragma unroll
+                for (int e = 0; e < O::KPL; ++e) {
+                    const int k = k0 + e;
+                    tmp[e] = (valid && k < S) ? xr[k] : (T)0;
+                }
+                xf[u] = O::make(tmp);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- F1: z1^T = W1 * s^T
+    f32x16 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
+#pragma unroll
+    for (int u = 0; u < KU1; ++u) {
+        const int k0 = O::KS * u + O::KPL * h;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            acc[t] = O::mma(O::load(R0 + (32 * t + l32) * C::LDW1 + k0), xf[u], acc[t]);
+    }
+    // epilogue: h1 = relu(z1 + b1); h1^T tile to R3
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int f = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+            const float z = acc[t][r] + sb1[f];
+            const float y = z > 0.f ? z : 0.f;
+            acc[t][r] = y;
+            R3[f * C::LDA + bl] = O::cvt(y);
+        }
+    }
+    typename O::frag h1f[KUH];
+#pragma unroll
+    for (int u = 0; u < KUH; ++u) h1f[u] = O::template from_acc<NT>(acc, u);
+    __syncthreads();
+
+    // ---- F2: z2^T = W2 * h1^T  (A read with the chained k order)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
+#pragma unroll
+    for (int u = 0; u < KUH; ++u) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            acc[t] = O::mma(O::load_chain(R1 + (32 * t + l32) * C::LDW2, u, h), h1f[u], acc[t]);
+    }
+    // epilogue: v, expectile, dv, dz2
+    float vpart = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int f = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+            const float z = acc[t][r] + sb2[f];
+            acc[t][r] = z;
+            vpart = fmaf(sw3[f], z > 0.f ? z : 0.f, vpart);
+        }
+    }
+    const float v = vpart + __shfl_xor(vpart, 32, 64) + prm[po.b3];
+    float dv = 0.f, lterm = 0.f;
+    if (valid) {
+        const float diff = a.q[b] - v;
+        const float w = diff >= 0.f ? tau : 1.f - tau;
+        lterm = w * diff * diff;
+        dv = -2.f * w * diff * a.invB;
+        if (h == 0 && a.out_v) a.out_v[(int64_t)g * B + b] = v;
+    }
+    {
+        const float ls = wave_sum(h == 0 ? lterm : 0.f);
+        const float ds = wave_sum(h == 0 ? dv : 0.f);
+        if (lane == 0) { sred[wv] = ls; sred[NW + wv] = ds; }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int f = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+            const float z = acc[t][r];
+            const float hv = z > 0.f ? z : 0.f;
+            const float dz = z > 0.f ? dv * sw3[f] : 0.f;
+            acc[t][r] = dz;
+            R0[f * C::LDA + bl] = O::cvt(dz);        // dz2^T
+            R2[f * C::LDA + bl] = O::cvt(hv * dv);   // h2 * dv, row sums give dw3
+        }
+    }
+    typename O::frag dz2f[KUH];
+#pragma unroll
+    for (int u = 0; u < KUH; ++u) dz2f[u] = O::template from_acc<NT>(acc, u);
+    __syncthreads();
+
+    // ---- row sums (db2, dw3, db3, loss) and dW2 = dz2^T h1
+    row_sums<T, BT, NTHR>(R0, H, C::LDA, part + po.b2);
+    row_sums<T, BT, NTHR>(R2, H, C::LDA, part + po.w3);
+    if (tid == 0) {
+        float ls = 0.f, ds = 0.f;
+        for (int i = 0; i < NW; ++i) { ls += sred[i]; ds += sred[NW + i]; }
+        a.loss_part[(int64_t)g * a.nwg + wg] = ls;
+        part[po.b3] = ds;
+    }
+    // W2^T shadow into R1 (W2 is no longer read after F2)
+    for (int idx = tid * O::KPL; idx < H * H; idx += NTHR * O::KPL) {
+        const int r = idx / H, c = idx - r * H;
+        *(typename O::frag*)(R1 + r * C::LDW2 + c) = O::load(w2ts + idx);
+    }
+    {
+        constexpr int T2 = NT * NT;
+        const int t0 = wv * T2 / NW, t1 = (wv + 1) * T2 / NW;
+        lds_gemm_store<T, BT, 4>(R0, R3, C::LDA, NT, t0, t1, part + po.w2, H, H);
+    }
+    __syncthreads();
+
+    // ---- s^T tile to R3 (h1^T no longer needed); B1: dh1^T = W2^T dz2^T
+#pragma unroll
+    for (int u = 0; u < KU1; ++u) {
+        float e[O::KPL];
+        O::elems(xf[u], e);
+#pragma unroll
+        for (int i = 0; i < O::KPL; ++i) R3[(O::KS * u + O::KPL * h + i) * C::LDA + bl] = O::cvt(e[i]);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
+#pragma unroll
+    for (int u = 0; u < KUH; ++u) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            acc[t] = O::mma(O::load_chain(R1 + (32 * t + l32) * C::LDW2, u, h), dz2f[u], acc[t]);
+    }
+    // dz1 = dh1 * relu'(z1) (mask from the rounded h1 operands), dz1^T to R2
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int f = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+            // register (t, r) sits in chained k step u = (16 t + r) / KPLH
+            bool pos;
+            if constexpr (O::KPL == 8) pos = O::chain_positive(h1f[2 * t + (r >> 3)], r & 7);
+            else pos = O::chain_positive(h1f[16 * t + r], 0);
+            const float dz = pos ? acc[t][r] : 0.f;
+            R2[f * C::LDA + bl] = O::cvt(dz);
+        }
+    }
+    __syncthreads();
+
+    // ---- db1 and dW1 = dz1^T s
+    row_sums<T, BT, NTHR>(R2, H, C::LDA, part + po.b1);
+    {
+        constexpr int NCT = SP / 32;
+        constexpr int T3 = NT * NCT;
+        const int t0 = wv * T3 / NW, t1 = (wv + 1) * T3 / NW;
+        lds_gemm_store<T, BT, 4>(R2, R3, C::LDA, NCT, t0, t1, part + po.w1, S, S);
+    }
+}
+
+// Sums the per-workgroup partials of every parameter in workgroup order,
+// writes grad, per-block sums of squares, the mean loss, and advances t and
+// the step counter.
+__global__ __launch_bounds__(256) void iql_reduce_kernel(const float* __restrict__ part,
+                                                         const float* __restrict__ loss_part,
+                                                         int nwg, int64_t P, float invB,
+                                                         float* __restrict__ grad,
+                                                         float* __restrict__ sq_part, int rb,
+                                                         int32_t* __restrict__ tcount,
+                                                         int64_t* __restrict__ step,
+                                                         float* __restrict__ out_loss,
+                                                         int32_t* __restrict__ flags) {
+    __shared__ float red[4];
+    const int g = blockIdx.y;
+    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    float s = 0.f;
+    if (p < P) {
+        const float* src = part + (int64_t)g * nwg * P + p;
+        for (int w = 0; w < nwg; ++w) s += src[(int64_t)w * P];
+        grad[(int64_t)g * P + p] = s;
+    }
+    const float sq = block_sum<256>(s * s, red);
+    if (threadIdx.x == 0) sq_part[(int64_t)g * rb + blockIdx.x] = sq;
+    if (blockIdx.x == 0) {
+        float l = 0.f;
+        for (int w = threadIdx.x; w < nwg; w += 256) l += loss_part[(int64_t)g * nwg + w];
+        l = block_sum<256>(l, red);
+        if (threadIdx.x == 0) {
+            const float loss = l * invB;
+            if (out_loss) out_loss[g] = loss;
+            if (!isfinite(loss)) set_flag(flags, 0x4);
+            tcount[g] += 1;
+            if (g == 0) *step += 1;
+        }
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void iql_adam_kernel(IqlDims d, IqlBuffers b, AdamHyper hp,
+                                                       float* __restrict__ out_gnorm, int rb) {
+    __shared__ float red[4];
+    const int g = blockIdx.y;
+    const int64_t P = d.P;
+    float a = 0.f;
+    for (int i = threadIdx.x; i < rb; i += 256) a += b.sq_part[(int64_t)g * rb + i];
+    const float nrm = sqrtf(block_sum<256>(a, red));
+    if (blockIdx.x == 0 && threadIdx.x == 0 && out_gnorm) out_gnorm[g] = nrm;
+    const float c = !isfinite(nrm) ? __int_as_float(0x7FC00000)
+                                   : ((nrm > hp.max_grad_norm && nrm > 0.f) ? hp.max_grad_norm / nrm : 1.f);
+    const float tt = (float)b.t[g];
+    const float bc1 = 1.f - powf(hp.beta1, tt), bc2 = 1.f - powf(hp.beta2, tt);
+    const float decay = 1.f - hp.lr * hp.weight_decay;
+    const int H = d.H, S = d.S, SP = d.S_pad;
+    const int64_t ow2 = (int64_t)H * S + H, ow2e = ow2 + (int64_t)H * H;
+    float* prm = b.params + (int64_t)g * P;
+    float* gr = b.grad + (int64_t)g * P;
+    float* m = b.m + (int64_t)g * P;
+    float* v = b.v + (int64_t)g * P;
+    T* w1s = (T*)b.w1s + (int64_t)g * H * SP;
+    T* w2s = (T*)b.w2s + (int64_t)g * H * H;
+    T* w2ts = (T*)b.w2ts + (int64_t)g * H * H;
+    bool bad = false;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < P; i += (int64_t)gridDim.x * 256) {
+        const float gi = gr[i] * c;
+        gr[i] = 0.f;
+        float p = prm[i];
+        if (isfinite(gi)) {
+            const float mi = hp.beta1 * m[i] + (1.f - hp.beta1) * gi;
+            const float vi = hp.beta2 * v[i] + (1.f - hp.beta2) * gi * gi;
+            const float mh = mi / bc1, vh = vi / bc2;
+            if (hp.weight_decay != 0.f) p *= decay;
+            p -= hp.lr * mh / (sqrtf(vh) + hp.eps);
+            if (hp.clamp > 0.f) p = fminf(fmaxf(p, -hp.clamp), hp.clamp);
+            prm[i] = p;
+            m[i] = mi;
+            v[i] = vi;
+        } else {
+            bad = true;
+        }
+        if (i < (int64_t)H * S) {
+            const int64_t r = i / S, cc = i - r * S;
+            w1s[r * SP + cc] = Op<T>::cvt(p);
+        } else if (i >= ow2 && i < ow2e) {
+            const int64_t q = i - ow2, r = q / H, cc = q - r * H;
+            w2s[q] = Op<T>::cvt(p);
+            w2ts[cc * H + r] = Op<T>::cvt(p);
+        }
+    }
+    if (bad) set_flag(b.flags, 0x1);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void iql_shadow_kernel(IqlDims d, IqlBuffers b) {
+    const int g = blockIdx.y, H = d.H, S = d.S, SP = d.S_pad;
+    const float* prm = b.params + (int64_t)g * d.P;
+    T* w1s = (T*)b.w1s + (int64_t)g * H * SP;
+    T* w2s = (T*)b.w2s + (int64_t)g * H * H;
+    T* w2ts = (T*)b.w2ts + (int64_t)g * H * H;
+    const int64_t ow2 = (int64_t)H * S + H;
+    const int64_t n1 = (int64_t)H * SP, n2 = (int64_t)H * H;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n1 + n2; i += (int64_t)gridDim.x * 256) {
+        if (i < n1) {
+            const int64_t r = i / SP, c = i - r * SP;
+            w1s[i] = Op<T>::cvt(c < S ? prm[r * S + c] : 0.f);
+        } else {
+            const int64_t q = i - n1, r = q / H, c = q - r * H;
+            const float p = prm[ow2 + q];
+            w2s[q] = Op<T>::cvt(p);
+            w2ts[c * H + r] = Op<T>::cvt(p);
+        }
+    }
+}
+
+// ------------------------------------------------------------- dispatch
+template <typename T, int SP, int H, int NW>
+static hipError_t run_fused(const FusedArgs& fa, int G, hipStream_t stream, hipEvent_t ev0,
+                            hipEvent_t ev1) {
+    typedef FusedCfg<T, SP, H, NW> C;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)iql_fused_kernel<T, SP, H, NW>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::BYTES);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    if (ev0)  // events recorded by the dispatch itself: kernel time only
+        hipExtLaunchKernelGGL((iql_fused_kernel<T, SP, H, NW>), dim3(fa.nwg, G), dim3(64 * NW),
+                              C::BYTES, stream, ev0, ev1, 0, fa);
+    else
+        hipLaunchKernelGGL((iql_fused_kernel<T, SP, H, NW>), dim3(fa.nwg, G), dim3(64 * NW), C::BYTES,
+                           stream, fa);
+    return hipGetLastError();
+}
+
+struct Variant {
+    int dtype, SP, H, NW;
+    hipError_t (*fn)(const FusedArgs&, int, hipStream_t, hipEvent_t, hipEvent_t);
+};
+static const Variant kVariants[] = {
+    {1, 128, 128, 4, &run_fused<uint16_t, 128, 128, 4>},
+    {1, 64, 128, 4, &run_fused<uint16_t, 64, 128, 4>},
+    {1, 32, 32, 4, &run_fused<uint16_t, 32, 32, 4>},
+    {0, 32, 32, 4, &run_fused<float, 32, 32, 4>},
+    {0, 64, 128, 1, &run_fused<float, 64, 128, 1>},
+};
+
+static const Variant* pick(int dtype, int S, int H) {
+    const Variant* best = nullptr;
+    for (const Variant& v : kVariants)
+        if (v.dtype == dtype && v.H == H && S <= v.SP && (!best || v.SP < best->SP)) best = &v;
+    return best;
+}
+
+bool iql_supported(int dtype, int S, int H) { return pick(dtype, S, H) != nullptr; }
+int iql_tile_samples(int dtype, int S, int H) {
+    const Variant* v = pick(dtype, S, H);
+    return v ? 32 * v->NW : 0;
+}
+int iql_s_pad(int dtype, int S, int H) {
+    const Variant* v = pick(dtype, S, H);
+    return v ? v->SP : 0;
+}
+int iql_reduce_blocks(int64_t P) { return (int)((P + 255) / 256); }
+
+hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float* tau,
+                              const void* states, int64_t ld, const float* q, int B, float* out_v,
+                              hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    const Variant* var = pick(d.dtype, d.S, d.H);
+    if (!var) return hipErrorInvalidValue;
+    const int BT = 32 * var->NW;
+    FusedArgs fa;
+    fa.states = states; fa.ld = ld; fa.q = q; fa.params = b.params;
+    fa.w1s = b.w1s; fa.w2s = b.w2s; fa.w2ts = b.w2ts;
+    fa.part = b.part; fa.loss_part = b.loss_part; fa.out_v = out_v;
+    fa.tau0 = tau[0]; fa.tau1 = tau[d.G > 1 ? 1 : 0]; fa.invB = 1.f / (float)B;
+    fa.B = B; fa.S = d.S; fa.nwg = (B + BT - 1) / BT; fa.P = d.P; fa.flags = b.flags;
+    return var->fn(fa, d.G, stream, ev0, ev1);
+}
+
+hipError_t launch_iql_update(const IqlDims& d, const IqlBuffers& b, const AdamHyper& hp, int B,
+                             float* out_loss, float* out_gnorm, hipStream_t stream) {
+    const Variant* var = pick(d.dtype, d.S, d.H);
+    if (!var) return hipErrorInvalidValue;
+    const int BT = 32 * var->NW;
+    const int nwg = (B + BT - 1) / BT;
+    const int rb = iql_reduce_blocks(d.P);
+    hipLaunchKernelGGL(iql_reduce_kernel, dim3(rb, d.G), dim3(256), 0, stream, b.part, b.loss_part,
+                       nwg, d.P, 1.f / (float)B, b.grad, b.sq_part, rb, b.t, b.step, out_loss, b.flags);
+    const int64_t abn = (d.P + 255) / 256;
+    const int ab = (int)(abn < 512 ? abn : 512);
+    if (d.dtype == 1)
+        hipLaunchKernelGGL(iql_adam_kernel<uint16_t>, dim3(ab, d.G), dim3(256), 0, stream, d, b, hp,
+                           out_gnorm, rb);
+    else
+        hipLaunchKernelGGL(iql_adam_kernel<float>, dim3(ab, d.G), dim3(256), 0, stream, d, b, hp,
+                           out_gnorm, rb);
+    return hipGetLastError();
+}
+
+hipError_t launch_iql_refresh_shadows(const IqlDims& d, const IqlBuffers& b, hipStream_t stream) {
+    const int64_t n = (int64_t)d.H * d.S_pad + (int64_t)d.H * d.H;
+    const int64_t bn = (n + 255) / 256;
+    const int blocks = (int)(bn < 1024 ? bn : 1024);
+    if (d.dtype == 1)
+        hipLaunchKernelGGL(iql_shadow_kernel<uint16_t>, dim3(blocks, d.G), dim3(256), 0, stream, d, b);
+    else
+        hipLaunchKernelGGL(iql_shadow_kernel<float>, dim3(blocks, d.G), dim3(256), 0, stream, d, b);
+    return hipGetLastError();
+}
+
+}  // namespace iqlh

@@ -1,0 +1,100 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace iqlh {
+
+// ------------------------------------------------------------------- HER
+struct HerArgs {
+    const float* states;
+    const float* next_states;
+    const int32_t* actions;
+    const float* dones;
+    const int32_t* episode_ends;
+    const int32_t* source_idx;
+    const int64_t* d_step;
+    int32_t* donor_out;
+    void* out_states;
+    float* out_next_states;
+    int32_t* out_actions;
+    float* out_rewards;
+    float* out_dones;
+    int32_t* flags;
+    int64_t buffer_size;
+    int64_t out_ld;
+    uint64_t seed;
+    int32_t num_episodes;
+    int32_t n;
+    int32_t S, G, strategy, out_bf16;
+    float threshold, reward_hit, reward_miss;
+};
+hipError_t launch_her_relabel(const HerArgs& a, hipStream_t stream);
+
+// ------------------------------------------------------------- AW policy
+hipError_t launch_aw_policy(const float* q, const float* v, int G, int B, int A, float beta,
+                            float* pi, hipStream_t stream);
+
+// ---------------------------------------------------- gradient budget
+constexpr int kMaxSources = 8;
+struct SourceSet {
+    const float* ptr[kMaxSources];
+    float frac[kMaxSources];
+    float alpha[kMaxSources];
+    int32_t k;
+};
+struct AdamHyper {
+    float lr, beta1, beta2, eps, weight_decay, max_grad_norm, clamp;
+};
+int budget_num_blocks(int64_t n);
+// workspace floats: k * nb (source partials) + nb (combined partials)
+hipError_t launch_budget(float* grad, const SourceSet& s, int64_t n, float mgn,
+                         float* out_norms, float* params, float* m, float* v, int32_t* t,
+                         int32_t* flags, const AdamHyper* hp, float* work, hipStream_t stream);
+
+// Flat clipped Adam over n elements whose gradient L2 norm is the fixed-order
+// sum of `nb` partial sums of squares.  Zeroes grad.  `t` was already
+// incremented.  out_norm (nullable) receives the pre-clip norm.
+hipError_t launch_adam_flat(float* params, float* grad, float* m, float* v, const int32_t* t,
+                            const float* sq_partials, int nb, int64_t n, const AdamHyper& hp,
+                            float* out_norm, int32_t* flags, hipStream_t stream);
+
+// ------------------------------------------------------------------ IQL
+struct IqlDims {
+    int S, H, G, dtype;  // dtype: 0 f32, 1 bf16
+    int S_pad;           // columns of the W1 shadow (multiple of 32)
+    int64_t P;           // parameters per group
+};
+// Per-group device buffers, group stride = P (or the shadow sizes).
+struct IqlBuffers {
+    float* params;    // [G][P] fp32 master
+    float* m;         // [G][P]
+    float* v;         // [G][P]
+    float* grad;      // [G][P]
+    int32_t* t;       // [G]
+    int64_t* step;    // [1]
+    int32_t* flags;   // [1]
+    void* w1s;        // [G][H][S_pad]   operand-typed shadow of W1 (zero padded)
+    void* w2s;        // [G][H][H]       shadow of W2
+    void* w2ts;       // [G][H][H]       shadow of W2 transposed
+    float* part;      // [G][max_wg][P]  per-workgroup gradient partials
+    float* loss_part; // [G][max_wg]
+    float* sq_part;   // [G][max_rb]     per-block sums of squares of grad
+    int max_wg;
+    int max_rb;
+};
+bool iql_supported(int dtype, int S, int H);
+int iql_tile_samples(int dtype, int S, int H);
+int iql_reduce_blocks(int64_t P);
+// Fused forward/backward: V(s) and the per-workgroup gradient partials.
+hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float* tau,
+                              const void* states, int64_t ld, const float* q, int B,
+                              float* out_v, hipStream_t stream, hipEvent_t ev0 = nullptr,
+                              hipEvent_t ev1 = nullptr);
+// Fixed-order reduction of the partials of a batch of B rows, clip, Adam.
+hipError_t launch_iql_update(const IqlDims& d, const IqlBuffers& b, const AdamHyper& hp, int B,
+                             float* out_loss, float* out_gnorm, hipStream_t stream);
+int iql_s_pad(int dtype, int S, int H);
+hipError_t launch_iql_refresh_shadows(const IqlDims& d, const IqlBuffers& b, hipStream_t stream);
+
+}  // namespace iqlh

@@ -1,0 +1,237 @@
+"""GPU parity of iql_train_step (fused value-MLP forward/backward, reduction,
+clipped Adam) against the fp64 oracle.
+
+Tolerances: 1e-4 relative for the fp32 operand path and 2e-2 for bf16
+operands (fp32 accumulate), per tensor, norm-wise and max-wise.  Multi-step
+runs are checked per step from the GPU's own state ("teacher forced"), where
+the bound applies to one step's arithmetic; the free-running trajectory is
+checked at the drift a correct float32 implementation shows against fp64
+(Adam amplifies rounding on near-zero gradients: about 2e-4 norm-wise on the
+parameters after 100 steps), i.e. 1e-3 on parameters and 1e-4 on the loss.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import iql
+from tests.gpu_util import adam_update_close, assert_rel, assert_scalar_rel, dev, host, sync, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def m():
+    import offline_rl_step_amd as m
+    return m
+
+
+class Setup:
+    def __init__(self, m, w, B=None, seed=0, ld=None, taus=None):
+        import torch
+        self.m, self.w = m, w
+        self.B = B or w.B
+        self.S, self.H, self.G = w.S, w.H, w.groups
+        self.ld = ld or w.S
+        self.taus = taus or w.taus
+        self.bf16 = w.dtype == "bf16"
+        g = np.random.default_rng(seed)
+        X = g.standard_normal((self.B, self.S)).astype(np.float32)
+        if self.bf16:
+            X = synth._bf16_values(X)
+        self.X = X
+        self.q = (g.standard_normal(self.B) * w.q_sd).astype(np.float32)
+        self.inits = synth.group_inits(w, seed=synth.DEFAULT_SEED + 10 + seed)
+        self.hp = iql.AdamHP(lr=w.lr, max_grad_norm=w.max_grad_norm)
+        self.P = iql.num_params(self.S, self.H, self.H)
+        self.cfg = m.make_config(self.S, self.H, self.B, num_groups=self.G,
+                                 compute_dtype=m.BF16 if self.bf16 else m.F32, states_ld=self.ld,
+                                 tau=self.taus, lr=w.lr, max_grad_norm=w.max_grad_norm)
+        self.tr = m.IqlTrainer(self.cfg, np.concatenate(self.inits))
+        Xp = np.zeros((self.B, self.ld), np.float32)
+        Xp[:, :self.S] = X
+        self.tX = to_dev(Xp, torch.bfloat16 if self.bf16 else torch.float32)
+        self.tq = to_dev(self.q)
+        self.out_v = torch.zeros((self.G, self.B), dtype=torch.float32, device=dev())
+        self.out_loss = torch.zeros(self.G, dtype=torch.float32, device=dev())
+        self.out_gn = torch.zeros(self.G, dtype=torch.float32, device=dev())
+        self.oracle = [iql.AdamState.fresh(p) for p in self.inits]
+
+    def gpu_step(self):
+        self.tr.train_step(self.tX, self.tq, self.B, self.out_v, self.out_loss, self.out_gn)
+
+    def oracle_step(self, states=None):
+        sts = self.oracle if states is None else states
+        return [iql.train_step(sts[g], self.X, self.q, self.S, self.H, self.H, self.taus[g], self.hp)
+                for g in range(self.G)]
+
+    def state(self, g):
+        import torch
+        p = torch.zeros(self.P, dtype=torch.float32, device=dev())
+        mm, vv = torch.zeros_like(p), torch.zeros_like(p)
+        t = torch.zeros(1, dtype=torch.int32, device=dev())
+        self.tr.get_state(g, p, mm, vv, t)
+        sync()
+        st = iql.AdamState(host(p).astype(np.float64), host(mm).astype(np.float64),
+                           host(vv).astype(np.float64), int(t.item()))
+        return st
+
+    def compare_step(self, refs, before, rtol, steps_since_init, what=""):
+        for g in range(self.G):
+            r = refs[g]
+            assert_rel(host(self.out_v[g]), r.v, rtol, f"{what} V g{g}")
+            assert_scalar_rel(host(self.out_loss)[g], r.loss, rtol, f"{what} loss g{g}")
+            assert_scalar_rel(host(self.out_gn)[g], r.grad_norm, rtol, f"{what} grad norm g{g}")
+            st = self.state(g)
+            o = before[g]
+            assert st.t == o.t
+            assert_rel(st.m, o.m, rtol, f"{what} Adam m g{g}")
+            assert_rel(st.v, o.v, 2 * rtol, f"{what} Adam v g{g}")
+            adam_update_close(st.params, o.params, None, self.hp.lr, 1, rtol, f"{what} params g{g}")
+
+
+def _one_step(m, w, rtol, **kw):
+    s = Setup(m, w, **kw)
+    s.gpu_step()
+    sync()
+    refs = s.oracle_step()
+    s.compare_step(refs, s.oracle, rtol, 1, w.name)
+    rc, flags = s.tr.status()
+    assert rc == m.OK and flags == 0
+    return s
+
+
+def test_tiny_fp32_one_step(m):
+    _one_step(m, synth.WORKLOADS["tiny_b256_s16_h32"], 1e-4)
+
+
+def test_tiny_fp32_ragged_batch(m):
+    _one_step(m, synth.WORKLOADS["tiny_b256_s16_h32"], 1e-4, B=203)
+
+
+def test_b4096_s42_fp32_one_step_padded_ld(m):
+    _one_step(m, synth.WORKLOADS["b4096_s42_h128_f32"], 1e-4, ld=45)
+
+
+def test_b4096_s42_fp32_hundred_steps(m):
+    w = synth.WORKLOADS["b4096_s42_h128_f32"]
+    s = Setup(m, w)
+    losses = []
+    for k in range(1, w.steps + 1):
+        if k in (10, 100):
+            before = [s.state(g) for g in range(s.G)]
+            s.gpu_step()
+            sync()
+            forced = [st.copy() for st in before]
+            refs = s.oracle_step(forced)
+            s.compare_step(refs, forced, 1e-4, k, f"teacher-forced step {k}")
+        else:
+            s.gpu_step()
+        sync()
+        losses.append(float(host(s.out_loss)[0]))
+        r = s.oracle_step()
+        assert_scalar_rel(losses[-1], r[0].loss, 1e-4, f"free-running loss step {k}")
+    st = s.state(0)
+    assert st.t == w.steps
+    # a float32 emulation of the same arithmetic ends 2.3e-4 (norm-wise) and at
+    # most 1.4e-3 absolute (about 4.8 lr) away from fp64 after 100 steps
+    d = st.params - s.oracle[0].params
+    assert np.linalg.norm(d) <= 1e-3 * np.linalg.norm(s.oracle[0].params), "free-running params"
+    assert np.max(np.abs(d)) <= 10 * w.lr, "free-running params beyond 10 lr"
+    assert losses[-1] < losses[0]
+
+
+@pytest.mark.parametrize("B", [16384, 1000])
+def test_b16384_bf16_two_groups_one_step(m, B):
+    _one_step(m, synth.WORKLOADS["b16384_s128_h128_bf16_g2"], 2e-2, B=B, taus=(0.7, 0.3))
+
+
+def test_bf16_small_shapes(m):
+    w = synth.shrink(synth.WORKLOADS["b16384_s128_h128_bf16_g2"], S=42, G=8)
+    _one_step(m, w, 2e-2, B=2000, ld=48)
+    w = synth.shrink(synth.WORKLOADS["tiny_b256_s16_h32"], dtype="bf16", groups=2, taus=(0.7, 0.9))
+    _one_step(m, w, 2e-2, B=300)
+
+
+def test_b16384_bf16_ten_steps(m):
+    w = synth.WORKLOADS["b16384_s128_h128_bf16_g2"]
+    s = Setup(m, w)
+    for k in range(1, 11):
+        if k == 10:
+            before = [s.state(g) for g in range(s.G)]
+        s.gpu_step()
+        sync()
+        if k == 10:
+            forced = [st.copy() for st in before]
+            refs = s.oracle_step(forced)
+            s.compare_step(refs, forced, 2e-2, k, "bf16 teacher-forced step 10")
+        r = s.oracle_step()
+        for g in range(s.G):
+            assert_scalar_rel(host(s.out_loss)[g], r[g].loss, 2e-2, f"bf16 loss step {k} g{g}")
+    for g in range(s.G):
+        assert_rel(s.state(g).params, s.oracle[g].params, 2e-2, f"bf16 params after 10 steps g{g}")
+
+
+def test_deterministic_and_checkpoint_resume(m):
+    import torch
+    w = synth.WORKLOADS["b16384_s128_h128_bf16_g2"]
+    a = Setup(m, w, B=4096)
+    b = Setup(m, w, B=4096)
+    for _ in range(5):
+        a.gpu_step()
+        b.gpu_step()
+    sync()
+    for g in range(2):
+        sa, sb = a.state(g), b.state(g)
+        assert np.array_equal(sa.params, sb.params) and np.array_equal(sa.m, sb.m)
+    assert np.array_equal(host(a.out_v), host(b.out_v))
+    # checkpoint a after 5 steps into a fresh trainer c; 5 more steps on both
+    c = Setup(m, w, B=4096)
+    for g in range(2):
+        P = a.P
+        bufs = [torch.zeros(P, dtype=torch.float32, device=dev()) for _ in range(3)]
+        t = torch.zeros(1, dtype=torch.int32, device=dev())
+        a.tr.get_state(g, bufs[0], bufs[1], bufs[2], t)
+        c.tr.set_state(g, bufs[0], bufs[1], bufs[2], t)
+    for _ in range(5):
+        a.gpu_step()
+        c.gpu_step()
+    sync()
+    for g in range(2):
+        sa, sc = a.state(g), c.state(g)
+        assert np.array_equal(sa.params, sc.params) and np.array_equal(sa.v, sc.v) and sa.t == sc.t == 10
+
+
+def test_nonfinite_target_skips_update(m):
+    w = synth.WORKLOADS["tiny_b256_s16_h32"]
+    s = Setup(m, w)
+    q = s.q.copy()
+    q[5] = np.nan
+    s.tq = to_dev(q)
+    s.gpu_step()
+    rc, flags = s.tr.status()
+    assert rc == m.ENONFINITE and flags & m.FLAG_NONFINITE_GRAD
+    st = s.state(0)
+    assert np.array_equal(st.params.astype(np.float32), s.inits[0]) and st.t == 1 and np.all(st.m == 0)
+
+
+def test_step_counter_drives_her_donors(m):
+    import torch
+    from oracle import her
+    w = synth.WORKLOADS["tiny_b256_s16_h32"]
+    s = Setup(m, w)
+    for _ in range(3):
+        s.gpu_step()
+    buf = synth.replay_buffer(w)
+    src = synth.her_sources(w, buf)
+    n = len(src)
+    d = dev()
+    X = torch.zeros((n, w.S), dtype=torch.float32, device=d)
+    rew = torch.zeros(n, dtype=torch.float32, device=d)
+    don = torch.zeros(n, dtype=torch.int32, device=d)
+    hb = m.her_buffer(to_dev(buf["states"]), to_dev(buf["next_states"]), to_dev(buf["actions"]),
+                      to_dev(buf["dones"]), to_dev(buf["episode_ends"]))
+    ho = m.her_out(X, m.F32, w.S, rew, donor_idx=don)
+    m.her_relabel(m.her_config(w.S, w.G, m.HER_FUTURE), hb, to_dev(src), n, 77, s.tr.step_counter, ho)
+    sync()
+    ref = her.her_step(buf, src, w.G, her.FUTURE, seed=77, step=3)
+    assert np.array_equal(host(don), ref["donor_idx"])
