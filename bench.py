@@ -40,7 +40,22 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--kernel-reps", type=int, default=200)
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="only run 10 plain device copies of MIB MiB (counter calibration) and exit")
     return p.parse_args()
+
+
+def copy_probe(mib):
+    """A plain copy kernel of known size: HBM counters of one dispatch should
+    read mib MiB and write mib MiB; the ratio calibrates FETCH_SIZE/WRITE_SIZE."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_mib": mib, "bytes_per_copy": n * 4}), flush=True)
 
 
 def fused_flops_per_launch(w):
@@ -170,6 +185,9 @@ def cpu_baseline(ctx, seconds, np):
 
 def main():
     a = parse()
+    if a.copy_probe:
+        copy_probe(a.copy_probe)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported by this build "
               "(the step has no cross-GPU exchange; see the sharding notes).", file=sys.stderr)

@@ -10,7 +10,7 @@
 #include <new>
 #include <vector>
 
-#include "../../include/iqlher.h"
+#include "iqlher.h"
 #include "launch.hpp"
 
 using namespace iqlh;
@@ -111,6 +111,7 @@ int iql_create(const iqlh_config* cfg, const float* init_params_host, iql_handle
     d.S = S; d.H = H; d.G = G; d.dtype = cfg->compute_dtype;
     d.S_pad = iql_s_pad(d.dtype, S, H);
     d.P = P;
+    d.Pp = (P + 127) / 128 * 128;
     const int BT = iql_tile_samples(d.dtype, S, H);
     const int max_wg = (cfg->max_batch + BT - 1) / BT;
     const int rb = iql_reduce_blocks(P);
@@ -129,7 +130,7 @@ int iql_create(const iqlh_config* cfg, const float* init_params_host, iql_handle
         {(void**)&b.w1s, esz * G * H * d.S_pad},
         {(void**)&b.w2s, esz * G * H * H},
         {(void**)&b.w2ts, esz * G * H * H},
-        {(void**)&b.part, sizeof(float) * G * (size_t)max_wg * P},
+        {(void**)&b.part, sizeof(float) * G * (size_t)max_wg * d.Pp},
         {(void**)&b.loss_part, sizeof(float) * G * (size_t)max_wg},
         {(void**)&b.sq_part, sizeof(float) * G * (size_t)rb},
     };

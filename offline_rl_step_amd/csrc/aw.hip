@@ -5,18 +5,19 @@
 // clamp to [-10, 10], scale by the temperature beta, softmax over actions with
 // the row maximum subtracted.
 //
-// HBM-bound.  A workgroup owns 256 consecutive rows: the [256, A] slab of Q is
-// read once with coalesced loads into LDS (padded to an odd row stride so the
-// per-row reads are bank-conflict free), every group's policy is computed from
-// that one copy, and each result slab is written back with coalesced stores.
+// HBM-bound.  A one-wave workgroup owns 64 consecutive rows (16384 rows give
+// 256 workgroups, one per CU): the [64, A] slab of Q is read once with
+// coalesced loads into LDS (padded to an odd row stride so the per-row reads
+// are bank-conflict free), every group's policy is computed from that one
+// copy, and each result slab is written back with coalesced stores.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace iqlh {
 
-constexpr int kAwRows = 256;
+constexpr int kAwRows = 64;
 
-__global__ __launch_bounds__(256) void aw_policy_kernel(const float* __restrict__ q,
+__global__ __launch_bounds__(kAwRows) void aw_policy_kernel(const float* __restrict__ q,
                                                          const float* __restrict__ v, int G, int B,
                                                          int A, float beta, float* __restrict__ pi) {
     extern __shared__ float lds[];
@@ -27,7 +28,7 @@ __global__ __launch_bounds__(256) void aw_policy_kernel(const float* __restrict_
     const int rows = (int)min<int64_t>(kAwRows, (int64_t)B - row0);
     const int cnt = rows * A;
     const float* qs = q + row0 * A;
-    for (int idx = threadIdx.x; idx < cnt; idx += 256) {
+    for (int idx = threadIdx.x; idx < cnt; idx += kAwRows) {
         const int r = idx / A, c = idx - r * A;
         sq[r * AP + c] = qs[idx];
     }
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(256) void aw_policy_kernel(const float* __restrict_
         }
         __syncthreads();
         float* ps = pi + ((int64_t)g * B + row0) * A;
-        for (int idx = threadIdx.x; idx < cnt; idx += 256) {
+        for (int idx = threadIdx.x; idx < cnt; idx += kAwRows) {
             const int rr = idx / A, c = idx - rr * A;
             ps[idx] = sp[rr * AP + c];
         }
@@ -67,15 +68,7 @@ hipError_t launch_aw_policy(const float* q, const float* v, int G, int B, int A,
     if (B <= 0) return hipSuccess;
     const unsigned blocks = (unsigned)((B + kAwRows - 1) / kAwRows);
     const size_t lds = (size_t)2 * kAwRows * (A | 1) * sizeof(float);
-    static bool attr_set = false;
-    if (lds > 64 * 1024 && !attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)aw_policy_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)(2 * kAwRows * 65 * sizeof(float)));
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    hipLaunchKernelGGL(aw_policy_kernel, dim3(blocks), dim3(256), lds, stream, q, v, G, B, A, beta, pi);
+    hipLaunchKernelGGL(aw_policy_kernel, dim3(blocks), dim3(kAwRows), lds, stream, q, v, G, B, A, beta, pi);
     return hipGetLastError();
 }
 

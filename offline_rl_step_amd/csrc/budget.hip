@@ -22,30 +22,52 @@
 
 namespace iqlh {
 
-constexpr int kBT = 256;          // threads per block
-constexpr int kPerThread = 8;     // elements per thread per sweep
-constexpr int kMaxBlocks = 1024;
+constexpr int kBT = 256;          // threads per block; each thread owns float4 quads
+constexpr int kMaxBlocks = 2048;
 
 int budget_num_blocks(int64_t n) {
-    int64_t nb = (n + (int64_t)kBT * kPerThread - 1) / ((int64_t)kBT * kPerThread);
+    const int64_t quads = (n + 3) / 4;
+    int64_t nb = (quads + kBT - 1) / kBT;
     if (nb < 1) nb = 1;
     if (nb > kMaxBlocks) nb = kMaxBlocks;
     return (int)nb;
 }
 
-__global__ __launch_bounds__(kBT) void budget_norms_kernel(SourceSet s, int64_t n,
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Quad qd covers elements 4qd .. 4qd+3 (those < n); 16-byte loads when every
+// pointer involved is 16-byte aligned.
+IQLH_DEV f32x4 ld4(const float* __restrict__ p, int64_t i, int64_t n, bool vec) {
+    if (vec && i + 3 < n) return *(const f32x4*)(p + i);
+    f32x4 r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (i + e < n) r[e] = p[i + e];
+    return r;
+}
+IQLH_DEV void st4(float* __restrict__ p, int64_t i, int64_t n, bool vec, f32x4 x) {
+    if (vec && i + 3 < n) {
+        *(f32x4*)(p + i) = x;
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (i + e < n) p[i + e] = x[e];
+}
+
+__global__ __launch_bounds__(kBT) void budget_norms_kernel(SourceSet s, int64_t n, int vec,
                                                              float* __restrict__ partials) {
     __shared__ float red[kBT / kWave];
     float acc[kMaxSources];
 #pragma unroll
     for (int j = 0; j < kMaxSources; ++j) acc[j] = 0.f;
-    const int64_t stride = (int64_t)gridDim.x * kBT;
-    for (int64_t i = (int64_t)blockIdx.x * kBT + threadIdx.x; i < n; i += stride) {
+    const int64_t quads = (n + 3) / 4, stride = (int64_t)gridDim.x * kBT;
+    for (int64_t qd = (int64_t)blockIdx.x * kBT + threadIdx.x; qd < quads; qd += stride) {
 #pragma unroll
         for (int j = 0; j < kMaxSources; ++j) {
             if (j < s.k) {
-                const float x = s.ptr[j][i];
-                acc[j] = fmaf(x, x, acc[j]);
+                const f32x4 x = ld4(s.ptr[j], 4 * qd, n, vec);
+                acc[j] = fmaf(x.x, x.x, fmaf(x.y, x.y, fmaf(x.z, x.z, fmaf(x.w, x.w, acc[j]))));
             }
         }
     }
@@ -75,7 +97,7 @@ IQLH_DEV float adam_clip(float norm, float max_norm) {
     return (norm > max_norm && norm > 0.f) ? max_norm / norm : 1.f;
 }
 
-__global__ __launch_bounds__(kBT) void budget_saxpy_kernel(SourceSet s, int64_t n, float mgn,
+__global__ __launch_bounds__(kBT) void budget_saxpy_kernel(SourceSet s, int64_t n, int vec, float mgn,
                                                             const float* __restrict__ partials,
                                                             float* __restrict__ grad,
                                                             float* __restrict__ gpart,
@@ -98,14 +120,14 @@ __global__ __launch_bounds__(kBT) void budget_saxpy_kernel(SourceSet s, int64_t 
 #pragma unroll
     for (int j = 0; j < kMaxSources; ++j) c[j] = j < s.k ? coef[j] : 0.f;
     float acc = 0.f;
-    const int64_t stride = (int64_t)nb * kBT;
-    for (int64_t i = (int64_t)blockIdx.x * kBT + threadIdx.x; i < n; i += stride) {
-        float g = 0.f;
+    const int64_t quads = (n + 3) / 4, stride = (int64_t)nb * kBT;
+    for (int64_t qd = (int64_t)blockIdx.x * kBT + threadIdx.x; qd < quads; qd += stride) {
+        f32x4 g = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < kMaxSources; ++j)
-            if (j < s.k) g = fmaf(c[j], s.ptr[j][i], g);
-        grad[i] = g;
-        acc = fmaf(g, g, acc);
+            if (j < s.k) g += c[j] * ld4(s.ptr[j], 4 * qd, n, vec);
+        st4(grad, 4 * qd, n, vec, g);
+        acc = fmaf(g.x, g.x, fmaf(g.y, g.y, fmaf(g.z, g.z, fmaf(g.w, g.w, acc))));
     }
     const float t = block_sum<kBT>(acc, red);
     if (threadIdx.x == 0) gpart[blockIdx.x] = t;
@@ -124,7 +146,7 @@ __global__ __launch_bounds__(kBT) void adam_flat_kernel(float* __restrict__ para
                                                          float* __restrict__ v,
                                                          const int32_t* __restrict__ tptr,
                                                          const float* __restrict__ sq_part, int nb,
-                                                         int64_t n, AdamHyper hp,
+                                                         int64_t n, int vec, AdamHyper hp,
                                                          float* __restrict__ out_norm,
                                                          int32_t* __restrict__ flags) {
     __shared__ float red[kBT / kWave];
@@ -137,31 +159,43 @@ __global__ __launch_bounds__(kBT) void adam_flat_kernel(float* __restrict__ para
     const float bc2 = 1.f - powf(hp.beta2, tt);
     const float decay = 1.f - hp.lr * hp.weight_decay;
     bool bad = false;
-    const int64_t stride = (int64_t)gridDim.x * kBT;
-    for (int64_t i = (int64_t)blockIdx.x * kBT + threadIdx.x; i < n; i += stride) {
-        const float g = grad[i] * c;
-        grad[i] = 0.f;
-        if (!isfinite(g)) { bad = true; continue; }
-        const float mi = hp.beta1 * m[i] + (1.f - hp.beta1) * g;
-        const float vi = hp.beta2 * v[i] + (1.f - hp.beta2) * g * g;
-        const float mh = mi / bc1, vh = vi / bc2;
-        float p = params[i];
-        if (hp.weight_decay != 0.f) p *= decay;
-        p -= hp.lr * mh / (sqrtf(vh) + hp.eps);
-        if (hp.clamp > 0.f) p = fminf(fmaxf(p, -hp.clamp), hp.clamp);
-        params[i] = p;
-        m[i] = mi;
-        v[i] = vi;
+    const int64_t quads = (n + 3) / 4, stride = (int64_t)gridDim.x * kBT;
+    for (int64_t qd = (int64_t)blockIdx.x * kBT + threadIdx.x; qd < quads; qd += stride) {
+        const int64_t i = 4 * qd;
+        const f32x4 g4 = ld4(grad, i, n, vec) * c;
+        f32x4 m4 = ld4(m, i, n, vec), v4 = ld4(v, i, n, vec), p4 = ld4(params, i, n, vec);
+        st4(grad, i, n, vec, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float g = g4[e];
+            if (!isfinite(g)) { bad |= (i + e < n); continue; }
+            const float mi = hp.beta1 * m4[e] + (1.f - hp.beta1) * g;
+            const float vi = hp.beta2 * v4[e] + (1.f - hp.beta2) * g * g;
+            const float mh = mi / bc1, vh = vi / bc2;
+            float p = p4[e];
+            if (hp.weight_decay != 0.f) p *= decay;
+            p -= hp.lr * mh / (sqrtf(vh) + hp.eps);
+            if (hp.clamp > 0.f) p = fminf(fmaxf(p, -hp.clamp), hp.clamp);
+            p4[e] = p;
+            m4[e] = mi;
+            v4[e] = vi;
+        }
+        st4(params, i, n, vec, p4);
+        st4(m, i, n, vec, m4);
+        st4(v, i, n, vec, v4);
     }
     if (bad) set_flag(flags, 0x1);
 }
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 hipError_t launch_adam_flat(float* params, float* grad, float* m, float* v, const int32_t* t,
                             const float* sq_partials, int nb, int64_t n, const AdamHyper& hp,
                             float* out_norm, int32_t* flags, hipStream_t stream) {
     const int blocks = budget_num_blocks(n);
+    const int vec = aligned16(params) && aligned16(grad) && aligned16(m) && aligned16(v);
     hipLaunchKernelGGL(adam_flat_kernel, dim3(blocks), dim3(kBT), 0, stream, params, grad, m, v, t,
-                       sq_partials, nb, n, hp, out_norm, flags);
+                       sq_partials, nb, n, vec, hp, out_norm, flags);
     return hipGetLastError();
 }
 
@@ -171,8 +205,10 @@ hipError_t launch_budget(float* grad, const SourceSet& s, int64_t n, float mgn, 
     const int nb = budget_num_blocks(n);
     float* partials = work;
     float* gpart = work + (int64_t)s.k * nb;
-    hipLaunchKernelGGL(budget_norms_kernel, dim3(nb), dim3(kBT), 0, stream, s, n, partials);
-    hipLaunchKernelGGL(budget_saxpy_kernel, dim3(nb), dim3(kBT), 0, stream, s, n, mgn, partials,
+    int vec = aligned16(grad);
+    for (int j = 0; j < s.k; ++j) vec = vec && aligned16(s.ptr[j]);
+    hipLaunchKernelGGL(budget_norms_kernel, dim3(nb), dim3(kBT), 0, stream, s, n, vec, partials);
+    hipLaunchKernelGGL(budget_saxpy_kernel, dim3(nb), dim3(kBT), 0, stream, s, n, vec, mgn, partials,
                        grad, gpart, out_norms, hp ? t : (int32_t*)nullptr);
     if (hp) {
         float* comb = out_norms ? out_norms + s.k : nullptr;

@@ -22,8 +22,9 @@ constexpr uint64_t kHerKey1 = 0x484552646F6E6F72ull;
 // First e in [0, E) with ends[e] > src, or -1.  All 64 lanes call it with the
 // same arguments; every branch is wave-uniform.
 IQLH_DEV int find_episode(const int32_t* __restrict__ ends, int E, int64_t src, int lane) {
-    if ((int64_t)ends[E - 1] <= src) return -1;
-    int lo = 0, hi = E - 1;  // answer in [lo, hi] and ends[hi] > src
+    // answer in [lo, hi] if one exists; a source past the last end converges
+    // to hi and fails the final check
+    int lo = 0, hi = E - 1;
     for (int it = 0; it < 64 && lo < hi; ++it) {
         const int64_t span = (int64_t)(hi - lo) + 1;
         const int p = lo + (int)((span * lane) >> 6);
@@ -42,6 +43,8 @@ IQLH_DEV int find_episode(const int32_t* __restrict__ ends, int E, int64_t src, 
     return lo;
 }
 
+constexpr int kRowRegs = 4;  // source-row columns held per lane (S <= 256)
+
 __global__ __launch_bounds__(256) void her_relabel_kernel(HerArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -50,6 +53,17 @@ __global__ __launch_bounds__(256) void her_relabel_kernel(HerArgs a) {
     const uint64_t step = a.d_step ? (uint64_t)(*a.d_step) : 0ull;
     const int64_t src = a.source_idx[i];
     bool ok = src >= 0 && src < a.buffer_size;
+    const float* __restrict__ s_src = a.states + (ok ? src : 0) * S;
+    const float* __restrict__ n_src = a.next_states + (ok ? src : 0) * S;
+    // The source row does not depend on the donor: issue its loads first so
+    // they overlap the random draw and the episode search.
+    float sv[kRowRegs], nv[kRowRegs];
+#pragma unroll
+    for (int r = 0; r < kRowRegs; ++r) {
+        const int d = lane + 64 * r;
+        sv[r] = (ok && d < S) ? s_src[d] : 0.f;
+        nv[r] = (ok && d < S) ? n_src[d] : 0.f;
+    }
     int64_t donor = -1;
     if (ok) {
         uint64_t r = 0;
@@ -93,26 +107,35 @@ __global__ __launch_bounds__(256) void her_relabel_kernel(HerArgs a) {
         return;
     }
 
-    const float* __restrict__ s_src = a.states + src * S;
-    const float* __restrict__ n_src = a.next_states + src * S;
     const float* __restrict__ n_don = a.next_states + donor * S;
-    for (int d = lane; d < S; d += 64) {
-        const bool goal = d < G;
-        const float gv = goal ? n_don[d] : 0.f;
-        const float vs = goal ? gv : s_src[d];
-        const float vn = goal ? gv : n_src[d];
+    const float dg = lane < G ? n_don[lane] : 0.f;  // donor goal, column = lane
+    auto put = [&](int d, float vs, float vn) {
         if (a.out_bf16) ((uint16_t*)a.out_states)[i * ld + d] = f2bf(vs);
         else ((float*)a.out_states)[i * ld + d] = vs;
         if (a.out_next_states) a.out_next_states[i * S + d] = vn;
+    };
+#pragma unroll
+    for (int r = 0; r < kRowRegs; ++r) {
+        const int d = lane + 64 * r;
+        if (d < S) {
+            const float gv = d < G ? (r == 0 ? dg : n_don[d]) : 0.f;
+            put(d, d < G ? gv : sv[r], d < G ? gv : nv[r]);
+        }
+    }
+    for (int d = lane + 64 * kRowRegs; d < S; d += 64) {
+        const float gv = d < G ? n_don[d] : 0.f;
+        put(d, d < G ? gv : s_src[d], d < G ? gv : n_src[d]);
+    }
+    // Binary32 sum of squares in goal order, no contraction, correctly rounded
+    // square root, strict comparison.  Goal d < 64 sits in lane d.
+    float acc = 0.f;
+    for (int d = 0; d < G; ++d) {
+        const float x = d < 64 ? __shfl(nv[0], d, 64) : n_src[d];
+        const float y = d < 64 ? __shfl(dg, d, 64) : n_don[d];
+        const float diff = __fsub_rn(x, y);
+        acc = __fadd_rn(acc, __fmul_rn(diff, diff));
     }
     if (lane == 0) {
-        // Binary32 sum of squares in goal order, no contraction, correctly
-        // rounded square root, strict comparison.
-        float acc = 0.f;
-        for (int d = 0; d < G; ++d) {
-            const float diff = __fsub_rn(n_src[d], n_don[d]);
-            acc = __fadd_rn(acc, __fmul_rn(diff, diff));
-        }
         const float dist = __fsqrt_rn(acc);
         a.out_rewards[i] = dist < a.threshold ? a.reward_hit : a.reward_miss;
         if (a.donor_out) a.donor_out[i] = (int32_t)donor;

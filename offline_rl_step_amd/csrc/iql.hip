@@ -44,6 +44,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- operands
 template <typename T> struct Op;
@@ -68,13 +70,32 @@ template <> struct Op<uint16_t> {  // bfloat16 storage
         const u32x2 hi = *(const u32x2*)(row + c0 + 8);
         return __builtin_bit_cast(frag, u32x4{lo.x, lo.y, hi.x, hi.y});
     }
+    // two floats -> packed bfloat16 pair, round to nearest even
+    // (v_cvt_pk_bf16_f32 on gfx950)
+    static IQLH_DEV uint32_t cvt2(float lo, float hi) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+    }
     // B operand of k step u from a layer's accumulators
     template <int NT>
     static IQLH_DEV frag from_acc(const f32x16 (&acc)[NT], int u) {
         const f32x16& a = acc[u >> 1];
         const int r = 8 * (u & 1);
-        return __builtin_bit_cast(frag, u32x4{pack_bf2(a[r + 0], a[r + 1]), pack_bf2(a[r + 2], a[r + 3]),
-                                             pack_bf2(a[r + 4], a[r + 5]), pack_bf2(a[r + 6], a[r + 7])});
+        return __builtin_bit_cast(frag, u32x4{cvt2(a[r + 0], a[r + 1]), cvt2(a[r + 2], a[r + 3]),
+                                             cvt2(a[r + 4], a[r + 5]), cvt2(a[r + 6], a[r + 7])});
+    }
+    static IQLH_DEV frag ones() {
+        return __builtin_bit_cast(frag, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+    }
+    // element e (0 .. KPL-1) of a fragment, as stored
+    static IQLH_DEV uint16_t half(frag f, int e) {
+        const u32x4 u = __builtin_bit_cast(u32x4, f);
+        return (e & 1) ? (uint16_t)(u[e >> 1] >> 16) : (uint16_t)(u[e >> 1] & 0xFFFFu);
+    }
+    // writes two consecutive-feature values of one sample into a [feature][sample] tile
+    static IQLH_DEV void put2(uint16_t* tile, int idx, int ld, float lo, float hi) {
+        const uint32_t pk = cvt2(lo, hi);
+        tile[idx] = (uint16_t)(pk & 0xFFFFu);
+        tile[idx + ld] = (uint16_t)(pk >> 16);
     }
     static IQLH_DEV frag make(const uint16_t* t) {
         return __builtin_bit_cast(frag, u32x4{(uint32_t)t[0] | ((uint32_t)t[1] << 16),
@@ -82,7 +103,7 @@ template <> struct Op<uint16_t> {  // bfloat16 storage
                                              (uint32_t)t[4] | ((uint32_t)t[5] << 16),
                                              (uint32_t)t[6] | ((uint32_t)t[7] << 16)});
     }
-    static IQLH_DEV uint16_t cvt(float x) { return f2bf(x); }
+    static IQLH_DEV uint16_t cvt(float x) { return (uint16_t)(cvt2(x, 0.f) & 0xFFFFu); }
     static IQLH_DEV float tof(uint16_t x) { return bf2f(x); }
     static IQLH_DEV void elems(frag f, float* out) {
         const u32x4 u = __builtin_bit_cast(u32x4, f);
@@ -118,6 +139,12 @@ template <> struct Op<float> {
         return acc[u >> 4][u & 15];
     }
     static IQLH_DEV frag make(const float* t) { return t[0]; }
+    static IQLH_DEV frag ones() { return 1.f; }
+    static IQLH_DEV float half(frag f, int) { return f; }
+    static IQLH_DEV void put2(float* tile, int idx, int ld, float lo, float hi) {
+        tile[idx] = lo;
+        tile[idx + ld] = hi;
+    }
     static IQLH_DEV float cvt(float x) { return x; }
     static IQLH_DEV float tof(float x) { return x; }
     static IQLH_DEV void elems(frag f, float* out) { out[0] = f; }
@@ -140,12 +167,12 @@ struct FusedArgs {
     const void* w1s;      // [G][H][SP]
     const void* w2s;      // [G][H][H]
     const void* w2ts;     // [G][H][H]
-    float* part;          // [G][nwg][P]
+    float* part;          // [G][nwg][Pp]
     float* loss_part;     // [G][nwg]
     float* out_v;         // [G][B] or null
     float tau0, tau1, invB;
     int B, S, nwg;
-    int64_t P;
+    int64_t P, Pp;
     int32_t* flags;
 };
 
@@ -167,35 +194,23 @@ struct FusedCfg {
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-// Row sums of a [rows][ld] LDS tile over its first BT columns, into dst[row].
-template <typename T, int BT, int NTHR>
-IQLH_DEV void row_sums(const T* tile, int rows, int ld, float* dst) {
-    for (int r = threadIdx.x; r < rows; r += NTHR) {
-        const T* p = tile + (int64_t)r * ld;
-        float s = 0.f;
-        for (int c = 0; c < BT; c += Op<T>::KPL) {
-            float e[Op<T>::KPL];
-            Op<T>::elems(Op<T>::load(p + c), e);
-#pragma unroll
-            for (int i = 0; i < Op<T>::KPL; ++i) s += e[i];
-        }
-        dst[r] = s;
-    }
-}
-
-// out[i][j] += sum_k A[i][k] * B[j][k] over K = BT columns of two LDS tiles,
+// out[i][j] = sum_k A[i][k] * B[j][k] over K = BT columns of two LDS tiles,
 // for 32x32 output tiles [t0, t1) (row-major over NCT column tiles); stores
-// fp32 results to dst[i * ldo + j] for j < ncols.
+// fp32 results to dst[i * ldo + j] for j < ncols.  When bias_dst is given,
+// the row sums sum_k A[i][k] of every row tile whose column tile 0 is in
+// the range go to bias_dst[i], from an extra MFMA against an all-ones
+// operand (a reduction over samples, i.e. across lanes, for free).
 template <typename T, int BT, int MAXT>
 IQLH_DEV void lds_gemm_store(const T* A, const T* Bm, int lda, int NCT, int t0, int t1,
-                             float* dst, int ldo, int ncols) {
+                             float* dst, int ldo, int ncols, float* bias_dst) {
     typedef Op<T> O;
     const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
+    const typename O::frag one = O::ones();
     for (int tb = t0; tb < t1; tb += MAXT) {
         const int nb = min(MAXT, t1 - tb);
-        f32x16 acc[MAXT];
+        f32x16 acc[MAXT], accb[MAXT];
 #pragma unroll
-        for (int q = 0; q < MAXT; ++q) acc[q] = f32x16{};
+        for (int q = 0; q < MAXT; ++q) acc[q] = accb[q] = f32x16{};
         for (int u = 0; u < BT / O::KS; ++u) {
             const int k0 = O::KS * u + O::KPL * h;
             int last_row = -1;
@@ -210,6 +225,7 @@ IQLH_DEV void lds_gemm_store(const T* A, const T* Bm, int lda, int NCT, int t0, 
                     }
                     const typename O::frag b = O::load(Bm + (int64_t)(32 * ct + l32) * lda + k0);
                     acc[q] = O::mma(a, b, acc[q]);
+                    if (bias_dst && ct == 0) accb[q] = O::mma(a, one, accb[q]);
                 }
             }
         }
@@ -219,18 +235,38 @@ IQLH_DEV void lds_gemm_store(const T* A, const T* Bm, int lda, int NCT, int t0, 
                 const int tau = tb + q, rt = tau / NCT, ct = tau - rt * NCT;
                 const int j = 32 * ct + l32;
                 if (j < ncols) {
+                    float* d0 = dst + (32 * rt + 4 * h) * ldo + j;  // 32-bit offsets from a uniform base
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int i = 32 * rt + 8 * (r >> 2) + 4 * h + (r & 3);
-                        dst[(int64_t)i * ldo + j] = acc[q][r];
-                    }
+                    for (int r = 0; r < 16; ++r) d0[(8 * (r >> 2) + (r & 3)) * ldo] = acc[q][r];
+                }
+                if (bias_dst && ct == 0 && l32 == 0) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) bias_dst[32 * rt + 8 * (r >> 2) + 4 * h + (r & 3)] = accb[q][r];
                 }
             }
         }
     }
 }
 
-template <typename T, int SP, int H, int NW>
+// dst[i] = sum_k A[i][k] over K = BT for the 32-row tiles [rt0, rt1), by
+// MFMA against an all-ones operand.
+template <typename T, int BT>
+IQLH_DEV void lds_rowsum(const T* A, int lda, int rt0, int rt1, float* dst) {
+    typedef Op<T> O;
+    const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
+    const typename O::frag one = O::ones();
+    for (int rt = rt0; rt < rt1; ++rt) {
+        f32x16 acc = f32x16{};
+        for (int u = 0; u < BT / O::KS; ++u)
+            acc = O::mma(O::load(A + (int64_t)(32 * rt + l32) * lda + O::KS * u + O::KPL * h), one, acc);
+        if (l32 == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dst[32 * rt + 8 * (r >> 2) + 4 * h + (r & 3)] = acc[r];
+        }
+    }
+}
+
+template <typename T, int SP, int H, int NW, bool XVEC>
 __global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
     typedef Op<T> O;
     typedef FusedCfg<T, SP, H, NW> C;
@@ -247,7 +283,8 @@ __global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
     float* sw3 = sb2 + H;
     float* sred = sw3 + H;  // [2][NW]
 
-    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
     const int g = blockIdx.y, wg = blockIdx.x;
     const int S = a.S, B = a.B;
     const POff po(S, H);
@@ -255,7 +292,7 @@ __global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
     const T* w1s = (const T*)a.w1s + (int64_t)g * H * SP;
     const T* w2s = (const T*)a.w2s + (int64_t)g * H * H;
     const T* w2ts = (const T*)a.w2ts + (int64_t)g * H * H;
-    float* part = a.part + ((int64_t)g * a.nwg + wg) * a.P;
+    float* part = a.part + ((int64_t)g * a.nwg + wg) * a.Pp;
     const float tau = g == 0 ? a.tau0 : a.tau1;
 
     // ---- S0: weights to LDS, biases and w3 to LDS, X fragments to registers
@@ -278,12 +315,12 @@ __global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
     typename O::frag xf[KU1];
     {
         const T* xr = (const T*)a.states + (int64_t)b * a.ld;
-        const bool vec = (S == SP) && ((a.ld % O::KPL) == 0);
+        // XVEC: S == SP and rows aligned to whole fragments (checked on the host)
 #pragma unroll
         for (int u = 0; u < KU1; ++u) {
             const int k0 = O::KS * u + O::KPL * h;
-            if (valid && vec) {
-                xf[u] = O::load(xr + k0);
+            if (XVEC) {
+                xf[u] = valid ? O::load(xr + k0) : O::zero();
             } else {
                 T tmp[O::KPL];
 #pragma unroll
@@ -308,21 +345,35 @@ __global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
         for (int t = 0; t < NT; ++t)
             acc[t] = O::mma(O::load(R0 + (32 * t + l32) * C::LDW1 + k0), xf[u], acc[t]);
     }
-    // epilogue: h1 = relu(z1 + b1); h1^T tile to R3
+    // epilogue: h1 = relu(z1 + b1); h1^T tile to R3 (registers r, r+1 hold
+    // features f, f+1 of this lane's sample)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < 16; r += 2) {
             const int f = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-            const float z = acc[t][r] + sb1[f];
-            const float y = z > 0.f ? z : 0.f;
-            acc[t][r] = y;
-            R3[f * C::LDA + bl] = O::cvt(y);
+            const float z0 = acc[t][r] + sb1[f], z1 = acc[t][r + 1] + sb1[f + 1];
+            const float y0 = z0 > 0.f ? z0 : 0.f, y1 = z1 > 0.f ? z1 : 0.f;
+            acc[t][r] = y0;
+            acc[t][r + 1] = y1;
+            O::put2(R3, f * C::LDA + bl, C::LDA, y0, y1);
         }
     }
     typename O::frag h1f[KUH];
 #pragma unroll
     for (int u = 0; u < KUH; ++u) h1f[u] = O::template from_acc<NT>(acc, u);
+    // relu'(z1) of this lane's 16*NT features, one bit per accumulator register
+    uint32_t mask1[(16 * NT + 31) / 32];
+#pragma unroll
+    for (int w = 0; w < (16 * NT + 31) / 32; ++w) mask1[w] = 0u;
+    // acc holds relu outputs (+0 or positive): bits + 0x7FFFFFFF carries into
+    // bit 31 exactly when the value is positive (no compare, no lane mask)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            mask1[(16 * t + r) >> 5] |= ((__float_as_uint(acc[t][r]) + 0x7FFFFFFFu) >> 31)
+                                        << ((16 * t + r) & 31);
     __syncthreads();
 
     // ---- F2: z2^T = W2 * h1^T  (A read with the chained k order)
@@ -363,14 +414,17 @@ __global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < 16; r += 2) {
             const int f = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-            const float z = acc[t][r];
-            const float hv = z > 0.f ? z : 0.f;
-            const float dz = z > 0.f ? dv * sw3[f] : 0.f;
-            acc[t][r] = dz;
-            R0[f * C::LDA + bl] = O::cvt(dz);        // dz2^T
-            R2[f * C::LDA + bl] = O::cvt(hv * dv);   // h2 * dv, row sums give dw3
+            const float z0 = acc[t][r], z1 = acc[t][r + 1];
+            const float dz0 = z0 > 0.f ? dv * sw3[f] : 0.f;
+            const float dz1 = z1 > 0.f ? dv * sw3[f + 1] : 0.f;
+            const float p0 = z0 > 0.f ? z0 * dv : 0.f;   // h2 * dv: row sums give dw3
+            const float p1 = z1 > 0.f ? z1 * dv : 0.f;
+            acc[t][r] = dz0;
+            acc[t][r + 1] = dz1;
+            O::put2(R0, f * C::LDA + bl, C::LDA, dz0, dz1);  // dz2^T
+            O::put2(R2, f * C::LDA + bl, C::LDA, p0, p1);
         }
     }
     typename O::frag dz2f[KUH];
@@ -378,9 +432,8 @@ __global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
     for (int u = 0; u < KUH; ++u) dz2f[u] = O::template from_acc<NT>(acc, u);
     __syncthreads();
 
-    // ---- row sums (db2, dw3, db3, loss) and dW2 = dz2^T h1
-    row_sums<T, BT, NTHR>(R0, H, C::LDA, part + po.b2);
-    row_sums<T, BT, NTHR>(R2, H, C::LDA, part + po.w3);
+    // ---- dw3 (row sums of h2 * dv), db3, loss, then dW2 = dz2^T h1 with db2
+    lds_rowsum<T, BT>(R2, C::LDA, wv * NT / NW, (wv + 1) * NT / NW, part + po.w3);
     if (tid == 0) {
         float ls = 0.f, ds = 0.f;
         for (int i = 0; i < NW; ++i) { ls += sred[i]; ds += sred[NW + i]; }
@@ -395,17 +448,15 @@ __global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
     {
         constexpr int T2 = NT * NT;
         const int t0 = wv * T2 / NW, t1 = (wv + 1) * T2 / NW;
-        lds_gemm_store<T, BT, 4>(R0, R3, C::LDA, NT, t0, t1, part + po.w2, H, H);
+        lds_gemm_store<T, BT, 4>(R0, R3, C::LDA, NT, t0, t1, part + po.w2, H, H, part + po.b2);
     }
     __syncthreads();
 
     // ---- s^T tile to R3 (h1^T no longer needed); B1: dh1^T = W2^T dz2^T
 #pragma unroll
     for (int u = 0; u < KU1; ++u) {
-        float e[O::KPL];
-        O::elems(xf[u], e);
 #pragma unroll
-        for (int i = 0; i < O::KPL; ++i) R3[(O::KS * u + O::KPL * h + i) * C::LDA + bl] = O::cvt(e[i]);
+        for (int i = 0; i < O::KPL; ++i) R3[(O::KS * u + O::KPL * h + i) * C::LDA + bl] = O::half(xf[u], i);
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
@@ -419,56 +470,73 @@ __global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < 16; r += 2) {
             const int f = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-            // register (t, r) sits in chained k step u = (16 t + r) / KPLH
-            bool pos;
-            if constexpr (O::KPL == 8) pos = O::chain_positive(h1f[2 * t + (r >> 3)], r & 7);
-            else pos = O::chain_positive(h1f[16 * t + r], 0);
-            const float dz = pos ? acc[t][r] : 0.f;
-            R2[f * C::LDA + bl] = O::cvt(dz);
+            const int bit = 16 * t + r;
+            const bool pos0 = (mask1[bit >> 5] >> (bit & 31)) & 1u;
+            const bool pos1 = (mask1[(bit + 1) >> 5] >> ((bit + 1) & 31)) & 1u;
+            O::put2(R2, f * C::LDA + bl, C::LDA, pos0 ? acc[t][r] : 0.f, pos1 ? acc[t][r + 1] : 0.f);
         }
     }
     __syncthreads();
 
-    // ---- db1 and dW1 = dz1^T s
-    row_sums<T, BT, NTHR>(R2, H, C::LDA, part + po.b1);
+    // ---- dW1 = dz1^T s with db1
     {
         constexpr int NCT = SP / 32;
         constexpr int T3 = NT * NCT;
         const int t0 = wv * T3 / NW, t1 = (wv + 1) * T3 / NW;
-        lds_gemm_store<T, BT, 4>(R2, R3, C::LDA, NCT, t0, t1, part + po.w1, S, S);
+        lds_gemm_store<T, BT, 4>(R2, R3, C::LDA, NCT, t0, t1, part + po.w1, S, S, part + po.b1);
     }
 }
 
-// Sums the per-workgroup partials of every parameter in workgroup order,
-// writes grad, per-block sums of squares, the mean loss, and advances t and
-// the step counter.
+// Sums the per-workgroup partials of every parameter in a fixed order (slice
+// sl of a block adds workgroups sl, sl + 8, ... in turn; the eight slice sums
+// are then added in slice order), writes grad and per-block sums of squares,
+// and, in block 0, the mean loss and the t / step-counter increments.  Each
+// thread streams float4 quads of four parameters, so a wave keeps many
+// independent 16-byte loads in flight.
+constexpr int kRedParams = 128;
+constexpr int kRedSlices = 8;
+
 __global__ __launch_bounds__(256) void iql_reduce_kernel(const float* __restrict__ part,
                                                          const float* __restrict__ loss_part,
-                                                         int nwg, int64_t P, float invB,
+                                                         int nwg, int64_t P, int64_t Pp, float invB,
                                                          float* __restrict__ grad,
                                                          float* __restrict__ sq_part, int rb,
                                                          int32_t* __restrict__ tcount,
                                                          int64_t* __restrict__ step,
                                                          float* __restrict__ out_loss,
                                                          int32_t* __restrict__ flags) {
-    __shared__ float red[4];
-    const int g = blockIdx.y;
-    const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    float s = 0.f;
-    if (p < P) {
-        const float* src = part + (int64_t)g * nwg * P + p;
-        for (int w = 0; w < nwg; ++w) s += src[(int64_t)w * P];
-        grad[(int64_t)g * P + p] = s;
+    __shared__ f32x4 red[kRedSlices][32];
+    __shared__ float wred[4];
+    const int g = blockIdx.y, tid = threadIdx.x, q = tid & 31, sl = tid >> 5;
+    const int64_t p0 = (int64_t)blockIdx.x * kRedParams + 4 * q;  // < Pp
+    const float* src = part + (int64_t)g * nwg * Pp + p0;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int w = sl; w < nwg; w += kRedSlices) acc += *(const f32x4*)(src + (int64_t)w * Pp);
+    red[sl][q] = acc;
+    __syncthreads();
+    float sq = 0.f;
+    if (sl == 0) {
+        f32x4 s = red[0][q];
+#pragma unroll
+        for (int i = 1; i < kRedSlices; ++i) s += red[i][q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (p0 + e < P) {
+                grad[(int64_t)g * P + p0 + e] = s[e];
+                sq = fmaf(s[e], s[e], sq);
+            }
+        }
     }
-    const float sq = block_sum<256>(s * s, red);
-    if (threadIdx.x == 0) sq_part[(int64_t)g * rb + blockIdx.x] = sq;
+    sq = block_sum<256>(sq, wred);
+    if (tid == 0) sq_part[(int64_t)g * rb + blockIdx.x] = sq;
     if (blockIdx.x == 0) {
         float l = 0.f;
-        for (int w = threadIdx.x; w < nwg; w += 256) l += loss_part[(int64_t)g * nwg + w];
-        l = block_sum<256>(l, red);
-        if (threadIdx.x == 0) {
+        for (int w = tid; w < nwg; w += 256) l += loss_part[(int64_t)g * nwg + w];
+        l = block_sum<256>(l, wred);
+        if (tid == 0) {
             const float loss = l * invB;
             if (out_loss) out_loss[g] = loss;
             if (!isfinite(loss)) set_flag(flags, 0x4);
@@ -555,24 +623,33 @@ __global__ __launch_bounds__(256) void iql_shadow_kernel(IqlDims d, IqlBuffers b
 }
 
 // ------------------------------------------------------------- dispatch
-template <typename T, int SP, int H, int NW>
-static hipError_t run_fused(const FusedArgs& fa, int G, hipStream_t stream, hipEvent_t ev0,
-                            hipEvent_t ev1) {
+template <typename T, int SP, int H, int NW, bool XVEC>
+static hipError_t run_fused_x(const FusedArgs& fa, int G, hipStream_t stream, hipEvent_t ev0,
+                              hipEvent_t ev1) {
     typedef FusedCfg<T, SP, H, NW> C;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)iql_fused_kernel<T, SP, H, NW>,
+        hipError_t e = hipFuncSetAttribute((const void*)iql_fused_kernel<T, SP, H, NW, XVEC>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::BYTES);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     if (ev0)  // events recorded by the dispatch itself: kernel time only
-        hipExtLaunchKernelGGL((iql_fused_kernel<T, SP, H, NW>), dim3(fa.nwg, G), dim3(64 * NW),
+        hipExtLaunchKernelGGL((iql_fused_kernel<T, SP, H, NW, XVEC>), dim3(fa.nwg, G), dim3(64 * NW),
                               C::BYTES, stream, ev0, ev1, 0, fa);
     else
-        hipLaunchKernelGGL((iql_fused_kernel<T, SP, H, NW>), dim3(fa.nwg, G), dim3(64 * NW), C::BYTES,
-                           stream, fa);
+        hipLaunchKernelGGL((iql_fused_kernel<T, SP, H, NW, XVEC>), dim3(fa.nwg, G), dim3(64 * NW),
+                           C::BYTES, stream, fa);
     return hipGetLastError();
+}
+
+template <typename T, int SP, int H, int NW>
+static hipError_t run_fused(const FusedArgs& fa, int G, hipStream_t stream, hipEvent_t ev0,
+                            hipEvent_t ev1) {
+    const bool xvec = fa.S == SP && fa.ld % Op<T>::KPL == 0 &&
+                      ((uintptr_t)fa.states % (sizeof(T) * Op<T>::KPL)) == 0;
+    return xvec ? run_fused_x<T, SP, H, NW, true>(fa, G, stream, ev0, ev1)
+                : run_fused_x<T, SP, H, NW, false>(fa, G, stream, ev0, ev1);
 }
 
 struct Variant {
@@ -603,7 +680,7 @@ int iql_s_pad(int dtype, int S, int H) {
     const Variant* v = pick(dtype, S, H);
     return v ? v->SP : 0;
 }
-int iql_reduce_blocks(int64_t P) { return (int)((P + 255) / 256); }
+int iql_reduce_blocks(int64_t P) { return (int)((P + kRedParams - 1) / kRedParams); }
 
 hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float* tau,
                               const void* states, int64_t ld, const float* q, int B, float* out_v,
@@ -616,7 +693,7 @@ hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float
     fa.w1s = b.w1s; fa.w2s = b.w2s; fa.w2ts = b.w2ts;
     fa.part = b.part; fa.loss_part = b.loss_part; fa.out_v = out_v;
     fa.tau0 = tau[0]; fa.tau1 = tau[d.G > 1 ? 1 : 0]; fa.invB = 1.f / (float)B;
-    fa.B = B; fa.S = d.S; fa.nwg = (B + BT - 1) / BT; fa.P = d.P; fa.flags = b.flags;
+    fa.B = B; fa.S = d.S; fa.nwg = (B + BT - 1) / BT; fa.P = d.P; fa.Pp = d.Pp; fa.flags = b.flags;
     return var->fn(fa, d.G, stream, ev0, ev1);
 }
 
@@ -628,7 +705,8 @@ hipError_t launch_iql_update(const IqlDims& d, const IqlBuffers& b, const AdamHy
     const int nwg = (B + BT - 1) / BT;
     const int rb = iql_reduce_blocks(d.P);
     hipLaunchKernelGGL(iql_reduce_kernel, dim3(rb, d.G), dim3(256), 0, stream, b.part, b.loss_part,
-                       nwg, d.P, 1.f / (float)B, b.grad, b.sq_part, rb, b.t, b.step, out_loss, b.flags);
+                       nwg, d.P, d.Pp, 1.f / (float)B, b.grad, b.sq_part, rb, b.t, b.step, out_loss,
+                       b.flags);
     const int64_t abn = (d.P + 255) / 256;
     const int ab = (int)(abn < 512 ? abn : 512);
     if (d.dtype == 1)

@@ -64,6 +64,7 @@ struct IqlDims {
     int S, H, G, dtype;  // dtype: 0 f32, 1 bf16
     int S_pad;           // columns of the W1 shadow (multiple of 32)
     int64_t P;           // parameters per group
+    int64_t Pp;          // row stride of the gradient partials (P rounded up to 128)
 };
 // Per-group device buffers, group stride = P (or the shadow sizes).
 struct IqlBuffers {
@@ -77,7 +78,7 @@ struct IqlBuffers {
     void* w1s;        // [G][H][S_pad]   operand-typed shadow of W1 (zero padded)
     void* w2s;        // [G][H][H]       shadow of W2
     void* w2ts;       // [G][H][H]       shadow of W2 transposed
-    float* part;      // [G][max_wg][P]  per-workgroup gradient partials
+    float* part;      // [G][max_wg][Pp] per-workgroup gradient partials
     float* loss_part; // [G][max_wg]
     float* sq_part;   // [G][max_rb]     per-block sums of squares of grad
     int max_wg;
