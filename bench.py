@@ -37,6 +37,9 @@ def parse():
     p.add_argument("--steps", type=int, default=1000)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-graph", action="store_true", help="eager launches instead of graph replay")
+    p.add_argument("--side-streams", action="store_true",
+                   help="fork the budget chain and the AW policy onto side streams (measured slower "
+                        "than one stream in graph replay at this size)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--kernel-reps", type=int, default=200)
@@ -141,11 +144,34 @@ class Context:
         self.adam = m.make_adam(self.theta, self.theta_m, self.theta_v, self.theta_t, lr=w.lr,
                                 max_grad_norm=w.max_grad_norm, d_flags=self.tr.flags)
 
-    def step(self):
+    def step(self, torch=None, side=None):
+        """One step.  With side streams, the budgeted accumulation (independent
+        of HER and IQL) forks at the start and the AW policy forks once V is
+        ready, both joining at the end: the fork/join layout of the pages'
+        multi-stream aux graph, on HIP streams."""
         m, w = self.m, self.w
+        main = torch.cuda.current_stream() if side else None
+        if side:
+            side[0].wait_stream(main)
+            with torch.cuda.stream(side[0]):
+                self.budget()
         m.her_relabel(self.hcfg, self.hbuf, self.src, w.n_her, 20261202, self.tr.step_counter, self.hout)
-        self.tr.train_step(self.X, self.q, w.B, self.out_v, self.out_loss, self.out_gn)
-        m.iql_aw_policy(self.Q, self.out_v, w.groups, w.B, w.A, w.beta, self.pi)
+        self.tr.compute_gradients(self.X, self.q, w.B, self.out_v)
+        if side:
+            side[1].wait_stream(main)
+            with torch.cuda.stream(side[1]):
+                m.iql_aw_policy(self.Q, self.out_v, w.groups, w.B, w.A, w.beta, self.pi)
+        else:
+            m.iql_aw_policy(self.Q, self.out_v, w.groups, w.B, w.A, w.beta, self.pi)
+        self.tr.apply_gradients(w.B, self.out_loss, self.out_gn)
+        if side:
+            main.wait_stream(side[0])
+            main.wait_stream(side[1])
+        else:
+            self.budget()
+
+    def budget(self):
+        m, w = self.m, self.w
         m.grad_budget_accumulate(self.grad, self.sources, w.budget_fractions, (1.0, 1.0, 1.0, 1.0),
                                  w.n_budget, w.max_grad_norm, self.norms, self.adam, self.ws)
 
@@ -202,19 +228,20 @@ def main():
     ctx = Context(m, w, torch, np, synth)
     torch.cuda.synchronize()
 
+    side = (torch.cuda.Stream(), torch.cuda.Stream()) if a.side_streams else None  # default priority
     for _ in range(a.warmup):
-        ctx.step()
+        ctx.step(torch, side)
     torch.cuda.synchronize()
     graph = None
     if not a.no_graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            ctx.step()
+            ctx.step(torch, side)
         for _ in range(3):
             graph.replay()
         torch.cuda.synchronize()
 
-    run = graph.replay if graph is not None else ctx.step
+    run = graph.replay if graph is not None else (lambda: ctx.step(torch, side))
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -245,7 +272,8 @@ def main():
            "config": {"workload": w.name, "global_batch": w.B, "state_dim": w.S, "hidden": w.H,
                       "actions": w.A, "groups": w.groups, "her_rows": w.n_her, "her_strategy": w.strategy,
                       "replay_rows": w.C, "budget_params": w.n_budget, "budget_sources": 4,
-                      "graph_replay": graph is not None, "parallelism": "single-gpu"},
+                      "graph_replay": graph is not None, "side_streams": side is not None,
+                      "parallelism": "single-gpu"},
            "event_ms_per_step": ev_ms / a.steps, "device_flags": flags, "status": rc,
            "roofline": roofline}
     if not a.no_cpu_baseline:

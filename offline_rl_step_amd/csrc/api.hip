@@ -73,7 +73,8 @@ static int check_config(const iqlh_config* c) {
         return fail(IQLH_EINVAL, "weight_decay must be finite and >= 0");
     if (!(c->max_grad_norm > 0.f)) return fail(IQLH_EINVAL, "max_grad_norm must be > 0");
     if (!(c->weight_clamp_max_abs >= 0.f)) return fail(IQLH_EINVAL, "weight_clamp_max_abs must be >= 0");
-    if (!iql_supported(c->compute_dtype, c->state_dim, c->hidden))
+    if (!iql_supported(c->compute_dtype, c->state_dim, c->hidden) &&
+        !iql_layered_supported(c->compute_dtype, c->state_dim, c->hidden))
         return fail(IQLH_ESHAPE, "no kernel for dtype=%d state_dim=%d hidden=%d", c->compute_dtype,
                     c->state_dim, c->hidden);
     return IQLH_OK;
@@ -109,16 +110,27 @@ int iql_create(const iqlh_config* cfg, const float* init_params_host, iql_handle
     iql_num_params(S, H, &P);
     IqlDims& d = t->dims;
     d.S = S; d.H = H; d.G = G; d.dtype = cfg->compute_dtype;
-    d.S_pad = iql_s_pad(d.dtype, S, H);
+    d.layered = iql_supported(d.dtype, S, H) ? 0 : 1;
+    d.S_pad = d.layered ? (S + 7) / 8 * 8 : iql_s_pad(d.dtype, S, H);
     d.P = P;
     d.Pp = (P + 127) / 128 * 128;
-    const int BT = iql_tile_samples(d.dtype, S, H);
-    const int max_wg = (cfg->max_batch + BT - 1) / BT;
+    const int64_t MB = cfg->max_batch;
+    int max_wg, max_loss;
+    if (d.layered) {
+        max_wg = (int)((MB + iql_layered_chunk() - 1) / iql_layered_chunk());
+        max_loss = (int)((MB + 63) / 64);
+    } else {
+        const int BT = iql_tile_samples(d.dtype, S, H);
+        max_wg = max_loss = (int)((MB + BT - 1) / BT);
+    }
     const int rb = iql_reduce_blocks(P);
     const size_t esz = d.dtype == IQLH_BF16 ? 2 : 4;
     IqlBuffers& b = t->buf;
     b.max_wg = max_wg;
     b.max_rb = rb;
+    b.act_h1 = b.act_dz2 = b.act_p2 = b.act_dz1 = nullptr;
+    b.act_z2 = b.act_dv = nullptr;
+    const size_t nact = d.layered ? (size_t)G * MB * H : 0;
     struct { void** p; size_t bytes; } plan[] = {
         {(void**)&b.params, sizeof(float) * G * P},
         {(void**)&b.m, sizeof(float) * G * P},
@@ -131,10 +143,17 @@ int iql_create(const iqlh_config* cfg, const float* init_params_host, iql_handle
         {(void**)&b.w2s, esz * G * H * H},
         {(void**)&b.w2ts, esz * G * H * H},
         {(void**)&b.part, sizeof(float) * G * (size_t)max_wg * d.Pp},
-        {(void**)&b.loss_part, sizeof(float) * G * (size_t)max_wg},
+        {(void**)&b.loss_part, sizeof(float) * G * (size_t)max_loss},
         {(void**)&b.sq_part, sizeof(float) * G * (size_t)rb},
+        {(void**)&b.act_h1, esz * nact},
+        {(void**)&b.act_z2, sizeof(float) * nact},
+        {(void**)&b.act_dz2, esz * nact},
+        {(void**)&b.act_p2, esz * nact},
+        {(void**)&b.act_dz1, esz * nact},
+        {(void**)&b.act_dv, sizeof(float) * (d.layered ? (size_t)G * MB : 0)},
     };
     for (auto& a : plan) {
+        if (a.bytes == 0) continue;
         rc = dev_alloc(t, a.p, a.bytes);
         if (rc) { free_all(t); delete t; return rc; }
     }

@@ -28,15 +28,35 @@ __global__ __launch_bounds__(kAwRows) void aw_policy_kernel(const float* __restr
     const int rows = (int)min<int64_t>(kAwRows, (int64_t)B - row0);
     const int cnt = rows * A;
     const float* qs = q + row0 * A;
-    for (int idx = threadIdx.x; idx < cnt; idx += kAwRows) {
-        const int r = idx / A, c = idx - r * A;
-        sq[r * AP + c] = qs[idx];
+    const int r = threadIdx.x;
+    // every load is issued before any is consumed: the slab arrives in one
+    // memory round trip (up to kStage values per thread; larger A loops)
+    constexpr int kStage = 16;
+    float stage[kStage];
+#pragma unroll
+    for (int k = 0; k < kStage; ++k) {
+        const int idx = threadIdx.x + k * kAwRows;
+        stage[k] = idx < cnt ? qs[idx] : 0.f;
+    }
+    float vg[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) vg[g] = (g < G && r < rows) ? v[(int64_t)g * B + row0 + r] : 0.f;
+#pragma unroll
+    for (int k = 0; k < kStage; ++k) {
+        const int idx = threadIdx.x + k * kAwRows;
+        if (idx < cnt) {
+            const int rr = idx / A, c = idx - rr * A;
+            sq[rr * AP + c] = stage[k];
+        }
+    }
+    for (int idx = threadIdx.x + kStage * kAwRows; idx < cnt; idx += kAwRows) {
+        const int rr = idx / A, c = idx - rr * A;
+        sq[rr * AP + c] = qs[idx];
     }
     __syncthreads();
-    const int r = threadIdx.x;
     for (int g = 0; g < G; ++g) {
         if (r < rows) {
-            const float vv = v[(int64_t)g * B + row0 + r];
+            const float vv = g == 0 ? vg[0] : (g == 1 ? vg[1] : v[(int64_t)g * B + row0 + r]);
             const float* qr = sq + r * AP;
             float* pr = sp + r * AP;
             float mx = -INFINITY;

@@ -106,6 +106,14 @@ __global__ __launch_bounds__(kBT) void budget_saxpy_kernel(SourceSet s, int64_t 
     __shared__ float red[kBT / kWave];
     __shared__ float coef[kMaxSources];
     const int nb = gridDim.x;
+    // this thread's first quad of every source does not depend on the clip
+    // scales: load it before folding the norm partials
+    const int64_t quads = (n + 3) / 4, stride = (int64_t)nb * kBT;
+    const int64_t q0 = (int64_t)blockIdx.x * kBT + threadIdx.x;
+    f32x4 pre[kMaxSources];
+#pragma unroll
+    for (int j = 0; j < kMaxSources; ++j)
+        pre[j] = (j < s.k && q0 < quads) ? ld4(s.ptr[j], 4 * q0, n, vec) : f32x4{0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < s.k; ++j) {
         const float sq = fold_partials(partials + (int64_t)j * nb, nb, red);
         if (threadIdx.x == 0) {
@@ -120,12 +128,11 @@ __global__ __launch_bounds__(kBT) void budget_saxpy_kernel(SourceSet s, int64_t 
 #pragma unroll
     for (int j = 0; j < kMaxSources; ++j) c[j] = j < s.k ? coef[j] : 0.f;
     float acc = 0.f;
-    const int64_t quads = (n + 3) / 4, stride = (int64_t)nb * kBT;
-    for (int64_t qd = (int64_t)blockIdx.x * kBT + threadIdx.x; qd < quads; qd += stride) {
+    for (int64_t qd = q0; qd < quads; qd += stride) {
         f32x4 g = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < kMaxSources; ++j)
-            if (j < s.k) g += c[j] * ld4(s.ptr[j], 4 * qd, n, vec);
+            if (j < s.k) g += c[j] * (qd == q0 ? pre[j] : ld4(s.ptr[j], 4 * qd, n, vec));
         st4(grad, 4 * qd, n, vec, g);
         acc = fmaf(g.x, g.x, fmaf(g.y, g.y, fmaf(g.z, g.z, fmaf(g.w, g.w, acc))));
     }
@@ -150,6 +157,16 @@ __global__ __launch_bounds__(kBT) void adam_flat_kernel(float* __restrict__ para
                                                          float* __restrict__ out_norm,
                                                          int32_t* __restrict__ flags) {
     __shared__ float red[kBT / kWave];
+    const int64_t quads = (n + 3) / 4, stride = (int64_t)gridDim.x * kBT;
+    const int64_t q0 = (int64_t)blockIdx.x * kBT + threadIdx.x;
+    // first quad's state loaded before the norm fold (independent of it)
+    f32x4 pg = {0.f, 0.f, 0.f, 0.f}, pm = pg, pv = pg, pp = pg;
+    if (q0 < quads) {
+        pg = ld4(grad, 4 * q0, n, vec);
+        pm = ld4(m, 4 * q0, n, vec);
+        pv = ld4(v, 4 * q0, n, vec);
+        pp = ld4(params, 4 * q0, n, vec);
+    }
     const float sq = fold_partials(sq_part, nb, red);
     const float nrm = sqrtf(sq);
     if (blockIdx.x == 0 && threadIdx.x == 0 && out_norm) *out_norm = nrm;
@@ -159,11 +176,12 @@ __global__ __launch_bounds__(kBT) void adam_flat_kernel(float* __restrict__ para
     const float bc2 = 1.f - powf(hp.beta2, tt);
     const float decay = 1.f - hp.lr * hp.weight_decay;
     bool bad = false;
-    const int64_t quads = (n + 3) / 4, stride = (int64_t)gridDim.x * kBT;
-    for (int64_t qd = (int64_t)blockIdx.x * kBT + threadIdx.x; qd < quads; qd += stride) {
+    for (int64_t qd = q0; qd < quads; qd += stride) {
         const int64_t i = 4 * qd;
-        const f32x4 g4 = ld4(grad, i, n, vec) * c;
-        f32x4 m4 = ld4(m, i, n, vec), v4 = ld4(v, i, n, vec), p4 = ld4(params, i, n, vec);
+        const bool first = qd == q0;
+        const f32x4 g4 = (first ? pg : ld4(grad, i, n, vec)) * c;
+        f32x4 m4 = first ? pm : ld4(m, i, n, vec), v4 = first ? pv : ld4(v, i, n, vec);
+        f32x4 p4 = first ? pp : ld4(params, i, n, vec);
         st4(grad, i, n, vec, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int e = 0; e < 4; ++e) {

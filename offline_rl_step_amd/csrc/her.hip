@@ -21,10 +21,29 @@ constexpr uint64_t kHerKey1 = 0x484552646F6E6F72ull;
 
 // First e in [0, E) with ends[e] > src, or -1.  All 64 lanes call it with the
 // same arguments; every branch is wave-uniform.
-IQLH_DEV int find_episode(const int32_t* __restrict__ ends, int E, int64_t src, int lane) {
-    // answer in [lo, hi] if one exists; a source past the last end converges
-    // to hi and fails the final check
-    int lo = 0, hi = E - 1;
+//
+// Round 0 probes the 64 episodes around the interpolation guess
+// src * E / buffer_size; when the answer lies strictly inside that window it
+// is found in one memory round trip (always, for equal-length episodes).
+// Otherwise the window's ballot still narrows the range before the 64-ary
+// search continues.
+IQLH_DEV int find_episode(const int32_t* __restrict__ ends, int E, int64_t src, int64_t size,
+                          int lane) {
+    int lo = 0, hi = E - 1;  // answer in [lo, hi] if one exists
+    {
+        int64_t gs = (src * (int64_t)E) / (size > 0 ? size : 1) - 31;
+        if (gs > (int64_t)E - 64) gs = (int64_t)E - 64;
+        if (gs < 0) gs = 0;
+        const int p = (int)gs + lane;
+        const bool pred = p < E && (int64_t)ends[p < E ? p : E - 1] > src;
+        const uint64_t m = __ballot(pred);
+        const int c = __popcll(~m & (E - (int)gs >= 64 ? ~0ull : ((1ull << (E - (int)gs)) - 1ull)));
+        // lanes [0, c) hold ends <= src, lanes [c, ...) ends > src
+        if (c > 0) lo = (int)gs + c;          // ends[gs + c - 1] <= src
+        if ((int)gs + c < E && c < 64) hi = (int)gs + c;  // ends[gs + c] > src
+        if (c == 0) hi = (int)gs;
+        if (lo > hi) lo = hi;  // source past the last end: checked below
+    }
     for (int it = 0; it < 64 && lo < hi; ++it) {
         const int64_t span = (int64_t)(hi - lo) + 1;
         const int p = lo + (int)((span * lane) >> 6);
@@ -64,6 +83,8 @@ __global__ __launch_bounds__(256) void her_relabel_kernel(HerArgs a) {
         sv[r] = (ok && d < S) ? s_src[d] : 0.f;
         nv[r] = (ok && d < S) ? n_src[d] : 0.f;
     }
+    const int32_t act = (ok && a.out_actions) ? a.actions[src] : 0;
+    const float done = (ok && a.out_dones) ? a.dones[src] : 0.f;
     int64_t donor = -1;
     if (ok) {
         uint64_t r = 0;
@@ -74,7 +95,7 @@ __global__ __launch_bounds__(256) void her_relabel_kernel(HerArgs a) {
         if (a.strategy == 2) {
             donor = uniform_index(r, 0, (uint64_t)a.buffer_size);
         } else {
-            const int e = find_episode(a.episode_ends, a.num_episodes, src, lane);
+            const int e = find_episode(a.episode_ends, a.num_episodes, src, a.buffer_size, lane);
             if (e < 0) {
                 ok = false;
             } else {
@@ -139,8 +160,8 @@ __global__ __launch_bounds__(256) void her_relabel_kernel(HerArgs a) {
         const float dist = __fsqrt_rn(acc);
         a.out_rewards[i] = dist < a.threshold ? a.reward_hit : a.reward_miss;
         if (a.donor_out) a.donor_out[i] = (int32_t)donor;
-        if (a.out_actions) a.out_actions[i] = a.actions[src];
-        if (a.out_dones) a.out_dones[i] = a.dones[src];
+        if (a.out_actions) a.out_actions[i] = act;
+        if (a.out_dones) a.out_dones[i] = done;
     }
 }
 

@@ -500,7 +500,8 @@ constexpr int kRedSlices = 8;
 
 __global__ __launch_bounds__(256) void iql_reduce_kernel(const float* __restrict__ part,
                                                          const float* __restrict__ loss_part,
-                                                         int nwg, int64_t P, int64_t Pp, float invB,
+                                                         int nwg, int nloss, int64_t P, int64_t Pp,
+                                                         float invB,
                                                          float* __restrict__ grad,
                                                          float* __restrict__ sq_part, int rb,
                                                          int32_t* __restrict__ tcount,
@@ -534,7 +535,7 @@ __global__ __launch_bounds__(256) void iql_reduce_kernel(const float* __restrict
     if (tid == 0) sq_part[(int64_t)g * rb + blockIdx.x] = sq;
     if (blockIdx.x == 0) {
         float l = 0.f;
-        for (int w = tid; w < nwg; w += 256) l += loss_part[(int64_t)g * nwg + w];
+        for (int w = tid; w < nloss; w += 256) l += loss_part[(int64_t)g * nloss + w];
         l = block_sum<256>(l, wred);
         if (tid == 0) {
             const float loss = l * invB;
@@ -685,6 +686,12 @@ int iql_reduce_blocks(int64_t P) { return (int)((P + kRedParams - 1) / kRedParam
 hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float* tau,
                               const void* states, int64_t ld, const float* q, int B, float* out_v,
                               hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    if (d.layered) {
+        if (ev0) (void)hipEventRecord(ev0, stream);
+        hipError_t e = launch_iql_layered_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream);
+        if (ev1 && e == hipSuccess) e = hipEventRecord(ev1, stream);
+        return e;
+    }
     const Variant* var = pick(d.dtype, d.S, d.H);
     if (!var) return hipErrorInvalidValue;
     const int BT = 32 * var->NW;
@@ -699,14 +706,20 @@ hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float
 
 hipError_t launch_iql_update(const IqlDims& d, const IqlBuffers& b, const AdamHyper& hp, int B,
                              float* out_loss, float* out_gnorm, hipStream_t stream) {
-    const Variant* var = pick(d.dtype, d.S, d.H);
-    if (!var) return hipErrorInvalidValue;
-    const int BT = 32 * var->NW;
-    const int nwg = (B + BT - 1) / BT;
+    int nwg, nloss;
+    if (d.layered) {
+        nwg = (B + iql_layered_chunk() - 1) / iql_layered_chunk();
+        nloss = (B + 63) / 64;
+    } else {
+        const Variant* var = pick(d.dtype, d.S, d.H);
+        if (!var) return hipErrorInvalidValue;
+        const int BT = 32 * var->NW;
+        nwg = nloss = (B + BT - 1) / BT;
+    }
     const int rb = iql_reduce_blocks(d.P);
     hipLaunchKernelGGL(iql_reduce_kernel, dim3(rb, d.G), dim3(256), 0, stream, b.part, b.loss_part,
-                       nwg, d.P, d.Pp, 1.f / (float)B, b.grad, b.sq_part, rb, b.t, b.step, out_loss,
-                       b.flags);
+                       nwg, nloss, d.P, d.Pp, 1.f / (float)B, b.grad, b.sq_part, rb, b.t, b.step,
+                       out_loss, b.flags);
     const int64_t abn = (d.P + 255) / 256;
     const int ab = (int)(abn < 512 ? abn : 512);
     if (d.dtype == 1)

@@ -62,6 +62,7 @@ hipError_t launch_adam_flat(float* params, float* grad, float* m, float* v, cons
 // ------------------------------------------------------------------ IQL
 struct IqlDims {
     int S, H, G, dtype;  // dtype: 0 f32, 1 bf16
+    int layered;         // 0: fused tile kernel; 1: layered GEMMs through HBM
     int S_pad;           // columns of the W1 shadow (multiple of 32)
     int64_t P;           // parameters per group
     int64_t Pp;          // row stride of the gradient partials (P rounded up to 128)
@@ -83,6 +84,13 @@ struct IqlBuffers {
     float* sq_part;   // [G][max_rb]     per-block sums of squares of grad
     int max_wg;
     int max_rb;
+    // layered path only: activations [G][max_batch][H] and dv [G][max_batch]
+    void* act_h1;
+    float* act_z2;
+    void* act_dz2;
+    void* act_p2;
+    void* act_dz1;
+    float* act_dv;
 };
 bool iql_supported(int dtype, int S, int H);
 int iql_tile_samples(int dtype, int S, int H);
@@ -96,6 +104,11 @@ hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float
 hipError_t launch_iql_update(const IqlDims& d, const IqlBuffers& b, const AdamHyper& hp, int B,
                              float* out_loss, float* out_gnorm, hipStream_t stream);
 int iql_s_pad(int dtype, int S, int H);
+bool iql_layered_supported(int dtype, int S, int H);
+int iql_layered_chunk();
+hipError_t launch_iql_layered_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float* tau,
+                                      const void* states, int64_t ld, const float* q, int B,
+                                      float* out_v, hipStream_t stream);
 hipError_t launch_iql_refresh_shadows(const IqlDims& d, const IqlBuffers& b, hipStream_t stream);
 
 }  // namespace iqlh

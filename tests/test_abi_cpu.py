@@ -62,7 +62,7 @@ def test_workspace_bytes(m):
 
 @pytest.mark.parametrize("field,value,code", [
     ("num_groups", 3, -1), ("max_batch", 0, -1), ("states_ld", 5, -1), ("compute_dtype", 7, -1),
-    ("hidden", 100, -2), ("max_grad_norm", 0.0, -1), ("beta2", 1.0, -1), ("eps", 0.0, -1),
+    ("hidden", 5000, -2), ("max_grad_norm", 0.0, -1), ("beta2", 1.0, -1), ("eps", 0.0, -1),
 ])
 def test_create_rejects_bad_config_on_host(m, field, value, code):
     import numpy as np

@@ -235,3 +235,34 @@ def test_step_counter_drives_her_donors(m):
     sync()
     ref = her.her_step(buf, src, w.G, her.FUTURE, seed=77, step=3)
     assert np.array_equal(host(don), ref["donor_idx"])
+
+
+# ------------------------------------------------------------ layered path
+def test_layered_bf16_ragged(m):
+    """Shapes the fused tile kernel does not hold on chip go through the
+    layered GEMM path; ragged against both the 128-row tiles and the
+    2048-row weight-gradient chunks."""
+    w = synth.shrink(synth.WORKLOADS["b16384_s128_h128_bf16_g2"], S=100, H=256, G=8)
+    _one_step(m, w, 2e-2, B=3000, ld=104, taus=(0.7, 0.2))
+
+
+def test_layered_fp32(m):
+    w = synth.shrink(synth.WORKLOADS["tiny_b256_s16_h32"], S=20, H=64, G=4)
+    _one_step(m, w, 1e-4, B=1000)
+
+
+def test_stress_b65536_s256_h512_one_step(m):
+    _one_step(m, synth.WORKLOADS["stress_b65536_s256_h512_bf16"], 2e-2)
+
+
+def test_stress_three_steps_teacher_forced(m):
+    w = synth.WORKLOADS["stress_b65536_s256_h512_bf16"]
+    s = Setup(m, w, B=8192)
+    for _ in range(2):
+        s.gpu_step()
+    before = [s.state(g) for g in range(s.G)]
+    s.gpu_step()
+    sync()
+    forced = [st.copy() for st in before]
+    refs = s.oracle_step(forced)
+    s.compare_step(refs, forced, 2e-2, 3, "stress teacher-forced step 3")
