@@ -7,7 +7,8 @@ two value trainers of hidden width 128, 9 actions, bf16 GEMM operands):
                           the merged bf16 batch (replay buffer of 2^20 rows);
   2. iql_train_step    -- both trainers: fused forward/backward (MFMA),
                           fixed-order gradient reduction, clipped Adam;
-  3. iql_aw_policy     -- pi for both trainers from this step's V;
+  3. the AW policy     -- pi for both trainers from this step's V, computed in
+                          the forward/backward launch (iql_train_step_aw);
   4. grad_budget_accumulate -- four sources over 132612 parameters, budgets
                           0.70/0.15/0.10/0.05 of max_grad_norm 1.0, then Adam.
 The step is captured once in a HIP graph and replayed (the HER donor counter
@@ -38,8 +39,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-graph", action="store_true", help="eager launches instead of graph replay")
     p.add_argument("--side-streams", action="store_true",
-                   help="fork the budget chain and the AW policy onto side streams (measured slower "
-                        "than one stream in graph replay at this size)")
+                   help="fork the budget chain onto a side stream (measured slower than one "
+                        "stream in graph replay at this size)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--kernel-reps", type=int, default=200)
@@ -146,9 +147,8 @@ class Context:
 
     def step(self, torch=None, side=None):
         """One step.  With side streams, the budgeted accumulation (independent
-        of HER and IQL) forks at the start and the AW policy forks once V is
-        ready, both joining at the end: the fork/join layout of the pages'
-        multi-stream aux graph, on HIP streams."""
+        of HER and IQL) forks at the start and joins at the end: the fork/join
+        layout of the pages' multi-stream aux graph, on HIP streams."""
         m, w = self.m, self.w
         main = torch.cuda.current_stream() if side else None
         if side:
@@ -156,17 +156,11 @@ class Context:
             with torch.cuda.stream(side[0]):
                 self.budget()
         m.her_relabel(self.hcfg, self.hbuf, self.src, w.n_her, 20261202, self.tr.step_counter, self.hout)
-        self.tr.compute_gradients(self.X, self.q, w.B, self.out_v)
-        if side:
-            side[1].wait_stream(main)
-            with torch.cuda.stream(side[1]):
-                m.iql_aw_policy(self.Q, self.out_v, w.groups, w.B, w.A, w.beta, self.pi)
-        else:
-            m.iql_aw_policy(self.Q, self.out_v, w.groups, w.B, w.A, w.beta, self.pi)
-        self.tr.apply_gradients(w.B, self.out_loss, self.out_gn)
+        # forward/backward with the AW policy in the same launch, then reduction + Adam
+        self.tr.train_step_aw(self.X, self.q, w.B, self.Q, w.A, w.beta, self.pi, self.out_v, self.out_loss,
+                              self.out_gn)
         if side:
             main.wait_stream(side[0])
-            main.wait_stream(side[1])
         else:
             self.budget()
 

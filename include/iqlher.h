@@ -106,6 +106,19 @@ int iql_destroy(iql_handle h);
 int iql_train_step(iql_handle h, const void* states, const float* q_taken, int32_t batch,
                    float* out_v, float* out_loss, float* out_grad_norm, void* stream);
 
+/* iql_train_step plus the advantage-weighted policy of every group from this
+ * step's V(s) (the policy of iql_aw_policy below):
+ *   q_all  device [B, num_actions] f32 Q(s, .);  out_pi device [G, B, A] f32;
+ *   out_v  required here.
+ * With bf16 operands, hidden 128 and num_actions <= 16 the policy is
+ * computed inside the forward/backward launch (V never leaves registers);
+ * otherwise the iql_aw_policy kernel runs after it.  The IQL trainer feeds
+ * its advantage weights to later trainers ([P3] "2A. Aux Child", IQL runs
+ * first because CQL reads the IQL advantage weights). */
+int iql_train_step_aw(iql_handle h, const void* states, const float* q_taken, int32_t batch,
+                      const float* q_all, int32_t num_actions, float beta, float* out_pi,
+                      float* out_v, float* out_loss, float* out_grad_norm, void* stream);
+
 /* The two halves of iql_train_step, for callers that time or schedule them
  * separately ([P1] "CUDA Kernel: iql_value_kernel.cu" fuses forward, loss and
  * backward into one launch; the norm and Adam follow as separate phases):

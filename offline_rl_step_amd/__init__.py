@@ -71,6 +71,7 @@ _lib_iql_num_params = _sig("iql_num_params", _i32, [_i32, _i32, ctypes.POINTER(_
 _lib_iql_create = _sig("iql_create", _i32, [ctypes.POINTER(IqlConfig), _p, ctypes.POINTER(_p)])
 _lib_iql_destroy = _sig("iql_destroy", _i32, [_p])
 _lib_iql_train_step = _sig("iql_train_step", _i32, [_p, _p, _p, _i32, _p, _p, _p, _p])
+_lib_iql_train_step_aw = _sig("iql_train_step_aw", _i32, [_p, _p, _p, _i32, _p, _i32, _f, _p, _p, _p, _p, _p])
 _lib_iql_compute_gradients = _sig("iql_compute_gradients", _i32, [_p, _p, _p, _i32, _p, _p])
 _lib_iql_apply_gradients = _sig("iql_apply_gradients", _i32, [_p, _i32, _p, _p, _p])
 _lib_iql_time_cg = _sig("iql_time_compute_gradients", _i32, [_p, _p, _p, _i32, _i32, ctypes.POINTER(_f), _p])
@@ -157,6 +158,13 @@ def iql_destroy(h):
 def iql_train_step(h, states, q_taken, batch, out_v=None, out_loss=None, out_grad_norm=None, stream=None):
     _check(_lib_iql_train_step(h, _ptr(states), _ptr(q_taken), batch, _ptr(out_v), _ptr(out_loss),
                                _ptr(out_grad_norm), _stream(stream)), "iql_train_step")
+
+
+def iql_train_step_aw(h, states, q_taken, batch, q_all, num_actions, beta, out_pi, out_v, out_loss=None,
+                      out_grad_norm=None, stream=None):
+    _check(_lib_iql_train_step_aw(h, _ptr(states), _ptr(q_taken), batch, _ptr(q_all), num_actions, beta,
+                                  _ptr(out_pi), _ptr(out_v), _ptr(out_loss), _ptr(out_grad_norm),
+                                  _stream(stream)), "iql_train_step_aw")
 
 
 def iql_compute_gradients(h, states, q_taken, batch, out_v=None, stream=None):
@@ -289,6 +297,11 @@ class IqlTrainer:
 
     def train_step(self, states, q_taken, batch, out_v=None, out_loss=None, out_grad_norm=None, stream=None):
         iql_train_step(self.h, states, q_taken, batch, out_v, out_loss, out_grad_norm, stream)
+
+    def train_step_aw(self, states, q_taken, batch, q_all, num_actions, beta, out_pi, out_v, out_loss=None,
+                      out_grad_norm=None, stream=None):
+        iql_train_step_aw(self.h, states, q_taken, batch, q_all, num_actions, beta, out_pi, out_v, out_loss,
+                          out_grad_norm, stream)
 
     def compute_gradients(self, states, q_taken, batch, out_v=None, stream=None):
         iql_compute_gradients(self.h, states, q_taken, batch, out_v, stream)

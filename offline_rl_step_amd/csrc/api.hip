@@ -229,6 +229,29 @@ int iql_apply_gradients(iql_handle h, int32_t batch, float* out_loss, float* out
     return IQLH_OK;
 }
 
+int iql_train_step_aw(iql_handle h, const void* states, const float* q_taken, int32_t batch,
+                      const float* q_all, int32_t num_actions, float beta, float* out_pi, float* out_v,
+                      float* out_loss, float* out_grad_norm, void* stream) {
+    int rc = check_step_args(h, states, q_taken, batch);
+    if (rc) return rc;
+    if (!q_all || !out_pi || !out_v) return fail(IQLH_EINVAL, "iql_train_step_aw: q_all, out_pi and out_v are required");
+    if (num_actions < 1 || num_actions > 64) return fail(IQLH_EINVAL, "num_actions must be in [1, 64]");
+    if (!std::isfinite(beta)) return fail(IQLH_EINVAL, "beta must be finite");
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (iql_fused_policy(h->dims, num_actions)) {
+        e = launch_iql_fwd_bwd(h->dims, h->buf, h->cfg.tau, states, h->cfg.states_ld, q_taken, batch, out_v, s,
+                               nullptr, nullptr, q_all, num_actions, beta, out_pi);
+    } else {
+        e = launch_iql_fwd_bwd(h->dims, h->buf, h->cfg.tau, states, h->cfg.states_ld, q_taken, batch, out_v, s);
+        if (e == hipSuccess) e = launch_aw_policy(q_all, out_v, h->dims.G, batch, num_actions, beta, out_pi, s);
+    }
+    if (e == hipSuccess)
+        e = launch_iql_update(h->dims, h->buf, adam_hyper(h->cfg), batch, out_loss, out_grad_norm, s);
+    if (e != hipSuccess) return hip_fail(e, "iql_train_step_aw launch");
+    return IQLH_OK;
+}
+
 int iql_train_step(iql_handle h, const void* states, const float* q_taken, int32_t batch,
                    float* out_v, float* out_loss, float* out_grad_norm, void* stream) {
     int rc = iql_compute_gradients(h, states, q_taken, batch, out_v, stream);

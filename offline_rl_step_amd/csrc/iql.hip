@@ -170,6 +170,10 @@ struct FusedArgs {
     float* part;          // [G][nwg][Pp]
     float* loss_part;     // [G][nwg]
     float* out_v;         // [G][B] or null
+    const float* q_all;   // [B][A] or null: advantage-weighted policy fused in
+    float* out_pi;        // [G][B][A]
+    int A;                // actions, <= 16 when fused
+    float beta;
     float tau0, tau1, invB;
     int B, S, nwg;
     int64_t P, Pp;
@@ -623,6 +627,313 @@ __global__ __launch_bounds__(256) void iql_shadow_kernel(IqlDims d, IqlBuffers b
     }
 }
 
+// ---------------------------------------------------- 16x16 MFMA variant
+// Same computation as iql_fused_kernel for bf16 operands and hidden 128, with
+// eight wave64s per workgroup (two per SIMD, so one wave's LDS and memory
+// waits overlap the other's MFMA work).  Each wave owns 16 samples and uses
+// v_mfma_f32_16x16x32_bf16: D[feature][sample] 16x16 tiles, lane l holding
+// sample l & 15 and features 4 (l >> 4) + r, r = 0..3.  The chained B operand
+// of the next layer packs two such tiles (32 features), and the weight
+// operand is read with the same k order (two 8-byte runs per lane).
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+IQLH_DEV f32x4v mma16(bf16x8 a, bf16x8 b, f32x4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+IQLH_DEV bf16x8 ld8(const uint16_t* p) { return __builtin_bit_cast(bf16x8, *(const u32x4*)p); }
+// chained weight fragment of k step u (32 features) for lane group q
+IQLH_DEV bf16x8 ld_chain16(const uint16_t* row, int u, int q) {
+    const u32x2 lo = *(const u32x2*)(row + 32 * u + 4 * q);
+    const u32x2 hi = *(const u32x2*)(row + 32 * u + 16 + 4 * q);
+    return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+}
+// chained B operand of k step u from tiles 2u, 2u + 1 of a layer's accumulators
+template <int NT>
+IQLH_DEV bf16x8 chain_from16(const f32x4v (&acc)[NT], int u) {
+    const f32x4v& a = acc[2 * u];
+    const f32x4v& b = acc[2 * u + 1];
+    typedef Op<uint16_t> O;
+    return __builtin_bit_cast(bf16x8, u32x4{O::cvt2(a[0], a[1]), O::cvt2(a[2], a[3]), O::cvt2(b[0], b[1]),
+                                             O::cvt2(b[2], b[3])});
+}
+
+// C[i][j] = sum_k A[i][k] B[j][k] over K = 128 samples for row tile rt (16 rows)
+// and column tiles [0, NCT) of 16; stores C rows to dst (ldo, j < ncols) and,
+// through the all-ones operand, the row sums of A to bias_dst.
+template <int NCT>
+IQLH_DEV void lds_gemm16_row(const uint16_t* A, const uint16_t* Bm, int lda, int rt, float* dst,
+                             int ldo, int ncols, float* bias_dst) {
+    const int lane = threadIdx.x & 63, l16 = lane & 15, q = lane >> 4;
+    const bf16x8 one = Op<uint16_t>::ones();
+    f32x4v acc[NCT], accb = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) acc[c] = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int k0 = 32 * u + 8 * q;
+        const bf16x8 a = ld8(A + (16 * rt + l16) * lda + k0);
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) acc[c] = mma16(a, ld8(Bm + (16 * c + l16) * lda + k0), acc[c]);
+        accb = mma16(a, one, accb);
+    }
+    float* d0 = dst + (16 * rt + 4 * q) * ldo;
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+        const int j = 16 * c + l16;
+        if (j < ncols) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) d0[r * ldo + j] = acc[c][r];
+        }
+    }
+    if (l16 == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bias_dst[16 * rt + 4 * q + r] = accb[r];
+    }
+}
+
+template <int SP, int H, bool XVEC>
+__global__ __launch_bounds__(512) void iql_fused16_kernel(FusedArgs a) {
+    typedef Op<uint16_t> O;
+    typedef FusedCfg<uint16_t, SP, H, 4> C;  // same LDS plan: BT = 128, padded rows
+    constexpr int NW = 8, BT = 128, NT = H / 16, KU1 = SP / 32, KUH = H / 32, NTHR = 512;
+    static_assert(H == 128 && SP % 32 == 0 && SP <= 128, "tile shape");
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint16_t* R0 = (uint16_t*)smem;
+    uint16_t* R1 = R0 + C::R0;
+    uint16_t* R2 = R1 + C::R1;
+    uint16_t* R3 = R2 + C::R2;
+    float* sb1 = (float*)(R3 + C::R3);
+    float* sb2 = sb1 + H;
+    float* sw3 = sb2 + H;
+    float* sred = sw3 + H;  // [2][NW]
+
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = blockIdx.y, wg = blockIdx.x;
+    const int S = a.S, B = a.B;
+    const POff po(S, H);
+    const float* prm = a.params + (int64_t)g * a.P;
+    const uint16_t* w1s = (const uint16_t*)a.w1s + (int64_t)g * H * SP;
+    const uint16_t* w2s = (const uint16_t*)a.w2s + (int64_t)g * H * H;
+    const uint16_t* w2ts = (const uint16_t*)a.w2ts + (int64_t)g * H * H;
+    float* part = a.part + ((int64_t)g * a.nwg + wg) * a.Pp;
+    const float tau = g == 0 ? a.tau0 : a.tau1;
+
+    // ---- S0: weights and small vectors to LDS, this lane's sample row to registers
+    const int bl = 16 * wv + l16;
+    const int b = wg * BT + bl;
+    const bool valid = b < B;
+    bf16x8 xf[KU1];
+    {
+        const uint16_t* xr = (const uint16_t*)a.states + (int64_t)b * a.ld;
+#pragma unroll
+        for (int u = 0; u < KU1; ++u) {
+            const int k0 = 32 * u + 8 * q;
+            if (XVEC) {
+                xf[u] = valid ? ld8(xr + k0) : O::zero();
+            } else {
+                uint16_t tmp[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) tmp[e] = (valid && k0 + e < S) ? xr[k0 + e] : (uint16_t)0;
+                xf[u] = O::make(tmp);
+            }
+        }
+    }
+    for (int idx = tid * 8; idx < H * SP; idx += NTHR * 8) {
+        const int r = idx / SP, c = idx - r * SP;
+        *(u32x4*)(R0 + r * C::LDW1 + c) = *(const u32x4*)(w1s + idx);
+    }
+    for (int idx = tid * 8; idx < H * H; idx += NTHR * 8) {
+        const int r = idx / H, c = idx - r * H;
+        *(u32x4*)(R1 + r * C::LDW2 + c) = *(const u32x4*)(w2s + idx);
+    }
+    for (int i = tid; i < H; i += NTHR) {
+        sb1[i] = prm[po.b1 + i];
+        sb2[i] = prm[po.b2 + i];
+        sw3[i] = prm[po.w3 + i];
+    }
+    // Loads whose values are needed only later are issued now, so their
+    // latency hides behind layers 1 and 2: the target, b3, and this
+    // thread's share of the W2^T shadow (staged into R1 once W2 is dead).
+    const float qb = valid ? a.q[b] : 0.f;
+    const float b3 = prm[po.b3];
+    // Q(s, .) of this lane's sample for the fused policy: lane group q takes
+    // actions q, q + 4, q + 8, q + 12
+    float qa[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int act = q + 4 * k;
+        qa[k] = (a.out_pi && valid && act < a.A) ? a.q_all[(int64_t)b * a.A + act] : 0.f;
+    }
+    constexpr int W2T_PER_THREAD = H * H / (NTHR * 8);
+    u32x4 w2t[W2T_PER_THREAD];
+#pragma unroll
+    for (int k = 0; k < W2T_PER_THREAD; ++k) w2t[k] = *(const u32x4*)(w2ts + (tid + k * NTHR) * 8);
+    __syncthreads();
+
+    // ---- F1: z1^T = W1 s^T
+    f32x4v acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < KU1; ++u)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            acc[t] = mma16(ld8(R0 + (16 * t + l16) * C::LDW1 + 32 * u + 8 * q), xf[u], acc[t]);
+    uint32_t mask1 = 0u;  // relu'(z1), bit 4t + r
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int r = 0; r < 4; r += 2) {
+            const int f = 16 * t + 4 * q + r;
+            const float z0 = acc[t][r] + sb1[f], z1 = acc[t][r + 1] + sb1[f + 1];
+            const float y0 = z0 > 0.f ? z0 : 0.f, y1 = z1 > 0.f ? z1 : 0.f;
+            acc[t][r] = y0;
+            acc[t][r + 1] = y1;
+            O::put2(R3, f * C::LDA + bl, C::LDA, y0, y1);  // h1^T
+            mask1 |= (((__float_as_uint(y0) + 0x7FFFFFFFu) >> 31) << (4 * t + r)) |
+                     (((__float_as_uint(y1) + 0x7FFFFFFFu) >> 31) << (4 * t + r + 1));
+        }
+    }
+    bf16x8 h1f[KUH];
+#pragma unroll
+    for (int u = 0; u < KUH; ++u) h1f[u] = chain_from16<NT>(acc, u);
+    __syncthreads();
+
+    // ---- F2: z2^T = W2 h1^T
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < KUH; ++u)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            acc[t] = mma16(ld_chain16(R1 + (16 * t + l16) * C::LDW2, u, q), h1f[u], acc[t]);
+    float vpart = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int f = 16 * t + 4 * q + r;
+            const float z = acc[t][r] + sb2[f];
+            acc[t][r] = z;
+            vpart = fmaf(sw3[f], z > 0.f ? z : 0.f, vpart);
+        }
+    vpart += __shfl_xor(vpart, 16, 64);
+    vpart += __shfl_xor(vpart, 32, 64);
+    const float v = vpart + b3;
+    float dv = 0.f, lterm = 0.f;
+    if (valid) {
+        const float diff = qb - v;
+        const float w = diff >= 0.f ? tau : 1.f - tau;
+        lterm = w * diff * diff;
+        dv = -2.f * w * diff * a.invB;
+        if (q == 0 && a.out_v) a.out_v[(int64_t)g * B + b] = v;
+    }
+    {
+        const float ls = wave_sum(q == 0 ? lterm : 0.f);
+        const float ds = wave_sum(q == 0 ? dv : 0.f);
+        if (lane == 0) { sred[wv] = ls; sred[NW + wv] = ds; }
+    }
+    if (a.out_pi) {
+        // pi = softmax(beta * clamp(Q - V, -10, 10)) with the row maximum
+        // subtracted ("Current State / IQL (CPU)", advantage-weighted action
+        // selection); the four lanes of a sample share it through shuffles
+        float x[4], mx = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const bool on = q + 4 * k < a.A;
+            x[k] = on ? a.beta * fminf(fmaxf(qa[k] - v, -10.f), 10.f) : -INFINITY;
+            mx = fmaxf(mx, x[k]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        float se = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            x[k] = q + 4 * k < a.A ? expf(x[k] - mx) : 0.f;
+            se += x[k];
+        }
+        se += __shfl_xor(se, 16, 64);
+        se += __shfl_xor(se, 32, 64);
+        if (valid) {
+            float* pr = a.out_pi + ((int64_t)g * B + b) * a.A;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (q + 4 * k < a.A) pr[q + 4 * k] = x[k] / se;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int r = 0; r < 4; r += 2) {
+            const int f = 16 * t + 4 * q + r;
+            const float z0 = acc[t][r], z1 = acc[t][r + 1];
+            const float dz0 = z0 > 0.f ? dv * sw3[f] : 0.f;
+            const float dz1 = z1 > 0.f ? dv * sw3[f + 1] : 0.f;
+            O::put2(R0, f * C::LDA + bl, C::LDA, dz0, dz1);                                // dz2^T
+            O::put2(R2, f * C::LDA + bl, C::LDA, z0 > 0.f ? z0 * dv : 0.f, z1 > 0.f ? z1 * dv : 0.f);  // h2 dv
+            acc[t][r] = dz0;
+            acc[t][r + 1] = dz1;
+        }
+    }
+    bf16x8 dz2f[KUH];
+#pragma unroll
+    for (int u = 0; u < KUH; ++u) dz2f[u] = chain_from16<NT>(acc, u);
+    __syncthreads();
+
+    // ---- dw3 (row sums of h2 dv), loss, db3; W2^T to R1; dW2 = dz2^T h1 with db2
+    {
+        const bf16x8 one = O::ones();
+        f32x4v s3 = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s3 = mma16(ld8(R2 + (16 * wv + l16) * C::LDA + 32 * u + 8 * q), one, s3);
+        if (l16 == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) part[po.w3 + 16 * wv + 4 * q + r] = s3[r];
+        }
+    }
+    if (tid == 0) {
+        float ls = 0.f, ds = 0.f;
+        for (int i = 0; i < NW; ++i) { ls += sred[i]; ds += sred[NW + i]; }
+        a.loss_part[(int64_t)g * a.nwg + wg] = ls;
+        part[po.b3] = ds;
+    }
+#pragma unroll
+    for (int k = 0; k < W2T_PER_THREAD; ++k) {
+        const int idx = (tid + k * NTHR) * 8, r = idx / H, c = idx - r * H;
+        *(u32x4*)(R1 + r * C::LDW2 + c) = w2t[k];
+    }
+    lds_gemm16_row<H / 16>(R0, R3, C::LDA, wv, part + po.w2, H, H, part + po.b2);
+    __syncthreads();
+
+    // ---- s^T to R3; B1: dh1^T = W2^T dz2^T; dz1 = dh1 relu'(z1) -> R2
+#pragma unroll
+    for (int u = 0; u < KU1; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) R3[(32 * u + 8 * q + i) * C::LDA + bl] = O::half(xf[u], i);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < KUH; ++u)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            acc[t] = mma16(ld_chain16(R1 + (16 * t + l16) * C::LDW2, u, q), dz2f[u], acc[t]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int r = 0; r < 4; r += 2) {
+            const int f = 16 * t + 4 * q + r;
+            const float d0 = (mask1 >> (4 * t + r)) & 1u ? acc[t][r] : 0.f;
+            const float d1 = (mask1 >> (4 * t + r + 1)) & 1u ? acc[t][r + 1] : 0.f;
+            O::put2(R2, f * C::LDA + bl, C::LDA, d0, d1);
+        }
+    }
+    __syncthreads();
+
+    // ---- dW1 = dz1^T s with db1
+    lds_gemm16_row<SP / 16>(R2, R3, C::LDA, wv, part + po.w1, S, S, part + po.b1);
+}
+
 // ------------------------------------------------------------- dispatch
 template <typename T, int SP, int H, int NW, bool XVEC>
 static hipError_t run_fused_x(const FusedArgs& fa, int G, hipStream_t stream, hipEvent_t ev0,
@@ -644,6 +955,35 @@ static hipError_t run_fused_x(const FusedArgs& fa, int G, hipStream_t stream, hi
     return hipGetLastError();
 }
 
+template <int SP, int H, bool XVEC>
+static hipError_t run_fused16_x(const FusedArgs& fa, int G, hipStream_t stream, hipEvent_t ev0,
+                                hipEvent_t ev1) {
+    typedef FusedCfg<uint16_t, SP, H, 4> C;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)iql_fused16_kernel<SP, H, XVEC>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)(C::BYTES + 16 * sizeof(float)));
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const size_t lds = C::BYTES + 16 * sizeof(float);  // sred holds 2 x 8 waves
+    if (ev0)
+        hipExtLaunchKernelGGL((iql_fused16_kernel<SP, H, XVEC>), dim3(fa.nwg, G), dim3(512), lds, stream,
+                              ev0, ev1, 0, fa);
+    else
+        hipLaunchKernelGGL((iql_fused16_kernel<SP, H, XVEC>), dim3(fa.nwg, G), dim3(512), lds, stream, fa);
+    return hipGetLastError();
+}
+
+template <int SP, int H>
+static hipError_t run_fused16(const FusedArgs& fa, int G, hipStream_t stream, hipEvent_t ev0,
+                              hipEvent_t ev1) {
+    const bool xvec = fa.S == SP && fa.ld % 8 == 0 && ((uintptr_t)fa.states % 16) == 0;
+    return xvec ? run_fused16_x<SP, H, true>(fa, G, stream, ev0, ev1)
+                : run_fused16_x<SP, H, false>(fa, G, stream, ev0, ev1);
+}
+
 template <typename T, int SP, int H, int NW>
 static hipError_t run_fused(const FusedArgs& fa, int G, hipStream_t stream, hipEvent_t ev0,
                             hipEvent_t ev1) {
@@ -658,8 +998,9 @@ struct Variant {
     hipError_t (*fn)(const FusedArgs&, int, hipStream_t, hipEvent_t, hipEvent_t);
 };
 static const Variant kVariants[] = {
-    {1, 128, 128, 4, &run_fused<uint16_t, 128, 128, 4>},
-    {1, 64, 128, 4, &run_fused<uint16_t, 64, 128, 4>},
+    // bf16, hidden 128: eight 16-sample waves per 128-sample workgroup
+    {1, 128, 128, 4, &run_fused16<128, 128>},
+    {1, 64, 128, 4, &run_fused16<64, 128>},
     {1, 32, 32, 4, &run_fused<uint16_t, 32, 32, 4>},
     {0, 32, 32, 4, &run_fused<float, 32, 32, 4>},
     {0, 64, 128, 1, &run_fused<float, 64, 128, 1>},
@@ -683,9 +1024,14 @@ int iql_s_pad(int dtype, int S, int H) {
 }
 int iql_reduce_blocks(int64_t P) { return (int)((P + kRedParams - 1) / kRedParams); }
 
+bool iql_fused_policy(const IqlDims& d, int A) {
+    return !d.layered && d.dtype == 1 && d.H == 128 && A >= 1 && A <= 16;
+}
+
 hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float* tau,
                               const void* states, int64_t ld, const float* q, int B, float* out_v,
-                              hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+                              hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1,
+                              const float* q_all, int A, float beta, float* out_pi) {
     if (d.layered) {
         if (ev0) (void)hipEventRecord(ev0, stream);
         hipError_t e = launch_iql_layered_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream);
@@ -699,6 +1045,7 @@ hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float
     fa.states = states; fa.ld = ld; fa.q = q; fa.params = b.params;
     fa.w1s = b.w1s; fa.w2s = b.w2s; fa.w2ts = b.w2ts;
     fa.part = b.part; fa.loss_part = b.loss_part; fa.out_v = out_v;
+    fa.q_all = q_all; fa.out_pi = out_pi; fa.A = A; fa.beta = beta;
     fa.tau0 = tau[0]; fa.tau1 = tau[d.G > 1 ? 1 : 0]; fa.invB = 1.f / (float)B;
     fa.B = B; fa.S = d.S; fa.nwg = (B + BT - 1) / BT; fa.P = d.P; fa.Pp = d.Pp; fa.flags = b.flags;
     return var->fn(fa, d.G, stream, ev0, ev1);

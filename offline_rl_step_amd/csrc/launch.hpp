@@ -96,10 +96,14 @@ bool iql_supported(int dtype, int S, int H);
 int iql_tile_samples(int dtype, int S, int H);
 int iql_reduce_blocks(int64_t P);
 // Fused forward/backward: V(s) and the per-workgroup gradient partials.
+// With out_pi non-null and iql_fused_policy(d, A), the advantage-weighted
+// policy of every group is computed in the same launch from this V.
 hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float* tau,
                               const void* states, int64_t ld, const float* q, int B,
                               float* out_v, hipStream_t stream, hipEvent_t ev0 = nullptr,
-                              hipEvent_t ev1 = nullptr);
+                              hipEvent_t ev1 = nullptr, const float* q_all = nullptr, int A = 0,
+                              float beta = 0.f, float* out_pi = nullptr);
+bool iql_fused_policy(const IqlDims& d, int A);
 // Fixed-order reduction of the partials of a batch of B rows, clip, Adam.
 hipError_t launch_iql_update(const IqlDims& d, const IqlBuffers& b, const AdamHyper& hp, int B,
                              float* out_loss, float* out_gnorm, hipStream_t stream);

@@ -266,3 +266,30 @@ def test_stress_three_steps_teacher_forced(m):
     forced = [st.copy() for st in before]
     refs = s.oracle_step(forced)
     s.compare_step(refs, forced, 2e-2, 3, "stress teacher-forced step 3")
+
+
+# ------------------------------------------------- train step + AW policy
+@pytest.mark.parametrize("wname,B,A", [("b16384_s128_h128_bf16_g2", 16384, 9), ("b16384_s128_h128_bf16_g2", 1000, 16),
+                                       ("b16384_s128_h128_bf16_g2", 777, 1), ("tiny_b256_s16_h32", 256, 4)])
+def test_train_step_with_policy(m, wname, B, A):
+    """The policy fused into the forward/backward launch (bf16, hidden 128,
+    A <= 16) or run after it (other shapes) equals the oracle's policy of the
+    step's own V, and the step itself is unchanged."""
+    import torch
+    from oracle import aw
+    w = synth.shrink(synth.WORKLOADS[wname], A=A)
+    s = Setup(m, w, B=B)
+    g = np.random.default_rng(A)
+    Q = (g.standard_normal((B, A)) * 2).astype(np.float32)
+    Q[::7, 0] = 1e3  # clamp path
+    pi = torch.zeros((s.G, B, A), dtype=torch.float32, device=dev())
+    s.tr.train_step_aw(s.tX, s.tq, B, to_dev(Q), A, w.beta, pi, s.out_v, s.out_loss, s.out_gn)
+    sync()
+    vg = host(s.out_v)
+    got = host(pi)
+    for gi in range(s.G):
+        ref = aw.aw_policy(Q, vg[gi], w.beta)
+        d = np.abs(got[gi] - ref)
+        assert np.all(d <= 1e-5 * np.abs(ref) + 1e-7), f"policy g{gi}: {d.max():.3e}"
+    refs = s.oracle_step()
+    s.compare_step(refs, s.oracle, 2e-2 if s.bf16 else 1e-4, 1, "train_step_aw")
