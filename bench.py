@@ -2,17 +2,21 @@
 """Throughput of the IQL + HER auxiliary-trainer step on one MI355X.
 
 One step, on synthetic inputs resident in HBM (batch 16384, state_dim 128,
-two value trainers of hidden width 128, 9 actions, bf16 GEMM operands):
-  1. her_relabel       -- 8192 rows, "future" donors, written into the tail of
-                          the merged bf16 batch (replay buffer of 2^20 rows);
-  2. iql_train_step    -- both trainers: fused forward/backward (MFMA),
-                          fixed-order gradient reduction, clipped Adam;
-  3. the AW policy     -- pi for both trainers from this step's V, computed in
-                          the forward/backward launch (iql_train_step_aw);
-  4. grad_budget_accumulate -- four sources over 132612 parameters, budgets
-                          0.70/0.15/0.10/0.05 of max_grad_norm 1.0, then Adam.
-The step is captured once in a HIP graph and replayed (the HER donor counter
-lives on the device, so every replay draws new donors).
+two value trainers of hidden width 128, 9 actions, bf16 GEMM operands), is
+one iql_aux_step call:
+  1. HER relabelling  -- 8192 rows, "future" donors, written into the tail of
+                         the merged bf16 batch (replay buffer of 2^20 rows);
+  2. the IQL step     -- both trainers: fused forward/backward (MFMA) with the
+                         AW policy from this step's V in the same launch,
+                         fixed-order gradient reduction, clipped Adam;
+  3. the budget       -- four sources over 132612 parameters, budgets
+                         0.70/0.15/0.10/0.05 of max_grad_norm 1.0, then Adam;
+in four launches (HER + budget norms | forward/backward + policy | reduction
++ SAXPY | both Adam updates).  --separate times her_relabel +
+iql_train_step_aw + grad_budget_accumulate called one after the other
+instead (same results bit for bit, seven launches).  The step is captured
+once in a HIP graph and replayed (the HER donor counter lives on the device,
+so every replay draws new donors).
 
 Prints ONE JSON line.  `value` = samples/s = batch / wall-clock time per step
 over the timed replays.  `roofline` is for the dominant kernel (the fused
@@ -38,9 +42,8 @@ def parse():
     p.add_argument("--steps", type=int, default=1000)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-graph", action="store_true", help="eager launches instead of graph replay")
-    p.add_argument("--side-streams", action="store_true",
-                   help="fork the budget chain onto a side stream (measured slower than one "
-                        "stream in graph replay at this size)")
+    p.add_argument("--separate", action="store_true",
+                   help="the three entry points one after the other instead of iql_aux_step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--kernel-reps", type=int, default=200)
@@ -145,27 +148,22 @@ class Context:
         self.adam = m.make_adam(self.theta, self.theta_m, self.theta_v, self.theta_t, lr=w.lr,
                                 max_grad_norm=w.max_grad_norm, d_flags=self.tr.flags)
 
-    def step(self, torch=None, side=None):
-        """One step.  With side streams, the budgeted accumulation (independent
-        of HER and IQL) forks at the start and joins at the end: the fork/join
-        layout of the pages' multi-stream aux graph, on HIP streams."""
+        self.her_step = m.her_step(self.hcfg, self.hbuf, self.src, w.n_her, 20261202, self.hout)
+        self.budget_step = m.budget_step(self.grad, self.sources, w.budget_fractions, (1.0, 1.0, 1.0, 1.0),
+                                         w.n_budget, w.max_grad_norm, self.norms, self.adam, self.ws)
+
+    def step(self):
+        """One whole step: iql_aux_step (four launches)."""
+        w = self.w
+        self.tr.aux_step(self.her_step, self.X, self.q, w.B, self.Q, w.A, w.beta, self.pi, self.out_v,
+                         self.out_loss, self.out_gn, self.budget_step)
+
+    def step_separate(self):
+        """The same step through the three separate entry points."""
         m, w = self.m, self.w
-        main = torch.cuda.current_stream() if side else None
-        if side:
-            side[0].wait_stream(main)
-            with torch.cuda.stream(side[0]):
-                self.budget()
         m.her_relabel(self.hcfg, self.hbuf, self.src, w.n_her, 20261202, self.tr.step_counter, self.hout)
-        # forward/backward with the AW policy in the same launch, then reduction + Adam
         self.tr.train_step_aw(self.X, self.q, w.B, self.Q, w.A, w.beta, self.pi, self.out_v, self.out_loss,
                               self.out_gn)
-        if side:
-            main.wait_stream(side[0])
-        else:
-            self.budget()
-
-    def budget(self):
-        m, w = self.m, self.w
         m.grad_budget_accumulate(self.grad, self.sources, w.budget_fractions, (1.0, 1.0, 1.0, 1.0),
                                  w.n_budget, w.max_grad_norm, self.norms, self.adam, self.ws)
 
@@ -222,20 +220,20 @@ def main():
     ctx = Context(m, w, torch, np, synth)
     torch.cuda.synchronize()
 
-    side = (torch.cuda.Stream(), torch.cuda.Stream()) if a.side_streams else None  # default priority
+    step = ctx.step_separate if a.separate else ctx.step
     for _ in range(a.warmup):
-        ctx.step(torch, side)
+        step()
     torch.cuda.synchronize()
     graph = None
     if not a.no_graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            ctx.step(torch, side)
+            step()
         for _ in range(3):
             graph.replay()
         torch.cuda.synchronize()
 
-    run = graph.replay if graph is not None else (lambda: ctx.step(torch, side))
+    run = graph.replay if graph is not None else step
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -255,7 +253,7 @@ def main():
     flops = fused_flops_per_launch(w)
     achieved = flops / (avg_us * 1e-6) / 1e12
     src_hash = kernel_source_hash()
-    roofline = {"bound": "mfma", "kernel": "iql_fused_kernel<bf16,128,128,4>", "achieved": achieved,
+    roofline = {"bound": "mfma", "kernel": "iql_fused16_kernel<128,128>", "achieved": achieved,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                 "traffic": traffic_from_profiles("iql_fused_b16384_s128_h128_g2", src_hash),
                 "avg_kernel_us": avg_us, "flops_per_launch": flops, "source_hash": src_hash}
@@ -266,7 +264,8 @@ def main():
            "config": {"workload": w.name, "global_batch": w.B, "state_dim": w.S, "hidden": w.H,
                       "actions": w.A, "groups": w.groups, "her_rows": w.n_her, "her_strategy": w.strategy,
                       "replay_rows": w.C, "budget_params": w.n_budget, "budget_sources": 4,
-                      "graph_replay": graph is not None, "side_streams": side is not None,
+                      "graph_replay": graph is not None,
+                      "entry_point": "separate calls" if a.separate else "iql_aux_step",
                       "parallelism": "single-gpu"},
            "event_ms_per_step": ev_ms / a.steps, "device_flags": flags, "status": rc,
            "roofline": roofline}

@@ -269,6 +269,56 @@ int grad_budget_accumulate(float* grad_buf, const float* const* sources, const f
                            float max_grad_norm, float* out_norms, const iqlh_adam* adam,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * The whole auxiliary step in one call: HER rows into the merged batch, the
+ * IQL step on it with the advantage-weighted policy, and the budgeted
+ * accumulation + Adam of the main network's gradient ([P1] "Phase 3:
+ * Combined IQL + HER" and "How HER Interacts with GPU PER"; [P5] "Task 1").
+ * The results equal, bit for bit, those of
+ *   her_relabel(her->cfg, her->buf, her->source_idx, her->n, her->seed,
+ *               iql_step_counter(h), her->out, stream);
+ *   iql_train_step_aw(h, states, q_taken, batch, q_all, ...)
+ *       (iql_train_step when q_all is NULL);
+ *   grad_budget_accumulate(budget->grad_buf, ..., stream);
+ * but the work is enqueued as four launches: passes that do not depend on
+ * each other share a launch.
+ *   her     NULL: no relabelling.  The Philox step word is the handle's step
+ *           counter before this step increments it.  her->out->states may
+ *           point into `states` (the merged batch); no other buffer of one
+ *           part may overlap a buffer of another part.
+ *   q_all   NULL: no policy (num_actions, beta, out_pi ignored).
+ *   budget  NULL: no accumulation.
+ * Each part is validated as its own entry point validates it; when any check
+ * fails nothing is enqueued. */
+typedef struct iqlh_her_step {
+    const her_config* cfg;
+    const her_buffer* buf;
+    const int32_t* source_idx;  /* device [n] */
+    const her_out* out;
+    uint64_t seed;
+    int32_t n;
+    int32_t reserved0;
+} iqlh_her_step;
+
+typedef struct iqlh_budget_step {
+    float* grad_buf;            /* as grad_budget_accumulate */
+    const float* const* sources;
+    const float* fractions;
+    const float* alphas;
+    float* out_norms;
+    const iqlh_adam* adam;
+    void* workspace;
+    size_t workspace_bytes;
+    int64_t n;
+    int32_t num_sources;
+    float max_grad_norm;
+} iqlh_budget_step;
+
+int iql_aux_step(iql_handle h, const iqlh_her_step* her, const void* states, const float* q_taken,
+                 int32_t batch, const float* q_all, int32_t num_actions, float beta, float* out_pi,
+                 float* out_v, float* out_loss, float* out_grad_norm, const iqlh_budget_step* budget,
+                 void* stream);
+
 /* Thread-local text of the last error returned on this thread ("" if none). */
 const char* iqlh_last_error(void);
 

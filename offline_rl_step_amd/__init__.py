@@ -60,6 +60,18 @@ class Adam(ctypes.Structure):
                 ("max_grad_norm", _f), ("weight_clamp_max_abs", _f), ("reserved0", _f)]
 
 
+class HerStep(ctypes.Structure):
+    _fields_ = [("cfg", ctypes.POINTER(HerConfig)), ("buf", ctypes.POINTER(HerBuffer)), ("source_idx", _p),
+                ("out", ctypes.POINTER(HerOut)), ("seed", _u64), ("n", _i32), ("reserved0", _i32)]
+
+
+class BudgetStep(ctypes.Structure):
+    _fields_ = [("grad_buf", _p), ("sources", ctypes.POINTER(_p)), ("fractions", ctypes.POINTER(_f)),
+                ("alphas", ctypes.POINTER(_f)), ("out_norms", _p), ("adam", ctypes.POINTER(Adam)),
+                ("workspace", _p), ("workspace_bytes", ctypes.c_size_t), ("n", _i64), ("num_sources", _i32),
+                ("max_grad_norm", _f)]
+
+
 def _sig(name, res, args):
     fn = getattr(_lib, name)
     fn.restype = res
@@ -87,6 +99,8 @@ _lib_ws_bytes = _sig("grad_budget_workspace_bytes", _i32, [_i64, _i32, ctypes.PO
 _lib_budget = _sig("grad_budget_accumulate", _i32, [_p, ctypes.POINTER(_p), ctypes.POINTER(_f),
                                                     ctypes.POINTER(_f), _i32, _i64, _f, _p,
                                                     ctypes.POINTER(Adam), _p, ctypes.c_size_t, _p])
+_lib_iql_aux_step = _sig("iql_aux_step", _i32, [_p, ctypes.POINTER(HerStep), _p, _p, _i32, _p, _i32, _f, _p, _p,
+                                                _p, _p, ctypes.POINTER(BudgetStep), _p])
 _lib_last_error = _sig("iqlh_last_error", ctypes.c_char_p, [])
 
 
@@ -287,6 +301,42 @@ def grad_budget_accumulate(grad_buf, sources, fractions, alphas, n, max_grad_nor
            "grad_budget_accumulate")
 
 
+# ------------------------------------------------------------ whole step
+def her_step(cfg, buf, source_idx, n, seed, out):
+    """HerStep for iql_aux_step (the HER arguments of her_relabel minus d_step)."""
+    st = HerStep()
+    st.cfg, st.buf, st.out = ctypes.pointer(cfg), ctypes.pointer(buf), ctypes.pointer(out)
+    st.source_idx = None if source_idx is None else source_idx.data_ptr()
+    st.seed, st.n = seed, n
+    return st
+
+
+def budget_step(grad_buf, sources, fractions, alphas, n, max_grad_norm, out_norms, adam, workspace):
+    """BudgetStep for iql_aux_step (the arguments of grad_budget_accumulate)."""
+    k = len(sources)
+    st = BudgetStep()
+    st.grad_buf = grad_buf.data_ptr()
+    st.sources = (_p * k)(*[x.data_ptr() for x in sources])
+    st.fractions = (_f * k)(*fractions)
+    st.alphas = (_f * k)(*alphas)
+    st.out_norms = None if out_norms is None else out_norms.data_ptr()
+    if adam is not None:
+        st.adam = ctypes.pointer(adam)
+    st.workspace = workspace.data_ptr()
+    st.workspace_bytes = workspace.numel() * workspace.element_size()
+    st.n, st.num_sources, st.max_grad_norm = n, k, max_grad_norm
+    return st
+
+
+def iql_aux_step(h, her, states, q_taken, batch, q_all=None, num_actions=0, beta=0.0, out_pi=None, out_v=None,
+                 out_loss=None, out_grad_norm=None, budget=None, stream=None):
+    """HER + IQL step (+ AW policy) + budgeted accumulation in four launches."""
+    _check(_lib_iql_aux_step(h, None if her is None else ctypes.byref(her), _ptr(states), _ptr(q_taken), batch,
+                             _ptr(q_all), num_actions, beta, _ptr(out_pi), _ptr(out_v), _ptr(out_loss),
+                             _ptr(out_grad_norm), None if budget is None else ctypes.byref(budget),
+                             _stream(stream)), "iql_aux_step")
+
+
 class IqlTrainer:
     """Owns an iql_handle; methods forward to the C entry points."""
 
@@ -302,6 +352,11 @@ class IqlTrainer:
                       out_grad_norm=None, stream=None):
         iql_train_step_aw(self.h, states, q_taken, batch, q_all, num_actions, beta, out_pi, out_v, out_loss,
                           out_grad_norm, stream)
+
+    def aux_step(self, her, states, q_taken, batch, q_all=None, num_actions=0, beta=0.0, out_pi=None, out_v=None,
+                 out_loss=None, out_grad_norm=None, budget=None, stream=None):
+        iql_aux_step(self.h, her, states, q_taken, batch, q_all, num_actions, beta, out_pi, out_v, out_loss,
+                     out_grad_norm, budget, stream)
 
     def compute_gradients(self, states, q_taken, batch, out_v=None, stream=None):
         iql_compute_gradients(self.h, states, q_taken, batch, out_v, stream)

@@ -181,6 +181,14 @@ static int check_step_args(iql_handle h, const void* states, const float* q_take
     return IQLH_OK;
 }
 
+static int check_policy_args(const float* q_all, int32_t num_actions, float beta, const float* out_pi,
+                             const float* out_v) {
+    if (!q_all || !out_pi || !out_v) return fail(IQLH_EINVAL, "policy: q_all, out_pi and out_v are required");
+    if (num_actions < 1 || num_actions > 64) return fail(IQLH_EINVAL, "num_actions must be in [1, 64]");
+    if (!std::isfinite(beta)) return fail(IQLH_EINVAL, "beta must be finite");
+    return IQLH_OK;
+}
+
 static AdamHyper adam_hyper(const iqlh_config& c) {
     return AdamHyper{c.lr, c.beta1, c.beta2, c.eps, c.weight_decay, c.max_grad_norm, c.weight_clamp_max_abs};
 }
@@ -234,9 +242,8 @@ int iql_train_step_aw(iql_handle h, const void* states, const float* q_taken, in
                       float* out_loss, float* out_grad_norm, void* stream) {
     int rc = check_step_args(h, states, q_taken, batch);
     if (rc) return rc;
-    if (!q_all || !out_pi || !out_v) return fail(IQLH_EINVAL, "iql_train_step_aw: q_all, out_pi and out_v are required");
-    if (num_actions < 1 || num_actions > 64) return fail(IQLH_EINVAL, "num_actions must be in [1, 64]");
-    if (!std::isfinite(beta)) return fail(IQLH_EINVAL, "beta must be finite");
+    rc = check_policy_args(q_all, num_actions, beta, out_pi, out_v);
+    if (rc) return rc;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if (iql_fused_policy(h->dims, num_actions)) {
@@ -321,8 +328,8 @@ int iql_aw_policy(const float* q, const float* v, int32_t num_groups, int32_t ba
     return IQLH_OK;
 }
 
-int her_relabel(const her_config* cfg, const her_buffer* buf, const int32_t* source_idx, int32_t n,
-                uint64_t seed, const int64_t* d_step, const her_out* out, void* stream) {
+static int make_her_args(const her_config* cfg, const her_buffer* buf, const int32_t* source_idx, int32_t n,
+                         uint64_t seed, const int64_t* d_step, const her_out* out, HerArgs* ap) {
     if (!cfg || !buf || !out) return fail(IQLH_EINVAL, "her_relabel: NULL argument struct");
     if (n < 0) return fail(IQLH_EINVAL, "her_relabel: n < 0");
     if (cfg->state_dim < 1) return fail(IQLH_EINVAL, "her_relabel: state_dim < 1");
@@ -339,21 +346,31 @@ int her_relabel(const her_config* cfg, const her_buffer* buf, const int32_t* sou
     if (out->states_dtype != IQLH_F32 && out->states_dtype != IQLH_BF16)
         return fail(IQLH_EINVAL, "her_relabel: bad out.states_dtype");
     if (out->states_ld < cfg->state_dim) return fail(IQLH_EINVAL, "her_relabel: out.states_ld < state_dim");
+    HerArgs& a = *ap;
+    std::memset(&a, 0, sizeof(a));
+    a.n = n;
     if (n == 0) return IQLH_OK;
     if (!buf->states || !buf->next_states || !source_idx || !out->states || !out->rewards)
         return fail(IQLH_EINVAL, "her_relabel: NULL device pointer");
     if ((out->actions && !buf->actions) || (out->dones && !buf->dones))
         return fail(IQLH_EINVAL, "her_relabel: out.actions/out.dones need buf.actions/buf.dones");
-    HerArgs a;
     a.states = buf->states; a.next_states = buf->next_states; a.actions = buf->actions; a.dones = buf->dones;
     a.episode_ends = buf->episode_ends; a.source_idx = source_idx; a.d_step = d_step;
     a.donor_out = out->donor_idx; a.out_states = out->states; a.out_next_states = out->next_states;
     a.out_actions = out->actions; a.out_rewards = out->rewards; a.out_dones = out->dones; a.flags = out->d_flags;
     a.buffer_size = buf->buffer_size; a.out_ld = out->states_ld; a.seed = seed;
-    a.num_episodes = buf->num_episodes; a.n = n;
+    a.num_episodes = buf->num_episodes;
     a.S = cfg->state_dim; a.G = cfg->goal_dim; a.strategy = cfg->strategy;
     a.out_bf16 = out->states_dtype == IQLH_BF16;
     a.threshold = cfg->goal_threshold; a.reward_hit = cfg->reward_hit; a.reward_miss = cfg->reward_miss;
+    return IQLH_OK;
+}
+
+int her_relabel(const her_config* cfg, const her_buffer* buf, const int32_t* source_idx, int32_t n,
+                uint64_t seed, const int64_t* d_step, const her_out* out, void* stream) {
+    HerArgs a;
+    int rc = make_her_args(cfg, buf, source_idx, n, seed, d_step, out, &a);
+    if (rc || n == 0) return rc;
     hipError_t e = launch_her_relabel(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "her_relabel launch");
     return IQLH_OK;
@@ -369,10 +386,10 @@ int grad_budget_workspace_bytes(int64_t n, int32_t num_sources, size_t* bytes) {
     return IQLH_OK;
 }
 
-int grad_budget_accumulate(float* grad_buf, const float* const* sources, const float* fractions,
-                           const float* alphas, int32_t num_sources, int64_t n, float max_grad_norm,
-                           float* out_norms, const iqlh_adam* adam, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+static int make_budget_args(float* grad_buf, const float* const* sources, const float* fractions,
+                            const float* alphas, int32_t num_sources, int64_t n, float max_grad_norm,
+                            float* out_norms, const iqlh_adam* adam, void* workspace, size_t workspace_bytes,
+                            BudgetArgs* bp) {
     size_t need = 0;
     int rc = grad_budget_workspace_bytes(n, num_sources, &need);
     if (rc) return rc;
@@ -381,8 +398,9 @@ int grad_budget_accumulate(float* grad_buf, const float* const* sources, const f
     if (workspace_bytes < need) return fail(IQLH_EINVAL, "workspace too small: %zu < %zu", workspace_bytes, need);
     if (!(max_grad_norm > 0.f) || !std::isfinite(max_grad_norm))
         return fail(IQLH_EINVAL, "max_grad_norm must be finite and > 0");
-    SourceSet s;
-    std::memset(&s, 0, sizeof(s));
+    BudgetArgs& b = *bp;
+    std::memset(&b, 0, sizeof(b));
+    SourceSet& s = b.s;
     s.k = num_sources;
     for (int j = 0; j < num_sources; ++j) {
         if (!sources[j]) return fail(IQLH_EINVAL, "sources[%d] is NULL", j);
@@ -393,7 +411,6 @@ int grad_budget_accumulate(float* grad_buf, const float* const* sources, const f
         s.frac[j] = fractions[j];
         s.alpha[j] = alphas[j];
     }
-    AdamHyper hp{};
     if (adam) {
         if (!adam->params || !adam->m || !adam->v || !adam->t)
             return fail(IQLH_EINVAL, "adam: params, m, v and t must be non-NULL");
@@ -402,14 +419,62 @@ int grad_budget_accumulate(float* grad_buf, const float* const* sources, const f
         if (!finite_pos(adam->eps) || !std::isfinite(adam->lr) || !(adam->lr >= 0.f))
             return fail(IQLH_EINVAL, "adam: bad eps or lr");
         if (!(adam->max_grad_norm > 0.f)) return fail(IQLH_EINVAL, "adam: max_grad_norm must be > 0");
-        hp = AdamHyper{adam->lr, adam->beta1, adam->beta2, adam->eps, adam->weight_decay, adam->max_grad_norm,
-                       adam->weight_clamp_max_abs};
+        b.hp = AdamHyper{adam->lr, adam->beta1, adam->beta2, adam->eps, adam->weight_decay, adam->max_grad_norm,
+                         adam->weight_clamp_max_abs};
+        b.params = adam->params;
+        b.m = adam->m;
+        b.v = adam->v;
+        b.t = adam->t;
+        b.flags = adam->d_flags;
     }
-    hipError_t e = launch_budget(grad_buf, s, n, max_grad_norm, out_norms, adam ? adam->params : nullptr,
-                                 adam ? adam->m : nullptr, adam ? adam->v : nullptr, adam ? adam->t : nullptr,
-                                 adam ? adam->d_flags : nullptr, adam ? &hp : nullptr, (float*)workspace,
-                                 (hipStream_t)stream);
+    b.n = n;
+    b.mgn = max_grad_norm;
+    b.grad = grad_buf;
+    b.out_norms = out_norms;
+    b.work = (float*)workspace;
+    return IQLH_OK;
+}
+
+int grad_budget_accumulate(float* grad_buf, const float* const* sources, const float* fractions,
+                           const float* alphas, int32_t num_sources, int64_t n, float max_grad_norm,
+                           float* out_norms, const iqlh_adam* adam, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    BudgetArgs b;
+    int rc = make_budget_args(grad_buf, sources, fractions, alphas, num_sources, n, max_grad_norm, out_norms,
+                              adam, workspace, workspace_bytes, &b);
+    if (rc) return rc;
+    hipError_t e = launch_budget(b.grad, b.s, b.n, b.mgn, b.out_norms, b.params, b.m, b.v, b.t, b.flags,
+                                 b.params ? &b.hp : nullptr, b.work, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "grad_budget_accumulate launch");
+    return IQLH_OK;
+}
+
+int iql_aux_step(iql_handle h, const iqlh_her_step* her, const void* states, const float* q_taken,
+                 int32_t batch, const float* q_all, int32_t num_actions, float beta, float* out_pi,
+                 float* out_v, float* out_loss, float* out_grad_norm, const iqlh_budget_step* budget,
+                 void* stream) {
+    int rc = check_step_args(h, states, q_taken, batch);
+    if (rc) return rc;
+    if (q_all) {
+        rc = check_policy_args(q_all, num_actions, beta, out_pi, out_v);
+        if (rc) return rc;
+    }
+    HerArgs ha;
+    if (her) {
+        rc = make_her_args(her->cfg, her->buf, her->source_idx, her->n, her->seed, h->buf.step, her->out, &ha);
+        if (rc) return rc;
+    }
+    BudgetArgs ba;
+    if (budget) {
+        rc = make_budget_args(budget->grad_buf, budget->sources, budget->fractions, budget->alphas,
+                              budget->num_sources, budget->n, budget->max_grad_norm, budget->out_norms,
+                              budget->adam, budget->workspace, budget->workspace_bytes, &ba);
+        if (rc) return rc;
+    }
+    hipError_t e = launch_aux_step(h->dims, h->buf, adam_hyper(h->cfg), h->cfg.tau, her ? &ha : nullptr, states,
+                                   h->cfg.states_ld, q_taken, batch, q_all, num_actions, beta, out_pi, out_v,
+                                   out_loss, out_grad_norm, budget ? &ba : nullptr, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "iql_aux_step launch");
     return IQLH_OK;
 }
 

@@ -1,0 +1,132 @@
+// Block-level bodies of the IQL gradient reduction and clipped Adam, shared
+// by their own launches and by the merged whole-step launches.  The method is
+// described in iql.hip.
+#pragma once
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace iqlh {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// fp32 master weight -> operand-typed shadow (bfloat16: round to nearest
+// even, v_cvt_pk_bf16_f32)
+template <typename T> IQLH_DEV T to_shadow(float x);
+template <> IQLH_DEV float to_shadow<float>(float x) { return x; }
+template <> IQLH_DEV uint16_t to_shadow<uint16_t>(float x) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(f2{x, 0.f}, b2)) & 0xFFFFu);
+}
+
+// Sums the per-workgroup partials of every parameter in a fixed order (slice
+// sl of a block adds workgroups sl, sl + 8, ... in turn; the eight slice sums
+// are then added in slice order), writes grad and per-block sums of squares,
+// and, in block 0, the mean loss and the t / step-counter increments.  Each
+// thread streams float4 quads of four parameters, so a wave keeps many
+// independent 16-byte loads in flight.
+constexpr int kRedParams = 128;
+constexpr int kRedSlices = 8;
+
+// Block bx (of rb per group) of group g.
+IQLH_DEV void iql_reduce_block(const float* __restrict__ part, const float* __restrict__ loss_part, int nwg,
+                               int nloss, int64_t P, int64_t Pp, float invB, float* __restrict__ grad,
+                               float* __restrict__ sq_part, int rb, int32_t* __restrict__ tcount,
+                               int64_t* __restrict__ step, float* __restrict__ out_loss,
+                               int32_t* __restrict__ flags, int bx, int g) {
+    __shared__ f32x4 red[kRedSlices][32];
+    __shared__ float wred[4];
+    const int tid = threadIdx.x, q = tid & 31, sl = tid >> 5;
+    const int64_t p0 = (int64_t)bx * kRedParams + 4 * q;  // < Pp
+    const float* src = part + (int64_t)g * nwg * Pp + p0;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int w = sl; w < nwg; w += kRedSlices) acc += *(const f32x4*)(src + (int64_t)w * Pp);
+    red[sl][q] = acc;
+    __syncthreads();
+    float sq = 0.f;
+    if (sl == 0) {
+        f32x4 s = red[0][q];
+#pragma unroll
+        for (int i = 1; i < kRedSlices; ++i) s += red[i][q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (p0 + e < P) {
+                grad[(int64_t)g * P + p0 + e] = s[e];
+                sq = fmaf(s[e], s[e], sq);
+            }
+        }
+    }
+    sq = block_sum<256>(sq, wred);
+    if (tid == 0) sq_part[(int64_t)g * rb + bx] = sq;
+    if (bx == 0) {
+        float l = 0.f;
+        for (int w = tid; w < nloss; w += 256) l += loss_part[(int64_t)g * nloss + w];
+        l = block_sum<256>(l, wred);
+        if (tid == 0) {
+            const float loss = l * invB;
+            if (out_loss) out_loss[g] = loss;
+            if (!isfinite(loss)) set_flag(flags, 0x4);
+            tcount[g] += 1;
+            if (g == 0) *step += 1;
+        }
+    }
+}
+
+// Clip and Adam over the parameters of group g, block bx of nbx; refreshes
+// the operand-typed W1 / W2 / W2^T shadows of the updated weights and zeroes
+// grad.
+template <typename T>
+IQLH_DEV void iql_adam_block(const IqlDims& d, const IqlBuffers& b, const AdamHyper& hp,
+                             float* __restrict__ out_gnorm, int rb, int bx, int g, int nbx) {
+    __shared__ float red[4];
+    const int64_t P = d.P;
+    float a = 0.f;
+    for (int i = threadIdx.x; i < rb; i += 256) a += b.sq_part[(int64_t)g * rb + i];
+    const float nrm = sqrtf(block_sum<256>(a, red));
+    if (bx == 0 && threadIdx.x == 0 && out_gnorm) out_gnorm[g] = nrm;
+    const float c = !isfinite(nrm) ? __int_as_float(0x7FC00000)
+                                   : ((nrm > hp.max_grad_norm && nrm > 0.f) ? hp.max_grad_norm / nrm : 1.f);
+    const float tt = (float)b.t[g];
+    const float bc1 = 1.f - powf(hp.beta1, tt), bc2 = 1.f - powf(hp.beta2, tt);
+    const float decay = 1.f - hp.lr * hp.weight_decay;
+    const int H = d.H, S = d.S, SP = d.S_pad;
+    const int64_t ow2 = (int64_t)H * S + H, ow2e = ow2 + (int64_t)H * H;
+    float* prm = b.params + (int64_t)g * P;
+    float* gr = b.grad + (int64_t)g * P;
+    float* m = b.m + (int64_t)g * P;
+    float* v = b.v + (int64_t)g * P;
+    T* w1s = (T*)b.w1s + (int64_t)g * H * SP;
+    T* w2s = (T*)b.w2s + (int64_t)g * H * H;
+    T* w2ts = (T*)b.w2ts + (int64_t)g * H * H;
+    bool bad = false;
+    for (int64_t i = (int64_t)bx * 256 + threadIdx.x; i < P; i += (int64_t)nbx * 256) {
+        const float gi = gr[i] * c;
+        gr[i] = 0.f;
+        float p = prm[i];
+        if (isfinite(gi)) {
+            const float mi = hp.beta1 * m[i] + (1.f - hp.beta1) * gi;
+            const float vi = hp.beta2 * v[i] + (1.f - hp.beta2) * gi * gi;
+            const float mh = mi / bc1, vh = vi / bc2;
+            if (hp.weight_decay != 0.f) p *= decay;
+            p -= hp.lr * mh / (sqrtf(vh) + hp.eps);
+            if (hp.clamp > 0.f) p = fminf(fmaxf(p, -hp.clamp), hp.clamp);
+            prm[i] = p;
+            m[i] = mi;
+            v[i] = vi;
+        } else {
+            bad = true;
+        }
+        if (i < (int64_t)H * S) {
+            const int64_t r = i / S, cc = i - r * S;
+            w1s[r * SP + cc] = to_shadow<T>(p);
+        } else if (i >= ow2 && i < ow2e) {
+            const int64_t q = i - ow2, r = q / H, cc = q - r * H;
+            w2s[q] = to_shadow<T>(p);
+            w2ts[cc * H + r] = to_shadow<T>(p);
+        }
+    }
+    if (bad) set_flag(b.flags, 0x1);
+}
+
+}  // namespace iqlh

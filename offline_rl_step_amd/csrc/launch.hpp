@@ -114,5 +114,35 @@ hipError_t launch_iql_layered_fwd_bwd(const IqlDims& d, const IqlBuffers& b, con
                                       const void* states, int64_t ld, const float* q, int B,
                                       float* out_v, hipStream_t stream);
 hipError_t launch_iql_refresh_shadows(const IqlDims& d, const IqlBuffers& b, hipStream_t stream);
+// workgroup and loss partials that a batch of B rows leaves for the reduction
+bool iql_partial_counts(const IqlDims& d, int B, int* nwg, int* nloss);
+int iql_adam_blocks(int64_t P);
+
+// ------------------------------------------------------- whole step
+// One pass of the hot path in four launches:
+//   A  HER relabelling + budget source norms   (independent of each other)
+//   B  fused V forward/backward (+ AW policy)   (reads the relabelled rows)
+//   C  IQL partial reduction + budget SAXPY
+//   D  IQL clipped Adam + budget clipped Adam (or the combined norm only)
+// `her` and `budget` may be null (that part is skipped).
+struct BudgetArgs {
+    SourceSet s;
+    int64_t n;
+    float mgn;
+    float* grad;
+    float* out_norms;
+    float* work;
+    // flat Adam over grad (params null: accumulation only)
+    float* params;
+    float* m;
+    float* v;
+    int32_t* t;
+    int32_t* flags;
+    AdamHyper hp;
+};
+hipError_t launch_aux_step(const IqlDims& d, const IqlBuffers& b, const AdamHyper& hp, const float* tau,
+                           const HerArgs* her, const void* states, int64_t ld, const float* q, int B,
+                           const float* q_all, int A, float beta, float* out_pi, float* out_v,
+                           float* out_loss, float* out_gnorm, const BudgetArgs* budget, hipStream_t stream);
 
 }  // namespace iqlh

@@ -1,0 +1,178 @@
+// The whole auxiliary step in four launches.  The pages run HER, the IQL
+// update and the budgeted accumulation as separate kernels ("GPU IQL + HER
+// Porting Plan", sections "Phase 3: Combined IQL + HER" and "How HER
+// Interacts with GPU PER"; "Gradient Stability -- Proper Multi-Task Gradient
+// Isolation + Full Spectral Norm", section "Task 1"); HER and the IQL value
+// net share no state beyond the relabelled rows, and the budgeted
+// accumulation touches neither.  Each small pass is too short to cover a
+// launch, so here
+// independent passes share a launch, each taking a contiguous range of its
+// blocks (a block-uniform branch, no divergence inside a wave):
+//   A  HER rows                 | budget: per-source sums of squares
+//   B  fused V forward/backward and advantage-weighted policy
+//   C  IQL: fixed-order sum of the workgroup partials | budget: clip + SAXPY
+//   D  IQL: clip + Adam + shadows | budget: clip + Adam (or the norm only)
+// Results are bit-for-bit those of the separate launches: every block runs
+// the same block function with the same block index and count.
+#include "budget_block.hpp"
+#include "her_block.hpp"
+#include "iql_update.hpp"
+#include "launch.hpp"
+
+namespace iqlh {
+
+struct NormsPart {
+    SourceSet s;
+    int64_t n;
+    float* partials;
+    int vec, nb;
+};
+
+__global__ __launch_bounds__(256) void step_her_norms_kernel(HerArgs her, int her_blocks, NormsPart np) {
+    const int bx = blockIdx.x;
+    if (bx < her_blocks) her_block(her, bx);
+    else norms_block(np.s, np.n, np.vec, np.partials, bx - her_blocks, np.nb);
+}
+
+struct ReducePart {
+    const float* part;
+    const float* loss_part;
+    float* grad;
+    float* sq_part;
+    int32_t* tcount;
+    int64_t* step;
+    float* out_loss;
+    int32_t* flags;
+    int64_t P, Pp;
+    float invB;
+    int nwg, nloss, rb, G;
+};
+struct SaxpyPart {
+    SourceSet s;
+    int64_t n;
+    const float* partials;
+    float* grad;
+    float* gpart;
+    float* out_norms;
+    int32_t* adam_t;
+    float mgn;
+    int vec, nb;
+};
+
+__global__ __launch_bounds__(256) void step_reduce_saxpy_kernel(ReducePart r, SaxpyPart x) {
+    const int bx = blockIdx.x, nr = r.rb * r.G;
+    if (bx < nr) {
+        iql_reduce_block(r.part, r.loss_part, r.nwg, r.nloss, r.P, r.Pp, r.invB, r.grad, r.sq_part, r.rb,
+                         r.tcount, r.step, r.out_loss, r.flags, bx % r.rb, bx / r.rb);
+    } else {
+        saxpy_block(x.s, x.n, x.vec, x.mgn, x.partials, x.grad, x.gpart, x.out_norms, x.adam_t, bx - nr, x.nb);
+    }
+}
+
+struct FlatPart {
+    float* params;  // null: the combined norm only (one block)
+    float* grad;
+    float* m;
+    float* v;
+    const int32_t* t;
+    const float* gpart;
+    float* out_norm;
+    int32_t* flags;
+    AdamHyper hp;
+    int64_t n;
+    int vec, nb;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void step_adam_kernel(IqlDims d, IqlBuffers b, AdamHyper hp,
+                                                        float* __restrict__ out_gnorm, int rb, int ab,
+                                                        FlatPart f) {
+    const int bx = blockIdx.x, na = ab * d.G;
+    if (bx < na) {
+        iql_adam_block<T>(d, b, hp, out_gnorm, rb, bx % ab, bx / ab, ab);
+    } else if (f.params) {
+        adam_flat_block(f.params, f.grad, f.m, f.v, f.t, f.gpart, f.nb, f.n, f.vec, f.hp, f.out_norm, f.flags,
+                        bx - na, f.nb);
+    } else {
+        norm_finalize_block(f.gpart, f.nb, f.out_norm);
+    }
+}
+
+static bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+hipError_t launch_aux_step(const IqlDims& d, const IqlBuffers& b, const AdamHyper& hp, const float* tau,
+                           const HerArgs* her, const void* states, int64_t ld, const float* q, int B,
+                           const float* q_all, int A, float beta, float* out_pi, float* out_v,
+                           float* out_loss, float* out_gnorm, const BudgetArgs* bud, hipStream_t stream) {
+    int nwg, nloss;
+    if (!iql_partial_counts(d, B, &nwg, &nloss)) return hipErrorInvalidValue;
+    const int nb = bud ? budget_num_blocks(bud->n) : 0;
+    int vec = 0;
+    float* partials = nullptr;
+    float* gpart = nullptr;
+    if (bud) {
+        partials = bud->work;
+        gpart = bud->work + (int64_t)bud->s.k * nb;
+        vec = al16(bud->grad);
+        for (int j = 0; j < bud->s.k; ++j) vec = vec && al16(bud->s.ptr[j]);
+    }
+    const bool flat_adam = bud && bud->params;
+
+    // A: HER + budget norms
+    const int her_blocks = (her && her->n > 0) ? (her->n + 31) / 32 : 0;
+    if (her_blocks + nb > 0) {
+        HerArgs ha{};
+        if (her_blocks) ha = *her;
+        NormsPart np{};
+        if (bud) np = NormsPart{bud->s, bud->n, partials, vec, nb};
+        hipLaunchKernelGGL(step_her_norms_kernel, dim3(her_blocks + nb), dim3(256), 0, stream, ha, her_blocks,
+                           np);
+    }
+
+    // B: fused forward/backward (+ policy)
+    hipError_t e;
+    const bool fused_pi = q_all && iql_fused_policy(d, A);
+    if (fused_pi) {
+        e = launch_iql_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream, nullptr, nullptr, q_all, A, beta,
+                               out_pi);
+    } else {
+        e = launch_iql_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream);
+        if (e == hipSuccess && q_all) e = launch_aw_policy(q_all, out_v, d.G, B, A, beta, out_pi, stream);
+    }
+    if (e != hipSuccess) return e;
+
+    // C: reduce + SAXPY
+    const int rb = iql_reduce_blocks(d.P);
+    ReducePart rp{b.part, b.loss_part, b.grad, b.sq_part, b.t, b.step, out_loss, b.flags, d.P, d.Pp,
+                  1.f / (float)B, nwg, nloss, rb, d.G};
+    SaxpyPart sp{};
+    if (bud)
+        sp = SaxpyPart{bud->s, bud->n, partials, bud->grad, gpart, bud->out_norms,
+                       flat_adam ? bud->t : (int32_t*)nullptr, bud->mgn, vec, nb};
+    hipLaunchKernelGGL(step_reduce_saxpy_kernel, dim3(rb * d.G + nb), dim3(256), 0, stream, rp, sp);
+
+    // D: both Adam updates
+    const int ab = iql_adam_blocks(d.P);
+    FlatPart fp{};
+    int extra = 0;
+    if (flat_adam) {
+        const int fvec = al16(bud->grad) && al16(bud->params) && al16(bud->m) && al16(bud->v);
+        fp = FlatPart{bud->params, bud->grad, bud->m, bud->v, bud->t, gpart,
+                      bud->out_norms ? bud->out_norms + bud->s.k : nullptr, bud->flags, bud->hp, bud->n, fvec, nb};
+        extra = nb;
+    } else if (bud && bud->out_norms) {
+        fp.gpart = gpart;
+        fp.nb = nb;
+        fp.out_norm = bud->out_norms + bud->s.k;
+        extra = 1;
+    }
+    if (d.dtype == 1)
+        hipLaunchKernelGGL(step_adam_kernel<uint16_t>, dim3(ab * d.G + extra), dim3(256), 0, stream, d, b, hp,
+                           out_gnorm, rb, ab, fp);
+    else
+        hipLaunchKernelGGL(step_adam_kernel<float>, dim3(ab * d.G + extra), dim3(256), 0, stream, d, b, hp,
+                           out_gnorm, rb, ab, fp);
+    return hipGetLastError();
+}
+
+}  // namespace iqlh

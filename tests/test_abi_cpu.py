@@ -39,6 +39,44 @@ def test_struct_sizes_match_header_layout(m):
     assert ctypes.sizeof(m.HerBuffer) == 72
     assert ctypes.sizeof(m.HerOut) == 72
     assert ctypes.sizeof(m.Adam) == 72
+    assert ctypes.sizeof(m.HerStep) == 48
+    assert ctypes.sizeof(m.BudgetStep) == 80
+
+
+STRUCTS = {"iqlh_config": "IqlConfig", "her_config": "HerConfig", "her_buffer": "HerBuffer",
+           "her_out": "HerOut", "iqlh_adam": "Adam", "iqlh_her_step": "HerStep",
+           "iqlh_budget_step": "BudgetStep"}
+
+
+def test_binding_structs_match_the_c_compiler(m, tmp_path):
+    """Every field of every binding struct sits at the offset gcc gives it."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "iqlher.h"', "int main(void) {"]
+    for c_name, py_name in STRUCTS.items():
+        cls = getattr(m, py_name)
+        lines.append(f'printf("{c_name} sizeof %zu\\n", sizeof({c_name}));')
+        for f in cls._fields_:
+            lines.append(f'printf("{c_name} {f[0]} %zu\\n", offsetof({c_name}, {f[0]}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                    str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {}
+    for ln in out:
+        if ln.strip():
+            a, b, c = ln.split()
+            got[(a, b)] = int(c)
+    for c_name, py_name in STRUCTS.items():
+        cls = getattr(m, py_name)
+        assert got[(c_name, "sizeof")] == ctypes.sizeof(cls), c_name
+        for f in cls._fields_:
+            assert got[(c_name, f[0])] == getattr(cls, f[0]).offset, (c_name, f[0])
 
 
 def test_num_params(m):
@@ -115,6 +153,8 @@ def test_host_validation_of_kernel_entry_points(m):
     assert rc == m.EINVAL
     rc = m._lib_budget(ctypes.c_void_p(16), srcs, fr, fr, 4, 100, 1.0, None, None, ctypes.c_void_p(16), 4, None)
     assert rc == m.EINVAL and "workspace" in m.last_error()
-    # train step on a NULL handle
+    # train step / whole step on a NULL handle
     assert m._lib_iql_train_step(None, None, None, 1, None, None, None, None) == m.EINVAL
+    assert m._lib_iql_aux_step(None, None, None, None, 1, None, 0, 0.0, None, None, None, None, None,
+                               None) == m.EINVAL
     assert m._lib_iql_step_counter(None) is None

@@ -1,0 +1,232 @@
+"""GPU parity of iql_aux_step, the whole step in four launches.
+
+The whole-step call must give, bit for bit, what her_relabel +
+iql_train_step_aw + grad_budget_accumulate give when called one after the
+other (the same block functions run in both), on every output and on the
+state it leaves behind, over several steps; and one step of it must match
+the oracle directly.  Optional parts (no HER, no policy, no budget, budget
+without Adam) are covered the same way.
+"""
+import numpy as np
+import pytest
+
+import synth
+from tests.gpu_util import adam_update_close, assert_rel, assert_scalar_rel, dev, host, sync, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def m():
+    import offline_rl_step_amd as m
+    return m
+
+
+class Inputs:
+    """Read-only inputs shared by the two rigs."""
+
+    def __init__(self, w, B, n_budget):
+        import torch
+        self.w, self.B = w, B
+        self.n = int(B * w.her_ratio)
+        self.buf = buf = synth.replay_buffer(w)
+        self.src = synth.her_sources(synth.shrink(w, B=B), buf)
+        assert len(self.src) == self.n
+        self.Xn = synth.batch_states(synth.shrink(w, B=B))
+        self.Q, _, self.q = synth.q_values(synth.shrink(w, B=B), buf, self.src)
+        self.inits = synth.group_inits(w)
+        self.sources = synth.budget_sources(w, n=n_budget)
+        self.theta = synth.budget_params(w, n=n_budget)
+        self.n_budget = n_budget
+        self.bf16 = w.dtype == "bf16"
+        self.sdt = torch.bfloat16 if self.bf16 else torch.float32
+        self.t_states, self.t_next = to_dev(buf["states"]), to_dev(buf["next_states"])
+        self.t_actions, self.t_dones = to_dev(buf["actions"]), to_dev(buf["dones"])
+        self.t_ends = to_dev(buf["episode_ends"].astype(np.int32))
+        self.t_src = to_dev(self.src.astype(np.int32))
+        self.t_Q, self.t_q = to_dev(self.Q), to_dev(self.q)
+        self.t_sources = [to_dev(s) for s in self.sources]
+
+
+class Rig:
+    """Outputs and trainer state of one way of running the step."""
+
+    def __init__(self, m, inp, her=True, policy=True, budget=True, adam=True, norms=True):
+        import torch
+        w, B, n, d = inp.w, inp.B, inp.n, dev()
+        self.m, self.inp = m, inp
+        self.use_her, self.use_pi, self.use_budget = her, policy, budget
+        S = w.S
+        self.X = torch.zeros((B, S), dtype=inp.sdt, device=d)
+        self.X[: B - n] = to_dev(inp.Xn, inp.sdt)
+        if not her:  # rows the relabelling would have written: fixed values
+            self.X[B - n:] = to_dev(inp.buf["states"][inp.src], inp.sdt)
+        cfg = m.make_config(S, w.H, B, num_groups=w.groups, compute_dtype=m.BF16 if inp.bf16 else m.F32,
+                            states_ld=S, tau=w.taus, lr=w.lr, max_grad_norm=w.max_grad_norm)
+        self.tr = m.IqlTrainer(cfg, np.concatenate(inp.inits))
+        self.out_v = torch.zeros((w.groups, B), dtype=torch.float32, device=d)
+        self.out_loss = torch.zeros(w.groups, dtype=torch.float32, device=d)
+        self.out_gn = torch.zeros(w.groups, dtype=torch.float32, device=d)
+        self.pi = torch.zeros((w.groups, B, w.A), dtype=torch.float32, device=d)
+        self.rew = torch.zeros(n, dtype=torch.float32, device=d)
+        self.nxt = torch.zeros((n, S), dtype=torch.float32, device=d)
+        self.act = torch.zeros(n, dtype=torch.int32, device=d)
+        self.done = torch.zeros(n, dtype=torch.float32, device=d)
+        self.donor = torch.zeros(n, dtype=torch.int32, device=d)
+        self.hcfg = m.her_config(S, w.G, m.HER_FUTURE)
+        self.hbuf = m.her_buffer(inp.t_states, inp.t_next, inp.t_actions, inp.t_dones, inp.t_ends)
+        tail = self.X.data_ptr() + (B - n) * S * self.X.element_size()
+        self.hout = m.her_out(tail, m.BF16 if inp.bf16 else m.F32, S, self.rew, next_states=self.nxt,
+                              actions=self.act, dones=self.done, donor_idx=self.donor, d_flags=self.tr.flags)
+        P = inp.n_budget
+        self.theta = to_dev(inp.theta)
+        self.tm = torch.zeros(P, dtype=torch.float32, device=d)
+        self.tv = torch.zeros(P, dtype=torch.float32, device=d)
+        self.tt = torch.zeros(1, dtype=torch.int32, device=d)
+        self.grad = torch.zeros(P, dtype=torch.float32, device=d)
+        self.norms = torch.zeros(len(inp.sources) + 1, dtype=torch.float32, device=d) if norms else None
+        self.ws = torch.zeros(m.grad_budget_workspace_bytes(P, len(inp.sources)) // 4, dtype=torch.float32,
+                              device=d)
+        self.adam = m.make_adam(self.theta, self.tm, self.tv, self.tt, lr=w.lr, max_grad_norm=w.max_grad_norm,
+                                d_flags=self.tr.flags) if adam else None
+        self.seed = 20261202
+
+    def separate(self):
+        m, inp, w = self.m, self.inp, self.inp.w
+        if self.use_her:
+            m.her_relabel(self.hcfg, self.hbuf, inp.t_src, inp.n, self.seed, self.tr.step_counter, self.hout)
+        if self.use_pi:
+            self.tr.train_step_aw(self.X, inp.t_q, inp.B, inp.t_Q, w.A, w.beta, self.pi, self.out_v,
+                                  self.out_loss, self.out_gn)
+        else:
+            self.tr.train_step(self.X, inp.t_q, inp.B, self.out_v, self.out_loss, self.out_gn)
+        if self.use_budget:
+            m.grad_budget_accumulate(self.grad, inp.t_sources, w.budget_fractions, (1.0, 1.0, 1.0, 1.0),
+                                     inp.n_budget, w.max_grad_norm, self.norms, self.adam, self.ws)
+
+    def whole(self):
+        m, inp, w = self.m, self.inp, self.inp.w
+        her = m.her_step(self.hcfg, self.hbuf, inp.t_src, inp.n, self.seed, self.hout) if self.use_her else None
+        bud = (m.budget_step(self.grad, inp.t_sources, w.budget_fractions, (1.0, 1.0, 1.0, 1.0), inp.n_budget,
+                             w.max_grad_norm, self.norms, self.adam, self.ws) if self.use_budget else None)
+        if self.use_pi:
+            self.tr.aux_step(her, self.X, inp.t_q, inp.B, inp.t_Q, w.A, w.beta, self.pi, self.out_v,
+                             self.out_loss, self.out_gn, bud)
+        else:
+            self.tr.aux_step(her, self.X, inp.t_q, inp.B, out_v=self.out_v, out_loss=self.out_loss,
+                             out_grad_norm=self.out_gn, budget=bud)
+
+    def tensors(self):
+        import torch
+        out = {"X": self.X, "rew": self.rew, "next": self.nxt, "act": self.act, "done": self.done,
+               "donor": self.donor, "v": self.out_v, "loss": self.out_loss, "gn": self.out_gn, "pi": self.pi,
+               "theta": self.theta, "theta_m": self.tm, "theta_v": self.tv, "theta_t": self.tt,
+               "grad": self.grad}
+        if self.norms is not None:
+            out["norms"] = self.norms
+        P = self.tr.n_params
+        for g in range(self.inp.w.groups):
+            p = torch.zeros(P, dtype=torch.float32, device=dev())
+            mm, vv = torch.zeros_like(p), torch.zeros_like(p)
+            t = torch.zeros(1, dtype=torch.int32, device=dev())
+            self.tr.get_state(g, p, mm, vv, t)
+            out.update({f"params{g}": p, f"m{g}": mm, f"v{g}": vv, f"t{g}": t})
+        return out
+
+
+def _bitwise_equal(a, b, what):
+    import torch
+    ta, tb = a.tensors(), b.tensors()
+    sync()
+    for k in ta:
+        x, y = ta[k], tb[k]
+        if x.dtype == torch.bfloat16:
+            x, y = x.view(torch.int16), y.view(torch.int16)
+        elif x.dtype == torch.float32:
+            x, y = x.view(torch.int32), y.view(torch.int32)
+        assert torch.equal(x, y), f"{what}: {k} differs"
+
+
+def _run_pair(m, inp, steps=3, **kw):
+    a, b = Rig(m, inp, **kw), Rig(m, inp, **kw)
+    for s in range(steps):
+        a.separate()
+        b.whole()
+        _bitwise_equal(a, b, f"step {s + 1} {kw}")
+    for r in (a, b):
+        rc, flags = r.tr.status()
+        assert rc == m.OK and flags == 0
+        r.tr.close()
+
+
+@pytest.fixture(scope="module")
+def bench_inputs():
+    w = synth.WORKLOADS["b16384_s128_h128_bf16_g2_budget"]
+    return Inputs(w, w.B, w.n_budget)
+
+
+def test_whole_step_equals_separate_calls_b16384(m, bench_inputs):
+    """The production shape (batch 16384, two bf16 groups, policy fused,
+    budget over 132612 parameters), three steps: the step counter drives the
+    relabelling draws, Adam's t and the budget's t advance."""
+    _run_pair(m, bench_inputs, steps=3)
+
+
+@pytest.mark.parametrize("kw", [dict(her=False), dict(policy=False), dict(budget=False),
+                                dict(adam=False), dict(adam=False, norms=False),
+                                dict(her=False, policy=False, budget=False)])
+def test_whole_step_optional_parts(m, kw):
+    w = synth.shrink(synth.WORKLOADS["b16384_s128_h128_bf16_g2_budget"], C=1 << 14)
+    _run_pair(m, Inputs(w, 3000, 70001), steps=2, **kw)
+
+
+def test_whole_step_fp32_unfused_policy(m):
+    """fp32 operands: the policy runs as its own kernel after the
+    forward/backward launch; ragged batch and budget lengths."""
+    w = synth.shrink(synth.WORKLOADS["b4096_s42_h128_f32"], A=9, budget=True)
+    _run_pair(m, Inputs(w, 1001, 5003), steps=2)
+
+
+def test_whole_step_layered_shape(m):
+    """A shape beyond the fused tile kernel (hidden 256) goes through the
+    layered GEMM path inside the whole step."""
+    w = synth.shrink(synth.WORKLOADS["b16384_s128_h128_bf16_g2_budget"], S=100, H=256, C=1 << 14)
+    _run_pair(m, Inputs(w, 2500, 4096), steps=2)
+
+
+def test_whole_step_matches_oracle(m):
+    """One whole step on the small fp32 workload against the oracle: HER
+    rows exact, V / loss / parameters within 1e-4, policy within 1e-5, the
+    budgeted gradient's clip bound and the budget parameters' Adam update."""
+    from oracle import aw, budget, her, iql
+    w = synth.shrink(synth.WORKLOADS["tiny_b256_s16_h32"], budget=True)
+    inp = Inputs(w, w.B, 4099)
+    r = Rig(m, inp, adam=True)
+    r.whole()
+    sync()
+    ref_h = her.her_step(inp.buf, inp.src, w.G, her.FUTURE, r.seed, 0)
+    assert np.array_equal(host(r.donor), ref_h["donor_idx"])
+    assert np.array_equal(host(r.rew), ref_h["rewards"])
+    assert np.array_equal(host(r.X)[w.B - inp.n:], ref_h["states"])
+    X = host(r.X).astype(np.float64)
+    hp = iql.AdamHP(lr=w.lr, max_grad_norm=w.max_grad_norm)
+    st = iql.AdamState.fresh(inp.inits[0])
+    ref = iql.train_step(st, X, inp.q, w.S, w.H, w.H, w.taus[0], hp)
+    assert_rel(host(r.out_v[0]), ref.v, 1e-4, "V")
+    assert_scalar_rel(host(r.out_loss)[0], ref.loss, 1e-4, "loss")
+    assert_scalar_rel(host(r.out_gn)[0], ref.grad_norm, 1e-4, "grad norm")
+    p = r.tensors()["params0"]
+    sync()
+    adam_update_close(host(p), st.params, None, w.lr, 1, 1e-4, "params")
+    ref_pi = aw.aw_policy(inp.Q, host(r.out_v[0]), w.beta)
+    assert np.max(np.abs(host(r.pi[0]) - ref_pi)) <= 1e-5
+    g_ref, n_ref, comb_ref, _ = budget.accumulate(inp.sources, w.budget_fractions, (1, 1, 1, 1), w.max_grad_norm)
+    got_norms = host(r.norms)
+    assert_rel(got_norms[:4], n_ref, 1e-5, "source norms")
+    assert_scalar_rel(got_norms[4], comb_ref, 1e-5, "combined norm")
+    th = iql.AdamState.fresh(inp.theta)
+    iql.adam_step(th, g_ref, hp)
+    adam_update_close(host(r.theta), th.params, None, w.lr, 1, 1e-5, "budget params")
+    assert int(host(r.tt)[0]) == 1
+    assert np.all(host(r.grad) == 0)  # consumed by Adam
+    r.tr.close()
