@@ -246,7 +246,11 @@ def her_config(state_dim, goal_dim, strategy, goal_threshold=0.01, reward_hit=1.
 
 
 def her_buffer(states, next_states, actions, dones, episode_ends, buffer_size=None, rewards=None):
+    """HerBuffer over device tensors.  The struct holds raw addresses, so it
+    keeps references to the tensors: they stay allocated while it lives (a
+    captured graph that replays a launch built from it needs that too)."""
     b = HerBuffer()
+    b._keep = (states, next_states, actions, dones, episode_ends, rewards)
     b.states, b.next_states = states.data_ptr(), next_states.data_ptr()
     b.actions = actions.data_ptr() if actions is not None else None
     b.rewards = rewards.data_ptr() if rewards is not None else None
@@ -260,7 +264,9 @@ def her_buffer(states, next_states, actions, dones, episode_ends, buffer_size=No
 
 def her_out(states, states_dtype, states_ld, rewards, next_states=None, actions=None, dones=None,
             donor_idx=None, d_flags=None):
+    """HerOut; keeps references to the tensors it was given (see her_buffer)."""
     o = HerOut()
+    o._keep = (states, rewards, next_states, actions, dones, donor_idx, d_flags)
     o.states = states if isinstance(states, int) else states.data_ptr()
     o.states_dtype, o.states_ld = states_dtype, states_ld
     o.rewards = rewards.data_ptr()
@@ -281,7 +287,9 @@ def grad_budget_workspace_bytes(n, num_sources):
 
 def make_adam(params, m, v, t, lr=3e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
               max_grad_norm=1.0, weight_clamp_max_abs=0.0, d_flags=None):
+    """Adam state struct; keeps references to the tensors (see her_buffer)."""
     a = Adam()
+    a._keep = (params, m, v, t, d_flags)
     a.params, a.m, a.v, a.t = params.data_ptr(), m.data_ptr(), v.data_ptr(), t.data_ptr()
     a.d_flags = None if d_flags is None else (d_flags if isinstance(d_flags, int) else d_flags.data_ptr())
     a.lr, a.beta1, a.beta2, a.eps = lr, beta1, beta2, eps
@@ -305,6 +313,7 @@ def grad_budget_accumulate(grad_buf, sources, fractions, alphas, n, max_grad_nor
 def her_step(cfg, buf, source_idx, n, seed, out):
     """HerStep for iql_aux_step (the HER arguments of her_relabel minus d_step)."""
     st = HerStep()
+    st._keep = (cfg, buf, out, source_idx)
     st.cfg, st.buf, st.out = ctypes.pointer(cfg), ctypes.pointer(buf), ctypes.pointer(out)
     st.source_idx = None if source_idx is None else source_idx.data_ptr()
     st.seed, st.n = seed, n
@@ -315,6 +324,7 @@ def budget_step(grad_buf, sources, fractions, alphas, n, max_grad_norm, out_norm
     """BudgetStep for iql_aux_step (the arguments of grad_budget_accumulate)."""
     k = len(sources)
     st = BudgetStep()
+    st._keep = (grad_buf, tuple(sources), out_norms, adam, workspace)
     st.grad_buf = grad_buf.data_ptr()
     st.sources = (_p * k)(*[x.data_ptr() for x in sources])
     st.fractions = (_f * k)(*fractions)

@@ -34,10 +34,47 @@ IQLH_DEV void st4(float* __restrict__ p, int64_t i, int64_t n, bool vec, f32x4 x
         if (i + e < n) p[i + e] = x[e];
 }
 
+// block_sum of k values per thread at once (one pair of barriers for all k);
+// v[j] becomes the block sum of v[j], in block_sum's order.
+IQLH_DEV void block_sum_k(float (&v)[kMaxSources], int k, float (*red)[kBT / kWave]) {
+#pragma unroll
+    for (int j = 0; j < kMaxSources; ++j)
+        if (j < k) v[j] = wave_sum(v[j]);
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    __syncthreads();
+    if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < kMaxSources; ++j)
+            if (j < k) red[j][w] = v[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kMaxSources; ++j) {
+        float t = 0.f;
+#pragma unroll
+        for (int i = 0; i < kBT / kWave; ++i) t += j < k ? red[j][i] : 0.f;
+        v[j] = t;
+    }
+}
+
+// fold_partials of k consecutive sets of nb partials, all loads in flight
+// together; out[j] equals fold_partials(p + j * nb, nb).
+IQLH_DEV void fold_partials_k(const float* __restrict__ p, int nb, int k, float (&out)[kMaxSources],
+                              float (*red)[kBT / kWave]) {
+#pragma unroll
+    for (int j = 0; j < kMaxSources; ++j) out[j] = 0.f;
+    for (int i = threadIdx.x; i < nb; i += kBT) {
+#pragma unroll
+        for (int j = 0; j < kMaxSources; ++j)
+            if (j < k) out[j] += p[(int64_t)j * nb + i];
+    }
+    block_sum_k(out, k, red);
+}
+
 // Pass 1 for block bx of nb: partial sums of squares of every source.
 IQLH_DEV void norms_block(const SourceSet& s, int64_t n, int vec, float* __restrict__ partials, int bx,
                          int nb) {
-    __shared__ float red[kBT / kWave];
+    __shared__ float red[kMaxSources][kBT / kWave];
     float acc[kMaxSources];
 #pragma unroll
     for (int j = 0; j < kMaxSources; ++j) acc[j] = 0.f;
@@ -51,9 +88,11 @@ IQLH_DEV void norms_block(const SourceSet& s, int64_t n, int vec, float* __restr
             }
         }
     }
-    for (int j = 0; j < s.k; ++j) {
-        const float t = block_sum<kBT>(acc[j], red);
-        if (threadIdx.x == 0) partials[(int64_t)j * nb + bx] = t;
+    block_sum_k(acc, s.k, red);
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int j = 0; j < kMaxSources; ++j)
+            if (j < s.k) partials[(int64_t)j * nb + bx] = acc[j];
     }
 }
 
@@ -83,7 +122,7 @@ IQLH_DEV void saxpy_block(const SourceSet& s, int64_t n, int vec, float mgn, con
                           float* __restrict__ grad, float* __restrict__ gpart, float* __restrict__ out_norms,
                           int32_t* __restrict__ adam_t, int bx, int nb) {
     __shared__ float red[kBT / kWave];
-    __shared__ float coef[kMaxSources];
+    __shared__ float redk[kMaxSources][kBT / kWave];
     // this thread's first quad of every source does not depend on the clip
     // scales: load it before folding the norm partials
     const int64_t quads = (n + 3) / 4, stride = (int64_t)nb * kBT;
@@ -92,19 +131,21 @@ IQLH_DEV void saxpy_block(const SourceSet& s, int64_t n, int vec, float mgn, con
 #pragma unroll
     for (int j = 0; j < kMaxSources; ++j)
         pre[j] = (j < s.k && q0 < quads) ? ld4(s.ptr[j], 4 * q0, n, vec) : f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < s.k; ++j) {
-        const float sq = fold_partials(partials + (int64_t)j * nb, nb, red);
-        if (threadIdx.x == 0) {
-            const float nrm = sqrtf(sq);
-            coef[j] = s.alpha[j] * budget_scale(nrm, s.frac[j] * mgn);
-            if (bx == 0 && out_norms) out_norms[j] = nrm;
+    // every thread folds every source's partials (same value in all threads
+    // and blocks) and derives the clip scales itself
+    float c[kMaxSources];
+    fold_partials_k(partials, nb, s.k, c, redk);
+#pragma unroll
+    for (int j = 0; j < kMaxSources; ++j) {
+        if (j < s.k) {
+            const float nrm = sqrtf(c[j]);
+            if (bx == 0 && threadIdx.x == 0 && out_norms) out_norms[j] = nrm;
+            c[j] = s.alpha[j] * budget_scale(nrm, s.frac[j] * mgn);
+        } else {
+            c[j] = 0.f;
         }
     }
     if (bx == 0 && threadIdx.x == 0 && adam_t) *adam_t += 1;
-    __syncthreads();
-    float c[kMaxSources];
-#pragma unroll
-    for (int j = 0; j < kMaxSources; ++j) c[j] = j < s.k ? coef[j] : 0.f;
     float acc = 0.f;
     for (int64_t qd = q0; qd < quads; qd += stride) {
         f32x4 g = {0.f, 0.f, 0.f, 0.f};

@@ -158,3 +158,30 @@ def test_host_validation_of_kernel_entry_points(m):
     assert m._lib_iql_aux_step(None, None, None, None, 1, None, 0, 0.0, None, None, None, None, None,
                                None) == m.EINVAL
     assert m._lib_iql_step_counter(None) is None
+
+
+def test_binding_structs_keep_their_tensors(m):
+    """The structs hold raw addresses; they must keep the tensors alive (a
+    temporary freed after the call and released by the allocator would leave
+    a captured launch reading unmapped memory)."""
+    import gc
+    import weakref
+    import torch
+    t = torch.zeros((8, 4))
+    ref = weakref.ref(t)
+    b = m.her_buffer(t, torch.zeros((8, 4)), None, None, torch.zeros(2, dtype=torch.int32))
+    del t
+    gc.collect()
+    assert ref() is not None and b.states == ref().data_ptr()
+    p = torch.zeros(16)
+    ref = weakref.ref(p)
+    a = m.make_adam(p, torch.zeros(16), torch.zeros(16), torch.zeros(1, dtype=torch.int32))
+    del p
+    gc.collect()
+    assert ref() is not None and a.params == ref().data_ptr()
+    g = torch.zeros(16)
+    ref = weakref.ref(g)
+    st = m.budget_step(g, [torch.zeros(16)], (1.0,), (1.0,), 16, 1.0, None, a, torch.zeros(64))
+    del g
+    gc.collect()
+    assert ref() is not None and st.grad_buf == ref().data_ptr()
