@@ -75,7 +75,7 @@ def fused_flops_per_launch(w):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("iql.hip", "common.hpp"):
+    for f in ("iql.hip", "common.hpp", "her_block.hpp", "iql_update.hpp", "launch.hpp"):
         with open(os.path.join(ROOT, "offline_rl_step_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -157,6 +157,12 @@ class Context:
         w = self.w
         self.tr.aux_step(self.her_step, self.X, self.q, w.B, self.Q, w.A, w.beta, self.pi, self.out_v,
                          self.out_loss, self.out_gn, self.budget_step)
+
+    def time_launches(self, reps):
+        """Mean kernel time (us) of each launch of the whole step."""
+        w = self.w
+        return self.tr.time_aux_step(self.her_step, self.X, self.q, w.B, self.Q, w.A, w.beta, self.pi, self.out_v,
+                                     self.out_loss, self.out_gn, self.budget_step, reps=reps)
 
     def step_separate(self):
         """The same step through the three separate entry points."""
@@ -248,12 +254,14 @@ def main():
     rc, flags = ctx.tr.status()
     ms_per_step = wall * 1e3 / a.steps
 
-    # dominant kernel: the fused forward/backward, timed by its own dispatch events
-    avg_us = ctx.tr_time = m.iql_time_compute_gradients(ctx.tr.h, ctx.X, ctx.q, w.B, a.kernel_reps)
+    # every launch of the step timed by its own dispatch events, on the
+    # stream the step runs on; the dominant one is the forward/backward
+    launch_us = ctx.time_launches(a.kernel_reps)
+    avg_us = launch_us[1]
     flops = fused_flops_per_launch(w)
     achieved = flops / (avg_us * 1e-6) / 1e12
     src_hash = kernel_source_hash()
-    roofline = {"bound": "mfma", "kernel": "iql_fused16_kernel<128,128>", "achieved": achieved,
+    roofline = {"bound": "mfma", "kernel": "iql_fused16_kernel<128,128,xvec>", "achieved": achieved,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                 "traffic": traffic_from_profiles("iql_fused_b16384_s128_h128_g2", src_hash),
                 "avg_kernel_us": avg_us, "flops_per_launch": flops, "source_hash": src_hash}
@@ -268,6 +276,8 @@ def main():
                       "entry_point": "separate calls" if a.separate else "iql_aux_step",
                       "parallelism": "single-gpu"},
            "event_ms_per_step": ev_ms / a.steps, "device_flags": flags, "status": rc,
+           "launch_us": {"relabel_norms": launch_us[0], "fwd_bwd": launch_us[1], "reduce_saxpy": launch_us[2],
+                         "adam": launch_us[3]},
            "roofline": roofline}
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(ctx, a.cpu_seconds, np)

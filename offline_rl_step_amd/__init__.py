@@ -101,6 +101,9 @@ _lib_budget = _sig("grad_budget_accumulate", _i32, [_p, ctypes.POINTER(_p), ctyp
                                                     ctypes.POINTER(Adam), _p, ctypes.c_size_t, _p])
 _lib_iql_aux_step = _sig("iql_aux_step", _i32, [_p, ctypes.POINTER(HerStep), _p, _p, _i32, _p, _i32, _f, _p, _p,
                                                 _p, _p, ctypes.POINTER(BudgetStep), _p])
+_lib_iql_time_aux_step = _sig("iql_time_aux_step", _i32, [_p, ctypes.POINTER(HerStep), _p, _p, _i32, _p, _i32, _f,
+                                                          _p, _p, _p, _p, ctypes.POINTER(BudgetStep), _i32,
+                                                          ctypes.POINTER(_f), _p])
 _lib_last_error = _sig("iqlh_last_error", ctypes.c_char_p, [])
 
 
@@ -347,6 +350,18 @@ def iql_aux_step(h, her, states, q_taken, batch, q_all=None, num_actions=0, beta
                              _stream(stream)), "iql_aux_step")
 
 
+def iql_time_aux_step(h, her, states, q_taken, batch, q_all=None, num_actions=0, beta=0.0, out_pi=None,
+                      out_v=None, out_loss=None, out_grad_norm=None, budget=None, reps=100, stream=None):
+    """Runs `reps` whole steps with per-launch dispatch events; returns the mean
+    duration (us) of launches [relabel+norms, forward/backward, reduce+SAXPY, Adam]."""
+    out = (_f * 4)()
+    _check(_lib_iql_time_aux_step(h, None if her is None else ctypes.byref(her), _ptr(states), _ptr(q_taken), batch,
+                                  _ptr(q_all), num_actions, beta, _ptr(out_pi), _ptr(out_v), _ptr(out_loss),
+                                  _ptr(out_grad_norm), None if budget is None else ctypes.byref(budget), reps, out,
+                                  _stream(stream)), "iql_time_aux_step")
+    return list(out)
+
+
 class IqlTrainer:
     """Owns an iql_handle; methods forward to the C entry points."""
 
@@ -367,6 +382,11 @@ class IqlTrainer:
                  out_loss=None, out_grad_norm=None, budget=None, stream=None):
         iql_aux_step(self.h, her, states, q_taken, batch, q_all, num_actions, beta, out_pi, out_v, out_loss,
                      out_grad_norm, budget, stream)
+
+    def time_aux_step(self, her, states, q_taken, batch, q_all=None, num_actions=0, beta=0.0, out_pi=None,
+                      out_v=None, out_loss=None, out_grad_norm=None, budget=None, reps=100, stream=None):
+        return iql_time_aux_step(self.h, her, states, q_taken, batch, q_all, num_actions, beta, out_pi, out_v,
+                                 out_loss, out_grad_norm, budget, reps, stream)
 
     def compute_gradients(self, states, q_taken, batch, out_v=None, stream=None):
         iql_compute_gradients(self.h, states, q_taken, batch, out_v, stream)

@@ -449,32 +449,77 @@ int grad_budget_accumulate(float* grad_buf, const float* const* sources, const f
     return IQLH_OK;
 }
 
-int iql_aux_step(iql_handle h, const iqlh_her_step* her, const void* states, const float* q_taken,
-                 int32_t batch, const float* q_all, int32_t num_actions, float beta, float* out_pi,
-                 float* out_v, float* out_loss, float* out_grad_norm, const iqlh_budget_step* budget,
-                 void* stream) {
+struct AuxPlan {
+    HerArgs ha;
+    BudgetArgs ba;
+    bool her, budget;
+};
+
+static int plan_aux_step(iql_handle h, const iqlh_her_step* her, const void* states, const float* q_taken,
+                         int32_t batch, const float* q_all, int32_t num_actions, float beta, const float* out_pi,
+                         const float* out_v, const iqlh_budget_step* budget, AuxPlan* p) {
     int rc = check_step_args(h, states, q_taken, batch);
     if (rc) return rc;
     if (q_all) {
         rc = check_policy_args(q_all, num_actions, beta, out_pi, out_v);
         if (rc) return rc;
     }
-    HerArgs ha;
+    p->her = her != nullptr;
+    p->budget = budget != nullptr;
     if (her) {
-        rc = make_her_args(her->cfg, her->buf, her->source_idx, her->n, her->seed, h->buf.step, her->out, &ha);
+        rc = make_her_args(her->cfg, her->buf, her->source_idx, her->n, her->seed, h->buf.step, her->out, &p->ha);
         if (rc) return rc;
     }
-    BudgetArgs ba;
     if (budget) {
         rc = make_budget_args(budget->grad_buf, budget->sources, budget->fractions, budget->alphas,
                               budget->num_sources, budget->n, budget->max_grad_norm, budget->out_norms,
-                              budget->adam, budget->workspace, budget->workspace_bytes, &ba);
+                              budget->adam, budget->workspace, budget->workspace_bytes, &p->ba);
         if (rc) return rc;
     }
-    hipError_t e = launch_aux_step(h->dims, h->buf, adam_hyper(h->cfg), h->cfg.tau, her ? &ha : nullptr, states,
-                                   h->cfg.states_ld, q_taken, batch, q_all, num_actions, beta, out_pi, out_v,
-                                   out_loss, out_grad_norm, budget ? &ba : nullptr, (hipStream_t)stream);
+    return IQLH_OK;
+}
+
+int iql_aux_step(iql_handle h, const iqlh_her_step* her, const void* states, const float* q_taken,
+                 int32_t batch, const float* q_all, int32_t num_actions, float beta, float* out_pi,
+                 float* out_v, float* out_loss, float* out_grad_norm, const iqlh_budget_step* budget,
+                 void* stream) {
+    AuxPlan p;
+    int rc = plan_aux_step(h, her, states, q_taken, batch, q_all, num_actions, beta, out_pi, out_v, budget, &p);
+    if (rc) return rc;
+    hipError_t e = launch_aux_step(h->dims, h->buf, adam_hyper(h->cfg), h->cfg.tau, p.her ? &p.ha : nullptr,
+                                   states, h->cfg.states_ld, q_taken, batch, q_all, num_actions, beta, out_pi,
+                                   out_v, out_loss, out_grad_norm, p.budget ? &p.ba : nullptr, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "iql_aux_step launch");
+    return IQLH_OK;
+}
+
+int iql_time_aux_step(iql_handle h, const iqlh_her_step* her, const void* states, const float* q_taken,
+                      int32_t batch, const float* q_all, int32_t num_actions, float beta, float* out_pi,
+                      float* out_v, float* out_loss, float* out_grad_norm, const iqlh_budget_step* budget,
+                      int32_t reps, float* out_avg_us, void* stream) {
+    AuxPlan p;
+    int rc = plan_aux_step(h, her, states, q_taken, batch, q_all, num_actions, beta, out_pi, out_v, budget, &p);
+    if (rc) return rc;
+    if (reps < 1 || !out_avg_us) return fail(IQLH_EINVAL, "reps must be >= 1 and out_avg_us non-NULL");
+    hipEvent_t ev[8] = {};
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < 8 && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
+    double total[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int r = 0; r < reps && e == hipSuccess; ++r) {
+        e = launch_aux_step(h->dims, h->buf, adam_hyper(h->cfg), h->cfg.tau, p.her ? &p.ha : nullptr, states,
+                            h->cfg.states_ld, q_taken, batch, q_all, num_actions, beta, out_pi, out_v, out_loss,
+                            out_grad_norm, p.budget ? &p.ba : nullptr, (hipStream_t)stream, ev);
+        if (e == hipSuccess) e = hipEventSynchronize(ev[7]);
+        for (int k = 0; k < 4 && e == hipSuccess; ++k) {
+            float ms = 0.f;
+            e = hipEventElapsedTime(&ms, ev[2 * k], ev[2 * k + 1]);
+            total[k] += ms;
+        }
+    }
+    for (int i = 0; i < 8; ++i)
+        if (ev[i]) (void)hipEventDestroy(ev[i]);
+    if (e != hipSuccess) return hip_fail(e, "iql_time_aux_step");
+    for (int k = 0; k < 4; ++k) out_avg_us[k] = (float)(total[k] * 1000.0 / reps);
     return IQLH_OK;
 }
 

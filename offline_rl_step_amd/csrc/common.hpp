@@ -28,14 +28,28 @@ IQLH_DEV uint32_t pack_bf2(float lo, float hi) {
 // key bumped by two Weyl constants between rounds.
 struct u64x4 { uint64_t x, y, z, w; };
 
+// Full 64 x 64 -> 128-bit product, schoolbook on 32-bit halves: four
+// 32 x 32 -> 64 multiply-adds (v_mad_u64_u32) with the partial products
+// shared between the high and the low word.
+IQLH_DEV void mulhilo64(uint64_t a, uint64_t b, uint64_t& hi, uint64_t& lo) {
+    const uint32_t a0 = (uint32_t)a, a1 = (uint32_t)(a >> 32);
+    const uint32_t b0 = (uint32_t)b, b1 = (uint32_t)(b >> 32);
+    const uint64_t p00 = (uint64_t)a0 * b0;
+    const uint64_t t1 = (uint64_t)a0 * b1 + (p00 >> 32);    // < 2^64
+    const uint64_t t2 = (uint64_t)a1 * b0 + (uint32_t)t1;   // < 2^64
+    hi = (uint64_t)a1 * b1 + (t1 >> 32) + (t2 >> 32);
+    lo = (t2 << 32) | (uint32_t)p00;
+}
+
 IQLH_DEV u64x4 philox4x64_10(u64x4 c, uint64_t k0, uint64_t k1) {
     const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
     const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
         if (r > 0) { k0 += W0; k1 += W1; }
-        const uint64_t hi0 = __umul64hi(M0, c.x), lo0 = M0 * c.x;
-        const uint64_t hi1 = __umul64hi(M1, c.z), lo1 = M1 * c.z;
+        uint64_t hi0, lo0, hi1, lo1;
+        mulhilo64(M0, c.x, hi0, lo0);
+        mulhilo64(M1, c.z, hi1, lo1);
         c = u64x4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
     }
     return c;
@@ -71,6 +85,12 @@ IQLH_DEV float block_sum(float v, float* red) {
     for (int i = 0; i < NT / kWave; ++i) s += red[i];
     return s;
 }
+
+// c ? x : 0 by bit masking.  The loaded x is consumed on every path, which
+// keeps the compiler from sinking its load into a lane-dependent branch (a
+// branch whose end then waits for every load the wave has in flight).
+IQLH_DEV float keep_if(bool c, float x) { return __uint_as_float(__float_as_uint(x) & (c ? 0xFFFFFFFFu : 0u)); }
+IQLH_DEV uint32_t keep_if(bool c, uint32_t x) { return x & (c ? 0xFFFFFFFFu : 0u); }
 
 IQLH_DEV void set_flag(int32_t* flags, int32_t bit) {
     if (flags) atomicOr(flags, bit);

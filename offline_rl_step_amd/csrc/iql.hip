@@ -624,43 +624,28 @@ __global__ __launch_bounds__(512) void iql_fused16_kernel(FusedArgs a) {
     float* part = a.part + ((int64_t)g * a.nwg + wg) * a.Pp;
     const float tau = g == 0 ? a.tau0 : a.tau1;
 
-    // ---- S0: weights and small vectors to LDS, this lane's sample row to registers
+    // ---- S0: weights and small vectors to LDS, this lane's sample row to
+    // registers.  A wave waits for a load by draining every load it issued
+    // before it, so loads are issued in the order they are consumed and none
+    // sits behind a lane-dependent branch (indexes are clamped into range,
+    // unused values masked): the weight shadows, the target, b3, Q(s, .),
+    // the W2^T shadow (staged into R1 once W2 is dead), the sample row.
     const int bl = 16 * wv + l16;
     const int b = wg * BT + bl;
     const bool valid = b < B;
-    bf16x8 xf[KU1];
-    {
-        const uint16_t* xr = (const uint16_t*)a.states + (int64_t)b * a.ld;
+    const int bc = valid ? b : B - 1;
+    constexpr int W1_PER_THREAD = H * SP / (NTHR * 8);
+    constexpr int W2_PER_THREAD = H * H / (NTHR * 8);
+    constexpr int W2T_PER_THREAD = H * H / (NTHR * 8);
+    static_assert(W1_PER_THREAD * NTHR * 8 == H * SP && W2_PER_THREAD * NTHR * 8 == H * H, "staging split");
+    u32x4 w1r[W1_PER_THREAD], w2r[W2_PER_THREAD], w2t[W2T_PER_THREAD];
 #pragma unroll
-        for (int u = 0; u < KU1; ++u) {
-            const int k0 = 32 * u + 8 * q;
-            if (XVEC) {
-                xf[u] = valid ? ld8(xr + k0) : O::zero();
-            } else {
-                uint16_t tmp[8];
+    for (int k = 0; k < W1_PER_THREAD; ++k) w1r[k] = *(const u32x4*)(w1s + (tid + k * NTHR) * 8);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) tmp[e] = (valid && k0 + e < S) ? xr[k0 + e] : (uint16_t)0;
-                xf[u] = O::make(tmp);
-            }
-        }
-    }
-    for (int idx = tid * 8; idx < H * SP; idx += NTHR * 8) {
-        const int r = idx / SP, c = idx - r * SP;
-        *(u32x4*)(R0 + r * C::LDW1 + c) = *(const u32x4*)(w1s + idx);
-    }
-    for (int idx = tid * 8; idx < H * H; idx += NTHR * 8) {
-        const int r = idx / H, c = idx - r * H;
-        *(u32x4*)(R1 + r * C::LDW2 + c) = *(const u32x4*)(w2s + idx);
-    }
-    for (int i = tid; i < H; i += NTHR) {
-        sb1[i] = prm[po.b1 + i];
-        sb2[i] = prm[po.b2 + i];
-        sw3[i] = prm[po.w3 + i];
-    }
-    // Loads whose values are needed only later are issued now, so their
-    // latency hides behind layers 1 and 2: the target, b3, and this
-    // thread's share of the W2^T shadow (staged into R1 once W2 is dead).
-    const float qb = valid ? a.q[b] : 0.f;
+    for (int k = 0; k < W2_PER_THREAD; ++k) w2r[k] = *(const u32x4*)(w2s + (tid + k * NTHR) * 8);
+    const int th = tid < H ? tid : 0;
+    const float vb1 = prm[po.b1 + th], vb2 = prm[po.b2 + th], vw3 = prm[po.w3 + th];
+    const float qb = a.q[bc];  // used by valid lanes only
     const float b3 = prm[po.b3];
     // Q(s, .) of this lane's sample for the fused policy: lane group q takes
     // actions q, q + 4, q + 8, q + 12
@@ -668,12 +653,49 @@ __global__ __launch_bounds__(512) void iql_fused16_kernel(FusedArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int act = q + 4 * k;
-        qa[k] = (a.out_pi && valid && act < a.A) ? a.q_all[(int64_t)b * a.A + act] : 0.f;
+        // used by valid lanes and actions < A only
+        qa[k] = a.out_pi ? a.q_all[(int64_t)bc * a.A + min(act, a.A - 1)] : 0.f;
     }
-    constexpr int W2T_PER_THREAD = H * H / (NTHR * 8);
-    u32x4 w2t[W2T_PER_THREAD];
 #pragma unroll
     for (int k = 0; k < W2T_PER_THREAD; ++k) w2t[k] = *(const u32x4*)(w2ts + (tid + k * NTHR) * 8);
+    bf16x8 xf[KU1];
+    {
+        const uint16_t* xr = (const uint16_t*)a.states + (int64_t)bc * a.ld;
+#pragma unroll
+        for (int u = 0; u < KU1; ++u) {
+            const int k0 = 32 * u + 8 * q;
+            bf16x8 x;
+            if (XVEC) {
+                x = ld8(xr + k0);
+            } else {
+                uint16_t tmp[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint16_t v = xr[min(k0 + e, S - 1)];
+                    tmp[e] = (uint16_t)keep_if(k0 + e < S, (uint32_t)v);
+                }
+                x = O::make(tmp);
+            }
+            const u32x4 xb = __builtin_bit_cast(u32x4, x);
+            xf[u] = __builtin_bit_cast(bf16x8, u32x4{keep_if(valid, xb.x), keep_if(valid, xb.y), keep_if(valid, xb.z),
+                                                     keep_if(valid, xb.w)});
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < W1_PER_THREAD; ++k) {
+        const int idx = (tid + k * NTHR) * 8, r = idx / SP, c = idx - r * SP;
+        *(u32x4*)(R0 + r * C::LDW1 + c) = w1r[k];
+    }
+#pragma unroll
+    for (int k = 0; k < W2_PER_THREAD; ++k) {
+        const int idx = (tid + k * NTHR) * 8, r = idx / H, c = idx - r * H;
+        *(u32x4*)(R1 + r * C::LDW2 + c) = w2r[k];
+    }
+    if (tid < H) {
+        sb1[tid] = vb1;
+        sb2[tid] = vb2;
+        sw3[tid] = vw3;
+    }
     __syncthreads();
 
     // ---- F1: z1^T = W1 s^T
@@ -874,8 +896,8 @@ static hipError_t run_fused16_x(const FusedArgs& fa, int G, hipStream_t stream, 
     }
     const size_t lds = C::BYTES + 16 * sizeof(float);  // sred holds 2 x 8 waves
     if (ev0)
-        hipExtLaunchKernelGGL((iql_fused16_kernel<SP, H, XVEC>), dim3(fa.nwg, G), dim3(512), lds, stream,
-                              ev0, ev1, 0, fa);
+        hipExtLaunchKernelGGL((iql_fused16_kernel<SP, H, XVEC>), dim3(fa.nwg, G), dim3(512), lds, stream, ev0, ev1,
+                              0, fa);
     else
         hipLaunchKernelGGL((iql_fused16_kernel<SP, H, XVEC>), dim3(fa.nwg, G), dim3(512), lds, stream, fa);
     return hipGetLastError();

@@ -14,6 +14,8 @@
 //   D  IQL: clip + Adam + shadows | budget: clip + Adam (or the norm only)
 // Results are bit-for-bit those of the separate launches: every block runs
 // the same block function with the same block index and count.
+#include <hip/hip_ext.h>
+
 #include "budget_block.hpp"
 #include "her_block.hpp"
 #include "iql_update.hpp"
@@ -100,10 +102,21 @@ __global__ __launch_bounds__(256) void step_adam_kernel(IqlDims d, IqlBuffers b,
 
 static bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// A launch of 256-thread blocks, with dispatch events (kernel time only) when
+// the caller times the step.
+#define STEP_LAUNCH(kern, blocks, evp, ...)                                                               \
+    do {                                                                                                  \
+        if (evp)                                                                                          \
+            hipExtLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, stream, (evp)[0], (evp)[1], 0, __VA_ARGS__); \
+        else                                                                                              \
+            hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, stream, __VA_ARGS__);                    \
+    } while (0)
+
 hipError_t launch_aux_step(const IqlDims& d, const IqlBuffers& b, const AdamHyper& hp, const float* tau,
                            const HerArgs* her, const void* states, int64_t ld, const float* q, int B,
                            const float* q_all, int A, float beta, float* out_pi, float* out_v,
-                           float* out_loss, float* out_gnorm, const BudgetArgs* bud, hipStream_t stream) {
+                           float* out_loss, float* out_gnorm, const BudgetArgs* bud, hipStream_t stream,
+                           hipEvent_t* ev) {
     int nwg, nloss;
     if (!iql_partial_counts(d, B, &nwg, &nloss)) return hipErrorInvalidValue;
     const int nb = bud ? budget_num_blocks(bud->n) : 0;
@@ -125,18 +138,20 @@ hipError_t launch_aux_step(const IqlDims& d, const IqlBuffers& b, const AdamHype
         if (her_blocks) ha = *her;
         NormsPart np{};
         if (bud) np = NormsPart{bud->s, bud->n, partials, vec, nb};
-        hipLaunchKernelGGL(step_her_norms_kernel, dim3(her_blocks + nb), dim3(256), 0, stream, ha, her_blocks,
-                           np);
+        STEP_LAUNCH(step_her_norms_kernel, her_blocks + nb, ev, ha, her_blocks, np);
+    } else if (ev) {  // nothing to launch: an empty interval keeps the timing uniform
+        (void)hipEventRecord(ev[0], stream);
+        (void)hipEventRecord(ev[1], stream);
     }
 
     // B: fused forward/backward (+ policy)
     hipError_t e;
     const bool fused_pi = q_all && iql_fused_policy(d, A);
+    hipEvent_t e0 = ev ? ev[2] : nullptr, e1 = ev ? ev[3] : nullptr;
     if (fused_pi) {
-        e = launch_iql_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream, nullptr, nullptr, q_all, A, beta,
-                               out_pi);
+        e = launch_iql_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream, e0, e1, q_all, A, beta, out_pi);
     } else {
-        e = launch_iql_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream);
+        e = launch_iql_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream, e0, e1);
         if (e == hipSuccess && q_all) e = launch_aw_policy(q_all, out_v, d.G, B, A, beta, out_pi, stream);
     }
     if (e != hipSuccess) return e;
@@ -149,7 +164,7 @@ hipError_t launch_aux_step(const IqlDims& d, const IqlBuffers& b, const AdamHype
     if (bud)
         sp = SaxpyPart{bud->s, bud->n, partials, bud->grad, gpart, bud->out_norms,
                        flat_adam ? bud->t : (int32_t*)nullptr, bud->mgn, vec, nb};
-    hipLaunchKernelGGL(step_reduce_saxpy_kernel, dim3(rb * d.G + nb), dim3(256), 0, stream, rp, sp);
+    STEP_LAUNCH(step_reduce_saxpy_kernel, rb * d.G + nb, ev ? ev + 4 : nullptr, rp, sp);
 
     // D: both Adam updates
     const int ab = iql_adam_blocks(d.P);
@@ -167,11 +182,11 @@ hipError_t launch_aux_step(const IqlDims& d, const IqlBuffers& b, const AdamHype
         extra = 1;
     }
     if (d.dtype == 1)
-        hipLaunchKernelGGL(step_adam_kernel<uint16_t>, dim3(ab * d.G + extra), dim3(256), 0, stream, d, b, hp,
-                           out_gnorm, rb, ab, fp);
+        STEP_LAUNCH((step_adam_kernel<uint16_t>), ab * d.G + extra, ev ? ev + 6 : nullptr, d, b, hp, out_gnorm, rb,
+                    ab, fp);
     else
-        hipLaunchKernelGGL(step_adam_kernel<float>, dim3(ab * d.G + extra), dim3(256), 0, stream, d, b, hp,
-                           out_gnorm, rb, ab, fp);
+        STEP_LAUNCH((step_adam_kernel<float>), ab * d.G + extra, ev ? ev + 6 : nullptr, d, b, hp, out_gnorm, rb, ab,
+                    fp);
     return hipGetLastError();
 }
 

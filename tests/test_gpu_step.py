@@ -25,7 +25,7 @@ def m():
 class Inputs:
     """Read-only inputs shared by the two rigs."""
 
-    def __init__(self, w, B, n_budget):
+    def __init__(self, w, B, n_budget, bad_sources=False):
         import torch
         self.w, self.B = w, B
         self.n = int(B * w.her_ratio)
@@ -34,6 +34,10 @@ class Inputs:
         assert len(self.src) == self.n
         self.Xn = synth.batch_states(synth.shrink(w, B=B))
         self.Q, _, self.q = synth.q_values(synth.shrink(w, B=B), buf, self.src)
+        if bad_sources:  # indices outside the buffer: flagged, zero rows
+            self.src = self.src.copy()
+            self.src[::97] = -1
+            self.src[5::101] = w.C + 3
         self.inits = synth.group_inits(w)
         self.sources = synth.budget_sources(w, n=n_budget)
         self.theta = synth.budget_params(w, n=n_budget)
@@ -51,7 +55,8 @@ class Inputs:
 class Rig:
     """Outputs and trainer state of one way of running the step."""
 
-    def __init__(self, m, inp, her=True, policy=True, budget=True, adam=True, norms=True):
+    def __init__(self, m, inp, her=True, policy=True, budget=True, adam=True, norms=True, strategy=None,
+                 minimal_out=False, alias=True):
         import torch
         w, B, n, d = inp.w, inp.B, inp.n, dev()
         self.m, self.inp = m, inp
@@ -59,8 +64,10 @@ class Rig:
         S = w.S
         self.X = torch.zeros((B, S), dtype=inp.sdt, device=d)
         self.X[: B - n] = to_dev(inp.Xn, inp.sdt)
-        if not her:  # rows the relabelling would have written: fixed values
-            self.X[B - n:] = to_dev(inp.buf["states"][inp.src], inp.sdt)
+        if not her or not alias:  # rows the relabelling does not write: fixed values
+            self.X[B - n:] = to_dev(inp.buf["states"][np.clip(inp.src, 0, w.C - 1)], inp.sdt)
+        # relabelled rows outside the batch when not aliased
+        self.Xh = torch.zeros((n, S), dtype=inp.sdt, device=d)
         cfg = m.make_config(S, w.H, B, num_groups=w.groups, compute_dtype=m.BF16 if inp.bf16 else m.F32,
                             states_ld=S, tau=w.taus, lr=w.lr, max_grad_norm=w.max_grad_norm)
         self.tr = m.IqlTrainer(cfg, np.concatenate(inp.inits))
@@ -73,11 +80,14 @@ class Rig:
         self.act = torch.zeros(n, dtype=torch.int32, device=d)
         self.done = torch.zeros(n, dtype=torch.float32, device=d)
         self.donor = torch.zeros(n, dtype=torch.int32, device=d)
-        self.hcfg = m.her_config(S, w.G, m.HER_FUTURE)
+        self.hcfg = m.her_config(S, w.G, m.HER_FUTURE if strategy is None else strategy)
         self.hbuf = m.her_buffer(inp.t_states, inp.t_next, inp.t_actions, inp.t_dones, inp.t_ends)
-        tail = self.X.data_ptr() + (B - n) * S * self.X.element_size()
-        self.hout = m.her_out(tail, m.BF16 if inp.bf16 else m.F32, S, self.rew, next_states=self.nxt,
-                              actions=self.act, dones=self.done, donor_idx=self.donor, d_flags=self.tr.flags)
+        tail = (self.X.data_ptr() + (B - n) * S * self.X.element_size()) if alias else self.Xh.data_ptr()
+        if minimal_out:
+            self.hout = m.her_out(tail, m.BF16 if inp.bf16 else m.F32, S, self.rew, d_flags=self.tr.flags)
+        else:
+            self.hout = m.her_out(tail, m.BF16 if inp.bf16 else m.F32, S, self.rew, next_states=self.nxt,
+                                  actions=self.act, dones=self.done, donor_idx=self.donor, d_flags=self.tr.flags)
         P = inp.n_budget
         self.theta = to_dev(inp.theta)
         self.tm = torch.zeros(P, dtype=torch.float32, device=d)
@@ -118,7 +128,7 @@ class Rig:
 
     def tensors(self):
         import torch
-        out = {"X": self.X, "rew": self.rew, "next": self.nxt, "act": self.act, "done": self.done,
+        out = {"X": self.X, "Xh": self.Xh, "rew": self.rew, "next": self.nxt, "act": self.act, "done": self.done,
                "donor": self.donor, "v": self.out_v, "loss": self.out_loss, "gn": self.out_gn, "pi": self.pi,
                "theta": self.theta, "theta_m": self.tm, "theta_v": self.tv, "theta_t": self.tt,
                "grad": self.grad}
@@ -147,7 +157,7 @@ def _bitwise_equal(a, b, what):
         assert torch.equal(x, y), f"{what}: {k} differs"
 
 
-def _run_pair(m, inp, steps=3, **kw):
+def _run_pair(m, inp, steps=3, expect_flags=0, **kw):
     a, b = Rig(m, inp, **kw), Rig(m, inp, **kw)
     for s in range(steps):
         a.separate()
@@ -155,8 +165,9 @@ def _run_pair(m, inp, steps=3, **kw):
         _bitwise_equal(a, b, f"step {s + 1} {kw}")
     for r in (a, b):
         rc, flags = r.tr.status()
-        assert rc == m.OK and flags == 0
+        assert flags == expect_flags and (rc == m.OK) == (expect_flags == 0)
         r.tr.close()
+    return a, b
 
 
 @pytest.fixture(scope="module")
@@ -178,6 +189,64 @@ def test_whole_step_equals_separate_calls_b16384(m, bench_inputs):
 def test_whole_step_optional_parts(m, kw):
     w = synth.shrink(synth.WORKLOADS["b16384_s128_h128_bf16_g2_budget"], C=1 << 14)
     _run_pair(m, Inputs(w, 3000, 70001), steps=2, **kw)
+
+
+@pytest.mark.parametrize("strategy", ["final", "future", "random"])
+def test_whole_step_relabelling_strategies(m, strategy):
+    """Every donor strategy inside the whole step, the HER rows starting
+    inside a 128-row tile of the forward/backward launch, two groups."""
+    w = synth.shrink(synth.WORKLOADS["b16384_s128_h128_bf16_g2_budget"], C=1 << 15)
+    code = {"final": m.HER_FINAL, "future": m.HER_FUTURE, "random": m.HER_RANDOM}[strategy]
+    _run_pair(m, Inputs(w, 4000, 3001), steps=2, strategy=code)
+
+
+@pytest.mark.parametrize("S,G,minimal", [(61, 20, False), (100, 8, True), (64, 3, False)])
+def test_whole_step_relabelling_ragged_rows(m, S, G, minimal):
+    """State widths that are not a multiple of the operand tile (scalar
+    loads, padded features), goals longer than 16 entries, and HER without
+    its optional outputs."""
+    w = synth.shrink(synth.WORKLOADS["b16384_s128_h128_bf16_g2_budget"], S=S, G=G, C=1 << 14)
+    _run_pair(m, Inputs(w, 1111, 2048), steps=2, minimal_out=minimal)
+
+
+def test_whole_step_relabelling_bad_sources(m):
+    """Source indices outside the buffer: zero rows, reward 0, donor -1 and
+    the bad-index flag, the same in both ways of running the step."""
+    w = synth.shrink(synth.WORKLOADS["b16384_s128_h128_bf16_g2_budget"], C=1 << 14)
+    a, _ = _run_pair(m, Inputs(w, 2048, 1000, bad_sources=True), steps=1, expect_flags=m.FLAG_BAD_INDEX)
+    assert np.all(host(a.donor)[::97] == -1) and np.all(host(a.rew)[5::101] == 0.0)
+
+
+def test_whole_step_relabelled_rows_outside_the_batch(m):
+    """HER output rows that are not the tail of the batch: the batch keeps
+    its rows and the relabelled rows land where the caller asked."""
+    w = synth.shrink(synth.WORKLOADS["b16384_s128_h128_bf16_g2_budget"], C=1 << 14)
+    a, _ = _run_pair(m, Inputs(w, 2048, 1000), steps=2, alias=False)
+    assert np.any(host(a.Xh) != 0)
+
+
+def test_whole_step_relabelling_matches_oracle(m):
+    """One whole step with bf16 operands against the oracle's HER pass
+    (donors, rewards, the bf16 rows in the batch, s' with the new goal,
+    actions, dones), and V against the oracle's step on that batch."""
+    from oracle import her, iql
+    w = synth.shrink(synth.WORKLOADS["b16384_s128_h128_bf16_g2_budget"], C=1 << 14)
+    inp = Inputs(w, 3000, 1000)
+    r = Rig(m, inp)
+    r.whole()
+    sync()
+    ref = her.her_step(inp.buf, inp.src, w.G, her.FUTURE, r.seed, 0, out_bf16=True)
+    assert np.array_equal(host(r.donor), ref["donor_idx"])
+    assert np.array_equal(host(r.rew), ref["rewards"])
+    assert np.array_equal(host(r.X)[inp.B - inp.n:], ref["states"])
+    assert np.array_equal(host(r.nxt), ref["next_states"])
+    assert np.array_equal(host(r.act), ref["actions"]) and np.array_equal(host(r.done), ref["dones"])
+    X = host(r.X).astype(np.float64)
+    for g in range(w.groups):
+        st = iql.AdamState.fresh(inp.inits[g])
+        res = iql.train_step(st, X, inp.q, w.S, w.H, w.H, w.taus[g], iql.AdamHP(lr=w.lr))
+        assert_rel(host(r.out_v[g]), res.v, 2e-2, f"V g{g}")
+    r.tr.close()
 
 
 def test_whole_step_fp32_unfused_policy(m):
@@ -229,4 +298,24 @@ def test_whole_step_matches_oracle(m):
     adam_update_close(host(r.theta), th.params, None, w.lr, 1, 1e-5, "budget params")
     assert int(host(r.tt)[0]) == 1
     assert np.all(host(r.grad) == 0)  # consumed by Adam
+    r.tr.close()
+
+
+def test_time_aux_step_reports_every_launch(m):
+    """The measurement entry point runs real steps (Adam's t advances) and
+    reports a positive kernel time for each of the four launches."""
+    w = synth.shrink(synth.WORKLOADS["b16384_s128_h128_bf16_g2_budget"], C=1 << 14)
+    inp = Inputs(w, 2048, 5000)
+    r = Rig(m, inp)
+    her = m.her_step(r.hcfg, r.hbuf, inp.t_src, inp.n, r.seed, r.hout)
+    bud = m.budget_step(r.grad, inp.t_sources, w.budget_fractions, (1.0, 1.0, 1.0, 1.0), inp.n_budget,
+                        w.max_grad_norm, r.norms, r.adam, r.ws)
+    us = r.tr.time_aux_step(her, r.X, inp.t_q, inp.B, inp.t_Q, w.A, w.beta, r.pi, r.out_v, r.out_loss, r.out_gn,
+                            bud, reps=5)
+    assert len(us) == 4 and all(np.isfinite(us)) and min(us) > 0.0, us
+    t = r.tensors()
+    sync()
+    assert int(host(t["t0"])[0]) == 5 and int(host(r.tt)[0]) == 5
+    rc, flags = r.tr.status()
+    assert rc == m.OK and flags == 0
     r.tr.close()
