@@ -552,6 +552,44 @@ IQLH_DEV bf16x8 ld_chain16(const uint16_t* row, int u, int q) {
     const u32x2 hi = *(const u32x2*)(row + 32 * u + 16 + 4 * q);
     return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
 }
+// Cross-lane sums and maxima of the 16x16 kernel on VALU lane permutes
+// (v_permlane16/32_swap, DPP) rather than LDS-routed shuffles.
+// Over the four lane groups q (rows of 16 lanes) holding one sample, the
+// same value in all four: ((x_0 + x_1) + (x_2 + x_3)).
+IQLH_DEV float sum_q4(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+IQLH_DEV float max_q4(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+// Sum over the 16 lanes of each row (rotations by 8, 4, 2, 1 within the row),
+// every lane of the row ends with it.
+IQLH_DEV float row_sum16(float x) {
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x128, 0xF, 0xF, false);  // row_ror:8
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x124, 0xF, 0xF, false);  // row_ror:4
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x122, 0xF, 0xF, false);  // row_ror:2
+    x += __builtin_amdgcn_update_dpp(0.f, x, 0x121, 0xF, 0xF, false);  // row_ror:1
+    return x;
+}
+
+// acc[t] += sum_u A(t, u) B[u] over NT row tiles and KU k steps, with the A
+// fragments read from LDS one k step ahead (double-buffered in registers):
+// the reads of step u + 1 are in flight while the MFMAs of step u run, so a
+// wave waits for LDS once per k step instead of once per MFMA.
+template <int NT, int KU, int RD, typename LoadA>
+IQLH_DEV void mma16_pipelined(f32x4v (&acc)[NT], const bf16x8 (&bop)[KU], LoadA load_a) {
+#pragma unroll
+    for (int u = 0; u < KU; ++u)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = mma16(load_a(t, u), bop[u], acc[t]);
+}
+
 // chained B operand of k step u from tiles 2u, 2u + 1 of a layer's accumulators
 template <int NT>
 IQLH_DEV bf16x8 chain_from16(const f32x4v (&acc)[NT], int u) {
@@ -562,24 +600,91 @@ IQLH_DEV bf16x8 chain_from16(const f32x4v (&acc)[NT], int u) {
                                              O::cvt2(b[2], b[3])});
 }
 
-// C[i][j] = sum_k A[i][k] B[j][k] over K = 128 samples for row tile rt (16 rows)
-// and column tiles [0, NCT) of 16; stores C rows to dst (ldo, j < ncols) and,
-// through the all-ones operand, the row sums of A to bias_dst.
+// ---- activation tiles of the 16x16 kernel: natural [sample][feature]
+// layout, rows of kNatLd elements, the 16-byte unit u of row s stored at
+// unit u ^ ((s >> 2) & 3).  A lane writes its 4 consecutive features of its
+// sample as one 8-byte store (no transposed 2-byte stores), and the
+// weight-gradient products read their operands with the LDS transpose load
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane 4i + j receives
+// element j of the 8-byte rows addressed by lanes 4e + i, e = 0..3.  Padding
+// and swizzle keep the transpose loads and the 16-byte row writes free of
+// bank conflicts (the 8-byte writes are two-way).
+constexpr int kNatLd = 144;
+IQLH_DEV int nat_off(int s, int f) { return s * kNatLd + ((((f >> 3) ^ ((s >> 2) & 3)) << 3) | (f & 7)); }
+
+// features f .. f + 3 (f % 4 == 0) of sample s, rounded to bfloat16
+IQLH_DEV void put4(uint16_t* tile, int s, int f, float x0, float x1, float x2, float x3) {
+    typedef Op<uint16_t> O;
+    *(u32x2*)(tile + nat_off(s, f)) = u32x2{O::cvt2(x0, x1), O::cvt2(x2, x3)};
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+IQLH_DEV u32x2 ld_tr4(const uint16_t* p) {
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+    return __builtin_bit_cast(u32x2, r);
+}
+// Per-lane parts of the transpose-load addresses into a natural tile: the
+// operand of column tile c (features 16c + l16) and sample block u (samples
+// 32u + 8q .. 32u + 8q + 7) is read by two loads at base[h][c & 1] +
+// 32u * kNatLd + 16c, h = 0, 1 -- this lane addresses sample
+// 32u + 8 (lane >> 4) + ((lane >> 2) & 3) + 4h, features 16c + 4 (lane & 3);
+// the swizzle folds into the two bases, so every load of an operand sweep
+// takes one base register and an immediate offset.
+struct NatLane {
+    int base[2][2];  // [h][c & 1], elements
+};
+IQLH_DEV NatLane nat_lane() {
+    const int lane = threadIdx.x & 63, g = lane >> 4, e = (lane >> 2) & 3, i = lane & 3;
+    NatLane L;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int b = (8 * g + e + 4 * h) * kNatLd + 8 * ((i >> 1) ^ h) + 4 * (i & 1);
+        L.base[h][0] = b + 16 * (g & 1);
+        L.base[h][1] = b - 16 * (g & 1);
+    }
+    return L;
+}
+IQLH_DEV bf16x8 frag_nat(const uint16_t* tile, const NatLane& L, int c, int u) {
+    const int off = 32 * u * kNatLd + 16 * c;
+    const u32x2 lo = ld_tr4(tile + L.base[0][c & 1] + off);
+    const u32x2 hi = ld_tr4(tile + L.base[1][c & 1] + off);
+    return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+}
+
+// C[i][j] = sum_s A[s][i] B[s][j] over the 128 samples of two natural tiles,
+// for row tile rt (16 rows i) and column tiles [0, NCT) of 16; stores C rows
+// to dst (ldo, j < ncols) and, through the all-ones operand, the column sums
+// of A (sum over samples) to bias_dst.
 template <int NCT>
-IQLH_DEV void lds_gemm16_row(const uint16_t* A, const uint16_t* Bm, int lda, int rt, float* dst,
-                             int ldo, int ncols, float* bias_dst) {
+IQLH_DEV void nat_gemm16_row(const uint16_t* A, const uint16_t* Bm, int rt, float* dst, int ldo, int ncols,
+                             float* bias_dst) {
     const int lane = threadIdx.x & 63, l16 = lane & 15, q = lane >> 4;
     const bf16x8 one = Op<uint16_t>::ones();
     f32x4v acc[NCT], accb = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NCT; ++c) acc[c] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    // operands of k step u + 1 read while the MFMAs of step u run
+    const NatLane L = nat_lane();
+    bf16x8 fa[2], fb[2][NCT];
+    fa[0] = frag_nat(A, L, rt, 0);
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) fb[0][c] = frag_nat(Bm, L, c, 0);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int k0 = 32 * u + 8 * q;
-        const bf16x8 a = ld8(A + (16 * rt + l16) * lda + k0);
+        if (u + 1 < 4) {
+            fa[(u + 1) & 1] = frag_nat(A, L, rt, u + 1);
 #pragma unroll
-        for (int c = 0; c < NCT; ++c) acc[c] = mma16(a, ld8(Bm + (16 * c + l16) * lda + k0), acc[c]);
-        accb = mma16(a, one, accb);
+            for (int c = 0; c < NCT; ++c) fb[(u + 1) & 1][c] = frag_nat(Bm, L, c, u + 1);
+        }
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) acc[c] = mma16(fa[u & 1], fb[u & 1][c], acc[c]);
+        accb = mma16(fa[u & 1], one, accb);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (NCT + 1), 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        if (u + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2 * (NCT + 1), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NCT + 1, 0);
     }
     float* d0 = dst + (16 * rt + 4 * q) * ldo;
 #pragma unroll
@@ -596,10 +701,26 @@ IQLH_DEV void lds_gemm16_row(const uint16_t* A, const uint16_t* Bm, int lda, int
     }
 }
 
+// LDS plan of the 16x16 kernel: R0 = W1 then dz2, R1 = W2 then W2^T,
+// R2 = h2 dv then dz1, R3 = h1 then s (activation tiles natural, 128 rows).
+template <int SP, int H>
+struct Fused16Cfg {
+    static constexpr int BT = 128;
+    static constexpr int LDW1 = SP + 8, LDW2 = H + 8;  // weight rows, 16-byte padded
+    static constexpr int NAT = BT * kNatLd;            // one activation tile
+    static constexpr int R0 = (H * LDW1 > NAT) ? H * LDW1 : NAT;
+    static constexpr int R1 = H * LDW2;
+    static constexpr int R2 = NAT;
+    static constexpr int R3 = NAT;
+    static constexpr size_t BYTES = (size_t)(R0 + R1 + R2 + R3) * 2 + (size_t)(3 * H + 16) * sizeof(float);
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+    static_assert(SP <= kNatLd - 16 && H <= kNatLd - 16, "natural tile width");
+};
+
 template <int SP, int H, bool XVEC>
 __global__ __launch_bounds__(512) void iql_fused16_kernel(FusedArgs a) {
     typedef Op<uint16_t> O;
-    typedef FusedCfg<uint16_t, SP, H, 4> C;  // same LDS plan: BT = 128, padded rows
+    typedef Fused16Cfg<SP, H> C;
     constexpr int NW = 8, BT = 128, NT = H / 16, KU1 = SP / 32, KUH = H / 32, NTHR = 512;
     static_assert(H == 128 && SP % 32 == 0 && SP <= 128, "tile shape");
     extern __shared__ __align__(16) unsigned char smem[];
@@ -698,56 +819,44 @@ __global__ __launch_bounds__(512) void iql_fused16_kernel(FusedArgs a) {
     }
     __syncthreads();
 
-    // ---- F1: z1^T = W1 s^T
+    // ---- F1: z1^T = W1 s^T + b1 (the bias is the accumulators' initial value)
     f32x4v acc[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < KU1; ++u)
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-            acc[t] = mma16(ld8(R0 + (16 * t + l16) * C::LDW1 + 32 * u + 8 * q), xf[u], acc[t]);
+    for (int t = 0; t < NT; ++t) acc[t] = *(const f32x4v*)(sb1 + 16 * t + 4 * q);
+    mma16_pipelined<NT, KU1, 1>(acc, xf, [&](int t, int u) { return ld8(R0 + (16 * t + l16) * C::LDW1 + 32 * u + 8 * q); });
     uint32_t mask1 = 0u;  // relu'(z1), bit 4t + r
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
-        for (int r = 0; r < 4; r += 2) {
-            const int f = 16 * t + 4 * q + r;
-            const float z0 = acc[t][r] + sb1[f], z1 = acc[t][r + 1] + sb1[f + 1];
-            const float y0 = z0 > 0.f ? z0 : 0.f, y1 = z1 > 0.f ? z1 : 0.f;
-            acc[t][r] = y0;
-            acc[t][r + 1] = y1;
-            O::put2(R3, f * C::LDA + bl, C::LDA, y0, y1);  // h1^T
-            mask1 |= (((__float_as_uint(y0) + 0x7FFFFFFFu) >> 31) << (4 * t + r)) |
-                     (((__float_as_uint(y1) + 0x7FFFFFFFu) >> 31) << (4 * t + r + 1));
+        for (int r = 0; r < 4; ++r) {
+            const float z = acc[t][r];
+            const float y = z > 0.f ? z : 0.f;
+            acc[t][r] = y;
+            mask1 |= ((__float_as_uint(y) + 0x7FFFFFFFu) >> 31) << (4 * t + r);
         }
+        put4(R3, bl, 16 * t + 4 * q, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);  // h1
     }
     bf16x8 h1f[KUH];
 #pragma unroll
     for (int u = 0; u < KUH; ++u) h1f[u] = chain_from16<NT>(acc, u);
     __syncthreads();
 
-    // ---- F2: z2^T = W2 h1^T
+    // ---- F2: z2^T = W2 h1^T + b2 (bias as the initial value)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NT; ++t) acc[t] = *(const f32x4v*)(sb2 + 16 * t + 4 * q);
+    mma16_pipelined<NT, KUH, 2>(acc, h1f, [&](int t, int u) { return ld_chain16(R1 + (16 * t + l16) * C::LDW2, u, q); });
+    f32x4v w3v[NT];  // this lane's w3 entries, read together
 #pragma unroll
-    for (int u = 0; u < KUH; ++u)
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-            acc[t] = mma16(ld_chain16(R1 + (16 * t + l16) * C::LDW2, u, q), h1f[u], acc[t]);
+    for (int t = 0; t < NT; ++t) w3v[t] = *(const f32x4v*)(sw3 + 16 * t + 4 * q);
     float vpart = 0.f;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int f = 16 * t + 4 * q + r;
-            const float z = acc[t][r] + sb2[f];
-            acc[t][r] = z;
-            vpart = fmaf(sw3[f], z > 0.f ? z : 0.f, vpart);
+            const float z = acc[t][r];
+            vpart = fmaf(w3v[t][r], z > 0.f ? z : 0.f, vpart);
         }
-    vpart += __shfl_xor(vpart, 16, 64);
-    vpart += __shfl_xor(vpart, 32, 64);
-    const float v = vpart + b3;
+    const float v = sum_q4(vpart) + b3;
     float dv = 0.f, lterm = 0.f;
     if (valid) {
         const float diff = qb - v;
@@ -757,8 +866,9 @@ __global__ __launch_bounds__(512) void iql_fused16_kernel(FusedArgs a) {
         if (q == 0 && a.out_v) a.out_v[(int64_t)g * B + b] = v;
     }
     {
-        const float ls = wave_sum(q == 0 ? lterm : 0.f);
-        const float ds = wave_sum(q == 0 ? dv : 0.f);
+        // lanes 0..15 (lane group 0) hold one copy of each of the wave's samples
+        const float ls = row_sum16(lterm);
+        const float ds = row_sum16(dv);
         if (lane == 0) { sred[wv] = ls; sred[NW + wv] = ds; }
     }
     if (a.out_pi) {
@@ -772,16 +882,14 @@ __global__ __launch_bounds__(512) void iql_fused16_kernel(FusedArgs a) {
             x[k] = on ? a.beta * fminf(fmaxf(qa[k] - v, -10.f), 10.f) : -INFINITY;
             mx = fmaxf(mx, x[k]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = max_q4(mx);
         float se = 0.f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             x[k] = q + 4 * k < a.A ? expf(x[k] - mx) : 0.f;
             se += x[k];
         }
-        se += __shfl_xor(se, 16, 64);
-        se += __shfl_xor(se, 32, 64);
+        se = sum_q4(se);
         if (valid) {
             float* pr = a.out_pi + ((int64_t)g * B + b) * a.A;
 #pragma unroll
@@ -791,17 +899,15 @@ __global__ __launch_bounds__(512) void iql_fused16_kernel(FusedArgs a) {
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
+        float hd[4];
 #pragma unroll
-        for (int r = 0; r < 4; r += 2) {
-            const int f = 16 * t + 4 * q + r;
-            const float z0 = acc[t][r], z1 = acc[t][r + 1];
-            const float dz0 = z0 > 0.f ? dv * sw3[f] : 0.f;
-            const float dz1 = z1 > 0.f ? dv * sw3[f + 1] : 0.f;
-            O::put2(R0, f * C::LDA + bl, C::LDA, dz0, dz1);                                // dz2^T
-            O::put2(R2, f * C::LDA + bl, C::LDA, z0 > 0.f ? z0 * dv : 0.f, z1 > 0.f ? z1 * dv : 0.f);  // h2 dv
-            acc[t][r] = dz0;
-            acc[t][r + 1] = dz1;
+        for (int r = 0; r < 4; ++r) {
+            const float z = acc[t][r];
+            hd[r] = z > 0.f ? z * dv : 0.f;
+            acc[t][r] = z > 0.f ? dv * w3v[t][r] : 0.f;
         }
+        put4(R0, bl, 16 * t + 4 * q, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);  // dz2
+        put4(R2, bl, 16 * t + 4 * q, hd[0], hd[1], hd[2], hd[3]);                  // h2 dv
     }
     bf16x8 dz2f[KUH];
 #pragma unroll
@@ -812,8 +918,9 @@ __global__ __launch_bounds__(512) void iql_fused16_kernel(FusedArgs a) {
     {
         const bf16x8 one = O::ones();
         f32x4v s3 = f32x4v{0.f, 0.f, 0.f, 0.f};
+        const NatLane L = nat_lane();
 #pragma unroll
-        for (int u = 0; u < 4; ++u) s3 = mma16(ld8(R2 + (16 * wv + l16) * C::LDA + 32 * u + 8 * q), one, s3);
+        for (int u = 0; u < 4; ++u) s3 = mma16(frag_nat(R2, L, wv, u), one, s3);
         if (l16 == 0) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) part[po.w3 + 16 * wv + 4 * q + r] = s3[r];
@@ -830,35 +937,26 @@ __global__ __launch_bounds__(512) void iql_fused16_kernel(FusedArgs a) {
         const int idx = (tid + k * NTHR) * 8, r = idx / H, c = idx - r * H;
         *(u32x4*)(R1 + r * C::LDW2 + c) = w2t[k];
     }
-    lds_gemm16_row<H / 16>(R0, R3, C::LDA, wv, part + po.w2, H, H, part + po.b2);
+    nat_gemm16_row<H / 16>(R0, R3, wv, part + po.w2, H, H, part + po.b2);
     __syncthreads();
 
     // ---- s^T to R3; B1: dh1^T = W2^T dz2^T; dz1 = dh1 relu'(z1) -> R2
 #pragma unroll
-    for (int u = 0; u < KU1; ++u)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) R3[(32 * u + 8 * q + i) * C::LDA + bl] = O::half(xf[u], i);
+    for (int u = 0; u < KU1; ++u) *(u32x4*)(R3 + nat_off(bl, 32 * u + 8 * q)) = __builtin_bit_cast(u32x4, xf[u]);
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < KUH; ++u)
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-            acc[t] = mma16(ld_chain16(R1 + (16 * t + l16) * C::LDW2, u, q), dz2f[u], acc[t]);
+    mma16_pipelined<NT, KUH, 2>(acc, dz2f, [&](int t, int u) { return ld_chain16(R1 + (16 * t + l16) * C::LDW2, u, q); });
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
+        float d[4];
 #pragma unroll
-        for (int r = 0; r < 4; r += 2) {
-            const int f = 16 * t + 4 * q + r;
-            const float d0 = (mask1 >> (4 * t + r)) & 1u ? acc[t][r] : 0.f;
-            const float d1 = (mask1 >> (4 * t + r + 1)) & 1u ? acc[t][r + 1] : 0.f;
-            O::put2(R2, f * C::LDA + bl, C::LDA, d0, d1);
-        }
+        for (int r = 0; r < 4; ++r) d[r] = (mask1 >> (4 * t + r)) & 1u ? acc[t][r] : 0.f;
+        put4(R2, bl, 16 * t + 4 * q, d[0], d[1], d[2], d[3]);  // dz1
     }
     __syncthreads();
 
     // ---- dW1 = dz1^T s with db1
-    lds_gemm16_row<SP / 16>(R2, R3, C::LDA, wv, part + po.w1, S, S, part + po.b1);
+    nat_gemm16_row<SP / 16>(R2, R3, wv, part + po.w1, S, S, part + po.b1);
 }
 
 // ------------------------------------------------------------- dispatch
@@ -885,16 +983,15 @@ static hipError_t run_fused_x(const FusedArgs& fa, int G, hipStream_t stream, hi
 template <int SP, int H, bool XVEC>
 static hipError_t run_fused16_x(const FusedArgs& fa, int G, hipStream_t stream, hipEvent_t ev0,
                                 hipEvent_t ev1) {
-    typedef FusedCfg<uint16_t, SP, H, 4> C;
+    typedef Fused16Cfg<SP, H> C;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)iql_fused16_kernel<SP, H, XVEC>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)(C::BYTES + 16 * sizeof(float)));
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::BYTES);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const size_t lds = C::BYTES + 16 * sizeof(float);  // sred holds 2 x 8 waves
+    const size_t lds = C::BYTES;  // sred holds 2 x 8 waves
     if (ev0)
         hipExtLaunchKernelGGL((iql_fused16_kernel<SP, H, XVEC>), dim3(fa.nwg, G), dim3(512), lds, stream, ev0, ev1,
                               0, fa);
