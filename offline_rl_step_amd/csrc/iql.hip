@@ -959,6 +959,344 @@ __global__ __launch_bounds__(512) void iql_fused16_kernel(FusedArgs a) {
     nat_gemm16_row<SP / 16>(R2, R3, wv, part + po.w1, S, S, part + po.b1);
 }
 
+// ------------------------------------------------- 16-wave 16x16 variant
+// Same computation for bf16 operands and hidden 128 with sixteen wave64s per
+// 128-sample workgroup (four per SIMD, so the waits of one wave overlap the
+// MFMA and LDS work of three others).  Wave w owns samples 16 (w >> 1) ..
+// + 15 and the feature half 64 (w & 1) .. + 63 of every layer: a layer's
+// input comes from its natural tile in LDS (the batch rows, h1, dz2), so the
+// two halves of a sample group exchange activations through the tiles the
+// weight-gradient products read anyway.  The products themselves are split
+// over the sixteen waves as 8 row tiles x 2 column halves.
+
+// C rows of row tile rt and column tiles c0 .. c0 + NCW - 1 of
+// C[i][j] = sum_s A[s][i] B[s][j] over the 128 samples of two natural tiles;
+// with bias_dst, also the column sums of A (over samples) of that row tile.
+template <int NCW>
+IQLH_DEV void nat_gemm16_part(const uint16_t* A, const uint16_t* Bm, int rt, int c0, float* dst, int ldo,
+                              int ncols, float* bias_dst) {
+    const int lane = threadIdx.x & 63, l16 = lane & 15, q = lane >> 4;
+    const bf16x8 one = Op<uint16_t>::ones();
+    const NatLane L = nat_lane();
+    f32x4v acc[NCW], accb = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NCW; ++c) acc[c] = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const bf16x8 fa = frag_nat(A, L, rt, u);
+#pragma unroll
+        for (int c = 0; c < NCW; ++c) acc[c] = mma16(fa, frag_nat(Bm, L, c0 + c, u), acc[c]);
+        if (bias_dst) accb = mma16(fa, one, accb);
+    }
+    float* d0 = dst + (16 * rt + 4 * q) * ldo;
+#pragma unroll
+    for (int c = 0; c < NCW; ++c) {
+        const int j = 16 * (c0 + c) + l16;
+        if (j < ncols) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) d0[r * ldo + j] = acc[c][r];
+        }
+    }
+    if (bias_dst && l16 == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bias_dst[16 * rt + 4 * q + r] = accb[r];
+    }
+}
+
+// LDS plan: R0 = W1 then dz2, R1 = W2 then W2^T, R2 = the batch rows s (kept
+// to the end), R3 = h1 then dz1; then b1, b2, w3, the V halves, the loss
+// sums and the per-sample-group dw3 sums.
+template <int SP, int H>
+struct Fused16wCfg {
+    static constexpr int BT = 128, NW = 16;
+    static constexpr int LDW1 = SP + 8, LDW2 = H + 8;
+    static constexpr int NAT = BT * kNatLd;
+    static constexpr int R0 = (H * LDW1 > NAT) ? H * LDW1 : NAT;
+    static constexpr int R1 = H * LDW2;
+    static constexpr int R2 = NAT;
+    static constexpr int R3 = NAT;
+    static constexpr int NF = 3 * H + 2 * BT + 2 * NW + (NW / 2) * H;
+    static constexpr size_t BYTES = (size_t)(R0 + R1 + R2 + R3) * 2 + (size_t)NF * sizeof(float);
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+    static_assert(SP <= kNatLd - 16 && H <= kNatLd - 16, "natural tile width");
+};
+
+template <int SP, int H, bool XVEC>
+__global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
+    typedef Op<uint16_t> O;
+    typedef Fused16wCfg<SP, H> C;
+    constexpr int NW = 16, BT = 128, FT = H / 32, KU1 = SP / 32, KUH = H / 32, NTHR = 1024;
+    static_assert(H == 128 && SP % 32 == 0 && SP <= 128, "tile shape");
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint16_t* R0 = (uint16_t*)smem;
+    uint16_t* R1 = R0 + C::R0;
+    uint16_t* R2 = R1 + C::R1;
+    uint16_t* R3 = R2 + C::R2;
+    float* sb1 = (float*)(R3 + C::R3);
+    float* sb2 = sb1 + H;
+    float* sw3 = sb2 + H;
+    float* svh = sw3 + H;        // [2][BT] V halves
+    float* sred = svh + 2 * BT;  // [2][NW / 2] loss and dv sums of the sample groups
+    float* sdw3 = sred + NW;     // [NW / 2][H] dw3 over each sample group
+
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int sg = wv >> 1, fh = wv & 1, fb = 64 * fh;
+    const int g = blockIdx.y, wg = blockIdx.x;
+    const int S = a.S, B = a.B;
+    const POff po(S, H);
+    const float* prm = a.params + (int64_t)g * a.P;
+    const uint16_t* w1s = (const uint16_t*)a.w1s + (int64_t)g * H * SP;
+    const uint16_t* w2s = (const uint16_t*)a.w2s + (int64_t)g * H * H;
+    const uint16_t* w2ts = (const uint16_t*)a.w2ts + (int64_t)g * H * H;
+    float* part = a.part + ((int64_t)g * a.nwg + wg) * a.Pp;
+    const float tau = g == 0 ? a.tau0 : a.tau1;
+
+    // ---- S0: weights, small vectors and the batch rows to LDS (all loads
+    // issued before the first wait; indexes clamped, unused values masked)
+    const int bl = 16 * sg + l16;
+    const int b = wg * BT + bl;
+    const bool valid = b < B;
+    const int bc = valid ? b : B - 1;
+    constexpr int W1_PER_THREAD = H * SP / (NTHR * 8);
+    constexpr int W2_PER_THREAD = H * H / (NTHR * 8);
+    constexpr int X_PER_THREAD = BT * SP / (NTHR * 8);
+    static_assert(W1_PER_THREAD * NTHR * 8 == H * SP && W2_PER_THREAD * NTHR * 8 == H * H &&
+                  X_PER_THREAD * NTHR * 8 == BT * SP, "staging split");
+    u32x4 w1r[W1_PER_THREAD], w2r[W2_PER_THREAD], xr[X_PER_THREAD];
+#pragma unroll
+    for (int k = 0; k < W1_PER_THREAD; ++k) w1r[k] = *(const u32x4*)(w1s + (tid + k * NTHR) * 8);
+#pragma unroll
+    for (int k = 0; k < W2_PER_THREAD; ++k) w2r[k] = *(const u32x4*)(w2s + (tid + k * NTHR) * 8);
+#pragma unroll
+    for (int k = 0; k < X_PER_THREAD; ++k) {
+        const int c = tid + k * NTHR, sr = c / (SP / 8), k0 = 8 * (c - sr * (SP / 8));
+        const int row = wg * BT + sr;
+        const bool ok = row < B;
+        const uint16_t* src = (const uint16_t*)a.states + (int64_t)(ok ? row : B - 1) * a.ld;
+        u32x4 x;
+        if (XVEC) {
+            x = *(const u32x4*)(src + k0);
+        } else {
+            uint16_t t8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint16_t v = src[min(k0 + e, S - 1)];
+                t8[e] = (uint16_t)keep_if(k0 + e < S, (uint32_t)v);
+            }
+            x = u32x4{(uint32_t)t8[0] | ((uint32_t)t8[1] << 16), (uint32_t)t8[2] | ((uint32_t)t8[3] << 16),
+                      (uint32_t)t8[4] | ((uint32_t)t8[5] << 16), (uint32_t)t8[6] | ((uint32_t)t8[7] << 16)};
+        }
+        xr[k] = u32x4{keep_if(ok, x.x), keep_if(ok, x.y), keep_if(ok, x.z), keep_if(ok, x.w)};
+    }
+    const int th = tid < H ? tid : 0;
+    const float vb1 = prm[po.b1 + th], vb2 = prm[po.b2 + th], vw3 = prm[po.w3 + th];
+    const float qb = a.q[bc];  // used by valid lanes only
+    const float b3 = prm[po.b3];
+    float qa[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qa[k] = a.out_pi ? a.q_all[(int64_t)bc * a.A + min(q + 4 * k, a.A - 1)] : 0.f;
+#pragma unroll
+    for (int k = 0; k < W1_PER_THREAD; ++k) {
+        const int idx = (tid + k * NTHR) * 8, r = idx / SP, c = idx - r * SP;
+        *(u32x4*)(R0 + r * C::LDW1 + c) = w1r[k];
+    }
+#pragma unroll
+    for (int k = 0; k < W2_PER_THREAD; ++k) {
+        const int idx = (tid + k * NTHR) * 8, r = idx / H, c = idx - r * H;
+        *(u32x4*)(R1 + r * C::LDW2 + c) = w2r[k];
+    }
+#pragma unroll
+    for (int k = 0; k < X_PER_THREAD; ++k) {
+        const int c = tid + k * NTHR, sr = c / (SP / 8), k0 = 8 * (c - sr * (SP / 8));
+        *(u32x4*)(R2 + nat_off(sr, k0)) = xr[k];
+    }
+    if (tid < H) {
+        sb1[tid] = vb1;
+        sb2[tid] = vb2;
+        sw3[tid] = vw3;
+    }
+    __syncthreads();
+
+    // ---- F1: z1^T = W1 s^T + b1 for this wave's 64 features
+    f32x4v acc[FT];
+#pragma unroll
+    for (int t = 0; t < FT; ++t) acc[t] = *(const f32x4v*)(sb1 + fb + 16 * t + 4 * q);
+#pragma unroll
+    for (int u = 0; u < KU1; ++u) {
+        const bf16x8 xb = ld8(R2 + nat_off(bl, 32 * u + 8 * q));
+#pragma unroll
+        for (int t = 0; t < FT; ++t)
+            acc[t] = mma16(ld8(R0 + (fb + 16 * t + l16) * C::LDW1 + 32 * u + 8 * q), xb, acc[t]);
+    }
+    uint32_t mask1 = 0u;  // relu'(z1), bit 4t + r
+#pragma unroll
+    for (int t = 0; t < FT; ++t) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float y = acc[t][r] > 0.f ? acc[t][r] : 0.f;
+            acc[t][r] = y;
+            mask1 |= ((__float_as_uint(y) + 0x7FFFFFFFu) >> 31) << (4 * t + r);
+        }
+        put4(R3, bl, fb + 16 * t + 4 * q, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);  // h1
+    }
+    __syncthreads();
+
+    // ---- F2: z2^T = W2 h1^T + b2, V = w3 . relu(z2) + b3 over both halves
+#pragma unroll
+    for (int t = 0; t < FT; ++t) acc[t] = *(const f32x4v*)(sb2 + fb + 16 * t + 4 * q);
+#pragma unroll
+    for (int u = 0; u < KUH; ++u) {
+        const bf16x8 hb = ld8(R3 + nat_off(bl, 32 * u + 8 * q));
+#pragma unroll
+        for (int t = 0; t < FT; ++t)
+            acc[t] = mma16(ld8(R1 + (fb + 16 * t + l16) * C::LDW2 + 32 * u + 8 * q), hb, acc[t]);
+    }
+    f32x4v w3v[FT];
+#pragma unroll
+    for (int t = 0; t < FT; ++t) w3v[t] = *(const f32x4v*)(sw3 + fb + 16 * t + 4 * q);
+    float vpart = 0.f;
+#pragma unroll
+    for (int t = 0; t < FT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vpart = fmaf(w3v[t][r], acc[t][r] > 0.f ? acc[t][r] : 0.f, vpart);
+    vpart = sum_q4(vpart);
+    if (q == 0) svh[fh * BT + bl] = vpart;
+    __syncthreads();
+    const float v = (svh[bl] + svh[BT + bl]) + b3;
+    float dv = 0.f, lterm = 0.f;
+    if (valid) {
+        const float diff = qb - v;
+        const float w = diff >= 0.f ? tau : 1.f - tau;
+        lterm = w * diff * diff;
+        dv = -2.f * w * diff * a.invB;
+        if (fh == 0 && q == 0 && a.out_v) a.out_v[(int64_t)g * B + b] = v;
+    }
+    // the two waves of a sample group split the epilogue: half 0 the loss
+    // sums, half 1 the policy
+    if (fh == 0) {
+        const float ls = row_sum16(lterm);
+        const float ds = row_sum16(dv);
+        if (lane == 0) { sred[sg] = ls; sred[NW / 2 + sg] = ds; }
+    } else {
+        if (a.out_pi) {
+            // pi = softmax(beta * clamp(Q - V, -10, 10)) with the row maximum
+            // subtracted ("Current State / IQL (CPU)", advantage-weighted
+            // action selection); the four lanes of a sample share it
+            float x[4], mx = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const bool on = q + 4 * k < a.A;
+                x[k] = on ? a.beta * fminf(fmaxf(qa[k] - v, -10.f), 10.f) : -INFINITY;
+                mx = fmaxf(mx, x[k]);
+            }
+            mx = max_q4(mx);
+            float se = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                x[k] = q + 4 * k < a.A ? expf(x[k] - mx) : 0.f;
+                se += x[k];
+            }
+            se = sum_q4(se);
+            if (valid) {
+                float* pr = a.out_pi + ((int64_t)g * B + b) * a.A;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (q + 4 * k < a.A) pr[q + 4 * k] = x[k] / se;
+            }
+        }
+    }
+    // dz2 = dv w3 relu'(z2) -> R0 (W1 is dead); dw3 over this sample group
+#pragma unroll
+    for (int t = 0; t < FT; ++t) {
+        float hd[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float z = acc[t][r];
+            hd[r] = row_sum16(z > 0.f ? z * dv : 0.f);
+            acc[t][r] = z > 0.f ? dv * w3v[t][r] : 0.f;
+        }
+        put4(R0, bl, fb + 16 * t + 4 * q, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+        if (l16 == 0) *(f32x4v*)(sdw3 + sg * H + fb + 16 * t + 4 * q) = f32x4v{hd[0], hd[1], hd[2], hd[3]};
+    }
+    __syncthreads();
+
+    // ---- W2^T to R1 (W2 is dead); loss, db3, dw3; dW2 = dz2^T h1 with db2
+    {
+        u32x4 w2t[W2_PER_THREAD];
+#pragma unroll
+        for (int k = 0; k < W2_PER_THREAD; ++k) w2t[k] = *(const u32x4*)(w2ts + (tid + k * NTHR) * 8);
+        if (tid < H) {
+            float s3 = 0.f;
+#pragma unroll
+            for (int i = 0; i < NW / 2; ++i) s3 += sdw3[i * H + tid];
+            part[po.w3 + tid] = s3;
+        }
+        if (tid == 0) {
+            float ls = 0.f, ds = 0.f;
+            for (int i = 0; i < NW / 2; ++i) { ls += sred[i]; ds += sred[NW / 2 + i]; }
+            a.loss_part[(int64_t)g * a.nwg + wg] = ls;
+            part[po.b3] = ds;
+        }
+        nat_gemm16_part<H / 32>(R0, R3, sg, (H / 32) * fh, part + po.w2, H, H, fh == 0 ? part + po.b2 : nullptr);
+#pragma unroll
+        for (int k = 0; k < W2_PER_THREAD; ++k) {
+            const int idx = (tid + k * NTHR) * 8, r = idx / H, c = idx - r * H;
+            *(u32x4*)(R1 + r * C::LDW2 + c) = w2t[k];
+        }
+    }
+    __syncthreads();
+
+    // ---- B1: dh1^T = W2^T dz2^T for this wave's features; dz1 -> R3 (h1 is dead)
+#pragma unroll
+    for (int t = 0; t < FT; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < KUH; ++u) {
+        const bf16x8 db = ld8(R0 + nat_off(bl, 32 * u + 8 * q));
+#pragma unroll
+        for (int t = 0; t < FT; ++t)
+            acc[t] = mma16(ld8(R1 + (fb + 16 * t + l16) * C::LDW2 + 32 * u + 8 * q), db, acc[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < FT; ++t) {
+        float d[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) d[r] = (mask1 >> (4 * t + r)) & 1u ? acc[t][r] : 0.f;
+        put4(R3, bl, fb + 16 * t + 4 * q, d[0], d[1], d[2], d[3]);
+    }
+    __syncthreads();
+
+    // ---- dW1 = dz1^T s with db1
+    nat_gemm16_part<SP / 32>(R3, R2, sg, (SP / 32) * fh, part + po.w1, S, S, fh == 0 ? part + po.b1 : nullptr);
+}
+
+template <int SP, int H, bool XVEC>
+static hipError_t run_fused16w_x(const FusedArgs& fa, int G, hipStream_t stream, hipEvent_t ev0,
+                                 hipEvent_t ev1) {
+    typedef Fused16wCfg<SP, H> C;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)iql_fused16w_kernel<SP, H, XVEC>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::BYTES);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    if (ev0)
+        hipExtLaunchKernelGGL((iql_fused16w_kernel<SP, H, XVEC>), dim3(fa.nwg, G), dim3(1024), C::BYTES, stream,
+                              ev0, ev1, 0, fa);
+    else
+        hipLaunchKernelGGL((iql_fused16w_kernel<SP, H, XVEC>), dim3(fa.nwg, G), dim3(1024), C::BYTES, stream, fa);
+    return hipGetLastError();
+}
+
+template <int SP, int H>
+static hipError_t run_fused16w(const FusedArgs& fa, int G, hipStream_t stream, hipEvent_t ev0,
+                               hipEvent_t ev1) {
+    const bool xvec = fa.S == SP && fa.ld % 8 == 0 && ((uintptr_t)fa.states % 16) == 0;
+    return xvec ? run_fused16w_x<SP, H, true>(fa, G, stream, ev0, ev1)
+                : run_fused16w_x<SP, H, false>(fa, G, stream, ev0, ev1);
+}
+
 // ------------------------------------------------------------- dispatch
 template <typename T, int SP, int H, int NW, bool XVEC>
 static hipError_t run_fused_x(const FusedArgs& fa, int G, hipStream_t stream, hipEvent_t ev0,
@@ -1023,8 +1361,8 @@ struct Variant {
 };
 static const Variant kVariants[] = {
     // bf16, hidden 128: eight 16-sample waves per 128-sample workgroup
-    {1, 128, 128, 4, &run_fused16<128, 128>},
-    {1, 64, 128, 4, &run_fused16<64, 128>},
+    {1, 128, 128, 4, &run_fused16w<128, 128>},
+    {1, 64, 128, 4, &run_fused16w<64, 128>},
     {1, 32, 32, 4, &run_fused<uint16_t, 32, 32, 4>},
     {0, 32, 32, 4, &run_fused<float, 32, 32, 4>},
     {0, 64, 128, 1, &run_fused<float, 64, 128, 1>},

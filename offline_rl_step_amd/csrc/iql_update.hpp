@@ -26,8 +26,9 @@ template <> IQLH_DEV uint16_t to_shadow<uint16_t>(float x) {
 // thread streams float4 quads of four parameters, so a wave keeps many
 // independent 16-byte loads in flight (unrolling further measured no faster:
 // the read runs at the chip's streaming rate).
-constexpr int kRedParams = 128;
-constexpr int kRedSlices = 8;
+constexpr int kRedLanes = 32;                 // threads per slice, 4 parameters each
+constexpr int kRedSlices = 256 / kRedLanes;
+constexpr int kRedParams = 4 * kRedLanes;     // parameters per block (divides 128)
 
 // Block bx (of rb per group) of group g.
 IQLH_DEV void iql_reduce_block(const float* __restrict__ part, const float* __restrict__ loss_part, int nwg,
@@ -35,9 +36,9 @@ IQLH_DEV void iql_reduce_block(const float* __restrict__ part, const float* __re
                                float* __restrict__ sq_part, int rb, int32_t* __restrict__ tcount,
                                int64_t* __restrict__ step, float* __restrict__ out_loss,
                                int32_t* __restrict__ flags, int bx, int g) {
-    __shared__ f32x4 red[kRedSlices][32];
+    __shared__ f32x4 red[kRedSlices][kRedLanes];
     __shared__ float wred[4];
-    const int tid = threadIdx.x, q = tid & 31, sl = tid >> 5;
+    const int tid = threadIdx.x, q = tid % kRedLanes, sl = tid / kRedLanes;
     const int64_t p0 = (int64_t)bx * kRedParams + 4 * q;  // < Pp
     const float* src = part + (int64_t)g * nwg * Pp + p0;
     // block 0's share of the loss partials, issued with the gradient loads
