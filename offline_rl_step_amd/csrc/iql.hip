@@ -12,26 +12,24 @@
 // "2C. Grouped GEMM for IQL") run as one grouped launch: blockIdx.y = group.
 //
 // MI355X design (not the pages' warp-per-sample kernel nor a chain of library
-// GEMMs):
-//   * One workgroup = NW wave64s = BT = 32*NW samples of one group.  Each wave
-//     owns 32 samples and computes every hidden feature for them with
-//     v_mfma_f32_32x32x16_bf16 (bf16 operands, fp32 accumulate) or
-//     v_mfma_f32_32x32x2f32, in the feature-major orientation
-//     D[feature][sample] = W[feature][k] * act[sample][k].
-//   * The accumulator layout of one layer (lane = sample, registers = four
-//     runs of four features) is fed back, rounded to the operand type, as the
-//     B operand of the next layer; the weight operand is read from LDS with
-//     its k columns permuted to the same order.  h1 never leaves registers for
-//     layer 2, nor dz2 for the dh1 = W2^T dz2 product.
-//   * The weight gradients reduce over samples (K = batch); their operands are
-//     written to LDS transposed ([feature][sample], padded rows) once, and the
-//     products dW2 = dz2^T h1 and dW1 = dz1^T s run from LDS.  Bias gradients
-//     and dw3 are row sums of the same LDS tiles.
-//   * W1, W2 and W2^T come from operand-typed shadows written by the Adam
-//     kernel, so no conversion or transpose happens in the hot kernel.
-//   * Gradients leave the workgroup as fp32 partials; a second kernel sums
-//     them in workgroup order (no float atomics: bitwise reproducible) and a
-//     third applies the clip and Adam and refreshes the shadows.
+// GEMMs): one workgroup holds 128 samples of one group and runs the whole
+// forward, loss and backward for them on MFMA, with the weights and the
+// activations in LDS; gradients leave the workgroup as fp32 partials, a
+// second kernel sums them in workgroup order (no float atomics: bitwise
+// reproducible) and a third applies the clip and Adam and refreshes the
+// operand-typed W1 / W2 / W2^T shadows the next step reads (no conversion or
+// transpose in the hot kernel).  Two kernels:
+//   * iql_fused16w_kernel (bf16 operands, hidden 128): sixteen wave64s,
+//     v_mfma_f32_16x16x32_bf16, activations in natural [sample][feature]
+//     tiles read back with LDS transpose loads; described at its definition.
+//   * iql_fused_kernel (fp32 operands, small hidden widths): NW wave64s of 32
+//     samples each on v_mfma_f32_32x32x16_bf16 / v_mfma_f32_32x32x2f32 in the
+//     orientation D[feature][sample] = W[feature][k] act[sample][k]; the
+//     accumulators of one layer are fed back, rounded to the operand type, as
+//     the B operand of the next (the weight operand is read with its k
+//     columns permuted to the same order), and the weight-gradient operands
+//     are written to LDS transposed ([feature][sample]); bias gradients and
+//     dw3 are row sums of the same tiles through an all-ones operand.
 #include <hip/hip_ext.h>
 
 #include "common.hpp"
@@ -532,26 +530,16 @@ __global__ __launch_bounds__(256) void iql_shadow_kernel(IqlDims d, IqlBuffers b
     }
 }
 
-// ---------------------------------------------------- 16x16 MFMA variant
-// Same computation as iql_fused_kernel for bf16 operands and hidden 128, with
-// eight wave64s per workgroup (two per SIMD, so one wave's LDS and memory
-// waits overlap the other's MFMA work).  Each wave owns 16 samples and uses
-// v_mfma_f32_16x16x32_bf16: D[feature][sample] 16x16 tiles, lane l holding
-// sample l & 15 and features 4 (l >> 4) + r, r = 0..3.  The chained B operand
-// of the next layer packs two such tiles (32 features), and the weight
-// operand is read with the same k order (two 8-byte runs per lane).
+// ---------------------------------------------- 16x16 MFMA building blocks
+// v_mfma_f32_16x16x32_bf16: D[16][16] tiles, lane l holding column l & 15 and
+// rows 4 (l >> 4) + r, r = 0..3; A and B operands hold 8 consecutive k per
+// lane (k = 8 (l >> 4) + 0..7 of a 32-wide step).
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 IQLH_DEV f32x4v mma16(bf16x8 a, bf16x8 b, f32x4v c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 IQLH_DEV bf16x8 ld8(const uint16_t* p) { return __builtin_bit_cast(bf16x8, *(const u32x4*)p); }
-// chained weight fragment of k step u (32 features) for lane group q
-IQLH_DEV bf16x8 ld_chain16(const uint16_t* row, int u, int q) {
-    const u32x2 lo = *(const u32x2*)(row + 32 * u + 4 * q);
-    const u32x2 hi = *(const u32x2*)(row + 32 * u + 16 + 4 * q);
-    return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-}
 // Cross-lane sums and maxima of the 16x16 kernel on VALU lane permutes
 // (v_permlane16/32_swap, DPP) rather than LDS-routed shuffles.
 // Over the four lane groups q (rows of 16 lanes) holding one sample, the
@@ -576,28 +564,6 @@ IQLH_DEV float row_sum16(float x) {
     x += __builtin_amdgcn_update_dpp(0.f, x, 0x122, 0xF, 0xF, false);  // row_ror:2
     x += __builtin_amdgcn_update_dpp(0.f, x, 0x121, 0xF, 0xF, false);  // row_ror:1
     return x;
-}
-
-// acc[t] += sum_u A(t, u) B[u] over NT row tiles and KU k steps, with the A
-// fragments read from LDS one k step ahead (double-buffered in registers):
-// the reads of step u + 1 are in flight while the MFMAs of step u run, so a
-// wave waits for LDS once per k step instead of once per MFMA.
-template <int NT, int KU, int RD, typename LoadA>
-IQLH_DEV void mma16_pipelined(f32x4v (&acc)[NT], const bf16x8 (&bop)[KU], LoadA load_a) {
-#pragma unroll
-    for (int u = 0; u < KU; ++u)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = mma16(load_a(t, u), bop[u], acc[t]);
-}
-
-// chained B operand of k step u from tiles 2u, 2u + 1 of a layer's accumulators
-template <int NT>
-IQLH_DEV bf16x8 chain_from16(const f32x4v (&acc)[NT], int u) {
-    const f32x4v& a = acc[2 * u];
-    const f32x4v& b = acc[2 * u + 1];
-    typedef Op<uint16_t> O;
-    return __builtin_bit_cast(bf16x8, u32x4{O::cvt2(a[0], a[1]), O::cvt2(a[2], a[3]), O::cvt2(b[0], b[1]),
-                                             O::cvt2(b[2], b[3])});
 }
 
 // ---- activation tiles of the 16x16 kernel: natural [sample][feature]
@@ -649,314 +615,6 @@ IQLH_DEV bf16x8 frag_nat(const uint16_t* tile, const NatLane& L, int c, int u) {
     const u32x2 lo = ld_tr4(tile + L.base[0][c & 1] + off);
     const u32x2 hi = ld_tr4(tile + L.base[1][c & 1] + off);
     return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-}
-
-// C[i][j] = sum_s A[s][i] B[s][j] over the 128 samples of two natural tiles,
-// for row tile rt (16 rows i) and column tiles [0, NCT) of 16; stores C rows
-// to dst (ldo, j < ncols) and, through the all-ones operand, the column sums
-// of A (sum over samples) to bias_dst.
-template <int NCT>
-IQLH_DEV void nat_gemm16_row(const uint16_t* A, const uint16_t* Bm, int rt, float* dst, int ldo, int ncols,
-                             float* bias_dst) {
-    const int lane = threadIdx.x & 63, l16 = lane & 15, q = lane >> 4;
-    const bf16x8 one = Op<uint16_t>::ones();
-    f32x4v acc[NCT], accb = f32x4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < NCT; ++c) acc[c] = f32x4v{0.f, 0.f, 0.f, 0.f};
-    // operands of k step u + 1 read while the MFMAs of step u run
-    const NatLane L = nat_lane();
-    bf16x8 fa[2], fb[2][NCT];
-    fa[0] = frag_nat(A, L, rt, 0);
-#pragma unroll
-    for (int c = 0; c < NCT; ++c) fb[0][c] = frag_nat(Bm, L, c, 0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        if (u + 1 < 4) {
-            fa[(u + 1) & 1] = frag_nat(A, L, rt, u + 1);
-#pragma unroll
-            for (int c = 0; c < NCT; ++c) fb[(u + 1) & 1][c] = frag_nat(Bm, L, c, u + 1);
-        }
-#pragma unroll
-        for (int c = 0; c < NCT; ++c) acc[c] = mma16(fa[u & 1], fb[u & 1][c], acc[c]);
-        accb = mma16(fa[u & 1], one, accb);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (NCT + 1), 0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        if (u + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2 * (NCT + 1), 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, NCT + 1, 0);
-    }
-    float* d0 = dst + (16 * rt + 4 * q) * ldo;
-#pragma unroll
-    for (int c = 0; c < NCT; ++c) {
-        const int j = 16 * c + l16;
-        if (j < ncols) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) d0[r * ldo + j] = acc[c][r];
-        }
-    }
-    if (l16 == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) bias_dst[16 * rt + 4 * q + r] = accb[r];
-    }
-}
-
-// LDS plan of the 16x16 kernel: R0 = W1 then dz2, R1 = W2 then W2^T,
-// R2 = h2 dv then dz1, R3 = h1 then s (activation tiles natural, 128 rows).
-template <int SP, int H>
-struct Fused16Cfg {
-    static constexpr int BT = 128;
-    static constexpr int LDW1 = SP + 8, LDW2 = H + 8;  // weight rows, 16-byte padded
-    static constexpr int NAT = BT * kNatLd;            // one activation tile
-    static constexpr int R0 = (H * LDW1 > NAT) ? H * LDW1 : NAT;
-    static constexpr int R1 = H * LDW2;
-    static constexpr int R2 = NAT;
-    static constexpr int R3 = NAT;
-    static constexpr size_t BYTES = (size_t)(R0 + R1 + R2 + R3) * 2 + (size_t)(3 * H + 16) * sizeof(float);
-    static_assert(BYTES <= 160 * 1024, "LDS budget");
-    static_assert(SP <= kNatLd - 16 && H <= kNatLd - 16, "natural tile width");
-};
-
-template <int SP, int H, bool XVEC>
-__global__ __launch_bounds__(512) void iql_fused16_kernel(FusedArgs a) {
-    typedef Op<uint16_t> O;
-    typedef Fused16Cfg<SP, H> C;
-    constexpr int NW = 8, BT = 128, NT = H / 16, KU1 = SP / 32, KUH = H / 32, NTHR = 512;
-    static_assert(H == 128 && SP % 32 == 0 && SP <= 128, "tile shape");
-    extern __shared__ __align__(16) unsigned char smem[];
-    uint16_t* R0 = (uint16_t*)smem;
-    uint16_t* R1 = R0 + C::R0;
-    uint16_t* R2 = R1 + C::R1;
-    uint16_t* R3 = R2 + C::R2;
-    float* sb1 = (float*)(R3 + C::R3);
-    float* sb2 = sb1 + H;
-    float* sw3 = sb2 + H;
-    float* sred = sw3 + H;  // [2][NW]
-
-    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = blockIdx.y, wg = blockIdx.x;
-    const int S = a.S, B = a.B;
-    const POff po(S, H);
-    const float* prm = a.params + (int64_t)g * a.P;
-    const uint16_t* w1s = (const uint16_t*)a.w1s + (int64_t)g * H * SP;
-    const uint16_t* w2s = (const uint16_t*)a.w2s + (int64_t)g * H * H;
-    const uint16_t* w2ts = (const uint16_t*)a.w2ts + (int64_t)g * H * H;
-    float* part = a.part + ((int64_t)g * a.nwg + wg) * a.Pp;
-    const float tau = g == 0 ? a.tau0 : a.tau1;
-
-    // ---- S0: weights and small vectors to LDS, this lane's sample row to
-    // registers.  A wave waits for a load by draining every load it issued
-    // before it, so loads are issued in the order they are consumed and none
-    // sits behind a lane-dependent branch (indexes are clamped into range,
-    // unused values masked): the weight shadows, the target, b3, Q(s, .),
-    // the W2^T shadow (staged into R1 once W2 is dead), the sample row.
-    const int bl = 16 * wv + l16;
-    const int b = wg * BT + bl;
-    const bool valid = b < B;
-    const int bc = valid ? b : B - 1;
-    constexpr int W1_PER_THREAD = H * SP / (NTHR * 8);
-    constexpr int W2_PER_THREAD = H * H / (NTHR * 8);
-    constexpr int W2T_PER_THREAD = H * H / (NTHR * 8);
-    static_assert(W1_PER_THREAD * NTHR * 8 == H * SP && W2_PER_THREAD * NTHR * 8 == H * H, "staging split");
-    u32x4 w1r[W1_PER_THREAD], w2r[W2_PER_THREAD], w2t[W2T_PER_THREAD];
-#pragma unroll
-    for (int k = 0; k < W1_PER_THREAD; ++k) w1r[k] = *(const u32x4*)(w1s + (tid + k * NTHR) * 8);
-#pragma unroll
-    for (int k = 0; k < W2_PER_THREAD; ++k) w2r[k] = *(const u32x4*)(w2s + (tid + k * NTHR) * 8);
-    const int th = tid < H ? tid : 0;
-    const float vb1 = prm[po.b1 + th], vb2 = prm[po.b2 + th], vw3 = prm[po.w3 + th];
-    const float qb = a.q[bc];  // used by valid lanes only
-    const float b3 = prm[po.b3];
-    // Q(s, .) of this lane's sample for the fused policy: lane group q takes
-    // actions q, q + 4, q + 8, q + 12
-    float qa[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int act = q + 4 * k;
-        // used by valid lanes and actions < A only
-        qa[k] = a.out_pi ? a.q_all[(int64_t)bc * a.A + min(act, a.A - 1)] : 0.f;
-    }
-#pragma unroll
-    for (int k = 0; k < W2T_PER_THREAD; ++k) w2t[k] = *(const u32x4*)(w2ts + (tid + k * NTHR) * 8);
-    bf16x8 xf[KU1];
-    {
-        const uint16_t* xr = (const uint16_t*)a.states + (int64_t)bc * a.ld;
-#pragma unroll
-        for (int u = 0; u < KU1; ++u) {
-            const int k0 = 32 * u + 8 * q;
-            bf16x8 x;
-            if (XVEC) {
-                x = ld8(xr + k0);
-            } else {
-                uint16_t tmp[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint16_t v = xr[min(k0 + e, S - 1)];
-                    tmp[e] = (uint16_t)keep_if(k0 + e < S, (uint32_t)v);
-                }
-                x = O::make(tmp);
-            }
-            const u32x4 xb = __builtin_bit_cast(u32x4, x);
-            xf[u] = __builtin_bit_cast(bf16x8, u32x4{keep_if(valid, xb.x), keep_if(valid, xb.y), keep_if(valid, xb.z),
-                                                     keep_if(valid, xb.w)});
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < W1_PER_THREAD; ++k) {
-        const int idx = (tid + k * NTHR) * 8, r = idx / SP, c = idx - r * SP;
-        *(u32x4*)(R0 + r * C::LDW1 + c) = w1r[k];
-    }
-#pragma unroll
-    for (int k = 0; k < W2_PER_THREAD; ++k) {
-        const int idx = (tid + k * NTHR) * 8, r = idx / H, c = idx - r * H;
-        *(u32x4*)(R1 + r * C::LDW2 + c) = w2r[k];
-    }
-    if (tid < H) {
-        sb1[tid] = vb1;
-        sb2[tid] = vb2;
-        sw3[tid] = vw3;
-    }
-    __syncthreads();
-
-    // ---- F1: z1^T = W1 s^T + b1 (the bias is the accumulators' initial value)
-    f32x4v acc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = *(const f32x4v*)(sb1 + 16 * t + 4 * q);
-    mma16_pipelined<NT, KU1, 1>(acc, xf, [&](int t, int u) { return ld8(R0 + (16 * t + l16) * C::LDW1 + 32 * u + 8 * q); });
-    uint32_t mask1 = 0u;  // relu'(z1), bit 4t + r
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float z = acc[t][r];
-            const float y = z > 0.f ? z : 0.f;
-            acc[t][r] = y;
-            mask1 |= ((__float_as_uint(y) + 0x7FFFFFFFu) >> 31) << (4 * t + r);
-        }
-        put4(R3, bl, 16 * t + 4 * q, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);  // h1
-    }
-    bf16x8 h1f[KUH];
-#pragma unroll
-    for (int u = 0; u < KUH; ++u) h1f[u] = chain_from16<NT>(acc, u);
-    __syncthreads();
-
-    // ---- F2: z2^T = W2 h1^T + b2 (bias as the initial value)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = *(const f32x4v*)(sb2 + 16 * t + 4 * q);
-    mma16_pipelined<NT, KUH, 2>(acc, h1f, [&](int t, int u) { return ld_chain16(R1 + (16 * t + l16) * C::LDW2, u, q); });
-    f32x4v w3v[NT];  // this lane's w3 entries, read together
-#pragma unroll
-    for (int t = 0; t < NT; ++t) w3v[t] = *(const f32x4v*)(sw3 + 16 * t + 4 * q);
-    float vpart = 0.f;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float z = acc[t][r];
-            vpart = fmaf(w3v[t][r], z > 0.f ? z : 0.f, vpart);
-        }
-    const float v = sum_q4(vpart) + b3;
-    float dv = 0.f, lterm = 0.f;
-    if (valid) {
-        const float diff = qb - v;
-        const float w = diff >= 0.f ? tau : 1.f - tau;
-        lterm = w * diff * diff;
-        dv = -2.f * w * diff * a.invB;
-        if (q == 0 && a.out_v) a.out_v[(int64_t)g * B + b] = v;
-    }
-    {
-        // lanes 0..15 (lane group 0) hold one copy of each of the wave's samples
-        const float ls = row_sum16(lterm);
-        const float ds = row_sum16(dv);
-        if (lane == 0) { sred[wv] = ls; sred[NW + wv] = ds; }
-    }
-    if (a.out_pi) {
-        // pi = softmax(beta * clamp(Q - V, -10, 10)) with the row maximum
-        // subtracted ("Current State / IQL (CPU)", advantage-weighted action
-        // selection); the four lanes of a sample share it through shuffles
-        float x[4], mx = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const bool on = q + 4 * k < a.A;
-            x[k] = on ? a.beta * fminf(fmaxf(qa[k] - v, -10.f), 10.f) : -INFINITY;
-            mx = fmaxf(mx, x[k]);
-        }
-        mx = max_q4(mx);
-        float se = 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            x[k] = q + 4 * k < a.A ? expf(x[k] - mx) : 0.f;
-            se += x[k];
-        }
-        se = sum_q4(se);
-        if (valid) {
-            float* pr = a.out_pi + ((int64_t)g * B + b) * a.A;
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (q + 4 * k < a.A) pr[q + 4 * k] = x[k] / se;
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        float hd[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float z = acc[t][r];
-            hd[r] = z > 0.f ? z * dv : 0.f;
-            acc[t][r] = z > 0.f ? dv * w3v[t][r] : 0.f;
-        }
-        put4(R0, bl, 16 * t + 4 * q, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);  // dz2
-        put4(R2, bl, 16 * t + 4 * q, hd[0], hd[1], hd[2], hd[3]);                  // h2 dv
-    }
-    bf16x8 dz2f[KUH];
-#pragma unroll
-    for (int u = 0; u < KUH; ++u) dz2f[u] = chain_from16<NT>(acc, u);
-    __syncthreads();
-
-    // ---- dw3 (row sums of h2 dv), loss, db3; W2^T to R1; dW2 = dz2^T h1 with db2
-    {
-        const bf16x8 one = O::ones();
-        f32x4v s3 = f32x4v{0.f, 0.f, 0.f, 0.f};
-        const NatLane L = nat_lane();
-#pragma unroll
-        for (int u = 0; u < 4; ++u) s3 = mma16(frag_nat(R2, L, wv, u), one, s3);
-        if (l16 == 0) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) part[po.w3 + 16 * wv + 4 * q + r] = s3[r];
-        }
-    }
-    if (tid == 0) {
-        float ls = 0.f, ds = 0.f;
-        for (int i = 0; i < NW; ++i) { ls += sred[i]; ds += sred[NW + i]; }
-        a.loss_part[(int64_t)g * a.nwg + wg] = ls;
-        part[po.b3] = ds;
-    }
-#pragma unroll
-    for (int k = 0; k < W2T_PER_THREAD; ++k) {
-        const int idx = (tid + k * NTHR) * 8, r = idx / H, c = idx - r * H;
-        *(u32x4*)(R1 + r * C::LDW2 + c) = w2t[k];
-    }
-    nat_gemm16_row<H / 16>(R0, R3, wv, part + po.w2, H, H, part + po.b2);
-    __syncthreads();
-
-    // ---- s^T to R3; B1: dh1^T = W2^T dz2^T; dz1 = dh1 relu'(z1) -> R2
-#pragma unroll
-    for (int u = 0; u < KU1; ++u) *(u32x4*)(R3 + nat_off(bl, 32 * u + 8 * q)) = __builtin_bit_cast(u32x4, xf[u]);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
-    mma16_pipelined<NT, KUH, 2>(acc, dz2f, [&](int t, int u) { return ld_chain16(R1 + (16 * t + l16) * C::LDW2, u, q); });
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        float d[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) d[r] = (mask1 >> (4 * t + r)) & 1u ? acc[t][r] : 0.f;
-        put4(R2, bl, 16 * t + 4 * q, d[0], d[1], d[2], d[3]);  // dz1
-    }
-    __syncthreads();
-
-    // ---- dW1 = dz1^T s with db1
-    nat_gemm16_row<SP / 16>(R2, R3, wv, part + po.w1, S, S, part + po.b1);
 }
 
 // ------------------------------------------------- 16-wave 16x16 variant
@@ -1316,34 +974,6 @@ static hipError_t run_fused_x(const FusedArgs& fa, int G, hipStream_t stream, hi
         hipLaunchKernelGGL((iql_fused_kernel<T, SP, H, NW, XVEC>), dim3(fa.nwg, G), dim3(64 * NW),
                            C::BYTES, stream, fa);
     return hipGetLastError();
-}
-
-template <int SP, int H, bool XVEC>
-static hipError_t run_fused16_x(const FusedArgs& fa, int G, hipStream_t stream, hipEvent_t ev0,
-                                hipEvent_t ev1) {
-    typedef Fused16Cfg<SP, H> C;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)iql_fused16_kernel<SP, H, XVEC>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::BYTES);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    const size_t lds = C::BYTES;  // sred holds 2 x 8 waves
-    if (ev0)
-        hipExtLaunchKernelGGL((iql_fused16_kernel<SP, H, XVEC>), dim3(fa.nwg, G), dim3(512), lds, stream, ev0, ev1,
-                              0, fa);
-    else
-        hipLaunchKernelGGL((iql_fused16_kernel<SP, H, XVEC>), dim3(fa.nwg, G), dim3(512), lds, stream, fa);
-    return hipGetLastError();
-}
-
-template <int SP, int H>
-static hipError_t run_fused16(const FusedArgs& fa, int G, hipStream_t stream, hipEvent_t ev0,
-                              hipEvent_t ev1) {
-    const bool xvec = fa.S == SP && fa.ld % 8 == 0 && ((uintptr_t)fa.states % 16) == 0;
-    return xvec ? run_fused16_x<SP, H, true>(fa, G, stream, ev0, ev1)
-                : run_fused16_x<SP, H, false>(fa, G, stream, ev0, ev1);
 }
 
 template <typename T, int SP, int H, int NW>
