@@ -49,6 +49,10 @@ def parse():
     p.add_argument("--kernel-reps", type=int, default=200)
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run 10 plain device copies of MIB MiB (counter calibration) and exit")
+    p.add_argument("--summarize-profiles", metavar="DIR", default=None,
+                   help="only write the profile summaries (markdown + traffic JSON) into profiles/ from the "
+                        "rocprofv3 CSV output under DIR (trace/, FETCH_SIZE/, WRITE_SIZE/, copy_FETCH_SIZE/, "
+                        "copy_WRITE_SIZE/); needs no GPU")
     return p.parse_args()
 
 
@@ -71,6 +75,42 @@ def fused_flops_per_launch(w):
     (dh1, dW2, dW1) and 5H for the output layer, dw3 and the bias sums."""
     S, H = w.S, w.H
     return w.groups * w.B * (4 * S * H + 6 * H * H + 5 * H)
+
+
+def partial_layout(w):
+    """Per-workgroup gradient partials of the forward/backward launch: one row
+    of P rounded up to 128 floats per 128-sample workgroup and trainer."""
+    P = w.S * w.H + w.H + w.H * w.H + w.H + w.H + 1
+    return P, (P + 127) // 128 * 128, (w.B + 127) // 128
+
+
+def launch_bytes(w):
+    """Bytes each of the four launches of one step must read and write, given
+    its inputs and outputs (what a perfect cache would leave of its traffic):
+      relabel+norms: per HER row, source s and s' rows (f32), the donor's goal,
+                     the source index, action, done and two episode ends;
+                     written: the bf16 state row, the f32 s' row, action,
+                     reward, done, donor.  Norms: every budget source once.
+      fwd_bwd:       the bf16 batch, q_taken, Q, the weight shadows and biases
+                     of every trainer; written: V, the policy and the
+                     per-workgroup gradient partials.
+      reduce_saxpy:  the partials and loss partials, the gradient written; the
+                     budget sources again, the accumulated gradient written.
+      adam:          p, m, v, g read and written (g zeroed) per parameter of
+                     both trainers and of the budgeted network, plus the bf16
+                     weight shadows the trainers' update rewrites."""
+    n, S, H, A, B, grp = w.n_her, w.S, w.H, w.A, w.B, w.groups
+    k, nb = 4, w.n_budget
+    P, Pp, nwg = partial_layout(w)
+    shadows = 2 * (H * S + 2 * H * H)
+    her = n * (8 * S + 4 * w.G + 4 + 4 + 4 + 8) + n * (2 * S + 4 * S + 4 * 4)
+    return {
+        "relabel_norms": her + k * nb * 4,
+        "fwd_bwd": B * S * 2 + B * 4 + B * A * 4 + grp * (shadows + 4 * (3 * H + 1))
+                   + grp * B * 4 + grp * B * A * 4 + grp * nwg * Pp * 4,
+        "reduce_saxpy": grp * nwg * Pp * 4 + grp * nwg * 4 + grp * P * 4 + k * nb * 4 + nb * 4,
+        "adam": grp * (P * 32 + shadows) + nb * 32,
+    }
 
 
 def kernel_source_hash():
@@ -174,6 +214,149 @@ class Context:
                                  w.n_budget, w.max_grad_norm, self.norms, self.adam, self.ws)
 
 
+LAUNCH_KERNELS = (("relabel_norms", "step_her_norms_kernel"), ("fwd_bwd", "iql_fused16w_kernel"),
+                  ("reduce_saxpy", "step_reduce_saxpy_kernel"), ("adam", "step_adam_kernel"))
+PROFILE_COMMANDS = (
+    "rocprofv3 --kernel-trace --stats -f csv -d OUT/trace -o step -- python3 $REPO/bench.py --steps 200 "
+    "--no-cpu-baseline",
+    "rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/FETCH_SIZE -o p -- python3 $REPO/bench.py --steps 5 --warmup 1 "
+    "--no-graph --no-cpu-baseline --kernel-reps 5",
+    "rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/copy_FETCH_SIZE -o p -- python3 $REPO/bench.py --copy-probe 256",
+    "rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/WRITE_SIZE -o p -- python3 $REPO/bench.py --steps 5 --warmup 1 "
+    "--no-graph --no-cpu-baseline --kernel-reps 5",
+    "rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/copy_WRITE_SIZE -o p -- python3 $REPO/bench.py --copy-probe 256",
+    "python3 $REPO/bench.py --summarize-profiles OUT",
+)
+
+
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _short(name):
+    s = name[5:] if name.startswith("void ") else name
+    s = s.split("(")[0]
+    return s.replace("iqlh::", "")
+
+
+def _median(xs):
+    xs = sorted(xs)
+    m = len(xs) // 2
+    return xs[m] if len(xs) % 2 else 0.5 * (xs[m - 1] + xs[m])
+
+
+def _counter_per_kernel(path):
+    """Median counter value (KiB) per kernel over its dispatches."""
+    per = {}
+    for r in _csv_rows(path):
+        per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: _median(v) for k, v in per.items()}
+
+
+def summarize_profiles(d):
+    """Writes the committed summaries of one profiling session: kernel times
+    from the kernel-trace stats, HBM bytes per dispatch from FETCH_SIZE and
+    WRITE_SIZE scaled by what the same counters read for a plain copy of
+    known size, and each launch's fraction of the HBM peak."""
+    import glob
+    import subprocess
+    sys.path.insert(0, ROOT)
+    import synth
+    w = synth.WORKLOADS[synth.BENCH_WORKLOAD]
+    stats = _csv_rows(glob.glob(os.path.join(d, "trace", "*_kernel_stats.csv"))[0])
+    bench_line = None
+    log = os.path.join(d, "trace.log")
+    if os.path.exists(log):
+        for line in open(log):
+            if line.startswith("{"):
+                bench_line = json.loads(line)
+    cnt = {c: _counter_per_kernel(glob.glob(os.path.join(d, c, "*_counter_collection.csv"))[0])
+           for c in ("FETCH_SIZE", "WRITE_SIZE", "copy_FETCH_SIZE", "copy_WRITE_SIZE")}
+    factors = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        copy = [v for k, v in cnt["copy_" + c].items() if "copyBuffer" in k]
+        factors[c] = (256 * 1024) / max(copy)
+    abytes = launch_bytes(w)
+    try:
+        commit = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short", "HEAD"], capture_output=True,
+                                text=True, check=True).stdout.strip()
+    except Exception:  # pragma: no cover
+        commit = "unknown"
+    src_hash = kernel_source_hash()
+
+    L = []
+    L.append(f"# Kernel time and HBM traffic of one whole step, batch {w.B}, state {w.S}, hidden {w.H}, "
+             f"{w.groups} trainers, budget over {w.n_budget} parameters")
+    L.append("")
+    L.append(f"One `iql_aux_step` per step (four launches), graph replay, one MI355X.  Source of commit {commit} "
+             f"(forward/backward source hash {src_hash}).")
+    L.append("")
+    L.append("Commands (from /tmp, each its own run, `REPO` = the repository root, `OUT` = an output folder):")
+    L.append("")
+    for c in PROFILE_COMMANDS:
+        L.append("    " + c)
+    L.append("")
+    if bench_line:
+        L.append(f"bench line of the trace run: {bench_line['ms_per_step'] * 1e3:.1f} us per step, "
+                 f"{bench_line['value']:.4g} samples/s (profiler attached).")
+        L.append("")
+    L.append("## Kernel time (`--kernel-trace --stats`)")
+    L.append("")
+    L.append("| kernel | calls | average us | min us | % of GPU time |")
+    L.append("|---|---:|---:|---:|---:|")
+    avg = {}
+    for r in stats:
+        nm = _short(r["Name"])
+        avg[nm] = float(r["AverageNs"]) / 1e3
+        L.append(f"| `{nm}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                 f"{float(r['Percentage']):.1f} |")
+    L.append("")
+    L.append("## HBM traffic per dispatch (median over the dispatches of the counter runs)")
+    L.append("")
+    cf = {c: max(v for k, v in cnt["copy_" + c].items() if "copyBuffer" in k) for c in factors}
+    L.append(f"Calibration: a plain 256 MiB device copy (`__amd_rocclr_copyBuffer`) reads FETCH_SIZE = "
+             f"{cf['FETCH_SIZE']:.0f} KiB and WRITE_SIZE = {cf['WRITE_SIZE']:.0f} KiB for 262144 KiB moved each "
+             f"way: factors {factors['FETCH_SIZE']:.3f} (fetch) and {factors['WRITE_SIZE']:.3f} (write).")
+    L.append("")
+    L.append("| launch | kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB | write MB | needed MB | "
+             "kernel us | GB/s (needed) | % of 8 TB/s |")
+    L.append("|---|---|---:|---:|---:|---:|---:|---:|---:|---:|")
+    traffic = None
+    for launch, key in LAUNCH_KERNELS:
+        names = [k for k in cnt["FETCH_SIZE"] if key in k]
+        if not names:
+            continue
+        nm = names[0]
+        fk, wk = cnt["FETCH_SIZE"][nm], cnt["WRITE_SIZE"].get(nm, float("nan"))
+        rd, wr = fk * 1024 * factors["FETCH_SIZE"], wk * 1024 * factors["WRITE_SIZE"]
+        us = next((v for k, v in avg.items() if key in k), float("nan"))
+        gbs = abytes[launch] / (us * 1e-6) / 1e9
+        L.append(f"| {launch} | `{_short(nm)}` | {fk:.0f} | {wk:.0f} | {rd / 1e6:.2f} | {wr / 1e6:.2f} | "
+                 f"{abytes[launch] / 1e6:.2f} | {us:.2f} | {gbs:.0f} | {100 * gbs / PEAK_HBM_GBS:.1f} |")
+        if launch == "fwd_bwd":
+            traffic = {"kernel": _short(nm), "workload": w.name, "source_hash": src_hash,
+                       "hbm_bytes_per_launch": rd + wr, "fetch_kib_raw": fk, "write_kib_raw": wk,
+                       "fetch_factor": factors["FETCH_SIZE"], "write_factor": factors["WRITE_SIZE"],
+                       "commit": commit}
+    L.append("")
+    P, Pp, nwg = partial_layout(w)
+    L.append(f"`needed MB` is each launch's inputs and outputs read or written once (`launch_bytes` in "
+             f"bench.py).  For the forward/backward launch it includes its per-workgroup fp32 gradient "
+             f"partials ({w.groups} x {nwg} workgroups x {Pp} floats = {w.groups * nwg * Pp * 4 / 1e6:.1f} MB), "
+             f"which the reduction reads back.")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    md = os.path.join(ROOT, "profiles", "step_b16384_s128_h128_g2_budget_kernels.md")
+    with open(md, "w") as fh:
+        fh.write("\n".join(L) + "\n")
+    if traffic:
+        with open(os.path.join(ROOT, "profiles", "iql_fused_b16384_s128_h128_g2_traffic.json"), "w") as fh:
+            json.dump(traffic, fh, indent=1)
+            fh.write("\n")
+    print(md)
+
+
 def cpu_baseline(ctx, seconds, np):
     """The oracle as it stands, one full step at a time, on the host cores."""
     from oracle import aw, budget, her, iql
@@ -209,6 +392,9 @@ def cpu_baseline(ctx, seconds, np):
 
 def main():
     a = parse()
+    if a.summarize_profiles:
+        summarize_profiles(a.summarize_profiles)
+        return
     if a.copy_probe:
         copy_probe(a.copy_probe)
         return
@@ -257,11 +443,13 @@ def main():
     # every launch of the step timed by its own dispatch events, on the
     # stream the step runs on; the dominant one is the forward/backward
     launch_us = ctx.time_launches(a.kernel_reps)
+    names = [k for k, _ in LAUNCH_KERNELS]
+    lb = launch_bytes(w)
     avg_us = launch_us[1]
     flops = fused_flops_per_launch(w)
     achieved = flops / (avg_us * 1e-6) / 1e12
     src_hash = kernel_source_hash()
-    roofline = {"bound": "mfma", "kernel": "iql_fused16_kernel<128,128,xvec>", "achieved": achieved,
+    roofline = {"bound": "mfma", "kernel": "iql_fused16w_kernel<128,128,xvec>", "achieved": achieved,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                 "traffic": traffic_from_profiles("iql_fused_b16384_s128_h128_g2", src_hash),
                 "avg_kernel_us": avg_us, "flops_per_launch": flops, "source_hash": src_hash}
@@ -276,8 +464,10 @@ def main():
                       "entry_point": "separate calls" if a.separate else "iql_aux_step",
                       "parallelism": "single-gpu"},
            "event_ms_per_step": ev_ms / a.steps, "device_flags": flags, "status": rc,
-           "launch_us": {"relabel_norms": launch_us[0], "fwd_bwd": launch_us[1], "reduce_saxpy": launch_us[2],
-                         "adam": launch_us[3]},
+           "launch_us": dict(zip(names, launch_us)),
+           "launch_hbm": {k: {"needed_bytes": lb[k], "GB/s": lb[k] / (us * 1e-6) / 1e9,
+                              "frac_of_8TBs": lb[k] / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+                          for k, us in zip(names, launch_us)},
            "roofline": roofline}
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(ctx, a.cpu_seconds, np)
