@@ -33,6 +33,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "IQL+HER train samples/sec at B=16384; % bf16 MFMA peak / % HBM BW"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # MI355X dense fp32 matrix
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 
@@ -44,6 +45,10 @@ def parse():
     p.add_argument("--no-graph", action="store_true", help="eager launches instead of graph replay")
     p.add_argument("--separate", action="store_true",
                    help="the three entry points one after the other instead of iql_aux_step")
+    p.add_argument("--workload", default=None,
+                   help="time another workload of the input recipe (default: the batch-16384 two-trainer "
+                        "step with the budget); the CPU baseline then runs only when --cpu-baseline is given")
+    p.add_argument("--cpu-baseline", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--kernel-reps", type=int, default=200)
@@ -77,14 +82,17 @@ def fused_flops_per_launch(w):
     return w.groups * w.B * (4 * S * H + 6 * H * H + 5 * H)
 
 
-def partial_layout(w):
-    """Per-workgroup gradient partials of the forward/backward launch: one row
-    of P rounded up to 128 floats per 128-sample workgroup and trainer."""
+def partial_layout(w, layout=None):
+    """Per-workgroup gradient partials of the forward/backward launch: `layout`
+    = (rows per trainer, floats per row) as the library reports it; without
+    it, the fused kernel's one row per 128-sample workgroup."""
     P = w.S * w.H + w.H + w.H * w.H + w.H + w.H + 1
-    return P, (P + 127) // 128 * 128, (w.B + 127) // 128
+    if layout is None:
+        layout = ((w.B + 127) // 128, (P + 127) // 128 * 128)
+    return P, layout[1], layout[0]
 
 
-def launch_bytes(w):
+def launch_bytes(w, layout=None):
     """Bytes each of the four launches of one step must read and write, given
     its inputs and outputs (what a perfect cache would leave of its traffic):
       relabel+norms: per HER row, source s and s' rows (f32), the donor's goal,
@@ -100,13 +108,14 @@ def launch_bytes(w):
                      both trainers and of the budgeted network, plus the bf16
                      weight shadows the trainers' update rewrites."""
     n, S, H, A, B, grp = w.n_her, w.S, w.H, w.A, w.B, w.groups
-    k, nb = 4, w.n_budget
-    P, Pp, nwg = partial_layout(w)
-    shadows = 2 * (H * S + 2 * H * H)
-    her = n * (8 * S + 4 * w.G + 4 + 4 + 4 + 8) + n * (2 * S + 4 * S + 4 * 4)
+    k, nb = (4, w.n_budget) if w.budget else (0, 0)
+    P, Pp, nwg = partial_layout(w, layout)
+    e = 2 if w.dtype == "bf16" else 4
+    shadows = e * (H * S + 2 * H * H)
+    her = n * (8 * S + 4 * w.G + 4 + 4 + 4 + 8) + n * (e * S + 4 * S + 4 * 4)
     return {
         "relabel_norms": her + k * nb * 4,
-        "fwd_bwd": B * S * 2 + B * 4 + B * A * 4 + grp * (shadows + 4 * (3 * H + 1))
+        "fwd_bwd": B * S * e + B * 4 + B * A * 4 + grp * (shadows + 4 * (3 * H + 1))
                    + grp * B * 4 + grp * B * A * 4 + grp * nwg * Pp * 4,
         "reduce_saxpy": grp * nwg * Pp * 4 + grp * nwg * 4 + grp * P * 4 + k * nb * 4 + nb * 4,
         "adam": grp * (P * 32 + shadows) + nb * 32,
@@ -144,16 +153,19 @@ class Context:
         self.host_Xn = synth.batch_states(w)
         self.host_Q, _, self.host_q = synth.q_values(w, buf, src)
         self.inits = synth.group_inits(w)
-        self.host_sources = synth.budget_sources(w)
-        self.host_theta = synth.budget_params(w)
+        if w.budget:
+            self.host_sources = synth.budget_sources(w)
+            self.host_theta = synth.budget_params(w)
 
         t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(d)  # noqa: E731
         self.rb_states, self.rb_next = t(buf["states"]), t(buf["next_states"])
         self.rb_actions, self.rb_dones = t(buf["actions"]), t(buf["dones"])
         self.rb_ends = t(buf["episode_ends"].astype(np.int32))
         self.src = t(src.astype(np.int32))
-        self.X = torch.empty((B, S), dtype=torch.bfloat16, device=d)
-        self.X[: B - n] = t(self.host_Xn).to(torch.bfloat16)
+        bf16 = w.dtype == "bf16"
+        xdt = torch.bfloat16 if bf16 else torch.float32
+        self.X = torch.empty((B, S), dtype=xdt, device=d)
+        self.X[: B - n] = t(self.host_Xn).to(xdt)
         self.Q, self.q = t(self.host_Q), t(self.host_q)
         self.her_next = torch.empty((n, S), dtype=torch.float32, device=d)
         self.her_act = torch.empty(n, dtype=torch.int32, device=d)
@@ -161,7 +173,8 @@ class Context:
         self.her_done = torch.empty(n, dtype=torch.float32, device=d)
         self.her_donor = torch.empty(n, dtype=torch.int32, device=d)
 
-        cfg = m.make_config(S, w.H, B, num_groups=w.groups, compute_dtype=m.BF16, states_ld=S,
+        cdt = m.BF16 if bf16 else m.F32
+        cfg = m.make_config(S, w.H, B, num_groups=w.groups, compute_dtype=cdt, states_ld=S,
                             tau=w.taus, lr=w.lr, max_grad_norm=w.max_grad_norm)
         self.tr = m.IqlTrainer(cfg, np.concatenate(self.inits))
         self.out_v = torch.empty((w.groups, B), dtype=torch.float32, device=d)
@@ -169,13 +182,18 @@ class Context:
         self.out_gn = torch.empty(w.groups, dtype=torch.float32, device=d)
         self.pi = torch.empty((w.groups, B, A), dtype=torch.float32, device=d)
 
-        self.hcfg = m.her_config(S, w.G, m.HER_FUTURE)
+        strategy = {"final": m.HER_FINAL, "future": m.HER_FUTURE, "random": m.HER_RANDOM}[w.strategy]
+        self.hcfg = m.her_config(S, w.G, strategy)
         self.hbuf = m.her_buffer(self.rb_states, self.rb_next, self.rb_actions, self.rb_dones, self.rb_ends)
         tail = self.X.data_ptr() + (B - n) * S * self.X.element_size()
-        self.hout = m.her_out(tail, m.BF16, S, self.her_rew, next_states=self.her_next,
+        self.hout = m.her_out(tail, cdt, S, self.her_rew, next_states=self.her_next,
                               actions=self.her_act, dones=self.her_done, donor_idx=self.her_donor,
                               d_flags=self.tr.flags)
 
+        self.her_step = m.her_step(self.hcfg, self.hbuf, self.src, w.n_her, 20261202, self.hout)
+        self.budget_step = None
+        if not w.budget:
+            return
         P = w.n_budget
         self.sources = [t(s) for s in self.host_sources]
         self.theta = t(self.host_theta)
@@ -188,7 +206,6 @@ class Context:
         self.adam = m.make_adam(self.theta, self.theta_m, self.theta_v, self.theta_t, lr=w.lr,
                                 max_grad_norm=w.max_grad_norm, d_flags=self.tr.flags)
 
-        self.her_step = m.her_step(self.hcfg, self.hbuf, self.src, w.n_her, 20261202, self.hout)
         self.budget_step = m.budget_step(self.grad, self.sources, w.budget_fractions, (1.0, 1.0, 1.0, 1.0),
                                          w.n_budget, w.max_grad_norm, self.norms, self.adam, self.ws)
 
@@ -210,8 +227,9 @@ class Context:
         m.her_relabel(self.hcfg, self.hbuf, self.src, w.n_her, 20261202, self.tr.step_counter, self.hout)
         self.tr.train_step_aw(self.X, self.q, w.B, self.Q, w.A, w.beta, self.pi, self.out_v, self.out_loss,
                               self.out_gn)
-        m.grad_budget_accumulate(self.grad, self.sources, w.budget_fractions, (1.0, 1.0, 1.0, 1.0),
-                                 w.n_budget, w.max_grad_norm, self.norms, self.adam, self.ws)
+        if self.budget_step is not None:
+            m.grad_budget_accumulate(self.grad, self.sources, w.budget_fractions, (1.0, 1.0, 1.0, 1.0),
+                                     w.n_budget, w.max_grad_norm, self.norms, self.adam, self.ws)
 
 
 LAUNCH_KERNELS = (("relabel_norms", "step_her_norms_kernel"), ("fwd_bwd", "iql_fused16w_kernel"),
@@ -369,18 +387,21 @@ def cpu_baseline(ctx, seconds, np):
         cores = 1
     Xn = ctx.host_Xn.astype(np.float64)
     states = [iql.AdamState.fresh(p) for p in ctx.inits]
-    theta = iql.AdamState.fresh(ctx.host_theta)
+    theta = iql.AdamState.fresh(ctx.host_theta) if w.budget else None
+    strategy = {"final": her.FINAL, "future": her.FUTURE, "random": her.RANDOM}[w.strategy]
     hp = iql.AdamHP(lr=w.lr, max_grad_norm=w.max_grad_norm)
     t0 = time.perf_counter()
     steps = 0
     while True:
-        r = her.her_step(ctx.host_buf, ctx.host_src, w.G, her.FUTURE, 20261202, steps, out_bf16=True)
+        r = her.her_step(ctx.host_buf, ctx.host_src, w.G, strategy, 20261202, steps, out_bf16=w.dtype == "bf16")
         X = np.concatenate([Xn, r["states"].astype(np.float64)])
         vs = [iql.train_step(states[g], X, ctx.host_q, w.S, w.H, w.H, w.taus[g], hp).v for g in range(w.groups)]
         for g in range(w.groups):
             aw.aw_policy(ctx.host_Q, vs[g], w.beta)
-        grad, _, _, _ = budget.accumulate(ctx.host_sources, w.budget_fractions, (1, 1, 1, 1), w.max_grad_norm)
-        iql.adam_step(theta, grad, hp)
+        if w.budget:
+            grad, _, _, _ = budget.accumulate(ctx.host_sources, w.budget_fractions, (1, 1, 1, 1),
+                                              w.max_grad_norm)
+            iql.adam_step(theta, grad, hp)
         steps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -408,7 +429,8 @@ def main():
     import offline_rl_step_amd as m
     import synth
 
-    w = synth.WORKLOADS[synth.BENCH_WORKLOAD]
+    default = a.workload is None or a.workload == synth.BENCH_WORKLOAD
+    w = synth.WORKLOADS[a.workload or synth.BENCH_WORKLOAD]
     ctx = Context(m, w, torch, np, synth)
     torch.cuda.synchronize()
 
@@ -444,22 +466,31 @@ def main():
     # stream the step runs on; the dominant one is the forward/backward
     launch_us = ctx.time_launches(a.kernel_reps)
     names = [k for k, _ in LAUNCH_KERNELS]
-    lb = launch_bytes(w)
+    layout = ctx.tr.partial_layout(w.B)
+    lb = launch_bytes(w, layout)
     avg_us = launch_us[1]
     flops = fused_flops_per_launch(w)
     achieved = flops / (avg_us * 1e-6) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     src_hash = kernel_source_hash()
-    roofline = {"bound": "mfma", "kernel": "iql_fused16w_kernel<128,128,xvec>", "achieved": achieved,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": traffic_from_profiles("iql_fused_b16384_s128_h128_g2", src_hash),
+    if default:
+        kernel = "iql_fused16w_kernel<128,128,xvec>"
+    elif w.H > 128:
+        kernel = "layered forward/backward (five kernels; events around the group)"
+    else:
+        kernel = "fused forward/backward"
+    roofline = {"bound": "mfma", "kernel": kernel, "achieved": achieved,
+                "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                "traffic": traffic_from_profiles("iql_fused_b16384_s128_h128_g2", src_hash) if default else None,
                 "avg_kernel_us": avg_us, "flops_per_launch": flops, "source_hash": src_hash}
 
     out = {"metric": METRIC, "value": w.B / (ms_per_step * 1e-3), "unit": "samples/s", "n_gpus": 1,
            "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
            "config": {"workload": w.name, "global_batch": w.B, "state_dim": w.S, "hidden": w.H,
                       "actions": w.A, "groups": w.groups, "her_rows": w.n_her, "her_strategy": w.strategy,
-                      "replay_rows": w.C, "budget_params": w.n_budget, "budget_sources": 4,
+                      "replay_rows": w.C, "budget_params": w.n_budget if w.budget else 0,
+                      "budget_sources": 4 if w.budget else 0,
                       "graph_replay": graph is not None,
                       "entry_point": "separate calls" if a.separate else "iql_aux_step",
                       "parallelism": "single-gpu"},
@@ -469,7 +500,7 @@ def main():
                               "frac_of_8TBs": lb[k] / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
                           for k, us in zip(names, launch_us)},
            "roofline": roofline}
-    if not a.no_cpu_baseline:
+    if (default or a.cpu_baseline) and not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(ctx, a.cpu_seconds, np)
     print(json.dumps(out), flush=True)
 

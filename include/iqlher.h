@@ -141,6 +141,12 @@ int iql_apply_gradients(iql_handle h, int32_t batch, float* out_loss, float* out
 int iql_time_compute_gradients(iql_handle h, const void* states, const float* q_taken,
                                int32_t batch, int32_t reps, float* out_avg_us, void* stream);
 
+/* Measurement aid: the layout of the per-workgroup gradient partials that
+ * iql_compute_gradients writes for `batch` rows -- *out_rows partial rows per
+ * group, each *out_row_floats floats (the parameter count rounded up to 128).
+ * Host only, no HIP call. */
+int iql_partial_layout(iql_handle h, int32_t batch, int32_t* out_rows, int64_t* out_row_floats);
+
 /* Copies one group's state to / from device buffers of iql_num_params floats
  * (params, m, v) and one int32 (t).  set_state also refreshes the shadows. */
 int iql_get_state(iql_handle h, int32_t group, float* d_params, float* d_m, float* d_v,

@@ -87,6 +87,7 @@ _lib_iql_train_step_aw = _sig("iql_train_step_aw", _i32, [_p, _p, _p, _i32, _p, 
 _lib_iql_compute_gradients = _sig("iql_compute_gradients", _i32, [_p, _p, _p, _i32, _p, _p])
 _lib_iql_apply_gradients = _sig("iql_apply_gradients", _i32, [_p, _i32, _p, _p, _p])
 _lib_iql_time_cg = _sig("iql_time_compute_gradients", _i32, [_p, _p, _p, _i32, _i32, ctypes.POINTER(_f), _p])
+_lib_iql_partial_layout = _sig("iql_partial_layout", _i32, [_p, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i64)])
 _lib_iql_get_state = _sig("iql_get_state", _i32, [_p, _i32, _p, _p, _p, _p, _p])
 _lib_iql_set_state = _sig("iql_set_state", _i32, [_p, _i32, _p, _p, _p, _p, _p])
 _lib_iql_step_counter = _sig("iql_step_counter", _p, [_p])
@@ -200,6 +201,14 @@ def iql_time_compute_gradients(h, states, q_taken, batch, reps, stream=None):
     _check(_lib_iql_time_cg(h, _ptr(states), _ptr(q_taken), batch, reps, ctypes.byref(out), _stream(stream)),
            "iql_time_compute_gradients")
     return out.value
+
+
+def iql_partial_layout(h, batch):
+    """(partial rows per group, floats per row) of the per-workgroup gradient
+    partials written for `batch` rows."""
+    rows, floats = _i32(), _i64()
+    _check(_lib_iql_partial_layout(h, batch, ctypes.byref(rows), ctypes.byref(floats)), "iql_partial_layout")
+    return rows.value, floats.value
 
 
 def iql_get_state(h, group, params=None, m=None, v=None, t=None, stream=None):
@@ -369,6 +378,9 @@ class IqlTrainer:
         self.cfg = cfg
         self.h = iql_create(cfg, init_params_host)
         self.n_params = iql_num_params(cfg.state_dim, cfg.hidden)
+
+    def partial_layout(self, batch):
+        return iql_partial_layout(self.h, batch)
 
     def train_step(self, states, q_taken, batch, out_v=None, out_loss=None, out_grad_norm=None, stream=None):
         iql_train_step(self.h, states, q_taken, batch, out_v, out_loss, out_grad_norm, stream)

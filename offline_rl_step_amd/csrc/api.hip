@@ -111,12 +111,16 @@ int iql_create(const iqlh_config* cfg, const float* init_params_host, iql_handle
     IqlDims& d = t->dims;
     d.S = S; d.H = H; d.G = G; d.dtype = cfg->compute_dtype;
     d.layered = iql_supported(d.dtype, S, H) ? 0 : 1;
+    d.big = d.layered && iql_big_supported(d.dtype, S, H) && cfg->states_ld % 8 == 0;
     d.S_pad = d.layered ? (S + 7) / 8 * 8 : iql_s_pad(d.dtype, S, H);
     d.P = P;
     d.Pp = (P + 127) / 128 * 128;
     const int64_t MB = cfg->max_batch;
     int max_wg, max_loss;
-    if (d.layered) {
+    if (d.big) {
+        max_wg = iql_big_max_chunks(S, H);
+        max_loss = iql_big_blocks((int)MB);
+    } else if (d.layered) {
         max_wg = (int)((MB + iql_layered_chunk() - 1) / iql_layered_chunk());
         max_loss = (int)((MB + 63) / 64);
     } else {
@@ -130,7 +134,9 @@ int iql_create(const iqlh_config* cfg, const float* init_params_host, iql_handle
     b.max_rb = rb;
     b.act_h1 = b.act_dz2 = b.act_p2 = b.act_dz1 = nullptr;
     b.act_z2 = b.act_dv = nullptr;
+    b.big_spart = nullptr;
     const size_t nact = d.layered ? (size_t)G * MB * H : 0;
+    const size_t nlay = d.layered && !d.big ? nact : 0;  // layered-only activations
     struct { void** p; size_t bytes; } plan[] = {
         {(void**)&b.params, sizeof(float) * G * P},
         {(void**)&b.m, sizeof(float) * G * P},
@@ -146,11 +152,12 @@ int iql_create(const iqlh_config* cfg, const float* init_params_host, iql_handle
         {(void**)&b.loss_part, sizeof(float) * G * (size_t)max_loss},
         {(void**)&b.sq_part, sizeof(float) * G * (size_t)rb},
         {(void**)&b.act_h1, esz * nact},
-        {(void**)&b.act_z2, sizeof(float) * nact},
+        {(void**)&b.act_z2, sizeof(float) * nlay},
         {(void**)&b.act_dz2, esz * nact},
-        {(void**)&b.act_p2, esz * nact},
+        {(void**)&b.act_p2, esz * nlay},
         {(void**)&b.act_dz1, esz * nact},
-        {(void**)&b.act_dv, sizeof(float) * (d.layered ? (size_t)G * MB : 0)},
+        {(void**)&b.act_dv, sizeof(float) * (nlay ? (size_t)G * MB : 0)},
+        {(void**)&b.big_spart, sizeof(float) * (d.big ? (size_t)G * iql_big_blocks((int)MB) * (2 * H + 1) : 0)},
     };
     for (auto& a : plan) {
         if (a.bytes == 0) continue;
@@ -178,6 +185,8 @@ static int check_step_args(iql_handle h, const void* states, const float* q_take
     if (!states || !q_taken) return fail(IQLH_EINVAL, "states and q_taken must be non-NULL");
     if (batch < 1 || batch > h->cfg.max_batch)
         return fail(IQLH_EINVAL, "batch %d outside [1, max_batch=%d]", batch, h->cfg.max_batch);
+    if (h->dims.big && ((uintptr_t)states & 15u))
+        return fail(IQLH_EINVAL, "states must be 16-byte aligned for bf16 operands at hidden %d", h->dims.H);
     return IQLH_OK;
 }
 
@@ -224,6 +233,17 @@ int iql_time_compute_gradients(iql_handle h, const void* states, const float* q_
     if (e1) (void)hipEventDestroy(e1);
     if (e != hipSuccess) return hip_fail(e, "iql_time_compute_gradients");
     *out_avg_us = (float)(total_ms * 1000.0 / reps);
+    return IQLH_OK;
+}
+
+int iql_partial_layout(iql_handle h, int32_t batch, int32_t* out_rows, int64_t* out_row_floats) {
+    if (!h || !out_rows || !out_row_floats) return fail(IQLH_EINVAL, "NULL argument");
+    if (batch < 1 || batch > h->cfg.max_batch)
+        return fail(IQLH_EINVAL, "batch %d outside [1, max_batch=%d]", batch, h->cfg.max_batch);
+    int nwg = 0, nloss = 0;
+    if (!iql_partial_counts(h->dims, batch, &nwg, &nloss)) return fail(IQLH_ESHAPE, "no kernel for this shape");
+    *out_rows = nwg;
+    *out_row_floats = h->dims.Pp;
     return IQLH_OK;
 }
 

@@ -1026,7 +1026,8 @@ hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float
                               const float* q_all, int A, float beta, float* out_pi) {
     if (d.layered) {
         if (ev0) (void)hipEventRecord(ev0, stream);
-        hipError_t e = launch_iql_layered_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream);
+        hipError_t e = d.big ? launch_iql_big_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream)
+                             : launch_iql_layered_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream);
         if (ev1 && e == hipSuccess) e = hipEventRecord(ev1, stream);
         return e;
     }
@@ -1044,6 +1045,12 @@ hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float
 }
 
 bool iql_partial_counts(const IqlDims& d, int B, int* nwg, int* nloss) {
+    if (d.big) {
+        const int c = iql_big_chunk(d.S, d.H, B);
+        *nwg = (B + c - 1) / c;
+        *nloss = iql_big_blocks(B);
+        return true;
+    }
     if (d.layered) {
         *nwg = (B + iql_layered_chunk() - 1) / iql_layered_chunk();
         *nloss = (B + 63) / 64;

@@ -63,6 +63,7 @@ hipError_t launch_adam_flat(float* params, float* grad, float* m, float* v, cons
 struct IqlDims {
     int S, H, G, dtype;  // dtype: 0 f32, 1 bf16
     int layered;         // 0: fused tile kernel; 1: layered GEMMs through HBM
+    int big;             // with layered: the wide-hidden bf16 kernels (iql_big.hip)
     int S_pad;           // columns of the W1 shadow (multiple of 32)
     int64_t P;           // parameters per group
     int64_t Pp;          // row stride of the gradient partials (P rounded up to 128)
@@ -91,6 +92,8 @@ struct IqlBuffers {
     void* act_p2;
     void* act_dz1;
     float* act_dv;
+    // wide-hidden path: per-128-sample-block sums of db2, dw3, db3 [G][nblk][2H + 1]
+    float* big_spart;
 };
 bool iql_supported(int dtype, int S, int H);
 int iql_tile_samples(int dtype, int S, int H);
@@ -113,6 +116,12 @@ int iql_layered_chunk();
 hipError_t launch_iql_layered_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float* tau,
                                       const void* states, int64_t ld, const float* q, int B,
                                       float* out_v, hipStream_t stream);
+bool iql_big_supported(int dtype, int S, int H);
+int iql_big_blocks(int B);
+int iql_big_max_chunks(int S, int H);
+int iql_big_chunk(int S, int H, int B);
+hipError_t launch_iql_big_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float* tau, const void* states,
+                                  int64_t ld, const float* q, int B, float* out_v, hipStream_t stream);
 hipError_t launch_iql_refresh_shadows(const IqlDims& d, const IqlBuffers& b, hipStream_t stream);
 // workgroup and loss partials that a batch of B rows leaves for the reduction
 bool iql_partial_counts(const IqlDims& d, int B, int* nwg, int* nloss);

@@ -20,6 +20,13 @@ Sources:
     (0 disables).
 
 Weights are [out, in] row-major; flat order w1, b1, w2, b2, w3, b3.
+
+``rnd`` (optional, e.g. ``bf16_operands``): the same definition with every
+matrix-product operand rounded as a bf16-operand implementation stores it --
+W1, W2, h1, dz2 (also in the b2 sum) and dz1 (also in the b1 sum); V, the
+loss, dv and dw3 stay unrounded.  It separates the effect of bf16 operand
+storage from that of the arithmetic order; the plain fp64 definition is the
+parity reference.
 Readings (listed in the design doc): ReLU'(0) = 0; weight tau at diff == 0; the
 finite-check is applied after clipping, so a non-finite norm skips the whole
 update; decoupled weight decay (AdamW order) when weight_decay != 0.
@@ -27,6 +34,17 @@ update; decoupled weight decay (AdamW order) when weight_decay != 0.
 from dataclasses import dataclass, field
 
 import numpy as np
+
+from oracle.bf16 import round_bf16
+
+
+def bf16_operands(a):
+    """fp64 values -> nearest bfloat16 (through binary32, as stored), fp64."""
+    return round_bf16(np.asarray(a, dtype=np.float64).astype(np.float32)).astype(np.float64)
+
+
+def _same(a):
+    return a
 
 
 def num_params(S, H1, H2):
@@ -52,12 +70,13 @@ def flatten(t):
                            t["w3"].ravel(), np.atleast_1d(t["b3"])])
 
 
-def forward(p, X):
+def forward(p, X, rnd=None):
     """V(s) for each row of X; returns (v, cache)."""
+    R = rnd or _same
     X = np.asarray(X, dtype=np.float64)
-    z1 = X @ p["w1"].T + p["b1"]
+    z1 = X @ R(p["w1"]).T + p["b1"]
     h1 = np.maximum(z1, 0.0)
-    z2 = h1 @ p["w2"].T + p["b2"]
+    z2 = R(h1) @ R(p["w2"]).T + p["b2"]
     h2 = np.maximum(z2, 0.0)
     v = h2 @ p["w3"] + p["b3"][0]
     return v, dict(X=X, z1=z1, h1=h1, z2=z2, h2=h2)
@@ -74,17 +93,18 @@ def expectile(q, v, tau):
     return loss, dv
 
 
-def backward(p, cache, dv):
+def backward(p, cache, dv, rnd=None):
     """Gradients of sum(dv * v) with respect to the six tensors."""
+    R = rnd or _same
     X, z1, h1, z2, h2 = cache["X"], cache["z1"], cache["h1"], cache["z2"], cache["h2"]
     g = {}
     g["w3"] = h2.T @ dv
     g["b3"] = np.array([np.sum(dv)])
-    dz2 = np.outer(dv, p["w3"]) * (z2 > 0.0)
-    g["w2"] = dz2.T @ h1
+    dz2 = R(np.outer(dv, p["w3"]) * (z2 > 0.0))
+    g["w2"] = dz2.T @ R(h1)
     g["b2"] = dz2.sum(axis=0)
-    dh1 = dz2 @ p["w2"]
-    dz1 = dh1 * (z1 > 0.0)
+    dh1 = dz2 @ R(p["w2"])
+    dz1 = R(dh1 * (z1 > 0.0))
     g["w1"] = dz1.T @ X
     g["b1"] = dz1.sum(axis=0)
     return g
@@ -175,14 +195,14 @@ class StepResult:
     skipped: np.ndarray = field(default=None)
 
 
-def train_step(st, X, q, S, H1, H2, tau, hp):
+def train_step(st, X, q, S, H1, H2, tau, hp, rnd=None):
     """V forward, expectile loss, backward and clipped Adam, in place on st.
 
     Returns the loss, V(s) before the update, the flat gradient and its
     pre-clip norm."""
     p = unflatten(st.params, S, H1, H2)
-    v, cache = forward(p, X)
+    v, cache = forward(p, X, rnd)
     loss, dv = expectile(q, v, tau)
-    g = flatten(backward(p, cache, dv))
+    g = flatten(backward(p, cache, dv, rnd))
     norm, skipped = adam_step(st, g, hp)
     return StepResult(loss=loss, v=v, grad=g, grad_norm=norm, skipped=skipped)

@@ -59,9 +59,9 @@ class Setup:
     def gpu_step(self):
         self.tr.train_step(self.tX, self.tq, self.B, self.out_v, self.out_loss, self.out_gn)
 
-    def oracle_step(self, states=None):
+    def oracle_step(self, states=None, rnd=None):
         sts = self.oracle if states is None else states
-        return [iql.train_step(sts[g], self.X, self.q, self.S, self.H, self.H, self.taus[g], self.hp)
+        return [iql.train_step(sts[g], self.X, self.q, self.S, self.H, self.H, self.taus[g], self.hp, rnd)
                 for g in range(self.G)]
 
     def state(self, g):
@@ -89,11 +89,11 @@ class Setup:
             adam_update_close(st.params, o.params, None, self.hp.lr, 1, rtol, f"{what} params g{g}")
 
 
-def _one_step(m, w, rtol, **kw):
+def _one_step(m, w, rtol, rnd=None, **kw):
     s = Setup(m, w, **kw)
     s.gpu_step()
     sync()
-    refs = s.oracle_step()
+    refs = s.oracle_step(rnd=rnd)
     s.compare_step(refs, s.oracle, rtol, 1, w.name)
     rc, flags = s.tr.status()
     assert rc == m.OK and flags == 0
@@ -249,6 +249,52 @@ def test_layered_bf16_ragged(m):
 def test_layered_fp32(m):
     w = synth.shrink(synth.WORKLOADS["tiny_b256_s16_h32"], S=20, H=64, G=4)
     _one_step(m, w, 1e-4, B=1000)
+
+
+# ------------------------------------------------- wide-hidden bf16 path
+WIDE_CASES = [(64, 256, 2, 3000, 72), (96, 512, 1, 1037, 96), (256, 512, 1, 4096, 256), (32, 256, 1, 1, 32),
+              (256, 256, 1, 130, 264)]
+
+
+@pytest.mark.parametrize("S,H,G,B,ld", WIDE_CASES)
+def test_wide_bf16_ragged(m, S, H, G, B, ld):
+    """bf16 operands at hidden 256/512 and state_dim a multiple of 32 take the
+    wide-hidden kernels (HBM-staged activations, weight gradients over sample
+    chunks).  Batches ragged against the 256-sample tiles, the 128-sample loss
+    blocks, the 32-sample stages and the chunks; state widths below and
+    between the 256-feature tiles; padded row strides."""
+    w = synth.shrink(synth.WORKLOADS["stress_b65536_s256_h512_bf16"], S=S, H=H, groups=G,
+                     taus=(0.9, 0.3)[:G], G=8)
+    _one_step(m, w, 2e-2, B=B, ld=ld)
+
+
+@pytest.mark.parametrize("S,H,G,B,ld", WIDE_CASES + [(256, 512, 2, 4096, 256)])
+def test_wide_bf16_matches_bf16_operand_oracle(m, S, H, G, B, ld):
+    """Against the oracle with the same bf16 operand storage, the wide kernels
+    agree to 2e-3 -- ten times tighter than the bf16 bar, so a kernel mistake
+    cannot hide in the rounding.  The last case is one where bf16 storage
+    alone moves the gradient of trainer 1 (tau 0.3) 2.3 % from the fp64
+    definition (dW1 3.5 %: the sum over samples cancels); it is checked here
+    only."""
+    w = synth.shrink(synth.WORKLOADS["stress_b65536_s256_h512_bf16"], S=S, H=H, groups=G,
+                     taus=(0.9, 0.3)[:G], G=8)
+    _one_step(m, w, 2e-3, rnd=iql.bf16_operands, B=B, ld=ld)
+
+
+def test_wide_bf16_unaligned_stride_uses_layered(m):
+    """A row stride that is not a multiple of 8 elements cannot feed 16-byte
+    copies; such a trainer runs the layered kernels, with the same results."""
+    w = synth.shrink(synth.WORKLOADS["stress_b65536_s256_h512_bf16"], S=64, H=256, G=8)
+    _one_step(m, w, 2e-2, B=700, ld=66)
+
+
+def test_wide_bf16_rejects_unaligned_states(m):
+    import torch
+    w = synth.shrink(synth.WORKLOADS["stress_b65536_s256_h512_bf16"], S=64, H=256, G=8)
+    s = Setup(m, w, B=256)
+    flat = torch.zeros(256 * 64 + 8, dtype=torch.bfloat16, device=dev())
+    with pytest.raises(m.IqlhError, match="aligned"):
+        m.iql_compute_gradients(s.tr.h, flat[1:], s.tq, 256)
 
 
 def test_stress_b65536_s256_h512_one_step(m):

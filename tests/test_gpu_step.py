@@ -319,3 +319,20 @@ def test_time_aux_step_reports_every_launch(m):
     rc, flags = r.tr.status()
     assert rc == m.OK and flags == 0
     r.tr.close()
+
+
+@pytest.mark.parametrize("name,batch,rows", [("b16384_s128_h128_bf16_g2_budget", 16384, 128),
+                                             ("b16384_s128_h128_bf16_g2_budget", 1000, 8),
+                                             ("stress_b65536_s256_h512_bf16", 65536, 32)])
+def test_partial_layout_query(m, name, batch, rows):
+    """The partial-buffer query the byte counts of bench.py rest on: one row
+    per 128-sample workgroup on the fused path, one per 2048-row chunk on the
+    layered one, each the parameter count rounded up to 128 floats."""
+    w = synth.WORKLOADS[name]
+    cfg = m.make_config(w.S, w.H, batch, num_groups=w.groups, compute_dtype=m.BF16, states_ld=w.S, tau=w.taus)
+    tr = m.IqlTrainer(cfg, np.concatenate(synth.group_inits(w)))
+    n, floats = tr.partial_layout(batch)
+    assert n == rows and floats == (w.n_params + 127) // 128 * 128
+    with pytest.raises(m.IqlhError):
+        tr.partial_layout(batch + 1)
+    tr.close()

@@ -90,6 +90,64 @@ def test_forward_backward_match_torch_autograd(S, H, B, tau):
     np.testing.assert_allclose(grad, tg, rtol=1e-10, atol=1e-14)
 
 
+def _torch_rounded(flat, X, q, tau, S, H):
+    """The same network with bf16 operand storage modelled in torch autograd:
+    weights and h1 take their bf16 values in the forward (straight-through,
+    fp64 identity in the backward), and hooks round the gradients arriving at
+    z2 and z1 (dz2, dz1) before they feed the weight and bias gradients and
+    dh1."""
+    import torch
+
+    def bf(a):
+        return a.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+
+    def st(a):  # bf16 value forward, identity backward (fp64 gradient)
+        return a + (bf(a) - a).detach()
+
+    t = torch.tensor(flat, dtype=torch.float64, requires_grad=True)
+    o = 0
+    w1 = t[o:o + H * S].view(H, S); o += H * S
+    b1 = t[o:o + H]; o += H
+    w2 = t[o:o + H * H].view(H, H); o += H * H
+    b2 = t[o:o + H]; o += H
+    w3 = t[o:o + H]; o += H
+    b3 = t[o]
+    Xt = torch.tensor(X, dtype=torch.float64)
+    z1 = Xt @ st(w1).T + b1
+    z1.register_hook(lambda g: bf(g))
+    z2 = st(torch.relu(z1)) @ st(w2).T + b2
+    z2.register_hook(lambda g: bf(g))
+    v = torch.relu(z2) @ w3 + b3
+    d = torch.tensor(q, dtype=torch.float64) - v
+    w = torch.where(d >= 0, torch.tensor(tau, dtype=torch.float64), torch.tensor(1 - tau, dtype=torch.float64))
+    loss = torch.mean(w * d * d)
+    loss.backward()
+    return loss.item(), v.detach().numpy(), t.grad.numpy()
+
+
+@pytest.mark.parametrize("S,H,B,tau", [(5, 4, 8, 0.7), (16, 32, 64, 0.3), (42, 16, 33, 0.9)])
+def test_bf16_operand_variant_matches_torch(S, H, B, tau):
+    """Pin of the rounded-operand variant against an independent autograd
+    model of the same storage; it also differs from the plain definition, so
+    every rounding point is exercised."""
+    flat = _net(S, H, seed=S * 100 + H + 1)
+    g = np.random.default_rng(B + 7)
+    X, q = g.standard_normal((B, S)), g.standard_normal(B) * 2
+    p = iql.unflatten(flat, S, H, H)
+    v, cache = iql.forward(p, X, iql.bf16_operands)
+    loss, dv = iql.expectile(q, v, tau)
+    grad = iql.flatten(iql.backward(p, cache, dv, iql.bf16_operands))
+    tl, tv, tg = _torch_rounded(flat, X, q, tau, S, H)
+    assert loss == pytest.approx(tl, rel=1e-10)
+    np.testing.assert_allclose(v, tv, rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(grad, tg, rtol=1e-9, atol=1e-13)
+    plain = iql.flatten(iql.backward(p, iql.forward(p, X)[1], iql.expectile(q, iql.forward(p, X)[0], tau)[1]))
+    o = 0
+    for name, n in (("w1", S * H), ("b1", H), ("w2", H * H), ("b2", H)):
+        assert not np.allclose(grad[o:o + n], plain[o:o + n], rtol=1e-6, atol=0), name
+        o += n
+
+
 def test_gradient_finite_differences():
     S, H, B, tau = 5, 4, 8, 0.7
     g = np.random.default_rng(5)
