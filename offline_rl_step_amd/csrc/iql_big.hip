@@ -197,6 +197,36 @@ IQLH_DEV bf16x8 nat_frag(const uint16_t* tile, const NatBase& nb, int c) {
     return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
 }
 
+// ---------------------------------------------------- staged epilogues
+// A workgroup's bf16 results go to LDS as [sample][feature] rows of NF
+// features, the 16-byte unit u of row s at u ^ (s & 7), and leave as 16-byte
+// stores covering whole rows (coalesced), not as the 8-byte pieces of the
+// MFMA layout.
+template <int NF>
+IQLH_DEV int stage_off(int s, int f) { return s * NF + ((((f >> 3) ^ (s & 7)) << 3) | (f & 7)); }
+
+// Rows [0, ns) of the staged tile to dst rows (row stride ld), columns
+// [0, NF).  With mask, an element is zeroed where the same element of mask
+// is zero (dz1 = dh1 relu'(z1), read from h1 = relu(z1) as stored).
+template <int NF, int NS>
+IQLH_DEV void stage_out(const uint16_t* lds, uint16_t* dst, int64_t ld, int ns, const uint16_t* mask) {
+    constexpr int UPR = NF / 8;  // 16-byte units per row
+#pragma unroll 4
+    for (int c = threadIdx.x; c < NS * UPR; c += kThreads) {
+        const int r = c / UPR, u = c - r * UPR;
+        if (r >= ns) break;
+        u32x4 v = *(const u32x4*)(lds + r * NF + ((u ^ (r & 7)) << 3));
+        if (mask) {
+            const u32x4 h = *(const u32x4*)(mask + (int64_t)r * ld + 8 * u);
+            v.x &= (h.x & 0xFFFFu ? 0xFFFFu : 0u) | (h.x >> 16 ? 0xFFFF0000u : 0u);
+            v.y &= (h.y & 0xFFFFu ? 0xFFFFu : 0u) | (h.y >> 16 ? 0xFFFF0000u : 0u);
+            v.z &= (h.z & 0xFFFFu ? 0xFFFFu : 0u) | (h.z >> 16 ? 0xFFFF0000u : 0u);
+            v.w &= (h.w & 0xFFFFu ? 0xFFFFu : 0u) | (h.w >> 16 ? 0xFFFF0000u : 0u);
+        }
+        *(u32x4*)(dst + (int64_t)r * ld + 8 * u) = v;
+    }
+}
+
 struct BigArgs {
     const uint16_t* x;      // [B][ldx] batch rows
     int64_t ldx;
@@ -294,41 +324,35 @@ __global__ __launch_bounds__(kThreads) void big_tile_kernel(BigArgs a) {
             reads_then_mfma<16, 64>();
         });
 
-    // epilogue: lane holds features fb0 + 16i + 4q + r of samples sb0 + 16j + l16
+    // epilogue: lane holds features 128 wm + 16 i + 4 q + r of samples
+    // 128 wn + 16 j + l16 (tile-local); staged as [sample][feature] rows
     const int l = threadIdx.x & 63, l16 = l & 15, q = l >> 4;
-    const int fbase = f0 + 128 * wm + 4 * q, sbase = s0 + 128 * wn + l16;
-    const float* bias = a.params + (int64_t)g * a.P + a.off_b1;
+    const float* bias = a.params + (int64_t)g * a.P + a.off_b1 + f0;
+    __syncthreads();  // every wave is done with the last stage
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int f = fbase + 16 * i;
-        float bb[4];
+        const int f = 128 * wm + 16 * i + 4 * q;
+        float bb[4] = {0.f, 0.f, 0.f, 0.f};
         if (MODE == 0) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) bb[r] = bias[f + r];
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int s = sbase + 16 * j;
-            if (s >= B) continue;
-            const int64_t o = ((int64_t)g * B + s) * H + f;
+            const int sl = 128 * wn + 16 * j + l16;
             float y[4];
-            if (MODE == 0) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float z = acc[i][j][r] + bb[r];
-                    y[r] = z > 0.f ? z : 0.f;
-                }
-                *(u32x2*)(a.h1 + o) = u32x2{cvt2(y[0], y[1]), cvt2(y[2], y[3])};
-            } else {
-                const u32x2 m = *(const u32x2*)(a.h1 + o);
-                y[0] = bf_lo(m.x) > 0.f ? acc[i][j][0] : 0.f;
-                y[1] = bf_hi(m.x) > 0.f ? acc[i][j][1] : 0.f;
-                y[2] = bf_lo(m.y) > 0.f ? acc[i][j][2] : 0.f;
-                y[3] = bf_hi(m.y) > 0.f ? acc[i][j][3] : 0.f;
-                *(u32x2*)(a.dz1 + o) = u32x2{cvt2(y[0], y[1]), cvt2(y[2], y[3])};
+            for (int r = 0; r < 4; ++r) {
+                const float z = acc[i][j][r] + bb[r];
+                y[r] = MODE == 0 ? (z > 0.f ? z : 0.f) : z;
             }
+            *(u32x2*)(smem + stage_off<kTile>(sl, f)) = u32x2{cvt2(y[0], y[1]), cvt2(y[2], y[3])};
         }
     }
+    __syncthreads();
+    const int64_t o = ((int64_t)g * B + s0) * H + f0;
+    if (MODE == 0) stage_out<kTile, kTile>(smem, a.h1 + o, H, srows, nullptr);
+    else stage_out<kTile, kTile>(smem, a.dz1 + o, H, srows, a.h1 + o);
 }
 
 // --------------------------------------------------------------- fwd2
@@ -346,7 +370,8 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
     const int srows = B - s0;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lo = kc_lane();
-    float* svp = (float*)(smem + NST * STG);  // [4][128] V partials of each wave
+    constexpr int RING = NST * STG, STAGE = kFwd2Samples * H;
+    float* svp = (float*)(smem + (RING > STAGE ? RING : STAGE));  // [4][128] V partials of each wave
 
     f4 acc[MT][8];
 #pragma unroll
@@ -437,7 +462,6 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
         float db2[4] = {0.f, 0.f, 0.f, 0.f}, dw3[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int s = s0 + 16 * j + l16;
             float d[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -451,7 +475,7 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
             db2[1] += bf_hi(pk.x);
             db2[2] += bf_lo(pk.y);
             db2[3] += bf_hi(pk.y);
-            if (s < B) *(u32x2*)(a.dz2 + ((int64_t)g * B + s) * H + fb0 + 16 * i) = pk;
+            *(u32x2*)(smem + stage_off<H>(16 * j + l16, fb0 + 16 * i)) = pk;
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -466,6 +490,8 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
             }
         }
     }
+    __syncthreads();
+    stage_out<H, kFwd2Samples>(smem, a.dz2 + ((int64_t)g * B + s0) * H, H, srows, nullptr);
 }
 
 // --------------------------------------------------------------- wgrad
@@ -588,7 +614,10 @@ __global__ __launch_bounds__(kThreads) void big_wgrad_kernel(BigArgs a) {
 
 constexpr size_t tile_lds_bytes() { return (size_t)4 * 2 * kTile * kBK * 2; }
 template <int H>
-constexpr size_t fwd2_lds_bytes() { return (size_t)3 * (H + kFwd2Samples) * kBK * 2 + 4 * kFwd2Samples * sizeof(float); }
+constexpr size_t fwd2_lds_bytes() {
+    return (size_t)(3 * (H + kFwd2Samples) * kBK > kFwd2Samples * H ? 3 * (H + kFwd2Samples) * kBK : kFwd2Samples * H) * 2 +
+           4 * kFwd2Samples * sizeof(float);
+}
 
 template <typename K>
 hipError_t allow_lds(K kern, size_t bytes) {
