@@ -232,19 +232,27 @@ class Context:
                                      w.n_budget, w.max_grad_norm, self.norms, self.adam, self.ws)
 
 
-LAUNCH_KERNELS = (("relabel_norms", "step_her_norms_kernel"), ("fwd_bwd", "iql_fused16w_kernel"),
-                  ("reduce_saxpy", "step_reduce_saxpy_kernel"), ("adam", "step_adam_kernel"))
-PROFILE_COMMANDS = (
-    "rocprofv3 --kernel-trace --stats -f csv -d OUT/trace -o step -- python3 $REPO/bench.py --steps 200 "
-    "--no-cpu-baseline",
-    "rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/FETCH_SIZE -o p -- python3 $REPO/bench.py --steps 5 --warmup 1 "
-    "--no-graph --no-cpu-baseline --kernel-reps 5",
-    "rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/copy_FETCH_SIZE -o p -- python3 $REPO/bench.py --copy-probe 256",
-    "rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/WRITE_SIZE -o p -- python3 $REPO/bench.py --steps 5 --warmup 1 "
-    "--no-graph --no-cpu-baseline --kernel-reps 5",
-    "rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/copy_WRITE_SIZE -o p -- python3 $REPO/bench.py --copy-probe 256",
-    "python3 $REPO/bench.py --summarize-profiles OUT",
-)
+LAUNCH_KERNELS = (("relabel_norms", ("step_her_norms_kernel", "her_relabel_kernel")),
+                  ("fwd_bwd", ("iql_fused16w_kernel", "iql_fused_kernel", "big_tile_kernel", "big_fwd2_kernel",
+                               "big_wgrad_kernel", "layer_gemm_kernel", "iql_rows_kernel", "iql_wgrad_kernel",
+                               "aw_policy_kernel")),
+                  ("reduce_saxpy", ("step_reduce_saxpy_kernel",)),
+                  ("adam", ("step_adam_kernel",)))
+
+
+def profile_commands(workload):
+    wl = "" if workload is None else f" --workload {workload}"
+    return (
+        f"rocprofv3 --kernel-trace --stats -f csv -d OUT/trace -o step -- python3 $REPO/bench.py{wl} --steps 200 "
+        "--no-cpu-baseline",
+        f"rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/FETCH_SIZE -o p -- python3 $REPO/bench.py{wl} --steps 5 "
+        "--warmup 1 --no-graph --no-cpu-baseline --kernel-reps 5",
+        "rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/copy_FETCH_SIZE -o p -- python3 $REPO/bench.py --copy-probe 256",
+        f"rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/WRITE_SIZE -o p -- python3 $REPO/bench.py{wl} --steps 5 "
+        "--warmup 1 --no-graph --no-cpu-baseline --kernel-reps 5",
+        "rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/copy_WRITE_SIZE -o p -- python3 $REPO/bench.py --copy-probe 256",
+        f"python3 $REPO/bench.py --summarize-profiles OUT{wl}",
+    )
 
 
 def _csv_rows(path):
@@ -255,7 +263,7 @@ def _csv_rows(path):
 
 def _short(name):
     s = name[5:] if name.startswith("void ") else name
-    s = s.split("(")[0]
+    s = s.replace("(anonymous namespace)::", "").split("(")[0]
     return s.replace("iqlh::", "")
 
 
@@ -273,16 +281,17 @@ def _counter_per_kernel(path):
     return {k: _median(v) for k, v in per.items()}
 
 
-def summarize_profiles(d):
+def summarize_profiles(d, workload=None):
     """Writes the committed summaries of one profiling session: kernel times
     from the kernel-trace stats, HBM bytes per dispatch from FETCH_SIZE and
     WRITE_SIZE scaled by what the same counters read for a plain copy of
-    known size, and each launch's fraction of the HBM peak."""
+    known size, and each launch's rate on the bytes it needs."""
     import glob
     import subprocess
     sys.path.insert(0, ROOT)
     import synth
-    w = synth.WORKLOADS[synth.BENCH_WORKLOAD]
+    w = synth.WORKLOADS[workload or synth.BENCH_WORKLOAD]
+    default = w.name == synth.BENCH_WORKLOAD
     stats = _csv_rows(glob.glob(os.path.join(d, "trace", "*_kernel_stats.csv"))[0])
     bench_line = None
     log = os.path.join(d, "trace.log")
@@ -290,30 +299,40 @@ def summarize_profiles(d):
         for line in open(log):
             if line.startswith("{"):
                 bench_line = json.loads(line)
+    layout = None
+    if bench_line and "partials" in bench_line:
+        layout = (bench_line["partials"]["rows"], bench_line["partials"]["floats"])
     cnt = {c: _counter_per_kernel(glob.glob(os.path.join(d, c, "*_counter_collection.csv"))[0])
            for c in ("FETCH_SIZE", "WRITE_SIZE", "copy_FETCH_SIZE", "copy_WRITE_SIZE")}
-    factors = {}
+    factors, cf = {}, {}
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
-        copy = [v for k, v in cnt["copy_" + c].items() if "copyBuffer" in k]
-        factors[c] = (256 * 1024) / max(copy)
-    abytes = launch_bytes(w)
+        cf[c] = max(v for k, v in cnt["copy_" + c].items() if "copyBuffer" in k)
+        factors[c] = (256 * 1024) / cf[c]
+    abytes = launch_bytes(w, layout)
     try:
         commit = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short", "HEAD"], capture_output=True,
                                 text=True, check=True).stdout.strip()
     except Exception:  # pragma: no cover
         commit = "unknown"
     src_hash = kernel_source_hash()
+    launch_of = {}
+    for launch, keys in LAUNCH_KERNELS:
+        for r in stats:
+            if any(k in r["Name"] for k in keys):
+                launch_of[r["Name"]] = launch
+    steps = max((int(r["Calls"]) for r in stats if "step_reduce_saxpy_kernel" in r["Name"]), default=1)
 
     L = []
+    what = f"budget over {w.n_budget} parameters" if w.budget else "no budget part"
     L.append(f"# Kernel time and HBM traffic of one whole step, batch {w.B}, state {w.S}, hidden {w.H}, "
-             f"{w.groups} trainers, budget over {w.n_budget} parameters")
+             f"{w.groups} trainer{'s' if w.groups > 1 else ''}, {what}")
     L.append("")
-    L.append(f"One `iql_aux_step` per step (four launches), graph replay, one MI355X.  Source of commit {commit} "
-             f"(forward/backward source hash {src_hash}).")
+    L.append(f"Workload `{w.name}`.  One `iql_aux_step` per step (four launches), graph replay, one MI355X.  "
+             f"Source of commit {commit} (forward/backward source hash {src_hash}).")
     L.append("")
     L.append("Commands (from /tmp, each its own run, `REPO` = the repository root, `OUT` = an output folder):")
     L.append("")
-    for c in PROFILE_COMMANDS:
+    for c in profile_commands(None if default else w.name):
         L.append("    " + c)
     L.append("")
     if bench_line:
@@ -322,53 +341,62 @@ def summarize_profiles(d):
         L.append("")
     L.append("## Kernel time (`--kernel-trace --stats`)")
     L.append("")
-    L.append("| kernel | calls | average us | min us | % of GPU time |")
-    L.append("|---|---:|---:|---:|---:|")
-    avg = {}
+    L.append("| kernel | launch | calls | average us | min us | % of GPU time |")
+    L.append("|---|---|---:|---:|---:|---:|")
     for r in stats:
-        nm = _short(r["Name"])
-        avg[nm] = float(r["AverageNs"]) / 1e3
-        L.append(f"| `{nm}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
-                 f"{float(r['Percentage']):.1f} |")
+        L.append(f"| `{_short(r['Name'])}` | {launch_of.get(r['Name'], '-')} | {r['Calls']} | "
+                 f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
     L.append("")
     L.append("## HBM traffic per dispatch (median over the dispatches of the counter runs)")
     L.append("")
-    cf = {c: max(v for k, v in cnt["copy_" + c].items() if "copyBuffer" in k) for c in factors}
     L.append(f"Calibration: a plain 256 MiB device copy (`__amd_rocclr_copyBuffer`) reads FETCH_SIZE = "
              f"{cf['FETCH_SIZE']:.0f} KiB and WRITE_SIZE = {cf['WRITE_SIZE']:.0f} KiB for 262144 KiB moved each "
              f"way: factors {factors['FETCH_SIZE']:.3f} (fetch) and {factors['WRITE_SIZE']:.3f} (write).")
     L.append("")
-    L.append("| launch | kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB | write MB | needed MB | "
-             "kernel us | GB/s (needed) | % of 8 TB/s |")
-    L.append("|---|---|---:|---:|---:|---:|---:|---:|---:|---:|")
-    traffic = None
-    for launch, key in LAUNCH_KERNELS:
-        names = [k for k in cnt["FETCH_SIZE"] if key in k]
-        if not names:
+    L.append("| kernel | launch | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB | write MB |")
+    L.append("|---|---|---:|---:|---:|---:|")
+    per_launch = {}
+    fwd_kernels = []
+    for nm, fk in cnt["FETCH_SIZE"].items():
+        launch = next((ln for ln, keys in LAUNCH_KERNELS if any(k in nm for k in keys)), None)
+        if launch is None:
             continue
-        nm = names[0]
-        fk, wk = cnt["FETCH_SIZE"][nm], cnt["WRITE_SIZE"].get(nm, float("nan"))
+        wk = cnt["WRITE_SIZE"].get(nm, float("nan"))
         rd, wr = fk * 1024 * factors["FETCH_SIZE"], wk * 1024 * factors["WRITE_SIZE"]
-        us = next((v for k, v in avg.items() if key in k), float("nan"))
-        gbs = abytes[launch] / (us * 1e-6) / 1e9
-        L.append(f"| {launch} | `{_short(nm)}` | {fk:.0f} | {wk:.0f} | {rd / 1e6:.2f} | {wr / 1e6:.2f} | "
-                 f"{abytes[launch] / 1e6:.2f} | {us:.2f} | {gbs:.0f} | {100 * gbs / PEAK_HBM_GBS:.1f} |")
+        L.append(f"| `{_short(nm)}` | {launch} | {fk:.0f} | {wk:.0f} | {rd / 1e6:.2f} | {wr / 1e6:.2f} |")
+        per_launch.setdefault(launch, 0.0)
+        per_launch[launch] += rd + wr
         if launch == "fwd_bwd":
-            traffic = {"kernel": _short(nm), "workload": w.name, "source_hash": src_hash,
-                       "hbm_bytes_per_launch": rd + wr, "fetch_kib_raw": fk, "write_kib_raw": wk,
-                       "fetch_factor": factors["FETCH_SIZE"], "write_factor": factors["WRITE_SIZE"],
-                       "commit": commit}
+            fwd_kernels.append((_short(nm), fk, wk))
     L.append("")
-    P, Pp, nwg = partial_layout(w)
+    L.append("## Per launch")
+    L.append("")
+    L.append("| launch | kernel us per step | measured MB | needed MB | GB/s on needed bytes | % of 8 TB/s |")
+    L.append("|---|---:|---:|---:|---:|---:|")
+    for launch, _ in LAUNCH_KERNELS:
+        us = sum(float(r["AverageNs"]) / 1e3 * int(r["Calls"]) / steps for r in stats
+                 if launch_of.get(r["Name"]) == launch)
+        if us <= 0:
+            continue
+        gbs = abytes[launch] / (us * 1e-6) / 1e9
+        L.append(f"| {launch} | {us:.2f} | {per_launch.get(launch, float('nan')) / 1e6:.2f} | "
+                 f"{abytes[launch] / 1e6:.2f} | {gbs:.0f} | {100 * gbs / PEAK_HBM_GBS:.1f} |")
+    L.append("")
+    P, Pp, nwg = partial_layout(w, layout)
     L.append(f"`needed MB` is each launch's inputs and outputs read or written once (`launch_bytes` in "
-             f"bench.py).  For the forward/backward launch it includes its per-workgroup fp32 gradient "
-             f"partials ({w.groups} x {nwg} workgroups x {Pp} floats = {w.groups * nwg * Pp * 4 / 1e6:.1f} MB), "
-             f"which the reduction reads back.")
+             f"bench.py).  For the forward/backward launch it includes its fp32 gradient partials "
+             f"({w.groups} x {nwg} rows x {Pp} floats = {w.groups * nwg * Pp * 4 / 1e6:.1f} MB), which the "
+             f"reduction reads back.")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    md = os.path.join(ROOT, "profiles", "step_b16384_s128_h128_g2_budget_kernels.md")
+    md = os.path.join(ROOT, "profiles", f"step_{w.name}_kernels.md")
     with open(md, "w") as fh:
         fh.write("\n".join(L) + "\n")
-    if traffic:
+    if default and len(fwd_kernels) == 1:
+        nm, fk, wk = fwd_kernels[0]
+        traffic = {"kernel": nm, "workload": w.name, "source_hash": src_hash,
+                   "hbm_bytes_per_launch": fk * 1024 * factors["FETCH_SIZE"] + wk * 1024 * factors["WRITE_SIZE"],
+                   "fetch_kib_raw": fk, "write_kib_raw": wk, "fetch_factor": factors["FETCH_SIZE"],
+                   "write_factor": factors["WRITE_SIZE"], "commit": commit}
         with open(os.path.join(ROOT, "profiles", "iql_fused_b16384_s128_h128_g2_traffic.json"), "w") as fh:
             json.dump(traffic, fh, indent=1)
             fh.write("\n")
@@ -414,7 +442,7 @@ def cpu_baseline(ctx, seconds, np):
 def main():
     a = parse()
     if a.summarize_profiles:
-        summarize_profiles(a.summarize_profiles)
+        summarize_profiles(a.summarize_profiles, a.workload)
         return
     if a.copy_probe:
         copy_probe(a.copy_probe)
@@ -495,6 +523,7 @@ def main():
                       "entry_point": "separate calls" if a.separate else "iql_aux_step",
                       "parallelism": "single-gpu"},
            "event_ms_per_step": ev_ms / a.steps, "device_flags": flags, "status": rc,
+           "partials": {"rows": layout[0], "floats": layout[1]},
            "launch_us": dict(zip(names, launch_us)),
            "launch_hbm": {k: {"needed_bytes": lb[k], "GB/s": lb[k] / (us * 1e-6) / 1e9,
                               "frac_of_8TBs": lb[k] / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
