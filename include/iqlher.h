@@ -51,6 +51,7 @@ typedef enum { IQLH_F32 = 0, IQLH_BF16 = 1 } iqlh_dtype;
 #define IQLH_FLAG_NONFINITE_GRAD 0x1  /* Adam saw a non-finite clipped grad  */
 #define IQLH_FLAG_BAD_INDEX      0x2  /* HER source/donor outside the buffer */
 #define IQLH_FLAG_NONFINITE_LOSS 0x4  /* non-finite expectile loss term      */
+#define IQLH_FLAG_NONFINITE_STATE 0x8 /* Adam wrote a non-finite p, m or v   */
 
 /* ------------------------------------------------------------------------
  * IQL value trainer ([P1] "Current State / IQL (CPU)", "CUDA Kernel:
@@ -153,6 +154,26 @@ int iql_get_state(iql_handle h, int32_t group, float* d_params, float* d_m, floa
                   int32_t* d_t, void* stream);
 int iql_set_state(iql_handle h, int32_t group, const float* d_params, const float* d_m,
                   const float* d_v, const int32_t* d_t, void* stream);
+
+/* Polyak (EMA) target copy of the value network ([P1] "Rust Integration:
+ * gpu_iql_trainer.rs", target_ema_update; run after the IQL step in "Where
+ * in the Training Loop IQL Gets Called").  The handle keeps a target copy of
+ * every group's flat parameters, equal to the initial parameters at
+ * iql_create, updated elementwise as
+ *   target <- target + tau (params - target)      (fp32, one rounding per step)
+ * iql_target_ema_update: one update of every group with the current params,
+ *   enqueued on `stream`.  0 <= tau <= 1.
+ * iql_set_target_ema: host-side setting; with tau > 0 every later step
+ *   (iql_train_step, iql_train_step_aw, iql_apply_gradients, iql_aux_step)
+ *   applies the same update to each parameter right after Adam writes it, in
+ *   the Adam launch (no extra pass).  0 (the default) turns it off.  The
+ *   result equals the step followed by iql_target_ema_update(tau), bit for bit.
+ * iql_get_target / iql_set_target: copy one group's target (iql_num_params
+ *   floats) to / from a device buffer. */
+int iql_target_ema_update(iql_handle h, float tau, void* stream);
+int iql_set_target_ema(iql_handle h, float tau);
+int iql_get_target(iql_handle h, int32_t group, float* d_params, void* stream);
+int iql_set_target(iql_handle h, int32_t group, const float* d_params, void* stream);
 
 /* Device int64 step counter owned by the handle (0 before the first step);
  * pass it to her_relabel as d_step so a replayed graph draws new donors. */
@@ -337,6 +358,20 @@ int iql_time_aux_step(iql_handle h, const iqlh_her_step* her, const void* states
                       int32_t num_actions, float beta, float* out_pi, float* out_v,
                       float* out_loss, float* out_grad_norm, const iqlh_budget_step* budget,
                       int32_t reps, float* out_avg_us, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Fused non-finite sentinel ([P2] "Phase E -- SP2 fused NaN check kernel":
+ * one launch over a table of buffers, a sticky flag per slot that is written
+ * 1 and never cleared, null entries skipped).
+ *   d_bufs        host array of num_slots device pointers to fp32 buffers
+ *                 (NULL entries are skipped; any alignment).
+ *   lens          host array of element counts (>= 0).
+ *   d_slot_flags  device int32 [num_slots]: slot s is set to 1 when buffer s
+ *                 holds a NaN or an infinity; a clean slot keeps its value.
+ * 1 <= num_slots <= 32.  Reads only.  (Every Adam launch of this library
+ * also checks the p, m, v it writes and raises IQLH_FLAG_NONFINITE_STATE.) */
+int iqlh_nonfinite_check(const float* const* d_bufs, const int64_t* lens, int32_t num_slots,
+                         int32_t* d_slot_flags, void* stream);
 
 /* Thread-local text of the last error returned on this thread ("" if none). */
 const char* iqlh_last_error(void);

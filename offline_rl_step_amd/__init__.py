@@ -23,7 +23,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 OK, EINVAL, ESHAPE, ENOMEM, EHIP, ENONFINITE = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
 HER_FINAL, HER_FUTURE, HER_RANDOM = 0, 1, 2
-FLAG_NONFINITE_GRAD, FLAG_BAD_INDEX, FLAG_NONFINITE_LOSS = 0x1, 0x2, 0x4
+FLAG_NONFINITE_GRAD, FLAG_BAD_INDEX, FLAG_NONFINITE_LOSS, FLAG_NONFINITE_STATE = 0x1, 0x2, 0x4, 0x8
 MAX_SOURCES = 8
 
 _p = ctypes.c_void_p
@@ -90,6 +90,10 @@ _lib_iql_time_cg = _sig("iql_time_compute_gradients", _i32, [_p, _p, _p, _i32, _
 _lib_iql_partial_layout = _sig("iql_partial_layout", _i32, [_p, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i64)])
 _lib_iql_get_state = _sig("iql_get_state", _i32, [_p, _i32, _p, _p, _p, _p, _p])
 _lib_iql_set_state = _sig("iql_set_state", _i32, [_p, _i32, _p, _p, _p, _p, _p])
+_lib_iql_target_ema_update = _sig("iql_target_ema_update", _i32, [_p, _f, _p])
+_lib_iql_set_target_ema = _sig("iql_set_target_ema", _i32, [_p, _f])
+_lib_iql_get_target = _sig("iql_get_target", _i32, [_p, _i32, _p, _p])
+_lib_iql_set_target = _sig("iql_set_target", _i32, [_p, _i32, _p, _p])
 _lib_iql_step_counter = _sig("iql_step_counter", _p, [_p])
 _lib_iql_flags = _sig("iql_flags", _p, [_p])
 _lib_iql_status = _sig("iql_status", _i32, [_p, ctypes.POINTER(_i32)])
@@ -105,6 +109,7 @@ _lib_iql_aux_step = _sig("iql_aux_step", _i32, [_p, ctypes.POINTER(HerStep), _p,
 _lib_iql_time_aux_step = _sig("iql_time_aux_step", _i32, [_p, ctypes.POINTER(HerStep), _p, _p, _i32, _p, _i32, _f,
                                                           _p, _p, _p, _p, ctypes.POINTER(BudgetStep), _i32,
                                                           ctypes.POINTER(_f), _p])
+_lib_nonfinite_check = _sig("iqlh_nonfinite_check", _i32, [ctypes.POINTER(_p), ctypes.POINTER(_i64), _i32, _p, _p])
 _lib_last_error = _sig("iqlh_last_error", ctypes.c_char_p, [])
 
 
@@ -209,6 +214,31 @@ def iql_partial_layout(h, batch):
     rows, floats = _i32(), _i64()
     _check(_lib_iql_partial_layout(h, batch, ctypes.byref(rows), ctypes.byref(floats)), "iql_partial_layout")
     return rows.value, floats.value
+
+
+def nonfinite_check(buffers, slot_flags, stream=None):
+    """Sets slot_flags[s] = 1 for every buffer (fp32 tensor or None) holding
+    a NaN or an infinity; clean slots keep their value."""
+    n = len(buffers)
+    ptrs = (_p * n)(*[None if b is None else b.data_ptr() for b in buffers])
+    lens = (_i64 * n)(*[0 if b is None else b.numel() for b in buffers])
+    _check(_lib_nonfinite_check(ptrs, lens, n, _ptr(slot_flags), _stream(stream)), "iqlh_nonfinite_check")
+
+
+def iql_target_ema_update(h, tau, stream=None):
+    _check(_lib_iql_target_ema_update(h, tau, _stream(stream)), "iql_target_ema_update")
+
+
+def iql_set_target_ema(h, tau):
+    _check(_lib_iql_set_target_ema(h, tau), "iql_set_target_ema")
+
+
+def iql_get_target(h, group, params, stream=None):
+    _check(_lib_iql_get_target(h, group, _ptr(params), _stream(stream)), "iql_get_target")
+
+
+def iql_set_target(h, group, params, stream=None):
+    _check(_lib_iql_set_target(h, group, _ptr(params), _stream(stream)), "iql_set_target")
 
 
 def iql_get_state(h, group, params=None, m=None, v=None, t=None, stream=None):
@@ -378,6 +408,18 @@ class IqlTrainer:
         self.cfg = cfg
         self.h = iql_create(cfg, init_params_host)
         self.n_params = iql_num_params(cfg.state_dim, cfg.hidden)
+
+    def target_ema_update(self, tau, stream=None):
+        iql_target_ema_update(self.h, tau, stream)
+
+    def set_target_ema(self, tau):
+        iql_set_target_ema(self.h, tau)
+
+    def get_target(self, group, params, stream=None):
+        iql_get_target(self.h, group, params, stream)
+
+    def set_target(self, group, params, stream=None):
+        iql_set_target(self.h, group, params, stream)
 
     def partial_layout(self, batch):
         return iql_partial_layout(self.h, batch)

@@ -40,6 +40,7 @@ struct iql_trainer {
     IqlDims dims;
     IqlBuffers buf;
     int device;
+    float ema_tau;  // Polyak weight folded into every step's Adam launch, 0 = off
     std::vector<void*> allocs;
 };
 
@@ -142,6 +143,7 @@ int iql_create(const iqlh_config* cfg, const float* init_params_host, iql_handle
         {(void**)&b.m, sizeof(float) * G * P},
         {(void**)&b.v, sizeof(float) * G * P},
         {(void**)&b.grad, sizeof(float) * G * P},
+        {(void**)&b.target, sizeof(float) * G * P},
         {(void**)&b.t, sizeof(int32_t) * G},
         {(void**)&b.step, sizeof(int64_t)},
         {(void**)&b.flags, sizeof(int32_t)},
@@ -165,6 +167,7 @@ int iql_create(const iqlh_config* cfg, const float* init_params_host, iql_handle
         if (rc) { free_all(t); delete t; return rc; }
     }
     e = hipMemcpy(b.params, init_params_host, sizeof(float) * G * P, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(b.target, init_params_host, sizeof(float) * G * P, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = launch_iql_refresh_shadows(d, b, nullptr);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) { free_all(t); delete t; return hip_fail(e, "iql_create upload"); }
@@ -198,8 +201,9 @@ static int check_policy_args(const float* q_all, int32_t num_actions, float beta
     return IQLH_OK;
 }
 
-static AdamHyper adam_hyper(const iqlh_config& c) {
-    return AdamHyper{c.lr, c.beta1, c.beta2, c.eps, c.weight_decay, c.max_grad_norm, c.weight_clamp_max_abs};
+static AdamHyper adam_hyper(const iql_trainer* h) {
+    const iqlh_config& c = h->cfg;
+    return AdamHyper{c.lr, c.beta1, c.beta2, c.eps, c.weight_decay, c.max_grad_norm, c.weight_clamp_max_abs, h->ema_tau};
 }
 
 int iql_compute_gradients(iql_handle h, const void* states, const float* q_taken, int32_t batch,
@@ -251,7 +255,7 @@ int iql_apply_gradients(iql_handle h, int32_t batch, float* out_loss, float* out
     if (!h) return fail(IQLH_EINVAL, "handle is NULL");
     if (batch < 1 || batch > h->cfg.max_batch)
         return fail(IQLH_EINVAL, "batch %d outside [1, max_batch=%d]", batch, h->cfg.max_batch);
-    hipError_t e = launch_iql_update(h->dims, h->buf, adam_hyper(h->cfg), batch, out_loss, out_grad_norm,
+    hipError_t e = launch_iql_update(h->dims, h->buf, adam_hyper(h), batch, out_loss, out_grad_norm,
                                      (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "iql_apply_gradients launch");
     return IQLH_OK;
@@ -274,7 +278,7 @@ int iql_train_step_aw(iql_handle h, const void* states, const float* q_taken, in
         if (e == hipSuccess) e = launch_aw_policy(q_all, out_v, h->dims.G, batch, num_actions, beta, out_pi, s);
     }
     if (e == hipSuccess)
-        e = launch_iql_update(h->dims, h->buf, adam_hyper(h->cfg), batch, out_loss, out_grad_norm, s);
+        e = launch_iql_update(h->dims, h->buf, adam_hyper(h), batch, out_loss, out_grad_norm, s);
     if (e != hipSuccess) return hip_fail(e, "iql_train_step_aw launch");
     return IQLH_OK;
 }
@@ -321,6 +325,43 @@ int iql_set_state(iql_handle h, int32_t group, const float* d_params, const floa
     return IQLH_OK;
 }
 
+int iql_target_ema_update(iql_handle h, float tau, void* stream) {
+    if (!h) return fail(IQLH_EINVAL, "handle is NULL");
+    if (!(tau >= 0.f && tau <= 1.f)) return fail(IQLH_EINVAL, "tau must be in [0, 1]");
+    hipError_t e = launch_iql_target_ema(h->dims, h->buf, tau, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "iql_target_ema_update");
+    return IQLH_OK;
+}
+
+int iql_set_target_ema(iql_handle h, float tau) {
+    if (!h) return fail(IQLH_EINVAL, "handle is NULL");
+    if (!(tau >= 0.f && tau <= 1.f)) return fail(IQLH_EINVAL, "tau must be in [0, 1]");
+    h->ema_tau = tau;
+    return IQLH_OK;
+}
+
+int iql_get_target(iql_handle h, int32_t group, float* d_params, void* stream) {
+    if (!h) return fail(IQLH_EINVAL, "handle is NULL");
+    if (group < 0 || group >= h->dims.G) return fail(IQLH_EINVAL, "group %d out of range", group);
+    if (!d_params) return fail(IQLH_EINVAL, "d_params is NULL");
+    const int64_t P = h->dims.P;
+    hipError_t e = hipMemcpyAsync(d_params, h->buf.target + group * P, sizeof(float) * P, hipMemcpyDeviceToDevice,
+                                  (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "iql_get_target");
+    return IQLH_OK;
+}
+
+int iql_set_target(iql_handle h, int32_t group, const float* d_params, void* stream) {
+    if (!h) return fail(IQLH_EINVAL, "handle is NULL");
+    if (group < 0 || group >= h->dims.G) return fail(IQLH_EINVAL, "group %d out of range", group);
+    if (!d_params) return fail(IQLH_EINVAL, "d_params is NULL");
+    const int64_t P = h->dims.P;
+    hipError_t e = hipMemcpyAsync(h->buf.target + group * P, d_params, sizeof(float) * P, hipMemcpyDeviceToDevice,
+                                  (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "iql_set_target");
+    return IQLH_OK;
+}
+
 const int64_t* iql_step_counter(iql_handle h) { return h ? h->buf.step : nullptr; }
 int32_t* iql_flags(iql_handle h) { return h ? h->buf.flags : nullptr; }
 
@@ -331,9 +372,34 @@ int iql_status(iql_handle h, int32_t* flags_host) {
     if (e == hipSuccess) e = hipMemcpy(&f, h->buf.flags, sizeof(int32_t), hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "iql_status");
     if (flags_host) *flags_host = f;
-    if (f & (IQLH_FLAG_NONFINITE_GRAD | IQLH_FLAG_NONFINITE_LOSS))
+    if (f & (IQLH_FLAG_NONFINITE_GRAD | IQLH_FLAG_NONFINITE_LOSS | IQLH_FLAG_NONFINITE_STATE))
         return fail(IQLH_ENONFINITE, "device flagged a non-finite value (flags=0x%x)", f);
     if (f & IQLH_FLAG_BAD_INDEX) return fail(IQLH_ESHAPE, "device flagged an index outside the buffer");
+    return IQLH_OK;
+}
+
+int iqlh_nonfinite_check(const float* const* d_bufs, const int64_t* lens, int32_t num_slots,
+                         int32_t* d_slot_flags, void* stream) {
+    if (!d_bufs || !lens || !d_slot_flags) return fail(IQLH_EINVAL, "iqlh_nonfinite_check: NULL argument");
+    if (num_slots < 1 || num_slots > kSentinelSlots)
+        return fail(IQLH_EINVAL, "num_slots must be in [1, %d]", kSentinelSlots);
+    SentinelArgs a{};
+    a.flags = d_slot_flags;
+    a.nslots = num_slots;
+    int64_t blocks = 0;
+    for (int s = 0; s < num_slots; ++s) {
+        if (lens[s] < 0) return fail(IQLH_EINVAL, "lens[%d] < 0", s);
+        const int64_t n = d_bufs[s] ? lens[s] : 0;  // null entries are skipped
+        a.ptr[s] = d_bufs[s];
+        a.n[s] = n;
+        a.block0[s] = (int)blocks;
+        if ((((uintptr_t)d_bufs[s]) & 15u) == 0) a.vec |= 1u << s;
+        blocks += (n + kSentinelPiece - 1) / kSentinelPiece;
+        if (blocks > (int64_t)1 << 30) return fail(IQLH_EINVAL, "iqlh_nonfinite_check: buffers too large");
+    }
+    a.block0[num_slots] = (int)blocks;
+    hipError_t e = launch_nonfinite_sentinel(a, (int)blocks, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "iqlh_nonfinite_check");
     return IQLH_OK;
 }
 
@@ -506,7 +572,7 @@ int iql_aux_step(iql_handle h, const iqlh_her_step* her, const void* states, con
     AuxPlan p;
     int rc = plan_aux_step(h, her, states, q_taken, batch, q_all, num_actions, beta, out_pi, out_v, budget, &p);
     if (rc) return rc;
-    hipError_t e = launch_aux_step(h->dims, h->buf, adam_hyper(h->cfg), h->cfg.tau, p.her ? &p.ha : nullptr,
+    hipError_t e = launch_aux_step(h->dims, h->buf, adam_hyper(h), h->cfg.tau, p.her ? &p.ha : nullptr,
                                    states, h->cfg.states_ld, q_taken, batch, q_all, num_actions, beta, out_pi,
                                    out_v, out_loss, out_grad_norm, p.budget ? &p.ba : nullptr, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "iql_aux_step launch");
@@ -526,7 +592,7 @@ int iql_time_aux_step(iql_handle h, const iqlh_her_step* her, const void* states
     for (int i = 0; i < 8 && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
     double total[4] = {0.0, 0.0, 0.0, 0.0};
     for (int r = 0; r < reps && e == hipSuccess; ++r) {
-        e = launch_aux_step(h->dims, h->buf, adam_hyper(h->cfg), h->cfg.tau, p.her ? &p.ha : nullptr, states,
+        e = launch_aux_step(h->dims, h->buf, adam_hyper(h), h->cfg.tau, p.her ? &p.ha : nullptr, states,
                             h->cfg.states_ld, q_taken, batch, q_all, num_actions, beta, out_pi, out_v, out_loss,
                             out_grad_norm, p.budget ? &p.ba : nullptr, (hipStream_t)stream, ev);
         if (e == hipSuccess) e = hipEventSynchronize(ev[7]);

@@ -191,7 +191,7 @@ IQLH_DEV void adam_flat_block(float* __restrict__ params, float* __restrict__ gr
     const float bc1 = 1.f - powf(hp.beta1, tt);
     const float bc2 = 1.f - powf(hp.beta2, tt);
     const float decay = 1.f - hp.lr * hp.weight_decay;
-    bool bad = false;
+    bool bad = false, bad_state = false;
     for (int64_t qd = q0; qd < quads; qd += stride) {
         const int64_t i = 4 * qd;
         const bool first = qd == q0;
@@ -213,12 +213,14 @@ IQLH_DEV void adam_flat_block(float* __restrict__ params, float* __restrict__ gr
             p4[e] = p;
             m4[e] = mi;
             v4[e] = vi;
+            bad_state |= (i + e < n) && !(isfinite(p) && isfinite(mi) && isfinite(vi));
         }
         st4(params, i, n, vec, p4);
         st4(m, i, n, vec, m4);
         st4(v, i, n, vec, v4);
     }
     if (bad) set_flag(flags, 0x1);
+    if (bad_state) set_flag(flags, 0x8);
 }
 
 }  // namespace iqlh

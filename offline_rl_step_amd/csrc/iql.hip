@@ -1086,6 +1086,23 @@ hipError_t launch_iql_update(const IqlDims& d, const IqlBuffers& b, const AdamHy
     return hipGetLastError();
 }
 
+// Polyak averaging of the target copy ("GPU IQL + HER Porting Plan", section
+// "Rust Integration: gpu_iql_trainer.rs", target_ema_update): target +=
+// tau (params - target), every element of every group.
+__global__ __launch_bounds__(256) void iql_target_ema_kernel(float* __restrict__ target,
+                                                             const float* __restrict__ params, int64_t n, float tau) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        target[i] = fmaf(tau, params[i] - target[i], target[i]);
+}
+
+hipError_t launch_iql_target_ema(const IqlDims& d, const IqlBuffers& b, float tau, hipStream_t stream) {
+    const int64_t n = (int64_t)d.G * d.P;
+    const int64_t bn = (n + 255) / 256;
+    const int blocks = (int)(bn < 1024 ? bn : 1024);
+    hipLaunchKernelGGL(iql_target_ema_kernel, dim3(blocks), dim3(256), 0, stream, b.target, b.params, n, tau);
+    return hipGetLastError();
+}
+
 hipError_t launch_iql_refresh_shadows(const IqlDims& d, const IqlBuffers& b, hipStream_t stream) {
     const int64_t n = (int64_t)d.H * d.S_pad + (int64_t)d.H * d.H;
     const int64_t bn = (n + 255) / 256;

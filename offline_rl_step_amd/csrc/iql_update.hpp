@@ -91,6 +91,7 @@ IQLH_DEV void iql_adam_block(const IqlDims& d, const IqlBuffers& b, const AdamHy
     float* gr = b.grad + (int64_t)g * P;
     float* m = b.m + (int64_t)g * P;
     float* v = b.v + (int64_t)g * P;
+    float* tg = b.target + (int64_t)g * P;
     T* w1s = (T*)b.w1s + (int64_t)g * H * SP;
     T* w2s = (T*)b.w2s + (int64_t)g * H * H;
     T* w2ts = (T*)b.w2ts + (int64_t)g * H * H;
@@ -113,7 +114,7 @@ IQLH_DEV void iql_adam_block(const IqlDims& d, const IqlBuffers& b, const AdamHy
                                    : ((nrm > hp.max_grad_norm && nrm > 0.f) ? hp.max_grad_norm / nrm : 1.f);
     const float bc1 = 1.f - powf(hp.beta1, tt), bc2 = 1.f - powf(hp.beta2, tt);
     const float decay = 1.f - hp.lr * hp.weight_decay;
-    bool bad = false;
+    bool bad = false, bad_state = false;
     for (int64_t i = i0; i < P; i += (int64_t)nbx * 256) {
         const bool first = i == i0;
         const float gi = (first ? pg : gr[i]) * c;
@@ -129,9 +130,13 @@ IQLH_DEV void iql_adam_block(const IqlDims& d, const IqlBuffers& b, const AdamHy
             prm[i] = p;
             m[i] = mi;
             v[i] = vi;
+            bad_state |= !(isfinite(p) && isfinite(mi) && isfinite(vi));
         } else {
             bad = true;
         }
+        // Polyak target with the step's parameters (unchanged ones when the
+        // update was skipped): target += ema (p - target)
+        if (hp.ema > 0.f) tg[i] = fmaf(hp.ema, p - tg[i], tg[i]);
         if (i < (int64_t)H * S) {
             const int64_t r = i / S, cc = i - r * S;
             w1s[r * SP + cc] = to_shadow<T>(p);
@@ -142,6 +147,7 @@ IQLH_DEV void iql_adam_block(const IqlDims& d, const IqlBuffers& b, const AdamHy
         }
     }
     if (bad) set_flag(b.flags, 0x1);
+    if (bad_state) set_flag(b.flags, 0x8);
 }
 
 }  // namespace iqlh

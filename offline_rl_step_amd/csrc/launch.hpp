@@ -45,6 +45,7 @@ struct SourceSet {
 };
 struct AdamHyper {
     float lr, beta1, beta2, eps, weight_decay, max_grad_norm, clamp;
+    float ema;  // IQL trainers: Polyak weight of the target copy updated with the step, 0 = off
 };
 int budget_num_blocks(int64_t n);
 // workspace floats: k * nb (source partials) + nb (combined partials)
@@ -74,6 +75,7 @@ struct IqlBuffers {
     float* m;         // [G][P]
     float* v;         // [G][P]
     float* grad;      // [G][P]
+    float* target;    // [G][P] Polyak (EMA) target copy of params
     int32_t* t;       // [G]
     int64_t* step;    // [1]
     int32_t* flags;   // [1]
@@ -122,10 +124,24 @@ int iql_big_max_chunks(int S, int H);
 int iql_big_chunk(int S, int H, int B);
 hipError_t launch_iql_big_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float* tau, const void* states,
                                   int64_t ld, const float* q, int B, float* out_v, hipStream_t stream);
+hipError_t launch_iql_target_ema(const IqlDims& d, const IqlBuffers& b, float tau, hipStream_t stream);
 hipError_t launch_iql_refresh_shadows(const IqlDims& d, const IqlBuffers& b, hipStream_t stream);
 // workgroup and loss partials that a batch of B rows leaves for the reduction
 bool iql_partial_counts(const IqlDims& d, int B, int* nwg, int* nloss);
 int iql_adam_blocks(int64_t P);
+
+// ------------------------------------------------- non-finite sentinel
+constexpr int kSentinelSlots = 32;
+constexpr int kSentinelPiece = 4096;  // elements per block
+struct SentinelArgs {
+    const float* ptr[kSentinelSlots];
+    int64_t n[kSentinelSlots];
+    int block0[kSentinelSlots + 1];  // first block of each slot
+    int32_t* flags;                  // [nslots]
+    uint32_t vec;                    // bit s: slot s is 16-byte aligned
+    int nslots;
+};
+hipError_t launch_nonfinite_sentinel(const SentinelArgs& a, int blocks, hipStream_t stream);
 
 // ------------------------------------------------------- whole step
 // One pass of the hot path in four launches:

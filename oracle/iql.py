@@ -186,6 +186,14 @@ def adam_step(st, grad, hp):
     return norm, ~ok
 
 
+def target_ema(target, online, tau):
+    """Polyak averaging of the target copy ("GPU IQL + HER Porting Plan",
+    section "Rust Integration: gpu_iql_trainer.rs", target_ema_update; applied
+    after the IQL step, section "Where in the Training Loop IQL Gets
+    Called"): (1 - tau) target + tau online, elementwise."""
+    return (1.0 - tau) * np.asarray(target, dtype=np.float64) + tau * np.asarray(online, dtype=np.float64)
+
+
 @dataclass
 class StepResult:
     loss: float

@@ -323,11 +323,14 @@ def test_time_aux_step_reports_every_launch(m):
 
 @pytest.mark.parametrize("name,batch,rows", [("b16384_s128_h128_bf16_g2_budget", 16384, 128),
                                              ("b16384_s128_h128_bf16_g2_budget", 1000, 8),
-                                             ("stress_b65536_s256_h512_bf16", 65536, 32)])
+                                             ("stress_b65536_s256_h512_bf16", 65536, 40),
+                                             ("stress_b65536_s256_h512_bf16", 1000, 8)])
 def test_partial_layout_query(m, name, batch, rows):
     """The partial-buffer query the byte counts of bench.py rest on: one row
-    per 128-sample workgroup on the fused path, one per 2048-row chunk on the
-    layered one, each the parameter count rounded up to 128 floats."""
+    per 128-sample workgroup on the fused path; on the wide-hidden path one
+    per sample chunk (at most 42 chunks for six 256 x 256 weight-gradient
+    tiles, each a multiple of 128 samples: 1664 at batch 65536, 128 at 1000);
+    each row the parameter count rounded up to 128 floats."""
     w = synth.WORKLOADS[name]
     cfg = m.make_config(w.S, w.H, batch, num_groups=w.groups, compute_dtype=m.BF16, states_ld=w.S, tau=w.taus)
     tr = m.IqlTrainer(cfg, np.concatenate(synth.group_inits(w)))

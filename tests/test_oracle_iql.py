@@ -291,3 +291,24 @@ def test_train_step_matches_torch_composition():
         tp.grad = torch.tensor(tg * c, dtype=torch.float64)
         opt.step()
     np.testing.assert_allclose(st.params, tp.detach().numpy(), rtol=1e-11, atol=1e-14)
+
+
+# ------------------------------------------------------------ target EMA
+def test_target_ema_hand_worked_and_limits():
+    """Polyak averaging: weight tau on the online value, 1 - tau on the
+    target; tau = 0 keeps the target, tau = 1 copies the online network."""
+    t, o = np.array([1.0, -2.0, 0.5]), np.array([3.0, 2.0, 0.5])
+    np.testing.assert_array_equal(iql.target_ema(t, o, 0.25), [1.5, -1.0, 0.5])
+    np.testing.assert_array_equal(iql.target_ema(t, o, 0.0), t)
+    np.testing.assert_array_equal(iql.target_ema(t, o, 1.0), o)
+
+
+def test_target_ema_geometric_convergence():
+    """k updates toward a fixed online vector leave (1 - tau)^k of the
+    initial gap: target_k = online + (1 - tau)^k (target_0 - online)."""
+    g = np.random.default_rng(3)
+    t0, o = g.standard_normal(50), g.standard_normal(50)
+    tau, t = 0.05, t0.copy()
+    for k in range(1, 41):
+        t = iql.target_ema(t, o, tau)
+        np.testing.assert_allclose(t, o + (1 - tau) ** k * (t0 - o), rtol=1e-12, atol=1e-14)
