@@ -155,6 +155,25 @@ int iql_get_state(iql_handle h, int32_t group, float* d_params, float* d_m, floa
 int iql_set_state(iql_handle h, int32_t group, const float* d_params, const float* d_m,
                   const float* d_v, const int32_t* d_t, void* stream);
 
+/* Forward-only V on next states and the IQL bootstrap target ([P1]
+ * "Rust Integration: gpu_iql_trainer.rs", forward_values; "Phase 2
+ * Integration": the DQN target becomes r + gamma V(s') in place of the
+ * target network's maximum).  Uses the online parameters of every group; no
+ * loss, no gradient, no state change.
+ *   next_states  device [B, states_ld] of states_dtype (IQLH_F32 or
+ *                IQLH_BF16; e.g. her_out.next_states, f32).  A dtype other
+ *                than the trainer's compute dtype is converted once (bf16
+ *                round to nearest even) into a handle-owned buffer first.
+ *   out_v        device [num_groups, B] f32: V(s').
+ *   rewards      device [B] f32, or NULL (then out_target must be NULL).
+ *   dones        device [B] f32 (1 = terminal), or NULL (no terminal rows).
+ *   out_target   device [num_groups, B] f32: r + gamma (1 - done) V(s').
+ * 1 <= B <= max_batch, gamma finite.  V(s') equals, bit for bit, the V(s)
+ * that iql_train_step reports for the same rows and parameters. */
+int iql_forward_values(iql_handle h, const void* next_states, int32_t states_dtype, int64_t states_ld,
+                       int32_t batch, float* out_v, const float* rewards, const float* dones, float gamma,
+                       float* out_target, void* stream);
+
 /* Polyak (EMA) target copy of the value network ([P1] "Rust Integration:
  * gpu_iql_trainer.rs", target_ema_update; run after the IQL step in "Where
  * in the Training Loop IQL Gets Called").  The handle keeps a target copy of

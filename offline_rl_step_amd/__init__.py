@@ -90,6 +90,7 @@ _lib_iql_time_cg = _sig("iql_time_compute_gradients", _i32, [_p, _p, _p, _i32, _
 _lib_iql_partial_layout = _sig("iql_partial_layout", _i32, [_p, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i64)])
 _lib_iql_get_state = _sig("iql_get_state", _i32, [_p, _i32, _p, _p, _p, _p, _p])
 _lib_iql_set_state = _sig("iql_set_state", _i32, [_p, _i32, _p, _p, _p, _p, _p])
+_lib_iql_forward_values = _sig("iql_forward_values", _i32, [_p, _p, _i32, _i64, _i32, _p, _p, _p, _f, _p, _p])
 _lib_iql_target_ema_update = _sig("iql_target_ema_update", _i32, [_p, _f, _p])
 _lib_iql_set_target_ema = _sig("iql_set_target_ema", _i32, [_p, _f])
 _lib_iql_get_target = _sig("iql_get_target", _i32, [_p, _i32, _p, _p])
@@ -223,6 +224,17 @@ def nonfinite_check(buffers, slot_flags, stream=None):
     ptrs = (_p * n)(*[None if b is None else b.data_ptr() for b in buffers])
     lens = (_i64 * n)(*[0 if b is None else b.numel() for b in buffers])
     _check(_lib_nonfinite_check(ptrs, lens, n, _ptr(slot_flags), _stream(stream)), "iqlh_nonfinite_check")
+
+
+def iql_forward_values(h, next_states, batch, out_v, rewards=None, dones=None, gamma=0.99, out_target=None,
+                       states_ld=None, stream=None):
+    """V(s') of every group (online parameters) and, with rewards, the
+    bootstrap target r + gamma (1 - done) V(s')."""
+    import torch
+    dt = BF16 if next_states.dtype == torch.bfloat16 else F32
+    ld = states_ld if states_ld is not None else next_states.stride(0)
+    _check(_lib_iql_forward_values(h, _ptr(next_states), dt, ld, batch, _ptr(out_v), _ptr(rewards), _ptr(dones),
+                                   gamma, _ptr(out_target), _stream(stream)), "iql_forward_values")
 
 
 def iql_target_ema_update(h, tau, stream=None):
@@ -408,6 +420,10 @@ class IqlTrainer:
         self.cfg = cfg
         self.h = iql_create(cfg, init_params_host)
         self.n_params = iql_num_params(cfg.state_dim, cfg.hidden)
+
+    def forward_values(self, next_states, batch, out_v, rewards=None, dones=None, gamma=0.99, out_target=None,
+                       states_ld=None, stream=None):
+        iql_forward_values(self.h, next_states, batch, out_v, rewards, dones, gamma, out_target, states_ld, stream)
 
     def target_ema_update(self, tau, stream=None):
         iql_target_ema_update(self.h, tau, stream)

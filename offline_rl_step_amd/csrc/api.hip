@@ -41,6 +41,7 @@ struct iql_trainer {
     IqlBuffers buf;
     int device;
     float ema_tau;  // Polyak weight folded into every step's Adam launch, 0 = off
+    void* fv_states;  // [max_batch][S_pad] compute dtype: next states converted for iql_forward_values
     std::vector<void*> allocs;
 };
 
@@ -140,6 +141,7 @@ int iql_create(const iqlh_config* cfg, const float* init_params_host, iql_handle
     const size_t nlay = d.layered && !d.big ? nact : 0;  // layered-only activations
     struct { void** p; size_t bytes; } plan[] = {
         {(void**)&b.params, sizeof(float) * G * P},
+        {&t->fv_states, esz * (size_t)MB * d.S_pad},
         {(void**)&b.m, sizeof(float) * G * P},
         {(void**)&b.v, sizeof(float) * G * P},
         {(void**)&b.grad, sizeof(float) * G * P},
@@ -322,6 +324,39 @@ int iql_set_state(iql_handle h, int32_t group, const float* d_params, const floa
         e = hipMemcpyAsync(h->buf.t + group, d_t, sizeof(int32_t), hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess) e = launch_iql_refresh_shadows(h->dims, h->buf, s);
     if (e != hipSuccess) return hip_fail(e, "iql_set_state");
+    return IQLH_OK;
+}
+
+int iql_forward_values(iql_handle h, const void* next_states, int32_t states_dtype, int64_t states_ld, int32_t batch,
+                       float* out_v, const float* rewards, const float* dones, float gamma, float* out_target,
+                       void* stream) {
+    if (!h) return fail(IQLH_EINVAL, "handle is NULL");
+    if (!next_states || !out_v) return fail(IQLH_EINVAL, "next_states and out_v must be non-NULL");
+    if (batch < 1 || batch > h->cfg.max_batch)
+        return fail(IQLH_EINVAL, "batch %d outside [1, max_batch=%d]", batch, h->cfg.max_batch);
+    if (states_dtype != IQLH_F32 && states_dtype != IQLH_BF16)
+        return fail(IQLH_EINVAL, "states_dtype must be IQLH_F32 or IQLH_BF16");
+    if (states_ld < h->dims.S) return fail(IQLH_EINVAL, "states_ld < state_dim");
+    if ((rewards == nullptr) != (out_target == nullptr))
+        return fail(IQLH_EINVAL, "rewards and out_target go together");
+    if (dones && !rewards) return fail(IQLH_EINVAL, "dones without rewards");
+    if (!std::isfinite(gamma)) return fail(IQLH_EINVAL, "gamma must be finite");
+    const IqlDims& d = h->dims;
+    hipStream_t s = (hipStream_t)stream;
+    const void* x = next_states;
+    int64_t ld = states_ld;
+    const bool aligned = ((uintptr_t)next_states & 15u) == 0 && states_ld % 8 == 0;
+    if (states_dtype != d.dtype || (d.big && !aligned)) {
+        // one conversion pass into the handle's buffer (row stride S_pad)
+        hipError_t e = launch_convert_rows(next_states, states_dtype, states_ld, h->fv_states, d.dtype, d.S_pad, batch,
+                                           d.S, s);
+        if (e != hipSuccess) return hip_fail(e, "iql_forward_values convert");
+        x = h->fv_states;
+        ld = d.S_pad;
+    }
+    ValueOut vo{out_v, rewards, dones, gamma, out_target};
+    hipError_t e = launch_iql_forward_values(d, h->buf, x, ld, batch, vo, s);
+    if (e != hipSuccess) return hip_fail(e, "iql_forward_values launch");
     return IQLH_OK;
 }
 

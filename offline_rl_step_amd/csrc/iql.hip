@@ -176,6 +176,8 @@ struct FusedArgs {
     int B, S, nwg;
     int64_t P, Pp;
     int32_t* flags;
+    int fwd_only;         // 1: V (and the bootstrap target) only, no loss or gradients
+    ValueOut vo;          // outputs of the forward-only pass
 };
 
 template <typename T, int SP, int H, int NW>
@@ -400,6 +402,10 @@ __global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
         }
     }
     const float v = vpart + __shfl_xor(vpart, 32, 64) + prm[po.b3];
+    if (a.fwd_only) {
+        if (valid && h == 0) write_value(a.vo, g, B, b, v);
+        return;
+    }
     float dv = 0.f, lterm = 0.f;
     if (valid) {
         const float diff = a.q[b] - v;
@@ -749,7 +755,7 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
     }
     const int th = tid < H ? tid : 0;
     const float vb1 = prm[po.b1 + th], vb2 = prm[po.b2 + th], vw3 = prm[po.w3 + th];
-    const float qb = a.q[bc];  // used by valid lanes only
+    const float qb = a.fwd_only ? 0.f : a.q[bc];  // used by valid lanes only
     const float b3 = prm[po.b3];
     float qa[4];
 #pragma unroll
@@ -822,6 +828,10 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
     if (q == 0) svh[fh * BT + bl] = vpart;
     __syncthreads();
     const float v = (svh[bl] + svh[BT + bl]) + b3;
+    if (a.fwd_only) {
+        if (valid && fh == 0 && q == 0) write_value(a.vo, g, B, b, v);
+        return;
+    }
     float dv = 0.f, lterm = 0.f;
     if (valid) {
         const float diff = qb - v;
@@ -1034,7 +1044,7 @@ hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float
     const Variant* var = pick(d.dtype, d.S, d.H);
     if (!var) return hipErrorInvalidValue;
     const int BT = 32 * var->NW;
-    FusedArgs fa;
+    FusedArgs fa{};  // zero: fwd_only = 0, vo unused
     fa.states = states; fa.ld = ld; fa.q = q; fa.params = b.params;
     fa.w1s = b.w1s; fa.w2s = b.w2s; fa.w2ts = b.w2ts;
     fa.part = b.part; fa.loss_part = b.loss_part; fa.out_v = out_v;
@@ -1042,6 +1052,50 @@ hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float
     fa.tau0 = tau[0]; fa.tau1 = tau[d.G > 1 ? 1 : 0]; fa.invB = 1.f / (float)B;
     fa.B = B; fa.S = d.S; fa.nwg = (B + BT - 1) / BT; fa.P = d.P; fa.Pp = d.Pp; fa.flags = b.flags;
     return var->fn(fa, d.G, stream, ev0, ev1);
+}
+
+hipError_t launch_iql_forward_values(const IqlDims& d, const IqlBuffers& b, const void* states, int64_t ld, int B,
+                                     const ValueOut& vo, hipStream_t stream) {
+    if (d.layered)
+        return d.big ? launch_iql_big_forward(d, b, states, ld, B, vo, stream)
+                     : launch_iql_layered_forward(d, b, states, ld, B, vo, stream);
+    const Variant* var = pick(d.dtype, d.S, d.H);
+    if (!var) return hipErrorInvalidValue;
+    const int BT = 32 * var->NW;
+    FusedArgs fa{};
+    fa.states = states; fa.ld = ld; fa.params = b.params;
+    fa.w1s = b.w1s; fa.w2s = b.w2s; fa.w2ts = b.w2ts;
+    fa.part = b.part; fa.loss_part = b.loss_part;
+    fa.invB = 1.f / (float)B;
+    fa.B = B; fa.S = d.S; fa.nwg = (B + BT - 1) / BT; fa.P = d.P; fa.Pp = d.Pp; fa.flags = b.flags;
+    fa.fwd_only = 1;
+    fa.vo = vo;
+    return var->fn(fa, d.G, stream, nullptr, nullptr);
+}
+
+// ---------------------------------------------------------- row conversion
+// f32 <-> bf16 (round to nearest even) of a [rows][cols] block; one thread per
+// element pair along a row.
+__global__ __launch_bounds__(256) void convert_rows_kernel(const void* __restrict__ src, int src_dtype, int64_t src_ld,
+                                                           void* __restrict__ dst, int dst_dtype, int64_t dst_ld,
+                                                           int rows, int cols) {
+    const int64_t n = (int64_t)rows * cols;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int64_t r = i / cols, c = i - r * cols;
+        const float x = src_dtype == 1 ? bf2f(((const uint16_t*)src)[r * src_ld + c]) : ((const float*)src)[r * src_ld + c];
+        if (dst_dtype == 1) ((uint16_t*)dst)[r * dst_ld + c] = f2bf(x);
+        else ((float*)dst)[r * dst_ld + c] = x;
+    }
+}
+
+hipError_t launch_convert_rows(const void* src, int src_dtype, int64_t src_ld, void* dst, int dst_dtype,
+                               int64_t dst_ld, int rows, int cols, hipStream_t stream) {
+    const int64_t n = (int64_t)rows * cols;
+    const int64_t bn = (n + 255) / 256;
+    const int blocks = (int)(bn < 2048 ? bn : 2048);
+    hipLaunchKernelGGL(convert_rows_kernel, dim3(blocks), dim3(256), 0, stream, src, src_dtype, src_ld, dst, dst_dtype,
+                       dst_ld, rows, cols);
+    return hipGetLastError();
 }
 
 bool iql_partial_counts(const IqlDims& d, int B, int* nwg, int* nloss) {

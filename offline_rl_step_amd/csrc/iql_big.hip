@@ -247,6 +247,8 @@ struct BigArgs {
     int64_t off_b1, off_w2, off_b2, off_w3, off_b3;
     float tau0, tau1, invB;
     int B, S, H, chunk, nchunk, nblk;
+    int fwd_only;  // 1: V (and the bootstrap target) only
+    ValueOut vo;
 };
 
 // Workgroup id -> (tile, group): consecutive ids go to different XCDs, so the
@@ -431,6 +433,18 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
     }
     __syncthreads();
     const float b3 = prm[a.off_b3];
+    if (a.fwd_only) {
+        if (wv == 0 && q == 0) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int sl = 16 * j + l16, s = s0 + sl;
+                const float v = ((svp[sl] + svp[kFwd2Samples + sl]) +
+                                 (svp[2 * kFwd2Samples + sl] + svp[3 * kFwd2Samples + sl])) + b3;
+                if (s < B) write_value(a.vo, g, B, s, v);
+            }
+        }
+        return;
+    }
     const float tau = g == 0 ? a.tau0 : a.tau1;
     float dv[8], lsum = 0.f, dsum = 0.f;
 #pragma unroll
@@ -644,8 +658,22 @@ int iql_big_chunk(int S, int H, int B) {
     return c < kFwd2Samples ? kFwd2Samples : c;
 }
 
+static hipError_t big_launch(const IqlDims& d, const IqlBuffers& b, const float* tau, const void* states, int64_t ld,
+                             const float* q, int B, float* out_v, const ValueOut* vo, hipStream_t stream);
+
 hipError_t launch_iql_big_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float* tau, const void* states,
                                   int64_t ld, const float* q, int B, float* out_v, hipStream_t stream) {
+    return big_launch(d, b, tau, states, ld, q, B, out_v, nullptr, stream);
+}
+
+hipError_t launch_iql_big_forward(const IqlDims& d, const IqlBuffers& b, const void* states, int64_t ld, int B,
+                                  const ValueOut& vo, hipStream_t stream) {
+    const float tau[2] = {0.f, 0.f};
+    return big_launch(d, b, tau, states, ld, nullptr, B, nullptr, &vo, stream);
+}
+
+static hipError_t big_launch(const IqlDims& d, const IqlBuffers& b, const float* tau, const void* states, int64_t ld,
+                             const float* q, int B, float* out_v, const ValueOut* vo, hipStream_t stream) {
     const int G = d.G, S = d.S, H = d.H;
     BigArgs a{};
     a.x = (const uint16_t*)states; a.ldx = ld;
@@ -662,6 +690,10 @@ hipError_t launch_iql_big_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const f
     a.chunk = iql_big_chunk(S, H, B);
     a.nchunk = (B + a.chunk - 1) / a.chunk;
     a.nblk = iql_big_blocks(B);
+    if (vo) {
+        a.fwd_only = 1;
+        a.vo = *vo;
+    }
 
     static bool attr = false;
     if (!attr) {
@@ -679,6 +711,7 @@ hipError_t launch_iql_big_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const f
     const dim3 g2(a.nblk, G);
     if (H == 512) hipLaunchKernelGGL(big_fwd2_kernel<512>, g2, dim3(kThreads), fwd2_lds_bytes<512>(), stream, a);
     else hipLaunchKernelGGL(big_fwd2_kernel<256>, g2, dim3(kThreads), fwd2_lds_bytes<256>(), stream, a);
+    if (vo) return hipGetLastError();
     hipLaunchKernelGGL(big_tile_kernel<1>, gt, dim3(kThreads), tile_lds_bytes(), stream, a);
     const int nth = H / kTile, nts = (S + kTile - 1) / kTile;
     const int njob = nth * nth + nth * nts + 1;

@@ -221,6 +221,8 @@ struct RowArgs {
     float tau0, tau1, invB;
     int B, H, nblk;
     int64_t P, w3off;
+    int fwd_only;  // 1: V (and the bootstrap target) only
+    ValueOut vo;
 };
 
 constexpr int kRowsPerBlock = 64;  // 4 waves x 16 rows
@@ -243,6 +245,10 @@ __global__ __launch_bounds__(256) void iql_rows_kernel(RowArgs a) {
             s = fmaf(w3[hh], zz > 0.f ? zz : 0.f, s);
         }
         const float v = wave_sum(s) + b3;
+        if (a.fwd_only) {
+            if (lane == 0) write_value(a.vo, g, a.B, b, v);
+            continue;
+        }
         const float diff = a.q[b] - v;
         const float w = diff >= 0.f ? tau : 1.f - tau;
         const float dv = -2.f * w * diff * a.invB;
@@ -261,7 +267,7 @@ __global__ __launch_bounds__(256) void iql_rows_kernel(RowArgs a) {
     }
     if (lane == 0) wl[wv] = lsum;
     __syncthreads();
-    if (threadIdx.x == 0) a.loss_part[(int64_t)g * a.nblk + blockIdx.x] = wl[0] + wl[1] + wl[2] + wl[3];
+    if (threadIdx.x == 0 && !a.fwd_only) a.loss_part[(int64_t)g * a.nblk + blockIdx.x] = wl[0] + wl[1] + wl[2] + wl[3];
 }
 
 // ---------------------------------------------- split-K weight gradients
@@ -364,9 +370,25 @@ bool iql_layered_supported(int dtype, int S, int H) {
 }
 int iql_layered_chunk() { return kChunk; }
 
+static hipError_t layered_launch(const IqlDims& d, const IqlBuffers& b, const float* tau, const void* states,
+                                 int64_t ld, const float* q, int B, float* out_v, const ValueOut* vo,
+                                 hipStream_t stream);
+
 hipError_t launch_iql_layered_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float* tau,
                                       const void* states, int64_t ld, const float* q, int B,
                                       float* out_v, hipStream_t stream) {
+    return layered_launch(d, b, tau, states, ld, q, B, out_v, nullptr, stream);
+}
+
+hipError_t launch_iql_layered_forward(const IqlDims& d, const IqlBuffers& b, const void* states, int64_t ld,
+                                      int B, const ValueOut& vo, hipStream_t stream) {
+    const float tau[2] = {0.f, 0.f};
+    return layered_launch(d, b, tau, states, ld, nullptr, B, nullptr, &vo, stream);
+}
+
+static hipError_t layered_launch(const IqlDims& d, const IqlBuffers& b, const float* tau, const void* states,
+                                 int64_t ld, const float* q, int B, float* out_v, const ValueOut* vo,
+                                 hipStream_t stream) {
     const int G = d.G, S = d.S, H = d.H;
     const int nchunk = (B + kChunk - 1) / kChunk;
     const int nblk = (B + kRowsPerBlock - 1) / kRowsPerBlock;
@@ -401,8 +423,13 @@ hipError_t launch_iql_layered_fwd_bwd(const IqlDims& d, const IqlBuffers& b, con
     ra.tau0 = tau[0]; ra.tau1 = tau[G > 1 ? 1 : 0]; ra.invB = 1.f / (float)B;
     ra.B = B; ra.H = H; ra.nblk = nblk; ra.P = d.P;
     ra.w3off = (int64_t)H * S + H + (int64_t)H * H + H;
+    if (vo) {
+        ra.fwd_only = 1;
+        ra.vo = *vo;
+    }
     if (d.dtype == 1) hipLaunchKernelGGL(iql_rows_kernel<uint16_t>, dim3(nblk, G), dim3(256), 0, stream, ra);
     else hipLaunchKernelGGL(iql_rows_kernel<float>, dim3(nblk, G), dim3(256), 0, stream, ra);
+    if (vo) return hipGetLastError();
     // L3: dz1 = (dz2 W2) * relu'(z1)   (B operand: W2^T shadow, rows h1, k = h2)
     FwdArgs f3{};
     f3.A = Operand{b.act_dz2, H, B, H, 0, 0, 0};

@@ -43,6 +43,21 @@ struct SourceSet {
     float alpha[kMaxSources];
     int32_t k;
 };
+// Outputs of a forward-only pass: V and, with rewards, the bootstrap target
+// r + gamma (1 - done) V.
+struct ValueOut {
+    float* v;           // [G][B]
+    const float* rew;   // [B] or null: no target
+    const float* done;  // [B] or null: no terminal rows
+    float gamma;
+    float* target;      // [G][B] (with rew)
+};
+__device__ __forceinline__ void write_value(const ValueOut& o, int g, int B, int b, float v) {
+    const int64_t i = (int64_t)g * B + b;
+    o.v[i] = v;
+    if (o.target) o.target[i] = fmaf(o.gamma * (1.f - (o.done ? o.done[b] : 0.f)), v, o.rew[b]);
+}
+
 struct AdamHyper {
     float lr, beta1, beta2, eps, weight_decay, max_grad_norm, clamp;
     float ema;  // IQL trainers: Polyak weight of the target copy updated with the step, 0 = off
@@ -125,6 +140,17 @@ int iql_big_chunk(int S, int H, int B);
 hipError_t launch_iql_big_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float* tau, const void* states,
                                   int64_t ld, const float* q, int B, float* out_v, hipStream_t stream);
 hipError_t launch_iql_target_ema(const IqlDims& d, const IqlBuffers& b, float tau, hipStream_t stream);
+hipError_t launch_iql_layered_forward(const IqlDims& d, const IqlBuffers& b, const void* states, int64_t ld,
+                                      int B, const ValueOut& vo, hipStream_t stream);
+hipError_t launch_iql_big_forward(const IqlDims& d, const IqlBuffers& b, const void* states, int64_t ld, int B,
+                                  const ValueOut& vo, hipStream_t stream);
+// V(s) of every group for B rows of `states` (compute dtype, row stride ld),
+// and the bootstrap target when vo.rew is set; no loss, no gradients.
+hipError_t launch_iql_forward_values(const IqlDims& d, const IqlBuffers& b, const void* states, int64_t ld, int B,
+                                     const ValueOut& vo, hipStream_t stream);
+// dst[r][c] = src[r][c] converted between f32 and the compute dtype (bf16 RNE)
+hipError_t launch_convert_rows(const void* src, int src_dtype, int64_t src_ld, void* dst, int dst_dtype,
+                               int64_t dst_ld, int rows, int cols, hipStream_t stream);
 hipError_t launch_iql_refresh_shadows(const IqlDims& d, const IqlBuffers& b, hipStream_t stream);
 // workgroup and loss partials that a batch of B rows leaves for the reduction
 bool iql_partial_counts(const IqlDims& d, int B, int* nwg, int* nloss);

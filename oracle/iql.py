@@ -186,6 +186,18 @@ def adam_step(st, grad, hp):
     return norm, ~ok
 
 
+def bootstrap_target(rewards, dones, v_next, gamma):
+    """IQL's bootstrap target with V(s') in place of the target network's
+    maximum ("GPU IQL + HER Porting Plan", section "Phase 2 Integration",
+    IQL modifies the target computation): r + gamma V(s').  Reading: terminal
+    rows (done = 1) drop the bootstrap term, r + gamma (1 - done) V(s'), the
+    usual DQN convention the pages' train step takes dones for; dones None
+    means no terminal rows."""
+    r = np.asarray(rewards, dtype=np.float64)
+    d = np.zeros_like(r) if dones is None else np.asarray(dones, dtype=np.float64)
+    return r + gamma * (1.0 - d) * np.asarray(v_next, dtype=np.float64)
+
+
 def target_ema(target, online, tau):
     """Polyak averaging of the target copy ("GPU IQL + HER Porting Plan",
     section "Rust Integration: gpu_iql_trainer.rs", target_ema_update; applied

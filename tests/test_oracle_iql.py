@@ -312,3 +312,13 @@ def test_target_ema_geometric_convergence():
     for k in range(1, 41):
         t = iql.target_ema(t, o, tau)
         np.testing.assert_allclose(t, o + (1 - tau) ** k * (t0 - o), rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------ bootstrap target
+def test_bootstrap_target_hand_worked():
+    """r + gamma (1 - done) V(s'): gamma 0 leaves the reward, a terminal row
+    leaves the reward, otherwise the discounted value is added."""
+    r, d, v = np.array([1.0, -0.01, 0.5]), np.array([0.0, 0.0, 1.0]), np.array([2.0, -4.0, 100.0])
+    np.testing.assert_array_equal(iql.bootstrap_target(r, d, v, 0.5), [2.0, -2.01, 0.5])
+    np.testing.assert_array_equal(iql.bootstrap_target(r, d, v, 0.0), r)
+    np.testing.assert_array_equal(iql.bootstrap_target(r, None, v, 0.5), r + 0.5 * v)
