@@ -379,6 +379,32 @@ int iql_time_aux_step(iql_handle h, const iqlh_her_step* her, const void* states
                       int32_t reps, float* out_avg_us, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Prioritized-replay source sampling ([P1] "Current State": the GPU PER
+ * buffer samples by a prefix sum of the priorities and a search in it and
+ * returns indices and IS weights; "How HER Interacts with GPU PER":
+ * sample_indices for the HER sources).
+ *   Row i is drawn with probability p_i / sum(p), n times independently, by
+ *   inverse transform: u = U * total with U = (word >> 11) * 2^-53, word =
+ *   word 0 of Philox4x64-10 with key (seed, 0x5045526472617773) and counter
+ *   (k, *d_step, 0, 0) for draw k, u capped just below the total; the row is
+ *   the first i whose inclusive binary64 prefix sum exceeds u.
+ *   IS weight of draw k: (p_min / p_idx[k])^beta, p_min the smallest drawn
+ *   priority (prioritized replay's (N P(i))^-beta over the batch maximum).
+ *   d_priorities  device [size] f32, >= 0 (already raised to any exponent).
+ *   d_out_idx     device [n] int32; d_out_weights device [n] f32.
+ *   d_step        device int64 counter or NULL (= 0).
+ *   d_flags       device sticky flag word or NULL: IQLH_FLAG_BAD_INDEX when a
+ *                 priority is negative or non-finite or the total is not > 0
+ *                 (then the draws are -1 with weight 0).
+ *   workspace     device, >= per_workspace_bytes(size), 8-byte aligned; holds
+ *                 the prefix sums afterwards ([size] binary64).
+ * 1 <= size < 2^31, n >= 0 (0 computes the prefix sums only), beta >= 0. */
+int per_workspace_bytes(int64_t size, size_t* bytes);
+int per_sample_indices(const float* d_priorities, int64_t size, int32_t n, uint64_t seed, const int64_t* d_step,
+                       float beta, int32_t* d_out_idx, float* d_out_weights, int32_t* d_flags, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Fused non-finite sentinel ([P2] "Phase E -- SP2 fused NaN check kernel":
  * one launch over a table of buffers, a sticky flag per slot that is written
  * 1 and never cleared, null entries skipped).

@@ -110,6 +110,8 @@ _lib_iql_aux_step = _sig("iql_aux_step", _i32, [_p, ctypes.POINTER(HerStep), _p,
 _lib_iql_time_aux_step = _sig("iql_time_aux_step", _i32, [_p, ctypes.POINTER(HerStep), _p, _p, _i32, _p, _i32, _f,
                                                           _p, _p, _p, _p, ctypes.POINTER(BudgetStep), _i32,
                                                           ctypes.POINTER(_f), _p])
+_lib_per_ws = _sig("per_workspace_bytes", _i32, [_i64, ctypes.POINTER(ctypes.c_size_t)])
+_lib_per_sample = _sig("per_sample_indices", _i32, [_p, _i64, _i32, _u64, _p, _f, _p, _p, _p, _p, ctypes.c_size_t, _p])
 _lib_nonfinite_check = _sig("iqlh_nonfinite_check", _i32, [ctypes.POINTER(_p), ctypes.POINTER(_i64), _i32, _p, _p])
 _lib_last_error = _sig("iqlh_last_error", ctypes.c_char_p, [])
 
@@ -215,6 +217,20 @@ def iql_partial_layout(h, batch):
     rows, floats = _i32(), _i64()
     _check(_lib_iql_partial_layout(h, batch, ctypes.byref(rows), ctypes.byref(floats)), "iql_partial_layout")
     return rows.value, floats.value
+
+
+def per_workspace_bytes(size):
+    out = ctypes.c_size_t()
+    _check(_lib_per_ws(size, ctypes.byref(out)), "per_workspace_bytes")
+    return out.value
+
+
+def per_sample_indices(priorities, n, seed, beta, out_idx, out_weights, workspace, d_step=None, d_flags=None,
+                       stream=None):
+    """n prioritized draws over the rows of `priorities` (f32 tensor)."""
+    _check(_lib_per_sample(_ptr(priorities), priorities.numel(), n, seed, _ptr(d_step), beta, _ptr(out_idx),
+                           _ptr(out_weights), _ptr(d_flags), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(stream)), "per_sample_indices")
 
 
 def nonfinite_check(buffers, slot_flags, stream=None):

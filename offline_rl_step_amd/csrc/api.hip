@@ -413,6 +413,30 @@ int iql_status(iql_handle h, int32_t* flags_host) {
     return IQLH_OK;
 }
 
+int per_workspace_bytes(int64_t size, size_t* bytes) {
+    if (!bytes) return fail(IQLH_EINVAL, "bytes is NULL");
+    if (size < 1 || size > INT32_MAX) return fail(IQLH_EINVAL, "size must be in [1, 2^31 - 1]");
+    *bytes = per_workspace_bytes_for(size);
+    return IQLH_OK;
+}
+
+int per_sample_indices(const float* d_priorities, int64_t size, int32_t n, uint64_t seed, const int64_t* d_step,
+                       float beta, int32_t* d_out_idx, float* d_out_weights, int32_t* d_flags, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    if (size < 1 || size > INT32_MAX) return fail(IQLH_EINVAL, "size must be in [1, 2^31 - 1]");
+    if (n < 0) return fail(IQLH_EINVAL, "n must be >= 0");
+    if (!(beta >= 0.f) || !std::isfinite(beta)) return fail(IQLH_EINVAL, "beta must be finite and >= 0");
+    if (!d_priorities || !workspace || (n > 0 && (!d_out_idx || !d_out_weights)))
+        return fail(IQLH_EINVAL, "per_sample_indices: NULL pointer");
+    if (workspace_bytes < per_workspace_bytes_for(size))
+        return fail(IQLH_EINVAL, "workspace too small: %zu < %zu bytes", workspace_bytes, per_workspace_bytes_for(size));
+    if (((uintptr_t)workspace & 7u) != 0) return fail(IQLH_EINVAL, "workspace must be 8-byte aligned");
+    hipError_t e = launch_per_sample(d_priorities, size, n, seed, d_step, beta, d_out_idx, d_out_weights, d_flags,
+                                     workspace, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "per_sample_indices launch");
+    return IQLH_OK;
+}
+
 int iqlh_nonfinite_check(const float* const* d_bufs, const int64_t* lens, int32_t num_slots,
                          int32_t* d_slot_flags, void* stream) {
     if (!d_bufs || !lens || !d_slot_flags) return fail(IQLH_EINVAL, "iqlh_nonfinite_check: NULL argument");

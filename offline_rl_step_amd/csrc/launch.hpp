@@ -156,6 +156,11 @@ hipError_t launch_iql_refresh_shadows(const IqlDims& d, const IqlBuffers& b, hip
 bool iql_partial_counts(const IqlDims& d, int B, int* nwg, int* nloss);
 int iql_adam_blocks(int64_t P);
 
+// ------------------------------------------------- prioritized sampling
+size_t per_workspace_bytes_for(int64_t size);
+hipError_t launch_per_sample(const float* p, int64_t size, int n, uint64_t seed, const int64_t* d_step, float beta,
+                             int32_t* idx, float* w, int32_t* flags, void* workspace, hipStream_t stream);
+
 // ------------------------------------------------- non-finite sentinel
 constexpr int kSentinelSlots = 32;
 constexpr int kSentinelPiece = 4096;  // elements per block

@@ -16,7 +16,8 @@ Readings (the pages name the method, not its constants):
     row of priority 0 is never drawn;
   * U is 53 random bits of word 0 of Philox4x64-10 under the key (seed,
     PER_KEY1) at counter (draw, step, 0, 0), times 2^-53 -- the generator the
-    HER donor draws use, with a key word of its own;
+    HER donor draws use, with a key word of its own; u is capped just below
+    the total (U * total can round up to it), so a row is always found;
   * importance weights are those of prioritized replay (Schaul et al., 2016):
     (N P(i))^-beta divided by the largest weight of the batch, which is
     (p_min / p_i)^beta with p_min the smallest priority among the batch's
@@ -42,7 +43,7 @@ def sample(priorities, n, seed, step, beta):
     p = np.asarray(priorities, dtype=np.float64)
     prefix = np.cumsum(p)
     total = prefix[-1]
-    u = uniforms(n, seed, step) * total
+    u = np.minimum(uniforms(n, seed, step) * total, np.nextafter(total, -np.inf))
     idx = np.searchsorted(prefix, u, side="right")
     pi = p[idx]
     w = (pi.min() / pi) ** beta
