@@ -50,6 +50,8 @@ def parse():
                         "step with the budget); the CPU baseline then runs only when --cpu-baseline is given")
     p.add_argument("--cpu-baseline", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-next-rows", action="store_true",
+                   help="skip timing the widening entry points (forward values, target EMA, sentinel, sampling)")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--kernel-reps", type=int, default=200)
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -403,6 +405,73 @@ def summarize_profiles(d, workload=None):
     print(md)
 
 
+def time_next_rows(ctx, torch, np, reps=100):
+    """Mean GPU time per call (inside a captured graph) of the widening entry
+    points on the bench workload, each with its roofline: V(s') + bootstrap target (MFMA flops of the two
+    forward products), the Polyak target update and the non-finite sentinel
+    (bytes each must move), prioritized sampling of the HER sources over the
+    whole replay buffer (prefix sums: read the priorities twice, write the
+    binary64 prefix; the searches touch a few lines per draw)."""
+    m, w, d = ctx.m, ctx.w, ctx.d
+    B, S, H, G = w.B, w.S, w.H, w.groups
+
+    def timed(fn, calls=50):
+        # `calls` back-to-back calls captured in one graph, replayed: GPU time
+        # per call, not the rate at which Python can issue them
+        fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(calls):
+                fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        stream = torch.cuda.current_stream()
+        e0.record(stream)
+        for _ in range(max(1, reps // 10)):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (max(1, reps // 10) * calls)
+
+    out = {}
+    g = np.random.default_rng(5)
+    nxt = torch.from_numpy(g.standard_normal((B, S)).astype(np.float32)).to(d).to(torch.bfloat16)
+    rew = torch.zeros(B, dtype=torch.float32, device=d)
+    don = torch.zeros(B, dtype=torch.float32, device=d)
+    vn = torch.zeros((G, B), dtype=torch.float32, device=d)
+    tg = torch.zeros_like(vn)
+    us = timed(lambda: ctx.tr.forward_values(nxt, B, vn, rewards=rew, dones=don, gamma=0.99, out_target=tg))
+    fl = 2.0 * B * G * (S * H + H * H + H)
+    out["forward_values_target"] = {"us": us, "flops": fl, "achieved": fl / (us * 1e-6) / 1e12, "unit": "TFLOP/s",
+                                    "peak": PEAK_BF16_TFLOPS, "frac": fl / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS}
+    P = w.n_params
+    us = timed(lambda: ctx.tr.target_ema_update(0.005))
+    by = 12.0 * G * P
+    out["target_ema"] = {"us": us, "bytes": by, "achieved": by / (us * 1e-6) / 1e9, "unit": "GB/s",
+                         "peak": PEAK_HBM_GBS, "frac": by / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    bufs = [ctx.Q, ctx.q, ctx.out_v, ctx.pi, ctx.her_next, ctx.her_rew]
+    if w.budget:
+        bufs += [ctx.theta, ctx.theta_m, ctx.theta_v]
+    flags = torch.zeros(len(bufs), dtype=torch.int32, device=d)
+    us = timed(lambda: m.nonfinite_check(bufs, flags))
+    by = 4.0 * sum(b.numel() for b in bufs)
+    out["nonfinite_check"] = {"us": us, "bytes": by, "slots": len(bufs), "achieved": by / (us * 1e-6) / 1e9,
+                              "unit": "GB/s", "peak": PEAK_HBM_GBS, "frac": by / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    C = w.C
+    pr = torch.from_numpy(g.random(C).astype(np.float32)).to(d)
+    ws = torch.zeros((m.per_workspace_bytes(C) + 7) // 8, dtype=torch.float64, device=d)
+    idx = torch.zeros(w.n_her, dtype=torch.int32, device=d)
+    wt = torch.zeros(w.n_her, dtype=torch.float32, device=d)
+    us = timed(lambda: m.per_sample_indices(pr, w.n_her, 1, 0.4, idx, wt, ws))
+    by = 4.0 * C + 4.0 * C + 8.0 * C
+    out["per_sample_indices"] = {"us": us, "bytes": by, "replay_rows": C, "draws": w.n_her,
+                                 "achieved": by / (us * 1e-6) / 1e9, "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                                 "frac": by / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    return out
+
+
 def cpu_baseline(ctx, seconds, np):
     """The oracle as it stands, one full step at a time, on the host cores."""
     from oracle import aw, budget, her, iql
@@ -529,6 +598,8 @@ def main():
                               "frac_of_8TBs": lb[k] / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
                           for k, us in zip(names, launch_us)},
            "roofline": roofline}
+    if not a.no_next_rows:
+        out["next_rows"] = time_next_rows(ctx, torch, np)
     if (default or a.cpu_baseline) and not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(ctx, a.cpu_seconds, np)
     print(json.dumps(out), flush=True)
