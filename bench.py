@@ -246,12 +246,12 @@ def profile_commands(workload):
     wl = "" if workload is None else f" --workload {workload}"
     return (
         f"rocprofv3 --kernel-trace --stats -f csv -d OUT/trace -o step -- python3 $REPO/bench.py{wl} --steps 200 "
-        "--no-cpu-baseline",
+        "--no-cpu-baseline --no-next-rows",
         f"rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/FETCH_SIZE -o p -- python3 $REPO/bench.py{wl} --steps 5 "
-        "--warmup 1 --no-graph --no-cpu-baseline --kernel-reps 5",
+        "--warmup 1 --no-graph --no-cpu-baseline --no-next-rows --kernel-reps 5",
         "rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/copy_FETCH_SIZE -o p -- python3 $REPO/bench.py --copy-probe 256",
         f"rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/WRITE_SIZE -o p -- python3 $REPO/bench.py{wl} --steps 5 "
-        "--warmup 1 --no-graph --no-cpu-baseline --kernel-reps 5",
+        "--warmup 1 --no-graph --no-cpu-baseline --no-next-rows --kernel-reps 5",
         "rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/copy_WRITE_SIZE -o p -- python3 $REPO/bench.py --copy-probe 256",
         f"python3 $REPO/bench.py --summarize-profiles OUT{wl}",
     )
