@@ -172,6 +172,8 @@ IQLH_DEV void adam_flat_block(float* __restrict__ params, float* __restrict__ gr
                               const float* __restrict__ sq_part, int nb, int64_t n, int vec,
                               const AdamHyper& hp, float* __restrict__ out_norm, int32_t* __restrict__ flags,
                               int bx, int nbx) {
+    // no contraction: the same roundings in every kernel this is inlined into
+#pragma clang fp contract(off)
     __shared__ float red[kBT / kWave];
     const int64_t quads = (n + 3) / 4, stride = (int64_t)nbx * kBT;
     const int64_t q0 = (int64_t)bx * kBT + threadIdx.x;

@@ -77,6 +77,42 @@ IQLH_DEV void iql_reduce_block(const float* __restrict__ part, const float* __re
     }
 }
 
+// One parameter's clipped Adam update ("DQN Backward-Path NaN Audit -- SP1
+// Phase A", section on iqn_adam_kernel): gi is the clipped gradient; returns
+// false (state untouched) when gi is not finite.  Contraction is off so that
+// every kernel this is inlined into rounds the same way (the compiler could
+// otherwise fuse beta1 m + (1 - beta1) g into a multiply-add differently in
+// each), which keeps the whole-step launch and the separate entry points
+// equal bit for bit.
+IQLH_DEV bool adam_elem(float gi, float& p, float& m, float& v, float bc1, float bc2, float decay,
+                        const AdamHyper& hp) {
+#pragma clang fp contract(off)
+    if (!isfinite(gi)) return false;
+    const float mi = hp.beta1 * m + (1.f - hp.beta1) * gi;
+    const float vi = hp.beta2 * v + (1.f - hp.beta2) * gi * gi;
+    const float mh = mi / bc1, vh = vi / bc2;
+    if (hp.weight_decay != 0.f) p *= decay;
+    p -= hp.lr * mh / (sqrtf(vh) + hp.eps);
+    if (hp.clamp > 0.f) p = fminf(fmaxf(p, -hp.clamp), hp.clamp);
+    m = mi;
+    v = vi;
+    return true;
+}
+
+// Operand-typed shadows of flat parameter i of one group.
+template <typename T>
+IQLH_DEV void iql_store_shadow(int64_t i, float p, int H, int S, int SP, T* w1s, T* w2s, T* w2ts) {
+    const int64_t ow2 = (int64_t)H * S + H, ow2e = ow2 + (int64_t)H * H;
+    if (i < (int64_t)H * S) {
+        const int64_t r = i / S, cc = i - r * S;
+        w1s[r * SP + cc] = to_shadow<T>(p);
+    } else if (i >= ow2 && i < ow2e) {
+        const int64_t q = i - ow2, r = q / H, cc = q - r * H;
+        w2s[q] = to_shadow<T>(p);
+        w2ts[cc * H + r] = to_shadow<T>(p);
+    }
+}
+
 // Clip and Adam over the parameters of group g, block bx of nbx; refreshes
 // the operand-typed W1 / W2 / W2^T shadows of the updated weights and zeroes
 // grad.
@@ -86,7 +122,6 @@ IQLH_DEV void iql_adam_block(const IqlDims& d, const IqlBuffers& b, const AdamHy
     __shared__ float red[4];
     const int64_t P = d.P;
     const int H = d.H, S = d.S, SP = d.S_pad;
-    const int64_t ow2 = (int64_t)H * S + H, ow2e = ow2 + (int64_t)H * H;
     float* prm = b.params + (int64_t)g * P;
     float* gr = b.grad + (int64_t)g * P;
     float* m = b.m + (int64_t)g * P;
@@ -119,14 +154,8 @@ IQLH_DEV void iql_adam_block(const IqlDims& d, const IqlBuffers& b, const AdamHy
         const bool first = i == i0;
         const float gi = (first ? pg : gr[i]) * c;
         gr[i] = 0.f;
-        float p = first ? pp : prm[i];
-        if (isfinite(gi)) {
-            const float mi = hp.beta1 * (first ? pm : m[i]) + (1.f - hp.beta1) * gi;
-            const float vi = hp.beta2 * (first ? pv : v[i]) + (1.f - hp.beta2) * gi * gi;
-            const float mh = mi / bc1, vh = vi / bc2;
-            if (hp.weight_decay != 0.f) p *= decay;
-            p -= hp.lr * mh / (sqrtf(vh) + hp.eps);
-            if (hp.clamp > 0.f) p = fminf(fmaxf(p, -hp.clamp), hp.clamp);
+        float p = first ? pp : prm[i], mi = first ? pm : m[i], vi = first ? pv : v[i];
+        if (adam_elem(gi, p, mi, vi, bc1, bc2, decay, hp)) {
             prm[i] = p;
             m[i] = mi;
             v[i] = vi;
@@ -137,14 +166,7 @@ IQLH_DEV void iql_adam_block(const IqlDims& d, const IqlBuffers& b, const AdamHy
         // Polyak target with the step's parameters (unchanged ones when the
         // update was skipped): target += ema (p - target)
         if (hp.ema > 0.f) tg[i] = fmaf(hp.ema, p - tg[i], tg[i]);
-        if (i < (int64_t)H * S) {
-            const int64_t r = i / S, cc = i - r * S;
-            w1s[r * SP + cc] = to_shadow<T>(p);
-        } else if (i >= ow2 && i < ow2e) {
-            const int64_t q = i - ow2, r = q / H, cc = q - r * H;
-            w2s[q] = to_shadow<T>(p);
-            w2ts[cc * H + r] = to_shadow<T>(p);
-        }
+        iql_store_shadow<T>(i, p, H, S, SP, w1s, w2s, w2ts);
     }
     if (bad) set_flag(b.flags, 0x1);
     if (bad_state) set_flag(b.flags, 0x8);
