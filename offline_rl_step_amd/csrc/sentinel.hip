@@ -15,6 +15,9 @@
 
 namespace iqlh {
 
+// All eight exponent bits set: an infinity or a NaN.
+IQLH_DEV bool nonfinite_bits(float x) { return (__float_as_uint(x) | 0x807FFFFFu) == 0xFFFFFFFFu; }
+
 __global__ __launch_bounds__(256) void nonfinite_sentinel_kernel(SentinelArgs a) {
     const int bx = blockIdx.x;
     int s = 0;
@@ -30,19 +33,16 @@ __global__ __launch_bounds__(256) void nonfinite_sentinel_kernel(SentinelArgs a)
             const int64_t e = base + 4 * (threadIdx.x + 256 * k);
             if (e + 4 <= n) {
                 const float4 x = p4[threadIdx.x + 256 * k];
-                bad |= ((__float_as_uint(x.x) | 0x807FFFFFu) == 0xFFFFFFFFu) |
-                       ((__float_as_uint(x.y) | 0x807FFFFFu) == 0xFFFFFFFFu) |
-                       ((__float_as_uint(x.z) | 0x807FFFFFu) == 0xFFFFFFFFu) |
-                       ((__float_as_uint(x.w) | 0x807FFFFFu) == 0xFFFFFFFFu);
+                bad |= nonfinite_bits(x.x) || nonfinite_bits(x.y) || nonfinite_bits(x.z) || nonfinite_bits(x.w);
             } else {
-                for (int64_t j = e; j < n && j < e + 4; ++j) bad |= (__float_as_uint(p[j]) | 0x807FFFFFu) == 0xFFFFFFFFu;
+                for (int64_t j = e; j < n && j < e + 4; ++j) bad |= nonfinite_bits(p[j]);
             }
         }
     } else {
 #pragma unroll 4
         for (int k = 0; k < kSentinelPiece / 256; ++k) {
             const int64_t e = base + threadIdx.x + 256 * k;
-            if (e < n) bad |= (__float_as_uint(p[e]) | 0x807FFFFFu) == 0xFFFFFFFFu;
+            if (e < n) bad |= nonfinite_bits(p[e]);
         }
     }
     if (__syncthreads_or(bad) && threadIdx.x == 0) a.flags[s] = 1;

@@ -129,3 +129,24 @@ def test_her_bad_index_flag(m):
     assert np.array_equal(don[ok], ref["donor_idx"][ok])
     assert np.array_equal(host(got["rewards"])[ok], ref["rewards"][ok])
     assert np.array_equal(host(got["states"])[ok], ref["states"][ok])
+
+
+@pytest.mark.parametrize("S,G", [(96, 40), (80, 72), (20, 0), (12, 12)])
+@pytest.mark.parametrize("strategy", ["final", "future"])
+def test_her_goal_widths_ragged(m, S, G, strategy):
+    """Goals wider than the 16 entries loaded with the episode probe, wider
+    than the 64 staged per row, empty, and rows narrower than 16 entries; the
+    episodes are ragged, so many guessed donors miss and are reloaded."""
+    g = np.random.default_rng(S * 100 + G)
+    lens = g.integers(1, 30, size=200)
+    ends = np.cumsum(lens).astype(np.int32)
+    C = int(ends[-1])
+    buf = dict(states=g.standard_normal((C, S), dtype=np.float32),
+               next_states=g.standard_normal((C, S), dtype=np.float32),
+               actions=g.integers(0, 9, C, dtype=np.int32), dones=np.zeros(C, np.float32),
+               episode_ends=ends, buffer_size=C)
+    buf["dones"][ends - 1] = 1.0
+    src = g.integers(0, C, 700).astype(np.int32)
+    ref = her.her_step(buf, src, G, STRATS[strategy], seed=7, step=2, out_bf16=False)
+    got = _run(m, buf, src, G, STRATS[strategy], 7, 2, False)
+    _compare(got, ref, False)
