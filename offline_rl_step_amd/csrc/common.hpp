@@ -89,6 +89,19 @@ IQLH_DEV float block_sum(float v, float* red) {
 // c ? x : 0 by bit masking.  The loaded x is consumed on every path, which
 // keeps the compiler from sinking its load into a lane-dependent branch (a
 // branch whose end then waits for every load the wave has in flight).
+// Workgroup barrier for data exchanged through LDS only: waits for this
+// wave's LDS operations (lgkmcnt 0), not for its global stores, which
+// __syncthreads' release fence would drain first (about a microsecond after
+// a burst of stores).  For kernels whose waves never read each other's global
+// writes.  The empty asm statements keep the compiler from moving memory
+// accesses across it.
+IQLH_DEV void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 IQLH_DEV float keep_if(bool c, float x) { return __uint_as_float(__float_as_uint(x) & (c ? 0xFFFFFFFFu : 0u)); }
 IQLH_DEV uint32_t keep_if(bool c, uint32_t x) { return x & (c ? 0xFFFFFFFFu : 0u); }
 

@@ -572,6 +572,29 @@ IQLH_DEV float row_sum16(float x) {
     return x;
 }
 
+// Sums over the 16 lanes of each row for sixteen values at once by recursive
+// halving: afterwards lane l16 of every row holds the sum of value l16.  The
+// partners l ^ 8, l ^ 4, l ^ 2, l ^ 1 are reached with the DPP row rotation
+// by 8, the half-row mirror followed by the quad reversal, and two quad
+// permutations; 19 DPP operations instead of 64 for sixteen row_sum16 calls.
+template <int CTRL>
+IQLH_DEV float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+IQLH_DEV float row_sum16_scatter(const float (&v)[16]) {
+    const int l16 = threadIdx.x & 15;
+    const bool b3 = (l16 & 8) != 0, b2 = (l16 & 4) != 0, b1 = (l16 & 2) != 0, b0 = (l16 & 1) != 0;
+    float a[8], c[4], d[2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = (b3 ? v[i + 8] : v[i]) + dpp_f<0x128>(b3 ? v[i] : v[i + 8]);  // row_ror:8
+#pragma unroll
+    for (int i = 0; i < 4; ++i)  // row_half_mirror, then quad_perm [3,2,1,0]
+        c[i] = (b2 ? a[i + 4] : a[i]) + dpp_f<0x1B>(dpp_f<0x141>(b2 ? a[i] : a[i + 4]));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) d[i] = (b1 ? c[i + 2] : c[i]) + dpp_f<0x4E>(b1 ? c[i] : c[i + 2]);  // quad_perm [2,3,0,1]
+    return (b0 ? d[1] : d[0]) + dpp_f<0xB1>(b0 ? d[0] : d[1]);  // quad_perm [1,0,3,2]
+}
+
 // ---- activation tiles of the 16x16 kernel: natural [sample][feature]
 // layout, rows of kNatLd elements, the 16-byte unit u of row s stored at
 // unit u ^ bit2(s) ^ 8 bit3(s).  A lane writes its 4 consecutive features of
@@ -622,10 +645,19 @@ IQLH_DEV NatLane nat_lane() {
     }
     return L;
 }
-IQLH_DEV bf16x8 frag_nat(const uint16_t* tile, const NatLane& L, int c, int u) {
+// The two bases of column tile c, chosen with selects: an index computed at
+// run time into NatLane would put the struct in scratch memory.
+struct NatBase {
+    int b0, b1;
+};
+IQLH_DEV NatBase nat_base(const NatLane& L, int c) {
+    const bool hi = c >= 4;
+    return NatBase{hi ? L.base[0][1] : L.base[0][0], hi ? L.base[1][1] : L.base[1][0]};
+}
+IQLH_DEV bf16x8 frag_nat(const uint16_t* tile, const NatBase& nb, int c, int u) {
     const int off = 32 * u * kNatLd + 16 * c;
-    const u32x2 lo = ld_tr4(tile + L.base[0][c >> 2] + off);
-    const u32x2 hi = ld_tr4(tile + L.base[1][c >> 2] + off);
+    const u32x2 lo = ld_tr4(tile + nb.b0 + off);
+    const u32x2 hi = ld_tr4(tile + nb.b1 + off);
     return __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
 }
 
@@ -648,14 +680,18 @@ IQLH_DEV void nat_gemm16_part(const uint16_t* A, const uint16_t* Bm, int rt, int
     const int lane = threadIdx.x & 63, l16 = lane & 15, q = lane >> 4;
     const bf16x8 one = Op<uint16_t>::ones();
     const NatLane L = nat_lane();
+    // column tiles c0 .. c0 + NCW - 1 share one half of the swizzle (c0 is a
+    // multiple of NCW, NCW divides 4)
+    static_assert(4 % NCW == 0, "column tiles within one swizzle half");
+    const NatBase na = nat_base(L, rt), nbb = nat_base(L, c0);
     f32x4v acc[NCW], accb = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NCW; ++c) acc[c] = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const bf16x8 fa = frag_nat(A, L, rt, u);
+        const bf16x8 fa = frag_nat(A, na, rt, u);
 #pragma unroll
-        for (int c = 0; c < NCW; ++c) acc[c] = mma16(fa, frag_nat(Bm, L, c0 + c, u), acc[c]);
+        for (int c = 0; c < NCW; ++c) acc[c] = mma16(fa, frag_nat(Bm, nbb, c0 + c, u), acc[c]);
         if (bias_dst) accb = mma16(fa, one, accb);
     }
     float* d0 = dst + (16 * rt + 4 * q) * ldo;
@@ -787,7 +823,7 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
         sb2[tid] = vb2;
         sw3[tid] = vw3;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- F1: z1^T = W1 s^T + b1 for this wave's 64 features
     f32x4v acc[FT];
@@ -811,7 +847,7 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
         }
         put4(R3, bl, fb + 16 * t + 4 * q, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);  // h1
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- F2: z2^T = W2 h1^T + b2, V = w3 . relu(z2) + b3 over both halves
 #pragma unroll
@@ -833,7 +869,7 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
         for (int r = 0; r < 4; ++r) vpart = fmaf(w3v[t][r], acc[t][r] > 0.f ? acc[t][r] : 0.f, vpart);
     vpart = sum_q4(vpart);
     if (q == 0) svh[fh * BT + bl] = vpart;
-    __syncthreads();
+    lds_barrier();
     const float v = (svh[bl] + svh[BT + bl]) + b3;
     if (a.fwd_only) {
         if (valid && fh == 0 && q == 0) write_value(a.vo, g, B, b, v);
@@ -847,9 +883,10 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
         dv = -2.f * w * diff * a.invB;
         if (fh == 0 && q == 0 && a.out_v) a.out_v[(int64_t)g * B + b] = v;
     }
-    // the two waves of a sample group split the epilogue: half 0 the loss
-    // sums, half 1 the policy
-    if (fh == 0) {
+    // the two waves of a sample group split the epilogue, one the loss sums
+    // and one the (heavier) policy, alternating with the sample group so that
+    // every SIMD runs two of each (waves go to SIMDs round-robin)
+    if (fh != ((sg >> 1) & 1)) {
         const float ls = row_sum16(lterm);
         const float ds = row_sum16(dv);
         if (lane == 0) { sred[sg] = ls; sred[NW / 2 + sg] = ds; }
@@ -875,26 +912,29 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
             se = sum_q4(se);
             if (valid) {
                 float* pr = a.out_pi + ((int64_t)g * B + b) * a.A;
+                const float inv = 1.f / se;  // one division, then products
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
-                    if (q + 4 * k < a.A) pr[q + 4 * k] = x[k] / se;
+                    if (q + 4 * k < a.A) pr[q + 4 * k] = x[k] * inv;
             }
         }
     }
     // dz2 = dv w3 relu'(z2) -> R0 (W1 is dead); dw3 over this sample group
+    static_assert(FT == 4, "sixteen values per lane for the dw3 sums");
+    float hv[16];  // h2 dv of this lane's sample, features fb + 16 t + 4 q + r at 4 t + r
 #pragma unroll
     for (int t = 0; t < FT; ++t) {
-        float hd[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float z = acc[t][r];
-            hd[r] = row_sum16(z > 0.f ? z * dv : 0.f);
+            hv[4 * t + r] = z > 0.f ? z * dv : 0.f;
             acc[t][r] = z > 0.f ? dv * w3v[t][r] : 0.f;
         }
         put4(R0, bl, fb + 16 * t + 4 * q, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
-        if (l16 == 0) *(f32x4v*)(sdw3 + sg * H + fb + 16 * t + 4 * q) = f32x4v{hd[0], hd[1], hd[2], hd[3]};
     }
-    __syncthreads();
+    // lane l16 ends with the sample-group sum of value l16
+    sdw3[sg * H + fb + 16 * (l16 >> 2) + 4 * q + (l16 & 3)] = row_sum16_scatter(hv);
+    lds_barrier();
 
     // ---- W2^T to R1 (W2 is dead); loss, db3, dw3; dW2 = dz2^T h1 with db2
     {
@@ -920,7 +960,7 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
             *(u32x4*)(R1 + r * C::LDW2 + c) = w2t[k];
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- B1: dh1^T = W2^T dz2^T for this wave's features; dz1 -> R3 (h1 is dead)
 #pragma unroll
@@ -939,7 +979,7 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
         for (int r = 0; r < 4; ++r) d[r] = (mask1 >> (4 * t + r)) & 1u ? acc[t][r] : 0.f;
         put4(R3, bl, fb + 16 * t + 4 * q, d[0], d[1], d[2], d[3]);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- dW1 = dz1^T s with db1
     nat_gemm16_part<SP / 32>(R3, R2, sg, (SP / 32) * fh, part + po.w1, S, S, fh == 0 ? part + po.b1 : nullptr);
