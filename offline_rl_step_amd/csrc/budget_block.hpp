@@ -71,15 +71,14 @@ IQLH_DEV void fold_partials_k(const float* __restrict__ p, int nb, int k, float 
     block_sum_k(out, k, red);
 }
 
-// Pass 1 for block bx of nb: partial sums of squares of every source.
-IQLH_DEV void norms_block(const SourceSet& s, int64_t n, int vec, float* __restrict__ partials, int bx,
-                         int nb) {
-    __shared__ float red[kMaxSources][kBT / kWave];
-    float acc[kMaxSources];
+// Thread t's share of block bx of nb of pass 1: the sums of squares of its
+// quads of every source (the block then adds its threads with block_sum_k).
+IQLH_DEV void norms_thread(const SourceSet& s, int64_t n, int vec, int bx, int nb, int t,
+                           float (&acc)[kMaxSources]) {
 #pragma unroll
     for (int j = 0; j < kMaxSources; ++j) acc[j] = 0.f;
     const int64_t quads = (n + 3) / 4, stride = (int64_t)nb * kBT;
-    for (int64_t qd = (int64_t)bx * kBT + threadIdx.x; qd < quads; qd += stride) {
+    for (int64_t qd = (int64_t)bx * kBT + t; qd < quads; qd += stride) {
 #pragma unroll
         for (int j = 0; j < kMaxSources; ++j) {
             if (j < s.k) {
@@ -88,6 +87,14 @@ IQLH_DEV void norms_block(const SourceSet& s, int64_t n, int vec, float* __restr
             }
         }
     }
+}
+
+// Pass 1 for block bx of nb: partial sums of squares of every source.
+IQLH_DEV void norms_block(const SourceSet& s, int64_t n, int vec, float* __restrict__ partials, int bx,
+                         int nb) {
+    __shared__ float red[kMaxSources][kBT / kWave];
+    float acc[kMaxSources];
+    norms_thread(s, n, vec, bx, nb, threadIdx.x, acc);
     block_sum_k(acc, s.k, red);
     if (threadIdx.x == 0) {
 #pragma unroll

@@ -86,9 +86,6 @@ IQLH_DEV float block_sum(float v, float* red) {
     return s;
 }
 
-// c ? x : 0 by bit masking.  The loaded x is consumed on every path, which
-// keeps the compiler from sinking its load into a lane-dependent branch (a
-// branch whose end then waits for every load the wave has in flight).
 // Workgroup barrier for data exchanged through LDS only: waits for this
 // wave's LDS operations (lgkmcnt 0), not for its global stores, which
 // __syncthreads' release fence would drain first (about a microsecond after
@@ -102,6 +99,9 @@ IQLH_DEV void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// c ? x : 0 by bit masking.  The loaded x is consumed on every path, which
+// keeps the compiler from sinking its load into a lane-dependent branch (a
+// branch whose end then waits for every load the wave has in flight).
 IQLH_DEV float keep_if(bool c, float x) { return __uint_as_float(__float_as_uint(x) & (c ? 0xFFFFFFFFu : 0u)); }
 IQLH_DEV uint32_t keep_if(bool c, uint32_t x) { return x & (c ? 0xFFFFFFFFu : 0u); }
 

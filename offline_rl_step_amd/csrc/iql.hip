@@ -32,7 +32,9 @@
 //     dw3 are row sums of the same tiles through an all-ones operand.
 #include <hip/hip_ext.h>
 
+#include "budget_block.hpp"
 #include "common.hpp"
+#include "her_block.hpp"
 #include "iql_update.hpp"
 #include "launch.hpp"
 
@@ -178,6 +180,14 @@ struct FusedArgs {
     int32_t* flags;
     int fwd_only;         // 1: V (and the bootstrap target) only, no loss or gradients
     ValueOut vo;          // outputs of the forward-only pass
+    // 16-wave kernel only: HER rows relabelled in the prologue (her_on) -- the
+    // batch rows from her_row0 (a multiple of 128) on are HER rows
+    // 0 .. B - her_row0 - 1, built from the replay buffer rather than read from
+    // `states`, and group 0 writes every HER output; the budget's pass 1
+    // (nrm.nb > 0) rides on the 256-thread quarters of the other workgroups.
+    int her_on, her_row0;
+    HerArgs her;
+    NormsArgs nrm;
 };
 
 template <typename T, int SP, int H, int NW>
@@ -723,10 +733,11 @@ struct Fused16wCfg {
     static constexpr int R1 = H * LDW2;
     static constexpr int R2 = NAT;
     static constexpr int R3 = NAT;
-    static constexpr int NF = 3 * H + 2 * BT + 2 * NW + (NW / 2) * H;
+    static constexpr int NF = 3 * H + 2 * BT + 2 * NW + (NW / 2) * H + 4 * kMaxSources * 4;
     static constexpr size_t BYTES = (size_t)(R0 + R1 + R2 + R3) * 2 + (size_t)NF * sizeof(float);
     static_assert(BYTES <= 160 * 1024, "LDS budget");
     static_assert(SP <= kNatLd - 16 && H <= kNatLd - 16, "natural tile width");
+    static_assert(R3 * 2 >= BT * kHerGoalLds * 4 + BT * 4, "HER goals staged in R3");
 };
 
 template <int SP, int H, bool XVEC>
@@ -770,39 +781,194 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
     constexpr int X_PER_THREAD = BT * SP / (NTHR * 8);
     static_assert(W1_PER_THREAD * NTHR * 8 == H * SP && W2_PER_THREAD * NTHR * 8 == H * H &&
                   X_PER_THREAD * NTHR * 8 == BT * SP, "staging split");
+    const int nrow = min(BT, B - wg * BT);  // batch rows of this tile
+    // a tile of HER rows (uniform): their sources are loaded first, since the
+    // relabelling below waits on them -- one lead row per thread of waves 0-1,
+    // and the row of each of this thread's chunks
+    const bool her_wg = a.her_on && wg * BT >= a.her_row0;
+    const HerArgs& h = a.her;
+    const int64_t hrow0 = (int64_t)wg * BT - a.her_row0;  // HER index of tile row 0
     u32x4 w1r[W1_PER_THREAD], w2r[W2_PER_THREAD], xr[X_PER_THREAD];
+    float vb1, vb2, vw3, qb, b3, qa[4];
+    // weights, biases, w3, q and Q (one copy of these loads in each branch
+    // below, so that each branch issues its loads in the order it waits on them)
+    auto load_weights = [&]() {
 #pragma unroll
-    for (int k = 0; k < W1_PER_THREAD; ++k) w1r[k] = *(const u32x4*)(w1s + (tid + k * NTHR) * 8);
+        for (int k = 0; k < W1_PER_THREAD; ++k) w1r[k] = *(const u32x4*)(w1s + (tid + k * NTHR) * 8);
 #pragma unroll
-    for (int k = 0; k < W2_PER_THREAD; ++k) w2r[k] = *(const u32x4*)(w2s + (tid + k * NTHR) * 8);
+        for (int k = 0; k < W2_PER_THREAD; ++k) w2r[k] = *(const u32x4*)(w2s + (tid + k * NTHR) * 8);
+        const int th = tid < H ? tid : 0;
+        vb1 = prm[po.b1 + th];
+        vb2 = prm[po.b2 + th];
+        vw3 = prm[po.w3 + th];
+        qb = a.fwd_only ? 0.f : a.q[bc];  // used by valid lanes only
+        b3 = prm[po.b3];
 #pragma unroll
-    for (int k = 0; k < X_PER_THREAD; ++k) {
-        const int c = tid + k * NTHR, sr = c / (SP / 8), k0 = 8 * (c - sr * (SP / 8));
-        const int row = wg * BT + sr;
-        const bool ok = row < B;
-        const uint16_t* src = (const uint16_t*)a.states + (int64_t)(ok ? row : B - 1) * a.ld;
-        u32x4 x;
-        if (XVEC) {
-            x = *(const u32x4*)(src + k0);
-        } else {
-            uint16_t t8[8];
+        for (int k = 0; k < 4; ++k) qa[k] = a.out_pi ? a.q_all[(int64_t)bc * a.A + min(q + 4 * k, a.A - 1)] : 0.f;
+    };
+    if (her_wg) {
+        // a tile of HER rows: the sources first, since the relabelling waits
+        // on them -- one lead row per thread of waves 0-1, and the row of each
+        // of this thread's chunks -- then the weights
+        const int64_t hsrc = h.source_idx[hrow0 + min(tid, nrow - 1)];
+        int64_t hsrck[X_PER_THREAD];
+#pragma unroll
+        for (int k = 0; k < X_PER_THREAD; ++k) {
+            const int c = tid + k * NTHR, sr = c / (SP / 8);
+            hsrck[k] = h.source_idx[hrow0 + min(sr, nrow - 1)];
+        }
+        load_weights();
+        // HER relabelling of the tile's rows, the steps and arithmetic of
+        // her_block ("GPU IQL + HER Porting Plan", Phase 2): the draw while the
+        // sources are in flight; the lead row's episode probe, action and
+        // done with the chunks' entries of s and s'; donor, goal, distance and
+        // reward; the goals exchanged through LDS (R3 is free until F1); the
+        // chunks with their goal entries replaced, rounded to bfloat16 for the
+        // tile.  Group 0 writes the HER outputs, group 1 only uses the rows.
+        const int S_ = h.S, G = h.G;
+        const bool wout = g == 0;
+        const bool hlead = tid < nrow;
+        const uint64_t hr = hlead ? her_draw(h, hrow0 + tid, her_step_word(h)) : 0ull;
+        bool hok = hlead && hsrc >= 0 && hsrc < h.buffer_size;
+        const EpisodeProbe probe = her_probe(h, hlead ? hsrc : 0);
+        const int64_t hsc = hok ? hsrc : 0;
+        // action and done through pointer selects: no branch around a load
+        // (the join of one would drain every load in flight)
+        const bool wact = wout && h.out_actions, wdone = wout && h.out_dones;  // uniform
+        const int32_t hact0 = *(wact ? h.actions + hsc : h.source_idx);
+        const float hdone0 = *(wdone ? h.dones + hsc : (const float*)h.source_idx);
+        // the chunks' entries of s and s' (group 1 reloads s, which it does not
+        // output, instead of s'); rows are whole 8-float chunks, 16-byte
+        // aligned (iql_fused_her_ok), and a chunk past the row end loads the
+        // row's last chunk and is masked
+        const bool wnext = wout && h.out_next_states != nullptr;
+        float xs[X_PER_THREAD][8], xn[X_PER_THREAD][8];
+#pragma unroll
+        for (int k = 0; k < X_PER_THREAD; ++k) {
+            const int c = tid + k * NTHR, sr = c / (SP / 8), k0 = 8 * (c - sr * (SP / 8));
+            const bool use = sr < nrow && hsrck[k] >= 0 && hsrck[k] < h.buffer_size;
+            const int64_t sk = use ? hsrck[k] : 0;
+            const int kc = min(k0, S_ - 8);
+            const float* srow = h.states + sk * S_ + kc;
+            const float* nrw = (wnext ? h.next_states : h.states) + sk * S_ + kc;
+            const float4 x0 = *(const float4*)srow, x1 = *(const float4*)(srow + 4);
+            const float4 y0 = *(const float4*)nrw, y1 = *(const float4*)(nrw + 4);
+            const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const uint16_t v = src[min(k0 + e, S - 1)];
-                t8[e] = (uint16_t)keep_if(k0 + e < S, (uint32_t)v);
+                xs[k][e] = keep_if(use && k0 + e < S_, xv[e]);
+                xn[k][e] = keep_if(wnext && use && k0 + e < S_, yv[e]);
             }
-            x = u32x4{(uint32_t)t8[0] | ((uint32_t)t8[1] << 16), (uint32_t)t8[2] | ((uint32_t)t8[3] << 16),
-                      (uint32_t)t8[4] | ((uint32_t)t8[5] << 16), (uint32_t)t8[6] | ((uint32_t)t8[7] << 16)};
         }
-        xr[k] = u32x4{keep_if(ok, x.x), keep_if(ok, x.y), keep_if(ok, x.z), keep_if(ok, x.w)};
-    }
-    const int th = tid < H ? tid : 0;
-    const float vb1 = prm[po.b1 + th], vb2 = prm[po.b2 + th], vw3 = prm[po.w3 + th];
-    const float qb = a.fwd_only ? 0.f : a.q[bc];  // used by valid lanes only
-    const float b3 = prm[po.b3];
-    float qa[4];
+        float* s_goal = (float*)R3;                              // [BT][kHerGoalLds]
+        int* s_hdon = (int*)(s_goal + BT * kHerGoalLds);         // [BT], -1: a zeroed row
+        if (hlead) {
+            const int64_t hi = hrow0 + tid;
+            int64_t donor = -1;
+            if (hok) hok = her_donor(h, hsrc, hr, probe, donor);
+            if (hok) {
+                const float* ns = h.next_states + hsrc * S_;
+                const float* nd = h.next_states + donor * S_;
+                float gd[16];
+                const float dist = her_distance(ns, nd, G, gd);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) qa[k] = a.out_pi ? a.q_all[(int64_t)bc * a.A + min(q + 4 * k, a.A - 1)] : 0.f;
+                for (int d = 0; d < 16; ++d)
+                    if (d < G) s_goal[tid * kHerGoalLds + d] = gd[d];
+                for (int d = 16; d < G && d < kHerGoalLds; ++d) s_goal[tid * kHerGoalLds + d] = nd[d];
+                if (wout) {
+                    h.out_rewards[hi] = dist < h.threshold ? h.reward_hit : h.reward_miss;
+                    if (h.donor_out) h.donor_out[hi] = (int32_t)donor;
+                    if (h.out_actions) h.out_actions[hi] = hact0;
+                    if (h.out_dones) h.out_dones[hi] = hdone0;
+                }
+            } else {
+                donor = -1;
+                if (wout) {
+                    h.out_rewards[hi] = 0.f;
+                    if (h.donor_out) h.donor_out[hi] = -1;
+                    if (h.out_actions) h.out_actions[hi] = 0;
+                    if (h.out_dones) h.out_dones[hi] = 0.f;
+                    set_flag(h.flags, 0x2);
+                }
+            }
+            s_hdon[tid] = (int)donor;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int k = 0; k < X_PER_THREAD; ++k) {
+            const int c = tid + k * NTHR, sr = c / (SP / 8), k0 = 8 * (c - sr * (SP / 8));
+            // branch-free: the row's donor and the 8 staged goal entries at
+            // k0 (clamped; G <= kHerGoalLds, iql_fused_her_ok) are read
+            // whatever the chunk, then selected per entry
+            const int src_r = min(sr, nrow - 1);
+            const bool zero = sr >= nrow || s_hdon[src_r] < 0;
+            const float* gp = s_goal + src_r * kHerGoalLds + min(k0, kHerGoalLds - 8);
+            const float4 g0 = *(const float4*)gp, g1 = *(const float4*)(gp + 4);
+            const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+            float x[8], y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const bool goal = k0 + e < G;
+                x[e] = zero ? 0.f : (goal ? gv[e] : xs[k][e]);
+                y[e] = zero ? 0.f : (goal ? gv[e] : xn[k][e]);
+            }
+            xr[k] = u32x4{(uint32_t)f2bf(x[0]) | ((uint32_t)f2bf(x[1]) << 16),
+                          (uint32_t)f2bf(x[2]) | ((uint32_t)f2bf(x[3]) << 16),
+                          (uint32_t)f2bf(x[4]) | ((uint32_t)f2bf(x[5]) << 16),
+                          (uint32_t)f2bf(x[6]) | ((uint32_t)f2bf(x[7]) << 16)};
+            if (wout && sr < nrow && k0 < S_) {  // whole chunks: S is a multiple of 8
+                const int64_t hi = hrow0 + sr;
+                *(u32x4*)((uint16_t*)h.out_states + hi * a.ld + k0) = xr[k];
+                if (wnext) {
+                    float* no = h.out_next_states + hi * S_ + k0;
+                    *(float4*)no = float4{y[0], y[1], y[2], y[3]};
+                    *(float4*)(no + 4) = float4{y[4], y[5], y[6], y[7]};
+                }
+            }
+        }
+    } else {
+        load_weights();
+#pragma unroll
+        for (int k = 0; k < X_PER_THREAD; ++k) {
+            const int c = tid + k * NTHR, sr = c / (SP / 8), k0 = 8 * (c - sr * (SP / 8));
+            const int row = wg * BT + sr;
+            const bool ok = row < B;
+            const uint16_t* src = (const uint16_t*)a.states + (int64_t)(ok ? row : B - 1) * a.ld;
+            u32x4 x;
+            if (XVEC) {
+                x = *(const u32x4*)(src + k0);
+            } else {
+                uint16_t t8[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint16_t v = src[min(k0 + e, S - 1)];
+                    t8[e] = (uint16_t)keep_if(k0 + e < S, (uint32_t)v);
+                }
+                x = u32x4{(uint32_t)t8[0] | ((uint32_t)t8[1] << 16), (uint32_t)t8[2] | ((uint32_t)t8[3] << 16),
+                          (uint32_t)t8[4] | ((uint32_t)t8[5] << 16), (uint32_t)t8[6] | ((uint32_t)t8[7] << 16)};
+            }
+            xr[k] = u32x4{keep_if(ok, x.x), keep_if(ok, x.y), keep_if(ok, x.z), keep_if(ok, x.w)};
+        }
+    }
+    // the budget's pass 1 on the workgroups that hold no HER rows: quarter
+    // wv / 4 (256 threads) of host workgroup hidx runs block
+    // quarter * hosts + hidx with the arithmetic of norms_block
+    const int nhost_wg = a.her_on ? a.her_row0 / BT : a.nwg;
+    const int hosts = (int)gridDim.y * nhost_wg;
+    const int nblk = (!her_wg && a.nrm.nb > 0) ? (wv >> 2) * hosts + g * nhost_wg + wg : a.nrm.nb;
+    float* snrm = sdw3 + (NW / 2) * H;  // [4 quarters][kMaxSources][4 waves]
+    if (nblk < a.nrm.nb) {  // uniform per wave
+        float acc[kMaxSources];
+        norms_thread(a.nrm.s, a.nrm.n, a.nrm.vec, nblk, a.nrm.nb, tid & 255, acc);
+#pragma unroll
+        for (int j = 0; j < kMaxSources; ++j) {
+            if (j < a.nrm.s.k) {
+                const float w = wave_sum(acc[j]);
+                if (lane == 0) snrm[((wv >> 2) * kMaxSources + j) * 4 + (wv & 3)] = w;
+            }
+        }
+    }
 #pragma unroll
     for (int k = 0; k < W1_PER_THREAD; ++k) {
         const int idx = (tid + k * NTHR) * 8, r = idx / SP, c = idx - r * SP;
@@ -824,6 +990,18 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
         sw3[tid] = vw3;
     }
     lds_barrier();
+    // the quarter's budget partials: its four wave sums added in block_sum_k's order
+    if (nblk < a.nrm.nb && (tid & 255) == 0) {
+#pragma unroll
+        for (int j = 0; j < kMaxSources; ++j) {
+            if (j < a.nrm.s.k) {
+                float t = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) t += snrm[((wv >> 2) * kMaxSources + j) * 4 + i];
+                a.nrm.partials[(int64_t)j * a.nrm.nb + nblk] = t;
+            }
+        }
+    }
 
     // ---- F1: z1^T = W1 s^T + b1 for this wave's 64 features
     f32x4v acc[FT];
@@ -1077,10 +1255,33 @@ bool iql_fused_policy(const IqlDims& d, int A) {
     return !d.layered && d.dtype == 1 && d.H == 128 && A >= 1 && A <= 16;
 }
 
+// The shapes that run iql_fused16w_kernel (bf16, hidden 128, state <= 128).
+static bool is_fused16w(const IqlDims& d) { return !d.layered && d.dtype == 1 && d.H == 128 && d.S <= 128; }
+
+// HER rows the forward/backward launch can relabel itself: the batch tail
+// from a 128-row boundary, bf16, rows of whole 16-byte-aligned 8-float chunks,
+// goals of at most kHerGoalLds entries.
+bool iql_fused_her_ok(const IqlDims& d, const HerArgs& her, const void* states, int64_t ld, int B) {
+    if (!is_fused16w(d) || her.n <= 0 || her.n > B || her.S != d.S || !her.out_bf16 || her.out_ld != ld) return false;
+    if (her.S % 8 != 0 || ld % 8 != 0 || her.G > kHerGoalLds) return false;
+    const uintptr_t al = (uintptr_t)her.states | (uintptr_t)her.next_states | (uintptr_t)her.out_states |
+                         (uintptr_t)her.out_next_states;
+    if (al & 15u) return false;
+    const int row0 = B - her.n;
+    return row0 % 128 == 0 && (const char*)her.out_states == (const char*)states + (int64_t)row0 * ld * 2;
+}
+
+bool iql_fused_norms_ok(const IqlDims& d, int B, int her_rows, int nb) {
+    if (!is_fused16w(d) || nb <= 0) return false;
+    const int hosts = d.G * (her_rows > 0 ? (B - her_rows) / 128 : (B + 127) / 128);
+    return nb <= 4 * hosts;
+}
+
 hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float* tau,
                               const void* states, int64_t ld, const float* q, int B, float* out_v,
                               hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1,
-                              const float* q_all, int A, float beta, float* out_pi) {
+                              const float* q_all, int A, float beta, float* out_pi, const HerArgs* her,
+                              const NormsArgs* nrm) {
     if (d.layered) {
         if (ev0) (void)hipEventRecord(ev0, stream);
         hipError_t e = d.big ? launch_iql_big_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream)
@@ -1098,6 +1299,16 @@ hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float
     fa.q_all = q_all; fa.out_pi = out_pi; fa.A = A; fa.beta = beta;
     fa.tau0 = tau[0]; fa.tau1 = tau[d.G > 1 ? 1 : 0]; fa.invB = 1.f / (float)B;
     fa.B = B; fa.S = d.S; fa.nwg = (B + BT - 1) / BT; fa.P = d.P; fa.Pp = d.Pp; fa.flags = b.flags;
+    if (her) {
+        if (!iql_fused_her_ok(d, *her, states, ld, B)) return hipErrorInvalidValue;
+        fa.her_on = 1;
+        fa.her_row0 = B - her->n;
+        fa.her = *her;
+    }
+    if (nrm) {
+        if (!iql_fused_norms_ok(d, B, her ? her->n : 0, nrm->nb)) return hipErrorInvalidValue;
+        fa.nrm = *nrm;
+    }
     return var->fn(fa, d.G, stream, ev0, ev1);
 }
 

@@ -43,6 +43,14 @@ struct SourceSet {
     float alpha[kMaxSources];
     int32_t k;
 };
+// Pass 1 of the budgeted accumulation (per-source sums of squares, blocks
+// 0 .. nb - 1 of 256 threads) run inside another launch.
+struct NormsArgs {
+    SourceSet s;
+    int64_t n;
+    float* partials;  // [k][nb]
+    int vec, nb;
+};
 // Outputs of a forward-only pass: V and, with rewards, the bootstrap target
 // r + gamma (1 - done) V.
 struct ValueOut {
@@ -118,12 +126,19 @@ int iql_reduce_blocks(int64_t P);
 // Fused forward/backward: V(s) and the per-workgroup gradient partials.
 // With out_pi non-null and iql_fused_policy(d, A), the advantage-weighted
 // policy of every group is computed in the same launch from this V.
+// With `her` (iql_fused_her_ok), the HER rows that form the batch tail from
+// row her_row0 on are relabelled inside the launch instead of read from
+// `states` (group 0 also writes every HER output); with `nrm`
+// (iql_fused_norms_ok), the launch also runs the budget's pass 1.
 hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float* tau,
                               const void* states, int64_t ld, const float* q, int B,
                               float* out_v, hipStream_t stream, hipEvent_t ev0 = nullptr,
                               hipEvent_t ev1 = nullptr, const float* q_all = nullptr, int A = 0,
-                              float beta = 0.f, float* out_pi = nullptr);
+                              float beta = 0.f, float* out_pi = nullptr, const HerArgs* her = nullptr,
+                              const NormsArgs* nrm = nullptr);
 bool iql_fused_policy(const IqlDims& d, int A);
+bool iql_fused_her_ok(const IqlDims& d, const HerArgs& her, const void* states, int64_t ld, int B);
+bool iql_fused_norms_ok(const IqlDims& d, int B, int her_rows, int nb);
 // Fixed-order reduction of the partials of a batch of B rows, clip, Adam.
 hipError_t launch_iql_update(const IqlDims& d, const IqlBuffers& b, const AdamHyper& hp, int B,
                              float* out_loss, float* out_gnorm, hipStream_t stream);

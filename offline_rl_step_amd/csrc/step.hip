@@ -23,14 +23,7 @@
 
 namespace iqlh {
 
-struct NormsPart {
-    SourceSet s;
-    int64_t n;
-    float* partials;
-    int vec, nb;
-};
-
-__global__ __launch_bounds__(256) void step_her_norms_kernel(HerArgs her, int her_blocks, NormsPart np) {
+__global__ __launch_bounds__(256) void step_her_norms_kernel(HerArgs her, int her_blocks, NormsArgs np) {
     const int bx = blockIdx.x;
     if (bx < her_blocks) her_block(her, bx);
     else norms_block(np.s, np.n, np.vec, np.partials, bx - her_blocks, np.nb);
@@ -131,27 +124,38 @@ hipError_t launch_aux_step(const IqlDims& d, const IqlBuffers& b, const AdamHype
     }
     const bool flat_adam = bud && bud->params;
 
-    // A: HER + budget norms
-    const int her_blocks = (her && her->n > 0) ? (her->n + 31) / 32 : 0;
-    if (her_blocks + nb > 0) {
+    // HER rows that are the tail of the batch, and the budget's pass 1, move
+    // into the forward/backward launch when its kernel can host them
+    const bool her_in_b = her && her->n > 0 && iql_fused_her_ok(d, *her, states, ld, B);
+    const bool norms_in_b = bud && iql_fused_norms_ok(d, B, her_in_b ? her->n : 0, nb);
+    NormsArgs np{};
+    if (bud) np = NormsArgs{bud->s, bud->n, partials, vec, nb};
+
+    // A: HER + budget norms (what launch B does not host)
+    const int her_blocks = (her && her->n > 0 && !her_in_b) ? (her->n + 31) / 32 : 0;
+    const int nb_a = norms_in_b ? 0 : nb;
+    if (her_blocks + nb_a > 0) {
         HerArgs ha{};
         if (her_blocks) ha = *her;
-        NormsPart np{};
-        if (bud) np = NormsPart{bud->s, bud->n, partials, vec, nb};
-        STEP_LAUNCH(step_her_norms_kernel, her_blocks + nb, ev, ha, her_blocks, np);
+        NormsArgs npa{};
+        if (nb_a) npa = np;
+        STEP_LAUNCH(step_her_norms_kernel, her_blocks + nb_a, ev, ha, her_blocks, npa);
     } else if (ev) {  // nothing to launch: an empty interval keeps the timing uniform
         (void)hipEventRecord(ev[0], stream);
         (void)hipEventRecord(ev[1], stream);
     }
 
-    // B: fused forward/backward (+ policy)
+    // B: fused forward/backward (+ policy, HER rows, budget norms)
     hipError_t e;
     const bool fused_pi = q_all && iql_fused_policy(d, A);
     hipEvent_t e0 = ev ? ev[2] : nullptr, e1 = ev ? ev[3] : nullptr;
+    const HerArgs* hb = her_in_b ? her : nullptr;
+    const NormsArgs* nbp = norms_in_b ? &np : nullptr;
     if (fused_pi) {
-        e = launch_iql_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream, e0, e1, q_all, A, beta, out_pi);
+        e = launch_iql_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream, e0, e1, q_all, A, beta, out_pi, hb, nbp);
     } else {
-        e = launch_iql_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream, e0, e1);
+        e = launch_iql_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream, e0, e1, nullptr, 0, 0.f, nullptr, hb,
+                               nbp);
         if (e == hipSuccess && q_all) e = launch_aw_policy(q_all, out_v, d.G, B, A, beta, out_pi, stream);
     }
     if (e != hipSuccess) return e;

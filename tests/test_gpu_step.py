@@ -225,13 +225,16 @@ def test_whole_step_relabelled_rows_outside_the_batch(m):
     assert np.any(host(a.Xh) != 0)
 
 
-def test_whole_step_relabelling_matches_oracle(m):
+@pytest.mark.parametrize("B", [3000, 2048])
+def test_whole_step_relabelling_matches_oracle(m, B):
     """One whole step with bf16 operands against the oracle's HER pass
     (donors, rewards, the bf16 rows in the batch, s' with the new goal,
-    actions, dones), and V against the oracle's step on that batch."""
+    actions, dones), and V against the oracle's step on that batch; at
+    batch 2048 the HER rows start at a tile boundary and are relabelled by
+    the forward/backward launch."""
     from oracle import her, iql
     w = synth.shrink(synth.WORKLOADS["b16384_s128_h128_bf16_g2_budget"], C=1 << 14)
-    inp = Inputs(w, 3000, 1000)
+    inp = Inputs(w, B, 1000)
     r = Rig(m, inp)
     r.whole()
     sync()
@@ -301,24 +304,51 @@ def test_whole_step_matches_oracle(m):
     r.tr.close()
 
 
-def test_time_aux_step_reports_every_launch(m):
+@pytest.mark.parametrize("B,n_budget", [(2048, 5000), (3000, 5000), (1024, 300000)])
+def test_time_aux_step_reports_every_launch(m, B, n_budget):
     """The measurement entry point runs real steps (Adam's t advances) and
-    reports a positive kernel time for each of the four launches."""
+    reports a kernel time for each of the four launches (for the first, the
+    interval between its two events when the forward/backward launch hosts
+    both of its passes)."""
     w = synth.shrink(synth.WORKLOADS["b16384_s128_h128_bf16_g2_budget"], C=1 << 14)
-    inp = Inputs(w, 2048, 5000)
+    inp = Inputs(w, B, n_budget)
     r = Rig(m, inp)
     her = m.her_step(r.hcfg, r.hbuf, inp.t_src, inp.n, r.seed, r.hout)
     bud = m.budget_step(r.grad, inp.t_sources, w.budget_fractions, (1.0, 1.0, 1.0, 1.0), inp.n_budget,
                         w.max_grad_norm, r.norms, r.adam, r.ws)
     us = r.tr.time_aux_step(her, r.X, inp.t_q, inp.B, inp.t_Q, w.A, w.beta, r.pi, r.out_v, r.out_loss, r.out_gn,
                             bud, reps=5)
-    assert len(us) == 4 and all(np.isfinite(us)) and min(us) > 0.0, us
+    assert len(us) == 4 and all(np.isfinite(us)) and min(us[1:]) > 0.0 and us[0] >= 0.0, us
     t = r.tensors()
     sync()
     assert int(host(t["t0"])[0]) == 5 and int(host(r.tt)[0]) == 5
     rc, flags = r.tr.status()
     assert rc == m.OK and flags == 0
     r.tr.close()
+
+
+@pytest.mark.parametrize("B,n,S,G,strategy,minimal,n_budget", [
+    (2048, 1024, 128, 8, "future", False, 3001),
+    (2000, 976, 128, 8, "final", False, 3001),     # last tile of 80 rows
+    (1536, 1024, 128, 8, "random", True, 3001),    # HER rows from row 512, no optional outputs
+    (1280, 768, 104, 20, "future", False, 2048),   # state of 13 chunks (SP 128), goal past 16 entries
+    (1280, 768, 100, 20, "future", False, 2048),   # state not a multiple of 8: relabelled by its own launch
+    (1280, 640, 56, 56, "final", False, 2048),     # 64-wide operand tile, goal = whole state
+    (1408, 640, 96, 64, "future", True, 2048),     # goal of 64 entries, all staged in LDS
+    (1408, 640, 96, 70, "future", False, 2048),    # longer goal: relabelled by its own launch
+    (1024, 512, 128, 8, "future", False, 300000),  # budget norms too many to ride along
+])
+def test_whole_step_relabelling_inside_forward_backward(m, B, n, S, G, strategy, minimal, n_budget):
+    """HER rows that form the batch tail from a 128-row boundary on are
+    relabelled by the forward/backward launch itself (group 0 writes the HER
+    outputs, every group builds its tile from the replay buffer), and the
+    budget's pass 1 rides on the workgroups without HER rows: bit for bit
+    what the separate calls give, over two steps."""
+    w = synth.shrink(synth.WORKLOADS["b16384_s128_h128_bf16_g2_budget"], S=S, G=G, C=1 << 14, her_ratio=n / B)
+    inp = Inputs(w, B, n_budget)
+    assert inp.n == n
+    code = {"final": m.HER_FINAL, "future": m.HER_FUTURE, "random": m.HER_RANDOM}[strategy]
+    _run_pair(m, inp, steps=2, strategy=code, minimal_out=minimal)
 
 
 @pytest.mark.parametrize("name,batch,rows", [("b16384_s128_h128_bf16_g2_budget", 16384, 128),
