@@ -98,22 +98,10 @@ IQLH_DEV EpisodeProbe her_probe(const HerArgs& a, int64_t src) {
 
 // Goal distance of the sparse reward: binary32 sum of squared differences of
 // the first G entries of two next states, in goal order (no contraction),
-// then the correctly rounded square root.  The first 16 entries of both
-// goals are loaded together (clamped indexes, no branch around a load); the
-// donor's are returned in gd for callers that stage them.
-IQLH_DEV float her_distance(const float* __restrict__ ns, const float* __restrict__ nd, int G, float (&gd)[16]) {
-    if (G <= 0) {
-#pragma unroll
-        for (int d = 0; d < 16; ++d) gd[d] = 0.f;
-        return 0.f;  // empty goal: the square root of an empty sum
-    }
-    float gs[16];
-#pragma unroll
-    for (int d = 0; d < 16; ++d) {
-        const int dd = min(d, G - 1);
-        gs[d] = ns[dd];
-        gd[d] = nd[dd];
-    }
+// then the correctly rounded square root (0 for an empty goal).  gs and gd
+// hold the first 16 entries of both goals; entries past 16 are loaded here.
+IQLH_DEV float her_distance_loaded(const float* __restrict__ ns, const float* __restrict__ nd, int G,
+                                   const float (&gs)[16], const float (&gd)[16]) {
     float acc = 0.f;
 #pragma unroll
     for (int d = 0; d < 16; ++d) {
@@ -127,6 +115,46 @@ IQLH_DEV float her_distance(const float* __restrict__ ns, const float* __restric
         acc = __fadd_rn(acc, __fmul_rn(diff, diff));
     }
     return __fsqrt_rn(acc);
+}
+// The same with the first 16 entries of both goals loaded together (clamped
+// indexes, no branch around a load); the donor's are returned in gd for
+// callers that stage them.
+IQLH_DEV float her_distance(const float* __restrict__ ns, const float* __restrict__ nd, int G, float (&gd)[16]) {
+    if (G <= 0) {
+#pragma unroll
+        for (int d = 0; d < 16; ++d) gd[d] = 0.f;
+        return 0.f;  // empty goal: the square root of an empty sum
+    }
+    float gs[16];
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+        const int dd = min(d, G - 1);
+        gs[d] = ns[dd];
+        gd[d] = nd[dd];
+    }
+    return her_distance_loaded(ns, nd, G, gs, gd);
+}
+
+// Donor guessed before the episode ends arrive, so that its goal can be
+// loaded with them: episodes of equal length size / E put the end of the
+// probe's guess e at (e + 1) size / E; "random" needs no episode, so its
+// guess is exact.  Clamped into the buffer (the caller loads its goal
+// unconditionally and keeps it only when the resolved donor equals it).
+IQLH_DEV int64_t her_guess_donor(const HerArgs& a, int64_t src, uint64_t r, const EpisodeProbe& p) {
+    int64_t donor;
+    if (a.strategy == 2) {
+        donor = uniform_index(r, 0, (uint64_t)a.buffer_size);
+    } else {
+        const int E = a.num_episodes > 0 ? a.num_episodes : 1;
+        const int64_t end = (p.e + 1) * a.buffer_size / E;
+        if (a.strategy == 0) {
+            donor = end - 1;
+        } else {
+            const int64_t span = end - src - 1;
+            donor = span > 0 ? uniform_index(r, src + 1, (uint64_t)span) : src;
+        }
+    }
+    return max<int64_t>(0, min<int64_t>(donor, a.buffer_size - 1));
 }
 
 // Relabels rows 32 blk .. 32 blk + 31; every thread of a 256-thread block

@@ -837,6 +837,22 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
         const bool wact = wout && h.out_actions, wdone = wout && h.out_dones;  // uniform
         const int32_t hact0 = *(wact ? h.actions + hsc : h.source_idx);
         const float hdone0 = *(wdone ? h.dones + hsc : (const float*)h.source_idx);
+        // the first 16 goal entries of the source's s' and of the guessed
+        // donor's, in the same round of loads as the probe (rows of at least
+        // 8 whole chunks: offsets past the row end re-read its start, entries
+        // past the goal are never used)
+        const int64_t guess = her_guess_donor(h, hsc, hr, probe);
+        auto goal16 = [&](int64_t row, float (&gv)[16]) {
+            const float* rp = h.next_states + row * S_;
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const float4 v = *(const float4*)(rp + (4 * qd + 4 <= S_ ? 4 * qd : 0));
+                gv[4 * qd] = v.x; gv[4 * qd + 1] = v.y; gv[4 * qd + 2] = v.z; gv[4 * qd + 3] = v.w;
+            }
+        };
+        float gs[16], gd[16];
+        goal16(hsc, gs);
+        goal16(guess, gd);
         // the chunks' entries of s and s' (group 1 reloads s, which it does not
         // output, instead of s'); rows are whole 8-float chunks, 16-byte
         // aligned (iql_fused_her_ok), and a chunk past the row end loads the
@@ -870,8 +886,8 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
             if (hok) {
                 const float* ns = h.next_states + hsrc * S_;
                 const float* nd = h.next_states + donor * S_;
-                float gd[16];
-                const float dist = her_distance(ns, nd, G, gd);
+                if (donor != guess) goal16(donor, gd);  // an episode end off the equal-length guess
+                const float dist = her_distance_loaded(ns, nd, G, gs, gd);
 #pragma unroll
                 for (int d = 0; d < 16; ++d)
                     if (d < G) s_goal[tid * kHerGoalLds + d] = gd[d];
