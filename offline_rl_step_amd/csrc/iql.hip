@@ -806,12 +806,29 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) qa[k] = a.out_pi ? a.q_all[(int64_t)bc * a.A + min(q + 4 * k, a.A - 1)] : 0.f;
     };
+    auto store_weights = [&]() {
+#pragma unroll
+        for (int k = 0; k < W1_PER_THREAD; ++k) {
+            const int idx = (tid + k * NTHR) * 8, r = idx / SP, c = idx - r * SP;
+            *(u32x4*)(R0 + r * C::LDW1 + c) = w1r[k];
+        }
+#pragma unroll
+        for (int k = 0; k < W2_PER_THREAD; ++k) {
+            const int idx = (tid + k * NTHR) * 8, r = idx / H, c = idx - r * H;
+            *(u32x4*)(R1 + r * C::LDW2 + c) = w2r[k];
+        }
+        if (tid < H) {
+            sb1[tid] = vb1;
+            sb2[tid] = vb2;
+            sw3[tid] = vw3;
+        }
+    };
     if (her_wg) {
         // a tile of HER rows: the sources first, since the relabelling waits
         // on them -- one lead row per thread of waves 0-1, and the row of each
         // of this thread's chunks -- then the weights
-        const int64_t hsrc = h.source_idx[hrow0 + min(tid, nrow - 1)];
-        int64_t hsrck[X_PER_THREAD];
+        const int32_t hsrc32 = h.source_idx[hrow0 + min(tid, nrow - 1)];
+        int32_t hsrck[X_PER_THREAD];
 #pragma unroll
         for (int k = 0; k < X_PER_THREAD; ++k) {
             const int c = tid + k * NTHR, sr = c / (SP / 8);
@@ -829,6 +846,10 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
         const bool wout = g == 0;
         const bool hlead = tid < nrow;
         const uint64_t hr = hlead ? her_draw(h, hrow0 + tid, her_step_word(h)) : 0ull;
+        // the draw runs while the sources are in flight: nothing that waits on
+        // them may be scheduled above this point
+        __builtin_amdgcn_sched_barrier(0);
+        const int64_t hsrc = hsrc32;
         bool hok = hlead && hsrc >= 0 && hsrc < h.buffer_size;
         const EpisodeProbe probe = her_probe(h, hlead ? hsrc : 0);
         const int64_t hsc = hok ? hsrc : 0;
@@ -877,6 +898,7 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
                 xn[k][e] = keep_if(wnext && use && k0 + e < S_, yv[e]);
             }
         }
+        store_weights();  // while the relabelling loads are in flight
         float* s_goal = (float*)R3;                              // [BT][kHerGoalLds]
         int* s_hdon = (int*)(s_goal + BT * kHerGoalLds);         // [BT], -1: a zeroed row
         if (hlead) {
@@ -985,25 +1007,11 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
             }
         }
     }
-#pragma unroll
-    for (int k = 0; k < W1_PER_THREAD; ++k) {
-        const int idx = (tid + k * NTHR) * 8, r = idx / SP, c = idx - r * SP;
-        *(u32x4*)(R0 + r * C::LDW1 + c) = w1r[k];
-    }
-#pragma unroll
-    for (int k = 0; k < W2_PER_THREAD; ++k) {
-        const int idx = (tid + k * NTHR) * 8, r = idx / H, c = idx - r * H;
-        *(u32x4*)(R1 + r * C::LDW2 + c) = w2r[k];
-    }
+    if (!her_wg) store_weights();
 #pragma unroll
     for (int k = 0; k < X_PER_THREAD; ++k) {
         const int c = tid + k * NTHR, sr = c / (SP / 8), k0 = 8 * (c - sr * (SP / 8));
         *(u32x4*)(R2 + nat_off(sr, k0)) = xr[k];
-    }
-    if (tid < H) {
-        sb1[tid] = vb1;
-        sb2[tid] = vb2;
-        sw3[tid] = vw3;
     }
     lds_barrier();
     // the quarter's budget partials: its four wave sums added in block_sum_k's order
