@@ -11,8 +11,11 @@ one iql_aux_step call:
                          fixed-order gradient reduction, clipped Adam;
   3. the budget       -- four sources over 132612 parameters, budgets
                          0.70/0.15/0.10/0.05 of max_grad_norm 1.0, then Adam;
-in four launches (HER + budget norms | forward/backward + policy | reduction
-+ SAXPY | both Adam updates).  --separate times her_relabel +
+in three launches (forward/backward + policy + HER rows + budget norms |
+reduction + SAXPY | both Adam updates): the HER rows form the batch tail from
+a 128-row boundary, so the forward/backward kernel relabels them itself, and
+the budget norms ride on its other workgroups.  Shapes where that does not
+hold add a first launch (HER + budget norms).  --separate times her_relabel +
 iql_train_step_aw + grad_budget_accumulate called one after the other
 instead (same results bit for bit, seven launches).  The step is captured
 once in a HIP graph and replayed (the HER donor counter lives on the device,
@@ -94,13 +97,35 @@ def partial_layout(w, layout=None):
     return P, layout[1], layout[0]
 
 
+def budget_blocks(n):
+    """Blocks of the budget's pass 1 (budget_num_blocks in budget.hip)."""
+    return max(1, min(2048, ((n + 3) // 4 + 255) // 256))
+
+
+def fused_parts(w):
+    """Which first-launch passes the forward/backward launch hosts, by the
+    rules of iql_fused_her_ok / iql_fused_norms_ok (16-wave kernel: bf16,
+    hidden 128, state <= 128): HER rows that form the batch tail from a
+    128-row boundary, with whole 8-float chunks and goals of at most 64
+    entries; budget norms when their blocks fit four per host workgroup."""
+    k16 = w.dtype == "bf16" and w.H == 128 and w.S <= 128
+    n = w.n_her
+    her = k16 and n > 0 and (w.B - n) % 128 == 0 and w.S % 8 == 0 and w.G <= 64
+    hosts = w.groups * ((w.B - n) // 128 if her else (w.B + 127) // 128)
+    norms = k16 and w.budget and budget_blocks(w.n_budget) <= 4 * hosts
+    return her, norms
+
+
 def launch_bytes(w, layout=None):
-    """Bytes each of the four launches of one step must read and write, given
-    its inputs and outputs (what a perfect cache would leave of its traffic):
+    """Bytes each launch of one step must read and write, given its inputs
+    and outputs (what a perfect cache would leave of its traffic):
       relabel+norms: per HER row, source s and s' rows (f32), the donor's goal,
                      the source index, action, done and two episode ends;
                      written: the bf16 state row, the f32 s' row, action,
                      reward, done, donor.  Norms: every budget source once.
+                     Either part moves to fwd_bwd when that launch hosts it
+                     (fused_parts); the HER rows are then not read back from
+                     the batch.
       fwd_bwd:       the bf16 batch, q_taken, Q, the weight shadows and biases
                      of every trainer; written: V, the policy and the
                      per-workgroup gradient partials.
@@ -115,10 +140,14 @@ def launch_bytes(w, layout=None):
     e = 2 if w.dtype == "bf16" else 4
     shadows = e * (H * S + 2 * H * H)
     her = n * (8 * S + 4 * w.G + 4 + 4 + 4 + 8) + n * (e * S + 4 * S + 4 * 4)
+    norms = k * nb * 4
+    her_b, norms_b = fused_parts(w)
+    batch_rows = B - n if her_b else B
     return {
-        "relabel_norms": her + k * nb * 4,
-        "fwd_bwd": B * S * e + B * 4 + B * A * 4 + grp * (shadows + 4 * (3 * H + 1))
-                   + grp * B * 4 + grp * B * A * 4 + grp * nwg * Pp * 4,
+        "relabel_norms": (0 if her_b else her) + (0 if norms_b else norms),
+        "fwd_bwd": batch_rows * S * e + B * 4 + B * A * 4 + grp * (shadows + 4 * (3 * H + 1))
+                   + grp * B * 4 + grp * B * A * 4 + grp * nwg * Pp * 4
+                   + (her if her_b else 0) + (norms if norms_b else 0),
         "reduce_saxpy": grp * nwg * Pp * 4 + grp * nwg * 4 + grp * P * 4 + k * nb * 4 + nb * 4,
         "adam": grp * (P * 32 + shadows) + nb * 32,
     }
@@ -329,8 +358,12 @@ def summarize_profiles(d, workload=None):
     L.append(f"# Kernel time and HBM traffic of one whole step, batch {w.B}, state {w.S}, hidden {w.H}, "
              f"{w.groups} trainer{'s' if w.groups > 1 else ''}, {what}")
     L.append("")
-    L.append(f"Workload `{w.name}`.  One `iql_aux_step` per step (four launches), graph replay, one MI355X.  "
-             f"Source of commit {commit} (forward/backward source hash {src_hash}).")
+    her_b, norms_b = fused_parts(w)
+    nl = 3 if (her_b or w.n_her == 0) and (norms_b or not w.budget) else 4
+    L.append(f"Workload `{w.name}`.  One `iql_aux_step` per step ({nl} launches"
+             + ("; the forward/backward launch also relabels the HER rows" if her_b else "")
+             + ("; it also runs the budget norms" if norms_b else "")
+             + f"), graph replay, one MI355X.  Source of commit {commit} (forward/backward source hash {src_hash}).")
     L.append("")
     L.append("Commands (from /tmp, each its own run, `REPO` = the repository root, `OUT` = an output folder):")
     L.append("")
@@ -388,7 +421,8 @@ def summarize_profiles(d, workload=None):
     L.append(f"`needed MB` is each launch's inputs and outputs read or written once (`launch_bytes` in "
              f"bench.py).  For the forward/backward launch it includes its fp32 gradient partials "
              f"({w.groups} x {nwg} rows x {Pp} floats = {w.groups * nwg * Pp * 4 / 1e6:.1f} MB), which the "
-             f"reduction reads back.")
+             f"reduction reads back"
+             + (", and the HER rows' replay reads and outputs" if her_b else "") + ".")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     md = os.path.join(ROOT, "profiles", f"step_{w.name}_kernels.md")
     with open(md, "w") as fh:
@@ -596,7 +630,7 @@ def main():
            "launch_us": dict(zip(names, launch_us)),
            "launch_hbm": {k: {"needed_bytes": lb[k], "GB/s": lb[k] / (us * 1e-6) / 1e9,
                               "frac_of_8TBs": lb[k] / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
-                          for k, us in zip(names, launch_us)},
+                          for k, us in zip(names, launch_us) if us > 0.0},
            "roofline": roofline}
     if not a.no_next_rows:
         out["next_rows"] = time_next_rows(ctx, torch, np)

@@ -369,9 +369,11 @@ int iql_aux_step(iql_handle h, const iqlh_her_step* her, const void* states, con
  * iql_aux_step (they update the state like any other step), each launch
  * timed by its own dispatch events (kernel time only, no launch gaps), and
  * writes the mean duration in microseconds of each of the four launches:
- * out_avg_us[0] relabelling and budget norms (about 0 when that launch is
- * not needed), [1] forward/backward, [2] reduction and SAXPY, [3] both Adam
- * updates.  Synchronises the stream. */
+ * out_avg_us[0] relabelling and budget norms (0 when that launch is not
+ * needed: HER rows that form the bf16 batch tail from a 128-row boundary and
+ * the budget norms then ride in the forward/backward launch), [1]
+ * forward/backward, [2] reduction and SAXPY, [3] both Adam updates.
+ * Synchronises the stream. */
 int iql_time_aux_step(iql_handle h, const iqlh_her_step* her, const void* states,
                       const float* q_taken, int32_t batch, const float* q_all,
                       int32_t num_actions, float beta, float* out_pi, float* out_v,

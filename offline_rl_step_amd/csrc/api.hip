@@ -651,11 +651,12 @@ int iql_time_aux_step(iql_handle h, const iqlh_her_step* her, const void* states
     for (int i = 0; i < 8 && e == hipSuccess; ++i) e = hipEventCreate(&ev[i]);
     double total[4] = {0.0, 0.0, 0.0, 0.0};
     for (int r = 0; r < reps && e == hipSuccess; ++r) {
+        bool ran_a = false;
         e = launch_aux_step(h->dims, h->buf, adam_hyper(h), h->cfg.tau, p.her ? &p.ha : nullptr, states,
                             h->cfg.states_ld, q_taken, batch, q_all, num_actions, beta, out_pi, out_v, out_loss,
-                            out_grad_norm, p.budget ? &p.ba : nullptr, (hipStream_t)stream, ev);
+                            out_grad_norm, p.budget ? &p.ba : nullptr, (hipStream_t)stream, ev, &ran_a);
         if (e == hipSuccess) e = hipEventSynchronize(ev[7]);
-        for (int k = 0; k < 4 && e == hipSuccess; ++k) {
+        for (int k = ran_a ? 0 : 1; k < 4 && e == hipSuccess; ++k) {
             float ms = 0.f;
             e = hipEventElapsedTime(&ms, ev[2 * k], ev[2 * k + 1]);
             total[k] += ms;

@@ -215,8 +215,9 @@ hipError_t launch_aux_step(const IqlDims& d, const IqlBuffers& b, const AdamHype
                            const HerArgs* her, const void* states, int64_t ld, const float* q, int B,
                            const float* q_all, int A, float beta, float* out_pi, float* out_v,
                            float* out_loss, float* out_gnorm, const BudgetArgs* budget, hipStream_t stream,
-                           hipEvent_t* ev = nullptr);
-// ev (optional): 8 events, start/stop of launches A, B, C, D (A's are
-// recorded back to back when A is not needed).
+                           hipEvent_t* ev = nullptr, bool* ran_a = nullptr);
+// ev (optional): 8 events, start/stop of launches A, B, C, D (A's are not
+// recorded when A is not needed: its HER rows and budget norms both ride in
+// B).  ran_a (optional) receives whether A was launched.
 
 }  // namespace iqlh

@@ -9,7 +9,9 @@
 // independent passes share a launch, each taking a contiguous range of its
 // blocks (a block-uniform branch, no divergence inside a wave):
 //   A  HER rows                 | budget: per-source sums of squares
-//   B  fused V forward/backward and advantage-weighted policy
+//   B  fused V forward/backward and advantage-weighted policy (with the 16-wave
+//      kernel also the HER rows that form the batch tail from a 128-row
+//      boundary and the budget norms, so that A is not launched)
 //   C  IQL: fixed-order sum of the workgroup partials | budget: clip + SAXPY
 //   D  IQL: clip + Adam + shadows | budget: clip + Adam (or the norm only)
 // Results are bit-for-bit those of the separate launches: every block runs
@@ -109,7 +111,7 @@ hipError_t launch_aux_step(const IqlDims& d, const IqlBuffers& b, const AdamHype
                            const HerArgs* her, const void* states, int64_t ld, const float* q, int B,
                            const float* q_all, int A, float beta, float* out_pi, float* out_v,
                            float* out_loss, float* out_gnorm, const BudgetArgs* bud, hipStream_t stream,
-                           hipEvent_t* ev) {
+                           hipEvent_t* ev, bool* ran_a) {
     int nwg, nloss;
     if (!iql_partial_counts(d, B, &nwg, &nloss)) return hipErrorInvalidValue;
     const int nb = bud ? budget_num_blocks(bud->n) : 0;
@@ -140,10 +142,8 @@ hipError_t launch_aux_step(const IqlDims& d, const IqlBuffers& b, const AdamHype
         NormsArgs npa{};
         if (nb_a) npa = np;
         STEP_LAUNCH(step_her_norms_kernel, her_blocks + nb_a, ev, ha, her_blocks, npa);
-    } else if (ev) {  // nothing to launch: an empty interval keeps the timing uniform
-        (void)hipEventRecord(ev[0], stream);
-        (void)hipEventRecord(ev[1], stream);
     }
+    if (ran_a) *ran_a = her_blocks + nb_a > 0;
 
     // B: fused forward/backward (+ policy, HER rows, budget norms)
     hipError_t e;

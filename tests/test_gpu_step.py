@@ -304,12 +304,13 @@ def test_whole_step_matches_oracle(m):
     r.tr.close()
 
 
-@pytest.mark.parametrize("B,n_budget", [(2048, 5000), (3000, 5000), (1024, 300000)])
-def test_time_aux_step_reports_every_launch(m, B, n_budget):
+@pytest.mark.parametrize("B,n_budget,first_launch", [(2048, 5000, False), (3000, 5000, True), (1024, 300000, True)])
+def test_time_aux_step_reports_every_launch(m, B, n_budget, first_launch):
     """The measurement entry point runs real steps (Adam's t advances) and
-    reports a kernel time for each of the four launches (for the first, the
-    interval between its two events when the forward/backward launch hosts
-    both of its passes)."""
+    reports a positive kernel time for every launch it makes, and 0 for the
+    first when the forward/backward launch hosts both of its passes (HER
+    rows at a 128-row boundary of the batch tail, budget norms small enough
+    to ride along)."""
     w = synth.shrink(synth.WORKLOADS["b16384_s128_h128_bf16_g2_budget"], C=1 << 14)
     inp = Inputs(w, B, n_budget)
     r = Rig(m, inp)
@@ -318,7 +319,8 @@ def test_time_aux_step_reports_every_launch(m, B, n_budget):
                         w.max_grad_norm, r.norms, r.adam, r.ws)
     us = r.tr.time_aux_step(her, r.X, inp.t_q, inp.B, inp.t_Q, w.A, w.beta, r.pi, r.out_v, r.out_loss, r.out_gn,
                             bud, reps=5)
-    assert len(us) == 4 and all(np.isfinite(us)) and min(us[1:]) > 0.0 and us[0] >= 0.0, us
+    assert len(us) == 4 and all(np.isfinite(us)) and min(us[1:]) > 0.0, us
+    assert (us[0] > 0.0) if first_launch else (us[0] == 0.0), us
     t = r.tensors()
     sync()
     assert int(host(t["t0"])[0]) == 5 and int(host(r.tt)[0]) == 5
