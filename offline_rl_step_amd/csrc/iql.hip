@@ -605,6 +605,12 @@ IQLH_DEV float row_sum16_scatter(const float (&v)[16]) {
     return (b0 ? d[1] : d[0]) + dpp_f<0xB1>(b0 ? d[0] : d[1]);  // quad_perm [1,0,3,2]
 }
 
+// ReLU on the bit pattern, one integer max: a float with the sign bit set is
+// a negative int32 and becomes +0 (a NaN keeps its payload unless its sign
+// bit is set, as the reference maximum propagates NaN).  The float max would
+// first canonicalise its operand, a second instruction.
+IQLH_DEV float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // ---- activation tiles of the 16x16 kernel: natural [sample][feature]
 // layout, rows of kNatLd elements, the 16-byte unit u of row s stored at
 // unit u ^ bit2(s) ^ 8 bit3(s).  A lane writes its 4 consecutive features of
@@ -1043,9 +1049,9 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
     for (int t = 0; t < FT; ++t) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float y = acc[t][r] > 0.f ? acc[t][r] : 0.f;
+            const float y = relu_bits(acc[t][r]);
             acc[t][r] = y;
-            mask1 |= ((__float_as_uint(y) + 0x7FFFFFFFu) >> 31) << (4 * t + r);
+            mask1 |= min(__float_as_uint(y), 1u) << (4 * t + r);  // y >= +0: bit set iff y != 0
         }
         put4(R3, bl, fb + 16 * t + 4 * q, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);  // h1
     }
@@ -1068,7 +1074,7 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
 #pragma unroll
     for (int t = 0; t < FT; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vpart = fmaf(w3v[t][r], acc[t][r] > 0.f ? acc[t][r] : 0.f, vpart);
+        for (int r = 0; r < 4; ++r) vpart = fmaf(w3v[t][r], relu_bits(acc[t][r]), vpart);
     vpart = sum_q4(vpart);
     if (q == 0) svh[fh * BT + bl] = vpart;
     lds_barrier();
@@ -1129,7 +1135,7 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float z = acc[t][r];
-            hv[4 * t + r] = z > 0.f ? z * dv : 0.f;
+            hv[4 * t + r] = relu_bits(z) * dv;
             acc[t][r] = z > 0.f ? dv * w3v[t][r] : 0.f;
         }
         put4(R0, bl, fb + 16 * t + 4 * q, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
@@ -1178,7 +1184,8 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
     for (int t = 0; t < FT; ++t) {
         float d[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) d[r] = (mask1 >> (4 * t + r)) & 1u ? acc[t][r] : 0.f;
+        for (int r = 0; r < 4; ++r)  // keep dh1 where relu'(z1) = 1: AND with the sign-extended mask bit
+            d[r] = __int_as_float(__float_as_int(acc[t][r]) & __builtin_amdgcn_sbfe((int)mask1, 4 * t + r, 1));
         put4(R3, bl, fb + 16 * t + 4 * q, d[0], d[1], d[2], d[3]);
     }
     lds_barrier();
