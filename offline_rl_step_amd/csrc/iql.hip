@@ -1091,41 +1091,15 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
         dv = -2.f * w * diff * a.invB;
         if (fh == 0 && q == 0 && a.out_v) a.out_v[(int64_t)g * B + b] = v;
     }
-    // the two waves of a sample group split the epilogue, one the loss sums
-    // and one the (heavier) policy, alternating with the sample group so that
-    // every SIMD runs two of each (waves go to SIMDs round-robin)
-    if (fh != ((sg >> 1) & 1)) {
+    // the two waves of a sample group split the per-sample work: one the loss
+    // sums (here), the other the (heavier) policy (in the dW2 phase, whose
+    // waves mostly wait on LDS and MFMA), alternating with the sample group so
+    // that every SIMD runs two of each (waves go to SIMDs round-robin)
+    const bool policy_wave = fh == ((sg >> 1) & 1);
+    if (!policy_wave) {
         const float ls = row_sum16(lterm);
         const float ds = row_sum16(dv);
         if (lane == 0) { sred[sg] = ls; sred[NW / 2 + sg] = ds; }
-    } else {
-        if (a.out_pi) {
-            // pi = softmax(beta * clamp(Q - V, -10, 10)) with the row maximum
-            // subtracted ("Current State / IQL (CPU)", advantage-weighted
-            // action selection); the four lanes of a sample share it
-            float x[4], mx = -INFINITY;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const bool on = q + 4 * k < a.A;
-                x[k] = on ? a.beta * fminf(fmaxf(qa[k] - v, -10.f), 10.f) : -INFINITY;
-                mx = fmaxf(mx, x[k]);
-            }
-            mx = max_q4(mx);
-            float se = 0.f;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                x[k] = q + 4 * k < a.A ? expf(x[k] - mx) : 0.f;
-                se += x[k];
-            }
-            se = sum_q4(se);
-            if (valid) {
-                float* pr = a.out_pi + ((int64_t)g * B + b) * a.A;
-                const float inv = 1.f / se;  // one division, then products
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    if (q + 4 * k < a.A) pr[q + 4 * k] = x[k] * inv;
-            }
-        }
     }
     // dz2 = dv w3 relu'(z2) -> R0 (W1 is dead); dw3 over this sample group
     static_assert(FT == 4, "sixteen values per lane for the dw3 sums");
@@ -1160,6 +1134,33 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
             for (int i = 0; i < NW / 2; ++i) { ls += sred[i]; ds += sred[NW / 2 + i]; }
             a.loss_part[(int64_t)g * a.nwg + wg] = ls;
             part[po.b3] = ds;
+        }
+        if (policy_wave && a.out_pi) {
+            // pi = softmax(beta * clamp(Q - V, -10, 10)) with the row maximum
+            // subtracted ("Current State / IQL (CPU)", advantage-weighted
+            // action selection); the four lanes of a sample share it
+            float x[4], mx = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const bool on = q + 4 * k < a.A;
+                x[k] = on ? a.beta * fminf(fmaxf(qa[k] - v, -10.f), 10.f) : -INFINITY;
+                mx = fmaxf(mx, x[k]);
+            }
+            mx = max_q4(mx);
+            float se = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                x[k] = q + 4 * k < a.A ? expf(x[k] - mx) : 0.f;
+                se += x[k];
+            }
+            se = sum_q4(se);
+            if (valid) {
+                float* pr = a.out_pi + ((int64_t)g * B + b) * a.A;
+                const float inv = 1.f / se;  // one division, then products
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (q + 4 * k < a.A) pr[q + 4 * k] = x[k] * inv;
+            }
         }
         nat_gemm16_part<H / 32>(R0, R3, sg, (H / 32) * fh, part + po.w2, H, H, fh == 0 ? part + po.b2 : nullptr);
 #pragma unroll
