@@ -847,10 +847,14 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
         // done with the chunks' entries of s and s'; donor, goal, distance and
         // reward; the goals exchanged through LDS (R3 is free until F1); the
         // chunks with their goal entries replaced, rounded to bfloat16 for the
-        // tile.  Group 0 writes the HER outputs, group 1 only uses the rows.
+        // tile.  Every group builds every row of the tile; the HER outputs of
+        // tile row r are written by group r * groups / 128 alone, so that the
+        // groups share the output traffic.
         const int S_ = h.S, G = h.G;
-        const bool wout = g == 0;
+        const int ngrp = (int)gridDim.y;
+        auto writes_row = [&](int r) { return r * ngrp / BT == g; };
         const bool hlead = tid < nrow;
+        const bool wout = writes_row(tid);  // this lead row's outputs
         const uint64_t hr = hlead ? her_draw(h, hrow0 + tid, her_step_word(h)) : 0ull;
         // the draw runs while the sources are in flight: nothing that waits on
         // them may be scheduled above this point
@@ -861,7 +865,7 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
         const int64_t hsc = hok ? hsrc : 0;
         // action and done through pointer selects: no branch around a load
         // (the join of one would drain every load in flight)
-        const bool wact = wout && h.out_actions, wdone = wout && h.out_dones;  // uniform
+        const bool wact = wout && h.out_actions, wdone = wout && h.out_dones;
         const int32_t hact0 = *(wact ? h.actions + hsc : h.source_idx);
         const float hdone0 = *(wdone ? h.dones + hsc : (const float*)h.source_idx);
         // the first 16 goal entries of the source's s' and of the guessed
@@ -880,15 +884,15 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
         float gs[16], gd[16];
         goal16(hsc, gs);
         goal16(guess, gd);
-        // the chunks' entries of s and s' (group 1 reloads s, which it does not
-        // output, instead of s'); rows are whole 8-float chunks, 16-byte
-        // aligned (iql_fused_her_ok), and a chunk past the row end loads the
-        // row's last chunk and is masked
-        const bool wnext = wout && h.out_next_states != nullptr;
+        // the chunks' entries of s and s' (a chunk whose row this group does
+        // not output reloads s instead of s'); rows are whole 8-float chunks,
+        // 16-byte aligned (iql_fused_her_ok), and a chunk past the row end
+        // loads the row's last chunk and is masked
         float xs[X_PER_THREAD][8], xn[X_PER_THREAD][8];
 #pragma unroll
         for (int k = 0; k < X_PER_THREAD; ++k) {
             const int c = tid + k * NTHR, sr = c / (SP / 8), k0 = 8 * (c - sr * (SP / 8));
+            const bool wnext = writes_row(sr) && h.out_next_states != nullptr;
             const bool use = sr < nrow && hsrck[k] >= 0 && hsrck[k] < h.buffer_size;
             const int64_t sk = use ? hsrck[k] : 0;
             const int kc = min(k0, S_ - 8);
@@ -961,10 +965,10 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
                           (uint32_t)f2bf(x[2]) | ((uint32_t)f2bf(x[3]) << 16),
                           (uint32_t)f2bf(x[4]) | ((uint32_t)f2bf(x[5]) << 16),
                           (uint32_t)f2bf(x[6]) | ((uint32_t)f2bf(x[7]) << 16)};
-            if (wout && sr < nrow && k0 < S_) {  // whole chunks: S is a multiple of 8
+            if (writes_row(sr) && sr < nrow && k0 < S_) {  // whole chunks: S is a multiple of 8
                 const int64_t hi = hrow0 + sr;
                 *(u32x4*)((uint16_t*)h.out_states + hi * a.ld + k0) = xr[k];
-                if (wnext) {
+                if (h.out_next_states) {
                     float* no = h.out_next_states + hi * S_ + k0;
                     *(float4*)no = float4{y[0], y[1], y[2], y[3]};
                     *(float4*)(no + 4) = float4{y[4], y[5], y[6], y[7]};
