@@ -56,13 +56,16 @@ struct SaxpyPart {
     int vec, nb;
 };
 
+// The budget's SAXPY blocks come first: their chain of dependent loads is
+// longer than the reduction's streaming, and blocks are dispatched in order.
 __global__ __launch_bounds__(256) void step_reduce_saxpy_kernel(ReducePart r, SaxpyPart x) {
-    const int bx = blockIdx.x, nr = r.rb * r.G;
-    if (bx < nr) {
-        iql_reduce_block(r.part, r.loss_part, r.nwg, r.nloss, r.P, r.Pp, r.invB, r.grad, r.sq_part, r.rb,
-                         r.tcount, r.step, r.out_loss, r.flags, bx % r.rb, bx / r.rb);
+    const int bx = blockIdx.x;
+    if (bx < x.nb) {
+        saxpy_block(x.s, x.n, x.vec, x.mgn, x.partials, x.grad, x.gpart, x.out_norms, x.adam_t, bx, x.nb);
     } else {
-        saxpy_block(x.s, x.n, x.vec, x.mgn, x.partials, x.grad, x.gpart, x.out_norms, x.adam_t, bx - nr, x.nb);
+        const int br = bx - x.nb;
+        iql_reduce_block(r.part, r.loss_part, r.nwg, r.nloss, r.P, r.Pp, r.invB, r.grad, r.sq_part, r.rb,
+                         r.tcount, r.step, r.out_loss, r.flags, br % r.rb, br / r.rb);
     }
 }
 
