@@ -346,7 +346,7 @@ __global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- F1: z1^T = W1 * s^T
     f32x16 acc[NT];
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
         for (int r = 0; r < 16; ++r)
             mask1[(16 * t + r) >> 5] |= ((__float_as_uint(acc[t][r]) + 0x7FFFFFFFu) >> 31)
                                         << ((16 * t + r) & 31);
-    __syncthreads();
+    lds_barrier();
 
     // ---- F2: z2^T = W2 * h1^T  (A read with the chained k order)
 #pragma unroll
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
     typename O::frag dz2f[KUH];
 #pragma unroll
     for (int u = 0; u < KUH; ++u) dz2f[u] = O::template from_acc<NT>(acc, u);
-    __syncthreads();
+    lds_barrier();
 
     // ---- dw3 (row sums of h2 * dv), db3, loss, then dW2 = dz2^T h1 with db2
     lds_rowsum<T, BT>(R2, C::LDA, wv * NT / NW, (wv + 1) * NT / NW, part + po.w3);
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
         const int t0 = wv * T2 / NW, t1 = (wv + 1) * T2 / NW;
         lds_gemm_store<T, BT, 4>(R0, R3, C::LDA, NT, t0, t1, part + po.w2, H, H, part + po.b2);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- s^T tile to R3 (h1^T no longer needed); B1: dh1^T = W2^T dz2^T
 #pragma unroll
@@ -496,7 +496,7 @@ __global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
             O::put2(R2, f * C::LDA + bl, C::LDA, pos0 ? acc[t][r] : 0.f, pos1 ? acc[t][r + 1] : 0.f);
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- dW1 = dz1^T s with db1
     {
