@@ -14,16 +14,21 @@ constexpr int kMaxBlocks = 2048;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Quad qd covers elements 4qd .. 4qd+3 (those < n); 16-byte loads when every
-// pointer involved is 16-byte aligned.
-IQLH_DEV f32x4 ld4(const float* __restrict__ p, int64_t i, int64_t n, bool vec) {
-    if (vec && i + 3 < n) return *(const f32x4*)(p + i);
-    f32x4 r = {0.f, 0.f, 0.f, 0.f};
+// Quad at element i (a multiple of 4 below n) with no lane-dependent branch:
+// one 16-byte load when vec4 (every pointer 16-byte aligned and n a multiple
+// of 4, the same for all lanes), else four element loads at clamped indices,
+// zero past n.  A lane-dependent branch around a load makes the code after
+// its end wait for every load in flight, which would serialise consecutive
+// quads.
+IQLH_DEV f32x4 ld4(const float* __restrict__ p, int64_t i, int64_t n, bool vec4) {
+    if (vec4) return *(const f32x4*)(p + i);
+    f32x4 r;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        if (i + e < n) r[e] = p[i + e];
+    for (int e = 0; e < 4; ++e) r[e] = keep_if(i + e < n, p[i + e < n ? i + e : n - 1]);
     return r;
 }
+// 16-byte quad loads are possible: aligned pointers and no partial last quad.
+IQLH_DEV bool quads_vec(int vec, int64_t n) { return vec && (n & 3) == 0; }
 IQLH_DEV void st4(float* __restrict__ p, int64_t i, int64_t n, bool vec, f32x4 x) {
     if (vec && i + 3 < n) {
         *(f32x4*)(p + i) = x;
@@ -59,14 +64,19 @@ IQLH_DEV void block_sum_k(float (&v)[kMaxSources], int k, float (*red)[kBT / kWa
 
 // fold_partials of k consecutive sets of nb partials, all loads in flight
 // together; out[j] equals fold_partials(p + j * nb, nb).
+// Every set's partial is loaded before any is added (at a clamped set index,
+// so no branch separates the loads from each other), so one wait covers them.
 IQLH_DEV void fold_partials_k(const float* __restrict__ p, int nb, int k, float (&out)[kMaxSources],
                               float (*red)[kBT / kWave]) {
 #pragma unroll
     for (int j = 0; j < kMaxSources; ++j) out[j] = 0.f;
     for (int i = threadIdx.x; i < nb; i += kBT) {
+        float x[kMaxSources];
+#pragma unroll
+        for (int j = 0; j < kMaxSources; ++j) x[j] = keep_if(j < k, p[(int64_t)(j < k ? j : k - 1) * nb + i]);
 #pragma unroll
         for (int j = 0; j < kMaxSources; ++j)
-            if (j < k) out[j] += p[(int64_t)j * nb + i];
+            if (j < k) out[j] += x[j];
     }
     block_sum_k(out, k, red);
 }
@@ -78,14 +88,17 @@ IQLH_DEV void norms_thread(const SourceSet& s, int64_t n, int vec, int bx, int n
 #pragma unroll
     for (int j = 0; j < kMaxSources; ++j) acc[j] = 0.f;
     const int64_t quads = (n + 3) / 4, stride = (int64_t)nb * kBT;
+    const bool vec4 = quads_vec(vec, n);
     for (int64_t qd = (int64_t)bx * kBT + t; qd < quads; qd += stride) {
+        // every source's quad in flight before the first is used
+        f32x4 x[kMaxSources];
 #pragma unroll
-        for (int j = 0; j < kMaxSources; ++j) {
-            if (j < s.k) {
-                const f32x4 x = ld4(s.ptr[j], 4 * qd, n, vec);
-                acc[j] = fmaf(x.x, x.x, fmaf(x.y, x.y, fmaf(x.z, x.z, fmaf(x.w, x.w, acc[j]))));
-            }
-        }
+        for (int j = 0; j < kMaxSources; ++j)
+            x[j] = j < s.k ? ld4(s.ptr[j], 4 * qd, n, vec4) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kMaxSources; ++j)
+            if (j < s.k)
+                acc[j] = fmaf(x[j].x, x[j].x, fmaf(x[j].y, x[j].y, fmaf(x[j].z, x[j].z, fmaf(x[j].w, x[j].w, acc[j]))));
     }
 }
 
@@ -134,42 +147,98 @@ IQLH_DEV void saxpy_block(const SourceSet& s, int64_t n, int vec, float mgn, con
     // scales: load it before folding the norm partials
     const int64_t quads = (n + 3) / 4, stride = (int64_t)nb * kBT;
     const int64_t q0 = (int64_t)bx * kBT + threadIdx.x;
+    const bool vec4 = quads_vec(vec, n);
+    // (at a clamped quad, so that no lane-dependent branch surrounds the
+    // loads; a thread past the last quad does not use them)
+    const int64_t c0 = q0 < quads ? q0 : quads - 1;
     f32x4 pre[kMaxSources];
 #pragma unroll
     for (int j = 0; j < kMaxSources; ++j)
-        pre[j] = (j < s.k && q0 < quads) ? ld4(s.ptr[j], 4 * q0, n, vec) : f32x4{0.f, 0.f, 0.f, 0.f};
+        pre[j] = (j < s.k && quads > 0) ? ld4(s.ptr[j], 4 * c0, n, vec4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    // block 0 bumps the Adam step count at its end; the old count is loaded
+    // now, by every thread (one address), with the other loads
+    const int32_t t_old = (bx == 0 && adam_t) ? *adam_t : 0;
     // every thread folds every source's partials (same value in all threads
     // and blocks) and derives the clip scales itself
-    float c[kMaxSources];
+    float c[kMaxSources], nrm[kMaxSources];
     fold_partials_k(partials, nb, s.k, c, redk);
 #pragma unroll
     for (int j = 0; j < kMaxSources; ++j) {
-        if (j < s.k) {
-            const float nrm = sqrtf(c[j]);
-            if (bx == 0 && threadIdx.x == 0 && out_norms) out_norms[j] = nrm;
-            c[j] = s.alpha[j] * budget_scale(nrm, s.frac[j] * mgn);
-        } else {
-            c[j] = 0.f;
-        }
+        nrm[j] = sqrtf(c[j]);
+        c[j] = j < s.k ? s.alpha[j] * budget_scale(nrm[j], s.frac[j] * mgn) : 0.f;
     }
-    if (bx == 0 && threadIdx.x == 0 && adam_t) *adam_t += 1;
     float acc = 0.f;
-    for (int64_t qd = q0; qd < quads; qd += stride) {
+    if (q0 < quads) {
         f32x4 g = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < kMaxSources; ++j)
-            if (j < s.k) g += c[j] * (qd == q0 ? pre[j] : ld4(s.ptr[j], 4 * qd, n, vec));
+            if (j < s.k) g += c[j] * pre[j];
+        st4(grad, 4 * q0, n, vec, g);
+        acc = fmaf(g.x, g.x, fmaf(g.y, g.y, fmaf(g.z, g.z, fmaf(g.w, g.w, acc))));
+    }
+    for (int64_t qd = q0 + stride; qd < quads; qd += stride) {
+        // every source's quad in flight before the first is used
+        f32x4 x[kMaxSources];
+#pragma unroll
+        for (int j = 0; j < kMaxSources; ++j)
+            x[j] = j < s.k ? ld4(s.ptr[j], 4 * qd, n, vec4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 g = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kMaxSources; ++j)
+            if (j < s.k) g += c[j] * x[j];
         st4(grad, 4 * qd, n, vec, g);
         acc = fmaf(g.x, g.x, fmaf(g.y, g.y, fmaf(g.z, g.z, fmaf(g.w, g.w, acc))));
     }
     const float t = block_sum<kBT>(acc, red);
     if (threadIdx.x == 0) gpart[bx] = t;
+    // block 0's other outputs last: a store issued earlier would make the
+    // wave's next wait for a load wait for it as well
+    if (bx == 0 && threadIdx.x == 0) {
+        if (out_norms) {
+#pragma unroll
+            for (int j = 0; j < kMaxSources; ++j)
+                if (j < s.k) out_norms[j] = nrm[j];
+        }
+        if (adam_t) *adam_t = t_old + 1;
+    }
 }
 
 IQLH_DEV void norm_finalize_block(const float* __restrict__ p, int nb, float* __restrict__ out) {
     __shared__ float red[kBT / kWave];
     const float sq = fold_partials(p, nb, red);
     if (threadIdx.x == 0) *out = sqrtf(sq);
+}
+
+// One quad of pass 3: the clipped Adam update of elements i .. i+3 (those
+// < n) from their loaded state, then every store of the quad (grad zeroed).
+// The stores come after the arithmetic: a store issued between a load and
+// its use would make the use wait for the store as well.
+IQLH_DEV void adam_flat_quad(float* __restrict__ params, float* __restrict__ grad, float* __restrict__ m,
+                             float* __restrict__ v, int64_t i, int64_t n, int vec, f32x4 g4, f32x4 m4, f32x4 v4,
+                             f32x4 p4, float bc1, float bc2, float decay, const AdamHyper& hp, bool& bad,
+                             bool& bad_state) {
+    // no contraction: the same roundings in every kernel this is inlined into
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float g = g4[e];
+        if (!isfinite(g)) { bad |= (i + e < n); continue; }
+        const float mi = hp.beta1 * m4[e] + (1.f - hp.beta1) * g;
+        const float vi = hp.beta2 * v4[e] + (1.f - hp.beta2) * g * g;
+        const float mh = mi / bc1, vh = vi / bc2;
+        float p = p4[e];
+        if (hp.weight_decay != 0.f) p *= decay;
+        p -= hp.lr * mh / (sqrtf(vh) + hp.eps);
+        if (hp.clamp > 0.f) p = fminf(fmaxf(p, -hp.clamp), hp.clamp);
+        p4[e] = p;
+        m4[e] = mi;
+        v4[e] = vi;
+        bad_state |= (i + e < n) && !(isfinite(p) && isfinite(mi) && isfinite(vi));
+    }
+    st4(grad, i, n, vec, f32x4{0.f, 0.f, 0.f, 0.f});
+    st4(params, i, n, vec, p4);
+    st4(m, i, n, vec, m4);
+    st4(v, i, n, vec, v4);
 }
 
 // Pass 3 for block bx of nbx: folds the nb grad partials into the norm and
@@ -179,55 +248,35 @@ IQLH_DEV void adam_flat_block(float* __restrict__ params, float* __restrict__ gr
                               const float* __restrict__ sq_part, int nb, int64_t n, int vec,
                               const AdamHyper& hp, float* __restrict__ out_norm, int32_t* __restrict__ flags,
                               int bx, int nbx) {
-    // no contraction: the same roundings in every kernel this is inlined into
 #pragma clang fp contract(off)
     __shared__ float red[kBT / kWave];
     const int64_t quads = (n + 3) / 4, stride = (int64_t)nbx * kBT;
     const int64_t q0 = (int64_t)bx * kBT + threadIdx.x;
-    // first quad's state loaded before the norm fold (independent of it)
-    f32x4 pg = {0.f, 0.f, 0.f, 0.f}, pm = pg, pv = pg, pp = pg;
-    if (q0 < quads) {
-        pg = ld4(grad, 4 * q0, n, vec);
-        pm = ld4(m, 4 * q0, n, vec);
-        pv = ld4(v, 4 * q0, n, vec);
-        pp = ld4(params, 4 * q0, n, vec);
-    }
+    // The first quad's state does not depend on the norm: it is loaded before
+    // the fold, at a clamped index so that no lane-dependent branch surrounds
+    // the loads.
+    const bool vec4 = quads_vec(vec, n), any = quads > 0;
+    const int64_t c0 = q0 < quads ? q0 : quads - 1;
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 pg = any ? ld4(grad, 4 * c0, n, vec4) : z4, pm = any ? ld4(m, 4 * c0, n, vec4) : z4;
+    const f32x4 pv = any ? ld4(v, 4 * c0, n, vec4) : z4, pp = any ? ld4(params, 4 * c0, n, vec4) : z4;
     const float sq = fold_partials(sq_part, nb, red);
     const float nrm = sqrtf(sq);
-    if (bx == 0 && threadIdx.x == 0 && out_norm) *out_norm = nrm;
     const float c = adam_clip(nrm, hp.max_grad_norm);
     const float tt = (float)(*tptr);
     const float bc1 = 1.f - powf(hp.beta1, tt);
     const float bc2 = 1.f - powf(hp.beta2, tt);
     const float decay = 1.f - hp.lr * hp.weight_decay;
     bool bad = false, bad_state = false;
-    for (int64_t qd = q0; qd < quads; qd += stride) {
+    if (q0 < quads)
+        adam_flat_quad(params, grad, m, v, 4 * q0, n, vec, pg * c, pm, pv, pp, bc1, bc2, decay, hp, bad, bad_state);
+    for (int64_t qd = q0 + stride; qd < quads; qd += stride) {
         const int64_t i = 4 * qd;
-        const bool first = qd == q0;
-        const f32x4 g4 = (first ? pg : ld4(grad, i, n, vec)) * c;
-        f32x4 m4 = first ? pm : ld4(m, i, n, vec), v4 = first ? pv : ld4(v, i, n, vec);
-        f32x4 p4 = first ? pp : ld4(params, i, n, vec);
-        st4(grad, i, n, vec, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float g = g4[e];
-            if (!isfinite(g)) { bad |= (i + e < n); continue; }
-            const float mi = hp.beta1 * m4[e] + (1.f - hp.beta1) * g;
-            const float vi = hp.beta2 * v4[e] + (1.f - hp.beta2) * g * g;
-            const float mh = mi / bc1, vh = vi / bc2;
-            float p = p4[e];
-            if (hp.weight_decay != 0.f) p *= decay;
-            p -= hp.lr * mh / (sqrtf(vh) + hp.eps);
-            if (hp.clamp > 0.f) p = fminf(fmaxf(p, -hp.clamp), hp.clamp);
-            p4[e] = p;
-            m4[e] = mi;
-            v4[e] = vi;
-            bad_state |= (i + e < n) && !(isfinite(p) && isfinite(mi) && isfinite(vi));
-        }
-        st4(params, i, n, vec, p4);
-        st4(m, i, n, vec, m4);
-        st4(v, i, n, vec, v4);
+        adam_flat_quad(params, grad, m, v, i, n, vec, ld4(grad, i, n, vec4) * c, ld4(m, i, n, vec4),
+                       ld4(v, i, n, vec4), ld4(params, i, n, vec4), bc1, bc2, decay, hp, bad, bad_state);
     }
+    // (stored last: a wave would wait for this store at its next use of a load)
+    if (bx == 0 && threadIdx.x == 0 && out_norm) *out_norm = nrm;
     if (bad) set_flag(flags, 0x1);
     if (bad_state) set_flag(flags, 0x8);
 }

@@ -41,13 +41,24 @@ IQLH_DEV void iql_reduce_block(const float* __restrict__ part, const float* __re
     const int tid = threadIdx.x, q = tid % kRedLanes, sl = tid / kRedLanes;
     const int64_t p0 = (int64_t)bx * kRedParams + 4 * q;  // < Pp
     const float* src = part + (int64_t)g * nwg * Pp + p0;
-    // block 0's share of the loss partials, issued with the gradient loads
-    float l = 0.f;
-    if (bx == 0)
-        for (int w = tid; w < nloss; w += 256) l += loss_part[(int64_t)g * nloss + w];
+    // block 0's share of the loss partials: the first one issued with the
+    // gradient loads (at a clamped index, nloss >= 1, so that no lane-dependent
+    // branch makes the gradient loads wait for it), any others after them
+    // (block 0 also loads the old step counts here, by every thread)
+    float l0 = 0.f;
+    int32_t t_old = 0;
+    int64_t step_old = 0;
+    if (bx == 0) {
+        l0 = loss_part[(int64_t)g * nloss + (tid < nloss ? tid : nloss - 1)];
+        t_old = tcount[g];
+        if (g == 0) step_old = *step;
+    }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
     for (int w = sl; w < nwg; w += kRedSlices) acc += *(const f32x4*)(src + (int64_t)w * Pp);
+    float l = 0.f + keep_if(tid < nloss, l0);
+    if (bx == 0)
+        for (int w = tid + 256; w < nloss; w += 256) l += loss_part[(int64_t)g * nloss + w];
     red[sl][q] = acc;
     __syncthreads();
     float sq = 0.f;
@@ -71,8 +82,8 @@ IQLH_DEV void iql_reduce_block(const float* __restrict__ part, const float* __re
             const float loss = l * invB;
             if (out_loss) out_loss[g] = loss;
             if (!isfinite(loss)) set_flag(flags, 0x4);
-            tcount[g] += 1;
-            if (g == 0) *step += 1;
+            tcount[g] = t_old + 1;
+            if (g == 0) *step = step_old + 1;
         }
     }
 }
@@ -99,18 +110,44 @@ IQLH_DEV bool adam_elem(float gi, float& p, float& m, float& v, float bc1, float
     return true;
 }
 
-// Operand-typed shadows of flat parameter i of one group.
+// Operand-typed shadows of flat parameter i of one group (a group has fewer
+// than 2^31 parameters, so the row / column split is a 32-bit division).
 template <typename T>
 IQLH_DEV void iql_store_shadow(int64_t i, float p, int H, int S, int SP, T* w1s, T* w2s, T* w2ts) {
     const int64_t ow2 = (int64_t)H * S + H, ow2e = ow2 + (int64_t)H * H;
     if (i < (int64_t)H * S) {
-        const int64_t r = i / S, cc = i - r * S;
-        w1s[r * SP + cc] = to_shadow<T>(p);
+        const uint32_t r = (uint32_t)i / (uint32_t)S, cc = (uint32_t)i - r * (uint32_t)S;
+        w1s[(int64_t)r * SP + cc] = to_shadow<T>(p);
     } else if (i >= ow2 && i < ow2e) {
-        const int64_t q = i - ow2, r = q / H, cc = q - r * H;
+        const uint32_t q = (uint32_t)(i - ow2), r = q / (uint32_t)H, cc = q - r * (uint32_t)H;
         w2s[q] = to_shadow<T>(p);
         w2ts[cc * H + r] = to_shadow<T>(p);
     }
+}
+
+// One parameter of iql_adam_block from its loaded state (gradient already
+// clipped): Adam, the fused target update and the shadows, then every store.
+// The stores come after the arithmetic, so no store sits between a load and
+// its use (the use would wait for the store too).
+template <typename T>
+IQLH_DEV void iql_adam_param(int64_t i, float gi, float p, float mi, float vi, float ti, float bc1, float bc2,
+                             float decay, const AdamHyper& hp, int H, int S, int SP, float* __restrict__ prm,
+                             float* __restrict__ gr, float* __restrict__ m, float* __restrict__ v,
+                             float* __restrict__ tg, T* w1s, T* w2s, T* w2ts, bool& bad, bool& bad_state) {
+    const bool ok = adam_elem(gi, p, mi, vi, bc1, bc2, decay, hp);
+    gr[i] = 0.f;
+    if (ok) {
+        prm[i] = p;
+        m[i] = mi;
+        v[i] = vi;
+        bad_state |= !(isfinite(p) && isfinite(mi) && isfinite(vi));
+    } else {
+        bad = true;
+    }
+    // Polyak target with the step's parameters (unchanged ones when the
+    // update was skipped): target += ema (p - target)
+    if (hp.ema > 0.f) tg[i] = fmaf(hp.ema, p - ti, ti);
+    iql_store_shadow<T>(i, p, H, S, SP, w1s, w2s, w2ts);
 }
 
 // Clip and Adam over the parameters of group g, block bx of nbx; refreshes
@@ -130,44 +167,29 @@ IQLH_DEV void iql_adam_block(const IqlDims& d, const IqlBuffers& b, const AdamHy
     T* w1s = (T*)b.w1s + (int64_t)g * H * SP;
     T* w2s = (T*)b.w2s + (int64_t)g * H * H;
     T* w2ts = (T*)b.w2ts + (int64_t)g * H * H;
-    // the first element's state does not depend on the norm: load it before
-    // folding the partials
-    const int64_t i0 = (int64_t)bx * 256 + threadIdx.x;
-    float pg = 0.f, pp = 0.f, pm = 0.f, pv = 0.f;
-    if (i0 < P) {
-        pg = gr[i0];
-        pp = prm[i0];
-        pm = m[i0];
-        pv = v[i0];
-    }
+    // The first element's state does not depend on the norm: it is loaded
+    // before the fold, at a clamped index (P >= 1) so that no lane-dependent
+    // branch surrounds the loads.
+    const int64_t i0 = (int64_t)bx * 256 + threadIdx.x, stride = (int64_t)nbx * 256;
+    const int64_t j0 = i0 < P ? i0 : P - 1;
+    const float pg = gr[j0], pp = prm[j0], pm = m[j0], pv = v[j0], pt = tg[j0];
     const float tt = (float)b.t[g];
     float a = 0.f;
     for (int i = threadIdx.x; i < rb; i += 256) a += b.sq_part[(int64_t)g * rb + i];
     const float nrm = sqrtf(block_sum<256>(a, red));
-    if (bx == 0 && threadIdx.x == 0 && out_gnorm) out_gnorm[g] = nrm;
     const float c = !isfinite(nrm) ? __int_as_float(0x7FC00000)
                                    : ((nrm > hp.max_grad_norm && nrm > 0.f) ? hp.max_grad_norm / nrm : 1.f);
     const float bc1 = 1.f - powf(hp.beta1, tt), bc2 = 1.f - powf(hp.beta2, tt);
     const float decay = 1.f - hp.lr * hp.weight_decay;
     bool bad = false, bad_state = false;
-    for (int64_t i = i0; i < P; i += (int64_t)nbx * 256) {
-        const bool first = i == i0;
-        const float gi = (first ? pg : gr[i]) * c;
-        gr[i] = 0.f;
-        float p = first ? pp : prm[i], mi = first ? pm : m[i], vi = first ? pv : v[i];
-        if (adam_elem(gi, p, mi, vi, bc1, bc2, decay, hp)) {
-            prm[i] = p;
-            m[i] = mi;
-            v[i] = vi;
-            bad_state |= !(isfinite(p) && isfinite(mi) && isfinite(vi));
-        } else {
-            bad = true;
-        }
-        // Polyak target with the step's parameters (unchanged ones when the
-        // update was skipped): target += ema (p - target)
-        if (hp.ema > 0.f) tg[i] = fmaf(hp.ema, p - tg[i], tg[i]);
-        iql_store_shadow<T>(i, p, H, S, SP, w1s, w2s, w2ts);
-    }
+    if (i0 < P)
+        iql_adam_param<T>(i0, pg * c, pp, pm, pv, pt, bc1, bc2, decay, hp, H, S, SP, prm, gr, m, v, tg, w1s, w2s,
+                          w2ts, bad, bad_state);
+    for (int64_t i = i0 + stride; i < P; i += stride)
+        iql_adam_param<T>(i, gr[i] * c, prm[i], m[i], v[i], tg[i], bc1, bc2, decay, hp, H, S, SP, prm, gr, m, v, tg,
+                          w1s, w2s, w2ts, bad, bad_state);
+    // (stored last: a wave would wait for this store at its next use of a load)
+    if (bx == 0 && threadIdx.x == 0 && out_gnorm) out_gnorm[g] = nrm;
     if (bad) set_flag(b.flags, 0x1);
     if (bad_state) set_flag(b.flags, 0x8);
 }
