@@ -147,6 +147,7 @@ int iql_create(const iqlh_config* cfg, const float* init_params_host, iql_handle
         {(void**)&b.grad, sizeof(float) * G * P},
         {(void**)&b.target, sizeof(float) * G * P},
         {(void**)&b.t, sizeof(int32_t) * G},
+        {(void**)&b.bc, sizeof(float) * G * 2},
         {(void**)&b.step, sizeof(int64_t)},
         {(void**)&b.flags, sizeof(int32_t)},
         {(void**)&b.w1s, esz * G * H * d.S_pad},
@@ -527,7 +528,8 @@ int grad_budget_workspace_bytes(int64_t n, int32_t num_sources, size_t* bytes) {
     if (num_sources < 1 || num_sources > kMaxSources)
         return fail(IQLH_EINVAL, "num_sources must be in [1, %d]", kMaxSources);
     const int nb = budget_num_blocks(n);
-    *bytes = sizeof(float) * (size_t)(num_sources + 1) * nb;
+    // [k][nb] source partials, [nb] combined partials, 2 Adam bias corrections
+    *bytes = sizeof(float) * ((size_t)(num_sources + 1) * nb + 2);
     return IQLH_OK;
 }
 

@@ -34,13 +34,18 @@ __global__ __launch_bounds__(kBT) void budget_norms_kernel(SourceSet s, int64_t 
     norms_block(s, n, vec, partials, blockIdx.x, gridDim.x);
 }
 
+// Blocks 0 .. nb - 1 run pass 2; with an Adam update, block nb counts its step.
 __global__ __launch_bounds__(kBT) void budget_saxpy_kernel(SourceSet s, int64_t n, int vec, float mgn,
                                                             const float* __restrict__ partials,
                                                             float* __restrict__ grad,
                                                             float* __restrict__ gpart,
-                                                            float* __restrict__ out_norms,
-                                                            int32_t* __restrict__ adam_t) {
-    saxpy_block(s, n, vec, mgn, partials, grad, gpart, out_norms, adam_t, blockIdx.x, gridDim.x);
+                                                            float* __restrict__ out_norms, int nb,
+                                                            int32_t* __restrict__ adam_t, float* __restrict__ bc,
+                                                            float beta1, float beta2) {
+    if ((int)blockIdx.x < nb)
+        saxpy_block(s, n, vec, mgn, partials, grad, gpart, out_norms, blockIdx.x, nb);
+    else
+        adam_count_block(adam_t, bc, beta1, beta2);
 }
 
 __global__ __launch_bounds__(kBT) void norm_finalize_kernel(const float* __restrict__ p, int nb,
@@ -50,21 +55,21 @@ __global__ __launch_bounds__(kBT) void norm_finalize_kernel(const float* __restr
 
 __global__ __launch_bounds__(kBT) void adam_flat_kernel(float* __restrict__ params, float* __restrict__ grad,
                                                          float* __restrict__ m, float* __restrict__ v,
-                                                         const int32_t* __restrict__ tptr,
+                                                         const float* __restrict__ bc,
                                                          const float* __restrict__ sq_part, int nb, int64_t n,
                                                          int vec, AdamHyper hp, float* __restrict__ out_norm,
                                                          int32_t* __restrict__ flags) {
-    adam_flat_block(params, grad, m, v, tptr, sq_part, nb, n, vec, hp, out_norm, flags, blockIdx.x, gridDim.x);
+    adam_flat_block(params, grad, m, v, bc, sq_part, nb, n, vec, hp, out_norm, flags, blockIdx.x, gridDim.x);
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-hipError_t launch_adam_flat(float* params, float* grad, float* m, float* v, const int32_t* t,
+hipError_t launch_adam_flat(float* params, float* grad, float* m, float* v, const float* bc,
                             const float* sq_partials, int nb, int64_t n, const AdamHyper& hp,
                             float* out_norm, int32_t* flags, hipStream_t stream) {
     const int blocks = budget_num_blocks(n);
     const int vec = aligned16(params) && aligned16(grad) && aligned16(m) && aligned16(v);
-    hipLaunchKernelGGL(adam_flat_kernel, dim3(blocks), dim3(kBT), 0, stream, params, grad, m, v, t,
+    hipLaunchKernelGGL(adam_flat_kernel, dim3(blocks), dim3(kBT), 0, stream, params, grad, m, v, bc,
                        sq_partials, nb, n, vec, hp, out_norm, flags);
     return hipGetLastError();
 }
@@ -75,14 +80,15 @@ hipError_t launch_budget(float* grad, const SourceSet& s, int64_t n, float mgn, 
     const int nb = budget_num_blocks(n);
     float* partials = work;
     float* gpart = work + (int64_t)s.k * nb;
+    float* bc = gpart + nb;
     int vec = aligned16(grad);
     for (int j = 0; j < s.k; ++j) vec = vec && aligned16(s.ptr[j]);
     hipLaunchKernelGGL(budget_norms_kernel, dim3(nb), dim3(kBT), 0, stream, s, n, vec, partials);
-    hipLaunchKernelGGL(budget_saxpy_kernel, dim3(nb), dim3(kBT), 0, stream, s, n, vec, mgn, partials,
-                       grad, gpart, out_norms, hp ? t : (int32_t*)nullptr);
+    hipLaunchKernelGGL(budget_saxpy_kernel, dim3(nb + (hp ? 1 : 0)), dim3(kBT), 0, stream, s, n, vec, mgn,
+                       partials, grad, gpart, out_norms, nb, t, bc, hp ? hp->beta1 : 0.f, hp ? hp->beta2 : 0.f);
     if (hp) {
         float* comb = out_norms ? out_norms + s.k : nullptr;
-        return launch_adam_flat(params, grad, m, v, t, gpart, nb, n, *hp, comb, flags, stream);
+        return launch_adam_flat(params, grad, m, v, bc, gpart, nb, n, *hp, comb, flags, stream);
     }
     if (out_norms)
         hipLaunchKernelGGL(norm_finalize_kernel, dim3(1), dim3(kBT), 0, stream, gpart, nb,

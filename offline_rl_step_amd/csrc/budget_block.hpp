@@ -139,8 +139,8 @@ IQLH_DEV float adam_clip(float norm, float max_norm) {
 // Pass 2 for block bx of nb: clip scales, grad = sum_k c_k s_k, and the
 // block's partial of ||grad||^2.
 IQLH_DEV void saxpy_block(const SourceSet& s, int64_t n, int vec, float mgn, const float* __restrict__ partials,
-                          float* __restrict__ grad, float* __restrict__ gpart, float* __restrict__ out_norms,
-                          int32_t* __restrict__ adam_t, int bx, int nb) {
+                          float* __restrict__ grad, float* __restrict__ gpart, float* __restrict__ out_norms, int bx,
+                          int nb) {
     __shared__ float red[kBT / kWave];
     __shared__ float redk[kMaxSources][kBT / kWave];
     // this thread's first quad of every source does not depend on the clip
@@ -155,9 +155,6 @@ IQLH_DEV void saxpy_block(const SourceSet& s, int64_t n, int vec, float mgn, con
 #pragma unroll
     for (int j = 0; j < kMaxSources; ++j)
         pre[j] = (j < s.k && quads > 0) ? ld4(s.ptr[j], 4 * c0, n, vec4) : f32x4{0.f, 0.f, 0.f, 0.f};
-    // block 0 bumps the Adam step count at its end; the old count is loaded
-    // now, by every thread (one address), with the other loads
-    const int32_t t_old = (bx == 0 && adam_t) ? *adam_t : 0;
     // every thread folds every source's partials (same value in all threads
     // and blocks) and derives the clip scales itself
     float c[kMaxSources], nrm[kMaxSources];
@@ -191,15 +188,25 @@ IQLH_DEV void saxpy_block(const SourceSet& s, int64_t n, int vec, float mgn, con
     }
     const float t = block_sum<kBT>(acc, red);
     if (threadIdx.x == 0) gpart[bx] = t;
-    // block 0's other outputs last: a store issued earlier would make the
-    // wave's next wait for a load wait for it as well
-    if (bx == 0 && threadIdx.x == 0) {
-        if (out_norms) {
+    // block 0's norms last: a store issued earlier would make the wave's next
+    // wait for a load wait for it as well
+    if (bx == 0 && threadIdx.x == 0 && out_norms) {
 #pragma unroll
-            for (int j = 0; j < kMaxSources; ++j)
-                if (j < s.k) out_norms[j] = nrm[j];
-        }
-        if (adam_t) *adam_t = t_old + 1;
+        for (int j = 0; j < kMaxSources; ++j)
+            if (j < s.k) out_norms[j] = nrm[j];
+    }
+}
+
+// The Adam step count of a pass-3 update: one thread increments t and stores
+// the bias corrections 1 - beta1^t, 1 - beta2^t of the new count for the
+// update blocks, so that they are computed once rather than by every wave.
+// Runs in the launch before the update, in a block of its own.
+IQLH_DEV void adam_count_block(int32_t* __restrict__ t, float* __restrict__ bc, float beta1, float beta2) {
+    if (threadIdx.x == 0) {
+        const int32_t tn = *t + 1;
+        *t = tn;
+        bc[0] = 1.f - powf(beta1, (float)tn);
+        bc[1] = 1.f - powf(beta2, (float)tn);
     }
 }
 
@@ -244,7 +251,7 @@ IQLH_DEV void adam_flat_quad(float* __restrict__ params, float* __restrict__ gra
 // Pass 3 for block bx of nbx: folds the nb grad partials into the norm and
 // applies the clipped Adam update to the block's quads, zeroing grad.
 IQLH_DEV void adam_flat_block(float* __restrict__ params, float* __restrict__ grad, float* __restrict__ m,
-                              float* __restrict__ v, const int32_t* __restrict__ tptr,
+                              float* __restrict__ v, const float* __restrict__ bcp,
                               const float* __restrict__ sq_part, int nb, int64_t n, int vec,
                               const AdamHyper& hp, float* __restrict__ out_norm, int32_t* __restrict__ flags,
                               int bx, int nbx) {
@@ -260,12 +267,10 @@ IQLH_DEV void adam_flat_block(float* __restrict__ params, float* __restrict__ gr
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
     const f32x4 pg = any ? ld4(grad, 4 * c0, n, vec4) : z4, pm = any ? ld4(m, 4 * c0, n, vec4) : z4;
     const f32x4 pv = any ? ld4(v, 4 * c0, n, vec4) : z4, pp = any ? ld4(params, 4 * c0, n, vec4) : z4;
+    const float bc1 = bcp[0], bc2 = bcp[1];
     const float sq = fold_partials(sq_part, nb, red);
     const float nrm = sqrtf(sq);
     const float c = adam_clip(nrm, hp.max_grad_norm);
-    const float tt = (float)(*tptr);
-    const float bc1 = 1.f - powf(hp.beta1, tt);
-    const float bc2 = 1.f - powf(hp.beta2, tt);
     const float decay = 1.f - hp.lr * hp.weight_decay;
     bool bad = false, bad_state = false;
     if (q0 < quads)

@@ -507,15 +507,20 @@ __global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
     }
 }
 
+// Blocks 0 .. rb - 1 of each group reduce; block rb updates its counters.
 __global__ __launch_bounds__(256) void iql_reduce_kernel(const float* __restrict__ part,
                                                          const float* __restrict__ loss_part, int nwg, int nloss,
                                                          int64_t P, int64_t Pp, float invB,
                                                          float* __restrict__ grad, float* __restrict__ sq_part,
                                                          int rb, int32_t* __restrict__ tcount,
-                                                         int64_t* __restrict__ step, float* __restrict__ out_loss,
+                                                         int64_t* __restrict__ step, float* __restrict__ bc,
+                                                         float beta1, float beta2, float* __restrict__ out_loss,
                                                          int32_t* __restrict__ flags) {
-    iql_reduce_block(part, loss_part, nwg, nloss, P, Pp, invB, grad, sq_part, rb, tcount, step, out_loss, flags,
-                     blockIdx.x, blockIdx.y);
+    if ((int)blockIdx.x < rb)
+        iql_reduce_block(part, loss_part, nwg, nloss, P, Pp, invB, grad, sq_part, rb, out_loss, flags, blockIdx.x,
+                         blockIdx.y);
+    else
+        iql_count_block(tcount, step, bc, beta1, beta2, blockIdx.y);
 }
 
 template <typename T>
@@ -1421,9 +1426,9 @@ hipError_t launch_iql_update(const IqlDims& d, const IqlBuffers& b, const AdamHy
     int nwg, nloss;
     if (!iql_partial_counts(d, B, &nwg, &nloss)) return hipErrorInvalidValue;
     const int rb = iql_reduce_blocks(d.P);
-    hipLaunchKernelGGL(iql_reduce_kernel, dim3(rb, d.G), dim3(256), 0, stream, b.part, b.loss_part,
-                       nwg, nloss, d.P, d.Pp, 1.f / (float)B, b.grad, b.sq_part, rb, b.t, b.step,
-                       out_loss, b.flags);
+    hipLaunchKernelGGL(iql_reduce_kernel, dim3(rb + 1, d.G), dim3(256), 0, stream, b.part, b.loss_part,
+                       nwg, nloss, d.P, d.Pp, 1.f / (float)B, b.grad, b.sq_part, rb, b.t, b.step, b.bc,
+                       hp.beta1, hp.beta2, out_loss, b.flags);
     const int ab = iql_adam_blocks(d.P);
     if (d.dtype == 1)
         hipLaunchKernelGGL(iql_adam_kernel<uint16_t>, dim3(ab, d.G), dim3(256), 0, stream, d, b, hp,

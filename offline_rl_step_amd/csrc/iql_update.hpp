@@ -22,7 +22,7 @@ template <> IQLH_DEV uint16_t to_shadow<uint16_t>(float x) {
 // Sums the per-workgroup partials of every parameter in a fixed order (slice
 // sl of a block adds workgroups sl, sl + 8, ... in turn; the eight slice sums
 // are then added in slice order), writes grad and per-block sums of squares,
-// and, in block 0, the mean loss and the t / step-counter increments.  Each
+// and, in block 0, the mean loss.  Each
 // thread streams float4 quads of four parameters, so a wave keeps many
 // independent 16-byte loads in flight (unrolling further measured no faster:
 // the read runs at the chip's streaming rate).
@@ -33,8 +33,7 @@ constexpr int kRedParams = 4 * kRedLanes;     // parameters per block (divides 1
 // Block bx (of rb per group) of group g.
 IQLH_DEV void iql_reduce_block(const float* __restrict__ part, const float* __restrict__ loss_part, int nwg,
                                int nloss, int64_t P, int64_t Pp, float invB, float* __restrict__ grad,
-                               float* __restrict__ sq_part, int rb, int32_t* __restrict__ tcount,
-                               int64_t* __restrict__ step, float* __restrict__ out_loss,
+                               float* __restrict__ sq_part, int rb, float* __restrict__ out_loss,
                                int32_t* __restrict__ flags, int bx, int g) {
     __shared__ f32x4 red[kRedSlices][kRedLanes];
     __shared__ float wred[4];
@@ -44,15 +43,8 @@ IQLH_DEV void iql_reduce_block(const float* __restrict__ part, const float* __re
     // block 0's share of the loss partials: the first one issued with the
     // gradient loads (at a clamped index, nloss >= 1, so that no lane-dependent
     // branch makes the gradient loads wait for it), any others after them
-    // (block 0 also loads the old step counts here, by every thread)
     float l0 = 0.f;
-    int32_t t_old = 0;
-    int64_t step_old = 0;
-    if (bx == 0) {
-        l0 = loss_part[(int64_t)g * nloss + (tid < nloss ? tid : nloss - 1)];
-        t_old = tcount[g];
-        if (g == 0) step_old = *step;
-    }
+    if (bx == 0) l0 = loss_part[(int64_t)g * nloss + (tid < nloss ? tid : nloss - 1)];
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
     for (int w = sl; w < nwg; w += kRedSlices) acc += *(const f32x4*)(src + (int64_t)w * Pp);
@@ -82,9 +74,22 @@ IQLH_DEV void iql_reduce_block(const float* __restrict__ part, const float* __re
             const float loss = l * invB;
             if (out_loss) out_loss[g] = loss;
             if (!isfinite(loss)) set_flag(flags, 0x4);
-            tcount[g] = t_old + 1;
-            if (g == 0) *step = step_old + 1;
         }
+    }
+}
+
+// The counters of group g's update, in a block of its own in the reduction's
+// launch: t[g] and (group 0) the step counter are incremented, and the Adam
+// bias corrections 1 - beta1^t, 1 - beta2^t of the new t are stored for the
+// update blocks, which would otherwise each compute them in every wave.
+IQLH_DEV void iql_count_block(int32_t* __restrict__ tcount, int64_t* __restrict__ step, float* __restrict__ bc,
+                              float beta1, float beta2, int g) {
+    if (threadIdx.x == 0) {
+        const int32_t tn = tcount[g] + 1;
+        tcount[g] = tn;
+        if (g == 0) *step += 1;
+        bc[2 * g] = 1.f - powf(beta1, (float)tn);
+        bc[2 * g + 1] = 1.f - powf(beta2, (float)tn);
     }
 }
 
@@ -173,13 +178,12 @@ IQLH_DEV void iql_adam_block(const IqlDims& d, const IqlBuffers& b, const AdamHy
     const int64_t i0 = (int64_t)bx * 256 + threadIdx.x, stride = (int64_t)nbx * 256;
     const int64_t j0 = i0 < P ? i0 : P - 1;
     const float pg = gr[j0], pp = prm[j0], pm = m[j0], pv = v[j0], pt = tg[j0];
-    const float tt = (float)b.t[g];
+    const float bc1 = b.bc[2 * g], bc2 = b.bc[2 * g + 1];
     float a = 0.f;
     for (int i = threadIdx.x; i < rb; i += 256) a += b.sq_part[(int64_t)g * rb + i];
     const float nrm = sqrtf(block_sum<256>(a, red));
     const float c = !isfinite(nrm) ? __int_as_float(0x7FC00000)
                                    : ((nrm > hp.max_grad_norm && nrm > 0.f) ? hp.max_grad_norm / nrm : 1.f);
-    const float bc1 = 1.f - powf(hp.beta1, tt), bc2 = 1.f - powf(hp.beta2, tt);
     const float decay = 1.f - hp.lr * hp.weight_decay;
     bool bad = false, bad_state = false;
     if (i0 < P)

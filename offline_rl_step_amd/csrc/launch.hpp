@@ -77,9 +77,10 @@ hipError_t launch_budget(float* grad, const SourceSet& s, int64_t n, float mgn,
                          int32_t* flags, const AdamHyper* hp, float* work, hipStream_t stream);
 
 // Flat clipped Adam over n elements whose gradient L2 norm is the fixed-order
-// sum of `nb` partial sums of squares.  Zeroes grad.  `t` was already
-// incremented.  out_norm (nullable) receives the pre-clip norm.
-hipError_t launch_adam_flat(float* params, float* grad, float* m, float* v, const int32_t* t,
+// sum of `nb` partial sums of squares.  Zeroes grad.  bc holds the bias
+// corrections 1 - beta1^t, 1 - beta2^t of the already incremented step count
+// t.  out_norm (nullable) receives the pre-clip norm.
+hipError_t launch_adam_flat(float* params, float* grad, float* m, float* v, const float* bc,
                             const float* sq_partials, int nb, int64_t n, const AdamHyper& hp,
                             float* out_norm, int32_t* flags, hipStream_t stream);
 
@@ -100,6 +101,7 @@ struct IqlBuffers {
     float* grad;      // [G][P]
     float* target;    // [G][P] Polyak (EMA) target copy of params
     int32_t* t;       // [G]
+    float* bc;        // [G][2] Adam bias corrections 1 - beta1^t, 1 - beta2^t for the current t
     int64_t* step;    // [1]
     int32_t* flags;   // [1]
     void* w1s;        // [G][H][S_pad]   operand-typed shadow of W1 (zero padded)

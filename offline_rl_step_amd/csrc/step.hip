@@ -12,7 +12,8 @@
 //   B  fused V forward/backward and advantage-weighted policy (with the 16-wave
 //      kernel also the HER rows that form the batch tail from a 128-row
 //      boundary and the budget norms, so that A is not launched)
-//   C  IQL: fixed-order sum of the workgroup partials | budget: clip + SAXPY
+//   C  IQL: fixed-order sum of the workgroup partials | budget: clip + SAXPY |
+//      the step counts and Adam bias corrections of both updates
 //   D  IQL: clip + Adam + shadows | budget: clip + Adam (or the norm only)
 // Results are bit-for-bit those of the separate launches: every block runs
 // the same block function with the same block index and count.
@@ -38,10 +39,11 @@ struct ReducePart {
     float* sq_part;
     int32_t* tcount;
     int64_t* step;
+    float* bc;
     float* out_loss;
     int32_t* flags;
     int64_t P, Pp;
-    float invB;
+    float invB, beta1, beta2;
     int nwg, nloss, rb, G;
 };
 struct SaxpyPart {
@@ -51,21 +53,28 @@ struct SaxpyPart {
     float* grad;
     float* gpart;
     float* out_norms;
-    int32_t* adam_t;
-    float mgn;
+    int32_t* adam_t;  // null: no Adam update, no counter block
+    float* bc;
+    float mgn, beta1, beta2;
     int vec, nb;
 };
 
-// The budget's SAXPY blocks come first: their chain of dependent loads is
-// longer than the reduction's streaming, and blocks are dispatched in order.
+// Blocks: the budget's SAXPY blocks first (their chain of dependent loads is
+// longer than the reduction's streaming, and blocks are dispatched in order),
+// the reduction's, one counter block per trainer, then the budget's counter
+// block when it updates with Adam.
 __global__ __launch_bounds__(256) void step_reduce_saxpy_kernel(ReducePart r, SaxpyPart x) {
-    const int bx = blockIdx.x;
+    const int bx = blockIdx.x, nr = r.rb * r.G;
     if (bx < x.nb) {
-        saxpy_block(x.s, x.n, x.vec, x.mgn, x.partials, x.grad, x.gpart, x.out_norms, x.adam_t, bx, x.nb);
-    } else {
+        saxpy_block(x.s, x.n, x.vec, x.mgn, x.partials, x.grad, x.gpart, x.out_norms, bx, x.nb);
+    } else if (bx < x.nb + nr) {
         const int br = bx - x.nb;
         iql_reduce_block(r.part, r.loss_part, r.nwg, r.nloss, r.P, r.Pp, r.invB, r.grad, r.sq_part, r.rb,
-                         r.tcount, r.step, r.out_loss, r.flags, br % r.rb, br / r.rb);
+                         r.out_loss, r.flags, br % r.rb, br / r.rb);
+    } else if (bx < x.nb + nr + r.G) {
+        iql_count_block(r.tcount, r.step, r.bc, r.beta1, r.beta2, bx - x.nb - nr);
+    } else {
+        adam_count_block(x.adam_t, x.bc, x.beta1, x.beta2);
     }
 }
 
@@ -74,7 +83,7 @@ struct FlatPart {
     float* grad;
     float* m;
     float* v;
-    const int32_t* t;
+    const float* bc;
     const float* gpart;
     float* out_norm;
     int32_t* flags;
@@ -91,7 +100,7 @@ __global__ __launch_bounds__(256) void step_adam_kernel(IqlDims d, IqlBuffers b,
     if (bx < na) {
         iql_adam_block<T>(d, b, hp, out_gnorm, rb, bx % ab, bx / ab, ab);
     } else if (f.params) {
-        adam_flat_block(f.params, f.grad, f.m, f.v, f.t, f.gpart, f.nb, f.n, f.vec, f.hp, f.out_norm, f.flags,
+        adam_flat_block(f.params, f.grad, f.m, f.v, f.bc, f.gpart, f.nb, f.n, f.vec, f.hp, f.out_norm, f.flags,
                         bx - na, f.nb);
     } else {
         norm_finalize_block(f.gpart, f.nb, f.out_norm);
@@ -121,9 +130,11 @@ hipError_t launch_aux_step(const IqlDims& d, const IqlBuffers& b, const AdamHype
     int vec = 0;
     float* partials = nullptr;
     float* gpart = nullptr;
+    float* bud_bc = nullptr;
     if (bud) {
         partials = bud->work;
         gpart = bud->work + (int64_t)bud->s.k * nb;
+        bud_bc = gpart + nb;
         vec = al16(bud->grad);
         for (int j = 0; j < bud->s.k; ++j) vec = vec && al16(bud->s.ptr[j]);
     }
@@ -165,13 +176,14 @@ hipError_t launch_aux_step(const IqlDims& d, const IqlBuffers& b, const AdamHype
 
     // C: reduce + SAXPY
     const int rb = iql_reduce_blocks(d.P);
-    ReducePart rp{b.part, b.loss_part, b.grad, b.sq_part, b.t, b.step, out_loss, b.flags, d.P, d.Pp,
-                  1.f / (float)B, nwg, nloss, rb, d.G};
+    ReducePart rp{b.part, b.loss_part, b.grad, b.sq_part, b.t, b.step, b.bc, out_loss, b.flags, d.P, d.Pp,
+                  1.f / (float)B, hp.beta1, hp.beta2, nwg, nloss, rb, d.G};
     SaxpyPart sp{};
     if (bud)
         sp = SaxpyPart{bud->s, bud->n, partials, bud->grad, gpart, bud->out_norms,
-                       flat_adam ? bud->t : (int32_t*)nullptr, bud->mgn, vec, nb};
-    STEP_LAUNCH(step_reduce_saxpy_kernel, rb * d.G + nb, ev ? ev + 4 : nullptr, rp, sp);
+                       flat_adam ? bud->t : (int32_t*)nullptr, bud_bc, bud->mgn,
+                       flat_adam ? bud->hp.beta1 : 0.f, flat_adam ? bud->hp.beta2 : 0.f, vec, nb};
+    STEP_LAUNCH(step_reduce_saxpy_kernel, nb + rb * d.G + d.G + (flat_adam ? 1 : 0), ev ? ev + 4 : nullptr, rp, sp);
 
     // D: both Adam updates
     const int ab = iql_adam_blocks(d.P);
@@ -179,7 +191,7 @@ hipError_t launch_aux_step(const IqlDims& d, const IqlBuffers& b, const AdamHype
     int extra = 0;
     if (flat_adam) {
         const int fvec = al16(bud->grad) && al16(bud->params) && al16(bud->m) && al16(bud->v);
-        fp = FlatPart{bud->params, bud->grad, bud->m, bud->v, bud->t, gpart,
+        fp = FlatPart{bud->params, bud->grad, bud->m, bud->v, bud_bc, gpart,
                       bud->out_norms ? bud->out_norms + bud->s.k : nullptr, bud->flags, bud->hp, bud->n, fvec, nb};
         extra = nb;
     } else if (bud && bud->out_norms) {
