@@ -771,7 +771,17 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int sg = wv >> 1, fh = wv & 1, fb = 64 * fh;
-    const int g = blockIdx.y, wg = blockIdx.x;
+    // HER tiles first (they carry the longer prologue), the trainers
+    // interleaved; the tile order of the partials is unchanged
+    int g, wg;
+    {
+        const int G = (int)gridDim.y, L = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+        const int h0 = a.her_on ? a.her_row0 / BT : a.nwg, nh = a.nwg - h0;
+        if (L < G * nh) { wg = h0 + L / G; g = L % G; }
+        else { wg = (L - G * nh) / G; g = (L - G * nh) % G; }
+        g = __builtin_amdgcn_readfirstlane(g);
+        wg = __builtin_amdgcn_readfirstlane(wg);
+    }
     const int S = a.S, B = a.B;
     const POff po(S, H);
     const float* prm = a.params + (int64_t)g * a.P;
