@@ -771,14 +771,21 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int sg = wv >> 1, fh = wv & 1, fb = 64 * fh;
-    // HER tiles first (they carry the longer prologue), the trainers
-    // interleaved; the tile order of the partials is unchanged
+    // HER tiles first (they carry the longer prologue).  Within each range,
+    // runs of 8 tiles take 8 G consecutive blocks, trainer-major, so the G
+    // workgroups of a tile are 8 blocks apart: a launch sends block i to XCD
+    // i mod 8, and they share that XCD's L2 for the rows they both read.  The
+    // tile order of the partials is unchanged.
     int g, wg;
     {
         const int G = (int)gridDim.y, L = (int)(blockIdx.y * gridDim.x + blockIdx.x);
         const int h0 = a.her_on ? a.her_row0 / BT : a.nwg, nh = a.nwg - h0;
-        if (L < G * nh) { wg = h0 + L / G; g = L % G; }
-        else { wg = (L - G * nh) / G; g = (L - G * nh) % G; }
+        const bool in_her = L < G * nh;
+        const int t0 = in_her ? h0 : 0, n = in_her ? nh : h0, h = in_her ? L : L - G * nh;
+        const int run = h / (8 * G), r = h % (8 * G);
+        const int nr = min(8, n - 8 * run);  // tiles in this run
+        g = r / nr;
+        wg = t0 + 8 * run + r % nr;
         g = __builtin_amdgcn_readfirstlane(g);
         wg = __builtin_amdgcn_readfirstlane(wg);
     }
