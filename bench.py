@@ -23,7 +23,8 @@ step the host stays ahead of the GPU, and the launches run back to back
 (measured 35.8 us per step, against 40.5 us when the step is captured once in
 a HIP graph and replayed, because each graph replay adds about 4.7 us).
 --graph times graph replay instead (the HER donor counter lives on the
-device, so every replay draws new donors).
+device, so every replay draws new donors); the line carries the other mode's
+time per step as well.
 
 Prints ONE JSON line.  `value` = samples/s = batch / wall-clock time per step
 over the timed replays.  `roofline` is for the dominant kernel (the fused
@@ -598,6 +599,25 @@ def main():
     rc, flags = ctx.tr.status()
     ms_per_step = wall * 1e3 / a.steps
 
+    # the other launch mode, for comparison: graph replay (one step per
+    # replay) when the timed run was eager, and the reverse
+    if graph is None:
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g2):
+            step()
+        other = g2.replay
+    else:
+        g2, other = None, step
+    for _ in range(3):
+        other()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(a.steps):
+        other()
+    torch.cuda.synchronize()
+    other_us = (time.perf_counter() - t1) * 1e6 / a.steps
+    del g2
+
     # every launch of the step timed by its own dispatch events, on the
     # stream the step runs on; the dominant one is the forward/backward
     launch_us = ctx.time_launches(a.kernel_reps)
@@ -631,6 +651,7 @@ def main():
                       "entry_point": "separate calls" if a.separate else "iql_aux_step",
                       "parallelism": "single-gpu"},
            "event_ms_per_step": ev_ms / a.steps, "device_flags": flags, "status": rc,
+           ("graph_replay_us_per_step" if graph is None else "eager_us_per_step"): other_us,
            "partials": {"rows": layout[0], "floats": layout[1]},
            "launch_us": dict(zip(names, launch_us)),
            "launch_hbm": {k: {"needed_bytes": lb[k], "GB/s": lb[k] / (us * 1e-6) / 1e9,
