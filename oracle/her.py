@@ -17,7 +17,7 @@ Source: "GPU IQL + HER Porting Plan"
     (float multiply then truncation), normal rows first, HER rows appended,
     importance weights 1 for HER rows.
 
-Readings where the page is silent (each listed in the design doc):
+Readings where the page is silent:
   * ``episode_ends`` are exclusive and ascending; the episode of ``src`` is the
     first e with episode_ends[e] > src; episode e starts at episode_ends[e-1].
   * future with an empty range (src is the episode's last step) uses the

@@ -27,7 +27,7 @@ W1, W2, h1, dz2 (also in the b2 sum) and dz1 (also in the b1 sum); V, the
 loss, dv and dw3 stay unrounded.  It separates the effect of bf16 operand
 storage from that of the arithmetic order; the plain fp64 definition is the
 parity reference.
-Readings (listed in the design doc): ReLU'(0) = 0; weight tau at diff == 0; the
+Readings: ReLU'(0) = 0; weight tau at diff == 0; the
 finite-check is applied after clipping, so a non-finite norm skips the whole
 update; decoupled weight decay (AdamW order) when weight_decay != 0.
 """
