@@ -450,8 +450,9 @@ def time_next_rows(ctx, torch, np, reps=100):
     points on the bench workload, each with its roofline: V(s') + bootstrap target (MFMA flops of the two
     forward products), the Polyak target update and the non-finite sentinel
     (bytes each must move), prioritized sampling of the HER sources over the
-    whole replay buffer (prefix sums: read the priorities twice, write the
-    binary64 prefix; the searches touch a few lines per draw)."""
+    whole replay buffer (bytes: the priorities once and the draws' indices and
+    weights; the prefix sums are never stored, and each draw's block table,
+    sub-block sums and 1 KB of rows come from the caches)."""
     m, w, d = ctx.m, ctx.w, ctx.d
     B, S, H, G = w.B, w.S, w.H, w.groups
 
@@ -505,7 +506,7 @@ def time_next_rows(ctx, torch, np, reps=100):
     idx = torch.zeros(w.n_her, dtype=torch.int32, device=d)
     wt = torch.zeros(w.n_her, dtype=torch.float32, device=d)
     us = timed(lambda: m.per_sample_indices(pr, w.n_her, 1, 0.4, idx, wt, ws))
-    by = 4.0 * C + 4.0 * C + 8.0 * C
+    by = 4.0 * C + 8.0 * w.n_her
     out["per_sample_indices"] = {"us": us, "bytes": by, "replay_rows": C, "draws": w.n_her,
                                  "achieved": by / (us * 1e-6) / 1e9, "unit": "GB/s", "peak": PEAK_HBM_GBS,
                                  "frac": by / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}

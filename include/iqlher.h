@@ -398,9 +398,10 @@ int iql_time_aux_step(iql_handle h, const iqlh_her_step* her, const void* states
  *   d_flags       device sticky flag word or NULL: IQLH_FLAG_BAD_INDEX when a
  *                 priority is negative or non-finite or the total is not > 0
  *                 (then the draws are -1 with weight 0).
- *   workspace     device, >= per_workspace_bytes(size), 8-byte aligned; holds
- *                 the prefix sums afterwards ([size] binary64).
- * 1 <= size < 2^31, n >= 0 (0 computes the prefix sums only), beta >= 0. */
+ *   workspace     device, >= per_workspace_bytes(size), 8-byte aligned; starts
+ *                 afterwards with the binary64 sum of every 2048-row block
+ *                ([ceil(size / 2048)]).
+ * 1 <= size < 2^31, n >= 0 (0 computes the block sums only), beta >= 0. */
 int per_workspace_bytes(int64_t size, size_t* bytes);
 int per_sample_indices(const float* d_priorities, int64_t size, int32_t n, uint64_t seed, const int64_t* d_step,
                        float beta, int32_t* d_out_idx, float* d_out_weights, int32_t* d_flags, void* workspace,

@@ -10,25 +10,37 @@
 // Weights are prioritized replay's (N P(i))^-beta over the batch maximum,
 // i.e. (p_min / p_i)^beta with p_min the smallest drawn priority.
 //
-// MI355X layout, four launches on a caller workspace:
-//   A  fp64 sum of each 2048-priority block (fixed order);
-//   B  inclusive fp64 prefix of every row: each block folds the sums of the
-//      blocks before it in a fixed order, then scans its own rows (runs of 8
-//      per thread in registers, one wave scan by shuffles, waves through LDS);
-//   C  one wave per draw, 64-ary searches (each lane probes one position,
-//      a ballot picks the segment): first over the table of block ends,
-//      staged in LDS once per workgroup, then inside the one 2048-row block
-//      -- two rounds of global loads per draw instead of twenty; each
-//      workgroup's smallest drawn priority (integer minimum on the bit
-//      pattern: order-independent) to a slot of its own;
-//   D  the weights, after every block folds the workgroup minima.
+// MI355X layout, three launches on a caller workspace; the prefix sums are
+// never stored whole:
+//   A  fp64 sums of every 256-row sub-block and of every 2048-row block (the
+//      block sum adds its eight sub-block sums in order);
+//   D  each workgroup scans the block sums into a table of block ends in LDS
+//      (fixed order); one wave per draw: a 64-ary search of the table (each
+//      lane probes one position, a ballot picks the segment), then the
+//      block's eight sub-block sums (one load round), then the 256 rows of
+//      the sub-block, scanned in registers (the second round).  Two rounds of
+//      global loads per draw, and no 8-byte-per-row prefix array to write and
+//      read.  The block, sub-block and row prefixes are formed in different
+//      orders, so at a boundary they may disagree by a rounding; the draw
+//      then takes the last row of positive priority before that boundary,
+//      a row on one side of it.  Each workgroup's smallest drawn priority
+//      (integer minimum on the bit pattern: order-independent) goes to a slot
+//      of its own;
+//   W  the weights, after every block folds the workgroup minima.
+// For more than 8192 blocks (2^24 rows) the table does not fit in LDS; a
+// one-workgroup launch T then writes it to the workspace and the draws search
+// it there.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace iqlh {
 
 constexpr uint64_t kPerKey1 = 0x5045526472617773ull;  // "PERdraws"
-constexpr int kPerBlock = 2048;                        // priorities per block of A and B
+constexpr int kPerBlock = 2048;                        // rows per block of the table
+constexpr int kPerSub = 256;                           // rows per sub-block (one wave scans one)
+constexpr int kPerSubs = kPerBlock / kPerSub;
+constexpr int kPerMaxWg = 1024;  // workgroups of the draw pass (each wave takes ceil(n / 4096) draws)
+constexpr int kPerTable = 8192;  // block ends kept in LDS (64 KB): up to 2^24 rows
 
 struct PerArgs {
     const float* p;
@@ -40,64 +52,61 @@ struct PerArgs {
     int32_t* idx;
     float* w;
     int32_t* flags;
-    double* prefix;  // [size]
-    double* bsum;    // [nb]
-    double* bend;    // [nb] prefix at the last row of each block
+    double* bsum;    // [nb] block sums
+    double* ssum;    // [nb][8] sub-block sums
+    double* bend;    // [nb] inclusive prefix at each block end (only when nb > kPerTable)
     uint32_t* wgmin; // [nwg] smallest drawn priority (bit pattern) of each draw workgroup
     int vec;         // priorities 16-byte aligned
-    int nb, nwg, dpw;  // blocks of A/B; draw workgroups; draws per wave
+    int nb, nwg, dpw;  // blocks; draw workgroups; draws per wave
 };
 
 IQLH_DEV bool bad_priority(float x) { return !(x >= 0.f) || !isfinite(x); }
 
+// One 2048-row block per workgroup: thread t holds row base + 256 k + t of
+// sub-block k; each sub-block sum is a fixed-order tree (wave sums, then the
+// four waves in order), and the block sum adds the eight in order.
 __global__ __launch_bounds__(256) void per_block_sums_kernel(PerArgs a) {
-    __shared__ double red[4];
+    __shared__ double red[kPerSubs][4];
     const int64_t base = (int64_t)blockIdx.x * kPerBlock + threadIdx.x;
-    double s = 0.0;
+    double s[kPerSubs];
     bool bad = false;
 #pragma unroll
-    for (int k = 0; k < kPerBlock / 256; ++k) {
-        const int64_t i = base + 256 * k;
+    for (int k = 0; k < kPerSubs; ++k) {
+        const int64_t i = base + kPerSub * k;
         const float x = i < a.size ? a.p[i] : 0.f;
         bad |= bad_priority(x);
-        s += (double)x;
+        s[k] = (double)x;
     }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+    for (int k = 0; k < kPerSubs; ++k) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) s[k] += __shfl_xor(s[k], o, 64);
+        if ((threadIdx.x & 63) == 0) red[k][threadIdx.x >> 6] = s[k];
+    }
     if (__syncthreads_or(bad) && threadIdx.x == 0) set_flag(a.flags, 0x2);
-    if (threadIdx.x == 0) a.bsum[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+    if (threadIdx.x < kPerSubs) {
+        const int k = threadIdx.x;
+        a.ssum[(int64_t)blockIdx.x * kPerSubs + k] = (red[k][0] + red[k][1]) + (red[k][2] + red[k][3]);
+    }
+    if (threadIdx.x == 0) {
+        double t = 0.0;
+#pragma unroll
+        for (int k = 0; k < kPerSubs; ++k) t += (red[k][0] + red[k][1]) + (red[k][2] + red[k][3]);
+        a.bsum[blockIdx.x] = t;
+    }
 }
 
-// Inclusive prefix of one block's rows: each thread scans a run of 8 rows in
-// registers (two 16-byte loads: a wave reads 2 KB contiguous), one wave scan
-// of the run totals by shuffles, the totals of the waves before through LDS,
-// 16-byte stores.
-__global__ __launch_bounds__(256) void per_prefix_kernel(PerArgs a) {
-    __shared__ double red[4], wtot[4];
+// Inclusive prefix of the nb block sums into out (LDS or global), by the 256
+// threads of one workgroup in a fixed order: thread t scans its run of
+// ceil(nb / 256) sums sequentially; the run totals are scanned across the
+// wave by shuffles and across the waves in order; each value is the run's
+// offset plus its running sum.
+IQLH_DEV void per_table_scan(const double* __restrict__ bsum, int nb, double* out) {
+    __shared__ double wtot[4];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int64_t base = (int64_t)blockIdx.x * kPerBlock + 8 * threadIdx.x;
-    float x[8];
-    if (a.vec && base + 8 <= a.size) {
-        const float4 lo = *(const float4*)(a.p + base), hi = *(const float4*)(a.p + base + 4);
-        x[0] = lo.x; x[1] = lo.y; x[2] = lo.z; x[3] = lo.w; x[4] = hi.x; x[5] = hi.y; x[6] = hi.z; x[7] = hi.w;
-    } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = base + k < a.size ? a.p[base + k] : 0.f;
-    }
-    // offset = sum of the blocks before this one, in a fixed order
-    double o = 0.0;
-    for (int j = threadIdx.x; j < (int)blockIdx.x; j += 256) o += a.bsum[j];
-#pragma unroll
-    for (int s = 32; s > 0; s >>= 1) o += __shfl_xor(o, s, 64);
-    if (lane == 0) red[wv] = o;
-    double run[8];
+    const int run = (nb + 255) / 256, j0 = threadIdx.x * run, j1 = min(j0 + run, nb);
     double t = 0.0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        t += (double)x[k];
-        run[k] = t;
-    }
+    for (int j = j0; j < j1; ++j) t += bsum[j];
     double incl = t;
 #pragma unroll
     for (int s = 1; s < 64; s <<= 1) {
@@ -106,24 +115,17 @@ __global__ __launch_bounds__(256) void per_prefix_kernel(PerArgs a) {
     }
     if (lane == 63) wtot[wv] = incl;
     __syncthreads();
-    double before = ((red[0] + red[1]) + (red[2] + red[3])) + (incl - t);
-    for (int w = 0; w < wv; ++w) before += wtot[w];
-    double v[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = before + run[k];
-    const int64_t last = min((int64_t)(blockIdx.x + 1) * kPerBlock, a.size) - 1;
-    if (base + 8 <= a.size) {
-#pragma unroll
-        for (int k = 0; k < 8; k += 2) *(double2*)(a.prefix + base + k) = double2{v[k], v[k + 1]};
-    } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            if (base + k < a.size) a.prefix[base + k] = v[k];
+    double off = __shfl_up(incl, 1, 64);
+    if (lane == 0) off = 0.0;
+    for (int w = 0; w < wv; ++w) off += wtot[w];
+    double r = 0.0;
+    for (int j = j0; j < j1; ++j) {
+        r += bsum[j];
+        out[j] = off + r;
     }
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-        if (base + k == last) a.bend[blockIdx.x] = v[k];
 }
+
+__global__ __launch_bounds__(256) void per_table_kernel(PerArgs a) { per_table_scan(a.bsum, a.nb, a.bend); }
 
 // First i in [lo, hi) with prefix[i] > u, given prefix[hi - 1] > u: each lane
 // probes one of 64 evenly spaced positions and the ballot picks the segment.
@@ -145,22 +147,97 @@ IQLH_DEV int64_t search64(int64_t lo, int64_t hi, double u, Load&& at) {
     return hi - lo == 1 ? lo : -1;
 }
 
-constexpr int kPerMaxWg = 1024;  // workgroups of the draw pass (each wave takes ceil(n / 4096) draws)
-constexpr int kPerTable = 8192;  // block ends staged in LDS (at most 64 KB): up to 2^24 rows
+// The row of one draw inside block blk (its prefix before the block is off):
+// the sub-block from the eight sub-block sums, then the row from the
+// sub-block's 256 priorities scanned in registers (four rows per lane).
+// Returns the row and, in every lane, its priority; u = +inf gives the
+// block's last row of positive priority.  Returns -2 for a block of zero sum
+// (chosen only at a rounding boundary of the table).
+IQLH_DEV int64_t per_find_row(const PerArgs& a, int64_t blk, double off, double u, float& prow) {
+    const int lane = threadIdx.x & 63;
+    double sv[kPerSubs];
+    bool any = false;
+#pragma unroll
+    for (int k = 0; k < kPerSubs; ++k) {
+        sv[k] = a.ssum[blk * kPerSubs + k];
+        any |= sv[k] > 0.0;
+    }
+    if (!any) return -2;  // wave-uniform
+    // the sub-block: first whose end prefix exceeds u, else (a rounding
+    // boundary) the last of positive sum
+    int j = -1, jpos = 0;
+    double r = 0.0, rbefore = 0.0;
+#pragma unroll
+    for (int k = 0; k < kPerSubs; ++k) {
+        const double rk = r + sv[k];
+        if (j < 0 && sv[k] > 0.0 && off + rk > u) { j = k; rbefore = r; }
+        if (sv[k] > 0.0) jpos = k;
+        r = rk;
+    }
+    if (j < 0) {
+        j = jpos;
+        rbefore = 0.0;
+        for (int k = 0; k < j; ++k) rbefore += sv[k];
+    }
+    const double soff = off + rbefore;
+    const int64_t base = blk * kPerBlock + (int64_t)j * kPerSub + 4 * lane;
+    float x[4];
+    if (a.vec && base + 4 <= a.size) {
+        const float4 v4 = *(const float4*)(a.p + base);
+        x[0] = v4.x; x[1] = v4.y; x[2] = v4.z; x[3] = v4.w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = keep_if(base + e < a.size, a.p[base + e < a.size ? base + e : a.size - 1]);
+    }
+    double c[4], t = 0.0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { t += (double)x[e]; c[e] = t; }
+    double incl = t;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+        const double y = __shfl_up(incl, s, 64);
+        if (lane >= s) incl += y;
+    }
+    double ex = __shfl_up(incl, 1, 64);
+    if (lane == 0) ex = 0.0;
+    // the first row of positive priority whose prefix soff + (ex + c)
+    // exceeds u (the lane prefixes are tree sums, so a lane of zero rows may
+    // sit an ulp above its predecessor: only lanes with a positive row
+    // qualify), else the last row of positive priority
+    const bool lpos = x[0] > 0.f || x[1] > 0.f || x[2] > 0.f || x[3] > 0.f;
+    const uint64_t above = __ballot(lpos && soff + (ex + c[3]) > u);
+    const uint64_t pos = __ballot(lpos);
+    int L, e = 3;
+    if (above) {
+        L = __builtin_ctzll(above);
+        int mine = 3;
+#pragma unroll
+        for (int k = 3; k >= 0; --k)
+            if (x[k] > 0.f && soff + (ex + c[k]) > u) mine = k;
+        e = __shfl(mine, L, 64);
+    } else {
+        L = 63 - __builtin_clzll(pos);  // pos != 0: the sub-block's sum is positive
+        int mine = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (x[k] > 0.f) mine = k;
+        e = __shfl(mine, L, 64);
+    }
+    const float xs = e == 0 ? x[0] : e == 1 ? x[1] : e == 2 ? x[2] : x[3];
+    prow = __shfl(xs, L, 64);
+    return blk * kPerBlock + (int64_t)j * kPerSub + 4 * L + e;
+}
 
-// Draws of one wave: the block of the row from the table of block ends
-// (binary64 prefix at the last row of every 2048-row block, staged in LDS
-// once per workgroup), then the row inside that block -- two rounds of
-// global loads per draw.
+// Draws of one wave (dpw per wave, four waves per workgroup).
 __global__ __launch_bounds__(256) void per_draw_kernel(PerArgs a) {
-    extern __shared__ double tbl[];  // [nb] when staged
+    extern __shared__ double tbl[];  // [nb] when the table fits in LDS
     const int lane = threadIdx.x & 63;
     const bool staged = a.nb <= kPerTable;
-    if (staged)
-        for (int j = threadIdx.x; j < a.nb; j += 256) tbl[j] = a.bend[j];
+    if (staged) per_table_scan(a.bsum, a.nb, tbl);
     __syncthreads();
+    const double* gtab = a.bend;
     const uint64_t step = a.step ? (uint64_t)*a.step : 0ull;
-    const double total = a.prefix[a.size - 1];
+    const double total = staged ? tbl[a.nb - 1] : gtab[a.nb - 1];
     const double cap = __longlong_as_double(__double_as_longlong(total) - 1);  // largest double below a positive total
     const bool ok = total > 0.0 && isfinite(total);
     const int k0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * a.dpw;
@@ -172,20 +249,28 @@ __global__ __launch_bounds__(256) void per_draw_kernel(PerArgs a) {
         double u = (double)(word >> 11) * 0x1.0p-53 * total;
         if (u > cap) u = cap;
         int64_t found = -1;
+        float pf = 0.f;
         if (ok) {
-            if (staged) {
-                const int64_t blk = search64(0, a.nb, u, [&](int64_t i) { return tbl[i]; });
-                if (blk >= 0) {
-                    const int64_t lo = blk * kPerBlock, hi = min(lo + kPerBlock, a.size);
-                    found = search64(lo, hi, u, [&](int64_t i) { return a.prefix[i]; });
+            const int64_t blk = staged ? search64(0, a.nb, u, [&](int64_t i) { return tbl[i]; })
+                                       : search64(0, a.nb, u, [&](int64_t i) { return gtab[i]; });
+            if (blk >= 0) {
+                const double off = blk == 0 ? 0.0 : (staged ? tbl[blk - 1] : gtab[blk - 1]);
+                found = per_find_row(a, blk, off, u, pf);
+                if (found == -2) {
+                    // a block of zero sum: u lies within a rounding of the
+                    // boundary before it, so the draw takes the last row of
+                    // positive priority before the boundary (a positive block
+                    // precedes: the table exceeds u >= 0 at blk, and sums of
+                    // zeros are exactly zero)
+                    int64_t b = blk - 1;
+                    while (b >= 0 && a.bsum[b] == 0.0) --b;  // wave-uniform
+                    found = b >= 0 ? per_find_row(a, b, 0.0, INFINITY, pf) : -1;
                 }
-            } else {
-                found = search64(0, a.size, u, [&](int64_t i) { return a.prefix[i]; });
             }
         }
         if (lane == 0) {
             a.idx[k] = (int32_t)found;
-            if (found >= 0) wmin = min(wmin, __float_as_uint(a.p[found]));
+            if (found >= 0) wmin = min(wmin, __float_as_uint(pf));
             else set_flag(a.flags, 0x2);
         }
     }
@@ -219,7 +304,7 @@ __global__ __launch_bounds__(256) void per_weight_kernel(PerArgs a) {
 
 size_t per_workspace_bytes_for(int64_t size) {
     const int64_t nb = (size + kPerBlock - 1) / kPerBlock;
-    return (size_t)(8 * size + 16 * nb + 4 * kPerMaxWg + 255) / 256 * 256;
+    return (size_t)(8 * nb * (2 + kPerSubs) + 4 * kPerMaxWg + 255) / 256 * 256;
 }
 
 hipError_t launch_per_sample(const float* p, int64_t size, int n, uint64_t seed, const int64_t* d_step, float beta,
@@ -229,13 +314,13 @@ hipError_t launch_per_sample(const float* p, int64_t size, int n, uint64_t seed,
     a.idx = idx; a.w = w; a.flags = flags;
     a.nb = (int)((size + kPerBlock - 1) / kPerBlock);
     a.vec = ((uintptr_t)p & 15u) == 0;
-    a.prefix = (double*)workspace;
-    a.bsum = a.prefix + size;
-    a.bend = a.bsum + a.nb;
+    a.bsum = (double*)workspace;
+    a.ssum = a.bsum + a.nb;
+    a.bend = a.ssum + (int64_t)a.nb * kPerSubs;
     a.wgmin = (uint32_t*)(a.bend + a.nb);
     hipLaunchKernelGGL(per_block_sums_kernel, dim3(a.nb), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(per_prefix_kernel, dim3(a.nb), dim3(256), 0, stream, a);
     if (n > 0) {
+        if (a.nb > kPerTable) hipLaunchKernelGGL(per_table_kernel, dim3(1), dim3(256), 0, stream, a);
         a.dpw = (n + 4 * kPerMaxWg - 1) / (4 * kPerMaxWg);
         const int waves = (n + a.dpw - 1) / a.dpw;
         a.nwg = (waves + 3) / 4;

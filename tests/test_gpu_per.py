@@ -3,7 +3,8 @@
 Indices are compared element by element; a draw may differ only where its u
 lies within rounding of a prefix-sum boundary (the GPU's binary64 prefix sums
 add in another order), and then the GPU's row must be one of the two rows at
-that boundary.  Weights: 1e-6 relative against the definition evaluated on the
+that boundary.  The block sums the GPU leaves in the workspace are checked
+against the plain binary64 sums.  Weights: 1e-6 relative against the definition evaluated on the
 GPU's own rows (one binary64 pow, one rounding to f32)."""
 import numpy as np
 import pytest
@@ -30,21 +31,28 @@ def _run(m, p, n, seed, beta, step=None):
     d_step = None if step is None else to_dev(np.array([step], np.int64))
     m.per_sample_indices(to_dev(p), n, seed, beta, idx, w, ws, d_step=d_step, d_flags=flags)
     sync()
-    return host(idx)[:n], host(w)[:n], host(ws)[:size], int(host(flags)[0])
+    nb = (size + 2047) // 2048
+    return host(idx)[:n], host(w)[:n], host(ws)[:nb], int(host(flags)[0])
 
 
 @pytest.mark.parametrize("size,n,zero_frac", [(1, 5, 0.0), (1000, 4096, 0.2), (2049, 777, 0.5),
-                                              ((1 << 20) + 7, 8192, 0.2), (5000, 1, 0.9)])
+                                              ((1 << 20) + 7, 8192, 0.2), (5000, 1, 0.9),
+                                              # more than 8192 blocks: the table of block ends in global memory
+                                              ((1 << 24) + 3001, 4096, 0.2)])
 def test_draws_match_oracle(m, size, n, zero_frac):
     g = np.random.default_rng(size)
     p = (g.random(size) * 3).astype(np.float32)
     p[g.random(size) < zero_frac] = 0.0
     p[g.integers(size)] = 1.5  # at least one positive row
     seed, step, beta = 20261202, 3, 0.4
-    gi, gw, gpre, flags = _run(m, p, n, seed, beta, step)
+    gi, gw, gbs, flags = _run(m, p, n, seed, beta, step)
     oi, ow, ou, opre = per.sample(p, n, seed, step, beta)
     assert flags == 0
-    np.testing.assert_allclose(gpre, opre, rtol=1e-12, atol=1e-300)
+    # the workspace starts with the binary64 sum of every 2048-row block
+    nb = gbs.size
+    padded = np.zeros(nb * 2048, np.float64)
+    padded[:size] = p
+    np.testing.assert_allclose(gbs, padded.reshape(nb, 2048).sum(axis=1), rtol=1e-12, atol=1e-300)
     total = opre[-1]
     diff = np.nonzero(gi != oi)[0]
     for k in diff:  # only at a boundary, and only to its neighbour row
