@@ -161,7 +161,7 @@ def launch_bytes(w, layout=None):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("iql.hip", "common.hpp", "her_block.hpp", "iql_update.hpp", "launch.hpp"):
+    for f in ("iql.hip", "common.hpp", "her_block.hpp", "budget_block.hpp", "iql_update.hpp", "launch.hpp"):
         with open(os.path.join(ROOT, "offline_rl_step_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
