@@ -558,8 +558,8 @@ def main():
         copy_probe(a.copy_probe)
         return
     if a.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported by this build "
-              "(the step has no cross-GPU exchange; see the sharding notes).", file=sys.stderr)
+        print(f"bench.py measures one GPU: the step has no cross-GPU exchange, so --gpus {a.gpus} "
+              "is not supported.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
