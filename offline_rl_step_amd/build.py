@@ -21,11 +21,15 @@ FLAGS = [
 ]
 
 
-# Per-file flags: the whole-step reduction / SAXPY and Adam launches
-# (step.hip) are chains of dependent loads, and the ILP-first scheduler
-# measured faster for them (it measured slower for the forward/backward
-# kernel).
-FILE_FLAGS = {"step.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# Per-file flags, each measured on the whole step: the reduction / SAXPY and
+# Adam launches (step.hip) are chains of dependent loads, and the ILP-first
+# scheduler is faster for them (slower for the forward/backward kernel).
+# Both files raise a wave's priority while it issues its vector-memory loads
+# (s_setprio), so that its loads go out ahead of the other waves' arithmetic.
+FILE_FLAGS = {
+    "step.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp", "-mllvm", "-amdgpu-set-wave-priority"],
+    "iql.hip": ["-mllvm", "-amdgpu-set-wave-priority"],
+}
 
 
 def sources():
