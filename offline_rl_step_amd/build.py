@@ -21,13 +21,15 @@ FLAGS = [
 ]
 
 
-# Per-file flags, each measured on the whole step: the reduction / SAXPY and
-# Adam launches (step.hip) are chains of dependent loads, and the ILP-first
-# scheduler is faster for them (slower for the forward/backward kernel).
-# Both files raise a wave's priority while it issues its vector-memory loads
-# (s_setprio), so that its loads go out ahead of the other waves' arithmetic.
+# Per-file flags, each measured: the reduction / SAXPY and Adam launches
+# (step.hip) and the PER passes (per.hip) are chains of dependent loads, and
+# the ILP-first scheduler is faster for them (slower for the forward/backward
+# kernel).  These files raise a wave's priority while it issues its
+# vector-memory loads (s_setprio), so that its loads go out ahead of the
+# other waves' arithmetic.
 FILE_FLAGS = {
     "step.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp", "-mllvm", "-amdgpu-set-wave-priority"],
+    "per.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp", "-mllvm", "-amdgpu-set-wave-priority"],
     "iql.hip": ["-mllvm", "-amdgpu-set-wave-priority"],
 }
 
