@@ -315,6 +315,23 @@ int grad_budget_accumulate(float* grad_buf, const float* const* sources, const f
                            float max_grad_norm, float* out_norms, const iqlh_adam* adam,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* grad_budget_accumulate for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and results, bit for bit, without the
+ * workspace -- the passes use a library-owned static device array of 73,736
+ * bytes ((8 + 1) * 2048 + 2 floats, enough for every n and k <= 8) instead.
+ * Nothing is allocated or freed, by the call or by the library.  The array's
+ * address is looked up once per device, on the first call with that device
+ * current.  Every call on one device shares that device's array and no
+ * contents carry over between calls, so calls that overlap in time on one
+ * device (other streams, other threads) race: serialise them.  A workspace
+ * the scratch cannot hold is rejected with IQLH_EINVAL (none can, for valid
+ * n and k); the other errors are those of grad_budget_accumulate. */
+int grad_budget_accumulate_noalloc(float* grad_buf, const float* const* sources, const float* fractions,
+                                   const float* alphas, int32_t num_sources, int64_t n,
+                                   float max_grad_norm, float* out_norms, const iqlh_adam* adam,
+                                   void* stream);
+
 /* ------------------------------------------------------------------------
  * The whole auxiliary step in one call: HER rows into the merged batch, the
  * IQL step on it with the advantage-weighted policy, and the budgeted

@@ -105,6 +105,9 @@ _lib_ws_bytes = _sig("grad_budget_workspace_bytes", _i32, [_i64, _i32, ctypes.PO
 _lib_budget = _sig("grad_budget_accumulate", _i32, [_p, ctypes.POINTER(_p), ctypes.POINTER(_f),
                                                     ctypes.POINTER(_f), _i32, _i64, _f, _p,
                                                     ctypes.POINTER(Adam), _p, ctypes.c_size_t, _p])
+_lib_budget_noalloc = _sig("grad_budget_accumulate_noalloc", _i32, [_p, ctypes.POINTER(_p), ctypes.POINTER(_f),
+                                                                    ctypes.POINTER(_f), _i32, _i64, _f, _p,
+                                                                    ctypes.POINTER(Adam), _p])
 _lib_iql_aux_step = _sig("iql_aux_step", _i32, [_p, ctypes.POINTER(HerStep), _p, _p, _i32, _p, _i32, _f, _p, _p,
                                                 _p, _p, ctypes.POINTER(BudgetStep), _p])
 _lib_iql_time_aux_step = _sig("iql_time_aux_step", _i32, [_p, ctypes.POINTER(HerStep), _p, _p, _i32, _p, _i32, _f,
@@ -377,6 +380,18 @@ def grad_budget_accumulate(grad_buf, sources, fractions, alphas, n, max_grad_nor
                        None if adam is None else ctypes.byref(adam), _ptr(workspace),
                        workspace.numel() * workspace.element_size(), _stream(stream)),
            "grad_budget_accumulate")
+
+
+def grad_budget_accumulate_noalloc(grad_buf, sources, fractions, alphas, n, max_grad_norm, out_norms, adam,
+                                   stream=None):
+    """grad_budget_accumulate on the library's static device scratch (no workspace)."""
+    k = len(sources)
+    srcs = (_p * k)(*[s.data_ptr() for s in sources])
+    fr = (_f * k)(*fractions)
+    al = (_f * k)(*alphas)
+    _check(_lib_budget_noalloc(_ptr(grad_buf), srcs, fr, al, k, n, max_grad_norm, _ptr(out_norms),
+                               None if adam is None else ctypes.byref(adam), _stream(stream)),
+           "grad_budget_accumulate_noalloc")
 
 
 # ------------------------------------------------------------ whole step

@@ -596,6 +596,30 @@ int grad_budget_accumulate(float* grad_buf, const float* const* sources, const f
     return IQLH_OK;
 }
 
+int grad_budget_accumulate_noalloc(float* grad_buf, const float* const* sources, const float* fractions,
+                                   const float* alphas, int32_t num_sources, int64_t n, float max_grad_norm,
+                                   float* out_norms, const iqlh_adam* adam, void* stream) {
+    size_t need = 0;
+    int rc = grad_budget_workspace_bytes(n, num_sources, &need);
+    if (rc) return rc;
+    if (need > budget_scratch_bytes())
+        return fail(IQLH_EINVAL, "grad_budget_accumulate_noalloc: workspace of %zu bytes exceeds the %zu-byte scratch",
+                    need, budget_scratch_bytes());
+    // every argument is checked before the first HIP call (the scratch
+    // address is filled in afterwards)
+    BudgetArgs b;
+    static char placeholder;
+    rc = make_budget_args(grad_buf, sources, fractions, alphas, num_sources, n, max_grad_norm, out_norms, adam,
+                          &placeholder, budget_scratch_bytes(), &b);
+    if (rc) return rc;
+    hipError_t e = budget_scratch_ptr(&b.work);
+    if (e != hipSuccess) return hip_fail(e, "grad_budget_accumulate_noalloc: scratch address");
+    e = launch_budget(b.grad, b.s, b.n, b.mgn, b.out_norms, b.params, b.m, b.v, b.t, b.flags,
+                      b.params ? &b.hp : nullptr, b.work, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "grad_budget_accumulate_noalloc launch");
+    return IQLH_OK;
+}
+
 struct AuxPlan {
     HerArgs ha;
     BudgetArgs ba;

@@ -17,6 +17,8 @@
 //              per-block partial of ||grad||^2;
 //   3. adam  : every block folds the grad partials into the combined norm and
 //              applies the clipped Adam update, zeroing grad.
+#include <mutex>
+
 #include "budget_block.hpp"
 
 namespace iqlh {
@@ -94,6 +96,40 @@ hipError_t launch_budget(float* grad, const SourceSet& s, int64_t n, float mgn, 
         hipLaunchKernelGGL(norm_finalize_kernel, dim3(1), dim3(kBT), 0, stream, gpart, nb,
                            out_norms + s.k);
     return hipGetLastError();
+}
+
+// ------------------------------------------------- allocation-free variant
+// The largest workspace the three passes use (kMaxSources + 1 sets of
+// kMaxBlocks partial sums and the two Adam bias corrections) as a file-scope
+// device array, for callers that cannot allocate.  Every device the library
+// runs on holds its own copy until the process ends.  In host code `scratch`
+// names a host-side stand-in, never the device copy: kernels receive the
+// address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchFloats = (size_t)(kMaxSources + 1) * kMaxBlocks + 2;
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+size_t budget_scratch_bytes() { return sizeof(float) * kScratchFloats; }
+
+// Device address of the current device's scratch, looked up once per device
+// (with that device current) and kept; the passes need no initial contents.
+hipError_t budget_scratch_ptr(float** out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static float* ptrs[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        ptrs[dev] = (float*)p;
+    }
+    *out = ptrs[dev];
+    return hipSuccess;
 }
 
 }  // namespace iqlh

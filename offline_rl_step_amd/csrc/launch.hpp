@@ -76,6 +76,11 @@ hipError_t launch_budget(float* grad, const SourceSet& s, int64_t n, float mgn,
                          float* out_norms, float* params, float* m, float* v, int32_t* t,
                          int32_t* flags, const AdamHyper* hp, float* work, hipStream_t stream);
 
+// The allocation-free entry point's workspace: a static device array of
+// budget_scratch_bytes() bytes (enough for any n and k), addressed per device.
+size_t budget_scratch_bytes();
+hipError_t budget_scratch_ptr(float** out);
+
 // Flat clipped Adam over n elements whose gradient L2 norm is the fixed-order
 // sum of `nb` partial sums of squares.  Zeroes grad.  bc holds the bias
 // corrections 1 - beta1^t, 1 - beta2^t of the already incremented step count
