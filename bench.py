@@ -128,7 +128,7 @@ def launch_bytes(w, layout=None):
       relabel+norms: per HER row, source s and s' rows (f32), the donor's goal,
                      the source index, action, done and two episode ends;
                      written: the bf16 state row, the f32 s' row, action,
-                     reward, done, donor.  Norms: every budget source once.
+                     reward, done, donor, IS weight.  Norms: every budget source once.
                      Either part moves to fwd_bwd when that launch hosts it
                      (fused_parts); the HER rows are then not read back from
                      the batch.
@@ -145,7 +145,7 @@ def launch_bytes(w, layout=None):
     P, Pp, nwg = partial_layout(w, layout)
     e = 2 if w.dtype == "bf16" else 4
     shadows = e * (H * S + 2 * H * H)
-    her = n * (8 * S + 4 * w.G + 4 + 4 + 4 + 8) + n * (e * S + 4 * S + 4 * 4)
+    her = n * (8 * S + 4 * w.G + 4 + 4 + 4 + 8) + n * (e * S + 4 * S + 5 * 4)
     norms = k * nb * 4
     her_b, norms_b = fused_parts(w)
     batch_rows = B - n if her_b else B
@@ -209,6 +209,7 @@ class Context:
         self.her_rew = torch.empty(n, dtype=torch.float32, device=d)
         self.her_done = torch.empty(n, dtype=torch.float32, device=d)
         self.her_donor = torch.empty(n, dtype=torch.int32, device=d)
+        self.isw = torch.ones(B, dtype=torch.float32, device=d)  # merged batch IS weights (HER tail written)
 
         cdt = m.BF16 if bf16 else m.F32
         cfg = m.make_config(S, w.H, B, num_groups=w.groups, compute_dtype=cdt, states_ld=S,
@@ -225,7 +226,8 @@ class Context:
         tail = self.X.data_ptr() + (B - n) * S * self.X.element_size()
         self.hout = m.her_out(tail, cdt, S, self.her_rew, next_states=self.her_next,
                               actions=self.her_act, dones=self.her_done, donor_idx=self.her_donor,
-                              d_flags=self.tr.flags)
+                              d_flags=self.tr.flags,
+                              is_weights=self.isw.data_ptr() + (B - n) * self.isw.element_size())
 
         self.her_step = m.her_step(self.hcfg, self.hbuf, self.src, w.n_her, 20261202, self.hout)
         self.budget_step = None

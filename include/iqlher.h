@@ -58,17 +58,22 @@ typedef enum { IQLH_F32 = 0, IQLH_BF16 = 1 } iqlh_dtype;
  * iql_value_kernel.cu", "Rust Integration: gpu_iql_trainer.rs"; grouped
  * high/low trainers: [P3] "2C. Grouped GEMM for IQL").
  *
- * V(s) = w3 . relu(W2 relu(W1 s + b1) + b2) + b3, W1 [hidden, state_dim],
- * W2 [hidden, hidden], w3 [hidden], b3 scalar.  Flat parameter order per
- * group: w1, b1, w2, b2, w3, b3 (iql_num_params elements).
+ * V(s) = w3 . relu(W2 relu(W1 s + b1) + b2) + b3, W1 [H1, state_dim],
+ * W2 [H2, H1], w3 [H2], b3 scalar, with H1 = hidden and H2 = hidden2 (the
+ * pages' IqlGpuConfig has separate v_h1 / v_h2, [P1] "Rust Integration:
+ * gpu_iql_trainer.rs").  Flat parameter order per group: w1, b1, w2, b2, w3,
+ * b3 (iql_config_num_params elements).
  * ---------------------------------------------------------------------- */
 typedef struct iqlh_config {
     int32_t state_dim;      /* S >= 1                                          */
-    int32_t hidden;         /* H: width of both hidden layers                  */
+    int32_t hidden;         /* H1: width of the first hidden layer (and of the
+                               second when hidden2 is 0)                       */
     int32_t max_batch;      /* largest B passed to iql_train_step              */
     int32_t num_groups;     /* 1 or 2 trainers sharing states and q_taken      */
     int32_t compute_dtype;  /* iqlh_dtype of `states` and of the GEMM operands */
-    int32_t reserved0;
+    int32_t hidden2;        /* H2: width of the second hidden layer, 0 = H1.
+                               H2 != H1 runs on the layered GEMM kernels (the
+                               fused and wide kernels are built for H2 = H1) */
     int64_t states_ld;      /* row stride of `states`, elements, >= state_dim  */
     float tau[2];           /* expectile tau per group, in [0, 1]              */
     float lr, beta1, beta2, eps, weight_decay, max_grad_norm;
@@ -77,11 +82,15 @@ typedef struct iqlh_config {
 
 typedef struct iql_trainer* iql_handle;
 
-/* Parameters per group: S*H + H + H*H + H + H + 1.  Host only. */
+/* Parameters per group with H1 = H2 = hidden: S*H + H + H*H + H + H + 1.
+ * Host only. */
 int iql_num_params(int32_t state_dim, int32_t hidden, int64_t* out_count);
+/* Parameters per group of a config: S*H1 + H1 + H2*H1 + H2 + H2 + 1.  Host
+ * only; checks only the three widths. */
+int iql_config_num_params(const iqlh_config* cfg, int64_t* out_count);
 
 /* Creates a trainer on the current device.  `init_params_host` holds
- * num_groups * iql_num_params floats (group-major) and is copied; Adam
+ * num_groups * iql_config_num_params floats (group-major) and is copied; Adam
  * moments start at zero and the step counter t at 0.  The handle owns the
  * fp32 master weights, Adam moments, gradients, the GEMM-operand shadows of
  * the weights and the per-workgroup partial buffers sized for max_batch.
@@ -233,6 +242,7 @@ int iql_aw_policy(const float* q, const float* v, int32_t num_groups, int32_t ba
  *                    next_states[donor][d])^2) < goal_threshold else
  *                    reward_miss, summed in goal order in binary32 without
  *                    fused multiply-add, correctly rounded sqrt.
+   out.is_weights[i] = 1.0
  * Writing out.states = X + (B - n) * ld appends the relabelled rows to a
  * merged batch X without a copy (normal rows first). */
 typedef enum { HER_FINAL = 0, HER_FUTURE = 1, HER_RANDOM = 2 } her_strategy;
@@ -274,6 +284,14 @@ typedef struct her_out {
     float* rewards;             /* device [n]                              */
     float* dones;               /* device [n] or NULL                      */
     int32_t* d_flags;           /* device sticky flag word or NULL         */
+    float* is_weights;          /* device [n] f32 or NULL: the rows' importance-
+                                   sampling weights in the merged batch, 1.0
+                                   for every relabelled row ([P1] "How HER
+                                   Interacts with GPU PER": HER rows are not
+                                   drawn by priority); 0 for a zeroed row.
+                                   Pointing it at W + (B - n) for the batch's
+                                   weight vector W completes the merged weights
+                                   in place, as out.states does for the rows. */
 } her_out;
 
 /* n >= 0 rows (n == 0 is a no-op).  d_step: device int64 counter (NULL = 0).

@@ -32,7 +32,7 @@ _i32, _i64, _u64, _f = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c
 
 class IqlConfig(ctypes.Structure):
     _fields_ = [("state_dim", _i32), ("hidden", _i32), ("max_batch", _i32), ("num_groups", _i32),
-                ("compute_dtype", _i32), ("reserved0", _i32), ("states_ld", _i64),
+                ("compute_dtype", _i32), ("hidden2", _i32), ("states_ld", _i64),
                 ("tau", _f * 2), ("lr", _f), ("beta1", _f), ("beta2", _f), ("eps", _f),
                 ("weight_decay", _f), ("max_grad_norm", _f), ("weight_clamp_max_abs", _f)]
 
@@ -51,7 +51,7 @@ class HerBuffer(ctypes.Structure):
 class HerOut(ctypes.Structure):
     _fields_ = [("donor_idx", _p), ("states", _p), ("states_dtype", _i32), ("reserved0", _i32),
                 ("states_ld", _i64), ("next_states", _p), ("actions", _p), ("rewards", _p),
-                ("dones", _p), ("d_flags", _p)]
+                ("dones", _p), ("d_flags", _p), ("is_weights", _p)]
 
 
 class Adam(ctypes.Structure):
@@ -80,6 +80,7 @@ def _sig(name, res, args):
 
 
 _lib_iql_num_params = _sig("iql_num_params", _i32, [_i32, _i32, ctypes.POINTER(_i64)])
+_lib_iql_config_num_params = _sig("iql_config_num_params", _i32, [ctypes.POINTER(IqlConfig), ctypes.POINTER(_i64)])
 _lib_iql_create = _sig("iql_create", _i32, [ctypes.POINTER(IqlConfig), _p, ctypes.POINTER(_p)])
 _lib_iql_destroy = _sig("iql_destroy", _i32, [_p])
 _lib_iql_train_step = _sig("iql_train_step", _i32, [_p, _p, _p, _i32, _p, _p, _p, _p])
@@ -157,11 +158,19 @@ def iql_num_params(state_dim, hidden):
     return out.value
 
 
+def iql_config_num_params(cfg):
+    out = _i64()
+    _check(_lib_iql_config_num_params(ctypes.byref(cfg), ctypes.byref(out)), "iql_config_num_params")
+    return out.value
+
+
 def make_config(state_dim, hidden, max_batch, num_groups=1, compute_dtype=F32, states_ld=None,
                 tau=(0.7, 0.7), lr=3e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
-                max_grad_norm=1.0, weight_clamp_max_abs=0.0):
+                max_grad_norm=1.0, weight_clamp_max_abs=0.0, hidden2=0):
+    """hidden: first hidden width H1; hidden2: second (0 = hidden)."""
     c = IqlConfig()
     c.state_dim, c.hidden, c.max_batch, c.num_groups = state_dim, hidden, max_batch, num_groups
+    c.hidden2 = hidden2
     c.compute_dtype = compute_dtype
     c.states_ld = state_dim if states_ld is None else states_ld
     taus = list(tau) + [tau[-1]] * (2 - len(tau))
@@ -336,10 +345,12 @@ def her_buffer(states, next_states, actions, dones, episode_ends, buffer_size=No
 
 
 def her_out(states, states_dtype, states_ld, rewards, next_states=None, actions=None, dones=None,
-            donor_idx=None, d_flags=None):
-    """HerOut; keeps references to the tensors it was given (see her_buffer)."""
+            donor_idx=None, d_flags=None, is_weights=None):
+    """HerOut; keeps references to the tensors it was given (see her_buffer).
+    `states` and `is_weights` may be a tensor or a raw device address (a view
+    into the merged batch)."""
     o = HerOut()
-    o._keep = (states, rewards, next_states, actions, dones, donor_idx, d_flags)
+    o._keep = (states, rewards, next_states, actions, dones, donor_idx, d_flags, is_weights)
     o.states = states if isinstance(states, int) else states.data_ptr()
     o.states_dtype, o.states_ld = states_dtype, states_ld
     o.rewards = rewards.data_ptr()
@@ -348,6 +359,7 @@ def her_out(states, states_dtype, states_ld, rewards, next_states=None, actions=
     o.dones = dones.data_ptr() if dones is not None else None
     o.donor_idx = donor_idx.data_ptr() if donor_idx is not None else None
     o.d_flags = d_flags if (d_flags is None or isinstance(d_flags, int)) else d_flags.data_ptr()
+    o.is_weights = is_weights if (is_weights is None or isinstance(is_weights, int)) else is_weights.data_ptr()
     return o
 
 
@@ -450,7 +462,7 @@ class IqlTrainer:
     def __init__(self, cfg, init_params_host):
         self.cfg = cfg
         self.h = iql_create(cfg, init_params_host)
-        self.n_params = iql_num_params(cfg.state_dim, cfg.hidden)
+        self.n_params = iql_config_num_params(cfg)
 
     def forward_values(self, next_states, batch, out_v, rewards=None, dones=None, gamma=0.99, out_target=None,
                        states_ld=None, stream=None):

@@ -57,9 +57,21 @@ int iql_num_params(int32_t state_dim, int32_t hidden, int64_t* out_count) {
     return IQLH_OK;
 }
 
+static int32_t hidden2_of(const iqlh_config* c) { return c->hidden2 ? c->hidden2 : c->hidden; }
+
+int iql_config_num_params(const iqlh_config* cfg, int64_t* out_count) {
+    if (!cfg || !out_count) return fail(IQLH_EINVAL, "iql_config_num_params: NULL argument");
+    if (cfg->state_dim < 1 || cfg->hidden < 1 || cfg->hidden2 < 0)
+        return fail(IQLH_EINVAL, "iql_config_num_params: state_dim and hidden must be >= 1, hidden2 >= 0");
+    const int64_t S = cfg->state_dim, H1 = cfg->hidden, H2 = hidden2_of(cfg);
+    *out_count = S * H1 + H1 + H2 * H1 + H2 + H2 + 1;
+    return IQLH_OK;
+}
+
 static int check_config(const iqlh_config* c) {
     if (!c) return fail(IQLH_EINVAL, "config is NULL");
     if (c->state_dim < 1 || c->hidden < 1) return fail(IQLH_EINVAL, "state_dim and hidden must be >= 1");
+    if (c->hidden2 < 0) return fail(IQLH_EINVAL, "hidden2 must be >= 0 (0: the same as hidden)");
     if (c->max_batch < 1) return fail(IQLH_EINVAL, "max_batch must be >= 1");
     if (c->num_groups < 1 || c->num_groups > 2) return fail(IQLH_EINVAL, "num_groups must be 1 or 2");
     if (c->compute_dtype != IQLH_F32 && c->compute_dtype != IQLH_BF16)
@@ -75,10 +87,13 @@ static int check_config(const iqlh_config* c) {
         return fail(IQLH_EINVAL, "weight_decay must be finite and >= 0");
     if (!(c->max_grad_norm > 0.f)) return fail(IQLH_EINVAL, "max_grad_norm must be > 0");
     if (!(c->weight_clamp_max_abs >= 0.f)) return fail(IQLH_EINVAL, "weight_clamp_max_abs must be >= 0");
+    const int32_t h2 = hidden2_of(c);
     if (!iql_supported(c->compute_dtype, c->state_dim, c->hidden) &&
         !iql_layered_supported(c->compute_dtype, c->state_dim, c->hidden))
         return fail(IQLH_ESHAPE, "no kernel for dtype=%d state_dim=%d hidden=%d", c->compute_dtype,
                     c->state_dim, c->hidden);
+    if (h2 != c->hidden && !iql_layered_supported(c->compute_dtype, c->state_dim, h2))
+        return fail(IQLH_ESHAPE, "no kernel for hidden2=%d", h2);
     return IQLH_OK;
 }
 
@@ -107,13 +122,15 @@ int iql_create(const iqlh_config* cfg, const float* init_params_host, iql_handle
     t->cfg = *cfg;
     hipError_t e = hipGetDevice(&t->device);
     if (e != hipSuccess) { delete t; return hip_fail(e, "hipGetDevice"); }
-    const int G = cfg->num_groups, S = cfg->state_dim, H = cfg->hidden;
+    const int G = cfg->num_groups, S = cfg->state_dim, H = cfg->hidden, H2 = hidden2_of(cfg);
     int64_t P = 0;
-    iql_num_params(S, H, &P);
+    iql_config_num_params(cfg, &P);
     IqlDims& d = t->dims;
-    d.S = S; d.H = H; d.G = G; d.dtype = cfg->compute_dtype;
-    d.layered = iql_supported(d.dtype, S, H) ? 0 : 1;
-    d.big = d.layered && iql_big_supported(d.dtype, S, H) && cfg->states_ld % 8 == 0;
+    d.S = S; d.H = H; d.H2 = H2; d.G = G; d.dtype = cfg->compute_dtype;
+    // two different hidden widths: the layered GEMMs (the fused and wide
+    // kernels are built for one width)
+    d.layered = (H2 == H && iql_supported(d.dtype, S, H)) ? 0 : 1;
+    d.big = d.layered && H2 == H && iql_big_supported(d.dtype, S, H) && cfg->states_ld % 8 == 0;
     d.S_pad = d.layered ? (S + 7) / 8 * 8 : iql_s_pad(d.dtype, S, H);
     d.P = P;
     d.Pp = (P + 127) / 128 * 128;
@@ -137,8 +154,12 @@ int iql_create(const iqlh_config* cfg, const float* init_params_host, iql_handle
     b.act_h1 = b.act_dz2 = b.act_p2 = b.act_dz1 = nullptr;
     b.act_z2 = b.act_dv = nullptr;
     b.big_spart = nullptr;
+    // activations: h1, dz1 [G][MB][H]; z2, dz2, p2 [G][MB][H2] (layered-only:
+    // z2, p2 and dv)
     const size_t nact = d.layered ? (size_t)G * MB * H : 0;
-    const size_t nlay = d.layered && !d.big ? nact : 0;  // layered-only activations
+    const size_t nact2 = d.layered ? (size_t)G * MB * H2 : 0;
+    const size_t nlay2 = d.layered && !d.big ? nact2 : 0;
+    const size_t nlay = d.layered && !d.big ? nact : 0;
     struct { void** p; size_t bytes; } plan[] = {
         {(void**)&b.params, sizeof(float) * G * P},
         {&t->fv_states, esz * (size_t)MB * d.S_pad},
@@ -151,15 +172,15 @@ int iql_create(const iqlh_config* cfg, const float* init_params_host, iql_handle
         {(void**)&b.step, sizeof(int64_t)},
         {(void**)&b.flags, sizeof(int32_t)},
         {(void**)&b.w1s, esz * G * H * d.S_pad},
-        {(void**)&b.w2s, esz * G * H * H},
-        {(void**)&b.w2ts, esz * G * H * H},
+        {(void**)&b.w2s, esz * G * H2 * H},
+        {(void**)&b.w2ts, esz * G * H2 * H},
         {(void**)&b.part, sizeof(float) * G * (size_t)max_wg * d.Pp},
         {(void**)&b.loss_part, sizeof(float) * G * (size_t)max_loss},
         {(void**)&b.sq_part, sizeof(float) * G * (size_t)rb},
         {(void**)&b.act_h1, esz * nact},
-        {(void**)&b.act_z2, sizeof(float) * nlay},
-        {(void**)&b.act_dz2, esz * nact},
-        {(void**)&b.act_p2, esz * nlay},
+        {(void**)&b.act_z2, sizeof(float) * nlay2},
+        {(void**)&b.act_dz2, esz * nact2},
+        {(void**)&b.act_p2, esz * nlay2},
         {(void**)&b.act_dz1, esz * nact},
         {(void**)&b.act_dv, sizeof(float) * (nlay ? (size_t)G * MB : 0)},
         {(void**)&b.big_spart, sizeof(float) * (d.big ? (size_t)G * iql_big_blocks((int)MB) * (2 * H + 1) : 0)},
@@ -504,6 +525,7 @@ static int make_her_args(const her_config* cfg, const her_buffer* buf, const int
     a.episode_ends = buf->episode_ends; a.source_idx = source_idx; a.d_step = d_step;
     a.donor_out = out->donor_idx; a.out_states = out->states; a.out_next_states = out->next_states;
     a.out_actions = out->actions; a.out_rewards = out->rewards; a.out_dones = out->dones; a.flags = out->d_flags;
+    a.out_isw = out->is_weights;
     a.buffer_size = buf->buffer_size; a.out_ld = out->states_ld; a.seed = seed;
     a.num_episodes = buf->num_episodes;
     a.S = cfg->state_dim; a.G = cfg->goal_dim; a.strategy = cfg->strategy;

@@ -238,12 +238,14 @@ IQLH_DEV void her_block(const HerArgs& a, int64_t blk) {
             if (a.donor_out) a.donor_out[i] = (int32_t)donor;
             if (a.out_actions) a.out_actions[i] = act;
             if (a.out_dones) a.out_dones[i] = done;
+            if (a.out_isw) a.out_isw[i] = 1.f;
         } else {
             donor = -1;
             a.out_rewards[i] = 0.f;
             if (a.donor_out) a.donor_out[i] = -1;
             if (a.out_actions) a.out_actions[i] = 0;
             if (a.out_dones) a.out_dones[i] = 0.f;
+            if (a.out_isw) a.out_isw[i] = 0.f;
             set_flag(a.flags, 0x2);
         }
         s_don[tid] = donor;

@@ -531,22 +531,23 @@ __global__ __launch_bounds__(256) void iql_adam_kernel(IqlDims d, IqlBuffers b, 
 
 template <typename T>
 __global__ __launch_bounds__(256) void iql_shadow_kernel(IqlDims d, IqlBuffers b) {
-    const int g = blockIdx.y, H = d.H, S = d.S, SP = d.S_pad;
+    const int g = blockIdx.y, H = d.H, H2 = d.H2, S = d.S, SP = d.S_pad;
     const float* prm = b.params + (int64_t)g * d.P;
     T* w1s = (T*)b.w1s + (int64_t)g * H * SP;
-    T* w2s = (T*)b.w2s + (int64_t)g * H * H;
-    T* w2ts = (T*)b.w2ts + (int64_t)g * H * H;
+    T* w2s = (T*)b.w2s + (int64_t)g * H2 * H;
+    T* w2ts = (T*)b.w2ts + (int64_t)g * H2 * H;
     const int64_t ow2 = (int64_t)H * S + H;
-    const int64_t n1 = (int64_t)H * SP, n2 = (int64_t)H * H;
+    const int64_t n1 = (int64_t)H * SP, n2 = (int64_t)H2 * H;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n1 + n2; i += (int64_t)gridDim.x * 256) {
         if (i < n1) {
             const int64_t r = i / SP, c = i - r * SP;
             w1s[i] = Op<T>::cvt(c < S ? prm[r * S + c] : 0.f);
         } else {
+            // W2 [H2][H] and its transpose [H][H2]
             const int64_t q = i - n1, r = q / H, c = q - r * H;
             const float p = prm[ow2 + q];
             w2s[q] = Op<T>::cvt(p);
-            w2ts[c * H + r] = Op<T>::cvt(p);
+            w2ts[c * H2 + r] = Op<T>::cvt(p);
         }
     }
 }
@@ -951,6 +952,7 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
                     if (h.donor_out) h.donor_out[hi] = (int32_t)donor;
                     if (h.out_actions) h.out_actions[hi] = hact0;
                     if (h.out_dones) h.out_dones[hi] = hdone0;
+                    if (h.out_isw) h.out_isw[hi] = 1.f;
                 }
             } else {
                 donor = -1;
@@ -959,6 +961,7 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
                     if (h.donor_out) h.donor_out[hi] = -1;
                     if (h.out_actions) h.out_actions[hi] = 0;
                     if (h.out_dones) h.out_dones[hi] = 0.f;
+                    if (h.out_isw) h.out_isw[hi] = 0.f;
                     set_flag(h.flags, 0x2);
                 }
             }
@@ -1477,7 +1480,7 @@ hipError_t launch_iql_target_ema(const IqlDims& d, const IqlBuffers& b, float ta
 }
 
 hipError_t launch_iql_refresh_shadows(const IqlDims& d, const IqlBuffers& b, hipStream_t stream) {
-    const int64_t n = (int64_t)d.H * d.S_pad + (int64_t)d.H * d.H;
+    const int64_t n = (int64_t)d.H * d.S_pad + (int64_t)d.H2 * d.H;
     const int64_t bn = (n + 255) / 256;
     const int blocks = (int)(bn < 1024 ? bn : 1024);
     if (d.dtype == 1)

@@ -161,7 +161,8 @@ struct FwdArgs {
     void* out;             // [M][N] operand-typed (L1) or f32 (L2)
     const void* mask;      // L3: H1 [M][N] operand-typed, relu'(z1) = (h1 > 0)
     int mode;              // 0: L1 relu -> T ; 1: L2 bias -> f32 ; 2: L3 mask -> T
-    int64_t gstride_w;     // per-group strides (elements) for weights / outputs
+    int64_t gstride_w;     // per-group strides (elements) for weights / activation inputs / outputs
+    int64_t gstride_in;
     int64_t gstride_out;
     int64_t gstride_bias;
 };
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(256) void layer_gemm_kernel(FwdArgs a) {
     const int g = blockIdx.z;
     Operand A = a.A, Bo = a.B;
     Bo.p = (const T*)Bo.p + g * a.gstride_w;
-    if (a.mode != 0) A.p = (const T*)A.p + g * a.gstride_out;  // per-group activations
+    if (a.mode != 0) A.p = (const T*)A.p + g * a.gstride_in;  // per-group activations
     const int m0 = blockIdx.x * kTM, n0 = blockIdx.y * kTN;
     f32x16 acc[2][2], accb[2];
 #pragma unroll
@@ -280,8 +281,8 @@ struct WgradArgs {
     const void* x;     // [B][ld]
     const float* dv;   // [G][B]
     int64_t ld;
-    int B, S, H, chunk, nchunk;
-    int nt_h, nt_s;    // 128-tiles along H and S
+    int B, S, H, H2, chunk, nchunk;  // H, H2: first and second hidden widths
+    int nt_h, nt_h2, nt_s;  // 128-tiles along H, H2 and S
     float* part;       // [G][nchunk][Pp]
     int64_t Pp;
     int64_t off_w1, off_b1, off_w2, off_b2, off_w3, off_b3;
@@ -295,13 +296,13 @@ __global__ __launch_bounds__(256) void iql_wgrad_kernel(WgradArgs a) {
     const int g = blockIdx.z / a.nchunk, c = blockIdx.z - g * a.nchunk;
     const int b0 = c * a.chunk;
     const int K = min(a.chunk, a.B - b0);
-    const int64_t gs = (int64_t)g * a.B * a.H;
+    const int64_t gs = (int64_t)g * a.B * a.H, gs2 = (int64_t)g * a.B * a.H2;
     float* part = a.part + ((int64_t)g * a.nchunk + c) * a.Pp;
-    const int n_w2 = a.nt_h * a.nt_h, n_w1 = a.nt_h * a.nt_s;
+    const int n_w2 = a.nt_h2 * a.nt_h, n_w1 = a.nt_h * a.nt_s;
     int job = blockIdx.x;
     const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
     const int wv = threadIdx.x >> 6, wm = wv >> 1, wn = wv & 1;
-    if (job == n_w2 + n_w1 + a.nt_h) {
+    if (job == n_w2 + n_w1 + a.nt_h2) {
         // db3 = sum of dv over the chunk
         float s = 0.f;
         for (int i = threadIdx.x; i < K; i += 256) s += a.dv[(int64_t)g * a.B + b0 + i];
@@ -314,10 +315,10 @@ __global__ __launch_bounds__(256) void iql_wgrad_kernel(WgradArgs a) {
     int M, N;
     float *dst, *bias_dst;
     int ldo;
-    if (job < n_w2) {
-        A = Operand{(const T*)a.dz2 + gs, a.H, a.H, K, 1, 0, b0};
+    if (job < n_w2) {  // dW2 [H2][H] = dz2^T h1
+        A = Operand{(const T*)a.dz2 + gs2, a.H2, a.H2, K, 1, 0, b0};
         Bo = Operand{(const T*)a.h1 + gs, a.H, a.H, K, 1, 0, b0};
-        M = a.H; N = a.H; dst = part + a.off_w2; bias_dst = part + a.off_b2; ldo = a.H;
+        M = a.H2; N = a.H; dst = part + a.off_w2; bias_dst = part + a.off_b2; ldo = a.H;
     } else if (job < n_w2 + n_w1) {
         job -= n_w2;
         A = Operand{(const T*)a.dz1 + gs, a.H, a.H, K, 1, 0, b0};
@@ -325,9 +326,9 @@ __global__ __launch_bounds__(256) void iql_wgrad_kernel(WgradArgs a) {
         M = a.H; N = a.S; dst = part + a.off_w1; bias_dst = part + a.off_b1; ldo = a.S;
     } else {
         job -= n_w2 + n_w1;  // dw3: row sums of p2^T, one 128-row tile
-        A = Operand{(const T*)a.p2 + gs, a.H, a.H, K, 1, 0, b0};
+        A = Operand{(const T*)a.p2 + gs2, a.H2, a.H2, K, 1, 0, b0};
         Bo = A;
-        M = a.H; N = 0; dst = nullptr; bias_dst = part + a.off_w3; ldo = 0;
+        M = a.H2; N = 0; dst = nullptr; bias_dst = part + a.off_w3; ldo = 0;
     }
     const int ntn = N > 0 ? (N + kTN - 1) / kTN : 1;
     const int m0 = (job / ntn) * kTM, n0 = (job % ntn) * kTN;
@@ -389,12 +390,12 @@ hipError_t launch_iql_layered_forward(const IqlDims& d, const IqlBuffers& b, con
 static hipError_t layered_launch(const IqlDims& d, const IqlBuffers& b, const float* tau, const void* states,
                                  int64_t ld, const float* q, int B, float* out_v, const ValueOut* vo,
                                  hipStream_t stream) {
-    const int G = d.G, S = d.S, H = d.H;
+    // H: first hidden width (h1, dz1), H2: second (z2, dz2, p2)
+    const int G = d.G, S = d.S, H = d.H, H2 = d.H2;
     const int nchunk = (B + kChunk - 1) / kChunk;
     const int nblk = (B + kRowsPerBlock - 1) / kRowsPerBlock;
-    const int64_t gH = (int64_t)B * H;  // per-group activation stride of this call
-    const size_t esz = d.dtype == 1 ? 2 : 4;
-    (void)esz;
+    const int64_t gH = (int64_t)B * H, gH2 = (int64_t)B * H2;  // per-group activation strides of this call
+    const int64_t ob2 = (int64_t)H * S + H + (int64_t)H2 * H;   // flat offset of b2
     // L1: h1 = relu(s W1^T + b1)
     FwdArgs f1{};
     f1.A = Operand{states, ld, B, S, 0, 0, 0};
@@ -406,23 +407,24 @@ static hipError_t layered_launch(const IqlDims& d, const IqlBuffers& b, const fl
     const dim3 gridf((B + kTM - 1) / kTM, (H + kTN - 1) / kTN, G);
     if (d.dtype == 1) hipLaunchKernelGGL(layer_gemm_kernel<uint16_t>, gridf, dim3(256), 0, stream, f1);
     else hipLaunchKernelGGL(layer_gemm_kernel<float>, gridf, dim3(256), 0, stream, f1);
-    // L2: z2 = h1 W2^T + b2 (f32)
+    // L2: z2 = h1 W2^T + b2 (f32), W2 [H2][H]
     FwdArgs f2{};
     f2.A = Operand{b.act_h1, H, B, H, 0, 0, 0};
-    f2.B = Operand{b.w2s, H, H, H, 0, 0, 0};
-    f2.M = B; f2.N = H; f2.K = H;
-    f2.bias = b.params + (int64_t)H * S + H + (int64_t)H * H; f2.gstride_bias = d.P;
+    f2.B = Operand{b.w2s, H, H2, H, 0, 0, 0};
+    f2.M = B; f2.N = H2; f2.K = H;
+    f2.bias = b.params + ob2; f2.gstride_bias = d.P;
     f2.out = b.act_z2; f2.mode = 1;
-    f2.gstride_w = (int64_t)H * H; f2.gstride_out = gH;
-    if (d.dtype == 1) hipLaunchKernelGGL(layer_gemm_kernel<uint16_t>, gridf, dim3(256), 0, stream, f2);
-    else hipLaunchKernelGGL(layer_gemm_kernel<float>, gridf, dim3(256), 0, stream, f2);
+    f2.gstride_w = (int64_t)H2 * H; f2.gstride_in = gH; f2.gstride_out = gH2;
+    const dim3 grid2((B + kTM - 1) / kTM, (H2 + kTN - 1) / kTN, G);
+    if (d.dtype == 1) hipLaunchKernelGGL(layer_gemm_kernel<uint16_t>, grid2, dim3(256), 0, stream, f2);
+    else hipLaunchKernelGGL(layer_gemm_kernel<float>, grid2, dim3(256), 0, stream, f2);
     // R: v, expectile, dv, dz2, p2
     RowArgs ra{};
     ra.z2 = b.act_z2; ra.q = q; ra.params = b.params; ra.dz2 = b.act_dz2; ra.p2 = b.act_p2;
     ra.dv_out = b.act_dv; ra.out_v = out_v; ra.loss_part = b.loss_part;
     ra.tau0 = tau[0]; ra.tau1 = tau[G > 1 ? 1 : 0]; ra.invB = 1.f / (float)B;
-    ra.B = B; ra.H = H; ra.nblk = nblk; ra.P = d.P;
-    ra.w3off = (int64_t)H * S + H + (int64_t)H * H + H;
+    ra.B = B; ra.H = H2; ra.nblk = nblk; ra.P = d.P;
+    ra.w3off = ob2 + H2;
     if (vo) {
         ra.fwd_only = 1;
         ra.vo = *vo;
@@ -430,24 +432,24 @@ static hipError_t layered_launch(const IqlDims& d, const IqlBuffers& b, const fl
     if (d.dtype == 1) hipLaunchKernelGGL(iql_rows_kernel<uint16_t>, dim3(nblk, G), dim3(256), 0, stream, ra);
     else hipLaunchKernelGGL(iql_rows_kernel<float>, dim3(nblk, G), dim3(256), 0, stream, ra);
     if (vo) return hipGetLastError();
-    // L3: dz1 = (dz2 W2) * relu'(z1)   (B operand: W2^T shadow, rows h1, k = h2)
+    // L3: dz1 = (dz2 W2) * relu'(z1)   (B operand: W2^T shadow [H][H2], rows h1, k = h2)
     FwdArgs f3{};
-    f3.A = Operand{b.act_dz2, H, B, H, 0, 0, 0};
-    f3.B = Operand{b.w2ts, H, H, H, 0, 0, 0};
-    f3.M = B; f3.N = H; f3.K = H;
+    f3.A = Operand{b.act_dz2, H2, B, H2, 0, 0, 0};
+    f3.B = Operand{b.w2ts, H2, H, H2, 0, 0, 0};
+    f3.M = B; f3.N = H; f3.K = H2;
     f3.bias = nullptr; f3.out = b.act_dz1; f3.mask = b.act_h1; f3.mode = 2;
-    f3.gstride_w = (int64_t)H * H; f3.gstride_out = gH;
+    f3.gstride_w = (int64_t)H2 * H; f3.gstride_in = gH2; f3.gstride_out = gH;
     if (d.dtype == 1) hipLaunchKernelGGL(layer_gemm_kernel<uint16_t>, gridf, dim3(256), 0, stream, f3);
     else hipLaunchKernelGGL(layer_gemm_kernel<float>, gridf, dim3(256), 0, stream, f3);
     // W: split-K weight gradients into the partial rows of each chunk
     WgradArgs wa{};
     wa.dz2 = b.act_dz2; wa.h1 = b.act_h1; wa.dz1 = b.act_dz1; wa.p2 = b.act_p2; wa.x = states;
-    wa.dv = b.act_dv; wa.ld = ld; wa.B = B; wa.S = S; wa.H = H; wa.chunk = kChunk; wa.nchunk = nchunk;
-    wa.nt_h = (H + kTM - 1) / kTM; wa.nt_s = (S + kTN - 1) / kTN;
+    wa.dv = b.act_dv; wa.ld = ld; wa.B = B; wa.S = S; wa.H = H; wa.H2 = H2; wa.chunk = kChunk; wa.nchunk = nchunk;
+    wa.nt_h = (H + kTM - 1) / kTM; wa.nt_h2 = (H2 + kTM - 1) / kTM; wa.nt_s = (S + kTN - 1) / kTN;
     wa.part = b.part; wa.Pp = d.Pp;
     wa.off_w1 = 0; wa.off_b1 = (int64_t)H * S; wa.off_w2 = wa.off_b1 + H;
-    wa.off_b2 = wa.off_w2 + (int64_t)H * H; wa.off_w3 = wa.off_b2 + H; wa.off_b3 = wa.off_w3 + H;
-    const int jobs = wa.nt_h * wa.nt_h + wa.nt_h * wa.nt_s + wa.nt_h + 1;
+    wa.off_b2 = ob2; wa.off_w3 = ob2 + H2; wa.off_b3 = wa.off_w3 + H2;
+    const int jobs = wa.nt_h2 * wa.nt_h + wa.nt_h * wa.nt_s + wa.nt_h2 + 1;
     const dim3 gridw(jobs, 1, nchunk * G);
     if (d.dtype == 1) hipLaunchKernelGGL(iql_wgrad_kernel<uint16_t>, gridw, dim3(256), 0, stream, wa);
     else hipLaunchKernelGGL(iql_wgrad_kernel<float>, gridw, dim3(256), 0, stream, wa);

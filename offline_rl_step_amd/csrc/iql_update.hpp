@@ -116,17 +116,18 @@ IQLH_DEV bool adam_elem(float gi, float& p, float& m, float& v, float bc1, float
 }
 
 // Operand-typed shadows of flat parameter i of one group (a group has fewer
-// than 2^31 parameters, so the row / column split is a 32-bit division).
+// than 2^31 parameters, so the row / column split is a 32-bit division):
+// W1 [H][SP], W2 [H2][H] and its transpose [H][H2].
 template <typename T>
-IQLH_DEV void iql_store_shadow(int64_t i, float p, int H, int S, int SP, T* w1s, T* w2s, T* w2ts) {
-    const int64_t ow2 = (int64_t)H * S + H, ow2e = ow2 + (int64_t)H * H;
+IQLH_DEV void iql_store_shadow(int64_t i, float p, int H, int H2, int S, int SP, T* w1s, T* w2s, T* w2ts) {
+    const int64_t ow2 = (int64_t)H * S + H, ow2e = ow2 + (int64_t)H2 * H;
     if (i < (int64_t)H * S) {
         const uint32_t r = (uint32_t)i / (uint32_t)S, cc = (uint32_t)i - r * (uint32_t)S;
         w1s[(int64_t)r * SP + cc] = to_shadow<T>(p);
     } else if (i >= ow2 && i < ow2e) {
         const uint32_t q = (uint32_t)(i - ow2), r = q / (uint32_t)H, cc = q - r * (uint32_t)H;
         w2s[q] = to_shadow<T>(p);
-        w2ts[cc * H + r] = to_shadow<T>(p);
+        w2ts[cc * H2 + r] = to_shadow<T>(p);
     }
 }
 
@@ -136,7 +137,8 @@ IQLH_DEV void iql_store_shadow(int64_t i, float p, int H, int S, int SP, T* w1s,
 // its use (the use would wait for the store too).
 template <typename T>
 IQLH_DEV void iql_adam_param(int64_t i, float gi, float p, float mi, float vi, float ti, float bc1, float bc2,
-                             float decay, const AdamHyper& hp, int H, int S, int SP, float* __restrict__ prm,
+                             float decay, const AdamHyper& hp, int H, int H2, int S, int SP,
+                             float* __restrict__ prm,
                              float* __restrict__ gr, float* __restrict__ m, float* __restrict__ v,
                              float* __restrict__ tg, T* w1s, T* w2s, T* w2ts, bool& bad, bool& bad_state) {
     const bool ok = adam_elem(gi, p, mi, vi, bc1, bc2, decay, hp);
@@ -152,7 +154,7 @@ IQLH_DEV void iql_adam_param(int64_t i, float gi, float p, float mi, float vi, f
     // Polyak target with the step's parameters (unchanged ones when the
     // update was skipped): target += ema (p - target)
     if (hp.ema > 0.f) tg[i] = fmaf(hp.ema, p - ti, ti);
-    iql_store_shadow<T>(i, p, H, S, SP, w1s, w2s, w2ts);
+    iql_store_shadow<T>(i, p, H, H2, S, SP, w1s, w2s, w2ts);
 }
 
 // Clip and Adam over the parameters of group g, block bx of nbx; refreshes
@@ -163,15 +165,15 @@ IQLH_DEV void iql_adam_block(const IqlDims& d, const IqlBuffers& b, const AdamHy
                              float* __restrict__ out_gnorm, int rb, int bx, int g, int nbx) {
     __shared__ float red[4];
     const int64_t P = d.P;
-    const int H = d.H, S = d.S, SP = d.S_pad;
+    const int H = d.H, H2 = d.H2, S = d.S, SP = d.S_pad;
     float* prm = b.params + (int64_t)g * P;
     float* gr = b.grad + (int64_t)g * P;
     float* m = b.m + (int64_t)g * P;
     float* v = b.v + (int64_t)g * P;
     float* tg = b.target + (int64_t)g * P;
     T* w1s = (T*)b.w1s + (int64_t)g * H * SP;
-    T* w2s = (T*)b.w2s + (int64_t)g * H * H;
-    T* w2ts = (T*)b.w2ts + (int64_t)g * H * H;
+    T* w2s = (T*)b.w2s + (int64_t)g * H2 * H;
+    T* w2ts = (T*)b.w2ts + (int64_t)g * H2 * H;
     // The first element's state does not depend on the norm: it is loaded
     // before the fold, at a clamped index (P >= 1) so that no lane-dependent
     // branch surrounds the loads.
@@ -187,11 +189,11 @@ IQLH_DEV void iql_adam_block(const IqlDims& d, const IqlBuffers& b, const AdamHy
     const float decay = 1.f - hp.lr * hp.weight_decay;
     bool bad = false, bad_state = false;
     if (i0 < P)
-        iql_adam_param<T>(i0, pg * c, pp, pm, pv, pt, bc1, bc2, decay, hp, H, S, SP, prm, gr, m, v, tg, w1s, w2s,
-                          w2ts, bad, bad_state);
+        iql_adam_param<T>(i0, pg * c, pp, pm, pv, pt, bc1, bc2, decay, hp, H, H2, S, SP, prm, gr, m, v, tg, w1s,
+                          w2s, w2ts, bad, bad_state);
     for (int64_t i = i0 + stride; i < P; i += stride)
-        iql_adam_param<T>(i, gr[i] * c, prm[i], m[i], v[i], tg[i], bc1, bc2, decay, hp, H, S, SP, prm, gr, m, v, tg,
-                          w1s, w2s, w2ts, bad, bad_state);
+        iql_adam_param<T>(i, gr[i] * c, prm[i], m[i], v[i], tg[i], bc1, bc2, decay, hp, H, H2, S, SP, prm, gr, m, v,
+                          tg, w1s, w2s, w2ts, bad, bad_state);
     // (stored last: a wave would wait for this store at its next use of a load)
     if (bx == 0 && threadIdx.x == 0 && out_gnorm) out_gnorm[g] = nrm;
     if (bad) set_flag(b.flags, 0x1);

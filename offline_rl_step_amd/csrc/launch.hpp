@@ -20,6 +20,7 @@ struct HerArgs {
     int32_t* out_actions;
     float* out_rewards;
     float* out_dones;
+    float* out_isw;  // importance-sampling weights of the HER rows (1; 0 for a zeroed row) or null
     int32_t* flags;
     int64_t buffer_size;
     int64_t out_ld;
@@ -91,7 +92,8 @@ hipError_t launch_adam_flat(float* params, float* grad, float* m, float* v, cons
 
 // ------------------------------------------------------------------ IQL
 struct IqlDims {
-    int S, H, G, dtype;  // dtype: 0 f32, 1 bf16
+    int S, H, G, dtype;  // H: first hidden width; dtype: 0 f32, 1 bf16
+    int H2;              // second hidden width (== H except on the layered path)
     int layered;         // 0: fused tile kernel; 1: layered GEMMs through HBM
     int big;             // with layered: the wide-hidden bf16 kernels (iql_big.hip)
     int S_pad;           // columns of the W1 shadow (multiple of 32)

@@ -325,6 +325,16 @@ hipError_t launch_per_sample(const float* p, int64_t size, int n, uint64_t seed,
         const int waves = (n + a.dpw - 1) / a.dpw;
         a.nwg = (waves + 3) / 4;
         const size_t lds = a.nb <= kPerTable ? (size_t)a.nb * sizeof(double) : 0;
+        // the staged table takes up to 64 KB of dynamic LDS (plus the
+        // kernel's few static words): raise the kernel's limit to that once
+        static bool attr_set = false;
+        if (!attr_set) {
+            const hipError_t e = hipFuncSetAttribute((const void*)per_draw_kernel,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)(kPerTable * sizeof(double)));
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
         hipLaunchKernelGGL(per_draw_kernel, dim3(a.nwg), dim3(256), lds, stream, a);
         hipLaunchKernelGGL(per_weight_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, a);
     }

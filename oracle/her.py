@@ -109,7 +109,9 @@ def relabel(states, next_states, actions, dones, source_idx, donor_idx, goal_dim
             threshold=0.01, reward_hit=1.0, reward_miss=-0.01, out_bf16=False):
     """Relabel the rows named by source_idx with the goals of donor_idx.
 
-    Returns dict(states, next_states, actions, rewards, dones).  ``states`` is
+    Returns dict(states, next_states, actions, rewards, dones, is_weights).
+    ``is_weights`` is 1 per row (relabelled rows are not sampled by
+    priority, section "How HER Interacts with GPU PER").  ``states`` is
     float32, or float32 holding bfloat16-rounded values when ``out_bf16``.
     """
     src = np.asarray(source_idx, dtype=np.int64)
@@ -126,7 +128,16 @@ def relabel(states, next_states, actions, dones, source_idx, donor_idx, goal_dim
     return dict(states=out_s, next_states=out_ns,
                 actions=np.asarray(actions[src], dtype=np.int32),
                 rewards=rew,
-                dones=np.asarray(dones[src], dtype=np.float32))
+                dones=np.asarray(dones[src], dtype=np.float32),
+                is_weights=np.ones(src.shape[0], dtype=np.float32))
+
+
+def merged_is_weights(normal_is_weights, n_her):
+    """Importance-sampling weights of the merged batch ("How HER Interacts
+    with GPU PER"): the prioritized rows keep their own weights and come
+    first; the relabelled rows are not drawn by priority and weigh 1 each."""
+    w = np.asarray(normal_is_weights, dtype=np.float32)
+    return np.concatenate([w, np.ones(int(n_her), dtype=np.float32)])
 
 
 def her_step(buffer, source_idx, goal_dim, strategy, seed, step, **kw):

@@ -22,7 +22,7 @@ class Workload:
     B: int                 # merged batch (normal + HER rows)
     S: int                 # state_dim
     G: int                 # goal_dim (first G state entries)
-    H: int                 # value-MLP hidden width (both hidden layers)
+    H: int                 # value-MLP first hidden width (and second when H2 is 0)
     A: int                 # number of actions
     dtype: str             # "f32" or "bf16" GEMM operand type
     groups: int            # independent IQL trainers sharing the batch
@@ -42,15 +42,20 @@ class Workload:
     budget: bool = False
     budget_scales: tuple = (1.0, 5.0, 0.5, 0.2)
     budget_fractions: tuple = (0.70, 0.15, 0.10, 0.05)
+    H2: int = 0            # second hidden width, 0 = H
 
     @property
     def n_her(self):
         return int(float(self.B) * float(self.her_ratio))
 
     @property
+    def hidden2(self):
+        return self.H2 or self.H
+
+    @property
     def n_params(self):
-        S, H = self.S, self.H
-        return S * H + H + H * H + H + H + 1
+        S, H1, H2 = self.S, self.H, self.hidden2
+        return S * H1 + H1 + H2 * H1 + H2 + H2 + 1
 
     @property
     def n_budget(self):
@@ -172,13 +177,13 @@ def kaiming_uniform(w, seed=DEFAULT_SEED + 10):
     """He-uniform float32 weights U(+-sqrt(6/fan_in)), zero biases, flat in the
     order w1, b1, w2, b2, w3, b3."""
     g = rng(seed)
-    S, H = w.S, w.H
+    S, H1, H2 = w.S, w.H, w.hidden2
     parts = [
-        g.uniform(-1, 1, size=H * S) * np.sqrt(6.0 / S),
-        np.zeros(H),
-        g.uniform(-1, 1, size=H * H) * np.sqrt(6.0 / H),
-        np.zeros(H),
-        g.uniform(-1, 1, size=H) * np.sqrt(6.0 / H),
+        g.uniform(-1, 1, size=H1 * S) * np.sqrt(6.0 / S),
+        np.zeros(H1),
+        g.uniform(-1, 1, size=H2 * H1) * np.sqrt(6.0 / H1),
+        np.zeros(H2),
+        g.uniform(-1, 1, size=H2) * np.sqrt(6.0 / H2),
         np.zeros(1),
     ]
     return np.concatenate(parts).astype(np.float32)

@@ -37,7 +37,7 @@ def test_struct_sizes_match_header_layout(m):
     assert ctypes.sizeof(m.IqlConfig) == 72
     assert ctypes.sizeof(m.HerConfig) == 32
     assert ctypes.sizeof(m.HerBuffer) == 72
-    assert ctypes.sizeof(m.HerOut) == 72
+    assert ctypes.sizeof(m.HerOut) == 80
     assert ctypes.sizeof(m.Adam) == 72
     assert ctypes.sizeof(m.HerStep) == 48
     assert ctypes.sizeof(m.BudgetStep) == 80

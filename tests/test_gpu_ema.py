@@ -58,7 +58,7 @@ def test_standalone_update_matches_oracle(m, wname):
     import torch
     w = synth.WORKLOADS[wname]
     tr, tX, tq = _trainer(m, w, 512)
-    P = iql.num_params(w.S, w.H, w.H)
+    P = iql.num_params(w.S, w.H, w.hidden2)
     assert np.array_equal(_get(tr, 0, "target"), _get(tr, 0, "params"))  # starts at the initial weights
     tr.train_step(tX, tq, 512)
     g = np.random.default_rng(5)

@@ -22,7 +22,8 @@ def m():
 
 CASES = [("b16384_s128_h128_bf16_g2", {}, 3000, 2e-2), ("tiny_b256_s16_h32", {}, 200, 1e-4),
          ("b4096_s42_h128_f32", {}, 1000, 1e-4), ("stress_b65536_s256_h512_bf16", {}, 2000, 2e-2),
-         ("b16384_s128_h128_bf16_g2", {"S": 100, "H": 256}, 700, 2e-2)]
+         ("b16384_s128_h128_bf16_g2", {"S": 100, "H": 256}, 700, 2e-2),
+         ("b16384_s128_h128_bf16_g2", {"S": 64, "H": 96, "H2": 160}, 900, 2e-2)]
 
 
 def _setup(m, wname, kw, B, seed=0):
@@ -36,7 +37,7 @@ def _setup(m, wname, kw, B, seed=0):
     r = np.where(g.random(B) < 0.3, 1.0, -0.01).astype(np.float32)
     d = (g.random(B) < 0.2).astype(np.float32)
     cfg = m.make_config(w.S, w.H, B, num_groups=w.groups, compute_dtype=m.BF16 if bf else m.F32, states_ld=w.S,
-                        tau=w.taus)
+                        tau=w.taus, hidden2=w.H2)
     inits = synth.group_inits(w)
     tr = m.IqlTrainer(cfg, np.concatenate(inits))
     tX = to_dev(Xn, torch.bfloat16 if bf else torch.float32)
@@ -52,7 +53,7 @@ def test_values_and_target_match_oracle(m, wname, kw, B, rtol):
     tr.forward_values(tX, B, v, rewards=to_dev(r), dones=to_dev(d), gamma=0.97, out_target=tg)
     sync()
     for g in range(w.groups):
-        ref_v = iql.forward(iql.unflatten(inits[g].astype(np.float64), w.S, w.H, w.H), Xn)[0]
+        ref_v = iql.forward(iql.unflatten(inits[g].astype(np.float64), w.S, w.H, w.hidden2), Xn)[0]
         assert_rel(host(v[g]), ref_v, rtol, f"{wname} V(s') g{g}")
         ref_t = iql.bootstrap_target(r, d, ref_v, 0.97)
         assert_rel(host(tg[g]), ref_t, rtol, f"{wname} target g{g}")
@@ -66,7 +67,7 @@ def test_values_and_target_match_oracle(m, wname, kw, B, rtol):
 def test_values_equal_train_step_v_and_change_nothing(m, wname, kw, B, rtol):
     import torch
     w, tr, Xn, tX, r, d, inits = _setup(m, wname, kw, B, seed=1)
-    P = iql.num_params(w.S, w.H, w.H)
+    P = iql.num_params(w.S, w.H, w.hidden2)
     before = torch.zeros(P, device=dev())
     tr.get_state(0, before)
     v = torch.zeros((w.groups, B), dtype=torch.float32, device=dev())

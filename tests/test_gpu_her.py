@@ -32,15 +32,17 @@ def _run(m, buf, src, G, strategy, seed, step, out_bf16, ld=None, merged_rows=0,
     o_rew = torch.zeros(n, dtype=torch.float32, device=d)
     o_done = torch.zeros(n, dtype=torch.float32, device=d)
     o_don = torch.zeros(n, dtype=torch.int32, device=d)
+    W = torch.full((merged_rows + n,), 7.0, dtype=torch.float32, device=d)  # the merged batch's IS weights
     cfg = m.her_config(S, G, strategy)
     hb = m.her_buffer(t_states, t_next, t_act, t_done, t_ends, buffer_size=buf["buffer_size"])
     tail = X.data_ptr() + merged_rows * ld * X.element_size()
     ho = m.her_out(tail, m.BF16 if out_bf16 else m.F32, ld, o_rew, next_states=o_next, actions=o_act,
-                   dones=o_done, donor_idx=o_don, d_flags=flags)
+                   dones=o_done, donor_idx=o_don, d_flags=flags,
+                   is_weights=W.data_ptr() + merged_rows * W.element_size())
     m.her_relabel(cfg, hb, t_src, n, seed, t_step, ho)
     sync()
     return dict(X=X, states=X[merged_rows:, :S], next_states=o_next, actions=o_act, rewards=o_rew,
-                dones=o_done, donor_idx=o_don)
+                dones=o_done, donor_idx=o_don, W=W, is_weights=W[merged_rows:])
 
 
 def _compare(got, ref, out_bf16):
@@ -51,6 +53,7 @@ def _compare(got, ref, out_bf16):
     assert np.array_equal(host(got["actions"]), ref["actions"])
     assert np.array_equal(host(got["dones"]), ref["dones"])
     assert np.array_equal(host(got["rewards"]).view(np.uint32), ref["rewards"].view(np.uint32))
+    assert np.array_equal(host(got["is_weights"]).view(np.uint32), ref["is_weights"].view(np.uint32))
 
 
 @pytest.fixture(scope="module")
@@ -90,6 +93,10 @@ def test_her_ragged_episodes_and_merged_batch(m, strategy):
     # rows before the HER block and the padding columns are untouched
     X = host(got["X"])
     assert np.all(X[:777] == 7.0) and np.all(X[777:, S:] == 7.0)
+    # the merged weights: the prioritized rows' own weights (here the 7.0
+    # sentinel), then 1 for every HER row
+    Wm = host(got["W"])
+    assert np.array_equal(Wm, her.merged_is_weights(np.full(777, 7.0, np.float32), len(src)))
 
 
 def test_her_equal_goals_reward_hit(m):
@@ -123,6 +130,7 @@ def test_her_bad_index_flag(m):
     don = host(got["donor_idx"])
     assert don[1] == -1 and don[3] == -1
     assert np.all(host(got["states"])[[1, 3]] == 0.0) and np.all(host(got["rewards"])[[1, 3]] == 0.0)
+    assert np.array_equal(host(got["is_weights"]), np.array([1, 0, 1, 0, 1], np.float32))
     ok = np.array([0, 2, 4])
     safe = np.where((src >= 0) & (src < w.C), src, 0)
     ref = her.her_step(buf, safe, w.G, her.FUTURE, seed=1, step=0)

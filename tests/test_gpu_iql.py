@@ -30,7 +30,7 @@ class Setup:
         import torch
         self.m, self.w = m, w
         self.B = B or w.B
-        self.S, self.H, self.G = w.S, w.H, w.groups
+        self.S, self.H, self.H2, self.G = w.S, w.H, w.hidden2, w.groups
         self.ld = ld or w.S
         self.taus = taus or w.taus
         self.bf16 = w.dtype == "bf16"
@@ -42,10 +42,11 @@ class Setup:
         self.q = (g.standard_normal(self.B) * w.q_sd).astype(np.float32)
         self.inits = synth.group_inits(w, seed=synth.DEFAULT_SEED + 10 + seed)
         self.hp = iql.AdamHP(lr=w.lr, max_grad_norm=w.max_grad_norm)
-        self.P = iql.num_params(self.S, self.H, self.H)
+        self.P = iql.num_params(self.S, self.H, self.H2)
         self.cfg = m.make_config(self.S, self.H, self.B, num_groups=self.G,
                                  compute_dtype=m.BF16 if self.bf16 else m.F32, states_ld=self.ld,
-                                 tau=self.taus, lr=w.lr, max_grad_norm=w.max_grad_norm)
+                                 tau=self.taus, lr=w.lr, max_grad_norm=w.max_grad_norm,
+                                 hidden2=w.H2)
         self.tr = m.IqlTrainer(self.cfg, np.concatenate(self.inits))
         Xp = np.zeros((self.B, self.ld), np.float32)
         Xp[:, :self.S] = X
@@ -61,7 +62,7 @@ class Setup:
 
     def oracle_step(self, states=None, rnd=None):
         sts = self.oracle if states is None else states
-        return [iql.train_step(sts[g], self.X, self.q, self.S, self.H, self.H, self.taus[g], self.hp, rnd)
+        return [iql.train_step(sts[g], self.X, self.q, self.S, self.H, self.H2, self.taus[g], self.hp, rnd)
                 for g in range(self.G)]
 
     def state(self, g):
@@ -249,6 +250,41 @@ def test_layered_bf16_ragged(m):
 def test_layered_fp32(m):
     w = synth.shrink(synth.WORKLOADS["tiny_b256_s16_h32"], S=20, H=64, G=4)
     _one_step(m, w, 1e-4, B=1000)
+
+
+# ------------------------------------------- two different hidden widths
+# W1 [H1, S], W2 [H2, H1], w3 [H2] (the pages' v_h1 / v_h2); the layered
+# kernels, with tiles ragged in each width separately
+@pytest.mark.parametrize("S,H1,H2,B", [(16, 48, 24, 300), (20, 130, 200, 1000), (42, 128, 64, 2049)])
+def test_two_hidden_widths_fp32(m, S, H1, H2, B):
+    w = synth.shrink(synth.WORKLOADS["tiny_b256_s16_h32"], S=S, H=H1, H2=H2, G=4)
+    _one_step(m, w, 1e-4, B=B)
+
+
+def test_two_hidden_widths_bf16_two_groups_ten_steps(m):
+    """bf16 operands, two groups with different tau, H1 = 160 > H2 = 96:
+    step 1 and a teacher-forced step 10 at the bf16 bar."""
+    w = synth.shrink(synth.WORKLOADS["b16384_s128_h128_bf16_g2"], S=40, H=160, H2=96, G=8)
+    s = Setup(m, w, B=3000, ld=48, taus=(0.7, 0.3))
+    before1 = [s.state(g) for g in range(s.G)]
+    for k in range(1, 11):
+        if k == 10:
+            before = [s.state(g) for g in range(s.G)]
+        s.gpu_step()
+        sync()
+        if k in (1, 10):
+            forced = [st.copy() for st in (before1 if k == 1 else before)]
+            refs = s.oracle_step(forced)
+            s.compare_step(refs, forced, 2e-2, k, f"H1 != H2 step {k}")
+    rc, flags = s.tr.status()
+    assert rc == m.OK and flags == 0
+
+
+def test_two_hidden_widths_param_count(m):
+    cfg = m.make_config(42, 128, 64, hidden2=64)
+    assert m.iql_config_num_params(cfg) == 42 * 128 + 128 + 64 * 128 + 64 + 64 + 1
+    cfg = m.make_config(42, 128, 64)
+    assert m.iql_config_num_params(cfg) == m.iql_num_params(42, 128)
 
 
 # ------------------------------------------------- wide-hidden bf16 path

@@ -37,7 +37,10 @@ def _run(m, p, n, seed, beta, step=None):
 
 @pytest.mark.parametrize("size,n,zero_frac", [(1, 5, 0.0), (1000, 4096, 0.2), (2049, 777, 0.5),
                                               ((1 << 20) + 7, 8192, 0.2), (5000, 1, 0.9),
-                                              # more than 8192 blocks: the table of block ends in global memory
+                                              # both sides of the switch at 8192 blocks (2^24 rows): the
+                                              # last table that fits in LDS (8192 and 8191 blocks), then
+                                              # the table of block ends in global memory
+                                              (1 << 24, 4096, 0.2), ((1 << 24) - 2048, 4096, 0.2),
                                               ((1 << 24) + 3001, 4096, 0.2)])
 def test_draws_match_oracle(m, size, n, zero_frac):
     g = np.random.default_rng(size)

@@ -69,7 +69,7 @@ class Rig:
         # relabelled rows outside the batch when not aliased
         self.Xh = torch.zeros((n, S), dtype=inp.sdt, device=d)
         cfg = m.make_config(S, w.H, B, num_groups=w.groups, compute_dtype=m.BF16 if inp.bf16 else m.F32,
-                            states_ld=S, tau=w.taus, lr=w.lr, max_grad_norm=w.max_grad_norm)
+                            states_ld=S, tau=w.taus, lr=w.lr, max_grad_norm=w.max_grad_norm, hidden2=w.H2)
         self.tr = m.IqlTrainer(cfg, np.concatenate(inp.inits))
         self.out_v = torch.zeros((w.groups, B), dtype=torch.float32, device=d)
         self.out_loss = torch.zeros(w.groups, dtype=torch.float32, device=d)
@@ -80,6 +80,9 @@ class Rig:
         self.act = torch.zeros(n, dtype=torch.int32, device=d)
         self.done = torch.zeros(n, dtype=torch.float32, device=d)
         self.donor = torch.zeros(n, dtype=torch.int32, device=d)
+        # the merged batch's importance-sampling weights: the caller's for the
+        # normal rows (0.5 here), the relabelling's for the HER tail
+        self.isw = torch.full((B,), 0.5, dtype=torch.float32, device=d)
         self.hcfg = m.her_config(S, w.G, m.HER_FUTURE if strategy is None else strategy)
         self.hbuf = m.her_buffer(inp.t_states, inp.t_next, inp.t_actions, inp.t_dones, inp.t_ends)
         tail = (self.X.data_ptr() + (B - n) * S * self.X.element_size()) if alias else self.Xh.data_ptr()
@@ -87,7 +90,8 @@ class Rig:
             self.hout = m.her_out(tail, m.BF16 if inp.bf16 else m.F32, S, self.rew, d_flags=self.tr.flags)
         else:
             self.hout = m.her_out(tail, m.BF16 if inp.bf16 else m.F32, S, self.rew, next_states=self.nxt,
-                                  actions=self.act, dones=self.done, donor_idx=self.donor, d_flags=self.tr.flags)
+                                  actions=self.act, dones=self.done, donor_idx=self.donor, d_flags=self.tr.flags,
+                                  is_weights=self.isw.data_ptr() + (B - n) * self.isw.element_size())
         P = inp.n_budget
         self.theta = to_dev(inp.theta)
         self.tm = torch.zeros(P, dtype=torch.float32, device=d)
@@ -131,7 +135,7 @@ class Rig:
         out = {"X": self.X, "Xh": self.Xh, "rew": self.rew, "next": self.nxt, "act": self.act, "done": self.done,
                "donor": self.donor, "v": self.out_v, "loss": self.out_loss, "gn": self.out_gn, "pi": self.pi,
                "theta": self.theta, "theta_m": self.tm, "theta_v": self.tv, "theta_t": self.tt,
-               "grad": self.grad}
+               "grad": self.grad, "isw": self.isw}
         if self.norms is not None:
             out["norms"] = self.norms
         P = self.tr.n_params
@@ -244,6 +248,7 @@ def test_whole_step_relabelling_matches_oracle(m, B):
     assert np.array_equal(host(r.X)[inp.B - inp.n:], ref["states"])
     assert np.array_equal(host(r.nxt), ref["next_states"])
     assert np.array_equal(host(r.act), ref["actions"]) and np.array_equal(host(r.done), ref["dones"])
+    assert np.array_equal(host(r.isw), her.merged_is_weights(np.full(inp.B - inp.n, 0.5, np.float32), inp.n))
     X = host(r.X).astype(np.float64)
     for g in range(w.groups):
         st = iql.AdamState.fresh(inp.inits[g])
@@ -259,10 +264,11 @@ def test_whole_step_fp32_unfused_policy(m):
     _run_pair(m, Inputs(w, 1001, 5003), steps=2)
 
 
-def test_whole_step_layered_shape(m):
-    """A shape beyond the fused tile kernel (hidden 256) goes through the
-    layered GEMM path inside the whole step."""
-    w = synth.shrink(synth.WORKLOADS["b16384_s128_h128_bf16_g2_budget"], S=100, H=256, C=1 << 14)
+@pytest.mark.parametrize("H,H2", [(256, 0), (128, 96)])
+def test_whole_step_layered_shape(m, H, H2):
+    """Shapes beyond the fused tile kernel (hidden 256; two hidden widths)
+    go through the layered GEMM path inside the whole step."""
+    w = synth.shrink(synth.WORKLOADS["b16384_s128_h128_bf16_g2_budget"], S=100, H=H, H2=H2, C=1 << 14)
     _run_pair(m, Inputs(w, 2500, 4096), steps=2)
 
 

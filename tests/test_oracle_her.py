@@ -149,3 +149,22 @@ def test_non_goal_columns_bitwise_and_goal_from_donor_next_state():
 def test_episode_lookup_rejects_out_of_range():
     with pytest.raises(ValueError):
         her.episode_bounds(np.array([10]), np.array([5, 10]))
+
+
+def test_merged_importance_weights():
+    """HER rows enter the merged batch with importance weight 1 after the
+    prioritized rows, which keep their own weights ("How HER Interacts with
+    GPU PER"); at the pages' batch 256 and ratio 0.5 that is 128 ones after
+    128 prioritized weights."""
+    p = GOLD["page_numbers"]
+    n = her.her_size(p["batch"], p["her_ratio"])
+    w_normal = np.linspace(0.1, 1.0, p["batch"] - n).astype(np.float32)
+    w = her.merged_is_weights(w_normal, n)
+    assert w.shape == (p["batch"],) and w.dtype == np.float32
+    assert np.array_equal(w[: p["batch"] - n], w_normal)
+    assert np.all(w[p["batch"] - n:] == np.float32(1.0))
+    # relabel returns one weight of exactly 1 per relabelled row
+    g = np.random.default_rng(0)
+    s = g.standard_normal((10, 4)).astype(np.float32)
+    out = her.relabel(s, s, np.zeros(10, np.int32), np.zeros(10, np.float32), [1, 2, 3], [4, 5, 6], 2)
+    assert np.array_equal(out["is_weights"], np.ones(3, np.float32))

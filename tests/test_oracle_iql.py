@@ -17,11 +17,12 @@ from oracle import iql
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "iql_hand.json")))
 
 
-def _net(S, H, seed):
+def _net(S, H, seed, H2=None):
+    H2 = H if H2 is None else H2
     g = np.random.default_rng(seed)
     flat = np.concatenate([g.uniform(-1, 1, S * H) * np.sqrt(6 / S), g.standard_normal(H) * 0.1,
-                           g.uniform(-1, 1, H * H) * np.sqrt(6 / H), g.standard_normal(H) * 0.1,
-                           g.uniform(-1, 1, H) * np.sqrt(6 / H), g.standard_normal(1) * 0.1])
+                           g.uniform(-1, 1, H2 * H) * np.sqrt(6 / H), g.standard_normal(H2) * 0.1,
+                           g.uniform(-1, 1, H2) * np.sqrt(6 / H2), g.standard_normal(1) * 0.1])
     return flat
 
 
@@ -55,14 +56,15 @@ def test_expectile_zero_diff_has_zero_gradient():
 
 
 # ------------------------------------------------------- network + autograd
-def _torch_loss(flat, X, q, tau, S, H):
+def _torch_loss(flat, X, q, tau, S, H, H2=None):
+    H2 = H if H2 is None else H2
     t = torch.tensor(flat, dtype=torch.float64, requires_grad=True)
     o = 0
     w1 = t[o:o + H * S].view(H, S); o += H * S
     b1 = t[o:o + H]; o += H
-    w2 = t[o:o + H * H].view(H, H); o += H * H
-    b2 = t[o:o + H]; o += H
-    w3 = t[o:o + H]; o += H
+    w2 = t[o:o + H2 * H].view(H2, H); o += H2 * H
+    b2 = t[o:o + H2]; o += H2
+    w3 = t[o:o + H2]; o += H2
     b3 = t[o]
     Xt = torch.tensor(X, dtype=torch.float64)
     h1 = torch.relu(torch.nn.functional.linear(Xt, w1, b1))
@@ -75,16 +77,19 @@ def _torch_loss(flat, X, q, tau, S, H):
     return loss.item(), v.detach().numpy(), t.grad.numpy()
 
 
-@pytest.mark.parametrize("S,H,B,tau", [(5, 4, 8, 0.7), (16, 32, 64, 0.7), (42, 16, 33, 0.9), (7, 8, 1, 0.3)])
-def test_forward_backward_match_torch_autograd(S, H, B, tau):
-    flat = _net(S, H, seed=S * 100 + H)
+@pytest.mark.parametrize("S,H,H2,B,tau", [(5, 4, 4, 8, 0.7), (16, 32, 32, 64, 0.7), (42, 16, 16, 33, 0.9),
+                                           (7, 8, 8, 1, 0.3), (6, 9, 4, 17, 0.7), (5, 3, 11, 12, 0.2)])
+def test_forward_backward_match_torch_autograd(S, H, H2, B, tau):
+    """The network with two hidden widths (W2 [H2, H1]) included: a
+    transposed W2 or a swapped width fails the second pair of shapes."""
+    flat = _net(S, H, seed=S * 100 + H, H2=H2)
     g = np.random.default_rng(B)
     X, q = g.standard_normal((B, S)), g.standard_normal(B) * 2
-    p = iql.unflatten(flat, S, H, H)
+    p = iql.unflatten(flat, S, H, H2)
     v, cache = iql.forward(p, X)
     loss, dv = iql.expectile(q, v, tau)
     grad = iql.flatten(iql.backward(p, cache, dv))
-    tl, tv, tg = _torch_loss(flat, X, q, tau, S, H)
+    tl, tv, tg = _torch_loss(flat, X, q, tau, S, H, H2)
     assert loss == pytest.approx(tl, rel=1e-12)
     np.testing.assert_allclose(v, tv, rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(grad, tg, rtol=1e-10, atol=1e-14)
@@ -182,6 +187,13 @@ def test_param_count_and_layout():
     p = iql.unflatten(flat, 3, 2, 2)
     assert p["w1"][1, 0] == 3 and p["b1"][0] == 6 and p["w2"][0, 1] == 9
     assert p["b2"][1] == 13 and p["w3"][0] == 14 and p["b3"][0] == 16
+    np.testing.assert_array_equal(iql.flatten(p), flat)
+    # two widths: S H1 + H1 + H2 H1 + H2 + H2 + 1, W2 stored [H2][H1] ([out, in])
+    assert iql.num_params(3, 2, 4) == 6 + 2 + 8 + 4 + 4 + 1
+    flat = np.arange(iql.num_params(3, 2, 4), dtype=np.float64)
+    p = iql.unflatten(flat, 3, 2, 4)
+    assert p["w2"].shape == (4, 2) and p["w2"][1, 0] == 10 and p["b2"][0] == 16 and p["w3"][3] == 23
+    assert p["b3"][0] == 24
     np.testing.assert_array_equal(iql.flatten(p), flat)
 
 
