@@ -65,6 +65,15 @@ def parse():
     p.add_argument("--kernel-reps", type=int, default=200)
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run 10 plain device copies of MIB MiB (counter calibration) and exit")
+    p.add_argument("--sweep", choices=("her", "aw", "budget", "copy"), default=None,
+                   help="only time one HBM-bound entry point on working sets of at least 1 GiB (her_relabel over "
+                        "a 2^22-row replay buffer, iql_aw_policy up to B*A = 2^26 for two trainers, "
+                        "grad_budget_accumulate + Adam up to n = 2^26) and print one JSON line per size")
+    p.add_argument("--sweep-calls", type=int, default=3, help="timed calls per sweep size (after one warm-up)")
+    p.add_argument("--summarize-sweeps", metavar="DIR", default=None,
+                   help="only write profiles/hbm_sweeps.md from the sweep logs and rocprofv3 CSV output under DIR "
+                        "(sweep_KIND.json, sweep_KIND_FETCH_SIZE/, sweep_KIND_WRITE_SIZE/ for each sweep, copy_FETCH_SIZE/, "
+                        "copy_WRITE_SIZE/); needs no GPU")
     p.add_argument("--summarize-profiles", metavar="DIR", default=None,
                    help="only write the profile summaries (markdown + traffic JSON) into profiles/ from the "
                         "rocprofv3 CSV output under DIR (trace/, FETCH_SIZE/, WRITE_SIZE/, copy_FETCH_SIZE/, "
@@ -157,6 +166,20 @@ def launch_bytes(w, layout=None):
         "reduce_saxpy": grp * nwg * Pp * 4 + grp * nwg * 4 + grp * P * 4 + k * nb * 4 + nb * 4,
         "adam": grp * (P * 32 + shadows) + nb * 32,
     }
+
+
+def mfma_from_profiles(name, src_hash):
+    """MFMA busy fraction and counter flops from a committed counter summary,
+    if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{name}_mfma.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("source_hash") != src_hash:
+        return None
+    return {k: d[k] for k in ("mfma_busy_frac", "mfma_flops_counter", "counter_rate_tflops", "lds_active_frac")
+            if k in d}
 
 
 def kernel_source_hash():
@@ -290,8 +313,27 @@ def profile_commands(workload):
         f"rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/WRITE_SIZE -o p -- python3 $REPO/bench.py{wl} --steps 5 "
         "--warmup 1 --no-graph --no-cpu-baseline --no-next-rows --kernel-reps 5",
         "rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/copy_WRITE_SIZE -o p -- python3 $REPO/bench.py --copy-probe 256",
+        f"rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} -f csv -d OUT/MFMA -o p -- python3 $REPO/bench.py{wl} "
+        "--steps 5 --warmup 1 --no-graph --no-cpu-baseline --no-next-rows --kernel-reps 5",
+        f"rocprofv3 --pmc {' '.join(LDS_COUNTERS)} -f csv -d OUT/LDS -o p -- python3 $REPO/bench.py{wl} "
+        "--steps 5 --warmup 1 --no-graph --no-cpu-baseline --no-next-rows --kernel-reps 5",
         f"python3 $REPO/bench.py --summarize-profiles OUT{wl}",
     )
+
+
+# matrix-core counters (one rocprofv3 pass): bf16 MFMA work in units of 512
+# flops, cycles the SIMDs' MFMA units were busy, GPU-active cycles
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE")
+LDS_COUNTERS = ("SQ_INSTS_LDS", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE")
+MI355X_SIMDS = 256 * 4
+
+
+def _counters_per_kernel(path):
+    """{kernel: {counter: median over dispatches}} of a multi-counter run."""
+    per = {}
+    for r in _csv_rows(path):
+        per.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: {c: _median(v) for c, v in cs.items()} for k, cs in per.items()}
 
 
 def _csv_rows(path):
@@ -426,6 +468,51 @@ def summarize_profiles(d, workload=None):
                  f"{abytes[launch] / 1e6:.2f} | {gbs:.0f} | {100 * gbs / PEAK_HBM_GBS:.1f} |")
     L.append("")
     P, Pp, nwg = partial_layout(w, layout)
+    mfma_json = None
+    gm = glob.glob(os.path.join(d, "MFMA", "*_counter_collection.csv"))
+    gl = glob.glob(os.path.join(d, "LDS", "*_counter_collection.csv"))
+    if gm:
+        mc = _counters_per_kernel(gm[0])
+        lc = _counters_per_kernel(gl[0]) if gl else {}
+        L.append("## Matrix cores and LDS (`--pmc`, median over dispatches)")
+        L.append("")
+        L.append("`MFMA flops` = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; `MFMA busy` = SQ_VALU_MFMA_BUSY_CYCLES "
+                 f"(summed over the SIMDs) / ({MI355X_SIMDS} SIMDs x the kernel's average time above x 2.4 GHz); "
+                 "`rate` = MFMA flops / that time; LDS `active` = SQ_LDS_IDX_ACTIVE (summed over the CUs) / "
+                 "(256 CUs x the same cycles), `conflict` = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.  "
+                 "(GRBM_GUI_ACTIVE, summed over the XCDs, spans the profiler's serialised dispatch window rather "
+                 "than the kernel, so the kernel-trace time is the denominator.)")
+        L.append("")
+        L.append("| kernel | MFMA flops | / algorithmic | MFMA busy | rate TFLOP/s | % of bf16 peak | LDS instrs | "
+                 "LDS active | LDS conflict |")
+        L.append("|---|---:|---:|---:|---:|---:|---:|---:|---:|")
+        alg = fused_flops_per_launch(w)
+        for nm, cs in mc.items():
+            fl = cs.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+            if fl <= 0:
+                continue
+            t_us = next((float(r["AverageNs"]) / 1e3 for r in stats if r["Name"] == nm), float("nan"))
+            cycles = t_us * 1e-6 * 2.4e9
+            busy = cs.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (cycles * MI355X_SIMDS)
+            rate = fl / (t_us * 1e-6) / 1e12
+            ls = lc.get(nm, {})
+            lact = ls.get("SQ_LDS_IDX_ACTIVE", float("nan")) / (cycles * 256)
+            lcon = ls.get("SQ_LDS_BANK_CONFLICT", float("nan")) / ls.get("SQ_LDS_IDX_ACTIVE", float("nan"))
+            fused = launch_of.get(nm) == "fwd_bwd" and len([1 for n2 in mc if launch_of.get(n2) == "fwd_bwd"]) == 1
+            ratio = f"{fl / alg:.3f}" if fused else "-"
+            L.append(f"| `{_short(nm)}` | {fl:.4g} | {ratio} | {100 * busy:.1f} % | {rate:.0f} | "
+                     f"{100 * rate / PEAK_BF16_TFLOPS:.1f} | {ls.get('SQ_INSTS_LDS', float('nan')):.4g} | "
+                     f"{100 * lact:.1f} % | {100 * lcon:.2f} % |")
+            if fused and default:
+                mfma_json = {"kernel": _short(nm), "workload": w.name, "source_hash": src_hash, "commit": commit,
+                             "mfma_flops_counter": fl, "algorithmic_flops": alg, "mfma_busy_frac": busy,
+                             "counter_rate_tflops": rate, "avg_kernel_us": t_us,
+                             "lds_active_frac": lact, "lds_conflict_frac": lcon}
+        L.append("")
+        L.append("The forward/backward kernel's MFMA flops exceed the algorithmic count by its bias-gradient "
+                 "products (an extra MFMA against an all-ones operand per weight-gradient sweep) and the zero "
+                 "padding of tiles.")
+        L.append("")
     L.append(f"`needed MB` is each launch's inputs and outputs read or written once (`launch_bytes` in "
              f"bench.py).  For the forward/backward launch it includes its fp32 gradient partials "
              f"({w.groups} x {nwg} rows x {Pp} floats = {w.groups * nwg * Pp * 4 / 1e6:.1f} MB), which the "
@@ -443,6 +530,10 @@ def summarize_profiles(d, workload=None):
                    "write_factor": factors["WRITE_SIZE"], "commit": commit}
         with open(os.path.join(ROOT, "profiles", "iql_fused_b16384_s128_h128_g2_traffic.json"), "w") as fh:
             json.dump(traffic, fh, indent=1)
+            fh.write("\n")
+    if mfma_json:
+        with open(os.path.join(ROOT, "profiles", "iql_fused_b16384_s128_h128_g2_mfma.json"), "w") as fh:
+            json.dump(mfma_json, fh, indent=1)
             fh.write("\n")
     print(md)
 
@@ -515,6 +606,199 @@ def time_next_rows(ctx, torch, np, reps=100):
     return out
 
 
+# ------------------------------------------------------------ HBM sweeps
+SWEEP_POINTS = {
+    "her": [1 << 16, 1 << 18, 1 << 20],      # relabelled rows
+    "aw": [1 << 20, 1 << 22, 1 << 24],       # rows B at A = 16, two trainers (B * A up to 2^26)
+    "budget": [1 << 22, 1 << 24, 1 << 26],   # elements n, four sources
+    "copy": [1 << 26, 1 << 28],              # a plain device copy of n floats (torch), for reference
+}
+SWEEP_KERNELS = {"her": ("her_relabel_kernel",), "aw": ("aw_policy",),
+                 "budget": ("budget_norms_kernel", "budget_saxpy_kernel", "adam_flat_kernel"),
+                 "copy": ("copy",)}
+
+
+def sweep_bytes(kind, x):
+    """Bytes one call must move (each input read once, each output written
+    once; what no cache can save at these sizes):
+      her:    per row the source's s and s' (f32), the donor's goal, the
+              source index, action, done and two episode ends; written the
+              bf16 state row, the f32 s' row, action, reward, done, donor and
+              importance weight (state 128, goal 8);
+      aw:     Q [B, 16] once, V [2, B], the policy [2, B, 16] written;
+      budget: pass 1 reads the four sources; pass 2 reads them again (the
+              clip needs every norm first) and writes grad; Adam reads grad,
+              p, m, v and writes p, m, v and the zeroed grad: 68 B/element."""
+    if kind == "her":
+        S, G = 128, 8
+        return x * ((8 * S + 4 * G + 4 + 4 + 4 + 8) + (2 * S + 4 * S + 5 * 4))
+    if kind == "aw":
+        A, G = 16, 2
+        return x * (4 * A + G * (4 + 4 * A))
+    if kind == "copy":
+        return x * 8
+    return x * 68
+
+
+def run_sweep(kind, calls):
+    """Times each size of one HBM-bound entry point with HIP events around
+    `calls` back-to-back calls (after one warm-up call); one JSON line each."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    import offline_rl_step_amd as m
+    d = torch.device("cuda:0")
+    gen = torch.Generator(device=d)
+    gen.manual_seed(20261202)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(calls):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / calls
+
+    rows = []
+    if kind == "her":
+        C, S, G, L = 1 << 22, 128, 8, 64
+        st = torch.randn((C, S), generator=gen, device=d)
+        nx = torch.randn((C, S), generator=gen, device=d)
+        act = torch.randint(0, 9, (C,), generator=gen, device=d, dtype=torch.int32)
+        done = torch.zeros(C, device=d)
+        ends = torch.arange(1, C // L + 1, device=d, dtype=torch.int32) * L
+        done[ends.long() - 1] = 1.0
+        buf = m.her_buffer(st, nx, act, done, ends)
+        cfg = m.her_config(S, G, m.HER_FUTURE)
+        step = torch.zeros(1, dtype=torch.int64, device=d)
+        for n in SWEEP_POINTS[kind]:
+            src = torch.randint(0, C, (n,), generator=gen, device=d, dtype=torch.int32)
+            X = torch.empty((n, S), dtype=torch.bfloat16, device=d)
+            o_next = torch.empty((n, S), device=d)
+            o_i = [torch.empty(n, dtype=torch.int32, device=d) for _ in range(2)]
+            o_f = [torch.empty(n, device=d) for _ in range(3)]
+            out = m.her_out(X, m.BF16, S, o_f[0], next_states=o_next, actions=o_i[0], dones=o_f[1],
+                            donor_idx=o_i[1], is_weights=o_f[2])
+            us = timed(lambda: m.her_relabel(cfg, buf, src, n, 7, step, out))
+            rows.append((n, us, f"{n} rows over a {C}-row replay buffer ({2 * C * S * 4 / 2**30:.0f} GiB)"))
+    elif kind == "aw":
+        A, G = 16, 2
+        for B in SWEEP_POINTS[kind]:
+            q = torch.randn((B, A), generator=gen, device=d)
+            v = torch.randn((G, B), generator=gen, device=d)
+            pi = torch.empty((G, B, A), device=d)
+            us = timed(lambda: m.iql_aw_policy(q, v, G, B, A, 3.0, pi))
+            rows.append((B, us, f"B = {B}, A = {A}, {G} trainers (B A = 2^{int(np.log2(B * A))})"))
+    elif kind == "copy":
+        for n in SWEEP_POINTS[kind]:
+            a_, b_ = torch.randn(n, generator=gen, device=d), torch.empty(n, device=d)
+            us = timed(lambda: b_.copy_(a_))
+            rows.append((n, us, f"device copy of {n * 4 / 2**20:.0f} MiB (reference)"))
+            del a_, b_
+    else:
+        for n in SWEEP_POINTS[kind]:
+            srcs = [torch.randn(n, generator=gen, device=d) * sc for sc in (1.0, 5.0, 0.5, 0.2)]
+            grad = torch.zeros(n, device=d)
+            p = torch.randn(n, generator=gen, device=d) * 0.05
+            mm, vv = torch.zeros(n, device=d), torch.zeros(n, device=d)
+            t = torch.zeros(1, dtype=torch.int32, device=d)
+            norms = torch.zeros(5, device=d)
+            ws = torch.zeros(m.grad_budget_workspace_bytes(n, 4) // 4, device=d)
+            adam = m.make_adam(p, mm, vv, t)
+            us = timed(lambda: m.grad_budget_accumulate(grad, srcs, (0.7, 0.15, 0.1, 0.05), (1.0,) * 4, n, 1.0,
+                                                        norms, adam, ws))
+            rows.append((n, us, f"n = {n} (2^{int(np.log2(n))}), four sources + Adam"))
+            del srcs, grad, p, mm, vv, ws
+            torch.cuda.empty_cache()
+    for x, us, what in rows:
+        by = sweep_bytes(kind, x)
+        print(json.dumps({"sweep": kind, "size": x, "what": what, "us_per_call": us, "bytes_per_call": by,
+                          "GB/s": by / (us * 1e-6) / 1e9, "frac_of_8TBs": by / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                          "calls": calls}), flush=True)
+
+
+def sweep_commands():
+    return [f"rocprofv3 --kernel-trace --stats -f csv -d OUT/sweep_{k}_trace -o t -- python3 $REPO/bench.py "
+            f"--sweep {k} > OUT/sweep_{k}.json" for k in SWEEP_POINTS] + \
+           [f"rocprofv3 --pmc {c} -f csv -d OUT/sweep_{k}_{c} -o p -- python3 $REPO/bench.py --sweep {k}"
+            for k in SWEEP_POINTS for c in ("FETCH_SIZE", "WRITE_SIZE")] + \
+           [f"rocprofv3 --pmc {c} -f csv -d OUT/copy_{c} -o p -- python3 $REPO/bench.py --copy-probe 256"
+            for c in ("FETCH_SIZE", "WRITE_SIZE")] + \
+           ["python3 $REPO/bench.py --summarize-sweeps OUT"]
+
+
+def _counter_dispatches(path):
+    """Counter value (KiB) of every dispatch, in dispatch order, per kernel."""
+    per = {}
+    rows = sorted(_csv_rows(path), key=lambda r: int(r.get("Dispatch_Id", 0)))
+    for r in rows:
+        per.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return per
+
+
+def summarize_sweeps(d):
+    """profiles/hbm_sweeps.md: per sweep size, the event-timed rate on the
+    bytes the call must move, and the HBM bytes the counters saw (FETCH_SIZE /
+    WRITE_SIZE summed over the call's kernels, median over the timed calls,
+    scaled by the plain-copy calibration)."""
+    import glob
+    cf = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        per = _counter_dispatches(glob.glob(os.path.join(d, "copy_" + c, "*_counter_collection.csv"))[0])
+        cf[c] = (256 * 1024) / max(v for k, vs in per.items() if "copyBuffer" in k for v in vs)
+    L = ["# HBM-bound entry points on working sets of at least 1 GiB", "",
+         "Each size is timed with HIP events around back-to-back calls after one warm-up call (`bench.py --sweep`), "
+         "in its own process per sweep; MI355X HBM3E peak 8 TB/s.  `needed` = the bytes the call must move "
+         "(`sweep_bytes` in bench.py).  `measured` = FETCH_SIZE + WRITE_SIZE of the call's kernels (median over "
+         f"the calls of the counter runs), scaled by a plain 256 MiB copy's counters (factors "
+         f"{cf['FETCH_SIZE']:.3f} fetch, {cf['WRITE_SIZE']:.3f} write).", "",
+         "Commands (from /tmp, each its own run, `REPO` = the repository root, `OUT` = an output folder):", ""]
+    L += ["    " + c for c in sweep_commands()]
+    L += ["", "| entry point | size | us per call | needed GB | measured read GB | measured write GB | "
+              "TB/s on needed bytes | % of 8 TB/s |", "|---|---|---:|---:|---:|---:|---:|---:|"]
+    for kind in SWEEP_POINTS:
+        jpath = os.path.join(d, f"sweep_{kind}.json")
+        if not os.path.exists(jpath):
+            continue
+        pts = [json.loads(x) for x in open(jpath) if x.startswith("{")]
+        meas = {}
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            g = glob.glob(os.path.join(d, f"sweep_{kind}_{c}", "*_counter_collection.csv"))
+            if not g:
+                continue
+            per = _counter_dispatches(g[0])
+            calls = pts[0]["calls"] + 1 if pts else 1
+            tot = []
+            for i in range(len(pts)):
+                per_call = []
+                for j in range(1, calls):  # skip the warm-up call
+                    v = 0.0
+                    for kn in SWEEP_KERNELS[kind]:
+                        vs = [x for k, x in per.items() if kn in k]
+                        vs = vs[0] if vs else []
+                        if len(vs) >= calls * len(pts):
+                            v += vs[i * calls + j]
+                    per_call.append(v)
+                tot.append(_median(per_call) * 1024 * cf[c])
+            meas[c] = tot
+        names = {"her": "her_relabel", "aw": "iql_aw_policy", "budget": "grad_budget_accumulate + Adam",
+                 "copy": "plain copy (torch)"}
+        for i, p in enumerate(pts):
+            rd = meas.get("FETCH_SIZE", [float("nan")] * len(pts))[i]
+            wr = meas.get("WRITE_SIZE", [float("nan")] * len(pts))[i]
+            L.append(f"| {names[kind]} | {p['what']} | {p['us_per_call']:.1f} | {p['bytes_per_call'] / 1e9:.3f} | "
+                     f"{rd / 1e9:.3f} | {wr / 1e9:.3f} | {p['GB/s'] / 1e3:.2f} | {100 * p['frac_of_8TBs']:.1f} |")
+    md = os.path.join(ROOT, "profiles", "hbm_sweeps.md")
+    os.makedirs(os.path.dirname(md), exist_ok=True)
+    with open(md, "w") as fh:
+        fh.write("\n".join(L) + "\n")
+    print(md)
+
+
 def cpu_baseline(ctx, seconds, np):
     """The oracle as it stands, one full step at a time, on the host cores."""
     from oracle import aw, budget, her, iql
@@ -546,13 +830,26 @@ def cpu_baseline(ctx, seconds, np):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": w.B * steps / el, "unit": "samples/s", "cores": int(cores), "kind": "oracle",
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), model)
+    except OSError:  # pragma: no cover
+        pass
+    return {"value": w.B * steps / el, "unit": "samples/s", "cores": int(cores), "cpu_model": model,
+            "kind": "oracle",
             "sample": f"{steps} full steps of the same workload (fp64 NumPy oracle; BLAS threads = cores), "
                       f"{el:.1f} s", "s_per_step": el / steps, "host_cpus": os.cpu_count()}
 
 
 def main():
     a = parse()
+    if a.summarize_sweeps:
+        summarize_sweeps(a.summarize_sweeps)
+        return
+    if a.sweep:
+        run_sweep(a.sweep, a.sweep_calls)
+        return
     if a.summarize_profiles:
         summarize_profiles(a.summarize_profiles, a.workload)
         return
@@ -638,10 +935,28 @@ def main():
         kernel = "layered forward/backward (five kernels; events around the group)"
     else:
         kernel = "fused forward/backward"
-    roofline = {"bound": "mfma", "kernel": kernel, "achieved": achieved,
-                "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                "traffic": traffic_from_profiles("iql_fused_b16384_s128_h128_g2", src_hash) if default else None,
-                "avg_kernel_us": avg_us, "flops_per_launch": flops, "source_hash": src_hash}
+    # the roof that bounds this launch: its algorithmic flops over the bytes
+    # it must move (inputs and outputs once, without the split-K partials)
+    # against the ridge point peak flops / peak bandwidth
+    P_, Pp_, nwg_ = partial_layout(w, layout)
+    alg_bytes = lb["fwd_bwd"] - w.groups * nwg_ * Pp_ * 4
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    intensity = flops / alg_bytes
+    mfma_frac = achieved / peak
+    bytes_rate = alg_bytes / (avg_us * 1e-6) / 1e9
+    counters = mfma_from_profiles("iql_fused_b16384_s128_h128_g2", src_hash) if default else None
+    if intensity < ridge:
+        roofline = {"bound": "hbm", "kernel": kernel, "achieved": bytes_rate, "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": bytes_rate / PEAK_HBM_GBS}
+    else:
+        roofline = {"bound": "mfma", "kernel": kernel, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                    "frac": mfma_frac}
+    roofline.update({
+        "traffic": traffic_from_profiles("iql_fused_b16384_s128_h128_g2", src_hash) if default else None,
+        "avg_kernel_us": avg_us, "flops_per_launch": flops, "algorithmic_bytes_per_launch": alg_bytes,
+        "intensity_flop_per_byte": intensity, "ridge_flop_per_byte": ridge,
+        "mfma_tflops": achieved, "mfma_frac": mfma_frac, "hbm_GBs_on_algorithmic_bytes": bytes_rate,
+        "hbm_frac": bytes_rate / PEAK_HBM_GBS, "mfma_counters": counters, "source_hash": src_hash})
 
     out = {"metric": METRIC, "value": w.B / (ms_per_step * 1e-3), "unit": "samples/s", "n_gpus": 1,
            "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,

@@ -5,7 +5,9 @@
 // clamp to [-10, 10], scale by the temperature beta, softmax over actions with
 // the row maximum subtracted.
 //
-// HBM-bound.  A one-wave workgroup owns 64 consecutive rows (16384 rows give
+// HBM-bound.  Action counts of 4, 8, 16, 32 or 64 with 16-byte aligned rows
+// take the streaming kernel below (float4 per lane, rows split over lanes).
+// Any other A: a one-wave workgroup owns 64 consecutive rows (16384 rows give
 // 256 workgroups, one per CU): the [64, A] slab of Q is read once with
 // coalesced loads into LDS (padded to an odd row stride so the per-row reads
 // are bank-conflict free), every group's policy is computed from that one
@@ -83,9 +85,84 @@ __global__ __launch_bounds__(kAwRows) void aw_policy_kernel(const float* __restr
     }
 }
 
+// Streaming form for action counts A = 4 LPR with LPR in {1, 2, 4, 8, 16} and
+// 16-byte aligned rows: LPR lanes own one row, one float4 of four actions
+// each, so a wave's load or store of 64 float4 covers 64 / LPR consecutive
+// rows (1 KB contiguous).  The row maximum and sum are xor-shuffles among the
+// row's lanes.  Each lane keeps kAwUnroll rows' loads in flight before it
+// computes, and the grid strides over the rows.
+constexpr int kAwVecThreads = 256, kAwUnroll = 4;
+
+template <int LPR>
+__global__ __launch_bounds__(kAwVecThreads) void aw_policy_vec_kernel(const float4* __restrict__ q,
+                                                                   const float* __restrict__ v, int G, int64_t B,
+                                                                   float beta, float4* __restrict__ pi) {
+    constexpr int RPW = kAwVecThreads / LPR;  // rows per workgroup pass
+    const int sub = threadIdx.x % LPR;
+    const int64_t stride = (int64_t)gridDim.x * RPW * kAwUnroll;
+    for (int64_t base = (int64_t)blockIdx.x * RPW * kAwUnroll; base < B; base += stride) {
+        float4 x[kAwUnroll];
+        int64_t row[kAwUnroll];
+#pragma unroll
+        for (int u = 0; u < kAwUnroll; ++u) {
+            row[u] = base + (int64_t)u * RPW + threadIdx.x / LPR;
+            const int64_t rc = row[u] < B ? row[u] : B - 1;
+            x[u] = q[rc * LPR + sub];
+        }
+        for (int g = 0; g < G; ++g) {
+            float vv[kAwUnroll];
+#pragma unroll
+            for (int u = 0; u < kAwUnroll; ++u) vv[u] = v[(int64_t)g * B + (row[u] < B ? row[u] : B - 1)];
+#pragma unroll
+            for (int u = 0; u < kAwUnroll; ++u) {
+                float e[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+                float mx = -INFINITY;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    e[j] = beta * fminf(fmaxf(e[j] - vv[u], -10.f), 10.f);
+                    mx = fmaxf(mx, e[j]);
+                }
+#pragma unroll
+                for (int o = LPR / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, LPR));
+                float s = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    e[j] = expf(e[j] - mx);
+                    s += e[j];
+                }
+#pragma unroll
+                for (int o = LPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, LPR);
+                if (row[u] < B)
+                    pi[((int64_t)g * B + row[u]) * LPR + sub] = float4{e[0] / s, e[1] / s, e[2] / s, e[3] / s};
+            }
+        }
+    }
+}
+
+template <int LPR>
+static hipError_t run_aw_vec(const float* q, const float* v, int G, int B, float beta, float* pi,
+                             hipStream_t stream) {
+    constexpr int RPW = kAwVecThreads / LPR;
+    const int64_t need = ((int64_t)B + RPW * kAwUnroll - 1) / (RPW * kAwUnroll);
+    const unsigned blocks = (unsigned)(need < 4096 ? need : 4096);
+    hipLaunchKernelGGL(aw_policy_vec_kernel<LPR>, dim3(blocks), dim3(kAwVecThreads), 0, stream, (const float4*)q,
+                       v, G, (int64_t)B, beta, (float4*)pi);
+    return hipGetLastError();
+}
+
 hipError_t launch_aw_policy(const float* q, const float* v, int G, int B, int A, float beta,
                             float* pi, hipStream_t stream) {
     if (B <= 0) return hipSuccess;
+    if (((uintptr_t)q & 15u) == 0 && ((uintptr_t)pi & 15u) == 0) {
+        switch (A) {
+            case 4: return run_aw_vec<1>(q, v, G, B, beta, pi, stream);
+            case 8: return run_aw_vec<2>(q, v, G, B, beta, pi, stream);
+            case 16: return run_aw_vec<4>(q, v, G, B, beta, pi, stream);
+            case 32: return run_aw_vec<8>(q, v, G, B, beta, pi, stream);
+            case 64: return run_aw_vec<16>(q, v, G, B, beta, pi, stream);
+            default: break;
+        }
+    }
     const unsigned blocks = (unsigned)((B + kAwRows - 1) / kAwRows);
     const size_t lds = (size_t)2 * kAwRows * (A | 1) * sizeof(float);
     hipLaunchKernelGGL(aw_policy_kernel, dim3(blocks), dim3(kAwRows), lds, stream, q, v, G, B, A, beta, pi);
