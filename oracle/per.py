@@ -38,13 +38,20 @@ def uniforms(n, seed, step):
     return (w0 >> np.uint64(11)).astype(np.float64) * 2.0 ** -53
 
 
+def find_rows(prefix, u):
+    """The first row whose inclusive prefix sum exceeds u, for each u (so a
+    u equal to a prefix value takes the next row of positive priority, and a
+    row of priority 0 is never found)."""
+    return np.searchsorted(prefix, u, side="right")
+
+
 def sample(priorities, n, seed, step, beta):
     """Returns (indices int64 [n], IS weights float64 [n], u [n], prefix [size])."""
     p = np.asarray(priorities, dtype=np.float64)
     prefix = np.cumsum(p)
     total = prefix[-1]
     u = np.minimum(uniforms(n, seed, step) * total, np.nextafter(total, -np.inf))
-    idx = np.searchsorted(prefix, u, side="right")
+    idx = find_rows(prefix, u)
     pi = p[idx]
     w = (pi.min() / pi) ** beta
     return idx.astype(np.int64), w, u, prefix

@@ -69,3 +69,17 @@ def test_uniform_words_are_philox_word_zero():
             c[i] = np.uint64(0xFFFFFFFFFFFFFFFF)
         w0 = np.random.Philox(counter=c, key=np.array([seed, per.PER_KEY1], dtype=np.uint64)).random_raw(1)[0]
         assert u[k] == float(w0 >> np.uint64(11)) * 2.0 ** -53
+
+
+def test_search_takes_the_first_prefix_exceeding_u():
+    """The row is the first whose inclusive prefix exceeds u: at u equal to a
+    prefix value the next row of positive priority is taken, a leading or
+    inner row of priority 0 is never found (brute force over exact values)."""
+    p = np.array([0.0, 1.0, 0.0, 0.0, 2.0, 0.5, 0.0])
+    prefix = np.cumsum(p)
+    us = np.array([0.0, 0.5, 1.0, 2.9, 3.0, 3.25, np.nextafter(3.5, 0)])
+    got = per.find_rows(prefix, us)
+    brute = [next(i for i in range(len(p)) if prefix[i] > u) for u in us]
+    np.testing.assert_array_equal(got, brute)
+    np.testing.assert_array_equal(got, [1, 1, 4, 4, 5, 5, 5])
+    assert np.all(p[got] > 0)
