@@ -255,6 +255,11 @@ IQLH_DEV void her_block(const HerArgs& a, int64_t blk) {
     // ---- goal replacement and stores
     const int64_t ld = a.out_ld;
     const bool lds_goals = G <= kHerGoalLds;  // uniform: no global load below
+    // whole quads leave as one store per output row (8 bytes of bf16 or 16 of
+    // f32 for the state, 16 for s'), not as four element stores each
+    const uintptr_t oal = (uintptr_t)a.out_states;
+    const bool wide = vec && ld % 4 == 0 && (a.out_bf16 ? (oal & 7u) == 0 : (oal & 15u) == 0) &&
+                      ((uintptr_t)a.out_next_states & 15u) == 0;
     auto emit = [&](int w, float* xs, float* xn, bool from_lds) {
         const int rr = w / C4, c = (w - rr * C4) * 4;
         const int64_t row = row0 + rr, don = s_don[rr];
@@ -270,6 +275,15 @@ IQLH_DEV void her_block(const HerArgs& a, int64_t blk) {
                     else xs[e] = xn[e] = d < kHerGoalLds ? s_goal[rr][d] : a.next_states[don * S + d];
                 }
             }
+        }
+        if (wide) {  // uniform; S % 4 == 0, so the quad is whole
+            if (a.out_bf16)
+                *(uint2*)((uint16_t*)a.out_states + row * ld + c) =
+                    uint2{pack_bf2(xs[0], xs[1]), pack_bf2(xs[2], xs[3])};
+            else
+                *(float4*)((float*)a.out_states + row * ld + c) = float4{xs[0], xs[1], xs[2], xs[3]};
+            if (a.out_next_states) *(float4*)(a.out_next_states + row * S + c) = float4{xn[0], xn[1], xn[2], xn[3]};
+            return;
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
