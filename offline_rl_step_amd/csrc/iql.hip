@@ -1422,7 +1422,7 @@ hipError_t launch_convert_rows(const void* src, int src_dtype, int64_t src_ld, v
 
 bool iql_partial_counts(const IqlDims& d, int B, int* nwg, int* nloss) {
     if (d.big) {
-        const int c = iql_big_chunk(d.S, d.H, B);
+        const int c = iql_big_chunk(d.S, d.H, d.G, B);
         *nwg = (B + c - 1) / c;
         *nloss = iql_big_blocks(B);
         return true;

@@ -11,8 +11,8 @@
 //          dz2 (db2), dv relu(z2) (dw3) and dv (db3)
 //   bwd1   dz1 = (W2^T dz2) * relu'(z1)                  -> DZ1 [B][H] bf16
 //   wgrad  dW2 = dz2^T h1, dW1 = dz1^T s (with db1 = column sums of dz1)
-//          over chunks of samples, one fp32 partial row per chunk; a small job
-//          per chunk adds the fwd2 block sums of the chunk into the same row
+//          over chunks of samples, one fp32 partial row per chunk; the jobs
+//          of a chunk also add its fwd2 block sums into the same row
 //
 // then the fixed-order partial reduction and Adam shared with the other
 // paths (no float atomics anywhere).
@@ -38,6 +38,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <type_traits>
+
 namespace iqlh {
 namespace {
 
@@ -54,6 +56,10 @@ constexpr int kThreads = 256;
 constexpr int kBK = 32;           // k per stage
 constexpr int kFwd2Samples = 128; // samples per fwd2 block (the loss blocks)
 constexpr int kTile = 256;        // fwd1 / bwd1 / wgrad output tile edge
+constexpr int kTileStages = 5;    // ring depth of fwd1 / bwd1 (5 x 32 KB)
+constexpr int kWgradStages = 5;   // ring depth of wgrad (5 x 32 KB)
+// entries of a loss block's sums: db2 [H], dw3 [H], db3, db1 [H]
+__host__ __device__ constexpr int spart_w(int H) { return 3 * H + 1; }
 
 IQLH_DEV f4 mma(bf16x8 a, bf16x8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
 
@@ -63,6 +69,8 @@ IQLH_DEV void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// s_waitcnt on lgkmcnt only: this wave's LDS operations are complete
+IQLH_DEV void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 // Workgroup barrier without a memory fence: the global->LDS copies of the
 // stages in flight must stay in flight across it (a fenced barrier would wait
 // for all of them).  The empty asm keeps the compiler from moving LDS
@@ -95,35 +103,111 @@ IQLH_DEV float sum_row16(float x) {
     return x;
 }
 
-// Scheduling hint for one stage: the NR LDS reads of the fragments first, then
-// the NM MFMAs (the compiler otherwise sinks each read to its first use, and
-// with one wave per SIMD every such read waits out the LDS latency).
-template <int NR, int NM>
-IQLH_DEV void reads_then_mfma() {
-    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // DS reads
-    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);  // MFMA
+// Scheduling hint for one stage: the next stage's NR LDS fragment reads
+// spread between this stage's NM MFMAs, so the reads complete under the
+// matrix work (with one wave per SIMD nothing else would hide them).
+template <int NR, int NM, int I = 0>
+IQLH_DEV void reads_among_mfma() {
+    if constexpr (I < NR) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NM * (I + 1) / NR - NM * I / NR, 0);  // MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                   // one DS read
+        reads_among_mfma<NR, NM, I + 1>();
+    }
+}
+
+// vmcnt wait leaving min(K, ahead) stages of LPT copies in flight (K <= 3
+// known at compile time; written as compares on ahead alone, which the
+// compiler keeps scalar)
+template <int K, int LPT>
+IQLH_DEV void wait_ahead(int ahead) {
+    static_assert(K >= 0 && K <= 3, "stages in flight");
+    if (K >= 3 && ahead >= 3) wait_vm<(K >= 3 ? 3 : 0) * LPT>();
+    else if (K >= 2 && ahead >= 2) wait_vm<(K >= 2 ? 2 : 0) * LPT>();
+    else if (K >= 1 && ahead >= 1) wait_vm<(K >= 1 ? 1 : 0) * LPT>();
+    else wait_vm<0>();
 }
 
 // ---------------------------------------------------------------- K-loop
 // Stage s of nsl goes to ring buffer s % NST; NST - 1 stages are issued
-// ahead.  LPT = copies each thread issues per stage.  issue(slice, buf) and
-// compute(slice, buf) are the product's own.
-template <int NST, int LPT, class Issue, class Compute>
-IQLH_DEV void kloop(int nsl, Issue&& issue, Compute&& compute) {
-    static_assert(NST >= 2 && NST <= 4, "ring depth");
+// ahead.  LPT = copies each thread issues per stage.  The product supplies
+// issue(slice, buf) (global -> LDS copies of a stage), mma(p) (the MFMAs of
+// the stage held in fragment set p), load(buf, p) (LDS -> fragment set p),
+// and pre(), run once after the first stages are issued (work whose memory
+// latency then overlaps theirs).  p is 0 or 1 as a type
+// (std::integral_constant), so the fragment sets stay in registers.
+//
+// Each step runs the MFMAs of stage s and reads the fragments of stage s + 1
+// into the other set; the product's scheduling hint spreads the reads among
+// the MFMAs.  A fragment used by one row of MFMAs only may be read into the
+// same registers once that row is done (the reads follow the MFMAs in
+// program order), so only the operand every row uses needs two sets.
+//
+// Buffer reuse: stage s + NST - 1 is issued into the buffer of stage s - 1
+// after the barrier of step s; every wave reaches that barrier after its
+// MFMAs of stage s - 1, i.e. after its reads of that buffer completed.
+template <int V>
+using Set = std::integral_constant<int, V>;
+template <int NST, int LPT, class Issue, class Load, class Mma, class Pre>
+IQLH_DEV void kloop(int nsl, Issue&& issue, Load&& load, Mma&& mma, Pre&& pre) {
+    static_assert(NST >= 2 && NST <= 5, "ring depth");
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s)
         if (s < nsl) issue(s, s);
+    pre();
+    // stage 0 landed: stages 1 .. min(NST - 2, nsl - 1) may stay in flight
+    wait_ahead<NST - 2, LPT>(nsl - 1);
+    bar();
+    load(0, Set<0>{});
+    auto step = [&](int s, auto cur, auto nxt) __attribute__((always_inline)) {
+        if (s + 1 < nsl) {
+            // issued so far: stages 0 .. min(s + NST - 2, nsl - 1); stage s + 1
+            // must have landed, stages s + 2 .. of those may stay in flight
+            wait_ahead<NST - 3, LPT>(nsl - 2 - s);
+            bar();
+            if (s + NST - 1 < nsl) issue(s + NST - 1, (s + NST - 1) % NST);
+        }
+        mma(cur);
+        // the last step re-reads its own (valid) stage: no branch around the
+        // reads, so they stay in the MFMAs' basic block
+        load((s + 1 < nsl ? s + 1 : s) % NST, nxt);
+    };
+    // pairs of steps, so that set 0 holds the current fragments at the top
+    // of every iteration; an odd last step after the loop
+    int s = 0;
+    for (; s + 2 <= nsl; s += 2) {
+        step(s, Set<0>{}, Set<1>{});
+        step(s + 1, Set<1>{}, Set<0>{});
+    }
+    if (s < nsl) step(s, Set<0>{}, Set<1>{});
+}
+constexpr auto no_pre = [] {};
+
+// The same ring with one fragment set: every step reads its own stage's
+// fragments and then runs its MFMAs (for a product whose epilogue leaves no
+// registers for a second set).
+template <int NST, int LPT, class Issue, class Compute, class Pre>
+IQLH_DEV void kloop1(int nsl, Issue&& issue, Compute&& compute, Pre&& pre) {
+    static_assert(NST >= 2 && NST <= 5, "ring depth");
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+        if (s < nsl) issue(s, s);
+    pre();
     for (int s = 0; s < nsl; ++s) {
-        // slices after s already issued: min(NST - 2, nsl - 1 - s)
-        const int ahead = nsl - 1 - s;
-        if (NST >= 4 && ahead >= 2) wait_vm<(NST >= 4 ? 2 : 0) * LPT>();
-        else if (NST >= 3 && ahead >= 1) wait_vm<LPT>();
-        else wait_vm<0>();
+        // issued so far: stages 0 .. min(s + NST - 2, nsl - 1); stage s must
+        // have landed, stages s + 1 .. of those may stay in flight
+        wait_ahead<NST - 2, LPT>(nsl - 1 - s);
         bar();
         if (s + NST - 1 < nsl) issue(s + NST - 1, (s + NST - 1) % NST);
-        compute(s, s % NST);
+        compute(s % NST);
     }
+}
+
+// Scheduling hint for kloop1: the NR fragment reads first, then the NM MFMAs
+// (the compiler otherwise sinks each read to its first use).
+template <int NR, int NM>
+IQLH_DEV void reads_then_mfma() {
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);  // MFMA
 }
 
 // ----------------------------------------------- K-contiguous operand tiles
@@ -151,11 +235,16 @@ IQLH_DEV int kc_lane() {
 }
 
 // --------------------------------------------------- natural operand tiles
+// A row of zeros in device memory: the copies of samples past the end of a
+// chunk read it, so that those samples contribute nothing to the products.
+__device__ __align__(16) const uint16_t kZeroRow[kTile] = {};
+
 // Samples [0, 32) x features [f0, f0 + 256) of a row-major [sample][feature]
 // activation: LDS chunk c holds sample c >> 5, feature unit (c & 31) ^ (2 (s & 3)).
-// Samples at or past smax re-read sample smax - 1, features at or past fmax
-// re-read feature 0 of the row (a ragged sample slice is zeroed afterwards;
-// columns past fmax are discarded).
+// Samples at or past smax read zeros (ZERO) or re-read sample smax - 1 (their
+// products are then discarded or multiplied by zeros); features at or past
+// fmax re-read feature 0 of the row (those columns are discarded).
+template <bool ZERO>
 IQLH_DEV void dma_nat(const uint16_t* g, int64_t ld, int smax, int f0, int fmax, uint16_t* lds) {
     const int tid = threadIdx.x, wbase = tid & ~63;
 #pragma unroll
@@ -165,8 +254,9 @@ IQLH_DEV void dma_nat(const uint16_t* g, int64_t ld, int smax, int f0, int fmax,
         const int gs = s < smax ? s : smax - 1;
         const int f = f0 + 8 * v;
         const int gf = f < fmax ? f : 0;
-        __builtin_amdgcn_global_load_lds((const void*)(g + (int64_t)gs * ld + gf), IQLH_LDS(lds + (i * kThreads + wbase) * 8),
-                                         16, 0, 0);
+        const uint16_t* src = g + (int64_t)gs * ld + gf;
+        if (ZERO) src = s < smax ? src : kZeroRow + 8 * v;
+        __builtin_amdgcn_global_load_lds((const void*)src, IQLH_LDS(lds + (i * kThreads + wbase) * 8), 16, 0, 0);
     }
 }
 IQLH_DEV u32x2 ld_tr(const uint16_t* p) {
@@ -206,24 +296,15 @@ template <int NF>
 IQLH_DEV int stage_off(int s, int f) { return s * NF + ((((f >> 3) ^ (s & 7)) << 3) | (f & 7)); }
 
 // Rows [0, ns) of the staged tile to dst rows (row stride ld), columns
-// [0, NF).  With mask, an element is zeroed where the same element of mask
-// is zero (dz1 = dh1 relu'(z1), read from h1 = relu(z1) as stored).
+// [0, NF).
 template <int NF, int NS>
-IQLH_DEV void stage_out(const uint16_t* lds, uint16_t* dst, int64_t ld, int ns, const uint16_t* mask) {
+IQLH_DEV void stage_out(const uint16_t* lds, uint16_t* dst, int64_t ld, int ns) {
     constexpr int UPR = NF / 8;  // 16-byte units per row
 #pragma unroll 4
     for (int c = threadIdx.x; c < NS * UPR; c += kThreads) {
         const int r = c / UPR, u = c - r * UPR;
         if (r >= ns) break;
-        u32x4 v = *(const u32x4*)(lds + r * NF + ((u ^ (r & 7)) << 3));
-        if (mask) {
-            const u32x4 h = *(const u32x4*)(mask + (int64_t)r * ld + 8 * u);
-            v.x &= (h.x & 0xFFFFu ? 0xFFFFu : 0u) | (h.x >> 16 ? 0xFFFF0000u : 0u);
-            v.y &= (h.y & 0xFFFFu ? 0xFFFFu : 0u) | (h.y >> 16 ? 0xFFFF0000u : 0u);
-            v.z &= (h.z & 0xFFFFu ? 0xFFFFu : 0u) | (h.z >> 16 ? 0xFFFF0000u : 0u);
-            v.w &= (h.w & 0xFFFFu ? 0xFFFFu : 0u) | (h.w >> 16 ? 0xFFFF0000u : 0u);
-        }
-        *(u32x4*)(dst + (int64_t)r * ld + 8 * u) = v;
+        *(u32x4*)(dst + (int64_t)r * ld + 8 * u) = *(const u32x4*)(lds + r * NF + ((u ^ (r & 7)) << 3));
     }
 }
 
@@ -239,7 +320,8 @@ struct BigArgs {
     uint16_t* h1;           // [G][B][H]
     uint16_t* dz2;          // [G][B][H]
     uint16_t* dz1;          // [G][B][H]
-    float* spart;           // [G][nblk][2H + 1]: db2, dw3, db3 of each 128-sample block
+    float* spart;           // [G][nblk][3H + 1]: db2, dw3, db3 (fwd2) and db1 (bwd1) of each 128-sample block
+    uint32_t* mask;         // [G][tiles][256 lanes][8 words]: relu'(z1) bits, fwd1 -> bwd1
     float* loss_part;       // [G][nblk]
     float* out_v;           // [G][B] or null
     float* part;            // [G][nchunk][Pp]
@@ -274,7 +356,7 @@ IQLH_DEV void xcd_map(int id, int nranges, int nper, int& range, int& job) {
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void big_tile_kernel(BigArgs a) {
     extern __shared__ __align__(16) uint16_t smem[];
-    constexpr int NST = 4, STG = 2 * kTile * kBK;  // elements per stage
+    constexpr int NST = kTileStages, STG = 2 * kTile * kBK;  // elements per stage
     const int g = blockIdx.y;
     const int H = a.H, B = a.B;
     const int nft = H / kTile, nst = (B + kTile - 1) / kTile;
@@ -298,12 +380,22 @@ __global__ __launch_bounds__(kThreads) void big_tile_kernel(BigArgs a) {
     const int wm = wv & 1, wn = wv >> 1;
     const int lo = kc_lane();
 
+    // bwd1: this lane's ReLU mask bits, loaded before the operand copies
+    // (the oldest loads, so the loop's vmcnt waits cover them as well)
+    u32x4 mk[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+    if (MODE == 1) {
+        const u32x4* mp = (const u32x4*)(a.mask + ((int64_t)g * gridDim.x + blockIdx.x) * kThreads * 8) + 2 * threadIdx.x;
+        mk[0] = mp[0];
+        mk[1] = mp[1];
+    }
     f4 acc[8][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+    const int l = threadIdx.x & 63, l16 = l & 15, q = l >> 4;
 
+    bf16x8 fa[8], fb[2][8];  // fa: one set, re-read row by row (see kloop)
     kloop<NST, 8>(
         K / kBK,
         [&](int s, int buf) {
@@ -311,33 +403,46 @@ __global__ __launch_bounds__(kThreads) void big_tile_kernel(BigArgs a) {
             dma_kc<kTile>(A, lda, kTile, s * kBK, st_);
             dma_kc<kTile>(Bm, ldb, srows, s * kBK, st_ + kTile * kBK);
         },
-        [&](int, int buf) {
+        [&](int buf, auto p) {
+            constexpr int P = decltype(p)::value;
             const uint16_t* ta = smem + buf * STG + (128 * wm) * kBK + lo;
             const uint16_t* tb = smem + buf * STG + kTile * kBK + (128 * wn) * kBK + lo;
-            bf16x8 fa[8], fb[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) fb[j] = *(const bf16x8*)(tb + j * 16 * kBK);
+            for (int j = 0; j < 8; ++j) fb[P][j] = *(const bf16x8*)(tb + j * 16 * kBK);
 #pragma unroll
             for (int i = 0; i < 8; ++i) fa[i] = *(const bf16x8*)(ta + i * 16 * kBK);
+        },
+        [&](auto p) {
+            constexpr int P = decltype(p)::value;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] = mma(fa[i], fb[j], acc[i][j]);
-            reads_then_mfma<16, 64>();
-        });
+                for (int j = 0; j < 8; ++j) acc[i][j] = mma(fa[i], fb[P][j], acc[i][j]);
+            reads_among_mfma<16, 64>();
+        },
+        no_pre);
 
     // epilogue: lane holds features 128 wm + 16 i + 4 q + r of samples
-    // 128 wn + 16 j + l16 (tile-local); staged as [sample][feature] rows
-    const int l = threadIdx.x & 63, l16 = l & 15, q = l >> 4;
+    // 128 wn + 16 j + l16 (tile-local); staged as [sample][feature] rows.
+    // The ReLU mask of h1 passes from fwd1 to bwd1 as bits in the lane
+    // layout both share: bit 4 j + r of word i of lane tid of tile (g, id).
     const float* bias = a.params + (int64_t)g * a.P + a.off_b1 + f0;
+    uint32_t mbits[8];
+    if (MODE == 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mbits[i] = mk[i / 4][i % 4];
+    }
+    // db1 over this wave's 128 samples (one loss block), from dz1 as stored
+    float* db1 = a.spart + ((int64_t)g * a.nblk + (s0 + 128 * wn) / kFwd2Samples) * spart_w(H) + 2 * H + 1 + f0;
     __syncthreads();  // every wave is done with the last stage
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int f = 128 * wm + 16 * i + 4 * q;
-        float bb[4] = {0.f, 0.f, 0.f, 0.f};
+        float bb[4] = {0.f, 0.f, 0.f, 0.f}, cs[4] = {0.f, 0.f, 0.f, 0.f};
         if (MODE == 0) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) bb[r] = bias[f + r];
+            mbits[i] = 0u;
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -346,15 +451,39 @@ __global__ __launch_bounds__(kThreads) void big_tile_kernel(BigArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float z = acc[i][j][r] + bb[r];
-                y[r] = MODE == 0 ? (z > 0.f ? z : 0.f) : z;
+                if (MODE == 0) {
+                    y[r] = z > 0.f ? z : 0.f;
+                    mbits[i] |= (z > 0.f ? 1u : 0u) << (4 * j + r);
+                } else {
+                    y[r] = (mbits[i] >> (4 * j + r)) & 1u ? z : 0.f;
+                }
             }
-            *(u32x2*)(smem + stage_off<kTile>(sl, f)) = u32x2{cvt2(y[0], y[1]), cvt2(y[2], y[3])};
+            const u32x2 pk = u32x2{cvt2(y[0], y[1]), cvt2(y[2], y[3])};
+            if (MODE == 1 && sl < srows) {
+                cs[0] += bf_lo(pk.x);
+                cs[1] += bf_hi(pk.x);
+                cs[2] += bf_lo(pk.y);
+                cs[3] += bf_hi(pk.y);
+            }
+            *(u32x2*)(smem + stage_off<kTile>(sl, f)) = pk;
         }
+        if (MODE == 1 && !a.fwd_only) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) cs[r] = sum_row16(cs[r]);
+            if (l16 == 0 && s0 + 128 * wn < B) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) db1[f + r] = cs[r];
+            }
+        }
+    }
+    if (MODE == 0) {
+        u32x4* mp = (u32x4*)(a.mask + ((int64_t)g * gridDim.x + blockIdx.x) * kThreads * 8) + 2 * threadIdx.x;
+        mp[0] = u32x4{mbits[0], mbits[1], mbits[2], mbits[3]};
+        mp[1] = u32x4{mbits[4], mbits[5], mbits[6], mbits[7]};
     }
     __syncthreads();
     const int64_t o = ((int64_t)g * B + s0) * H + f0;
-    if (MODE == 0) stage_out<kTile, kTile>(smem, a.h1 + o, H, srows, nullptr);
-    else stage_out<kTile, kTile>(smem, a.dz1 + o, H, srows, a.h1 + o);
+    stage_out<kTile, kTile>(smem, (MODE == 0 ? a.h1 : a.dz1) + o, H, srows);
 }
 
 // --------------------------------------------------------------- fwd2
@@ -374,6 +503,21 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
     const int lo = kc_lane();
     constexpr int RING = NST * STG, STAGE = kFwd2Samples * H;
     float* svp = (float*)(smem + (RING > STAGE ? RING : STAGE));  // [4][128] V partials of each wave
+    float* sq = svp + 4 * kFwd2Samples;                             // [128] q of the block's samples
+    float* sb2 = sq + kFwd2Samples;                                 // [H] b2
+    float* sw3 = sb2 + H;                                           // [H] w3
+    const float* prm = a.params + (int64_t)g * a.P;
+    // q, b2 and w3 to LDS while the first stages are in flight, so that the
+    // epilogue reads them without a memory round trip
+    auto pre = [&] {
+        const int t = threadIdx.x;
+        if (t < kFwd2Samples) sq[t] = (!a.fwd_only && t < srows) ? a.q[s0 + t] : 0.f;
+        for (int f = t; f < H; f += kThreads) {
+            sb2[f] = prm[a.off_b2 + f];
+            sw3[f] = prm[a.off_w3 + f];
+        }
+        wait_lgkm0();  // the stores are complete before the loop's first barrier
+    };
 
     f4 acc[MT][8];
 #pragma unroll
@@ -381,14 +525,14 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
-    kloop<NST, LPT>(
-        H / kBK,
-        [&](int s, int buf) {
-            uint16_t* st_ = smem + buf * STG;
-            dma_kc<H>(A, H, H, s * kBK, st_);
-            dma_kc<kFwd2Samples>(Bm, H, srows, s * kBK, st_ + H * kBK);
-        },
-        [&](int, int buf) {
+    auto issue = [&](int s, int buf) {
+        uint16_t* st_ = smem + buf * STG;
+        dma_kc<H>(A, H, H, s * kBK, st_);
+        dma_kc<kFwd2Samples>(Bm, H, srows, s * kBK, st_ + H * kBK);
+    };
+    if constexpr (H == 512) {
+        // no registers for a second fragment set next to this epilogue
+        kloop1<NST, LPT>(H / kBK, issue, [&](int buf) {
             const uint16_t* ta = smem + buf * STG + ((H / 4) * wv) * kBK + lo;
             const uint16_t* tb = smem + buf * STG + H * kBK + lo;
             bf16x8 fa[MT], fb[8];
@@ -401,13 +545,35 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) acc[i][j] = mma(fa[i], fb[j], acc[i][j]);
             reads_then_mfma<8 + MT, 8 * MT>();
-        });
+        }, pre);
+    } else {
+        bf16x8 fa[MT], fb[2][8];  // fa: one set, re-read row by row (see kloop)
+        kloop<NST, LPT>(
+            H / kBK, issue,
+            [&](int buf, auto p) {
+                constexpr int P = decltype(p)::value;
+                const uint16_t* ta = smem + buf * STG + ((H / 4) * wv) * kBK + lo;
+                const uint16_t* tb = smem + buf * STG + H * kBK + lo;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) fb[P][j] = *(const bf16x8*)(tb + j * 16 * kBK);
+#pragma unroll
+                for (int i = 0; i < MT; ++i) fa[i] = *(const bf16x8*)(ta + i * 16 * kBK);
+            },
+            [&](auto p) {
+                constexpr int P = decltype(p)::value;
+#pragma unroll
+                for (int i = 0; i < MT; ++i)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) acc[i][j] = mma(fa[i], fb[P][j], acc[i][j]);
+                reads_among_mfma<8 + MT, 8 * MT>();
+            },
+            pre);
+    }
 
     const int l = threadIdx.x & 63, l16 = l & 15, q = l >> 4;
-    const float* prm = a.params + (int64_t)g * a.P;
     const int fb0 = (H / 4) * wv + 4 * q;
-    // z2 = acc + b2; this wave's part of v for each of its 8 samples
-    float w3v[MT][4];
+    // z2 = acc + b2 (formed again in each pass below, so the accumulators
+    // are only read); this wave's part of v for each of its 8 samples
     float vp[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) vp[j] = 0.f;
@@ -416,13 +582,11 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int f = fb0 + 16 * i + r;
-            const float b2 = prm[a.off_b2 + f];
-            w3v[i][r] = prm[a.off_w3 + f];
+            const float b2 = sb2[f], w3 = sw3[f];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float z = acc[i][j][r] + b2;
-                acc[i][j][r] = z;
-                vp[j] = fmaf(w3v[i][r], z > 0.f ? z : 0.f, vp[j]);
+                vp[j] = fmaf(w3, z > 0.f ? z : 0.f, vp[j]);
             }
         }
     }
@@ -453,7 +617,7 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
         const float v = ((svp[sl] + svp[kFwd2Samples + sl]) + (svp[2 * kFwd2Samples + sl] + svp[3 * kFwd2Samples + sl])) + b3;
         dv[j] = 0.f;
         if (s < B) {
-            const float diff = a.q[s] - v;
+            const float diff = sq[sl] - v;
             const float w = diff >= 0.f ? tau : 1.f - tau;
             dv[j] = -2.f * w * diff * a.invB;
             lsum += w * diff * diff;
@@ -461,7 +625,7 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
             if (wv == 0 && q == 0 && a.out_v) a.out_v[(int64_t)g * B + s] = v;
         }
     }
-    float* sp = a.spart + ((int64_t)g * a.nblk + blk) * (2 * H + 1);
+    float* sp = a.spart + ((int64_t)g * a.nblk + blk) * spart_w(H);
     if (wv == 0) {
         lsum = sum_row16(lsum);
         dsum = sum_row16(dsum);
@@ -473,14 +637,19 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
     // dz2 = dv w3 relu'(z2) -> DZ2; block sums of dz2 and dv relu(z2)
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-        float db2[4] = {0.f, 0.f, 0.f, 0.f}, dw3[4] = {0.f, 0.f, 0.f, 0.f};
+        float db2[4] = {0.f, 0.f, 0.f, 0.f}, dw3[4] = {0.f, 0.f, 0.f, 0.f}, b2[4], w3[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            b2[r] = sb2[fb0 + 16 * i + r];
+            w3[r] = sw3[fb0 + 16 * i + r];
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             float d[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float z = acc[i][j][r];
-                d[r] = z > 0.f ? dv[j] * w3v[i][r] : 0.f;
+                const float z = acc[i][j][r] + b2[r];
+                d[r] = z > 0.f ? dv[j] * w3[r] : 0.f;
                 dw3[r] = fmaf(dv[j], z > 0.f ? z : 0.f, dw3[r]);
             }
             // db2 sums dz2 as stored (bf16), as the products that read it do
@@ -505,20 +674,21 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
         }
     }
     __syncthreads();
-    stage_out<H, kFwd2Samples>(smem, a.dz2 + ((int64_t)g * B + s0) * H, H, srows, nullptr);
+    stage_out<H, kFwd2Samples>(smem, a.dz2 + ((int64_t)g * B + s0) * H, H, srows);
 }
 
 // --------------------------------------------------------------- wgrad
-// Per (chunk, job): job < n2 -> a 256 x 256 tile of dW2 = dz2^T h1; job < n2
-// + n1 -> a tile of dW1 = dz1^T s (+ db1 rows when it is the first column
-// tile); job == n2 + n1 -> the fwd2 block sums of the chunk.
+// Per (chunk, job): job < n2 -> a 256 x 256 tile of dW2 = dz2^T h1; else a
+// tile of dW1 = dz1^T s.  After its tile, job j of a chunk also adds the
+// block sums of the chunk (db2, dw3, db3 from fwd2, db1 from bwd1) for its
+// share of the entries, so that no workgroup exists for that small sum alone.
 __global__ __launch_bounds__(kThreads) void big_wgrad_kernel(BigArgs a) {
     extern __shared__ __align__(16) uint16_t smem[];
-    constexpr int NST = 4, STG = 2 * kBK * kTile;
+    constexpr int NST = kWgradStages, STG = 2 * kBK * kTile;
     const int g = blockIdx.y;
     const int H = a.H, S = a.S, B = a.B;
     const int nth = H / kTile, nts = (S + kTile - 1) / kTile;
-    const int n2 = nth * nth, n1 = nth * nts, njob = n2 + n1 + 1;
+    const int n2 = nth * nth, n1 = nth * nts, njob = n2 + n1;
     int c, job;
     xcd_map(blockIdx.x, a.nchunk, njob, c, job);
     const int b0 = c * a.chunk;
@@ -526,24 +696,11 @@ __global__ __launch_bounds__(kThreads) void big_wgrad_kernel(BigArgs a) {
     float* part = a.part + ((int64_t)g * a.nchunk + c) * a.Pp;
     const int tid = threadIdx.x;
 
-    if (job == n2 + n1) {
-        // block sums of the chunk's 128-sample blocks, in block order
-        const int k0 = b0 / kFwd2Samples, k1 = (b0 + len + kFwd2Samples - 1) / kFwd2Samples;
-        const float* sp = a.spart + (int64_t)g * a.nblk * (2 * H + 1);
-        for (int e = tid; e < 2 * H + 1; e += kThreads) {
-            float s = 0.f;
-            for (int k = k0; k < k1; ++k) s += sp[(int64_t)k * (2 * H + 1) + e];
-            const int64_t off = e < H ? a.off_b2 + e : (e < 2 * H ? a.off_w3 + (e - H) : a.off_b3);
-            part[off] = s;
-        }
-        return;
-    }
     const uint16_t* A;
     const uint16_t* Bm;
     int64_t ldb;
     int fa0, fb0, fbmax, ldo;
     float* dst;
-    float* rowsum = nullptr;
     if (job < n2) {
         const int mt = job / nth, nt = job % nth;
         A = a.dz2 + ((int64_t)g * B + b0) * H;
@@ -556,56 +713,62 @@ __global__ __launch_bounds__(kThreads) void big_wgrad_kernel(BigArgs a) {
         Bm = a.x + (int64_t)b0 * a.ldx;
         ldb = a.ldx; fa0 = kTile * mt; fb0 = kTile * nt; fbmax = S;
         dst = part; ldo = S;  // dW1 sits at offset 0
-        if (nt == 0) rowsum = part + a.off_b1;
     }
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wv & 1, wn = wv >> 1;
     const NatBase nb = nat_base();
-    const bool sums = rowsum != nullptr && wn == 0;
-    const bf16x8 one = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
-    f4 acc[8][8], accb[8];
+    f4 acc[8][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        accb[i] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
-    }
     const int nsl = (len + kBK - 1) / kBK;
-    const int tail = len - (nsl - 1) * kBK;  // samples of the last slice, 1 .. 32
 
+    // this job's share of the chunk's block sums (db2, dw3, db3 from fwd2,
+    // db1 from bwd1), in block order, while the first stages are in flight
+    auto pre = [&] {
+        const int ne = spart_w(H), per = (ne + njob - 1) / njob;
+        const int k0 = b0 / kFwd2Samples, k1 = (b0 + len + kFwd2Samples - 1) / kFwd2Samples;
+        const float* sp = a.spart + (int64_t)g * a.nblk * ne;
+        for (int t = tid; t < per; t += kThreads) {
+            const int e = job * per + t;
+            if (e >= ne) break;
+            float s = 0.f;
+#pragma unroll 8
+            for (int k = k0; k < k1; ++k) s += sp[(int64_t)k * ne + e];
+            const int64_t off = e < H ? a.off_b2 + e
+                                      : (e < 2 * H ? a.off_w3 + (e - H) : (e == 2 * H ? a.off_b3 : a.off_b1 + (e - 2 * H - 1)));
+            part[off] = s;
+        }
+    };
+    bf16x8 fa[8], fb[2][8];  // fa: one set, re-read row by row (see kloop)
     kloop<NST, 8>(
         nsl,
         [&](int s, int buf) {
             uint16_t* st_ = smem + buf * STG;
             const int sm = len - s * kBK;
-            dma_nat(A + (int64_t)s * kBK * H, H, sm, fa0, H, st_);
-            dma_nat(Bm + (int64_t)s * kBK * ldb, ldb, sm, fb0, fbmax, st_ + kBK * kTile);
+            dma_nat<true>(A + (int64_t)s * kBK * H, H, sm, fa0, H, st_);
+            dma_nat<false>(Bm + (int64_t)s * kBK * ldb, ldb, sm, fb0, fbmax, st_ + kBK * kTile);
         },
-        [&](int s, int buf) {
-            uint16_t* ta = smem + buf * STG;
-            uint16_t* tb = ta + kBK * kTile;
-            if (s == nsl - 1 && tail < kBK) {
-                // samples past the end of the chunk contribute zero
-                for (int e = tid; e < 2 * (kBK - tail) * (kTile / 8); e += kThreads) {
-                    const int t = e / ((kBK - tail) * (kTile / 8)), rem = e - t * ((kBK - tail) * (kTile / 8));
-                    const int row = tail + rem / (kTile / 8), u = rem % (kTile / 8);
-                    *(u32x4*)((t ? tb : ta) + row * kTile + 8 * u) = u32x4{0u, 0u, 0u, 0u};
-                }
-                __syncthreads();
-            }
-            bf16x8 fa[8], fb[8];
+        [&](int buf, auto p) {
+            constexpr int P = decltype(p)::value;
+            const uint16_t* ta = smem + buf * STG;
+            const uint16_t* tb = ta + kBK * kTile;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) fb[j] = nat_frag(tb, nb, 8 * wn + j);
+            for (int j = 0; j < 8; ++j) fb[P][j] = nat_frag(tb, nb, 8 * wn + j);
 #pragma unroll
             for (int i = 0; i < 8; ++i) fa[i] = nat_frag(ta, nb, 8 * wm + i);
+        },
+        [&](auto p) {
+            constexpr int P = decltype(p)::value;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] = mma(fa[i], fb[j], acc[i][j]);
-                if (sums) accb[i] = mma(fa[i], one, accb[i]);
-            }
-        });
+                for (int j = 0; j < 8; ++j) acc[i][j] = mma(fa[i], fb[P][j], acc[i][j]);
+            reads_among_mfma<32, 64>();
+        },
+        pre);
 
     const int l = tid & 63, l16 = l & 15, q = l >> 4;
 #pragma unroll
@@ -619,18 +782,15 @@ __global__ __launch_bounds__(kThreads) void big_wgrad_kernel(BigArgs a) {
                 for (int r = 0; r < 4; ++r) dst[(int64_t)(m + r) * ldo + n] = acc[i][j][r];
             }
         }
-        if (sums && l16 == 0) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) rowsum[m + r] = accb[i][r];
-        }
     }
+
 }
 
-constexpr size_t tile_lds_bytes() { return (size_t)4 * 2 * kTile * kBK * 2; }
+constexpr size_t ring_lds_bytes(int nst) { return (size_t)nst * 2 * kTile * kBK * 2; }
 template <int H>
 constexpr size_t fwd2_lds_bytes() {
     return (size_t)(3 * (H + kFwd2Samples) * kBK > kFwd2Samples * H ? 3 * (H + kFwd2Samples) * kBK : kFwd2Samples * H) * 2 +
-           4 * kFwd2Samples * sizeof(float);
+           (5 * kFwd2Samples + 2 * H) * sizeof(float);
 }
 
 template <typename K>
@@ -644,15 +804,23 @@ bool iql_big_supported(int dtype, int S, int H) {
     return dtype == 1 && (H == 256 || H == 512) && S >= kBK && S % kBK == 0 && S <= 4096;
 }
 int iql_big_blocks(int B) { return (B + kFwd2Samples - 1) / kFwd2Samples; }
-int iql_big_max_chunks(int S, int H) {
-    const int nth = H / kTile, nts = (S + kTile - 1) / kTile;
-    const int tiles = nth * nth + nth * nts;
-    return 256 / tiles > 1 ? 256 / tiles : 1;
+int iql_big_spart_width(int H) { return spart_w(H); }
+// ReLU mask words: 8 per lane of every fwd1 tile (256 lanes)
+size_t iql_big_mask_words(int G, int B, int H) {
+    return (size_t)G * ((B + kTile - 1) / kTile) * (H / kTile) * kThreads * 8;
 }
-// samples per weight-gradient chunk for a batch of B rows: a multiple of the
-// fwd2 block, so every block's sums belong to exactly one chunk
-int iql_big_chunk(int S, int H, int B) {
-    const int target = iql_big_max_chunks(S, H);
+static int big_tiles(int S, int H) {
+    const int nth = H / kTile, nts = (S + kTile - 1) / kTile;
+    return nth * nth + nth * nts;
+}
+// chunks of one trainer: at most one weight-gradient tile per CU over all
+// trainers (256 CUs), so the launch runs as one round
+int iql_big_max_chunks(int S, int H) { return 256 / big_tiles(S, H) > 1 ? 256 / big_tiles(S, H) : 1; }
+// samples per weight-gradient chunk for a batch of B rows and G trainers: a
+// multiple of the fwd2 block, so every block's sums belong to exactly one chunk
+int iql_big_chunk(int S, int H, int G, int B) {
+    const int per = 256 / (big_tiles(S, H) * G);
+    const int target = per > 1 ? per : 1;
     int c = (B + target - 1) / target;
     c = (c + kFwd2Samples - 1) / kFwd2Samples * kFwd2Samples;
     return c < kFwd2Samples ? kFwd2Samples : c;
@@ -681,13 +849,13 @@ static hipError_t big_launch(const IqlDims& d, const IqlBuffers& b, const float*
     a.w2s = (const uint16_t*)b.w2s; a.w2ts = (const uint16_t*)b.w2ts;
     a.params = b.params; a.q = q;
     a.h1 = (uint16_t*)b.act_h1; a.dz2 = (uint16_t*)b.act_dz2; a.dz1 = (uint16_t*)b.act_dz1;
-    a.spart = b.big_spart; a.loss_part = b.loss_part; a.out_v = out_v; a.part = b.part;
+    a.spart = b.big_spart; a.mask = b.big_mask; a.loss_part = b.loss_part; a.out_v = out_v; a.part = b.part;
     a.P = d.P; a.Pp = d.Pp;
     a.off_b1 = (int64_t)H * S; a.off_w2 = a.off_b1 + H; a.off_b2 = a.off_w2 + (int64_t)H * H;
     a.off_w3 = a.off_b2 + H; a.off_b3 = a.off_w3 + H;
     a.tau0 = tau[0]; a.tau1 = tau[G > 1 ? 1 : 0]; a.invB = 1.f / (float)B;
     a.B = B; a.S = S; a.H = H;
-    a.chunk = iql_big_chunk(S, H, B);
+    a.chunk = iql_big_chunk(S, H, G, B);
     a.nchunk = (B + a.chunk - 1) / a.chunk;
     a.nblk = iql_big_blocks(B);
     if (vo) {
@@ -697,9 +865,9 @@ static hipError_t big_launch(const IqlDims& d, const IqlBuffers& b, const float*
 
     static bool attr = false;
     if (!attr) {
-        hipError_t e = allow_lds(big_tile_kernel<0>, tile_lds_bytes());
-        if (e == hipSuccess) e = allow_lds(big_tile_kernel<1>, tile_lds_bytes());
-        if (e == hipSuccess) e = allow_lds(big_wgrad_kernel, tile_lds_bytes());
+        hipError_t e = allow_lds(big_tile_kernel<0>, ring_lds_bytes(kTileStages));
+        if (e == hipSuccess) e = allow_lds(big_tile_kernel<1>, ring_lds_bytes(kTileStages));
+        if (e == hipSuccess) e = allow_lds(big_wgrad_kernel, ring_lds_bytes(kWgradStages));
         if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<256>, fwd2_lds_bytes<256>());
         if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<512>, fwd2_lds_bytes<512>());
         if (e != hipSuccess) return e;
@@ -707,16 +875,14 @@ static hipError_t big_launch(const IqlDims& d, const IqlBuffers& b, const float*
     }
     const int nst = (B + kTile - 1) / kTile;
     const dim3 gt(nst * (H / kTile), G);
-    hipLaunchKernelGGL(big_tile_kernel<0>, gt, dim3(kThreads), tile_lds_bytes(), stream, a);
+    hipLaunchKernelGGL(big_tile_kernel<0>, gt, dim3(kThreads), ring_lds_bytes(kTileStages), stream, a);
     const dim3 g2(a.nblk, G);
     if (H == 512) hipLaunchKernelGGL(big_fwd2_kernel<512>, g2, dim3(kThreads), fwd2_lds_bytes<512>(), stream, a);
     else hipLaunchKernelGGL(big_fwd2_kernel<256>, g2, dim3(kThreads), fwd2_lds_bytes<256>(), stream, a);
     if (vo) return hipGetLastError();
-    hipLaunchKernelGGL(big_tile_kernel<1>, gt, dim3(kThreads), tile_lds_bytes(), stream, a);
-    const int nth = H / kTile, nts = (S + kTile - 1) / kTile;
-    const int njob = nth * nth + nth * nts + 1;
-    const dim3 gw(a.nchunk * njob, G);
-    hipLaunchKernelGGL(big_wgrad_kernel, gw, dim3(kThreads), tile_lds_bytes(), stream, a);
+    hipLaunchKernelGGL(big_tile_kernel<1>, gt, dim3(kThreads), ring_lds_bytes(kTileStages), stream, a);
+    const dim3 gw(a.nchunk * big_tiles(S, H), G);
+    hipLaunchKernelGGL(big_wgrad_kernel, gw, dim3(kThreads), ring_lds_bytes(kWgradStages), stream, a);
     return hipGetLastError();
 }
 
