@@ -11,6 +11,9 @@ bar on the raw gradient of a bf16-operand step can only hold away from
 convergence; there the kernel is compared with the oracle that stores the same
 operands in bf16 (``iql.bf16_operands``, pinned against torch autograd in
 test_oracle_iql.py).
+
+The second case locates the error: it enters through V, from the forward's
+operand storage, not through the backward's (dz1 among them).
 """
 import numpy as np
 
@@ -57,3 +60,36 @@ def test_bf16_operand_error_grows_as_training_converges():
     assert gaps[300][0] > 0.1
     # ... while binary32 storage of the same operands stays inside it
     assert gaps[300][1] < 1e-2
+
+
+def _grad_split(p, X, q, tau, rnd_fwd, rnd_bwd):
+    v, cache = iql.forward(p, X, rnd_fwd)
+    _, dv = iql.expectile(q, v, tau)
+    return iql.unflatten(iql.flatten(iql.backward(p, cache, dv, rnd_bwd)), X.shape[1], p["w1"].shape[0],
+                         p["w2"].shape[0])
+
+
+def test_wide_tau03_gradient_error_comes_from_forward_storage():
+    """Batch 4096, state 256, hidden 512, tau 0.3 at its first step (the
+    inputs of the two-trainer wide GPU case): bf16 storage moves dW1 by a few
+    percent of the fp64 definition.  Rounding only the forward's operands (W1,
+    W2, h1) moves it as much, while rounding only the backward's (dz2, h1 in
+    dW2, W2 in dh1, dz1) moves it by about 1e-3: the error enters through V,
+    so keeping dz1 at a higher precision for dW1 would not remove it."""
+    import synth
+    w = synth.shrink(synth.WORKLOADS["stress_b65536_s256_h512_bf16"], S=256, H=512, groups=2,
+                     taus=(0.9, 0.3), G=8)
+    B = 4096
+    g = np.random.default_rng(0)
+    X = synth._bf16_values(g.standard_normal((B, w.S)).astype(np.float32)).astype(np.float64)
+    q = (g.standard_normal(B) * w.q_sd).astype(np.float32)
+    p = iql.unflatten(synth.group_inits(w, seed=synth.DEFAULT_SEED + 10)[1], w.S, w.H, w.H)
+    tau = 0.3
+    ref = _grad_split(p, X, q, tau, None, None)
+    both = _grad_split(p, X, q, tau, iql.bf16_operands, iql.bf16_operands)
+    fwd = _grad_split(p, X, q, tau, iql.bf16_operands, None)
+    bwd = _grad_split(p, X, q, tau, None, iql.bf16_operands)
+    r = {k: _rel(v["w1"], ref["w1"]) for k, v in (("both", both), ("fwd", fwd), ("bwd", bwd))}
+    assert r["both"] > 2e-2 and r["fwd"] > 2e-2
+    assert abs(r["fwd"] - r["both"]) < 0.2 * r["both"]
+    assert r["bwd"] < 3e-3
