@@ -297,7 +297,7 @@ class Context:
 LAUNCH_KERNELS = (("relabel_norms", ("step_her_norms_kernel", "her_relabel_kernel")),
                   ("fwd_bwd", ("iql_fused16w_kernel", "iql_fused_kernel", "big_tile_kernel", "big_fwd2_kernel",
                                "big_wgrad_kernel", "layer_gemm_kernel", "iql_rows_kernel", "iql_wgrad_kernel",
-                               "aw_policy_kernel")),
+                               "aw_policy_kernel", "aw_policy_vec_kernel")),
                   ("reduce_saxpy", ("step_reduce_saxpy_kernel",)),
                   ("adam", ("step_adam_kernel",)))
 
@@ -509,9 +509,13 @@ def summarize_profiles(d, workload=None):
                              "counter_rate_tflops": rate, "avg_kernel_us": t_us,
                              "lds_active_frac": lact, "lds_conflict_frac": lcon}
         L.append("")
-        L.append("The forward/backward kernel's MFMA flops exceed the algorithmic count by its bias-gradient "
-                 "products (an extra MFMA against an all-ones operand per weight-gradient sweep) and the zero "
-                 "padding of tiles.")
+        if mfma_json is not None:
+            L.append("The forward/backward kernel's MFMA flops exceed the algorithmic count by its bias-gradient "
+                     "products (an extra MFMA against an all-ones operand per weight-gradient sweep) and the zero "
+                     "padding of tiles.")
+        else:
+            L.append("Several kernels share the forward/backward launch here, so no single kernel's MFMA flops "
+                     "are set against the algorithmic count; the rate column is each kernel's own.")
         L.append("")
     L.append(f"`needed MB` is each launch's inputs and outputs read or written once (`launch_bytes` in "
              f"bench.py).  For the forward/backward launch it includes its fp32 gradient partials "
