@@ -182,9 +182,9 @@ def mfma_from_profiles(name, src_hash):
             if k in d}
 
 
-def kernel_source_hash():
+def kernel_source_hash(extra=()):
     h = hashlib.sha256()
-    for f in ("iql.hip", "common.hpp", "her_block.hpp", "budget_block.hpp", "iql_update.hpp", "launch.hpp"):
+    for f in ("iql.hip", "common.hpp", "her_block.hpp", "budget_block.hpp", "iql_update.hpp", "launch.hpp", *extra):
         with open(os.path.join(ROOT, "offline_rl_step_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -395,7 +395,8 @@ def summarize_profiles(d, workload=None):
                                 text=True, check=True).stdout.strip()
     except Exception:  # pragma: no cover
         commit = "unknown"
-    src_hash = kernel_source_hash()
+    # the wide-hidden kernels' source counts for the other workloads' summaries
+    src_hash = kernel_source_hash(() if default else ("iql_big.hip", "iql_layered.hip", "aw.hip"))
     launch_of = {}
     for launch, keys in LAUNCH_KERNELS:
         for r in stats:
