@@ -4,34 +4,36 @@
 // Plan", section "Current State / IQL (CPU)"; the backward products of "Phase
 // 2: Multi-Stream Graph Parallelism", section "2C. Grouped GEMM for IQL"):
 //
-//   fwd1   h1 = relu(W1 s + b1)                         -> H1  [B][H] bf16
+//   fwd1   h1 = relu(W1 s + b1)                         -> H1  [B][H] bf16,
+//          and relu'(z1) as bits for the backward product
 //   fwd2   z2 = W2 h1 + b2 over all H features of a 128-sample block, then in
 //          the epilogue v = w3 . relu(z2) + b3, the expectile loss, dv,
 //          dz2 = dv w3 relu'(z2) -> DZ2 [B][H] bf16, and the block's sums of
-//          dz2 (db2), dv relu(z2) (dw3) and dv (db3)
-//   bwd1   dz1 = (W2^T dz2) * relu'(z1)                  -> DZ1 [B][H] bf16
-//   wgrad  dW2 = dz2^T h1, dW1 = dz1^T s (with db1 = column sums of dz1)
-//          over chunks of samples, one fp32 partial row per chunk; the jobs
-//          of a chunk also add its fwd2 block sums into the same row
+//          dz2 (db2), dv relu(z2) (dw3) and dv (db3); in training the same
+//          workgroup goes on with dh1 = W2^T dz2 from its dz2 tile in LDS,
+//          dz1 = dh1 relu'(z1) -> DZ1 [B][H] bf16 and the block's db1 sums
+//   wgrad  dW2 = dz2^T h1, dW1 = dz1^T s over chunks of samples, one fp32
+//          partial row per chunk; the jobs of a chunk also add its block
+//          sums (db2, dw3, db3, db1) into the same row
 //
 // then the fixed-order partial reduction and Adam shared with the other
 // paths (no float atomics anywhere).
 //
 // MI355X design.  Every product runs on v_mfma_f32_16x16x32_bf16 with a
 // 128 x 128 output tile per wave (8 x 8 MFMA tiles, 256 accumulators), four
-// waves per workgroup.  Operands stream HBM -> LDS with global_load_lds_dwordx4
-// (no register staging) through a ring of 3-4 stages of 32 k each, so two or
-// three stages are in flight while one is consumed; each stage ends in one
-// s_barrier after the wave's own vmcnt wait.  Activations are row-major
-// [sample][feature]:
+// waves per workgroup and one workgroup per CU.  Operands stream HBM -> LDS
+// with global_load_lds_dwordx4 (no register staging) through a ring of 32-k
+// stages; each stage ends in one s_barrier after the wave's own vmcnt wait,
+// and the fragments of the next stage are read from LDS while the current
+// stage's MFMAs run.  Activations are row-major [sample][feature]:
 //   * in the forward products k is the feature (contiguous): LDS rows of 32 k
 //     (64 bytes), the 16-byte unit u of row r stored at u ^ ((r >> 1) & 3),
 //     read with ds_read_b128 (conflict-free);
 //   * in the weight gradients k is the sample: LDS keeps the natural
 //     [sample][feature] rows (512 bytes), unit v of sample s stored at
 //     v ^ (2 (s & 3)), and the MFMA operands are read with the LDS transpose
-//     load ds_read_b64_tr_b16 (conflict-free), so no transposed copy of an
-//     activation is ever written.
+//     load ds_read_b64_tr_b16, so no transposed copy of an activation is
+//     ever written.
 // The product orientation is D[feature][sample], so a lane ends with four
 // consecutive features of one sample: bias, ReLU masks and the bf16 stores
 // work on 8-byte runs of a row.
@@ -55,8 +57,8 @@ typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 constexpr int kBK = 32;           // k per stage
 constexpr int kFwd2Samples = 128; // samples per fwd2 block (the loss blocks)
-constexpr int kTile = 256;        // fwd1 / bwd1 / wgrad output tile edge
-constexpr int kTileStages = 5;    // ring depth of fwd1 / bwd1 (5 x 32 KB)
+constexpr int kTile = 256;        // fwd1 / wgrad output tile edge
+constexpr int kTileStages = 5;    // ring depth of fwd1 (5 x 32 KB)
 constexpr int kWgradStages = 5;   // ring depth of wgrad (5 x 32 KB)
 // entries of a loss block's sums: db2 [H], dw3 [H], db3, db1 [H]
 __host__ __device__ constexpr int spart_w(int H) { return 3 * H + 1; }
@@ -320,8 +322,8 @@ struct BigArgs {
     uint16_t* h1;           // [G][B][H]
     uint16_t* dz2;          // [G][B][H]
     uint16_t* dz1;          // [G][B][H]
-    float* spart;           // [G][nblk][3H + 1]: db2, dw3, db3 (fwd2) and db1 (bwd1) of each 128-sample block
-    uint32_t* mask;         // [G][tiles][256 lanes][8 words]: relu'(z1) bits, fwd1 -> bwd1
+    float* spart;           // [G][nblk][3H + 1]: db2, dw3, db3 and db1 of each 128-sample block
+    uint32_t* mask;         // [G][tiles][256 lanes][8 words]: relu'(z1) bits from fwd1
     float* loss_part;       // [G][nblk]
     float* out_v;           // [G][B] or null
     float* part;            // [G][nchunk][Pp]
@@ -332,6 +334,14 @@ struct BigArgs {
     int fwd_only;  // 1: V (and the bootstrap target) only
     ValueOut vo;
 };
+
+// First word of the ReLU mask bits of lane t of fwd1's tile (st, ft) of group
+// g: 8 words per lane, bit 4 j + r of word i for feature 128 wm + 16 i + 4 q + r
+// and sample 128 wn + 16 j + l16 of the tile (t = 64 (wm + 2 wn) + 16 q + l16).
+IQLH_DEV int64_t mask_word0(const BigArgs& a, int g, int st, int ft, int t) {
+    const int nst = (a.B + kTile - 1) / kTile, nft = a.H / kTile;
+    return ((((int64_t)g * nst + st) * nft + ft) * kThreads + t) * 8;
+}
 
 // Workgroup id -> (tile, group): consecutive ids go to different XCDs, so the
 // ids of one sample range are spread as id = xcd + 8 k; this picks the tiles
@@ -349,12 +359,10 @@ IQLH_DEV void xcd_map(int id, int nranges, int nper, int& range, int& job) {
     }
 }
 
-// ---------------------------------------------------- fwd1 / bwd1 products
-// D[f][s] = sum_k A[f][k] Bm[s][k] over a 256-feature x 256-sample tile.
-// MODE 0 (fwd1): A = W1 rows, Bm = batch rows, H1 = relu(D + b1).
-// MODE 1 (bwd1): A = W2^T rows, Bm = dz2 rows, DZ1 = D * (H1 > 0).
-template <int MODE>
-__global__ __launch_bounds__(kThreads) void big_tile_kernel(BigArgs a) {
+// ---------------------------------------------------------------- fwd1
+// D[f][s] = sum_k W1[f][k] s[s][k] over a 256-feature x 256-sample tile;
+// h1 = relu(D + b1), and the ReLU mask as bits for the backward product.
+__global__ __launch_bounds__(kThreads) void big_fwd1_kernel(BigArgs a) {
     extern __shared__ __align__(16) uint16_t smem[];
     constexpr int NST = kTileStages, STG = 2 * kTile * kBK;  // elements per stage
     const int g = blockIdx.y;
@@ -363,31 +371,13 @@ __global__ __launch_bounds__(kThreads) void big_tile_kernel(BigArgs a) {
     int st, ft;
     xcd_map(blockIdx.x, nst, nft, st, ft);
     const int f0 = ft * kTile, s0 = st * kTile;
-    const uint16_t* A;
-    int64_t lda;
-    const uint16_t* Bm;
-    int64_t ldb;
-    int K;
-    if (MODE == 0) {
-        A = a.w1s + (int64_t)g * H * a.ldw1 + (int64_t)f0 * a.ldw1; lda = a.ldw1;
-        Bm = a.x + (int64_t)s0 * a.ldx; ldb = a.ldx; K = a.S;
-    } else {
-        A = a.w2ts + (int64_t)g * H * H + (int64_t)f0 * H; lda = H;
-        Bm = a.dz2 + ((int64_t)g * B + s0) * H; ldb = H; K = H;
-    }
+    const uint16_t* A = a.w1s + (int64_t)g * H * a.ldw1 + (int64_t)f0 * a.ldw1;
+    const uint16_t* Bm = a.x + (int64_t)s0 * a.ldx;
     const int srows = B - s0;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wv & 1, wn = wv >> 1;
     const int lo = kc_lane();
 
-    // bwd1: this lane's ReLU mask bits, loaded before the operand copies
-    // (the oldest loads, so the loop's vmcnt waits cover them as well)
-    u32x4 mk[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
-    if (MODE == 1) {
-        const u32x4* mp = (const u32x4*)(a.mask + ((int64_t)g * gridDim.x + blockIdx.x) * kThreads * 8) + 2 * threadIdx.x;
-        mk[0] = mp[0];
-        mk[1] = mp[1];
-    }
     f4 acc[8][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -397,11 +387,11 @@ __global__ __launch_bounds__(kThreads) void big_tile_kernel(BigArgs a) {
 
     bf16x8 fa[8], fb[2][8];  // fa: one set, re-read row by row (see kloop)
     kloop<NST, 8>(
-        K / kBK,
+        a.S / kBK,
         [&](int s, int buf) {
             uint16_t* st_ = smem + buf * STG;
-            dma_kc<kTile>(A, lda, kTile, s * kBK, st_);
-            dma_kc<kTile>(Bm, ldb, srows, s * kBK, st_ + kTile * kBK);
+            dma_kc<kTile>(A, a.ldw1, kTile, s * kBK, st_);
+            dma_kc<kTile>(Bm, a.ldx, srows, s * kBK, st_ + kTile * kBK);
         },
         [&](int buf, auto p) {
             constexpr int P = decltype(p)::value;
@@ -424,72 +414,138 @@ __global__ __launch_bounds__(kThreads) void big_tile_kernel(BigArgs a) {
 
     // epilogue: lane holds features 128 wm + 16 i + 4 q + r of samples
     // 128 wn + 16 j + l16 (tile-local); staged as [sample][feature] rows.
-    // The ReLU mask of h1 passes from fwd1 to bwd1 as bits in the lane
-    // layout both share: bit 4 j + r of word i of lane tid of tile (g, id).
+    // relu'(z1) leaves as bits in this lane layout (mask_word0).
     const float* bias = a.params + (int64_t)g * a.P + a.off_b1 + f0;
     uint32_t mbits[8];
-    if (MODE == 1) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) mbits[i] = mk[i / 4][i % 4];
-    }
-    // db1 over this wave's 128 samples (one loss block), from dz1 as stored
-    float* db1 = a.spart + ((int64_t)g * a.nblk + (s0 + 128 * wn) / kFwd2Samples) * spart_w(H) + 2 * H + 1 + f0;
     __syncthreads();  // every wave is done with the last stage
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int f = 128 * wm + 16 * i + 4 * q;
-        float bb[4] = {0.f, 0.f, 0.f, 0.f}, cs[4] = {0.f, 0.f, 0.f, 0.f};
-        if (MODE == 0) {
+        float bb[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) bb[r] = bias[f + r];
-            mbits[i] = 0u;
-        }
+        for (int r = 0; r < 4; ++r) bb[r] = bias[f + r];
+        mbits[i] = 0u;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int sl = 128 * wn + 16 * j + l16;
             float y[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float z = acc[i][j][r] + bb[r];
-                if (MODE == 0) {
-                    y[r] = z > 0.f ? z : 0.f;
-                    mbits[i] |= (z > 0.f ? 1u : 0u) << (4 * j + r);
-                } else {
-                    y[r] = (mbits[i] >> (4 * j + r)) & 1u ? z : 0.f;
-                }
+                // relu as an integer max on the bit pattern (negative values
+                // and -0 become +0), and the mask bit from the result, so no
+                // compare results have to be held
+                const int zb = max(__float_as_int(acc[i][j][r] + bb[r]), 0);
+                y[r] = __int_as_float(zb);
+                mbits[i] |= min((uint32_t)zb, 1u) << (4 * j + r);
             }
+            *(u32x2*)(smem + stage_off<kTile>(sl, f)) = u32x2{cvt2(y[0], y[1]), cvt2(y[2], y[3])};
+        }
+    }
+    if (!a.fwd_only) {
+        u32x4* mp = (u32x4*)(a.mask + mask_word0(a, g, st, ft, threadIdx.x));
+        mp[0] = u32x4{mbits[0], mbits[1], mbits[2], mbits[3]};
+        mp[1] = u32x4{mbits[4], mbits[5], mbits[6], mbits[7]};
+    }
+    __syncthreads();
+    stage_out<kTile, kTile>(smem, a.h1 + ((int64_t)g * B + s0) * H + f0, H, srows);
+}
+
+// ------------------------------------------------- dh1 inside fwd2's workgroup
+// dh1[f][s] = sum_k W2^T[f][k] dz2[s][k] for the H features of this wave's
+// rows ((H / 4) w + 16 i + ..) and the block's 128 samples, K = H.  The B
+// operand is the dz2 tile staged in LDS ([sample][feature], 16-byte unit u of
+// row s at u ^ (s & 7)); the A operand comes from the W2^T shadow in global
+// memory (L2-resident after the first blocks), 16 bytes per lane, loaded one
+// k-step ahead.  Then dz1 = dh1 relu'(z1) from fwd1's mask bits, the block's
+// db1 sums from dz1 as stored, and dz1 staged and stored as whole rows.
+template <int H, int MT>
+IQLH_DEV const uint16_t* w2t_lane(const BigArgs& a, int g, int wv, int l16, int q) {
+    return a.w2ts + (int64_t)g * H * H + (int64_t)((H / 4) * wv + l16) * H + 8 * q;
+}
+// the first k-step's W2^T fragments (issued before the dz2 stores, so that
+// waiting for them does not wait for the stores)
+template <int H, int MT>
+IQLH_DEV void w2t_frags(const uint16_t* At, int kt, bf16x8 (&f)[MT]) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) f[i] = *(const bf16x8*)(At + (int64_t)16 * i * H + kBK * kt);
+}
+template <int H, int MT>
+IQLH_DEV void backward_h1(const BigArgs& a, uint16_t* smem, f4 (&acc)[MT][8], bf16x8 (&fa0)[MT], int g, int blk,
+                          int s0, int srows, int wv, int l, int l16, int q) {
+    constexpr int NK = H / kBK;
+    static_assert(NK % 2 == 0, "k-steps in pairs");
+    const uint16_t* At = w2t_lane<H, MT>(a, g, wv, l16, q);
+    // this lane's mask words: fwd1 tile (s0 / 256, f / 256), lane
+    // 64 (wm + 2 wn) + l with wn = the block's half of its 256-sample tile
+    uint32_t mb[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        const int f = (H / 4) * wv + 16 * i;
+        const int ft = f / kTile, wm = (f % kTile) / 128, word = (f % 128) / 16;
+        mb[i] = a.mask[mask_word0(a, g, s0 / kTile, ft, 64 * (wm + 2 * (blk & 1)) + l) + word];
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 fa1[MT], fb[8];
+    auto load_a = [&](int kt, bf16x8 (&f)[MT]) __attribute__((always_inline)) { w2t_frags<H, MT>(At, kt, f); };
+    auto step = [&](int kt, bf16x8 (&cur)[MT], bf16x8 (&nxt)[MT]) __attribute__((always_inline)) {
+        if (kt + 1 < NK) load_a(kt + 1, nxt);
+        // the next step's loads stay ahead of this step's MFMAs (the
+        // scheduler would otherwise sink each load to its first use)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) fb[j] = *(const bf16x8*)(smem + stage_off<H>(16 * j + l16, kBK * kt + 8 * q));
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[i][j] = mma(cur[i], fb[j], acc[i][j]);
+    };
+#pragma unroll
+    for (int kt = 0; kt < NK; kt += 2) {
+        step(kt, fa0, fa1);
+        step(kt + 1, fa1, fa0);
+    }
+    __syncthreads();  // every wave is done with the dz2 tile
+    float* db1 = a.spart + ((int64_t)g * a.nblk + blk) * spart_w(H) + 2 * H + 1;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        const int f = (H / 4) * wv + 16 * i + 4 * q;
+        float cs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int sl = 16 * j + l16;
+            float y[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[r] = (mb[i] >> (4 * j + r)) & 1u ? acc[i][j][r] : 0.f;
             const u32x2 pk = u32x2{cvt2(y[0], y[1]), cvt2(y[2], y[3])};
-            if (MODE == 1 && sl < srows) {
+            if (sl < srows) {
                 cs[0] += bf_lo(pk.x);
                 cs[1] += bf_hi(pk.x);
                 cs[2] += bf_lo(pk.y);
                 cs[3] += bf_hi(pk.y);
             }
-            *(u32x2*)(smem + stage_off<kTile>(sl, f)) = pk;
+            *(u32x2*)(smem + stage_off<H>(sl, f)) = pk;
         }
-        if (MODE == 1 && !a.fwd_only) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) cs[r] = sum_row16(cs[r]);
-            if (l16 == 0 && s0 + 128 * wn < B) {
+        for (int r = 0; r < 4; ++r) cs[r] = sum_row16(cs[r]);
+        if (l16 == 0) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) db1[f + r] = cs[r];
-            }
+            for (int r = 0; r < 4; ++r) db1[f + r] = cs[r];
         }
-    }
-    if (MODE == 0) {
-        u32x4* mp = (u32x4*)(a.mask + ((int64_t)g * gridDim.x + blockIdx.x) * kThreads * 8) + 2 * threadIdx.x;
-        mp[0] = u32x4{mbits[0], mbits[1], mbits[2], mbits[3]};
-        mp[1] = u32x4{mbits[4], mbits[5], mbits[6], mbits[7]};
     }
     __syncthreads();
-    const int64_t o = ((int64_t)g * B + s0) * H + f0;
-    stage_out<kTile, kTile>(smem, (MODE == 0 ? a.h1 : a.dz1) + o, H, srows);
+    stage_out<H, kFwd2Samples>(smem, a.dz1 + ((int64_t)g * a.B + s0) * H, H, srows);
 }
 
 // --------------------------------------------------------------- fwd2
 // All H features of 128 samples: z2 = W2 h1 + b2 and the loss epilogue.
 // Wave w owns features (H / 4) w .. + H / 4 - 1 (MT row tiles of 16).
-template <int H>
+// With BWD, the same workgroup then forms dh1 = W2^T dz2 for its samples from
+// the dz2 tile still staged in LDS, and dz1 = dh1 relu'(z1) with the block's
+// db1 sums, so dz2 is never read back from memory for it.
+template <int H, bool BWD>
 __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
     extern __shared__ __align__(16) uint16_t smem[];
     constexpr int MT = H / 64, NST = 3, STG = (H + kFwd2Samples) * kBK;
@@ -673,15 +729,18 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
             }
         }
     }
+    bf16x8 fa0[MT];
+    if constexpr (BWD) w2t_frags<H, MT>(w2t_lane<H, MT>(a, g, wv, l16, q), 0, fa0);
     __syncthreads();
     stage_out<H, kFwd2Samples>(smem, a.dz2 + ((int64_t)g * B + s0) * H, H, srows);
+    if constexpr (BWD) backward_h1<H, MT>(a, smem, acc, fa0, g, blk, s0, srows, wv, l, l16, q);
 }
 
 // --------------------------------------------------------------- wgrad
 // Per (chunk, job): job < n2 -> a 256 x 256 tile of dW2 = dz2^T h1; else a
-// tile of dW1 = dz1^T s.  After its tile, job j of a chunk also adds the
-// block sums of the chunk (db2, dw3, db3 from fwd2, db1 from bwd1) for its
-// share of the entries, so that no workgroup exists for that small sum alone.
+// tile of dW1 = dz1^T s.  Job j of a chunk also adds the chunk's block sums
+// (db2, dw3, db3, db1, all from fwd2) for its share of the entries, so that
+// no workgroup exists for that small sum alone.
 __global__ __launch_bounds__(kThreads) void big_wgrad_kernel(BigArgs a) {
     extern __shared__ __align__(16) uint16_t smem[];
     constexpr int NST = kWgradStages, STG = 2 * kBK * kTile;
@@ -725,8 +784,8 @@ __global__ __launch_bounds__(kThreads) void big_wgrad_kernel(BigArgs a) {
         for (int j = 0; j < 8; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
     const int nsl = (len + kBK - 1) / kBK;
 
-    // this job's share of the chunk's block sums (db2, dw3, db3 from fwd2,
-    // db1 from bwd1), in block order, while the first stages are in flight
+    // this job's share of the chunk's block sums, in block order, while the
+    // first stages are in flight
     auto pre = [&] {
         const int ne = spart_w(H), per = (ne + njob - 1) / njob;
         const int k0 = b0 / kFwd2Samples, k1 = (b0 + len + kFwd2Samples - 1) / kFwd2Samples;
@@ -865,22 +924,26 @@ static hipError_t big_launch(const IqlDims& d, const IqlBuffers& b, const float*
 
     static bool attr = false;
     if (!attr) {
-        hipError_t e = allow_lds(big_tile_kernel<0>, ring_lds_bytes(kTileStages));
-        if (e == hipSuccess) e = allow_lds(big_tile_kernel<1>, ring_lds_bytes(kTileStages));
+        hipError_t e = allow_lds(big_fwd1_kernel, ring_lds_bytes(kTileStages));
         if (e == hipSuccess) e = allow_lds(big_wgrad_kernel, ring_lds_bytes(kWgradStages));
-        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<256>, fwd2_lds_bytes<256>());
-        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<512>, fwd2_lds_bytes<512>());
+        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<256, false>, fwd2_lds_bytes<256>());
+        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<512, false>, fwd2_lds_bytes<512>());
+        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<256, true>, fwd2_lds_bytes<256>());
+        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<512, true>, fwd2_lds_bytes<512>());
         if (e != hipSuccess) return e;
         attr = true;
     }
     const int nst = (B + kTile - 1) / kTile;
     const dim3 gt(nst * (H / kTile), G);
-    hipLaunchKernelGGL(big_tile_kernel<0>, gt, dim3(kThreads), ring_lds_bytes(kTileStages), stream, a);
+    hipLaunchKernelGGL(big_fwd1_kernel, gt, dim3(kThreads), ring_lds_bytes(kTileStages), stream, a);
     const dim3 g2(a.nblk, G);
-    if (H == 512) hipLaunchKernelGGL(big_fwd2_kernel<512>, g2, dim3(kThreads), fwd2_lds_bytes<512>(), stream, a);
-    else hipLaunchKernelGGL(big_fwd2_kernel<256>, g2, dim3(kThreads), fwd2_lds_bytes<256>(), stream, a);
-    if (vo) return hipGetLastError();
-    hipLaunchKernelGGL(big_tile_kernel<1>, gt, dim3(kThreads), ring_lds_bytes(kTileStages), stream, a);
+    if (vo) {
+        if (H == 512) hipLaunchKernelGGL((big_fwd2_kernel<512, false>), g2, dim3(kThreads), fwd2_lds_bytes<512>(), stream, a);
+        else hipLaunchKernelGGL((big_fwd2_kernel<256, false>), g2, dim3(kThreads), fwd2_lds_bytes<256>(), stream, a);
+        return hipGetLastError();
+    }
+    if (H == 512) hipLaunchKernelGGL((big_fwd2_kernel<512, true>), g2, dim3(kThreads), fwd2_lds_bytes<512>(), stream, a);
+    else hipLaunchKernelGGL((big_fwd2_kernel<256, true>), g2, dim3(kThreads), fwd2_lds_bytes<256>(), stream, a);
     const dim3 gw(a.nchunk * big_tiles(S, H), G);
     hipLaunchKernelGGL(big_wgrad_kernel, gw, dim3(kThreads), ring_lds_bytes(kWgradStages), stream, a);
     return hipGetLastError();
