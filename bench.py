@@ -295,7 +295,7 @@ class Context:
 
 
 LAUNCH_KERNELS = (("relabel_norms", ("step_her_norms_kernel", "her_relabel_kernel")),
-                  ("fwd_bwd", ("iql_fused16w_kernel", "iql_fused_kernel", "big_tile_kernel", "big_fwd2_kernel",
+                  ("fwd_bwd", ("iql_fused16w_kernel", "iql_fused_kernel", "big_fwd1_kernel", "big_fwd2_kernel",
                                "big_wgrad_kernel", "layer_gemm_kernel", "iql_rows_kernel", "iql_wgrad_kernel",
                                "aw_policy_kernel", "aw_policy_vec_kernel")),
                   ("reduce_saxpy", ("step_reduce_saxpy_kernel",)),
