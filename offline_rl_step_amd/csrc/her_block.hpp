@@ -179,11 +179,13 @@ IQLH_DEV void her_block(const HerArgs& a, int64_t blk) {
     const bool lead = tid < nrows;
     const int64_t i = row0 + tid;
     const int64_t src = lead ? (int64_t)a.source_idx[i] : -1;
-    // (2) the sources of this thread's row quads (indexes clamped: no branch
-    // around a load, unused values replaced afterwards)
+    // (2) the sources of this thread's row quads (indexes clamped: no
+    // lane-dependent branch around a load, unused values replaced afterwards;
+    // slots beyond the block's quads, as at S = 128, are skipped uniformly)
     int64_t srck[kHerItems];
 #pragma unroll
-    for (int k = 0; k < kHerItems; ++k) srck[k] = a.source_idx[row0 + min(tid + 256 * k, items - 1) / C4];
+    for (int k = 0; k < kHerItems; ++k)
+        srck[k] = 256 * k < items ? a.source_idx[row0 + min(tid + 256 * k, items - 1) / C4] : 0;
     // (3) the draw, while those are in flight
     const uint64_t r = lead ? her_draw(a, i, her_step_word(a)) : 0ull;
     // (4) the lead row's episode probe, action and done
@@ -196,6 +198,11 @@ IQLH_DEV void her_block(const HerArgs& a, int64_t blk) {
     float vs[kHerItems][4], vn[kHerItems][4];
 #pragma unroll
     for (int k = 0; k < kHerItems; ++k) {
+        if (256 * k >= items) {  // uniform: a slot no quad of this block fills
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vs[k][e] = vn[k][e] = 0.f;
+            continue;
+        }
         const int w = tid + 256 * k;
         const int wc = min(w, items - 1);
         const int rr = wc / C4, c = (wc - rr * C4) * 4;

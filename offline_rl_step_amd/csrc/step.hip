@@ -148,7 +148,7 @@ hipError_t launch_aux_step(const IqlDims& d, const IqlBuffers& b, const AdamHype
     if (bud) np = NormsArgs{bud->s, bud->n, partials, vec, nb};
 
     // A: HER + budget norms (what launch B does not host)
-    const int her_blocks = (her && her->n > 0 && !her_in_b) ? (her->n + 31) / 32 : 0;
+    const int her_blocks = (her && her->n > 0 && !her_in_b) ? (her->n + kHerRows - 1) / kHerRows : 0;
     const int nb_a = norms_in_b ? 0 : nb;
     if (her_blocks + nb_a > 0) {
         HerArgs ha{};
