@@ -507,6 +507,177 @@ __global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
     }
 }
 
+// ------------------------------------------- fp32, four waves per 32 samples
+// The same step for fp32 operands at hidden 128 (e.g. batch 4096, state 42).
+// The fp32 weights fill ~140 KB of LDS, so one workgroup fits a CU; with one
+// wave per 32 samples (the kernel above) three of the CU's four SIMDs would
+// idle.  Here four waves share one 32-sample tile and split its features:
+// wave w owns row tile w (32 features) of every layer, its MFMAs read the
+// other waves' activations from the tiles in LDS (natural k order), and V
+// adds the four waves' partial dot products in a fixed order.  The weight
+// gradients split their output tiles over the waves as above.
+template <int SP, int H, bool XVEC>
+__global__ __launch_bounds__(256) void iql_fused_fs_kernel(FusedArgs a) {
+    typedef Op<float> O;
+    typedef FusedCfg<float, SP, H, 1> C;  // the 32-sample tile layout
+    constexpr int NW = 4, BT = 32, NT = H / 32, KU1 = SP / O::KS, KUH = H / O::KS, NTHR = 64 * NW;
+    static_assert(NT == NW, "one row tile per wave");
+    extern __shared__ __align__(16) unsigned char smem[];
+    float* R0 = (float*)smem;  // W1, then dz2^T
+    float* R1 = R0 + C::R0;    // W2, then W2^T
+    float* R2 = R1 + C::R1;    // h2 dv, then dz1^T
+    float* R3 = R2 + C::R2;    // h1^T, then s^T
+    float* sb1 = R3 + C::R3;
+    float* sb2 = sb1 + H;
+    float* sw3 = sb2 + H;
+    float* sred = sw3 + H;     // [2]: the tile's loss and dv sums
+    float* svp = sred + 2;     // [NW][BT]: each wave's part of V
+
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index = row tile, uniform
+    const int g = blockIdx.y, wg = blockIdx.x;
+    const int S = a.S, B = a.B;
+    const POff po(S, H);
+    const float* prm = a.params + (int64_t)g * a.P;
+    const float* w1s = (const float*)a.w1s + (int64_t)g * H * SP;
+    const float* w2s = (const float*)a.w2s + (int64_t)g * H * H;
+    const float* w2ts = (const float*)a.w2ts + (int64_t)g * H * H;
+    float* part = a.part + ((int64_t)g * a.nwg + wg) * a.Pp;
+    const float tau = g == 0 ? a.tau0 : a.tau1;
+
+    // ---- S0: weights, biases and w3 to LDS; every wave holds the tile's s
+    // fragments (lane half h: the odd or even k of each step)
+    // (rows of SP and H floats and LDS strides of LDW1, LDW2: whole float4s)
+    static_assert(C::LDW1 % 4 == 0 && C::LDW2 % 4 == 0 && SP % 4 == 0, "float4 rows");
+    for (int idx = 4 * tid; idx < H * SP; idx += 4 * NTHR) {
+        const int r = idx / SP, c = idx - r * SP;
+        *(float4*)(R0 + r * C::LDW1 + c) = *(const float4*)(w1s + idx);
+    }
+    for (int idx = 4 * tid; idx < H * H; idx += 4 * NTHR) {
+        const int r = idx / H, c = idx - r * H;
+        *(float4*)(R1 + r * C::LDW2 + c) = *(const float4*)(w2s + idx);
+    }
+    for (int i = tid; i < H; i += NTHR) {
+        sb1[i] = prm[po.b1 + i];
+        sb2[i] = prm[po.b2 + i];
+        sw3[i] = prm[po.w3 + i];
+    }
+    const int bl = l32, b = wg * BT + bl;
+    const bool valid = b < B;
+    float xf[KU1];
+    {
+        const float* xr = (const float*)a.states + (int64_t)b * a.ld;
+#pragma unroll
+        for (int u = 0; u < KU1; ++u) {
+            const int k = O::KS * u + h;
+            xf[u] = (valid && (XVEC || k < S)) ? xr[k] : 0.f;
+        }
+    }
+    lds_barrier();
+
+    // ---- F1: row tile wv of z1^T = W1 s^T; h1 = relu(z1 + b1) to h1^T (R3)
+    const float* w1r = R0 + (32 * wv + l32) * C::LDW1 + h;
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int u = 0; u < KU1; ++u) acc = O::mma(w1r[O::KS * u], xf[u], acc);
+    // lane (l32, h) holds features 32 wv + 8 (r >> 2) + 4 h + (r & 3) of sample l32
+    uint32_t mask1 = 0u;  // relu'(z1), one bit per accumulator register
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int f = 32 * wv + 8 * (r >> 2) + 4 * h + (r & 3);
+        const float z = acc[r] + sb1[f];
+        const float y = z > 0.f ? z : 0.f;
+        mask1 |= (z > 0.f ? 1u : 0u) << r;
+        R3[f * C::LDA + bl] = y;
+    }
+    lds_barrier();
+
+    // ---- F2: row tile wv of z2^T = W2 h1^T (h1^T from R3, every feature)
+    const float* w2r = R1 + (32 * wv + l32) * C::LDW2 + h;
+    acc = f32x16{};
+#pragma unroll
+    for (int u = 0; u < KUH; ++u) acc = O::mma(w2r[O::KS * u], R3[(O::KS * u + h) * C::LDA + l32], acc);
+    float vpart = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int f = 32 * wv + 8 * (r >> 2) + 4 * h + (r & 3);
+        const float z = acc[r] + sb2[f];
+        acc[r] = z;
+        vpart = fmaf(sw3[f], z > 0.f ? z : 0.f, vpart);
+    }
+    vpart += __shfl_xor(vpart, 32, 64);
+    if (h == 0) svp[wv * BT + l32] = vpart;
+    lds_barrier();
+    const float v = ((svp[l32] + svp[BT + l32]) + (svp[2 * BT + l32] + svp[3 * BT + l32])) + prm[po.b3];
+    if (a.fwd_only) {
+        if (valid && h == 0 && wv == 0) write_value(a.vo, g, B, b, v);
+        return;
+    }
+    float dv = 0.f, lterm = 0.f;
+    if (valid) {
+        const float diff = a.q[b] - v;
+        const float w = diff >= 0.f ? tau : 1.f - tau;
+        lterm = w * diff * diff;
+        dv = -2.f * w * diff * a.invB;
+        if (h == 0 && wv == 0 && a.out_v) a.out_v[(int64_t)g * B + b] = v;
+    }
+    if (wv == 0) {
+        const float ls = wave_sum(h == 0 ? lterm : 0.f);
+        const float ds = wave_sum(h == 0 ? dv : 0.f);
+        if (lane == 0) { sred[0] = ls; sred[1] = ds; }
+    }
+    // dz2 = dv w3 relu'(z2) to dz2^T (R0: W1 is no longer read), h2 dv to R2
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int f = 32 * wv + 8 * (r >> 2) + 4 * h + (r & 3);
+        const float z = acc[r];
+        R0[f * C::LDA + bl] = z > 0.f ? dv * sw3[f] : 0.f;
+        R2[f * C::LDA + bl] = z > 0.f ? z * dv : 0.f;
+    }
+    lds_barrier();
+
+    // ---- dw3 (row sums of h2 dv), db3, loss, then dW2 = dz2^T h1 with db2
+    lds_rowsum<float, BT>(R2, C::LDA, wv, wv + 1, part + po.w3);
+    if (tid == 0) {
+        a.loss_part[(int64_t)g * a.nwg + wg] = sred[0];
+        part[po.b3] = sred[1];
+    }
+    // W2^T shadow into R1 (W2 is no longer read after F2)
+    for (int idx = 4 * tid; idx < H * H; idx += 4 * NTHR) {
+        const int r = idx / H, c = idx - r * H;
+        *(float4*)(R1 + r * C::LDW2 + c) = *(const float4*)(w2ts + idx);
+    }
+    {
+        constexpr int T2 = NT * NT;
+        lds_gemm_store<float, BT, 4>(R0, R3, C::LDA, NT, wv * T2 / NW, (wv + 1) * T2 / NW, part + po.w2, H, H,
+                                     part + po.b2);
+    }
+    lds_barrier();
+
+    // ---- s^T to R3 (h1^T no longer read; each wave writes a quarter of the
+    // k steps); B1: row tile wv of dh1^T = W2^T dz2^T; dz1 = dh1 relu'(z1)
+    for (int u = wv * KU1 / NW; u < (wv + 1) * KU1 / NW; ++u) R3[(O::KS * u + h) * C::LDA + bl] = xf[u];
+    const float* w2tr = R1 + (32 * wv + l32) * C::LDW2 + h;
+    acc = f32x16{};
+#pragma unroll
+    for (int u = 0; u < KUH; ++u) acc = O::mma(w2tr[O::KS * u], R0[(O::KS * u + h) * C::LDA + l32], acc);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int f = 32 * wv + 8 * (r >> 2) + 4 * h + (r & 3);
+        R2[f * C::LDA + bl] = (mask1 >> r) & 1u ? acc[r] : 0.f;
+    }
+    lds_barrier();
+
+    // ---- dW1 = dz1^T s with db1
+    {
+        constexpr int NCT = SP / 32;
+        constexpr int T3 = NT * NCT;
+        lds_gemm_store<float, BT, 4>(R2, R3, C::LDA, NCT, wv * T3 / NW, (wv + 1) * T3 / NW, part + po.w1, S, S,
+                                     part + po.b1);
+    }
+}
+constexpr size_t fs_lds_bytes(size_t table_bytes, int H) { return table_bytes + (size_t)(3 * H + 2 + 4 * 32) * 4; }
+
 // Blocks 0 .. rb - 1 of each group reduce; block rb updates its counters.
 __global__ __launch_bounds__(256) void iql_reduce_kernel(const float* __restrict__ part,
                                                          const float* __restrict__ loss_part, int nwg, int nloss,
@@ -1284,6 +1455,32 @@ static hipError_t run_fused(const FusedArgs& fa, int G, hipStream_t stream, hipE
                 : run_fused_x<T, SP, H, NW, false>(fa, G, stream, ev0, ev1);
 }
 
+template <int SP, int H, bool XVEC>
+static hipError_t run_fused_fs_x(const FusedArgs& fa, int G, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    typedef FusedCfg<float, SP, H, 1> C;
+    const size_t bytes = fs_lds_bytes(C::BYTES_T, H);
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)iql_fused_fs_kernel<SP, H, XVEC>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    if (ev0)
+        hipExtLaunchKernelGGL((iql_fused_fs_kernel<SP, H, XVEC>), dim3(fa.nwg, G), dim3(256), bytes, stream, ev0, ev1,
+                              0, fa);
+    else
+        hipLaunchKernelGGL((iql_fused_fs_kernel<SP, H, XVEC>), dim3(fa.nwg, G), dim3(256), bytes, stream, fa);
+    return hipGetLastError();
+}
+
+template <int SP, int H>
+static hipError_t run_fused_fs(const FusedArgs& fa, int G, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    const bool xvec = fa.S == SP;
+    return xvec ? run_fused_fs_x<SP, H, true>(fa, G, stream, ev0, ev1)
+                : run_fused_fs_x<SP, H, false>(fa, G, stream, ev0, ev1);
+}
+
 struct Variant {
     int dtype, SP, H, NW;
     hipError_t (*fn)(const FusedArgs&, int, hipStream_t, hipEvent_t, hipEvent_t);
@@ -1294,7 +1491,8 @@ static const Variant kVariants[] = {
     {1, 64, 128, 4, &run_fused16w<64, 128>},
     {1, 32, 32, 4, &run_fused<uint16_t, 32, 32, 4>},
     {0, 32, 32, 4, &run_fused<float, 32, 32, 4>},
-    {0, 64, 128, 1, &run_fused<float, 64, 128, 1>},
+    // fp32, hidden 128: four waves share each 32-sample workgroup
+    {0, 64, 128, 1, &run_fused_fs<64, 128>},
 };
 
 static const Variant* pick(int dtype, int S, int H) {
