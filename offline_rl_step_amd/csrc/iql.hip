@@ -508,25 +508,80 @@ __global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
 }
 
 // ------------------------------------------- fp32, four waves per 32 samples
+// dst[32 rt + i] = the sum of the 32 columns of row 32 rt + i of an LDS tile
+// (row stride LDA floats, rows 16-byte aligned): lanes 2i and 2i + 1 each add
+// 16 columns from four 16-byte reads, then each other's sums.
+template <int LDA>
+IQLH_DEV void fs_rowsum(const float* T, int rt, float* dst) {
+    static_assert(LDA % 4 == 0, "16-byte rows");
+    const int lane = threadIdx.x & 63, i = lane >> 1, half = lane & 1;
+    const float4* p = (const float4*)(T + (32 * rt + i) * LDA + 16 * half);
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float4 x = p[k];
+        sum += (x.x + x.y) + (x.z + x.w);
+    }
+    sum += __shfl_xor(sum, 1, 64);
+    if (half == 0) dst[32 * rt + i] = sum;
+}
+
+// Output tiles (rt, 0 .. NCT - 1) of out[i][j] = sum_k A[i][k] Bm[j][k] over
+// the K = 32 columns of two LDS tiles (row stride LDA), unrolled over k;
+// fp32 results to dst[i * ldo + j] for j < ncols.
+template <int NCT, int LDA>
+IQLH_DEV void fs_wgrad(const float* A, const float* Bm, int rt, float* dst, int ldo, int ncols) {
+    typedef Op<float> O;
+    const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
+    f32x16 acc[NCT];
+#pragma unroll
+    for (int q = 0; q < NCT; ++q) acc[q] = f32x16{};
+    const float* ar = A + (32 * rt + l32) * LDA + h;
+    const float* br = Bm + l32 * LDA + h;
+#pragma unroll
+    for (int u = 0; u < 32 / O::KS; ++u) {
+        const float av = ar[O::KS * u];
+#pragma unroll
+        for (int q = 0; q < NCT; ++q) acc[q] = O::mma(av, br[32 * q * LDA + O::KS * u], acc[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < NCT; ++q) {
+        const int j = 32 * q + l32;
+        if (j < ncols) {
+            float* d0 = dst + (32 * rt + 4 * h) * ldo + j;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) d0[(8 * (r >> 2) + (r & 3)) * ldo] = acc[q][r];
+        }
+    }
+}
+
 // The same step for fp32 operands at hidden 128 (e.g. batch 4096, state 42).
 // The fp32 weights fill ~140 KB of LDS, so one workgroup fits a CU; with one
 // wave per 32 samples (the kernel above) three of the CU's four SIMDs would
 // idle.  Here four waves share one 32-sample tile and split its features:
 // wave w owns row tile w (32 features) of every layer, its MFMAs read the
 // other waves' activations from the tiles in LDS (natural k order), and V
-// adds the four waves' partial dot products in a fixed order.  The weight
-// gradients split their output tiles over the waves as above.
+// adds the four waves' partial dot products in a fixed order.  The backward
+// product dh1^T = W2^T dz2^T reads W2 from LDS by columns (lane l32 takes
+// column 32 w + l32 of row k: consecutive addresses), so no transposed copy
+// of W2 is staged.  The weight gradients of row tile w need only wave w's
+// rows of dz2 and dz1 (and every wave's h1 or s), and the bias and w3
+// gradients are row sums of those rows, so after the exchange of dz2 no
+// further barrier is needed.
 template <int SP, int H, bool XVEC>
 __global__ __launch_bounds__(256) void iql_fused_fs_kernel(FusedArgs a) {
     typedef Op<float> O;
     typedef FusedCfg<float, SP, H, 1> C;  // the 32-sample tile layout
     constexpr int NW = 4, BT = 32, NT = H / 32, KU1 = SP / O::KS, KUH = H / O::KS, NTHR = 64 * NW;
+    constexpr int LDA = C::LDA;
     static_assert(NT == NW, "one row tile per wave");
     extern __shared__ __align__(16) unsigned char smem[];
-    float* R0 = (float*)smem;  // W1, then dz2^T
-    float* R1 = R0 + C::R0;    // W2, then W2^T
-    float* R2 = R1 + C::R1;    // h2 dv, then dz1^T
-    float* R3 = R2 + C::R2;    // h1^T, then s^T
+    float* R0 = (float*)smem;  // W1, then dz2^T [H][LDA] and s^T [SP][LDA] behind it
+    float* R1 = R0 + C::R0;    // W2
+    float* R2 = R1 + C::R1;    // h2 dv, then dz1^T (each wave its own row tile)
+    float* R3 = R2 + C::R2;    // h1^T
+    float* Rs = R0 + H * LDA;
+    static_assert(H * LDA + SP * LDA <= C::R0, "s^T behind dz2^T");
     float* sb1 = R3 + C::R3;
     float* sb2 = sb1 + H;
     float* sw3 = sb2 + H;
@@ -541,27 +596,20 @@ __global__ __launch_bounds__(256) void iql_fused_fs_kernel(FusedArgs a) {
     const float* prm = a.params + (int64_t)g * a.P;
     const float* w1s = (const float*)a.w1s + (int64_t)g * H * SP;
     const float* w2s = (const float*)a.w2s + (int64_t)g * H * H;
-    const float* w2ts = (const float*)a.w2ts + (int64_t)g * H * H;
     float* part = a.part + ((int64_t)g * a.nwg + wg) * a.Pp;
     const float tau = g == 0 ? a.tau0 : a.tau1;
 
-    // ---- S0: weights, biases and w3 to LDS; every wave holds the tile's s
-    // fragments (lane half h: the odd or even k of each step)
+    // ---- S0: loads in the order of use: W1 and the tile's s (F1; lane half
+    // h holds the odd or even k of each step), q, b3, the biases and w3,
+    // then W2, which goes to LDS after F1's products
     // (rows of SP and H floats and LDS strides of LDW1, LDW2: whole float4s)
     static_assert(C::LDW1 % 4 == 0 && C::LDW2 % 4 == 0 && SP % 4 == 0, "float4 rows");
-    for (int idx = 4 * tid; idx < H * SP; idx += 4 * NTHR) {
-        const int r = idx / SP, c = idx - r * SP;
-        *(float4*)(R0 + r * C::LDW1 + c) = *(const float4*)(w1s + idx);
-    }
-    for (int idx = 4 * tid; idx < H * H; idx += 4 * NTHR) {
-        const int r = idx / H, c = idx - r * H;
-        *(float4*)(R1 + r * C::LDW2 + c) = *(const float4*)(w2s + idx);
-    }
-    for (int i = tid; i < H; i += NTHR) {
-        sb1[i] = prm[po.b1 + i];
-        sb2[i] = prm[po.b2 + i];
-        sw3[i] = prm[po.w3 + i];
-    }
+    static_assert((H * SP) % (4 * NTHR) == 0 && (H * H) % (4 * NTHR) == 0 && H <= NTHR, "whole passes");
+    constexpr int N1 = H * SP / (4 * NTHR), N2 = H * H / (4 * NTHR);
+    typedef float f4 __attribute__((ext_vector_type(4)));  // (a union-free vector: kept in registers)
+    f4 w1v[N1], w2v[N2];
+#pragma unroll
+    for (int i = 0; i < N1; ++i) w1v[i] = *(const f4*)(w1s + 4 * (tid + i * NTHR));
     const int bl = l32, b = wg * BT + bl;
     const bool valid = b < B;
     float xf[KU1];
@@ -573,6 +621,26 @@ __global__ __launch_bounds__(256) void iql_fused_fs_kernel(FusedArgs a) {
             xf[u] = (valid && (XVEC || k < S)) ? xr[k] : 0.f;
         }
     }
+    const float qb = (valid && !a.fwd_only) ? a.q[b] : 0.f;  // q is null in the forward-only pass
+    const float b3 = prm[po.b3];
+    float pb1 = 0.f, pb2 = 0.f, pw3 = 0.f;
+    if (tid < H) {
+        pb1 = prm[po.b1 + tid];
+        pb2 = prm[po.b2 + tid];
+        pw3 = prm[po.w3 + tid];
+    }
+#pragma unroll
+    for (int i = 0; i < N2; ++i) w2v[i] = *(const f4*)(w2s + 4 * (tid + i * NTHR));
+#pragma unroll
+    for (int i = 0; i < N1; ++i) {
+        const int idx = 4 * (tid + i * NTHR), r = idx / SP, c = idx - r * SP;
+        *(f4*)(R0 + r * C::LDW1 + c) = w1v[i];
+    }
+    if (tid < H) {
+        sb1[tid] = pb1;
+        sb2[tid] = pb2;
+        sw3[tid] = pw3;
+    }
     lds_barrier();
 
     // ---- F1: row tile wv of z1^T = W1 s^T; h1 = relu(z1 + b1) to h1^T (R3)
@@ -580,6 +648,12 @@ __global__ __launch_bounds__(256) void iql_fused_fs_kernel(FusedArgs a) {
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int u = 0; u < KU1; ++u) acc = O::mma(w1r[O::KS * u], xf[u], acc);
+    // W2 to R1 (first read by F2, after the next barrier)
+#pragma unroll
+    for (int i = 0; i < N2; ++i) {
+        const int idx = 4 * (tid + i * NTHR), r = idx / H, c = idx - r * H;
+        *(f4*)(R1 + r * C::LDW2 + c) = w2v[i];
+    }
     // lane (l32, h) holds features 32 wv + 8 (r >> 2) + 4 h + (r & 3) of sample l32
     uint32_t mask1 = 0u;  // relu'(z1), one bit per accumulator register
 #pragma unroll
@@ -588,7 +662,7 @@ __global__ __launch_bounds__(256) void iql_fused_fs_kernel(FusedArgs a) {
         const float z = acc[r] + sb1[f];
         const float y = z > 0.f ? z : 0.f;
         mask1 |= (z > 0.f ? 1u : 0u) << r;
-        R3[f * C::LDA + bl] = y;
+        R3[f * LDA + bl] = y;
     }
     lds_barrier();
 
@@ -596,7 +670,7 @@ __global__ __launch_bounds__(256) void iql_fused_fs_kernel(FusedArgs a) {
     const float* w2r = R1 + (32 * wv + l32) * C::LDW2 + h;
     acc = f32x16{};
 #pragma unroll
-    for (int u = 0; u < KUH; ++u) acc = O::mma(w2r[O::KS * u], R3[(O::KS * u + h) * C::LDA + l32], acc);
+    for (int u = 0; u < KUH; ++u) acc = O::mma(w2r[O::KS * u], R3[(O::KS * u + h) * LDA + l32], acc);
     float vpart = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -608,14 +682,14 @@ __global__ __launch_bounds__(256) void iql_fused_fs_kernel(FusedArgs a) {
     vpart += __shfl_xor(vpart, 32, 64);
     if (h == 0) svp[wv * BT + l32] = vpart;
     lds_barrier();
-    const float v = ((svp[l32] + svp[BT + l32]) + (svp[2 * BT + l32] + svp[3 * BT + l32])) + prm[po.b3];
+    const float v = ((svp[l32] + svp[BT + l32]) + (svp[2 * BT + l32] + svp[3 * BT + l32])) + b3;
     if (a.fwd_only) {
         if (valid && h == 0 && wv == 0) write_value(a.vo, g, B, b, v);
         return;
     }
     float dv = 0.f, lterm = 0.f;
     if (valid) {
-        const float diff = a.q[b] - v;
+        const float diff = qb - v;
         const float w = diff >= 0.f ? tau : 1.f - tau;
         lterm = w * diff * diff;
         dv = -2.f * w * diff * a.invB;
@@ -626,55 +700,45 @@ __global__ __launch_bounds__(256) void iql_fused_fs_kernel(FusedArgs a) {
         const float ds = wave_sum(h == 0 ? dv : 0.f);
         if (lane == 0) { sred[0] = ls; sred[1] = ds; }
     }
-    // dz2 = dv w3 relu'(z2) to dz2^T (R0: W1 is no longer read), h2 dv to R2
+    // dz2 = dv w3 relu'(z2) to dz2^T (R0: W1 is no longer read), h2 dv to
+    // R2, s^T behind dz2^T (each wave a quarter of the k steps)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int f = 32 * wv + 8 * (r >> 2) + 4 * h + (r & 3);
         const float z = acc[r];
-        R0[f * C::LDA + bl] = z > 0.f ? dv * sw3[f] : 0.f;
-        R2[f * C::LDA + bl] = z > 0.f ? z * dv : 0.f;
+        R0[f * LDA + bl] = z > 0.f ? dv * sw3[f] : 0.f;
+        R2[f * LDA + bl] = z > 0.f ? z * dv : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < KU1 / NW; ++u) {
+        const int uu = wv * (KU1 / NW) + u;
+        Rs[(O::KS * uu + h) * LDA + bl] = xf[uu];
     }
     lds_barrier();
 
-    // ---- dw3 (row sums of h2 dv), db3, loss, then dW2 = dz2^T h1 with db2
-    lds_rowsum<float, BT>(R2, C::LDA, wv, wv + 1, part + po.w3);
+    // ---- from here each wave reads its own rows of R0 and R2 and every row
+    // of R1, R3 and s^T: dw3 and db2 (row sums), db3 and the loss
+    fs_rowsum<LDA>(R2, wv, part + po.w3);
+    fs_rowsum<LDA>(R0, wv, part + po.b2);
     if (tid == 0) {
         a.loss_part[(int64_t)g * a.nwg + wg] = sred[0];
         part[po.b3] = sred[1];
     }
-    // W2^T shadow into R1 (W2 is no longer read after F2)
-    for (int idx = 4 * tid; idx < H * H; idx += 4 * NTHR) {
-        const int r = idx / H, c = idx - r * H;
-        *(float4*)(R1 + r * C::LDW2 + c) = *(const float4*)(w2ts + idx);
-    }
-    {
-        constexpr int T2 = NT * NT;
-        lds_gemm_store<float, BT, 4>(R0, R3, C::LDA, NT, wv * T2 / NW, (wv + 1) * T2 / NW, part + po.w2, H, H,
-                                     part + po.b2);
-    }
-    lds_barrier();
-
-    // ---- s^T to R3 (h1^T no longer read; each wave writes a quarter of the
-    // k steps); B1: row tile wv of dh1^T = W2^T dz2^T; dz1 = dh1 relu'(z1)
-    for (int u = wv * KU1 / NW; u < (wv + 1) * KU1 / NW; ++u) R3[(O::KS * u + h) * C::LDA + bl] = xf[u];
-    const float* w2tr = R1 + (32 * wv + l32) * C::LDW2 + h;
+    // B1: row tile wv of dh1^T = W2^T dz2^T (A: column 32 wv + l32 of W2);
+    // dz1 = dh1 relu'(z1) over this wave's rows of R2 (read above)
     acc = f32x16{};
 #pragma unroll
-    for (int u = 0; u < KUH; ++u) acc = O::mma(w2tr[O::KS * u], R0[(O::KS * u + h) * C::LDA + l32], acc);
+    for (int u = 0; u < KUH; ++u)
+        acc = O::mma(R1[(O::KS * u + h) * C::LDW2 + 32 * wv + l32], R0[(O::KS * u + h) * LDA + l32], acc);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int f = 32 * wv + 8 * (r >> 2) + 4 * h + (r & 3);
-        R2[f * C::LDA + bl] = (mask1 >> r) & 1u ? acc[r] : 0.f;
+        R2[f * LDA + bl] = (mask1 >> r) & 1u ? acc[r] : 0.f;
     }
-    lds_barrier();
-
-    // ---- dW1 = dz1^T s with db1
-    {
-        constexpr int NCT = SP / 32;
-        constexpr int T3 = NT * NCT;
-        lds_gemm_store<float, BT, 4>(R2, R3, C::LDA, NCT, wv * T3 / NW, (wv + 1) * T3 / NW, part + po.w1, S, S,
-                                     part + po.b1);
-    }
+    // dW2 = dz2^T h1, db1 (row sums of dz1), dW1 = dz1^T s
+    fs_wgrad<NT, LDA>(R0, R3, wv, part + po.w2, H, H);
+    fs_rowsum<LDA>(R2, wv, part + po.b1);
+    fs_wgrad<SP / 32, LDA>(R2, Rs, wv, part + po.w1, S, S);
 }
 constexpr size_t fs_lds_bytes(size_t table_bytes, int H) { return table_bytes + (size_t)(3 * H + 2 + 4 * 32) * 4; }
 
