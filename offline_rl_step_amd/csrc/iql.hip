@@ -18,11 +18,13 @@
 // second kernel sums them in workgroup order (no float atomics: bitwise
 // reproducible) and a third applies the clip and Adam and refreshes the
 // operand-typed W1 / W2 / W2^T shadows the next step reads (no conversion or
-// transpose in the hot kernel).  Two kernels:
+// transpose in the hot kernel).  Three kernels:
 //   * iql_fused16w_kernel (bf16 operands, hidden 128): sixteen wave64s,
 //     v_mfma_f32_16x16x32_bf16, activations in natural [sample][feature]
 //     tiles read back with LDS transpose loads; described at its definition.
-//   * iql_fused_kernel (fp32 operands, small hidden widths): NW wave64s of 32
+//   * iql_fused_fs_kernel (fp32 operands, hidden 128): four wave64s share a
+//     32-sample tile and split its features; described at its definition.
+//   * iql_fused_kernel (hidden 32, fp32 or bf16 operands): NW wave64s of 32
 //     samples each on v_mfma_f32_32x32x16_bf16 / v_mfma_f32_32x32x2f32 in the
 //     orientation D[feature][sample] = W[feature][k] act[sample][k]; the
 //     accumulators of one layer are fed back, rounded to the operand type, as
