@@ -13,7 +13,8 @@
 // MI355X layout, three launches on a caller workspace; the prefix sums are
 // never stored whole:
 //   A  fp64 sums of every 256-row sub-block and of every 2048-row block (the
-//      block sum adds its eight sub-block sums in order);
+//      block sum adds its eight sub-block sums in order), and the draws'
+//      counter words, one per lane, parked in the index and weight outputs;
 //   D  each workgroup scans the block sums into a table of block ends in LDS
 //      (fixed order); one wave per draw: a 64-ary search of the table (each
 //      lane probes one position, a ballot picks the segment), then the
@@ -26,7 +27,8 @@
 //      a row on one side of it.  Each workgroup's smallest drawn priority
 //      (integer minimum on the bit pattern: order-independent) goes to a slot
 //      of its own;
-//   W  the weights, after every block folds the workgroup minima.
+//   W  the weights, from the drawn priorities the draws leave in the weight
+//      output, after every block folds the workgroup minima.
 // For more than 8192 blocks (2^24 rows) the table does not fit in LDS; a
 // one-workgroup launch T then writes it to the workspace and the draws search
 // it there.
@@ -39,7 +41,7 @@ constexpr uint64_t kPerKey1 = 0x5045526472617773ull;  // "PERdraws"
 constexpr int kPerBlock = 2048;                        // rows per block of the table
 constexpr int kPerSub = 256;                           // rows per sub-block (one wave scans one)
 constexpr int kPerSubs = kPerBlock / kPerSub;
-constexpr int kPerMaxWg = 1024;  // workgroups of the draw pass (each wave takes ceil(n / 4096) draws)
+constexpr int kPerMaxWg = 2048;  // workgroups of the draw pass (each wave takes ceil(n / 8192) draws)
 constexpr int kPerTable = 8192;  // block ends kept in LDS (64 KB): up to 2^24 rows
 
 struct PerArgs {
@@ -56,42 +58,72 @@ struct PerArgs {
     double* ssum;    // [nb][8] sub-block sums
     double* bend;    // [nb] inclusive prefix at each block end (only when nb > kPerTable)
     uint32_t* wgmin; // [nwg] smallest drawn priority (bit pattern) of each draw workgroup
-    int vec;         // priorities 16-byte aligned
+    int vec;         // priorities 16-byte aligned, a whole number of quads
     int nb, nwg, dpw;  // blocks; draw workgroups; draws per wave
 };
 
 IQLH_DEV bool bad_priority(float x) { return !(x >= 0.f) || !isfinite(x); }
 
-// One 2048-row block per workgroup: thread t holds row base + 256 k + t of
-// sub-block k; each sub-block sum is a fixed-order tree (wave sums, then the
-// four waves in order), and the block sum adds the eight in order.
+// One 2048-row block per workgroup: wave w sums sub-blocks w and w + 4, four
+// consecutive rows per lane (one 16-byte load when the priorities are
+// aligned whole quads), each lane's four in a fixed order and then the 64
+// lanes by a butterfly; the block sum adds the eight sub-block sums in order.
+// While the rows load, workgroup b evaluates the counter words of draws b,
+// b + nb, b + 2 nb, ... one per lane, and parks each in the draw's outputs
+// (low half in idx, high half in w), which the draw pass reads and
+// overwrites: lane-parallel, instead of every lane of a draw's wave
+// evaluating the same word.
 __global__ __launch_bounds__(256) void per_block_sums_kernel(PerArgs a) {
-    __shared__ double red[kPerSubs][4];
-    const int64_t base = (int64_t)blockIdx.x * kPerBlock + threadIdx.x;
-    double s[kPerSubs];
+    __shared__ double red[kPerSubs];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    float x[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t r0 = (int64_t)blockIdx.x * kPerBlock + (int64_t)(wv + 4 * h) * kPerSub + 4 * lane;
+        if (a.vec) {  // uniform: the rows past the end are whole quads
+            const float4 v = *(const float4*)(a.p + (r0 < a.size ? r0 : 0));
+            x[h][0] = v.x; x[h][1] = v.y; x[h][2] = v.z; x[h][3] = v.w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[h][e] = keep_if(r0 < a.size, x[h][e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t i = r0 + e;
+                x[h][e] = keep_if(i < a.size, a.p[i < a.size ? i : a.size - 1]);
+            }
+        }
+    }
+    if (a.n > 0) {
+        const uint64_t step = a.step ? (uint64_t)*a.step : 0ull;
+        for (int64_t k = (int64_t)threadIdx.x * a.nb + blockIdx.x; k < a.n; k += (int64_t)256 * a.nb) {
+            const uint64_t word = philox4x64_10(u64x4{(uint64_t)k, step, 0ull, 0ull}, a.seed, kPerKey1).x;
+            a.idx[k] = (int32_t)(uint32_t)word;
+            a.w[k] = __uint_as_float((uint32_t)(word >> 32));
+        }
+    }
+    double s[2];
     bool bad = false;
 #pragma unroll
-    for (int k = 0; k < kPerSubs; ++k) {
-        const int64_t i = base + kPerSub * k;
-        const float x = i < a.size ? a.p[i] : 0.f;
-        bad |= bad_priority(x);
-        s[k] = (double)x;
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bad |= bad_priority(x[h][e]);
+        s[h] = ((double)x[h][0] + (double)x[h][1]) + ((double)x[h][2] + (double)x[h][3]);
     }
 #pragma unroll
-    for (int k = 0; k < kPerSubs; ++k) {
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) s[k] += __shfl_xor(s[k], o, 64);
-        if ((threadIdx.x & 63) == 0) red[k][threadIdx.x >> 6] = s[k];
+    for (int o = 32; o > 0; o >>= 1) {
+        s[0] += __shfl_xor(s[0], o, 64);
+        s[1] += __shfl_xor(s[1], o, 64);
+    }
+    if (lane == 0) {
+        red[wv] = s[0];
+        red[wv + 4] = s[1];
     }
     if (__syncthreads_or(bad) && threadIdx.x == 0) set_flag(a.flags, 0x2);
-    if (threadIdx.x < kPerSubs) {
-        const int k = threadIdx.x;
-        a.ssum[(int64_t)blockIdx.x * kPerSubs + k] = (red[k][0] + red[k][1]) + (red[k][2] + red[k][3]);
-    }
+    if (threadIdx.x < kPerSubs) a.ssum[(int64_t)blockIdx.x * kPerSubs + threadIdx.x] = red[threadIdx.x];
     if (threadIdx.x == 0) {
         double t = 0.0;
 #pragma unroll
-        for (int k = 0; k < kPerSubs; ++k) t += (red[k][0] + red[k][1]) + (red[k][2] + red[k][3]);
+        for (int k = 0; k < kPerSubs; ++k) t += red[k];
         a.bsum[blockIdx.x] = t;
     }
 }
@@ -100,13 +132,23 @@ __global__ __launch_bounds__(256) void per_block_sums_kernel(PerArgs a) {
 // threads of one workgroup in a fixed order: thread t scans its run of
 // ceil(nb / 256) sums sequentially; the run totals are scanned across the
 // wave by shuffles and across the waves in order; each value is the run's
-// offset plus its running sum.
+// offset plus its running sum.  The first four sums of a run are loaded
+// together (adding the zeros past a short run changes no sum).
 IQLH_DEV void per_table_scan(const double* __restrict__ bsum, int nb, double* out) {
     __shared__ double wtot[4];
+    constexpr int PF = 4;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int run = (nb + 255) / 256, j0 = threadIdx.x * run, j1 = min(j0 + run, nb);
+    double pf[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+        const double x = bsum[min(j0 + i, nb - 1)];
+        pf[i] = j0 + i < j1 ? x : 0.0;
+    }
     double t = 0.0;
-    for (int j = j0; j < j1; ++j) t += bsum[j];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) t += pf[i];
+    for (int j = j0 + PF; j < j1; ++j) t += bsum[j];
     double incl = t;
 #pragma unroll
     for (int s = 1; s < 64; s <<= 1) {
@@ -119,7 +161,14 @@ IQLH_DEV void per_table_scan(const double* __restrict__ bsum, int nb, double* ou
     if (lane == 0) off = 0.0;
     for (int w = 0; w < wv; ++w) off += wtot[w];
     double r = 0.0;
-    for (int j = j0; j < j1; ++j) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+        if (j0 + i < j1) {
+            r += pf[i];
+            out[j0 + i] = off + r;
+        }
+    }
+    for (int j = j0 + PF; j < j1; ++j) {
         r += bsum[j];
         out[j] = off + r;
     }
@@ -138,9 +187,11 @@ IQLH_DEV int64_t search64(int64_t lo, int64_t hi, double u, Load&& at) {
         if (pos > hi - 1) pos = hi - 1;
         const uint64_t bal = __ballot(at(pos) > u);
         if (!bal) return -1;  // cannot happen while at(hi - 1) > u
+        // lane j's and lane j - 1's probe positions, recomputed (uniform)
+        // rather than fetched by shuffles
         const int j = __builtin_ctzll(bal);
-        const int64_t pj = __shfl(pos, j, 64);
-        const int64_t pprev = j > 0 ? __shfl(pos, j - 1, 64) : lo - 1;
+        const int64_t pj = min(lo + (int64_t)(j + 1) * stp - 1, hi - 1);
+        const int64_t pprev = j > 0 ? min(lo + (int64_t)j * stp - 1, hi - 1) : lo - 1;
         hi = pj + 1;
         lo = pprev + 1;
     }
@@ -229,23 +280,27 @@ IQLH_DEV int64_t per_find_row(const PerArgs& a, int64_t blk, double off, double 
 }
 
 // Draws of one wave (dpw per wave, four waves per workgroup).
-__global__ __launch_bounds__(256) void per_draw_kernel(PerArgs a) {
+__global__ __launch_bounds__(256, 8) void per_draw_kernel(PerArgs a) {
     extern __shared__ double tbl[];  // [nb] when the table fits in LDS
     const int lane = threadIdx.x & 63;
     const bool staged = a.nb <= kPerTable;
+    const int k0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * a.dpw;
+    // the draws' counter words, parked in their outputs by the block-sums pass
+    auto draw_word = [&](int k) {
+        return ((uint64_t)__float_as_uint(a.w[k]) << 32) | (uint64_t)(uint32_t)a.idx[k];
+    };
+    const uint64_t word0 = draw_word(min(k0, a.n - 1));
     if (staged) per_table_scan(a.bsum, a.nb, tbl);
     __syncthreads();
     const double* gtab = a.bend;
-    const uint64_t step = a.step ? (uint64_t)*a.step : 0ull;
     const double total = staged ? tbl[a.nb - 1] : gtab[a.nb - 1];
     const double cap = __longlong_as_double(__double_as_longlong(total) - 1);  // largest double below a positive total
     const bool ok = total > 0.0 && isfinite(total);
-    const int k0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * a.dpw;
     uint32_t wmin = 0xFFFFFFFFu;  // smallest drawn priority of this wave (bit pattern: p >= 0)
     for (int kk = 0; kk < a.dpw; ++kk) {
         const int k = k0 + kk;
         if (k >= a.n) break;  // wave-uniform
-        const uint64_t word = philox4x64_10(u64x4{(uint64_t)k, step, 0ull, 0ull}, a.seed, kPerKey1).x;
+        const uint64_t word = kk == 0 ? word0 : draw_word(k);
         double u = (double)(word >> 11) * 0x1.0p-53 * total;
         if (u > cap) u = cap;
         int64_t found = -1;
@@ -270,6 +325,7 @@ __global__ __launch_bounds__(256) void per_draw_kernel(PerArgs a) {
         }
         if (lane == 0) {
             a.idx[k] = (int32_t)found;
+            a.w[k] = found >= 0 ? pf : 0.f;  // the drawn priority, turned into the weight by W
             if (found >= 0) wmin = min(wmin, __float_as_uint(pf));
             else set_flag(a.flags, 0x2);
         }
@@ -282,8 +338,14 @@ __global__ __launch_bounds__(256) void per_draw_kernel(PerArgs a) {
     if (threadIdx.x == 0) a.wgmin[blockIdx.x] = min(min(smin[0], smin[1]), min(smin[2], smin[3]));
 }
 
+// Weights from the drawn priorities the draw pass left in w, loaded with the
+// workgroup minima in one round.
 __global__ __launch_bounds__(256) void per_weight_kernel(PerArgs a) {
     __shared__ uint32_t red[4];
+    const int k = blockIdx.x * 256 + threadIdx.x;
+    const int kc = k < a.n ? k : a.n - 1;
+    const int32_t i = a.idx[kc];
+    const float pi = a.w[kc];
     uint32_t mn = 0xFFFFFFFFu;
     for (int j = threadIdx.x; j < a.nwg; j += 256) mn = min(mn, a.wgmin[j]);
 #pragma unroll
@@ -291,14 +353,9 @@ __global__ __launch_bounds__(256) void per_weight_kernel(PerArgs a) {
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mn;
     __syncthreads();
     mn = min(min(red[0], red[1]), min(red[2], red[3]));
-    const int k = blockIdx.x * 256 + threadIdx.x;
     if (k >= a.n) return;
-    const int32_t i = a.idx[k];
     float w = 0.f;
-    if (i >= 0) {
-        const double pm = (double)__uint_as_float(mn), pi = (double)a.p[i];
-        w = (float)pow(pm / pi, (double)a.beta);
-    }
+    if (i >= 0) w = (float)pow((double)__uint_as_float(mn) / (double)pi, (double)a.beta);
     a.w[k] = w;
 }
 
@@ -313,7 +370,7 @@ hipError_t launch_per_sample(const float* p, int64_t size, int n, uint64_t seed,
     a.p = p; a.size = size; a.n = n; a.seed = seed; a.step = d_step; a.beta = beta;
     a.idx = idx; a.w = w; a.flags = flags;
     a.nb = (int)((size + kPerBlock - 1) / kPerBlock);
-    a.vec = ((uintptr_t)p & 15u) == 0;
+    a.vec = ((uintptr_t)p & 15u) == 0 && size % 4 == 0;
     a.bsum = (double*)workspace;
     a.ssum = a.bsum + a.nb;
     a.bend = a.ssum + (int64_t)a.nb * kPerSubs;
