@@ -428,7 +428,9 @@ int iql_time_aux_step(iql_handle h, const iqlh_her_step* her, const void* states
  *   IS weight of draw k: (p_min / p_idx[k])^beta, p_min the smallest drawn
  *   priority (prioritized replay's (N P(i))^-beta over the batch maximum).
  *   d_priorities  device [size] f32, >= 0 (already raised to any exponent).
- *   d_out_idx     device [n] int32; d_out_weights device [n] f32.
+ *   d_out_idx     device [n] int32; d_out_weights device [n] f32 (both also
+ *                 hold each draw's counter word between the launches: they
+ *                 must not overlap each other or the priorities).
  *   d_step        device int64 counter or NULL (= 0).
  *   d_flags       device sticky flag word or NULL: IQLH_FLAG_BAD_INDEX when a
  *                 priority is negative or non-finite or the total is not > 0

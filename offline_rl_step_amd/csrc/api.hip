@@ -455,6 +455,17 @@ int per_sample_indices(const float* d_priorities, int64_t size, int32_t n, uint6
     if (workspace_bytes < per_workspace_bytes_for(size))
         return fail(IQLH_EINVAL, "workspace too small: %zu < %zu bytes", workspace_bytes, per_workspace_bytes_for(size));
     if (((uintptr_t)workspace & 7u) != 0) return fail(IQLH_EINVAL, "workspace must be 8-byte aligned");
+    if (n > 0) {
+        // the outputs hold the draws' counter words between the launches
+        auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+            const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+            return x < y + nb && y < x + na;
+        };
+        const size_t no = 4 * (size_t)n, np = 4 * (size_t)size;
+        if (overlap(d_out_idx, no, d_out_weights, no) || overlap(d_out_idx, no, d_priorities, np) ||
+            overlap(d_out_weights, no, d_priorities, np))
+            return fail(IQLH_EINVAL, "per_sample_indices: the outputs overlap each other or the priorities");
+    }
     hipError_t e = launch_per_sample(d_priorities, size, n, seed, d_step, beta, d_out_idx, d_out_weights, d_flags,
                                      workspace, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "per_sample_indices launch");

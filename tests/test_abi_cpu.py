@@ -160,6 +160,13 @@ def test_host_validation_of_kernel_entry_points(m):
     assert m._lib_iql_step_counter(None) is None
     rows, floats = ctypes.c_int32(), ctypes.c_int64()
     assert m._lib_iql_partial_layout(None, 1, ctypes.byref(rows), ctypes.byref(floats)) == m.EINVAL
+    # PER: outputs that overlap each other or the priorities (they hold the
+    # draws' counter words between the launches)
+    ws_bytes = m.per_workspace_bytes(100)
+    for idx_at, w_at in ((1 << 20, (1 << 20) + 16), ((1 << 16) + 64, 1 << 24), (1 << 20, (1 << 16) + 128)):
+        rc = m._lib_per_sample(ctypes.c_void_p(1 << 16), 100, 8, 1, None, 0.4, ctypes.c_void_p(idx_at),
+                               ctypes.c_void_p(w_at), None, ctypes.c_void_p(1 << 28), ws_bytes, None)
+        assert rc == m.EINVAL and "overlap" in m.last_error()
 
 
 def test_binding_structs_keep_their_tensors(m):
