@@ -1555,8 +1555,11 @@ static const Variant kVariants[] = {
     // bf16, hidden 128: eight 16-sample waves per 128-sample workgroup
     {1, 128, 128, 4, &run_fused16w<128, 128>},
     {1, 64, 128, 4, &run_fused16w<64, 128>},
-    {1, 32, 32, 4, &run_fused<uint16_t, 32, 32, 4>},
-    {0, 32, 32, 4, &run_fused<float, 32, 32, 4>},
+    // hidden 32: one wave per 32-sample workgroup (a single 32x32 output tile
+    // per weight-gradient product, so more waves would leave it to one wave
+    // over four times the samples)
+    {1, 32, 32, 1, &run_fused<uint16_t, 32, 32, 1>},
+    {0, 32, 32, 1, &run_fused<float, 32, 32, 1>},
     // fp32, hidden 128: four waves share each 32-sample workgroup
     {0, 64, 128, 1, &run_fused_fs<64, 128>},
 };
