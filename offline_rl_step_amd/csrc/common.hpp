@@ -104,6 +104,7 @@ IQLH_DEV void lds_barrier() {
 // branch whose end then waits for every load the wave has in flight).
 IQLH_DEV float keep_if(bool c, float x) { return __uint_as_float(__float_as_uint(x) & (c ? 0xFFFFFFFFu : 0u)); }
 IQLH_DEV uint32_t keep_if(bool c, uint32_t x) { return x & (c ? 0xFFFFFFFFu : 0u); }
+IQLH_DEV uint16_t keep_if(bool c, uint16_t x) { return (uint16_t)(x & (c ? 0xFFFFu : 0u)); }
 
 IQLH_DEV void set_flag(int32_t* flags, int32_t bit) {
     if (flags) atomicOr(flags, bit);

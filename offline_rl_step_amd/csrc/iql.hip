@@ -61,6 +61,10 @@ template <> struct Op<uint16_t> {  // bfloat16 storage
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
     static IQLH_DEV frag zero() { return __builtin_bit_cast(frag, u32x4{0u, 0u, 0u, 0u}); }
+    static IQLH_DEV frag keep(bool c, frag x) {
+        const uint32_t m = c ? 0xFFFFFFFFu : 0u;
+        return __builtin_bit_cast(frag, __builtin_bit_cast(u32x4, x) & u32x4{m, m, m, m});
+    }
     // KPL consecutive elements (16-byte aligned)
     static IQLH_DEV frag load(const uint16_t* p) {
         return __builtin_bit_cast(frag, *(const u32x4*)p);
@@ -131,6 +135,7 @@ template <> struct Op<float> {
     static IQLH_DEV f32x16 mma(frag a, frag b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
     }
+    static IQLH_DEV frag keep(bool c, frag x) { return keep_if(c, x); }
     static IQLH_DEV frag zero() { return 0.f; }
     static IQLH_DEV frag load(const float* p) { return *p; }
     static IQLH_DEV frag load_chain(const float* row, int u, int h) {
@@ -311,42 +316,69 @@ __global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
     float* part = a.part + ((int64_t)g * a.nwg + wg) * a.Pp;
     const float tau = g == 0 ? a.tau0 : a.tau1;
 
-    // ---- S0: weights to LDS, biases and w3 to LDS, X fragments to registers
-    for (int idx = tid * O::KPL; idx < H * SP; idx += NTHR * O::KPL) {
-        const int r = idx / SP, c = idx - r * SP;
-        *(typename O::frag*)(R0 + r * C::LDW1 + c) = O::load(w1s + idx);
-    }
-    for (int idx = tid * O::KPL; idx < H * H; idx += NTHR * O::KPL) {
-        const int r = idx / H, c = idx - r * H;
-        *(typename O::frag*)(R1 + r * C::LDW2 + c) = O::load(w2s + idx);
-    }
-    for (int i = tid; i < H; i += NTHR) {
-        sb1[i] = prm[po.b1 + i];
-        sb2[i] = prm[po.b2 + i];
-        sw3[i] = prm[po.w3 + i];
-    }
+    // ---- S0: every load first (weights, biases and w3, the X fragments,
+    // then Q below), the LDS stores after them: constant trip counts and
+    // clamped indexes, so that no load is waited on before the next one is
+    // issued (a load-store loop made each weight load a round trip of its own)
+    constexpr int NL1 = H * SP / (NTHR * O::KPL), NL2 = H * H / (NTHR * O::KPL);
+    static_assert(NL1 * NTHR * O::KPL == H * SP && NL2 * NTHR * O::KPL == H * H && H <= NTHR,
+                  "whole staging passes");
+    typename O::frag w1r[NL1], w2r[NL2];
+#pragma unroll
+    for (int i = 0; i < NL1; ++i) w1r[i] = O::load(w1s + (tid + i * NTHR) * O::KPL);
+#pragma unroll
+    for (int i = 0; i < NL2; ++i) w2r[i] = O::load(w2s + (tid + i * NTHR) * O::KPL);
+    const int th = tid < H ? tid : 0;
+    const float pb1 = prm[po.b1 + th], pb2 = prm[po.b2 + th], pw3 = prm[po.w3 + th];
     const int bl = 32 * wv + l32;              // sample within the tile
     const int b = wg * BT + bl;                // sample in the batch
     const bool valid = b < B;
     typename O::frag xf[KU1];
     {
-        const T* xr = (const T*)a.states + (int64_t)b * a.ld;
+        const T* xr = (const T*)a.states + (int64_t)(valid ? b : B - 1) * a.ld;
         // XVEC: S == SP and rows aligned to whole fragments (checked on the host)
 #pragma unroll
         for (int u = 0; u < KU1; ++u) {
             const int k0 = O::KS * u + O::KPL * h;
+            // (masked by AND rather than a select, which the compiler turns
+            // into a branch around each load with a wait inside it)
             if (XVEC) {
-                xf[u] = valid ? O::load(xr + k0) : O::zero();
+                xf[u] = O::keep(valid, O::load(xr + k0));
             } else {
                 T tmp[O::KPL];
 #pragma unroll
                 for (int e = 0; e < O::KPL; ++e) {
                     const int k = k0 + e;
-                    tmp[e] = (valid && k < S) ? xr[k] : (T)0;
+                    tmp[e] = keep_if(valid && k < S, xr[k < S ? k : S - 1]);
                 }
                 xf[u] = O::make(tmp);
             }
         }
+    }
+    // with the policy fused in: lane (l32, h) takes actions h, h + 2, ... of
+    // its sample
+    float qa[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) qa[k] = 0.f;
+    if (a.out_pi) {  // uniform; indexes clamped, unused values never read
+        const int64_t bc = valid ? b : B - 1;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) qa[k] = a.q_all[bc * a.A + min(h + 2 * k, a.A - 1)];
+    }
+#pragma unroll
+    for (int i = 0; i < NL1; ++i) {
+        const int idx = (tid + i * NTHR) * O::KPL, r = idx / SP, c = idx - r * SP;
+        *(typename O::frag*)(R0 + r * C::LDW1 + c) = w1r[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NL2; ++i) {
+        const int idx = (tid + i * NTHR) * O::KPL, r = idx / H, c = idx - r * H;
+        *(typename O::frag*)(R1 + r * C::LDW2 + c) = w2r[i];
+    }
+    if (tid < H) {
+        sb1[tid] = pb1;
+        sb2[tid] = pb2;
+        sw3[tid] = pw3;
     }
     lds_barrier();
 
@@ -417,6 +449,34 @@ __global__ __launch_bounds__(64 * NW) void iql_fused_kernel(FusedArgs a) {
     if (a.fwd_only) {
         if (valid && h == 0) write_value(a.vo, g, B, b, v);
         return;
+    }
+    if (a.out_pi) {
+        // pi = softmax(beta * clamp(Q - V, -10, 10)) with the row maximum
+        // subtracted ("Current State / IQL (CPU)", advantage-weighted action
+        // selection); the two lanes of a sample share it
+        float x[8], mx = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            x[k] = h + 2 * k < a.A ? a.beta * fminf(fmaxf(qa[k] - v, -10.f), 10.f) : -INFINITY;
+            mx = fmaxf(mx, x[k]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // the hardware exponential (about 1e-6 relative on these arguments,
+        // which lie in [-20 beta, 0]), as in the bf16 hidden-128 kernel
+        float se = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            x[k] = h + 2 * k < a.A ? __expf(x[k] - mx) : 0.f;
+            se += x[k];
+        }
+        se += __shfl_xor(se, 32, 64);
+        if (valid) {
+            float* pr = a.out_pi + ((int64_t)g * B + b) * a.A;
+            const float inv = 1.f / se;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (h + 2 * k < a.A) pr[h + 2 * k] = x[k] * inv;
+        }
     }
     float dv = 0.f, lterm = 0.f;
     if (valid) {
@@ -633,6 +693,15 @@ __global__ __launch_bounds__(256) void iql_fused_fs_kernel(FusedArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < N2; ++i) w2v[i] = *(const f4*)(w2s + 4 * (tid + i * NTHR));
+    // with the policy fused in: wave wv takes samples 8 wv .. 8 wv + 7 of the
+    // tile, eight lanes per sample, actions (lane & 7) and (lane & 7) + 8
+    const int psl = 8 * wv + (lane >> 3), pb = wg * BT + psl;
+    float qa[2] = {0.f, 0.f};
+    if (a.out_pi) {  // uniform; indexes clamped, unused values never read
+        const int64_t pbc = min(pb, B - 1);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) qa[k] = a.q_all[pbc * a.A + min((lane & 7) + 8 * k, a.A - 1)];
+    }
 #pragma unroll
     for (int i = 0; i < N1; ++i) {
         const int idx = 4 * (tid + i * NTHR), r = idx / SP, c = idx - r * SP;
@@ -688,6 +757,37 @@ __global__ __launch_bounds__(256) void iql_fused_fs_kernel(FusedArgs a) {
     if (a.fwd_only) {
         if (valid && h == 0 && wv == 0) write_value(a.vo, g, B, b, v);
         return;
+    }
+    if (a.out_pi) {
+        // pi = softmax(beta * clamp(Q - V, -10, 10)) with the row maximum
+        // subtracted ("Current State / IQL (CPU)", advantage-weighted action
+        // selection), from the same V (same sum order) as the step's own
+        const float vs = ((svp[psl] + svp[BT + psl]) + (svp[2 * BT + psl] + svp[3 * BT + psl])) + b3;
+        float x[2], mx = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            x[k] = (lane & 7) + 8 * k < a.A ? a.beta * fminf(fmaxf(qa[k] - vs, -10.f), 10.f) : -INFINITY;
+            mx = fmaxf(mx, x[k]);
+        }
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        // the hardware exponential (about 1e-6 relative on these arguments,
+        // which lie in [-20 beta, 0]), as in the bf16 kernel
+        float se = 0.f;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            x[k] = (lane & 7) + 8 * k < a.A ? __expf(x[k] - mx) : 0.f;
+            se += x[k];
+        }
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) se += __shfl_xor(se, o, 64);
+        if (pb < B) {
+            float* pr = a.out_pi + ((int64_t)g * B + pb) * a.A;
+            const float inv = 1.f / se;
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+                if ((lane & 7) + 8 * k < a.A) pr[(lane & 7) + 8 * k] = x[k] * inv;
+        }
     }
     float dv = 0.f, lterm = 0.f;
     if (valid) {
@@ -1582,8 +1682,10 @@ int iql_s_pad(int dtype, int S, int H) {
 }
 int iql_reduce_blocks(int64_t P) { return (int)((P + kRedParams - 1) / kRedParams); }
 
+// Every fused tile kernel computes the policy from its own V for up to 16
+// actions.
 bool iql_fused_policy(const IqlDims& d, int A) {
-    return !d.layered && d.dtype == 1 && d.H == 128 && A >= 1 && A <= 16;
+    return !d.layered && A >= 1 && A <= 16 && iql_supported(d.dtype, d.S, d.H);
 }
 
 // The shapes that run iql_fused16w_kernel (bf16, hidden 128, state <= 128).

@@ -352,11 +352,14 @@ def test_stress_three_steps_teacher_forced(m):
 
 # ------------------------------------------------- train step + AW policy
 @pytest.mark.parametrize("wname,B,A", [("b16384_s128_h128_bf16_g2", 16384, 9), ("b16384_s128_h128_bf16_g2", 1000, 16),
-                                       ("b16384_s128_h128_bf16_g2", 777, 1), ("tiny_b256_s16_h32", 256, 4)])
+                                       ("b16384_s128_h128_bf16_g2", 777, 1), ("tiny_b256_s16_h32", 256, 4),
+                                       ("tiny_b256_s16_h32", 100, 13), ("tiny_b256_s16_h32", 256, 20),
+                                       ("b4096_s42_h128_f32", 4096, 9), ("b4096_s42_h128_f32", 1001, 16)])
 def test_train_step_with_policy(m, wname, B, A):
-    """The policy fused into the forward/backward launch (bf16, hidden 128,
-    A <= 16) or run after it (other shapes) equals the oracle's policy of the
-    step's own V, and the step itself is unchanged."""
+    """The policy fused into the forward/backward launch (every fused tile
+    kernel, A <= 16: bf16 hidden 128, fp32 hidden 128, hidden 32; full and
+    ragged batches) or run after it (A > 16) equals the oracle's policy of
+    the step's own V, and the step itself is unchanged."""
     import torch
     from oracle import aw
     w = synth.shrink(synth.WORKLOADS[wname], A=A)

@@ -257,10 +257,12 @@ def test_whole_step_relabelling_matches_oracle(m, B):
     r.tr.close()
 
 
-def test_whole_step_fp32_unfused_policy(m):
-    """fp32 operands: the policy runs as its own kernel after the
-    forward/backward launch; ragged batch and budget lengths."""
-    w = synth.shrink(synth.WORKLOADS["b4096_s42_h128_f32"], A=9, budget=True)
+@pytest.mark.parametrize("A", [9, 20])
+def test_whole_step_fp32_policy(m, A):
+    """fp32 operands: the policy fused into the forward/backward launch
+    (A <= 16) or run as its own kernel after it (A = 20); ragged batch and
+    budget lengths."""
+    w = synth.shrink(synth.WORKLOADS["b4096_s42_h128_f32"], A=A, budget=True)
     _run_pair(m, Inputs(w, 1001, 5003), steps=2)
 
 
