@@ -361,6 +361,27 @@ def test_whole_step_relabelling_inside_forward_backward(m, B, n, S, G, strategy,
     _run_pair(m, inp, steps=2, strategy=code, minimal_out=minimal)
 
 
+@pytest.mark.parametrize("wname,B,n,G,strategy,minimal,budget", [
+    ("b4096_s42_h128_f32", 4096, 1024, 8, "final", False, False),   # the workload's own shape
+    ("b4096_s42_h128_f32", 1000, 488, 8, "future", False, True),    # last tile of 8 rows; budget norms in A
+    ("b4096_s42_h128_f32", 2048, 1024, 20, "random", True, False),  # goal past 16 entries, no optional outputs
+    ("b4096_s42_h128_f32", 2000, 1000, 8, "future", False, False),  # HER rows from row 1000
+    ("tiny_b256_s16_h32", 256, 128, 4, "future", False, False),     # hidden 32, one wave per tile
+    ("tiny_b256_s16_h32", 200, 104, 16, "final", False, False),     # goal = whole state, ragged last tile
+])
+def test_whole_step_relabelling_fp32(m, wname, B, n, G, strategy, minimal, budget):
+    """fp32 trainers (the four-wave hidden-128 kernel and the hidden-32 one):
+    the step's first launch relabels the HER rows into the batch tail (rows of
+    any width and alignment), and the whole step equals the separate calls
+    bit for bit over two steps, for every strategy, ragged last tiles, goals
+    past 16 entries and with or without the budget's norms in that launch."""
+    w = synth.shrink(synth.WORKLOADS[wname], G=G, her_ratio=n / B)
+    inp = Inputs(w, B, 4099)
+    assert inp.n == n
+    code = {"final": m.HER_FINAL, "future": m.HER_FUTURE, "random": m.HER_RANDOM}[strategy]
+    _run_pair(m, inp, steps=2, strategy=code, minimal_out=minimal, budget=budget)
+
+
 @pytest.mark.parametrize("name,batch,rows", [("b16384_s128_h128_bf16_g2_budget", 16384, 128),
                                              ("b16384_s128_h128_bf16_g2_budget", 1000, 8),
                                              ("stress_b65536_s256_h512_bf16", 65536, 40),
