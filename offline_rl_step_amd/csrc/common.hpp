@@ -10,17 +10,19 @@ namespace iqlh {
 constexpr int kWave = 64;
 
 // ---------------------------------------------------------------- bfloat16
-// Round-to-nearest-even float -> bfloat16 bits; NaN becomes 0x7FC0.
-IQLH_DEV uint16_t f2bf(float x) {
-    uint32_t u = __float_as_uint(x);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-IQLH_DEV float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+// Round-to-nearest-even float -> bfloat16 bits, NaN becoming 0x7FC0: the
+// hardware conversion (v_cvt_pk_bf16_f32, two values per instruction) with
+// NaN set explicitly.
+typedef float f32x2_cv __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_cv __attribute__((ext_vector_type(2)));
 IQLH_DEV uint32_t pack_bf2(float lo, float hi) {
-    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+    uint32_t p = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_cv{lo, hi}, bf16x2_cv));
+    if (lo != lo) p = (p & 0xFFFF0000u) | 0x7FC0u;
+    if (hi != hi) p = (p & 0x0000FFFFu) | 0x7FC00000u;
+    return p;
 }
+IQLH_DEV uint16_t f2bf(float x) { return (uint16_t)(pack_bf2(x, 0.f) & 0xFFFFu); }
+IQLH_DEV float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
 // ---------------------------------------------------------------- Philox
 // Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As

@@ -1323,10 +1323,7 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
                 x[e] = zero ? 0.f : (goal ? gv[e] : xs[k][e]);
                 y[e] = zero ? 0.f : (goal ? gv[e] : xn[k][e]);
             }
-            xr[k] = u32x4{(uint32_t)f2bf(x[0]) | ((uint32_t)f2bf(x[1]) << 16),
-                          (uint32_t)f2bf(x[2]) | ((uint32_t)f2bf(x[3]) << 16),
-                          (uint32_t)f2bf(x[4]) | ((uint32_t)f2bf(x[5]) << 16),
-                          (uint32_t)f2bf(x[6]) | ((uint32_t)f2bf(x[7]) << 16)};
+            xr[k] = u32x4{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]), pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7])};
             if (writes_row(sr) && sr < nrow && k0 < S_) {  // whole chunks: S is a multiple of 8
                 const int64_t hi = hrow0 + sr;
                 *(u32x4*)((uint16_t*)h.out_states + hi * a.ld + k0) = xr[k];

@@ -99,6 +99,35 @@ def test_her_ragged_episodes_and_merged_batch(m, strategy):
     assert np.array_equal(Wm, her.merged_is_weights(np.full(777, 7.0, np.float32), len(src)))
 
 
+# float32 bit patterns at the edges of round-to-nearest-even to bfloat16
+EDGE_BITS = np.array([0x3F808000, 0x3F818000, 0x3F807FFF, 0x3F808001, 0xBF818000, 0x00000001, 0x00008000,
+                      0x00018000, 0x007FFFFF, 0x807FFFFF, 0x7F7FFFFF, 0x7F7F7FFF, 0xFF7FFFFF, 0x7F800000,
+                      0xFF800000, 0x80000000, 0x7FC00000, 0x7F800001, 0xFFC12345, 0x7FFFFFFF], np.uint32)
+
+
+@pytest.mark.parametrize("S", [48, 45])
+def test_her_bf16_rounding_edges(m, S):
+    """Relabelled states stored as bfloat16 round to nearest even exactly as
+    the oracle does at ties (even and odd), near ties, denormals, overflow to
+    infinity, infinities, signed zero and NaN (quiet, signalling, negative,
+    with payloads: all 0x7FC0); S = 48 takes the paired stores, 45 the
+    element stores."""
+    g = np.random.default_rng(8)
+    C, G = 512, 6
+    ends = np.arange(16, C + 1, 16, dtype=np.int32)
+    states = g.standard_normal((C, S), dtype=np.float32)
+    cols = np.arange(G, S)
+    edge = EDGE_BITS[(np.arange(C)[:, None] + cols[None, :]) % EDGE_BITS.size].view(np.float32)
+    states[:, G:] = edge
+    buf = dict(states=states, next_states=g.standard_normal((C, S), dtype=np.float32),
+               actions=g.integers(0, 4, C, dtype=np.int32), dones=np.zeros(C, np.float32),
+               episode_ends=ends, buffer_size=C)
+    src = g.integers(0, C, 700).astype(np.int32)
+    ref = her.her_step(buf, src, G, her.FUTURE, seed=31, step=2, out_bf16=True)
+    got = _run(m, buf, src, G, her.FUTURE, 31, 2, True)
+    _compare(got, ref, True)
+
+
 def test_her_equal_goals_reward_hit(m):
     w = synth.shrink(synth.WORKLOADS["stress_b65536_s256_h512_bf16"], B=4096, C=1 << 14)
     buf = synth.replay_buffer(w)
