@@ -295,7 +295,8 @@ class Context:
 
 
 LAUNCH_KERNELS = (("relabel_norms", ("step_her_norms_kernel", "her_relabel_kernel")),
-                  ("fwd_bwd", ("iql_fused16w_kernel", "iql_fused_kernel", "big_fwd1_kernel", "big_fwd2_kernel",
+                  ("fwd_bwd", ("iql_fused16w_kernel", "iql_fused_fs_kernel", "iql_fused_kernel", "big_fwd1_kernel",
+                               "big_fwd2_kernel",
                                "big_wgrad_kernel", "layer_gemm_kernel", "iql_rows_kernel", "iql_wgrad_kernel",
                                "aw_policy_kernel", "aw_policy_vec_kernel")),
                   ("reduce_saxpy", ("step_reduce_saxpy_kernel",)),
@@ -304,6 +305,9 @@ LAUNCH_KERNELS = (("relabel_norms", ("step_her_norms_kernel", "her_relabel_kerne
 
 def profile_commands(workload):
     wl = "" if workload is None else f" --workload {workload}"
+    sys.path.insert(0, ROOT)
+    import synth
+    mfma = mfma_counters(synth.WORKLOADS[workload or synth.BENCH_WORKLOAD].dtype)
     return (
         f"rocprofv3 --kernel-trace --stats -f csv -d OUT/trace -o step -- python3 $REPO/bench.py{wl} --steps 200 "
         "--no-cpu-baseline --no-next-rows",
@@ -313,7 +317,7 @@ def profile_commands(workload):
         f"rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/WRITE_SIZE -o p -- python3 $REPO/bench.py{wl} --steps 5 "
         "--warmup 1 --no-graph --no-cpu-baseline --no-next-rows --kernel-reps 5",
         "rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/copy_WRITE_SIZE -o p -- python3 $REPO/bench.py --copy-probe 256",
-        f"rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} -f csv -d OUT/MFMA -o p -- python3 $REPO/bench.py{wl} "
+        f"rocprofv3 --pmc {' '.join(mfma)} -f csv -d OUT/MFMA -o p -- python3 $REPO/bench.py{wl} "
         "--steps 5 --warmup 1 --no-graph --no-cpu-baseline --no-next-rows --kernel-reps 5",
         f"rocprofv3 --pmc {' '.join(LDS_COUNTERS)} -f csv -d OUT/LDS -o p -- python3 $REPO/bench.py{wl} "
         "--steps 5 --warmup 1 --no-graph --no-cpu-baseline --no-next-rows --kernel-reps 5",
@@ -321,9 +325,12 @@ def profile_commands(workload):
     )
 
 
-# matrix-core counters (one rocprofv3 pass): bf16 MFMA work in units of 512
-# flops, cycles the SIMDs' MFMA units were busy, GPU-active cycles
-MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE")
+# matrix-core counters (one rocprofv3 pass): MFMA work of the workload's
+# operand type in units of 512 flops, cycles the SIMDs' MFMA units were busy,
+# MFMA instructions, GPU-active cycles
+def mfma_counters(dtype):
+    mops = "SQ_INSTS_VALU_MFMA_MOPS_BF16" if dtype == "bf16" else "SQ_INSTS_VALU_MFMA_MOPS_F32"
+    return (mops, "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE")
 LDS_COUNTERS = ("SQ_INSTS_LDS", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE")
 MI355X_SIMDS = 256 * 4
 
@@ -477,19 +484,21 @@ def summarize_profiles(d, workload=None):
         lc = _counters_per_kernel(gl[0]) if gl else {}
         L.append("## Matrix cores and LDS (`--pmc`, median over dispatches)")
         L.append("")
-        L.append("`MFMA flops` = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; `MFMA busy` = SQ_VALU_MFMA_BUSY_CYCLES "
+        mops = mfma_counters(w.dtype)[0]
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+        L.append(f"`MFMA flops` = {mops} x 512; `MFMA busy` = SQ_VALU_MFMA_BUSY_CYCLES "
                  f"(summed over the SIMDs) / ({MI355X_SIMDS} SIMDs x the kernel's average time above x 2.4 GHz); "
                  "`rate` = MFMA flops / that time; LDS `active` = SQ_LDS_IDX_ACTIVE (summed over the CUs) / "
                  "(256 CUs x the same cycles), `conflict` = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.  "
                  "(GRBM_GUI_ACTIVE, summed over the XCDs, spans the profiler's serialised dispatch window rather "
                  "than the kernel, so the kernel-trace time is the denominator.)")
         L.append("")
-        L.append("| kernel | MFMA flops | / algorithmic | MFMA busy | rate TFLOP/s | % of bf16 peak | LDS instrs | "
+        L.append(f"| kernel | MFMA flops | / algorithmic | MFMA busy | rate TFLOP/s | % of {w.dtype} peak | LDS instrs | "
                  "LDS active | LDS conflict |")
         L.append("|---|---:|---:|---:|---:|---:|---:|---:|---:|")
         alg = fused_flops_per_launch(w)
         for nm, cs in mc.items():
-            fl = cs.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+            fl = cs.get(mops, 0.0) * 512
             if fl <= 0:
                 continue
             t_us = next((float(r["AverageNs"]) / 1e3 for r in stats if r["Name"] == nm), float("nan"))
@@ -502,7 +511,7 @@ def summarize_profiles(d, workload=None):
             fused = launch_of.get(nm) == "fwd_bwd" and len([1 for n2 in mc if launch_of.get(n2) == "fwd_bwd"]) == 1
             ratio = f"{fl / alg:.3f}" if fused else "-"
             L.append(f"| `{_short(nm)}` | {fl:.4g} | {ratio} | {100 * busy:.1f} % | {rate:.0f} | "
-                     f"{100 * rate / PEAK_BF16_TFLOPS:.1f} | {ls.get('SQ_INSTS_LDS', float('nan')):.4g} | "
+                     f"{100 * rate / peak:.1f} | {ls.get('SQ_INSTS_LDS', float('nan')):.4g} | "
                      f"{100 * lact:.1f} % | {100 * lcon:.2f} % |")
             if fused and default:
                 mfma_json = {"kernel": _short(nm), "workload": w.name, "source_hash": src_hash, "commit": commit,
@@ -510,10 +519,14 @@ def summarize_profiles(d, workload=None):
                              "counter_rate_tflops": rate, "avg_kernel_us": t_us,
                              "lds_active_frac": lact, "lds_conflict_frac": lcon}
         L.append("")
+        single = len([1 for n2 in mc if launch_of.get(n2) == "fwd_bwd"]) == 1
         if mfma_json is not None:
             L.append("The forward/backward kernel's MFMA flops exceed the algorithmic count by its bias-gradient "
                      "products (an extra MFMA against an all-ones operand per weight-gradient sweep) and the zero "
                      "padding of tiles.")
+        elif single:
+            L.append("The forward/backward kernel's MFMA flops differ from the algorithmic count by the zero "
+                     "padding of its tiles (the state padded to the operand width).")
         else:
             L.append("Several kernels share the forward/backward launch here, so no single kernel's MFMA flops "
                      "are set against the algorithmic count; the rate column is each kernel's own.")
