@@ -113,6 +113,19 @@ def test_b4096_s42_fp32_one_step_padded_ld(m):
     _one_step(m, synth.WORKLOADS["b4096_s42_h128_f32"], 1e-4, ld=45)
 
 
+@pytest.mark.parametrize("wname,kw,B", [
+    ("b4096_s42_h128_f32", dict(S=64), 1000),                           # state = operand width: vector loads
+    ("b4096_s42_h128_f32", dict(S=64, groups=2, taus=(0.7, 0.3)), 4096),  # two groups, their own tau
+    ("b4096_s42_h128_f32", dict(groups=2, taus=(0.9, 0.3)), 777),       # ragged last tile, two groups
+    ("tiny_b256_s16_h32", dict(S=32), 200),                             # hidden 32 at its operand width
+])
+def test_fp32_tile_kernel_shapes(m, wname, kw, B):
+    """The fp32 tile kernels (four waves per tile at hidden 128, one wave at
+    hidden 32) at the state width of their operand tile, with two groups of
+    different tau and with ragged batches."""
+    _one_step(m, synth.shrink(synth.WORKLOADS[wname], **kw), 1e-4, B=B)
+
+
 def test_b4096_s42_fp32_hundred_steps(m):
     w = synth.WORKLOADS["b4096_s42_h128_f32"]
     s = Setup(m, w)
