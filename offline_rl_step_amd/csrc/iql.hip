@@ -195,6 +195,9 @@ struct FusedArgs {
     int her_on, her_row0;
     HerArgs her;
     NormsArgs nrm;
+    // fp32 four-wave kernel only: two workgroups per tile, workgroup 2 t
+    // forming tile t's dW2 part of the partial row and 2 t + 1 its dW1 part
+    int fs_split;
 };
 
 template <typename T, int SP, int H, int NW>
@@ -652,7 +655,13 @@ __global__ __launch_bounds__(256) void iql_fused_fs_kernel(FusedArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index = row tile, uniform
-    const int g = blockIdx.y, wg = blockIdx.x;
+    const int g = blockIdx.y;
+    // with fs_split, workgroups 2 t and 2 t + 1 both run tile t's forward and
+    // dz2; the first then forms dW2, db2, dw3, db3 and the loss, the second
+    // dh1, dz1, dW1 and db1 (disjoint slots of the tile's partial row)
+    const int wg = a.fs_split ? (int)blockIdx.x >> 1 : (int)blockIdx.x;
+    const bool do_w2 = !a.fs_split || (blockIdx.x & 1) == 0;  // uniform
+    const bool do_w1 = !a.fs_split || (blockIdx.x & 1) == 1;
     const int S = a.S, B = a.B;
     const POff po(S, H);
     const float* prm = a.params + (int64_t)g * a.P;
@@ -697,7 +706,7 @@ __global__ __launch_bounds__(256) void iql_fused_fs_kernel(FusedArgs a) {
     // tile, eight lanes per sample, actions (lane & 7) and (lane & 7) + 8
     const int psl = 8 * wv + (lane >> 3), pb = wg * BT + psl;
     float qa[2] = {0.f, 0.f};
-    if (a.out_pi) {  // uniform; indexes clamped, unused values never read
+    if (a.out_pi && do_w2) {  // uniform; indexes clamped, unused values never read
         const int64_t pbc = min(pb, B - 1);
 #pragma unroll
         for (int k = 0; k < 2; ++k) qa[k] = a.q_all[pbc * a.A + min((lane & 7) + 8 * k, a.A - 1)];
@@ -758,7 +767,7 @@ __global__ __launch_bounds__(256) void iql_fused_fs_kernel(FusedArgs a) {
         if (valid && h == 0 && wv == 0) write_value(a.vo, g, B, b, v);
         return;
     }
-    if (a.out_pi) {
+    if (a.out_pi && do_w2) {
         // pi = softmax(beta * clamp(Q - V, -10, 10)) with the row maximum
         // subtracted ("Current State / IQL (CPU)", advantage-weighted action
         // selection), from the same V (same sum order) as the step's own
@@ -795,7 +804,7 @@ __global__ __launch_bounds__(256) void iql_fused_fs_kernel(FusedArgs a) {
         const float w = diff >= 0.f ? tau : 1.f - tau;
         lterm = w * diff * diff;
         dv = -2.f * w * diff * a.invB;
-        if (h == 0 && wv == 0 && a.out_v) a.out_v[(int64_t)g * B + b] = v;
+        if (h == 0 && wv == 0 && do_w2 && a.out_v) a.out_v[(int64_t)g * B + b] = v;
     }
     if (wv == 0) {
         const float ls = wave_sum(h == 0 ? lterm : 0.f);
@@ -820,27 +829,33 @@ __global__ __launch_bounds__(256) void iql_fused_fs_kernel(FusedArgs a) {
 
     // ---- from here each wave reads its own rows of R0 and R2 and every row
     // of R1, R3 and s^T: dw3 and db2 (row sums), db3 and the loss
-    fs_rowsum<LDA>(R2, wv, part + po.w3);
-    fs_rowsum<LDA>(R0, wv, part + po.b2);
-    if (tid == 0) {
-        a.loss_part[(int64_t)g * a.nwg + wg] = sred[0];
-        part[po.b3] = sred[1];
+    if (do_w2) {
+        fs_rowsum<LDA>(R2, wv, part + po.w3);
+        fs_rowsum<LDA>(R0, wv, part + po.b2);
+        if (tid == 0) {
+            a.loss_part[(int64_t)g * a.nwg + wg] = sred[0];
+            part[po.b3] = sred[1];
+        }
     }
-    // B1: row tile wv of dh1^T = W2^T dz2^T (A: column 32 wv + l32 of W2);
-    // dz1 = dh1 relu'(z1) over this wave's rows of R2 (read above)
-    acc = f32x16{};
+    if (do_w1) {
+        // B1: row tile wv of dh1^T = W2^T dz2^T (A: column 32 wv + l32 of
+        // W2); dz1 = dh1 relu'(z1) over this wave's rows of R2 (read above)
+        acc = f32x16{};
 #pragma unroll
-    for (int u = 0; u < KUH; ++u)
-        acc = O::mma(R1[(O::KS * u + h) * C::LDW2 + 32 * wv + l32], R0[(O::KS * u + h) * LDA + l32], acc);
+        for (int u = 0; u < KUH; ++u)
+            acc = O::mma(R1[(O::KS * u + h) * C::LDW2 + 32 * wv + l32], R0[(O::KS * u + h) * LDA + l32], acc);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int f = 32 * wv + 8 * (r >> 2) + 4 * h + (r & 3);
-        R2[f * LDA + bl] = (mask1 >> r) & 1u ? acc[r] : 0.f;
+        for (int r = 0; r < 16; ++r) {
+            const int f = 32 * wv + 8 * (r >> 2) + 4 * h + (r & 3);
+            R2[f * LDA + bl] = (mask1 >> r) & 1u ? acc[r] : 0.f;
+        }
     }
     // dW2 = dz2^T h1, db1 (row sums of dz1), dW1 = dz1^T s
-    fs_wgrad<NT, LDA>(R0, R3, wv, part + po.w2, H, H);
-    fs_rowsum<LDA>(R2, wv, part + po.b1);
-    fs_wgrad<SP / 32, LDA>(R2, Rs, wv, part + po.w1, S, S);
+    if (do_w2) fs_wgrad<NT, LDA>(R0, R3, wv, part + po.w2, H, H);
+    if (do_w1) {
+        fs_rowsum<LDA>(R2, wv, part + po.b1);
+        fs_wgrad<SP / 32, LDA>(R2, Rs, wv, part + po.w1, S, S);
+    }
 }
 constexpr size_t fs_lds_bytes(size_t table_bytes, int H) { return table_bytes + (size_t)(3 * H + 2 + 4 * 32) * 4; }
 
@@ -1629,11 +1644,16 @@ static hipError_t run_fused_fs_x(const FusedArgs& fa, int G, hipStream_t stream,
         if (e != hipSuccess) return e;
         attr_set = true;
     }
+    // while the tiles leave compute units idle (one workgroup each on the
+    // MI355X's 256), two workgroups share each tile's backward pass
+    FusedArgs f = fa;
+    f.fs_split = !fa.fwd_only && 2 * fa.nwg * G <= 256;
+    const int gx = f.fs_split ? 2 * fa.nwg : fa.nwg;
     if (ev0)
-        hipExtLaunchKernelGGL((iql_fused_fs_kernel<SP, H, XVEC>), dim3(fa.nwg, G), dim3(256), bytes, stream, ev0, ev1,
-                              0, fa);
+        hipExtLaunchKernelGGL((iql_fused_fs_kernel<SP, H, XVEC>), dim3(gx, G), dim3(256), bytes, stream, ev0, ev1, 0,
+                              f);
     else
-        hipLaunchKernelGGL((iql_fused_fs_kernel<SP, H, XVEC>), dim3(fa.nwg, G), dim3(256), bytes, stream, fa);
+        hipLaunchKernelGGL((iql_fused_fs_kernel<SP, H, XVEC>), dim3(gx, G), dim3(256), bytes, stream, f);
     return hipGetLastError();
 }
 
