@@ -524,6 +524,11 @@ def summarize_profiles(d, workload=None):
             L.append("The forward/backward kernel's MFMA flops exceed the algorithmic count by its bias-gradient "
                      "products (an extra MFMA against an all-ones operand per weight-gradient sweep) and the zero "
                      "padding of tiles.")
+        elif single and any("fused_fs" in n2 for n2 in mc) and 2 * -(-w.B // 32) * w.groups <= 256:
+            L.append("The forward/backward kernel's MFMA flops exceed the algorithmic count by the zero padding "
+                     "of its tiles (the state padded to the operand width) and by the forward pass, which both "
+                     "workgroups of a 32-sample tile run while the tiles alone would leave compute units idle "
+                     "(each then forms half of the tile's weight gradients).")
         elif single:
             L.append("The forward/backward kernel's MFMA flops differ from the algorithmic count by the zero "
                      "padding of its tiles (the state padded to the operand width).")

@@ -117,12 +117,15 @@ def test_b4096_s42_fp32_one_step_padded_ld(m):
     ("b4096_s42_h128_f32", dict(S=64), 1000),                           # state = operand width: vector loads
     ("b4096_s42_h128_f32", dict(S=64, groups=2, taus=(0.7, 0.3)), 4096),  # two groups, their own tau
     ("b4096_s42_h128_f32", dict(groups=2, taus=(0.9, 0.3)), 777),       # ragged last tile, two groups
+    ("b4096_s42_h128_f32", dict(), 4128),                               # 129 tiles: one workgroup each
     ("tiny_b256_s16_h32", dict(S=32), 200),                             # hidden 32 at its operand width
 ])
 def test_fp32_tile_kernel_shapes(m, wname, kw, B):
     """The fp32 tile kernels (four waves per tile at hidden 128, one wave at
     hidden 32) at the state width of their operand tile, with two groups of
-    different tau and with ragged batches."""
+    different tau and with ragged batches.  At hidden 128 two workgroups share
+    a tile while tiles x groups <= 128 (batches 1000 and 777 here), one runs
+    it otherwise (4096 with two groups, 4128 with one)."""
     _one_step(m, synth.shrink(synth.WORKLOADS[wname], **kw), 1e-4, B=B)
 
 
