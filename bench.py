@@ -65,6 +65,11 @@ def parse():
     p.add_argument("--kernel-reps", type=int, default=200)
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run 10 plain device copies of MIB MiB (counter calibration) and exit")
+    p.add_argument("--probe", choices=("team-fold", "xcc-map"), default=None,
+                   help="only run one measurement probe of libiqlh_probes.so and print one JSON line: "
+                        "team-fold (the split-K partials summed inside the writing launch, against a "
+                        "separate summing launch), xcc-map (the XCD of each block of a launch of the "
+                        "forward/backward kernel's shape)")
     p.add_argument("--sweep", choices=("her", "aw", "budget", "copy"), default=None,
                    help="only time one HBM-bound entry point on working sets of at least 1 GiB (her_relabel over "
                         "a 2^22-row replay buffer, iql_aw_policy up to B*A = 2^26 for two trainers, "
@@ -92,6 +97,38 @@ def copy_probe(mib):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_mib": mib, "bytes_per_copy": n * 4}), flush=True)
+
+
+def run_probe(name, reps=50):
+    """One probe of libiqlh_probes.so (built by offline_rl_step_amd/build.py)."""
+    import ctypes
+    import torch
+    torch.cuda.init()
+    lib = ctypes.CDLL(os.path.join(ROOT, "offline_rl_step_amd", "libiqlh_probes.so"))
+    if name == "team-fold":
+        us = (ctypes.c_double * 9)()
+        eq = (ctypes.c_int * 2)()
+        to = ctypes.c_int(0)
+        rc = lib.iqlh_probe_team_fold(ctypes.c_int(reps), us, eq, ctypes.byref(to))
+        if rc != 0:
+            raise RuntimeError(f"iqlh_probe_team_fold returned {rc}")
+        out = {"probe": name, "reps": reps, "rows": 256, "row_floats": 33280, "team": 16}
+        for i, v in enumerate(("base", "fold_all_release", "fold_one_release")):
+            out[v] = {"rows_us": us[3 * i], "sum_us": us[3 * i + 1], "pair_us": us[3 * i + 2]}
+        out["fold_all_release"]["bitwise_equal"] = bool(eq[0])
+        out["fold_one_release"]["bitwise_equal"] = bool(eq[1])
+        out["timed_out_waits"] = to.value
+    else:
+        blocks, lds = 256, 154 * 1024
+        xcc = (ctypes.c_int * blocks)()
+        rc = lib.iqlh_probe_xcc_map(ctypes.c_int(blocks), ctypes.c_int(lds), xcc)
+        if rc != 0:
+            raise RuntimeError(f"iqlh_probe_xcc_map returned {rc}")
+        got = list(xcc)
+        out = {"probe": name, "blocks": blocks, "threads": 1024, "lds_bytes": lds,
+               "block_i_on_xcc_i_mod_8": all(x == i % 8 for i, x in enumerate(got)),
+               "blocks_per_xcc": [got.count(k) for k in range(8)], "xcc_of_first_16": got[:16]}
+    print(json.dumps(out), flush=True)
 
 
 def fused_flops_per_launch(w):
@@ -878,6 +915,9 @@ def main():
         return
     if a.copy_probe:
         copy_probe(a.copy_probe)
+        return
+    if a.probe:
+        run_probe(a.probe)
         return
     if a.gpus != 1:
         print(f"bench.py measures one GPU: the step has no cross-GPU exchange, so --gpus {a.gpus} "

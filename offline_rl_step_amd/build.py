@@ -1,4 +1,6 @@
-"""Builds libiqlher.so (the HIP kernels and the C ABI) for gfx950, in-tree.
+"""Builds libiqlher.so (the HIP kernels and the C ABI) for gfx950, in-tree,
+and libiqlh_probes.so (measurement probes run by bench.py --probe, not part
+of the step).
 
 Usage: python offline_rl_step_amd/build.py   (runs without importing the package,
 which would load the library being rebuilt)
@@ -11,6 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libiqlher.so")
+PROBE_LIB = os.path.join(HERE, "libiqlh_probes.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -62,7 +65,22 @@ def build(verbose=False, jobs=8):
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout)
     os.replace(tmp, LIB)
+    build_probes(verbose)
     return LIB
+
+
+def build_probes(verbose=False):
+    """The probe library: one source, compiled and linked in one step."""
+    src = os.path.join(HERE, "probes", "probes.hip")
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-shared", src, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("probe library build failed:\n" + r.stdout)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 def _wait(procs):
