@@ -359,6 +359,12 @@ IQLH_DEV void xcd_map(int id, int nranges, int nper, int& range, int& job) {
     }
 }
 
+// First k-slice of this workgroup's product, of nks: the workgroups of one
+// XCD (ids xcd + 8 k) start at different slices, so that they do not all
+// read the same weight rows from their shared L2 at the same time.  Each
+// workgroup still adds every slice once, in a fixed order (deterministic).
+IQLH_DEV int k_rotation(int nks) { return (int)((blockIdx.x >> 3) % (unsigned)nks); }
+
 // ---------------------------------------------------------------- fwd1
 // D[f][s] = sum_k W1[f][k] s[s][k] over a 256-feature x 256-sample tile;
 // h1 = relu(D + b1), and the ReLU mask as bits for the backward product.
@@ -386,12 +392,14 @@ __global__ __launch_bounds__(kThreads) void big_fwd1_kernel(BigArgs a) {
     const int l = threadIdx.x & 63, l16 = l & 15, q = l >> 4;
 
     bf16x8 fa[8], fb[2][8];  // fa: one set, re-read row by row (see kloop)
+    const int nks = a.S / kBK, krot = k_rotation(nks);
     kloop<NST, 8>(
-        a.S / kBK,
+        nks,
         [&](int s, int buf) {
             uint16_t* st_ = smem + buf * STG;
-            dma_kc<kTile>(A, a.ldw1, kTile, s * kBK, st_);
-            dma_kc<kTile>(Bm, a.ldx, srows, s * kBK, st_ + kTile * kBK);
+            const int k0 = ((s + krot) % nks) * kBK;
+            dma_kc<kTile>(A, a.ldw1, kTile, k0, st_);
+            dma_kc<kTile>(Bm, a.ldx, srows, k0, st_ + kTile * kBK);
         },
         [&](int buf, auto p) {
             constexpr int P = decltype(p)::value;
@@ -471,7 +479,7 @@ IQLH_DEV void w2t_frags(const uint16_t* At, int kt, bf16x8 (&f)[MT]) {
 }
 template <int H, int MT>
 IQLH_DEV void backward_h1(const BigArgs& a, uint16_t* smem, f4 (&acc)[MT][8], bf16x8 (&fa0)[MT], int g, int blk,
-                          int s0, int srows, int wv, int l, int l16, int q) {
+                          int s0, int srows, int wv, int l, int l16, int q, int krot) {
     constexpr int NK = H / kBK;
     static_assert(NK % 2 == 0, "k-steps in pairs");
     const uint16_t* At = w2t_lane<H, MT>(a, g, wv, l16, q);
@@ -490,13 +498,15 @@ IQLH_DEV void backward_h1(const BigArgs& a, uint16_t* smem, f4 (&acc)[MT][8], bf
         for (int j = 0; j < 8; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
     bf16x8 fa1[MT], fb[8];
     auto load_a = [&](int kt, bf16x8 (&f)[MT]) __attribute__((always_inline)) { w2t_frags<H, MT>(At, kt, f); };
+    // k-steps in the rotated order of the forward product (k_rotation)
     auto step = [&](int kt, bf16x8 (&cur)[MT], bf16x8 (&nxt)[MT]) __attribute__((always_inline)) {
-        if (kt + 1 < NK) load_a(kt + 1, nxt);
+        if (kt + 1 < NK) load_a((kt + 1 + krot) & (NK - 1), nxt);
         // the next step's loads stay ahead of this step's MFMAs (the
         // scheduler would otherwise sink each load to its first use)
         __builtin_amdgcn_sched_barrier(0);
+        const int kk = (kt + krot) & (NK - 1);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) fb[j] = *(const bf16x8*)(smem + stage_off<H>(16 * j + l16, kBK * kt + 8 * q));
+        for (int j = 0; j < 8; ++j) fb[j] = *(const bf16x8*)(smem + stage_off<H>(16 * j + l16, kBK * kk + 8 * q));
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -581,10 +591,12 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
+    const int krot = k_rotation(H / kBK);
     auto issue = [&](int s, int buf) {
         uint16_t* st_ = smem + buf * STG;
-        dma_kc<H>(A, H, H, s * kBK, st_);
-        dma_kc<kFwd2Samples>(Bm, H, srows, s * kBK, st_ + H * kBK);
+        const int k0 = ((s + krot) & (H / kBK - 1)) * kBK;
+        dma_kc<H>(A, H, H, k0, st_);
+        dma_kc<kFwd2Samples>(Bm, H, srows, k0, st_ + H * kBK);
     };
     if constexpr (H == 512) {
         // no registers for a second fragment set next to this epilogue
@@ -730,10 +742,10 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
         }
     }
     bf16x8 fa0[MT];
-    if constexpr (BWD) w2t_frags<H, MT>(w2t_lane<H, MT>(a, g, wv, l16, q), 0, fa0);
+    if constexpr (BWD) w2t_frags<H, MT>(w2t_lane<H, MT>(a, g, wv, l16, q), krot, fa0);
     __syncthreads();
     stage_out<H, kFwd2Samples>(smem, a.dz2 + ((int64_t)g * B + s0) * H, H, srows);
-    if constexpr (BWD) backward_h1<H, MT>(a, smem, acc, fa0, g, blk, s0, srows, wv, l, l16, q);
+    if constexpr (BWD) backward_h1<H, MT>(a, smem, acc, fa0, g, blk, s0, srows, wv, l, l16, q, krot);
 }
 
 // --------------------------------------------------------------- wgrad
