@@ -65,15 +65,17 @@ def parse():
     p.add_argument("--kernel-reps", type=int, default=200)
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run 10 plain device copies of MIB MiB (counter calibration) and exit")
-    p.add_argument("--probe", choices=("team-fold", "xcc-map"), default=None,
+    p.add_argument("--probe", choices=("team-fold", "xcc-map", "stream-sum"), default=None,
                    help="only run one measurement probe of libiqlh_probes.so and print one JSON line: "
                         "team-fold (the split-K partials summed inside the writing launch, against a "
                         "separate summing launch), xcc-map (the XCD of each block of a launch of the "
-                        "forward/backward kernel's shape)")
-    p.add_argument("--sweep", choices=("her", "aw", "budget", "copy"), default=None,
+                        "forward/backward kernel's shape), stream-sum (a read-only four-array sum of squares "
+                        "of 1 GiB cut into blocks three ways)")
+    p.add_argument("--sweep", choices=("her", "aw", "budget", "sentinel", "copy"), default=None,
                    help="only time one HBM-bound entry point on working sets of at least 1 GiB (her_relabel over "
                         "a 2^22-row replay buffer, iql_aw_policy up to B*A = 2^26 for two trainers, "
-                        "grad_budget_accumulate + Adam up to n = 2^26) and print one JSON line per size")
+                        "grad_budget_accumulate + Adam up to n = 2^26, iqlh_nonfinite_check over eight slots up to "
+                        "4 GiB) and print one JSON line per size")
     p.add_argument("--sweep-calls", type=int, default=3, help="timed calls per sweep size (after one warm-up)")
     p.add_argument("--summarize-sweeps", metavar="DIR", default=None,
                    help="only write profiles/hbm_sweeps.md from the sweep logs and rocprofv3 CSV output under DIR "
@@ -118,6 +120,17 @@ def run_probe(name, reps=50):
         out["fold_all_release"]["bitwise_equal"] = bool(eq[0])
         out["fold_one_release"]["bitwise_equal"] = bool(eq[1])
         out["timed_out_waits"] = to.value
+    elif name == "stream-sum":
+        n = 1 << 26
+        out = {"probe": name, "arrays": 4, "floats_each": n, "bytes": 16 * n, "reps": 10}
+        for nb in (1024, 2048, 4096):
+            us = (ctypes.c_double * 3)()
+            rc = lib.iqlh_probe_stream_sum(ctypes.c_int64(n), ctypes.c_int(nb), ctypes.c_int(10), us)
+            if rc != 0:
+                raise RuntimeError(f"iqlh_probe_stream_sum returned {rc}")
+            out[f"nb{nb}"] = {"strided_us": us[0], "chunked_us": us[1], "per_piece_us": us[2],
+                              "strided_TBs": 16 * n / us[0] / 1e6, "chunked_TBs": 16 * n / us[1] / 1e6,
+                              "per_piece_TBs": 16 * n / us[2] / 1e6}
     else:
         blocks, lds = 256, 154 * 1024
         xcc = (ctypes.c_int * blocks)()
@@ -671,11 +684,18 @@ SWEEP_POINTS = {
     "her": [1 << 16, 1 << 18, 1 << 20],      # relabelled rows
     "aw": [1 << 20, 1 << 22, 1 << 24],       # rows B at A = 16, two trainers (B * A up to 2^26)
     "budget": [1 << 22, 1 << 24, 1 << 26],   # elements n, four sources
+    "sentinel": [1 << 23, 1 << 25, 1 << 27], # elements per slot, eight slots
     "copy": [1 << 26, 1 << 28],              # a plain device copy of n floats (torch), for reference
 }
 SWEEP_KERNELS = {"her": ("her_relabel_kernel",), "aw": ("aw_policy",),
                  "budget": ("budget_norms_kernel", "budget_saxpy_kernel", "adam_flat_kernel"),
-                 "copy": ("copy",)}
+                 "sentinel": ("nonfinite_sentinel_kernel",), "copy": ("copy",)}
+# bytes per element each pass of a multi-kernel sweep must move: the budget's
+# pass 1 reads the four sources, pass 2 reads them again and writes grad,
+# Adam reads and writes p, m, v and grad
+SWEEP_PASS_BYTES = {"budget": (("budget_norms_kernel", "pass 1: per-source sums of squares", 16),
+                               ("budget_saxpy_kernel", "pass 2: clip + SAXPY", 20),
+                               ("adam_flat_kernel", "pass 3: clipped Adam", 32))}
 
 
 def sweep_bytes(kind, x):
@@ -688,7 +708,8 @@ def sweep_bytes(kind, x):
       aw:     Q [B, 16] once, V [2, B], the policy [2, B, 16] written;
       budget: pass 1 reads the four sources; pass 2 reads them again (the
               clip needs every norm first) and writes grad; Adam reads grad,
-              p, m, v and writes p, m, v and the zeroed grad: 68 B/element."""
+              p, m, v and writes p, m, v and the zeroed grad: 68 B/element;
+      sentinel: eight slots of x floats, read once."""
     if kind == "her":
         S, G = 128, 8
         return x * ((8 * S + 4 * G + 4 + 4 + 4 + 8) + (2 * S + 4 * S + 5 * 4))
@@ -697,6 +718,8 @@ def sweep_bytes(kind, x):
         return x * (4 * A + G * (4 + 4 * A))
     if kind == "copy":
         return x * 8
+    if kind == "sentinel":
+        return x * 8 * 4
     return x * 68
 
 
@@ -753,6 +776,14 @@ def run_sweep(kind, calls):
             pi = torch.empty((G, B, A), device=d)
             us = timed(lambda: m.iql_aw_policy(q, v, G, B, A, 3.0, pi))
             rows.append((B, us, f"B = {B}, A = {A}, {G} trainers (B A = 2^{int(np.log2(B * A))})"))
+    elif kind == "sentinel":
+        flags = torch.zeros(8, dtype=torch.int32, device=d)
+        for n in SWEEP_POINTS[kind]:
+            bufs = [torch.randn(n, generator=gen, device=d) for _ in range(8)]
+            us = timed(lambda: m.nonfinite_check(bufs, flags))
+            rows.append((n, us, f"eight slots of {n} floats ({8 * n * 4 / 2**30:.2f} GiB), all finite"))
+            del bufs
+            torch.cuda.empty_cache()
     elif kind == "copy":
         for n in SWEEP_POINTS[kind]:
             a_, b_ = torch.randn(n, generator=gen, device=d), torch.empty(n, device=d)
@@ -846,12 +877,35 @@ def summarize_sweeps(d):
                 tot.append(_median(per_call) * 1024 * cf[c])
             meas[c] = tot
         names = {"her": "her_relabel", "aw": "iql_aw_policy", "budget": "grad_budget_accumulate + Adam",
-                 "copy": "plain copy (torch)"}
+                 "sentinel": "iqlh_nonfinite_check", "copy": "plain copy (torch)"}
         for i, p in enumerate(pts):
             rd = meas.get("FETCH_SIZE", [float("nan")] * len(pts))[i]
             wr = meas.get("WRITE_SIZE", [float("nan")] * len(pts))[i]
             L.append(f"| {names[kind]} | {p['what']} | {p['us_per_call']:.1f} | {p['bytes_per_call'] / 1e9:.3f} | "
                      f"{rd / 1e9:.3f} | {wr / 1e9:.3f} | {p['GB/s'] / 1e3:.2f} | {100 * p['frac_of_8TBs']:.1f} |")
+    # the passes of a multi-kernel entry point on their own: kernel-trace
+    # durations per dispatch (median over the timed calls of each size)
+    for kind, passes in SWEEP_PASS_BYTES.items():
+        jpath = os.path.join(d, f"sweep_{kind}.json")
+        g = glob.glob(os.path.join(d, f"sweep_{kind}_trace", "*_kernel_trace.csv"))
+        if not os.path.exists(jpath) or not g:
+            continue
+        pts = [json.loads(x) for x in open(jpath) if x.startswith("{")]
+        calls = pts[0]["calls"] + 1 if pts else 1
+        rows = sorted(_csv_rows(g[0]), key=lambda r: int(r["Dispatch_Id"]))
+        L += ["", f"Passes of {names[kind]} on their own (kernel trace of the timing run; bytes per element: "
+              + ", ".join(f"{b} for {k}" for k, _, b in passes) + "):", "",
+              "| pass | size | us per call | needed GB | TB/s on needed bytes | % of 8 TB/s |",
+              "|---|---|---:|---:|---:|---:|"]
+        for kn, what, bpe in passes:
+            durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows if kn in r["Kernel_Name"]]
+            if len(durs) < calls * len(pts):
+                continue
+            for i, p in enumerate(pts):
+                us = _median(durs[i * calls + 1:(i + 1) * calls])
+                by = bpe * p["size"]
+                L.append(f"| {what} | {p['what']} | {us:.1f} | {by / 1e9:.3f} | {by / (us * 1e-6) / 1e12:.2f} | "
+                         f"{100 * by / (us * 1e-6) / 1e9 / PEAK_HBM_GBS:.1f} |")
     md = os.path.join(ROOT, "profiles", "hbm_sweeps.md")
     os.makedirs(os.path.dirname(md), exist_ok=True)
     with open(md, "w") as fh:

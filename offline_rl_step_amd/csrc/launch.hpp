@@ -192,7 +192,7 @@ hipError_t launch_per_sample(const float* p, int64_t size, int n, uint64_t seed,
 
 // ------------------------------------------------- non-finite sentinel
 constexpr int kSentinelSlots = 32;
-constexpr int kSentinelPiece = 4096;  // elements per block
+constexpr int kSentinelPiece = 8192;  // elements per block
 struct SentinelArgs {
     const float* ptr[kSentinelSlots];
     int64_t n[kSentinelSlots];

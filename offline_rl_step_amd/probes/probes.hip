@@ -21,6 +21,12 @@
 //   The three sums are compared bit for bit.
 // xcc_map: the XCC (XCD) each block of a launch runs on, from the hardware
 //   register, for a launch of the forward/backward kernel's shape.
+// stream_sum: sums of squares of four float arrays of n elements (a read-only
+//   streaming reduction, the gradient budget's first pass) with three ways of
+//   cutting the work into 256-thread blocks: a persistent grid of nb blocks
+//   striding over the arrays (block b, thread t takes quads b 256 + t +
+//   i nb 256); the same grid with each block owning one contiguous range;
+//   and one block per 8 KB of each array (no loop).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -146,6 +152,40 @@ __global__ __launch_bounds__(1024) void probe_xcc_kernel(int* out) {
     }
 }
 
+// four arrays, n a multiple of 4 * 256 * nb
+__global__ __launch_bounds__(256) void probe_sum_stride_kernel(const float* const* a, int64_t quads, float* out) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < quads; q += stride) {
+        f4 x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = ((const f4*)a[j])[q];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] += x[j].x * x[j].x + x[j].y * x[j].y + x[j].z * x[j].z + x[j].w * x[j].w;
+    }
+    if (acc[0] + acc[1] + acc[2] + acc[3] == -1.f) out[0] = 1.f;  // keeps the loads
+}
+__global__ __launch_bounds__(256) void probe_sum_chunk_kernel(const float* const* a, int64_t quads, float* out) {
+    const int64_t chunk = quads / gridDim.x, q0 = (int64_t)blockIdx.x * chunk;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t q = q0 + threadIdx.x; q < q0 + chunk; q += 256) {
+        f4 x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = ((const f4*)a[j])[q];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] += x[j].x * x[j].x + x[j].y * x[j].y + x[j].z * x[j].z + x[j].w * x[j].w;
+    }
+    if (acc[0] + acc[1] + acc[2] + acc[3] == -1.f) out[0] = 1.f;
+}
+// one block per 512 quads of one array (blockIdx.y = the array)
+__global__ __launch_bounds__(256) void probe_sum_piece_kernel(const float* const* a, int64_t quads, float* out) {
+    const f4* p = (const f4*)a[blockIdx.y] + (int64_t)blockIdx.x * 512;
+    const f4 x0 = p[threadIdx.x], x1 = p[threadIdx.x + 256];
+    const float acc = x0.x * x0.x + x0.y * x0.y + x0.z * x0.z + x0.w * x0.w + x1.x * x1.x + x1.y * x1.y +
+                      x1.z * x1.z + x1.w * x1.w;
+    if (acc == -1.f) out[0] = 1.f;
+}
+
 #define PCK(x)                                   \
     do {                                         \
         hipError_t e_ = (x);                     \
@@ -230,6 +270,50 @@ int iqlh_probe_team_fold(int reps, double* out_us, int* out_equal, int* out_time
     hipFree(team_rows);
     for (auto& s : sum) hipFree(s);
     hipFree(cnt);
+    return 0;
+}
+
+// out_us[0..2]: mean time of the strided, chunked and per-piece sums of four
+// arrays of n floats (n a multiple of 2^21), each over `reps` back-to-back
+// launches after one warm-up; nb = blocks of the first two.
+int iqlh_probe_stream_sum(int64_t n, int nb, int reps, double* out_us) {
+    if (n < (1 << 21) || (n & ((1 << 21) - 1)) || nb < 1 || nb > 8192 || reps < 1 || !out_us) return -1;
+    const int64_t quads = n / 4;
+    if (quads % ((int64_t)nb * 256) != 0) return -1;
+    float* arr[4] = {nullptr, nullptr, nullptr, nullptr};
+    float* out = nullptr;
+    const float** dptr = nullptr;
+    for (auto& x : arr) {
+        PCK(hipMalloc(&x, sizeof(float) * n));
+        PCK(hipMemset(x, 0, sizeof(float) * n));
+    }
+    PCK(hipMalloc(&out, sizeof(float)));
+    PCK(hipMalloc(&dptr, sizeof(arr)));
+    PCK(hipMemcpy(dptr, arr, sizeof(arr), hipMemcpyHostToDevice));
+    hipEvent_t e0, e1;
+    PCK(hipEventCreate(&e0));
+    PCK(hipEventCreate(&e1));
+    for (int v = 0; v < 3; ++v) {
+        auto launch = [&]() {
+            if (v == 0) hipLaunchKernelGGL(probe_sum_stride_kernel, dim3(nb), dim3(256), 0, 0, dptr, quads, out);
+            else if (v == 1) hipLaunchKernelGGL(probe_sum_chunk_kernel, dim3(nb), dim3(256), 0, 0, dptr, quads, out);
+            else hipLaunchKernelGGL(probe_sum_piece_kernel, dim3((unsigned)(quads / 512), 4), dim3(256), 0, 0, dptr,
+                                    quads, out);
+        };
+        launch();
+        PCK(hipEventRecord(e0, 0));
+        for (int i = 0; i < reps; ++i) launch();
+        PCK(hipEventRecord(e1, 0));
+        PCK(hipEventSynchronize(e1));
+        float ms = 0.f;
+        PCK(hipEventElapsedTime(&ms, e0, e1));
+        out_us[v] = 1e3 * ms / reps;
+    }
+    hipEventDestroy(e0);
+    hipEventDestroy(e1);
+    for (auto& x : arr) hipFree(x);
+    hipFree(out);
+    hipFree(dptr);
     return 0;
 }
 

@@ -46,6 +46,27 @@ def test_slots_match_oracle(m):
     assert list(ref) == [0, 1, 1, 1, 0, 0, 0, 1]
 
 
+def test_piece_edges(m):
+    """Special values at the edges of the kernel's 8192-element pieces: the
+    last element of a whole piece, the first of the next whole piece, the
+    first and last of a slot's partial last piece, and a clean slot of
+    whole pieces only."""
+    g = np.random.default_rng(5)
+    P = 8192
+    cases = []
+    for n, pos, val in ((P, P - 1, np.nan), (3 * P, P, np.inf), (2 * P + 5, 2 * P, -np.inf),
+                        (2 * P + 5, 2 * P + 4, np.nan), (4 * P, None, None)):
+        x = g.standard_normal(n).astype(np.float32)
+        if pos is not None:
+            x[pos] = val
+        cases.append(x)
+    init = [0] * len(cases)
+    got = _flags(m, [to_dev(x) for x in cases], init)
+    ref = sentinel.update_flags(init, cases)
+    assert np.array_equal(got, ref), (got, ref)
+    assert list(ref) == [1, 1, 1, 1, 0]
+
+
 def test_flags_are_sticky(m):
     clean = to_dev(np.ones(300, np.float32))
     got = _flags(m, [clean, clean, None], [1, 0, 1])
