@@ -71,6 +71,10 @@ def parse():
                         "separate summing launch), xcc-map (the XCD of each block of a launch of the "
                         "forward/backward kernel's shape), stream-sum (a read-only four-array sum of squares "
                         "of 1 GiB cut into blocks three ways)")
+    p.add_argument("--phases", action="store_true",
+                   help="only run the headline step through iql_aux_step_phase_stamps and print one JSON line: "
+                        "the forward/backward kernel's phase durations per workgroup (median over steps and "
+                        "workgroups, HER tiles and plain tiles apart)")
     p.add_argument("--sweep", choices=("her", "aw", "budget", "sentinel", "copy"), default=None,
                    help="only time one HBM-bound entry point on working sets of at least 1 GiB (her_relabel over "
                         "a 2^22-row replay buffer, iql_aw_policy up to B*A = 2^26 for two trainers, "
@@ -141,6 +145,47 @@ def run_probe(name, reps=50):
         out = {"probe": name, "blocks": blocks, "threads": 1024, "lds_bytes": lds,
                "block_i_on_xcc_i_mod_8": all(x == i % 8 for i, x in enumerate(got)),
                "blocks_per_xcc": [got.count(k) for k in range(8)], "xcc_of_first_16": got[:16]}
+    print(json.dumps(out), flush=True)
+
+
+PHASE_NAMES = ("S0 staging (HER relabelling, budget pass 1)", "F1", "F2 + V", "loss, dz2",
+               "dW2 + W2^T + policy", "dh1, dz1", "dW1 (stores issued)")
+
+
+def run_phases(steps, warmup):
+    """Phase durations of the forward/backward kernel of the headline step,
+    from the 100 MHz clock values each workgroup's thread 0 records at its
+    phase ends (iql_aux_step_phase_stamps)."""
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    import offline_rl_step_amd as m
+    import synth
+    w = synth.WORKLOADS[synth.BENCH_WORKLOAD]
+    ctx = Context(m, w, torch, np, synth)
+    ntile = (w.B + 127) // 128
+    stamps = torch.zeros(w.groups * ntile * m.PHASE_STAMPS, dtype=torch.int64, device=ctx.d)
+    for _ in range(warmup):
+        ctx.step()
+    runs = []
+    for _ in range(steps):
+        ctx.tr.aux_step_phase_stamps(ctx.her_step, ctx.X, ctx.q, w.B, ctx.Q, w.A, w.beta, ctx.pi, ctx.out_v,
+                                     ctx.out_loss, ctx.out_gn, ctx.budget_step, stamps)
+        torch.cuda.synchronize()
+        runs.append(stamps.cpu().numpy().reshape(w.groups, ntile, m.PHASE_STAMPS).astype(np.int64))
+    st = np.stack(runs)  # [steps][G][tile][8], 10 ns ticks
+    her_tile = np.arange(ntile) >= (w.B - w.n_her) // 128
+    dur = np.diff(st, axis=3) * 1e-2  # us
+    rel_end = (st[..., -1] - st[..., 0].min(axis=(1, 2), keepdims=True)) * 1e-2
+    out = {"probe": "phases", "workload": w.name, "steps": steps, "tiles": ntile, "groups": w.groups,
+           "her_tiles": int(her_tile.sum()), "clock": "s_memrealtime, 100 MHz, thread 0 of each workgroup"}
+    for name, sel in (("plain", ~her_tile), ("her", her_tile)):
+        d = dur[:, :, sel, :].reshape(-1, m.PHASE_STAMPS - 1)
+        out[name] = {"phase_us_median": {PHASE_NAMES[k]: float(np.median(d[:, k])) for k in range(len(PHASE_NAMES))},
+                     "span_us_median": float(np.median(d.sum(axis=1))),
+                     "end_after_first_start_us_median": float(np.median(rel_end[:, :, sel])),
+                     "end_after_first_start_us_max": float(rel_end[:, :, sel].max())}
+    out["kernel_event_us"] = ctx.time_launches(50)[1]
     print(json.dumps(out), flush=True)
 
 
@@ -972,6 +1017,9 @@ def main():
         return
     if a.probe:
         run_probe(a.probe)
+        return
+    if a.phases:
+        run_phases(min(a.steps, 200), a.warmup)
         return
     if a.gpus != 1:
         print(f"bench.py measures one GPU: the step has no cross-GPU exchange, so --gpus {a.gpus} "

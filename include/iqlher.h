@@ -415,6 +415,23 @@ int iql_time_aux_step(iql_handle h, const iqlh_her_step* her, const void* states
                       float* out_loss, float* out_grad_norm, const iqlh_budget_step* budget,
                       int32_t reps, float* out_avg_us, void* stream);
 
+/* Measurement aid: iql_aux_step (same arguments, same results, bit for
+ * bit) with the forward/backward launch run by an instantiation of its
+ * kernel that also records, per workgroup, the 100 MHz clock at the ends of
+ * its phases: d_stamps device [groups][ceil(batch / 128)][8] uint64 (tile
+ * order, the layout of the gradient partials): kernel start, then the ends
+ * of the staging of weights and rows (with the HER relabelling and the
+ * budget's pass 1 when the launch hosts them), F1, F2 + V, loss / dz2,
+ * dW2 (+ W2^T and the policy), dh1 / dz1, and the issue of the last dW1
+ * partial stores.  stamps_len = elements available.  Only for the kernel
+ * of bf16 trainers at hidden 128 (IQLH_ESHAPE otherwise). */
+int iql_aux_step_phase_stamps(iql_handle h, const iqlh_her_step* her, const void* states,
+                              const float* q_taken, int32_t batch, const float* q_all,
+                              int32_t num_actions, float beta, float* out_pi, float* out_v,
+                              float* out_loss, float* out_grad_norm,
+                              const iqlh_budget_step* budget, uint64_t* d_stamps,
+                              int32_t stamps_len, void* stream);
+
 /* ------------------------------------------------------------------------
  * Prioritized-replay source sampling ([P1] "Current State": the GPU PER
  * buffer samples by a prefix sum of the priorities and a search in it and

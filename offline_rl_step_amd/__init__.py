@@ -114,6 +114,9 @@ _lib_iql_aux_step = _sig("iql_aux_step", _i32, [_p, ctypes.POINTER(HerStep), _p,
 _lib_iql_time_aux_step = _sig("iql_time_aux_step", _i32, [_p, ctypes.POINTER(HerStep), _p, _p, _i32, _p, _i32, _f,
                                                           _p, _p, _p, _p, ctypes.POINTER(BudgetStep), _i32,
                                                           ctypes.POINTER(_f), _p])
+_lib_iql_aux_step_phase_stamps = _sig("iql_aux_step_phase_stamps", _i32,
+                                      [_p, ctypes.POINTER(HerStep), _p, _p, _i32, _p, _i32, _f, _p, _p, _p, _p,
+                                       ctypes.POINTER(BudgetStep), _p, _i32, _p])
 _lib_per_ws = _sig("per_workspace_bytes", _i32, [_i64, ctypes.POINTER(ctypes.c_size_t)])
 _lib_per_sample = _sig("per_sample_indices", _i32, [_p, _i64, _i32, _u64, _p, _f, _p, _p, _p, _p, ctypes.c_size_t, _p])
 _lib_nonfinite_check = _sig("iqlh_nonfinite_check", _i32, [ctypes.POINTER(_p), ctypes.POINTER(_i64), _i32, _p, _p])
@@ -456,6 +459,21 @@ def iql_time_aux_step(h, her, states, q_taken, batch, q_all=None, num_actions=0,
     return list(out)
 
 
+PHASE_STAMPS = 8  # clock values per workgroup recorded by iql_aux_step_phase_stamps
+
+
+def iql_aux_step_phase_stamps(h, her, states, q_taken, batch, q_all, num_actions, beta, out_pi, out_v, out_loss,
+                              out_grad_norm, budget, stamps, stream=None):
+    """iql_aux_step with the forward/backward kernel's phase ends recorded:
+    `stamps` is a device int64 tensor of groups * ceil(batch / 128) *
+    PHASE_STAMPS elements (100 MHz clock values, tile order)."""
+    _check(_lib_iql_aux_step_phase_stamps(h, None if her is None else ctypes.byref(her), _ptr(states),
+                                          _ptr(q_taken), batch, _ptr(q_all), num_actions, beta, _ptr(out_pi),
+                                          _ptr(out_v), _ptr(out_loss), _ptr(out_grad_norm),
+                                          None if budget is None else ctypes.byref(budget), _ptr(stamps),
+                                          stamps.numel(), _stream(stream)), "iql_aux_step_phase_stamps")
+
+
 class IqlTrainer:
     """Owns an iql_handle; methods forward to the C entry points."""
 
@@ -500,6 +518,11 @@ class IqlTrainer:
                       out_v=None, out_loss=None, out_grad_norm=None, budget=None, reps=100, stream=None):
         return iql_time_aux_step(self.h, her, states, q_taken, batch, q_all, num_actions, beta, out_pi, out_v,
                                  out_loss, out_grad_norm, budget, reps, stream)
+
+    def aux_step_phase_stamps(self, her, states, q_taken, batch, q_all, num_actions, beta, out_pi, out_v, out_loss,
+                              out_grad_norm, budget, stamps, stream=None):
+        iql_aux_step_phase_stamps(self.h, her, states, q_taken, batch, q_all, num_actions, beta, out_pi, out_v,
+                                  out_loss, out_grad_norm, budget, stamps, stream)
 
     def compute_gradients(self, states, q_taken, batch, out_v=None, stream=None):
         iql_compute_gradients(self.h, states, q_taken, batch, out_v, stream)

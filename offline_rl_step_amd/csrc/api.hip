@@ -730,4 +730,25 @@ int iql_time_aux_step(iql_handle h, const iqlh_her_step* her, const void* states
     return IQLH_OK;
 }
 
+int iql_aux_step_phase_stamps(iql_handle h, const iqlh_her_step* her, const void* states, const float* q_taken,
+                              int32_t batch, const float* q_all, int32_t num_actions, float beta, float* out_pi,
+                              float* out_v, float* out_loss, float* out_grad_norm, const iqlh_budget_step* budget,
+                              uint64_t* d_stamps, int32_t stamps_len, void* stream) {
+    AuxPlan p;
+    int rc = plan_aux_step(h, her, states, q_taken, batch, q_all, num_actions, beta, out_pi, out_v, budget, &p);
+    if (rc) return rc;
+    if (!d_stamps) return fail(IQLH_EINVAL, "iql_aux_step_phase_stamps: d_stamps is NULL");
+    if (!iql_runs_fused16w(h->dims))
+        return fail(IQLH_ESHAPE, "iql_aux_step_phase_stamps: phase ends are recorded by the bf16 hidden-128 kernel only");
+    const int64_t need = (int64_t)h->dims.G * ((batch + 127) / 128) * kPhaseStamps;
+    if (stamps_len < need)
+        return fail(IQLH_EINVAL, "iql_aux_step_phase_stamps: stamps_len %d < %lld", stamps_len, (long long)need);
+    hipError_t e = launch_aux_step(h->dims, h->buf, adam_hyper(h), h->cfg.tau, p.her ? &p.ha : nullptr, states,
+                                   h->cfg.states_ld, q_taken, batch, q_all, num_actions, beta, out_pi, out_v,
+                                   out_loss, out_grad_norm, p.budget ? &p.ba : nullptr, (hipStream_t)stream, nullptr,
+                                   nullptr, d_stamps);
+    if (e != hipSuccess) return hip_fail(e, "iql_aux_step_phase_stamps launch");
+    return IQLH_OK;
+}
+
 }  // extern "C"

@@ -198,6 +198,9 @@ struct FusedArgs {
     // fp32 four-wave kernel only: two workgroups per tile, workgroup 2 t
     // forming tile t's dW2 part of the partial row and 2 t + 1 its dW1 part
     int fs_split;
+    // 16-wave kernel only, measurement: [G][nwg][kPhaseStamps] clock values
+    // (100 MHz) at the workgroup's phase ends, or null (not recorded)
+    uint64_t* stamps;
 };
 
 template <typename T, int SP, int H, int NW>
@@ -1104,7 +1107,16 @@ struct Fused16wCfg {
     static_assert(R3 * 2 >= BT * kHerGoalLds * 4 + BT * 4, "HER goals staged in R3");
 };
 
-template <int SP, int H, bool XVEC>
+// Thread 0's clock value at a phase end of a 16-wave workgroup (the
+// instantiation that records them is used only for measurement).
+template <bool ON>
+IQLH_DEV void phase_stamp(uint64_t* row, int k) {
+    if constexpr (ON) {
+        if (threadIdx.x == 0) row[k] = __builtin_amdgcn_s_memrealtime();
+    }
+}
+
+template <int SP, int H, bool XVEC, bool STAMPS = false>
 __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
     typedef Fused16wCfg<SP, H> C;
     constexpr int NW = 16, BT = 128, FT = H / 32, KU1 = SP / 32, KUH = H / 32, NTHR = 1024;
@@ -1142,6 +1154,8 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
         g = __builtin_amdgcn_readfirstlane(g);
         wg = __builtin_amdgcn_readfirstlane(wg);
     }
+    uint64_t* const stamp_row = STAMPS ? a.stamps + ((int64_t)g * a.nwg + wg) * kPhaseStamps : nullptr;
+    phase_stamp<STAMPS>(stamp_row, 0);
     const int S = a.S, B = a.B;
     const POff po(S, H);
     const float* prm = a.params + (int64_t)g * a.P;
@@ -1398,6 +1412,7 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
         *(u32x4*)(R2 + nat_off(sr, k0)) = xr[k];
     }
     lds_barrier();
+    phase_stamp<STAMPS>(stamp_row, 1);
     // the quarter's budget partials: its four wave sums added in block_sum_k's order
     if (nblk < a.nrm.nb && (tid & 255) == 0) {
 #pragma unroll
@@ -1434,6 +1449,7 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
         put4(R3, bl, fb + 16 * t + 4 * q, acc[t][0], acc[t][1], acc[t][2], acc[t][3]);  // h1
     }
     lds_barrier();
+    phase_stamp<STAMPS>(stamp_row, 2);
 
     // ---- F2: z2^T = W2 h1^T + b2, V = w3 . relu(z2) + b3 over both halves
 #pragma unroll
@@ -1456,6 +1472,7 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
     vpart = sum_q4(vpart);
     if (q == 0) svh[fh * BT + bl] = vpart;
     lds_barrier();
+    phase_stamp<STAMPS>(stamp_row, 3);
     const float v = (svh[bl] + svh[BT + bl]) + b3;
     if (a.fwd_only) {
         if (valid && fh == 0 && q == 0) write_value(a.vo, g, B, b, v);
@@ -1495,6 +1512,7 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
     // lane l16 ends with the sample-group sum of value l16
     sdw3[sg * H + fb + 16 * (l16 >> 2) + 4 * q + (l16 & 3)] = row_sum16_scatter(hv);
     lds_barrier();
+    phase_stamp<STAMPS>(stamp_row, 4);
 
     // ---- W2^T to R1 (W2 is dead); loss, db3, dw3; dW2 = dz2^T h1 with db2
     {
@@ -1551,6 +1569,7 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
         }
     }
     lds_barrier();
+    phase_stamp<STAMPS>(stamp_row, 5);
 
     // ---- B1: dh1^T = W2^T dz2^T for this wave's features; dz1 -> R3 (h1 is dead)
 #pragma unroll
@@ -1571,9 +1590,11 @@ __global__ __launch_bounds__(1024) void iql_fused16w_kernel(FusedArgs a) {
         put4(R3, bl, fb + 16 * t + 4 * q, d[0], d[1], d[2], d[3]);
     }
     lds_barrier();
+    phase_stamp<STAMPS>(stamp_row, 6);
 
     // ---- dW1 = dz1^T s with db1
     nat_gemm16_part<SP / 32>(R3, R2, sg, (SP / 32) * fh, part + po.w1, S, S, fh == 0 ? part + po.b1 : nullptr);
+    phase_stamp<STAMPS>(stamp_row, 7);
 }
 
 template <int SP, int H, bool XVEC>
@@ -1584,8 +1605,16 @@ static hipError_t run_fused16w_x(const FusedArgs& fa, int G, hipStream_t stream,
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)iql_fused16w_kernel<SP, H, XVEC>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::BYTES);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute((const void*)iql_fused16w_kernel<SP, H, XVEC, true>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::BYTES);
         if (e != hipSuccess) return e;
         attr_set = true;
+    }
+    if (fa.stamps) {  // measurement: the instantiation that records phase ends
+        hipLaunchKernelGGL((iql_fused16w_kernel<SP, H, XVEC, true>), dim3(fa.nwg, G), dim3(1024), C::BYTES, stream,
+                           fa);
+        return hipGetLastError();
     }
     if (ev0)
         hipExtLaunchKernelGGL((iql_fused16w_kernel<SP, H, XVEC>), dim3(fa.nwg, G), dim3(1024), C::BYTES, stream,
@@ -1707,6 +1736,7 @@ bool iql_fused_policy(const IqlDims& d, int A) {
 
 // The shapes that run iql_fused16w_kernel (bf16, hidden 128, state <= 128).
 static bool is_fused16w(const IqlDims& d) { return !d.layered && d.dtype == 1 && d.H == 128 && d.S <= 128; }
+bool iql_runs_fused16w(const IqlDims& d) { return is_fused16w(d); }
 
 // HER rows the forward/backward launch can relabel itself: the batch tail
 // from a 128-row boundary, bf16, rows of whole 16-byte-aligned 8-float chunks,
@@ -1731,7 +1761,7 @@ hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float
                               const void* states, int64_t ld, const float* q, int B, float* out_v,
                               hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1,
                               const float* q_all, int A, float beta, float* out_pi, const HerArgs* her,
-                              const NormsArgs* nrm) {
+                              const NormsArgs* nrm, uint64_t* stamps) {
     if (d.layered) {
         if (ev0) (void)hipEventRecord(ev0, stream);
         hipError_t e = d.big ? launch_iql_big_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream)
@@ -1758,6 +1788,10 @@ hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float
     if (nrm) {
         if (!iql_fused_norms_ok(d, B, her ? her->n : 0, nrm->nb)) return hipErrorInvalidValue;
         fa.nrm = *nrm;
+    }
+    if (stamps) {
+        if (!is_fused16w(d)) return hipErrorInvalidValue;
+        fa.stamps = stamps;
     }
     return var->fn(fa, d.G, stream, ev0, ev1);
 }

@@ -147,7 +147,15 @@ hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float
                               float* out_v, hipStream_t stream, hipEvent_t ev0 = nullptr,
                               hipEvent_t ev1 = nullptr, const float* q_all = nullptr, int A = 0,
                               float beta = 0.f, float* out_pi = nullptr, const HerArgs* her = nullptr,
-                              const NormsArgs* nrm = nullptr);
+                              const NormsArgs* nrm = nullptr, uint64_t* stamps = nullptr);
+// Phase ends recorded per workgroup by the 16-wave kernel for measurement
+// (launch_iql_fwd_bwd's `stamps`, [G][nwg][kPhaseStamps]): kernel start, the
+// ends of the staging (S0), F1, F2 + V, loss / dz2, dW2 (+ W2^T, policy) and
+// dh1 / dz1 phases, and the issue of the last dW1 partial stores.
+constexpr int kPhaseStamps = 8;
+// The forward/backward launch runs the 16-wave kernel (bf16, hidden 128,
+// state <= 128), the one that can record phase ends.
+bool iql_runs_fused16w(const IqlDims& d);
 bool iql_fused_policy(const IqlDims& d, int A);
 bool iql_fused_her_ok(const IqlDims& d, const HerArgs& her, const void* states, int64_t ld, int B);
 bool iql_fused_norms_ok(const IqlDims& d, int B, int her_rows, int nb);
@@ -229,7 +237,7 @@ hipError_t launch_aux_step(const IqlDims& d, const IqlBuffers& b, const AdamHype
                            const HerArgs* her, const void* states, int64_t ld, const float* q, int B,
                            const float* q_all, int A, float beta, float* out_pi, float* out_v,
                            float* out_loss, float* out_gnorm, const BudgetArgs* budget, hipStream_t stream,
-                           hipEvent_t* ev = nullptr, bool* ran_a = nullptr);
+                           hipEvent_t* ev = nullptr, bool* ran_a = nullptr, uint64_t* stamps = nullptr);
 // ev (optional): 8 events, start/stop of launches A, B, C, D (A's are not
 // recorded when A is not needed: its HER rows and budget norms both ride in
 // B).  ran_a (optional) receives whether A was launched.

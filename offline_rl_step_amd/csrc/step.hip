@@ -123,7 +123,7 @@ hipError_t launch_aux_step(const IqlDims& d, const IqlBuffers& b, const AdamHype
                            const HerArgs* her, const void* states, int64_t ld, const float* q, int B,
                            const float* q_all, int A, float beta, float* out_pi, float* out_v,
                            float* out_loss, float* out_gnorm, const BudgetArgs* bud, hipStream_t stream,
-                           hipEvent_t* ev, bool* ran_a) {
+                           hipEvent_t* ev, bool* ran_a, uint64_t* stamps) {
     int nwg, nloss;
     if (!iql_partial_counts(d, B, &nwg, &nloss)) return hipErrorInvalidValue;
     const int nb = bud ? budget_num_blocks(bud->n) : 0;
@@ -166,10 +166,11 @@ hipError_t launch_aux_step(const IqlDims& d, const IqlBuffers& b, const AdamHype
     const HerArgs* hb = her_in_b ? her : nullptr;
     const NormsArgs* nbp = norms_in_b ? &np : nullptr;
     if (fused_pi) {
-        e = launch_iql_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream, e0, e1, q_all, A, beta, out_pi, hb, nbp);
+        e = launch_iql_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream, e0, e1, q_all, A, beta, out_pi, hb, nbp,
+                               stamps);
     } else {
         e = launch_iql_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream, e0, e1, nullptr, 0, 0.f, nullptr, hb,
-                               nbp);
+                               nbp, stamps);
         if (e == hipSuccess && q_all) e = launch_aw_policy(q_all, out_v, d.G, B, A, beta, out_pi, stream);
     }
     if (e != hipSuccess) return e;
