@@ -19,9 +19,12 @@
 // then the fixed-order partial reduction and Adam shared with the other
 // paths (no float atomics anywhere).
 //
-// MI355X design.  Every product runs on v_mfma_f32_16x16x32_bf16 with a
-// 128 x 128 output tile per wave (8 x 8 MFMA tiles, 256 accumulators), four
-// waves per workgroup and one workgroup per CU.  Operands stream HBM -> LDS
+// MI355X design.  Every product runs on v_mfma_f32_16x16x32_bf16.  fwd1 and
+// wgrad hold a 128 x 128 output tile per wave (8 x 8 MFMA tiles, 256
+// accumulators), four waves per workgroup and one workgroup per CU; fwd2
+// splits its H x 128 tile over eight waves (two per SIMD, H / 8 features
+// each), so that one wave's dependent epilogue arithmetic and LDS round
+// trips overlap the other's.  Operands stream HBM -> LDS
 // with global_load_lds_dwordx4 (no register staging) through a ring of 32-k
 // stages; each stage ends in one s_barrier after the wave's own vmcnt wait,
 // and the fragments of the next stage are read from LDS while the current
@@ -57,6 +60,7 @@ typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 constexpr int kBK = 32;           // k per stage
 constexpr int kFwd2Samples = 128; // samples per fwd2 block (the loss blocks)
+constexpr int kFwd2Waves = 8;     // waves of a fwd2 workgroup (two per SIMD)
 constexpr int kTile = 256;        // fwd1 / wgrad output tile edge
 constexpr int kTileStages = 5;    // ring depth of fwd1 (5 x 32 KB)
 constexpr int kWgradStages = 5;   // ring depth of wgrad (5 x 32 KB)
@@ -216,17 +220,17 @@ IQLH_DEV void reads_then_mfma() {
 // Rows [0, R) of a row-major operand (k contiguous), k in [k0, k0 + 32):
 // LDS chunk c (16 bytes) holds row c >> 2, k unit (c & 3) ^ ((row >> 1) & 3).
 // Rows at or past rmax re-read row rmax - 1 (their products are discarded).
-template <int R>
+template <int R, int NT = kThreads>
 IQLH_DEV void dma_kc(const uint16_t* g, int64_t ld, int rmax, int k0, uint16_t* lds) {
-    static_assert((R * 4) % kThreads == 0, "chunks per thread");
+    static_assert((R * 4) % NT == 0, "chunks per thread");
     const int tid = threadIdx.x, wbase = tid & ~63;
 #pragma unroll
-    for (int i = 0; i < R * 4 / kThreads; ++i) {
-        const int c = i * kThreads + tid;
+    for (int i = 0; i < R * 4 / NT; ++i) {
+        const int c = i * NT + tid;
         const int r = c >> 2, u = (c & 3) ^ ((r >> 1) & 3);
         const int gr = r < rmax ? r : rmax - 1;
         __builtin_amdgcn_global_load_lds((const void*)(g + (int64_t)gr * ld + k0 + 8 * u),
-                                         IQLH_LDS(lds + (i * kThreads + wbase) * 8), 16, 0, 0);
+                                         IQLH_LDS(lds + (i * NT + wbase) * 8), 16, 0, 0);
     }
 }
 // this lane's element offset of its fragment in row tile 0 of a K-contiguous
@@ -299,11 +303,11 @@ IQLH_DEV int stage_off(int s, int f) { return s * NF + ((((f >> 3) ^ (s & 7)) <<
 
 // Rows [0, ns) of the staged tile to dst rows (row stride ld), columns
 // [0, NF).
-template <int NF, int NS>
+template <int NF, int NS, int NT = kThreads>
 IQLH_DEV void stage_out(const uint16_t* lds, uint16_t* dst, int64_t ld, int ns) {
     constexpr int UPR = NF / 8;  // 16-byte units per row
 #pragma unroll 4
-    for (int c = threadIdx.x; c < NS * UPR; c += kThreads) {
+    for (int c = threadIdx.x; c < NS * UPR; c += NT) {
         const int r = c / UPR, u = c - r * UPR;
         if (r >= ns) break;
         *(u32x4*)(dst + (int64_t)r * ld + 8 * u) = *(const u32x4*)(lds + r * NF + ((u ^ (r & 7)) << 3));
@@ -460,15 +464,15 @@ __global__ __launch_bounds__(kThreads) void big_fwd1_kernel(BigArgs a) {
 
 // ------------------------------------------------- dh1 inside fwd2's workgroup
 // dh1[f][s] = sum_k W2^T[f][k] dz2[s][k] for the H features of this wave's
-// rows ((H / 4) w + 16 i + ..) and the block's 128 samples, K = H.  The B
+// rows ((H / NW) w + 16 i + .., NW waves) and the block's 128 samples, K = H.  The B
 // operand is the dz2 tile staged in LDS ([sample][feature], 16-byte unit u of
 // row s at u ^ (s & 7)); the A operand comes from the W2^T shadow in global
 // memory (L2-resident after the first blocks), 16 bytes per lane, loaded one
 // k-step ahead.  Then dz1 = dh1 relu'(z1) from fwd1's mask bits, the block's
 // db1 sums from dz1 as stored, and dz1 staged and stored as whole rows.
-template <int H, int MT>
+template <int H, int NW>
 IQLH_DEV const uint16_t* w2t_lane(const BigArgs& a, int g, int wv, int l16, int q) {
-    return a.w2ts + (int64_t)g * H * H + (int64_t)((H / 4) * wv + l16) * H + 8 * q;
+    return a.w2ts + (int64_t)g * H * H + (int64_t)((H / NW) * wv + l16) * H + 8 * q;
 }
 // the first k-step's W2^T fragments (issued before the dz2 stores, so that
 // waiting for them does not wait for the stores)
@@ -477,18 +481,19 @@ IQLH_DEV void w2t_frags(const uint16_t* At, int kt, bf16x8 (&f)[MT]) {
 #pragma unroll
     for (int i = 0; i < MT; ++i) f[i] = *(const bf16x8*)(At + (int64_t)16 * i * H + kBK * kt);
 }
-template <int H, int MT>
+template <int H, int MT, int NW>
 IQLH_DEV void backward_h1(const BigArgs& a, uint16_t* smem, f4 (&acc)[MT][8], bf16x8 (&fa0)[MT], int g, int blk,
                           int s0, int srows, int wv, int l, int l16, int q, int krot) {
     constexpr int NK = H / kBK;
     static_assert(NK % 2 == 0, "k-steps in pairs");
-    const uint16_t* At = w2t_lane<H, MT>(a, g, wv, l16, q);
+    static_assert(MT * 16 * NW == H, "row tiles");
+    const uint16_t* At = w2t_lane<H, NW>(a, g, wv, l16, q);
     // this lane's mask words: fwd1 tile (s0 / 256, f / 256), lane
     // 64 (wm + 2 wn) + l with wn = the block's half of its 256-sample tile
     uint32_t mb[MT];
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-        const int f = (H / 4) * wv + 16 * i;
+        const int f = (H / NW) * wv + 16 * i;
         const int ft = f / kTile, wm = (f % kTile) / 128, word = (f % 128) / 16;
         mb[i] = a.mask[mask_word0(a, g, s0 / kTile, ft, 64 * (wm + 2 * (blk & 1)) + l) + word];
     }
@@ -521,7 +526,7 @@ IQLH_DEV void backward_h1(const BigArgs& a, uint16_t* smem, f4 (&acc)[MT][8], bf
     float* db1 = a.spart + ((int64_t)g * a.nblk + blk) * spart_w(H) + 2 * H + 1;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-        const int f = (H / 4) * wv + 16 * i + 4 * q;
+        const int f = (H / NW) * wv + 16 * i + 4 * q;
         float cs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -546,20 +551,32 @@ IQLH_DEV void backward_h1(const BigArgs& a, uint16_t* smem, f4 (&acc)[MT][8], bf
         }
     }
     __syncthreads();
-    stage_out<H, kFwd2Samples>(smem, a.dz1 + ((int64_t)g * a.B + s0) * H, H, srows);
+    stage_out<H, kFwd2Samples, 64 * NW>(smem, a.dz1 + ((int64_t)g * a.B + s0) * H, H, srows);
+}
+
+// v's partial dot products of the NW waves for sample sl, added pairwise in a
+// fixed order
+template <int NW>
+IQLH_DEV float wave_parts_sum(const float* svp, int sl) {
+    static_assert(NW == 4 || NW == 8, "waves");
+    const float a = (svp[sl] + svp[kFwd2Samples + sl]) + (svp[2 * kFwd2Samples + sl] + svp[3 * kFwd2Samples + sl]);
+    if constexpr (NW == 4) return a;
+    const float b = (svp[4 * kFwd2Samples + sl] + svp[5 * kFwd2Samples + sl]) +
+                    (svp[6 * kFwd2Samples + sl] + svp[7 * kFwd2Samples + sl]);
+    return a + b;
 }
 
 // --------------------------------------------------------------- fwd2
 // All H features of 128 samples: z2 = W2 h1 + b2 and the loss epilogue.
-// Wave w owns features (H / 4) w .. + H / 4 - 1 (MT row tiles of 16).
+// Wave w of NW owns features (H / NW) w .. + H / NW - 1 (MT row tiles of 16).
 // With BWD, the same workgroup then forms dh1 = W2^T dz2 for its samples from
 // the dz2 tile still staged in LDS, and dz1 = dh1 relu'(z1) with the block's
 // db1 sums, so dz2 is never read back from memory for it.
-template <int H, bool BWD>
-__global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
+template <int H, bool BWD, int NW>
+__global__ __launch_bounds__(64 * NW) void big_fwd2_kernel(BigArgs a) {
     extern __shared__ __align__(16) uint16_t smem[];
-    constexpr int MT = H / 64, NST = 3, STG = (H + kFwd2Samples) * kBK;
-    constexpr int LPT = (H + kFwd2Samples) * 4 / kThreads;
+    constexpr int NT = 64 * NW, MT = H / (16 * NW), NST = 3, STG = (H + kFwd2Samples) * kBK;
+    constexpr int LPT = (H + kFwd2Samples) * 4 / NT;
     const int g = blockIdx.y, blk = blockIdx.x;
     const int B = a.B, s0 = blk * kFwd2Samples;
     const uint16_t* A = a.w2s + (int64_t)g * H * H;
@@ -568,8 +585,8 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lo = kc_lane();
     constexpr int RING = NST * STG, STAGE = kFwd2Samples * H;
-    float* svp = (float*)(smem + (RING > STAGE ? RING : STAGE));  // [4][128] V partials of each wave
-    float* sq = svp + 4 * kFwd2Samples;                             // [128] q of the block's samples
+    float* svp = (float*)(smem + (RING > STAGE ? RING : STAGE));  // [NW][128] V partials of each wave
+    float* sq = svp + NW * kFwd2Samples;                            // [128] q of the block's samples
     float* sb2 = sq + kFwd2Samples;                                 // [H] b2
     float* sw3 = sb2 + H;                                           // [H] w3
     const float* prm = a.params + (int64_t)g * a.P;
@@ -578,7 +595,7 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
     auto pre = [&] {
         const int t = threadIdx.x;
         if (t < kFwd2Samples) sq[t] = (!a.fwd_only && t < srows) ? a.q[s0 + t] : 0.f;
-        for (int f = t; f < H; f += kThreads) {
+        for (int f = t; f < H; f += NT) {
             sb2[f] = prm[a.off_b2 + f];
             sw3[f] = prm[a.off_w3 + f];
         }
@@ -595,13 +612,13 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
     auto issue = [&](int s, int buf) {
         uint16_t* st_ = smem + buf * STG;
         const int k0 = ((s + krot) & (H / kBK - 1)) * kBK;
-        dma_kc<H>(A, H, H, k0, st_);
-        dma_kc<kFwd2Samples>(Bm, H, srows, k0, st_ + H * kBK);
+        dma_kc<H, NT>(A, H, H, k0, st_);
+        dma_kc<kFwd2Samples, NT>(Bm, H, srows, k0, st_ + H * kBK);
     };
     if constexpr (H == 512) {
         // no registers for a second fragment set next to this epilogue
         kloop1<NST, LPT>(H / kBK, issue, [&](int buf) {
-            const uint16_t* ta = smem + buf * STG + ((H / 4) * wv) * kBK + lo;
+            const uint16_t* ta = smem + buf * STG + ((H / NW) * wv) * kBK + lo;
             const uint16_t* tb = smem + buf * STG + H * kBK + lo;
             bf16x8 fa[MT], fb[8];
 #pragma unroll
@@ -620,7 +637,7 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
             H / kBK, issue,
             [&](int buf, auto p) {
                 constexpr int P = decltype(p)::value;
-                const uint16_t* ta = smem + buf * STG + ((H / 4) * wv) * kBK + lo;
+                const uint16_t* ta = smem + buf * STG + ((H / NW) * wv) * kBK + lo;
                 const uint16_t* tb = smem + buf * STG + H * kBK + lo;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) fb[P][j] = *(const bf16x8*)(tb + j * 16 * kBK);
@@ -639,7 +656,7 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
     }
 
     const int l = threadIdx.x & 63, l16 = l & 15, q = l >> 4;
-    const int fb0 = (H / 4) * wv + 4 * q;
+    const int fb0 = (H / NW) * wv + 4 * q;
     // z2 = acc + b2 (formed again in each pass below, so the accumulators
     // are only read); this wave's part of v for each of its 8 samples
     float vp[8];
@@ -670,8 +687,7 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int sl = 16 * j + l16, s = s0 + sl;
-                const float v = ((svp[sl] + svp[kFwd2Samples + sl]) +
-                                 (svp[2 * kFwd2Samples + sl] + svp[3 * kFwd2Samples + sl])) + b3;
+                const float v = wave_parts_sum<NW>(svp, sl) + b3;
                 if (s < B) write_value(a.vo, g, B, s, v);
             }
         }
@@ -682,7 +698,7 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int sl = 16 * j + l16, s = s0 + sl;
-        const float v = ((svp[sl] + svp[kFwd2Samples + sl]) + (svp[2 * kFwd2Samples + sl] + svp[3 * kFwd2Samples + sl])) + b3;
+        const float v = wave_parts_sum<NW>(svp, sl) + b3;
         dv[j] = 0.f;
         if (s < B) {
             const float diff = sq[sl] - v;
@@ -742,10 +758,10 @@ __global__ __launch_bounds__(kThreads) void big_fwd2_kernel(BigArgs a) {
         }
     }
     bf16x8 fa0[MT];
-    if constexpr (BWD) w2t_frags<H, MT>(w2t_lane<H, MT>(a, g, wv, l16, q), krot, fa0);
+    if constexpr (BWD) w2t_frags<H, MT>(w2t_lane<H, NW>(a, g, wv, l16, q), krot, fa0);
     __syncthreads();
-    stage_out<H, kFwd2Samples>(smem, a.dz2 + ((int64_t)g * B + s0) * H, H, srows);
-    if constexpr (BWD) backward_h1<H, MT>(a, smem, acc, fa0, g, blk, s0, srows, wv, l, l16, q, krot);
+    stage_out<H, kFwd2Samples, NT>(smem, a.dz2 + ((int64_t)g * B + s0) * H, H, srows);
+    if constexpr (BWD) backward_h1<H, MT, NW>(a, smem, acc, fa0, g, blk, s0, srows, wv, l, l16, q, krot);
 }
 
 // --------------------------------------------------------------- wgrad
@@ -861,7 +877,7 @@ constexpr size_t ring_lds_bytes(int nst) { return (size_t)nst * 2 * kTile * kBK 
 template <int H>
 constexpr size_t fwd2_lds_bytes() {
     return (size_t)(3 * (H + kFwd2Samples) * kBK > kFwd2Samples * H ? 3 * (H + kFwd2Samples) * kBK : kFwd2Samples * H) * 2 +
-           (5 * kFwd2Samples + 2 * H) * sizeof(float);
+           ((kFwd2Waves + 1) * kFwd2Samples + 2 * H) * sizeof(float);
 }
 
 template <typename K>
@@ -938,10 +954,10 @@ static hipError_t big_launch(const IqlDims& d, const IqlBuffers& b, const float*
     if (!attr) {
         hipError_t e = allow_lds(big_fwd1_kernel, ring_lds_bytes(kTileStages));
         if (e == hipSuccess) e = allow_lds(big_wgrad_kernel, ring_lds_bytes(kWgradStages));
-        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<256, false>, fwd2_lds_bytes<256>());
-        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<512, false>, fwd2_lds_bytes<512>());
-        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<256, true>, fwd2_lds_bytes<256>());
-        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<512, true>, fwd2_lds_bytes<512>());
+        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<256, false, kFwd2Waves>, fwd2_lds_bytes<256>());
+        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<512, false, kFwd2Waves>, fwd2_lds_bytes<512>());
+        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<256, true, kFwd2Waves>, fwd2_lds_bytes<256>());
+        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<512, true, kFwd2Waves>, fwd2_lds_bytes<512>());
         if (e != hipSuccess) return e;
         attr = true;
     }
@@ -950,12 +966,12 @@ static hipError_t big_launch(const IqlDims& d, const IqlBuffers& b, const float*
     hipLaunchKernelGGL(big_fwd1_kernel, gt, dim3(kThreads), ring_lds_bytes(kTileStages), stream, a);
     const dim3 g2(a.nblk, G);
     if (vo) {
-        if (H == 512) hipLaunchKernelGGL((big_fwd2_kernel<512, false>), g2, dim3(kThreads), fwd2_lds_bytes<512>(), stream, a);
-        else hipLaunchKernelGGL((big_fwd2_kernel<256, false>), g2, dim3(kThreads), fwd2_lds_bytes<256>(), stream, a);
+        if (H == 512) hipLaunchKernelGGL((big_fwd2_kernel<512, false, kFwd2Waves>), g2, dim3(64 * kFwd2Waves), fwd2_lds_bytes<512>(), stream, a);
+        else hipLaunchKernelGGL((big_fwd2_kernel<256, false, kFwd2Waves>), g2, dim3(64 * kFwd2Waves), fwd2_lds_bytes<256>(), stream, a);
         return hipGetLastError();
     }
-    if (H == 512) hipLaunchKernelGGL((big_fwd2_kernel<512, true>), g2, dim3(kThreads), fwd2_lds_bytes<512>(), stream, a);
-    else hipLaunchKernelGGL((big_fwd2_kernel<256, true>), g2, dim3(kThreads), fwd2_lds_bytes<256>(), stream, a);
+    if (H == 512) hipLaunchKernelGGL((big_fwd2_kernel<512, true, kFwd2Waves>), g2, dim3(64 * kFwd2Waves), fwd2_lds_bytes<512>(), stream, a);
+    else hipLaunchKernelGGL((big_fwd2_kernel<256, true, kFwd2Waves>), g2, dim3(64 * kFwd2Waves), fwd2_lds_bytes<256>(), stream, a);
     const dim3 gw(a.nchunk * big_tiles(S, H), G);
     hipLaunchKernelGGL(big_wgrad_kernel, gw, dim3(kThreads), ring_lds_bytes(kWgradStages), stream, a);
     return hipGetLastError();
