@@ -63,7 +63,9 @@ constexpr int kFwd2Samples = 128; // samples per fwd2 block (the loss blocks)
 constexpr int kFwd2Waves = 8;     // waves of a fwd2 workgroup (two per SIMD)
 constexpr int kTile = 256;        // fwd1 / wgrad output tile edge
 constexpr int kTileStages = 5;    // ring depth of fwd1 (5 x 32 KB)
+constexpr int kFwd1Waves = 8;     // waves of a fwd1 workgroup (two per SIMD)
 constexpr int kWgradStages = 5;   // ring depth of wgrad (5 x 32 KB)
+constexpr int kWgradWaves = 8;    // waves of a wgrad workgroup (two per SIMD)
 // entries of a loss block's sums: db2 [H], dw3 [H], db3, db1 [H]
 __host__ __device__ constexpr int spart_w(int H) { return 3 * H + 1; }
 
@@ -250,19 +252,19 @@ __device__ __align__(16) const uint16_t kZeroRow[kTile] = {};
 // Samples at or past smax read zeros (ZERO) or re-read sample smax - 1 (their
 // products are then discarded or multiplied by zeros); features at or past
 // fmax re-read feature 0 of the row (those columns are discarded).
-template <bool ZERO>
+template <bool ZERO, int NT = kThreads>
 IQLH_DEV void dma_nat(const uint16_t* g, int64_t ld, int smax, int f0, int fmax, uint16_t* lds) {
     const int tid = threadIdx.x, wbase = tid & ~63;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = i * kThreads + tid;
+    for (int i = 0; i < 1024 / NT; ++i) {
+        const int c = i * NT + tid;
         const int s = c >> 5, v = (c & 31) ^ (2 * (s & 3));
         const int gs = s < smax ? s : smax - 1;
         const int f = f0 + 8 * v;
         const int gf = f < fmax ? f : 0;
         const uint16_t* src = g + (int64_t)gs * ld + gf;
         if (ZERO) src = s < smax ? src : kZeroRow + 8 * v;
-        __builtin_amdgcn_global_load_lds((const void*)src, IQLH_LDS(lds + (i * kThreads + wbase) * 8), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)src, IQLH_LDS(lds + (i * NT + wbase) * 8), 16, 0, 0);
     }
 }
 IQLH_DEV u32x2 ld_tr(const uint16_t* p) {
@@ -372,8 +374,11 @@ IQLH_DEV int k_rotation(int nks) { return (int)((blockIdx.x >> 3) % (unsigned)nk
 // ---------------------------------------------------------------- fwd1
 // D[f][s] = sum_k W1[f][k] s[s][k] over a 256-feature x 256-sample tile;
 // h1 = relu(D + b1), and the ReLU mask as bits for the backward product.
-__global__ __launch_bounds__(kThreads) void big_fwd1_kernel(BigArgs a) {
+__global__ __launch_bounds__(64 * kFwd1Waves) void big_fwd1_kernel(BigArgs a) {
     extern __shared__ __align__(16) uint16_t smem[];
+    // wave w: features 128 (w & 1) .. + 127 and samples (256 / NC) (w >> 1) ..
+    // of the tile, NC = waves / 2 sample groups of JT sample tiles
+    constexpr int NT = 64 * kFwd1Waves, NC = kFwd1Waves / 2, JT = 16 / NC;
     constexpr int NST = kTileStages, STG = 2 * kTile * kBK;  // elements per stage
     const int g = blockIdx.y;
     const int H = a.H, B = a.B;
@@ -388,29 +393,29 @@ __global__ __launch_bounds__(kThreads) void big_fwd1_kernel(BigArgs a) {
     const int wm = wv & 1, wn = wv >> 1;
     const int lo = kc_lane();
 
-    f4 acc[8][8];
+    f4 acc[8][JT];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < JT; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
     const int l = threadIdx.x & 63, l16 = l & 15, q = l >> 4;
 
-    bf16x8 fa[8], fb[2][8];  // fa: one set, re-read row by row (see kloop)
+    bf16x8 fa[8], fb[2][JT];  // fa: one set, re-read row by row (see kloop)
     const int nks = a.S / kBK, krot = k_rotation(nks);
-    kloop<NST, 8>(
+    kloop<NST, 2 * kTile * 4 / NT>(
         nks,
         [&](int s, int buf) {
             uint16_t* st_ = smem + buf * STG;
             const int k0 = ((s + krot) % nks) * kBK;
-            dma_kc<kTile>(A, a.ldw1, kTile, k0, st_);
-            dma_kc<kTile>(Bm, a.ldx, srows, k0, st_ + kTile * kBK);
+            dma_kc<kTile, NT>(A, a.ldw1, kTile, k0, st_);
+            dma_kc<kTile, NT>(Bm, a.ldx, srows, k0, st_ + kTile * kBK);
         },
         [&](int buf, auto p) {
             constexpr int P = decltype(p)::value;
             const uint16_t* ta = smem + buf * STG + (128 * wm) * kBK + lo;
-            const uint16_t* tb = smem + buf * STG + kTile * kBK + (128 * wn) * kBK + lo;
+            const uint16_t* tb = smem + buf * STG + kTile * kBK + (16 * JT * wn) * kBK + lo;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) fb[P][j] = *(const bf16x8*)(tb + j * 16 * kBK);
+            for (int j = 0; j < JT; ++j) fb[P][j] = *(const bf16x8*)(tb + j * 16 * kBK);
 #pragma unroll
             for (int i = 0; i < 8; ++i) fa[i] = *(const bf16x8*)(ta + i * 16 * kBK);
         },
@@ -419,14 +424,16 @@ __global__ __launch_bounds__(kThreads) void big_fwd1_kernel(BigArgs a) {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] = mma(fa[i], fb[P][j], acc[i][j]);
-            reads_among_mfma<16, 64>();
+                for (int j = 0; j < JT; ++j) acc[i][j] = mma(fa[i], fb[P][j], acc[i][j]);
+            reads_among_mfma<8 + JT, 8 * JT>();
         },
         no_pre);
 
     // epilogue: lane holds features 128 wm + 16 i + 4 q + r of samples
-    // 128 wn + 16 j + l16 (tile-local); staged as [sample][feature] rows.
-    // relu'(z1) leaves as bits in this lane layout (mask_word0).
+    // 16 (JT wn + j) + l16 (tile-local); staged as [sample][feature] rows.
+    // relu'(z1) leaves as bits in the layout of mask_word0, whose lane covers
+    // the 8 sample tiles of a 128-sample half: this wave's JT tiles are the
+    // bits 4 JT (wn % (8 / JT)) .. of each word.
     const float* bias = a.params + (int64_t)g * a.P + a.off_b1 + f0;
     uint32_t mbits[8];
     __syncthreads();  // every wave is done with the last stage
@@ -438,8 +445,8 @@ __global__ __launch_bounds__(kThreads) void big_fwd1_kernel(BigArgs a) {
         for (int r = 0; r < 4; ++r) bb[r] = bias[f + r];
         mbits[i] = 0u;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int sl = 128 * wn + 16 * j + l16;
+        for (int j = 0; j < JT; ++j) {
+            const int sl = 16 * (JT * wn + j) + l16;
             float y[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -454,12 +461,23 @@ __global__ __launch_bounds__(kThreads) void big_fwd1_kernel(BigArgs a) {
         }
     }
     if (!a.fwd_only) {
-        u32x4* mp = (u32x4*)(a.mask + mask_word0(a, g, st, ft, threadIdx.x));
-        mp[0] = u32x4{mbits[0], mbits[1], mbits[2], mbits[3]};
-        mp[1] = u32x4{mbits[4], mbits[5], mbits[6], mbits[7]};
+        static_assert(JT == 4 || JT == 8, "mask word pieces");
+        // lane t of the word layout: 128-feature half wm, 128-sample half
+        // (JT wn) / 8, this lane's place in the wave
+        const int t = 64 * (wm + 2 * ((JT * wn) / 8)) + l;
+        uint32_t* mw = a.mask + mask_word0(a, g, st, ft, t);
+        if constexpr (JT == 8) {
+            u32x4* mp = (u32x4*)mw;
+            mp[0] = u32x4{mbits[0], mbits[1], mbits[2], mbits[3]};
+            mp[1] = u32x4{mbits[4], mbits[5], mbits[6], mbits[7]};
+        } else {
+            uint16_t* mh = (uint16_t*)mw + (wn & 1);  // low or high half of each word
+#pragma unroll
+            for (int i = 0; i < 8; ++i) mh[2 * i] = (uint16_t)mbits[i];
+        }
     }
     __syncthreads();
-    stage_out<kTile, kTile>(smem, a.h1 + ((int64_t)g * B + s0) * H + f0, H, srows);
+    stage_out<kTile, kTile, NT>(smem, a.h1 + ((int64_t)g * B + s0) * H + f0, H, srows);
 }
 
 // ------------------------------------------------- dh1 inside fwd2's workgroup
@@ -769,8 +787,11 @@ __global__ __launch_bounds__(64 * NW) void big_fwd2_kernel(BigArgs a) {
 // tile of dW1 = dz1^T s.  Job j of a chunk also adds the chunk's block sums
 // (db2, dw3, db3, db1, all from fwd2) for its share of the entries, so that
 // no workgroup exists for that small sum alone.
-__global__ __launch_bounds__(kThreads) void big_wgrad_kernel(BigArgs a) {
+__global__ __launch_bounds__(64 * kWgradWaves) void big_wgrad_kernel(BigArgs a) {
     extern __shared__ __align__(16) uint16_t smem[];
+    // wave w: rows 128 (w & 1) .. + 127 and columns (256 / NC) (w >> 1) .. of
+    // the 256 x 256 tile, NC = waves / 2 column groups of JT feature tiles
+    constexpr int NT = 64 * kWgradWaves, NC = kWgradWaves / 2, JT = 16 / NC;
     constexpr int NST = kWgradStages, STG = 2 * kBK * kTile;
     const int g = blockIdx.y;
     const int H = a.H, S = a.S, B = a.B;
@@ -805,11 +826,11 @@ __global__ __launch_bounds__(kThreads) void big_wgrad_kernel(BigArgs a) {
     const int wm = wv & 1, wn = wv >> 1;
     const NatBase nb = nat_base();
 
-    f4 acc[8][8];
+    f4 acc[8][JT];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < JT; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
     const int nsl = (len + kBK - 1) / kBK;
 
     // this job's share of the chunk's block sums, in block order, while the
@@ -818,7 +839,7 @@ __global__ __launch_bounds__(kThreads) void big_wgrad_kernel(BigArgs a) {
         const int ne = spart_w(H), per = (ne + njob - 1) / njob;
         const int k0 = b0 / kFwd2Samples, k1 = (b0 + len + kFwd2Samples - 1) / kFwd2Samples;
         const float* sp = a.spart + (int64_t)g * a.nblk * ne;
-        for (int t = tid; t < per; t += kThreads) {
+        for (int t = tid; t < per; t += NT) {
             const int e = job * per + t;
             if (e >= ne) break;
             float s = 0.f;
@@ -829,21 +850,21 @@ __global__ __launch_bounds__(kThreads) void big_wgrad_kernel(BigArgs a) {
             part[off] = s;
         }
     };
-    bf16x8 fa[8], fb[2][8];  // fa: one set, re-read row by row (see kloop)
-    kloop<NST, 8>(
+    bf16x8 fa[8], fb[2][JT];  // fa: one set, re-read row by row (see kloop)
+    kloop<NST, 2 * 1024 / NT>(
         nsl,
         [&](int s, int buf) {
             uint16_t* st_ = smem + buf * STG;
             const int sm = len - s * kBK;
-            dma_nat<true>(A + (int64_t)s * kBK * H, H, sm, fa0, H, st_);
-            dma_nat<false>(Bm + (int64_t)s * kBK * ldb, ldb, sm, fb0, fbmax, st_ + kBK * kTile);
+            dma_nat<true, NT>(A + (int64_t)s * kBK * H, H, sm, fa0, H, st_);
+            dma_nat<false, NT>(Bm + (int64_t)s * kBK * ldb, ldb, sm, fb0, fbmax, st_ + kBK * kTile);
         },
         [&](int buf, auto p) {
             constexpr int P = decltype(p)::value;
             const uint16_t* ta = smem + buf * STG;
             const uint16_t* tb = ta + kBK * kTile;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) fb[P][j] = nat_frag(tb, nb, 8 * wn + j);
+            for (int j = 0; j < JT; ++j) fb[P][j] = nat_frag(tb, nb, JT * wn + j);
 #pragma unroll
             for (int i = 0; i < 8; ++i) fa[i] = nat_frag(ta, nb, 8 * wm + i);
         },
@@ -852,8 +873,8 @@ __global__ __launch_bounds__(kThreads) void big_wgrad_kernel(BigArgs a) {
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] = mma(fa[i], fb[P][j], acc[i][j]);
-            reads_among_mfma<32, 64>();
+                for (int j = 0; j < JT; ++j) acc[i][j] = mma(fa[i], fb[P][j], acc[i][j]);
+            reads_among_mfma<2 * (8 + JT), 8 * JT>();
         },
         pre);
 
@@ -862,8 +883,8 @@ __global__ __launch_bounds__(kThreads) void big_wgrad_kernel(BigArgs a) {
     for (int i = 0; i < 8; ++i) {
         const int m = fa0 + 128 * wm + 16 * i + 4 * q;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int n = fb0 + 128 * wn + 16 * j + l16;
+        for (int j = 0; j < JT; ++j) {
+            const int n = fb0 + 16 * (JT * wn + j) + l16;
             if (n < fbmax) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dst[(int64_t)(m + r) * ldo + n] = acc[i][j][r];
@@ -963,7 +984,7 @@ static hipError_t big_launch(const IqlDims& d, const IqlBuffers& b, const float*
     }
     const int nst = (B + kTile - 1) / kTile;
     const dim3 gt(nst * (H / kTile), G);
-    hipLaunchKernelGGL(big_fwd1_kernel, gt, dim3(kThreads), ring_lds_bytes(kTileStages), stream, a);
+    hipLaunchKernelGGL(big_fwd1_kernel, gt, dim3(64 * kFwd1Waves), ring_lds_bytes(kTileStages), stream, a);
     const dim3 g2(a.nblk, G);
     if (vo) {
         if (H == 512) hipLaunchKernelGGL((big_fwd2_kernel<512, false, kFwd2Waves>), g2, dim3(64 * kFwd2Waves), fwd2_lds_bytes<512>(), stream, a);
@@ -973,7 +994,7 @@ static hipError_t big_launch(const IqlDims& d, const IqlBuffers& b, const float*
     if (H == 512) hipLaunchKernelGGL((big_fwd2_kernel<512, true, kFwd2Waves>), g2, dim3(64 * kFwd2Waves), fwd2_lds_bytes<512>(), stream, a);
     else hipLaunchKernelGGL((big_fwd2_kernel<256, true, kFwd2Waves>), g2, dim3(64 * kFwd2Waves), fwd2_lds_bytes<256>(), stream, a);
     const dim3 gw(a.nchunk * big_tiles(S, H), G);
-    hipLaunchKernelGGL(big_wgrad_kernel, gw, dim3(kThreads), ring_lds_bytes(kWgradStages), stream, a);
+    hipLaunchKernelGGL(big_wgrad_kernel, gw, dim3(64 * kWgradWaves), ring_lds_bytes(kWgradStages), stream, a);
     return hipGetLastError();
 }
 
