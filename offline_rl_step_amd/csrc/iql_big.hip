@@ -303,13 +303,22 @@ IQLH_DEV bf16x8 nat_frag(const uint16_t* tile, const NatBase& nb, int c) {
 template <int NF>
 IQLH_DEV int stage_off(int s, int f) { return s * NF + ((((f >> 3) ^ (s & 7)) << 3) | (f & 7)); }
 
+// threadIdx.x through an empty asm statement: address arithmetic on it
+// cannot be hoisted above this point (so it is not held in registers across
+// an earlier loop).
+IQLH_DEV int opaque_tid() {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
 // Rows [0, ns) of the staged tile to dst rows (row stride ld), columns
 // [0, NF).
 template <int NF, int NS, int NT = kThreads>
-IQLH_DEV void stage_out(const uint16_t* lds, uint16_t* dst, int64_t ld, int ns) {
+IQLH_DEV void stage_out(const uint16_t* lds, uint16_t* dst, int64_t ld, int ns, int tid = threadIdx.x) {
     constexpr int UPR = NF / 8;  // 16-byte units per row
 #pragma unroll 4
-    for (int c = threadIdx.x; c < NS * UPR; c += NT) {
+    for (int c = tid; c < NS * UPR; c += NT) {
         const int r = c / UPR, u = c - r * UPR;
         if (r >= ns) break;
         *(u32x4*)(dst + (int64_t)r * ld + 8 * u) = *(const u32x4*)(lds + r * NF + ((u ^ (r & 7)) << 3));
@@ -502,6 +511,7 @@ IQLH_DEV void w2t_frags(const uint16_t* At, int kt, bf16x8 (&f)[MT]) {
 template <int H, int MT, int NW>
 IQLH_DEV void backward_h1(const BigArgs& a, uint16_t* smem, f4 (&acc)[MT][8], bf16x8 (&fa0)[MT], int g, int blk,
                           int s0, int srows, int wv, int l, int l16, int q, int krot) {
+    // (l16 and q are formed again from the thread index before the epilogue)
     constexpr int NK = H / kBK;
     static_assert(NK % 2 == 0, "k-steps in pairs");
     static_assert(MT * 16 * NW == H, "row tiles");
@@ -541,6 +551,12 @@ IQLH_DEV void backward_h1(const BigArgs& a, uint16_t* smem, f4 (&acc)[MT][8], bf
         step(kt + 1, fa1, fa0);
     }
     __syncthreads();  // every wave is done with the dz2 tile
+    // lane coordinates formed again here (opaque_tid): otherwise the compiler
+    // keeps the epilogue's LDS and store addresses, equal to or derived from
+    // the dz2 epilogue's, live across the loop above, and spills them
+    const int tid2 = opaque_tid();
+    l16 = tid2 & 15;
+    q = (tid2 & 63) >> 4;
     float* db1 = a.spart + ((int64_t)g * a.nblk + blk) * spart_w(H) + 2 * H + 1;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
@@ -569,7 +585,7 @@ IQLH_DEV void backward_h1(const BigArgs& a, uint16_t* smem, f4 (&acc)[MT][8], bf
         }
     }
     __syncthreads();
-    stage_out<H, kFwd2Samples, 64 * NW>(smem, a.dz1 + ((int64_t)g * a.B + s0) * H, H, srows);
+    stage_out<H, kFwd2Samples, 64 * NW>(smem, a.dz1 + ((int64_t)g * a.B + s0) * H, H, srows, opaque_tid());
 }
 
 // v's partial dot products of the NW waves for sample sl, added pairwise in a
