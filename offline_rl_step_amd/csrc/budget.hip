@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kBT) void budget_saxpy_kernel(SourceSet s, int64_t 
                                                             int32_t* __restrict__ adam_t, float* __restrict__ bc,
                                                             float beta1, float beta2) {
     if ((int)blockIdx.x < nb)
-        saxpy_block(s, n, vec, mgn, partials, grad, gpart, out_norms, blockIdx.x, nb);
+        saxpy_block<true>(s, n, vec, mgn, partials, grad, gpart, out_norms, blockIdx.x, nb);
     else
         adam_count_block(adam_t, bc, beta1, beta2);
 }

@@ -138,6 +138,7 @@ IQLH_DEV float adam_clip(float norm, float max_norm) {
 
 // Pass 2 for block bx of nb: clip scales, grad = sum_k c_k s_k, and the
 // block's partial of ||grad||^2.
+template <bool PIPE = false>
 IQLH_DEV void saxpy_block(const SourceSet& s, int64_t n, int vec, float mgn, const float* __restrict__ partials,
                           float* __restrict__ grad, float* __restrict__ gpart, float* __restrict__ out_norms, int bx,
                           int nb) {
@@ -164,27 +165,36 @@ IQLH_DEV void saxpy_block(const SourceSet& s, int64_t n, int vec, float mgn, con
         nrm[j] = sqrtf(c[j]);
         c[j] = j < s.k ? s.alpha[j] * budget_scale(nrm[j], s.frac[j] * mgn) : 0.f;
     }
+    // PIPE: software-pipelined, the next quad's loads (at a clamped index)
+    // issued before this quad's store, so that waiting for them never waits
+    // for the store as well (vmcnt counts both, in order) -- for the
+    // standalone pass, whose threads take many quads; it holds a second set
+    // of source quads, which would lower the occupancy of the merged launch
+    // whose reduction blocks share the kernel.  Same sums either way.
     float acc = 0.f;
-    if (q0 < quads) {
+    for (int64_t qd = q0; qd < quads; qd += stride) {
+        const int64_t nx = qd + stride, nc = nx < quads ? nx : quads - 1;
+        f32x4 x[kMaxSources];
+        if constexpr (PIPE) {
+#pragma unroll
+            for (int j = 0; j < kMaxSources; ++j)
+                x[j] = j < s.k ? ld4(s.ptr[j], 4 * nc, n, vec4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
         f32x4 g = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < kMaxSources; ++j)
             if (j < s.k) g += c[j] * pre[j];
-        st4(grad, 4 * q0, n, vec, g);
-        acc = fmaf(g.x, g.x, fmaf(g.y, g.y, fmaf(g.z, g.z, fmaf(g.w, g.w, acc))));
-    }
-    for (int64_t qd = q0 + stride; qd < quads; qd += stride) {
-        // every source's quad in flight before the first is used
-        f32x4 x[kMaxSources];
-#pragma unroll
-        for (int j = 0; j < kMaxSources; ++j)
-            x[j] = j < s.k ? ld4(s.ptr[j], 4 * qd, n, vec4) : f32x4{0.f, 0.f, 0.f, 0.f};
-        f32x4 g = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < kMaxSources; ++j)
-            if (j < s.k) g += c[j] * x[j];
         st4(grad, 4 * qd, n, vec, g);
         acc = fmaf(g.x, g.x, fmaf(g.y, g.y, fmaf(g.z, g.z, fmaf(g.w, g.w, acc))));
+        if constexpr (PIPE) {
+#pragma unroll
+            for (int j = 0; j < kMaxSources; ++j) pre[j] = x[j];
+        } else {
+            // the next quad's loads after this quad's store
+#pragma unroll
+            for (int j = 0; j < kMaxSources; ++j)
+                pre[j] = j < s.k ? ld4(s.ptr[j], 4 * nc, n, vec4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     }
     const float t = block_sum<kBT>(acc, red);
     if (threadIdx.x == 0) gpart[bx] = t;
@@ -273,12 +283,18 @@ IQLH_DEV void adam_flat_block(float* __restrict__ params, float* __restrict__ gr
     const float c = adam_clip(nrm, hp.max_grad_norm);
     const float decay = 1.f - hp.lr * hp.weight_decay;
     bool bad = false, bad_state = false;
-    if (q0 < quads)
-        adam_flat_quad(params, grad, m, v, 4 * q0, n, vec, pg * c, pm, pv, pp, bc1, bc2, decay, hp, bad, bad_state);
-    for (int64_t qd = q0 + stride; qd < quads; qd += stride) {
-        const int64_t i = 4 * qd;
-        adam_flat_quad(params, grad, m, v, i, n, vec, ld4(grad, i, n, vec4) * c, ld4(m, i, n, vec4),
-                       ld4(v, i, n, vec4), ld4(params, i, n, vec4), bc1, bc2, decay, hp, bad, bad_state);
+    // software-pipelined as in saxpy_block: the next quad's state is loaded
+    // (at a clamped index) before this quad's stores
+    f32x4 cg = pg, cm = pm, cv = pv, cp = pp;
+    for (int64_t qd = q0; qd < quads; qd += stride) {
+        const int64_t nx = qd + stride, i1 = 4 * (nx < quads ? nx : quads - 1);
+        const f32x4 ng = ld4(grad, i1, n, vec4), nm = ld4(m, i1, n, vec4), nv = ld4(v, i1, n, vec4),
+                    np = ld4(params, i1, n, vec4);
+        adam_flat_quad(params, grad, m, v, 4 * qd, n, vec, cg * c, cm, cv, cp, bc1, bc2, decay, hp, bad, bad_state);
+        cg = ng;
+        cm = nm;
+        cv = nv;
+        cp = np;
     }
     // (stored last: a wave would wait for this store at its next use of a load)
     if (bx == 0 && threadIdx.x == 0 && out_norm) *out_norm = nrm;

@@ -188,12 +188,21 @@ IQLH_DEV void iql_adam_block(const IqlDims& d, const IqlBuffers& b, const AdamHy
                                    : ((nrm > hp.max_grad_norm && nrm > 0.f) ? hp.max_grad_norm / nrm : 1.f);
     const float decay = 1.f - hp.lr * hp.weight_decay;
     bool bad = false, bad_state = false;
-    if (i0 < P)
-        iql_adam_param<T>(i0, pg * c, pp, pm, pv, pt, bc1, bc2, decay, hp, H, H2, S, SP, prm, gr, m, v, tg, w1s,
-                          w2s, w2ts, bad, bad_state);
-    for (int64_t i = i0 + stride; i < P; i += stride)
-        iql_adam_param<T>(i, gr[i] * c, prm[i], m[i], v[i], tg[i], bc1, bc2, decay, hp, H, H2, S, SP, prm, gr, m, v,
-                          tg, w1s, w2s, w2ts, bad, bad_state);
+    // software-pipelined: the next parameter's state is loaded (at a clamped
+    // index) before this parameter's stores, so waiting for it never waits
+    // for the stores as well (vmcnt counts both, in order)
+    float cg = pg, cp = pp, cm = pm, cv = pv, ct = pt;
+    for (int64_t i = i0; i < P; i += stride) {
+        const int64_t nx = i + stride, j1 = nx < P ? nx : P - 1;
+        const float ng = gr[j1], np = prm[j1], nm = m[j1], nv = v[j1], nt = tg[j1];
+        iql_adam_param<T>(i, cg * c, cp, cm, cv, ct, bc1, bc2, decay, hp, H, H2, S, SP, prm, gr, m, v, tg, w1s, w2s,
+                          w2ts, bad, bad_state);
+        cg = ng;
+        cp = np;
+        cm = nm;
+        cv = nv;
+        ct = nt;
+    }
     // (stored last: a wave would wait for this store at its next use of a load)
     if (bx == 0 && threadIdx.x == 0 && out_gnorm) out_gnorm[g] = nrm;
     if (bad) set_flag(b.flags, 0x1);
