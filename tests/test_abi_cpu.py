@@ -157,6 +157,8 @@ def test_host_validation_of_kernel_entry_points(m):
     assert m._lib_iql_train_step(None, None, None, 1, None, None, None, None) == m.EINVAL
     assert m._lib_iql_aux_step(None, None, None, None, 1, None, 0, 0.0, None, None, None, None, None,
                                None) == m.EINVAL
+    assert m._lib_iql_aux_step_phase_stamps(None, None, None, None, 1, None, 0, 0.0, None, None, None, None, None,
+                                            None, 0, None) == m.EINVAL
     assert m._lib_iql_step_counter(None) is None
     rows, floats = ctypes.c_int32(), ctypes.c_int64()
     assert m._lib_iql_partial_layout(None, 1, ctypes.byref(rows), ctypes.byref(floats)) == m.EINVAL
