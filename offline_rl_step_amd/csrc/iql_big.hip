@@ -61,6 +61,8 @@ constexpr int kThreads = 256;
 constexpr int kBK = 32;           // k per stage
 constexpr int kFwd2Samples = 128; // samples per fwd2 block (the loss blocks)
 constexpr int kFwd2Waves = 8;     // waves of a fwd2 workgroup (two per SIMD)
+// fwd2 forms z1 = W1 s itself and keeps h1 in LDS (no fwd1 launch)
+constexpr bool kFuseF1 = true;
 constexpr int kTile = 256;        // fwd1 / wgrad output tile edge
 constexpr int kTileStages = 5;    // ring depth of fwd1 (5 x 32 KB)
 constexpr int kFwd1Waves = 8;     // waves of a fwd1 workgroup (two per SIMD)
@@ -508,30 +510,21 @@ IQLH_DEV void w2t_frags(const uint16_t* At, int kt, bf16x8 (&f)[MT]) {
 #pragma unroll
     for (int i = 0; i < MT; ++i) f[i] = *(const bf16x8*)(At + (int64_t)16 * i * H + kBK * kt);
 }
-template <int H, int MT, int NW>
-IQLH_DEV void backward_h1(const BigArgs& a, uint16_t* smem, f4 (&acc)[MT][8], bf16x8 (&fa0)[MT], int g, int blk,
-                          int s0, int srows, int wv, int l, int l16, int q, int krot) {
-    // (l16 and q are formed again from the thread index before the epilogue)
+// acc[i][j] = sum_k A[f_i][k] Bt[s_j][k] over k = 0 .. H - 1, in the k-step
+// order rotated by krot: A row-major in global memory (At = this lane's row
+// and k-offset, 16-byte fragments loaded one k-step ahead, the first step's
+// in fa0 already), Bt the [sample][k] tile staged in LDS (stage_off<H>).
+template <int H, int MT>
+IQLH_DEV void lds_b_product(const uint16_t* At, const uint16_t* smem, f4 (&acc)[MT][8], bf16x8 (&fa0)[MT], int krot,
+                            int l16, int q) {
     constexpr int NK = H / kBK;
     static_assert(NK % 2 == 0, "k-steps in pairs");
-    static_assert(MT * 16 * NW == H, "row tiles");
-    const uint16_t* At = w2t_lane<H, NW>(a, g, wv, l16, q);
-    // this lane's mask words: fwd1 tile (s0 / 256, f / 256), lane
-    // 64 (wm + 2 wn) + l with wn = the block's half of its 256-sample tile
-    uint32_t mb[MT];
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-        const int f = (H / NW) * wv + 16 * i;
-        const int ft = f / kTile, wm = (f % kTile) / 128, word = (f % 128) / 16;
-        mb[i] = a.mask[mask_word0(a, g, s0 / kTile, ft, 64 * (wm + 2 * (blk & 1)) + l) + word];
-    }
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
     bf16x8 fa1[MT], fb[8];
     auto load_a = [&](int kt, bf16x8 (&f)[MT]) __attribute__((always_inline)) { w2t_frags<H, MT>(At, kt, f); };
-    // k-steps in the rotated order of the forward product (k_rotation)
     auto step = [&](int kt, bf16x8 (&cur)[MT], bf16x8 (&nxt)[MT]) __attribute__((always_inline)) {
         if (kt + 1 < NK) load_a((kt + 1 + krot) & (NK - 1), nxt);
         // the next step's loads stay ahead of this step's MFMAs (the
@@ -550,6 +543,29 @@ IQLH_DEV void backward_h1(const BigArgs& a, uint16_t* smem, f4 (&acc)[MT][8], bf
         step(kt, fa0, fa1);
         step(kt + 1, fa1, fa0);
     }
+}
+
+template <int H, int MT, int NW, bool FUSE>
+IQLH_DEV void backward_h1(const BigArgs& a, uint16_t* smem, f4 (&acc)[MT][8], bf16x8 (&fa0)[MT], int g, int blk,
+                          int s0, int srows, int wv, int l, int l16, int q, int krot, const uint32_t* smask) {
+    // (l16 and q are formed again from the thread index before the epilogue)
+    static_assert(MT * 16 * NW == H, "row tiles");
+    const uint16_t* At = w2t_lane<H, NW>(a, g, wv, l16, q);
+    // this lane's relu'(z1) words: from the fused forward's LDS copy (FUSE),
+    // else fwd1's words -- tile (s0 / 256, f / 256), lane 64 (wm + 2 wn) + l
+    // with wn = the block's half of its 256-sample tile
+    uint32_t mb[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        if constexpr (FUSE) {
+            mb[i] = smask[i * (64 * NW) + (int)threadIdx.x];
+        } else {
+            const int f = (H / NW) * wv + 16 * i;
+            const int ft = f / kTile, wm = (f % kTile) / 128, word = (f % 128) / 16;
+            mb[i] = a.mask[mask_word0(a, g, s0 / kTile, ft, 64 * (wm + 2 * (blk & 1)) + l) + word];
+        }
+    }
+    lds_b_product<H, MT>(At, smem, acc, fa0, krot, l16, q);
     __syncthreads();  // every wave is done with the dz2 tile
     // lane coordinates formed again here (opaque_tid): otherwise the compiler
     // keeps the epilogue's LDS and store addresses, equal to or derived from
@@ -606,15 +622,19 @@ IQLH_DEV float wave_parts_sum(const float* svp, int sl) {
 // With BWD, the same workgroup then forms dh1 = W2^T dz2 for its samples from
 // the dz2 tile still staged in LDS, and dz1 = dh1 relu'(z1) with the block's
 // db1 sums, so dz2 is never read back from memory for it.
-template <int H, bool BWD, int NW>
+template <int H, bool BWD, int NW, bool FUSE>
 __global__ __launch_bounds__(64 * NW) void big_fwd2_kernel(BigArgs a) {
     extern __shared__ __align__(16) uint16_t smem[];
     constexpr int NT = 64 * NW, MT = H / (16 * NW), NST = 3, STG = (H + kFwd2Samples) * kBK;
     constexpr int LPT = (H + kFwd2Samples) * 4 / NT;
     const int g = blockIdx.y, blk = blockIdx.x;
     const int B = a.B, s0 = blk * kFwd2Samples;
-    const uint16_t* A = a.w2s + (int64_t)g * H * H;
-    const uint16_t* Bm = a.h1 + ((int64_t)g * B + s0) * H;
+    // the ring's product: z1 = W1 s (FUSE) or z2 = W2 h1 with h1 from fwd1
+    const uint16_t* A = FUSE ? a.w1s + (int64_t)g * H * a.ldw1 : a.w2s + (int64_t)g * H * H;
+    const int64_t lda = FUSE ? a.ldw1 : H;
+    const uint16_t* Bm = FUSE ? a.x + (int64_t)s0 * a.ldx : a.h1 + ((int64_t)g * B + s0) * H;
+    const int64_t ldb = FUSE ? a.ldx : H;
+    const int nks = FUSE ? a.S / kBK : H / kBK;
     const int srows = B - s0;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lo = kc_lane();
@@ -623,6 +643,8 @@ __global__ __launch_bounds__(64 * NW) void big_fwd2_kernel(BigArgs a) {
     float* sq = svp + NW * kFwd2Samples;                            // [128] q of the block's samples
     float* sb2 = sq + kFwd2Samples;                                 // [H] b2
     float* sw3 = sb2 + H;                                           // [H] w3
+    float* sb1 = sw3 + H;                                           // [H] b1 (FUSE)
+    uint32_t* smask = (uint32_t*)(sb1 + H);                         // [MT][NT] relu'(z1) words (FUSE)
     const float* prm = a.params + (int64_t)g * a.P;
     // q, b2 and w3 to LDS while the first stages are in flight, so that the
     // epilogue reads them without a memory round trip
@@ -632,6 +654,7 @@ __global__ __launch_bounds__(64 * NW) void big_fwd2_kernel(BigArgs a) {
         for (int f = t; f < H; f += NT) {
             sb2[f] = prm[a.off_b2 + f];
             sw3[f] = prm[a.off_w3 + f];
+            if (FUSE) sb1[f] = prm[a.off_b1 + f];
         }
         wait_lgkm0();  // the stores are complete before the loop's first barrier
     };
@@ -642,16 +665,16 @@ __global__ __launch_bounds__(64 * NW) void big_fwd2_kernel(BigArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
-    const int krot = k_rotation(H / kBK);
+    const int krot = k_rotation(H / kBK), krot1 = FUSE ? k_rotation(nks) : krot;
     auto issue = [&](int s, int buf) {
         uint16_t* st_ = smem + buf * STG;
-        const int k0 = ((s + krot) & (H / kBK - 1)) * kBK;
-        dma_kc<H, NT>(A, H, H, k0, st_);
-        dma_kc<kFwd2Samples, NT>(Bm, H, srows, k0, st_ + H * kBK);
+        const int k0 = ((s + krot1) % nks) * kBK;
+        dma_kc<H, NT>(A, lda, H, k0, st_);
+        dma_kc<kFwd2Samples, NT>(Bm, ldb, srows, k0, st_ + H * kBK);
     };
     if constexpr (H == 512) {
         // no registers for a second fragment set next to this epilogue
-        kloop1<NST, LPT>(H / kBK, issue, [&](int buf) {
+        kloop1<NST, LPT>(nks, issue, [&](int buf) {
             const uint16_t* ta = smem + buf * STG + ((H / NW) * wv) * kBK + lo;
             const uint16_t* tb = smem + buf * STG + H * kBK + lo;
             bf16x8 fa[MT], fb[8];
@@ -668,7 +691,7 @@ __global__ __launch_bounds__(64 * NW) void big_fwd2_kernel(BigArgs a) {
     } else {
         bf16x8 fa[MT], fb[2][8];  // fa: one set, re-read row by row (see kloop)
         kloop<NST, LPT>(
-            H / kBK, issue,
+            nks, issue,
             [&](int buf, auto p) {
                 constexpr int P = decltype(p)::value;
                 const uint16_t* ta = smem + buf * STG + ((H / NW) * wv) * kBK + lo;
@@ -689,7 +712,48 @@ __global__ __launch_bounds__(64 * NW) void big_fwd2_kernel(BigArgs a) {
             pre);
     }
 
-    const int l = threadIdx.x & 63, l16 = l & 15, q = l >> 4;
+    if constexpr (FUSE) {
+        // lane coordinates formed afresh in each phase (opaque_tid), so that
+        // no phase's addresses are held across another phase's loop
+        const int ta1 = opaque_tid(), l16a = ta1 & 15, fb0a = (H / NW) * wv + 4 * ((ta1 & 63) >> 4);
+        // h1 = relu(z1 + b1) to the LDS tile ([sample][feature], the layout
+        // the dz2 tile takes below) and relu'(z1) as bits, bit 4 j + r of
+        // word i for this lane's feature 16 i + r and sample 16 j + l16 --
+        // the accumulator layout the dh1 product ends with
+        __syncthreads();  // every wave is done with the ring
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            uint32_t bits = 0u;
+            float b1[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) b1[r] = sb1[fb0a + 16 * i + r];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float y[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    // relu as an integer max on the bit pattern (negative
+                    // values and -0 become +0), the bit from the result
+                    const int zb = max(__float_as_int(acc[i][j][r] + b1[r]), 0);
+                    y[r] = __int_as_float(zb);
+                    bits |= min((uint32_t)zb, 1u) << (4 * j + r);
+                }
+                *(u32x2*)(smem + stage_off<H>(16 * j + l16a, fb0a + 16 * i)) = u32x2{cvt2(y[0], y[1]), cvt2(y[2], y[3])};
+            }
+            smask[i * NT + ta1] = bits;
+        }
+        // z2 = W2 h1 from the tile: W2's rows from global memory (the first
+        // k-step's fragments issued before the h1 stores, so that waiting for
+        // them does not wait for the stores), h1 from LDS
+        const int ta2 = opaque_tid(), l16b = ta2 & 15, qb = (ta2 & 63) >> 4;
+        const uint16_t* A2 = a.w2s + (int64_t)g * H * H + (int64_t)((H / NW) * wv + l16b) * H + 8 * qb;
+        bf16x8 fz[MT];
+        w2t_frags<H, MT>(A2, krot, fz);
+        __syncthreads();
+        if (!a.fwd_only) stage_out<H, kFwd2Samples, NT>(smem, a.h1 + ((int64_t)g * B + s0) * H, H, srows, opaque_tid());
+        lds_b_product<H, MT>(A2, smem, acc, fz, krot, l16b, qb);
+    }
+    const int l = (FUSE ? opaque_tid() : (int)threadIdx.x) & 63, l16 = l & 15, q = l >> 4;
     const int fb0 = (H / NW) * wv + 4 * q;
     // z2 = acc + b2 (formed again in each pass below, so the accumulators
     // are only read); this wave's part of v for each of its 8 samples
@@ -795,7 +859,7 @@ __global__ __launch_bounds__(64 * NW) void big_fwd2_kernel(BigArgs a) {
     if constexpr (BWD) w2t_frags<H, MT>(w2t_lane<H, NW>(a, g, wv, l16, q), krot, fa0);
     __syncthreads();
     stage_out<H, kFwd2Samples, NT>(smem, a.dz2 + ((int64_t)g * B + s0) * H, H, srows);
-    if constexpr (BWD) backward_h1<H, MT, NW>(a, smem, acc, fa0, g, blk, s0, srows, wv, l, l16, q, krot);
+    if constexpr (BWD) backward_h1<H, MT, NW, FUSE>(a, smem, acc, fa0, g, blk, s0, srows, wv, l, l16, q, krot, smask);
 }
 
 // --------------------------------------------------------------- wgrad
@@ -914,7 +978,7 @@ constexpr size_t ring_lds_bytes(int nst) { return (size_t)nst * 2 * kTile * kBK 
 template <int H>
 constexpr size_t fwd2_lds_bytes() {
     return (size_t)(3 * (H + kFwd2Samples) * kBK > kFwd2Samples * H ? 3 * (H + kFwd2Samples) * kBK : kFwd2Samples * H) * 2 +
-           ((kFwd2Waves + 1) * kFwd2Samples + 2 * H) * sizeof(float);
+           ((kFwd2Waves + 1) * kFwd2Samples + 3 * H + (H / (16 * kFwd2Waves)) * 64 * kFwd2Waves) * sizeof(float);
 }
 
 template <typename K>
@@ -991,24 +1055,30 @@ static hipError_t big_launch(const IqlDims& d, const IqlBuffers& b, const float*
     if (!attr) {
         hipError_t e = allow_lds(big_fwd1_kernel, ring_lds_bytes(kTileStages));
         if (e == hipSuccess) e = allow_lds(big_wgrad_kernel, ring_lds_bytes(kWgradStages));
-        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<256, false, kFwd2Waves>, fwd2_lds_bytes<256>());
-        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<512, false, kFwd2Waves>, fwd2_lds_bytes<512>());
-        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<256, true, kFwd2Waves>, fwd2_lds_bytes<256>());
-        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<512, true, kFwd2Waves>, fwd2_lds_bytes<512>());
+        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<256, false, kFwd2Waves, kFuseF1>, fwd2_lds_bytes<256>());
+        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<512, false, kFwd2Waves, kFuseF1>, fwd2_lds_bytes<512>());
+        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<256, true, kFwd2Waves, kFuseF1>, fwd2_lds_bytes<256>());
+        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<512, true, kFwd2Waves, kFuseF1>, fwd2_lds_bytes<512>());
         if (e != hipSuccess) return e;
         attr = true;
     }
-    const int nst = (B + kTile - 1) / kTile;
-    const dim3 gt(nst * (H / kTile), G);
-    hipLaunchKernelGGL(big_fwd1_kernel, gt, dim3(64 * kFwd1Waves), ring_lds_bytes(kTileStages), stream, a);
-    const dim3 g2(a.nblk, G);
+    if (!kFuseF1) {
+        const int nst = (B + kTile - 1) / kTile;
+        const dim3 gt(nst * (H / kTile), G);
+        hipLaunchKernelGGL(big_fwd1_kernel, gt, dim3(64 * kFwd1Waves), ring_lds_bytes(kTileStages), stream, a);
+    }
+    const dim3 g2(a.nblk, G), t2(64 * kFwd2Waves);
     if (vo) {
-        if (H == 512) hipLaunchKernelGGL((big_fwd2_kernel<512, false, kFwd2Waves>), g2, dim3(64 * kFwd2Waves), fwd2_lds_bytes<512>(), stream, a);
-        else hipLaunchKernelGGL((big_fwd2_kernel<256, false, kFwd2Waves>), g2, dim3(64 * kFwd2Waves), fwd2_lds_bytes<256>(), stream, a);
+        if (H == 512)
+            hipLaunchKernelGGL((big_fwd2_kernel<512, false, kFwd2Waves, kFuseF1>), g2, t2, fwd2_lds_bytes<512>(), stream, a);
+        else
+            hipLaunchKernelGGL((big_fwd2_kernel<256, false, kFwd2Waves, kFuseF1>), g2, t2, fwd2_lds_bytes<256>(), stream, a);
         return hipGetLastError();
     }
-    if (H == 512) hipLaunchKernelGGL((big_fwd2_kernel<512, true, kFwd2Waves>), g2, dim3(64 * kFwd2Waves), fwd2_lds_bytes<512>(), stream, a);
-    else hipLaunchKernelGGL((big_fwd2_kernel<256, true, kFwd2Waves>), g2, dim3(64 * kFwd2Waves), fwd2_lds_bytes<256>(), stream, a);
+    if (H == 512)
+        hipLaunchKernelGGL((big_fwd2_kernel<512, true, kFwd2Waves, kFuseF1>), g2, t2, fwd2_lds_bytes<512>(), stream, a);
+    else
+        hipLaunchKernelGGL((big_fwd2_kernel<256, true, kFwd2Waves, kFuseF1>), g2, t2, fwd2_lds_bytes<256>(), stream, a);
     const dim3 gw(a.nchunk * big_tiles(S, H), G);
     hipLaunchKernelGGL(big_wgrad_kernel, gw, dim3(64 * kWgradWaves), ring_lds_bytes(kWgradStages), stream, a);
     return hipGetLastError();
