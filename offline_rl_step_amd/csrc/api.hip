@@ -154,7 +154,6 @@ int iql_create(const iqlh_config* cfg, const float* init_params_host, iql_handle
     b.act_h1 = b.act_dz2 = b.act_p2 = b.act_dz1 = nullptr;
     b.act_z2 = b.act_dv = nullptr;
     b.big_spart = nullptr;
-    b.big_mask = nullptr;
     // activations: h1, dz1 [G][MB][H]; z2, dz2, p2 [G][MB][H2] (layered-only:
     // z2, p2 and dv)
     const size_t nact = d.layered ? (size_t)G * MB * H : 0;
@@ -185,7 +184,6 @@ int iql_create(const iqlh_config* cfg, const float* init_params_host, iql_handle
         {(void**)&b.act_dz1, esz * nact},
         {(void**)&b.act_dv, sizeof(float) * (nlay ? (size_t)G * MB : 0)},
         {(void**)&b.big_spart, sizeof(float) * (d.big ? (size_t)G * iql_big_blocks((int)MB) * iql_big_spart_width(H) : 0)},
-        {(void**)&b.big_mask, sizeof(uint32_t) * (d.big ? iql_big_mask_words(G, (int)MB, H) : 0)},
     };
     for (auto& a : plan) {
         if (a.bytes == 0) continue;

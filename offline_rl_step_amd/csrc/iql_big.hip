@@ -4,10 +4,10 @@
 // Plan", section "Current State / IQL (CPU)"; the backward products of "Phase
 // 2: Multi-Stream Graph Parallelism", section "2C. Grouped GEMM for IQL"):
 //
-//   fwd1   h1 = relu(W1 s + b1)                         -> H1  [B][H] bf16,
-//          and relu'(z1) as bits for the backward product
-//   fwd2   z2 = W2 h1 + b2 over all H features of a 128-sample block, then in
-//          the epilogue v = w3 . relu(z2) + b3, the expectile loss, dv,
+//   fwd2   for all H features of a 128-sample block: h1 = relu(W1 s + b1),
+//          kept in LDS (and stored -> H1 [B][H] bf16 for wgrad) with
+//          relu'(z1) as bits; z2 = W2 h1 + b2 from that tile, then in the
+//          epilogue v = w3 . relu(z2) + b3, the expectile loss, dv,
 //          dz2 = dv w3 relu'(z2) -> DZ2 [B][H] bf16, and the block's sums of
 //          dz2 (db2), dv relu(z2) (dw3) and dv (db3); in training the same
 //          workgroup goes on with dh1 = W2^T dz2 from its dz2 tile in LDS,
@@ -19,19 +19,21 @@
 // then the fixed-order partial reduction and Adam shared with the other
 // paths (no float atomics anywhere).
 //
-// MI355X design.  Every product runs on v_mfma_f32_16x16x32_bf16.  fwd1 and
-// wgrad hold a 128 x 128 output tile per wave (8 x 8 MFMA tiles, 256
-// accumulators), four waves per workgroup and one workgroup per CU; fwd2
-// splits its H x 128 tile over eight waves (two per SIMD, H / 8 features
-// each), so that one wave's dependent epilogue arithmetic and LDS round
-// trips overlap the other's.  Operands stream HBM -> LDS
-// with global_load_lds_dwordx4 (no register staging) through a ring of 32-k
-// stages; each stage ends in one s_barrier after the wave's own vmcnt wait,
-// and the fragments of the next stage are read from LDS while the current
-// stage's MFMAs run.  Activations are row-major [sample][feature]:
-//   * in the forward products k is the feature (contiguous): LDS rows of 32 k
-//     (64 bytes), the 16-byte unit u of row r stored at u ^ ((r >> 1) & 3),
-//     read with ds_read_b128 (conflict-free);
+// MI355X design.  Every product runs on v_mfma_f32_16x16x32_bf16, with
+// eight waves per workgroup (two per SIMD, so that one wave's dependent
+// epilogue arithmetic and LDS round trips overlap the other's MFMAs) and
+// one workgroup per CU: wgrad splits its 256 x 256 tile into 128 x 64 wave
+// tiles, fwd2 its H x 128 tile into H / 8 features per wave.  Streamed
+// operands go HBM -> LDS with global_load_lds_dwordx4 (no register staging)
+// through a ring of 32-k stages; each stage ends in one s_barrier after the
+// wave's own vmcnt wait, and the fragments of the next stage are read from
+// LDS while the current stage's MFMAs run.  The products whose B operand is
+// a tile already in LDS (z2 = W2 h1, dh1 = W2^T dz2) take their A operand
+// (weights, L2-resident) straight from global memory into registers, one
+// k-step ahead.  Activations are row-major [sample][feature]:
+//   * in the ring's forward product k is the feature (contiguous): LDS rows
+//     of 32 k (64 bytes), the 16-byte unit u of row r stored at
+//     u ^ ((r >> 1) & 3), read with ds_read_b128 (conflict-free);
 //   * in the weight gradients k is the sample: LDS keeps the natural
 //     [sample][feature] rows (512 bytes), unit v of sample s stored at
 //     v ^ (2 (s & 3)), and the MFMA operands are read with the LDS transpose
@@ -61,11 +63,7 @@ constexpr int kThreads = 256;
 constexpr int kBK = 32;           // k per stage
 constexpr int kFwd2Samples = 128; // samples per fwd2 block (the loss blocks)
 constexpr int kFwd2Waves = 8;     // waves of a fwd2 workgroup (two per SIMD)
-// fwd2 forms z1 = W1 s itself and keeps h1 in LDS (no fwd1 launch)
-constexpr bool kFuseF1 = true;
-constexpr int kTile = 256;        // fwd1 / wgrad output tile edge
-constexpr int kTileStages = 5;    // ring depth of fwd1 (5 x 32 KB)
-constexpr int kFwd1Waves = 8;     // waves of a fwd1 workgroup (two per SIMD)
+constexpr int kTile = 256;        // wgrad output tile edge
 constexpr int kWgradStages = 5;   // ring depth of wgrad (5 x 32 KB)
 constexpr int kWgradWaves = 8;    // waves of a wgrad workgroup (two per SIMD)
 // entries of a loss block's sums: db2 [H], dw3 [H], db3, db1 [H]
@@ -340,7 +338,6 @@ struct BigArgs {
     uint16_t* dz2;          // [G][B][H]
     uint16_t* dz1;          // [G][B][H]
     float* spart;           // [G][nblk][3H + 1]: db2, dw3, db3 and db1 of each 128-sample block
-    uint32_t* mask;         // [G][tiles][256 lanes][8 words]: relu'(z1) bits from fwd1
     float* loss_part;       // [G][nblk]
     float* out_v;           // [G][B] or null
     float* part;            // [G][nchunk][Pp]
@@ -352,13 +349,6 @@ struct BigArgs {
     ValueOut vo;
 };
 
-// First word of the ReLU mask bits of lane t of fwd1's tile (st, ft) of group
-// g: 8 words per lane, bit 4 j + r of word i for feature 128 wm + 16 i + 4 q + r
-// and sample 128 wn + 16 j + l16 of the tile (t = 64 (wm + 2 wn) + 16 q + l16).
-IQLH_DEV int64_t mask_word0(const BigArgs& a, int g, int st, int ft, int t) {
-    const int nst = (a.B + kTile - 1) / kTile, nft = a.H / kTile;
-    return ((((int64_t)g * nst + st) * nft + ft) * kThreads + t) * 8;
-}
 
 // Workgroup id -> (tile, group): consecutive ids go to different XCDs, so the
 // ids of one sample range are spread as id = xcd + 8 k; this picks the tiles
@@ -382,122 +372,13 @@ IQLH_DEV void xcd_map(int id, int nranges, int nper, int& range, int& job) {
 // workgroup still adds every slice once, in a fixed order (deterministic).
 IQLH_DEV int k_rotation(int nks) { return (int)((blockIdx.x >> 3) % (unsigned)nks); }
 
-// ---------------------------------------------------------------- fwd1
-// D[f][s] = sum_k W1[f][k] s[s][k] over a 256-feature x 256-sample tile;
-// h1 = relu(D + b1), and the ReLU mask as bits for the backward product.
-__global__ __launch_bounds__(64 * kFwd1Waves) void big_fwd1_kernel(BigArgs a) {
-    extern __shared__ __align__(16) uint16_t smem[];
-    // wave w: features 128 (w & 1) .. + 127 and samples (256 / NC) (w >> 1) ..
-    // of the tile, NC = waves / 2 sample groups of JT sample tiles
-    constexpr int NT = 64 * kFwd1Waves, NC = kFwd1Waves / 2, JT = 16 / NC;
-    constexpr int NST = kTileStages, STG = 2 * kTile * kBK;  // elements per stage
-    const int g = blockIdx.y;
-    const int H = a.H, B = a.B;
-    const int nft = H / kTile, nst = (B + kTile - 1) / kTile;
-    int st, ft;
-    xcd_map(blockIdx.x, nst, nft, st, ft);
-    const int f0 = ft * kTile, s0 = st * kTile;
-    const uint16_t* A = a.w1s + (int64_t)g * H * a.ldw1 + (int64_t)f0 * a.ldw1;
-    const uint16_t* Bm = a.x + (int64_t)s0 * a.ldx;
-    const int srows = B - s0;
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wv & 1, wn = wv >> 1;
-    const int lo = kc_lane();
-
-    f4 acc[8][JT];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < JT; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
-    const int l = threadIdx.x & 63, l16 = l & 15, q = l >> 4;
-
-    bf16x8 fa[8], fb[2][JT];  // fa: one set, re-read row by row (see kloop)
-    const int nks = a.S / kBK, krot = k_rotation(nks);
-    kloop<NST, 2 * kTile * 4 / NT>(
-        nks,
-        [&](int s, int buf) {
-            uint16_t* st_ = smem + buf * STG;
-            const int k0 = ((s + krot) % nks) * kBK;
-            dma_kc<kTile, NT>(A, a.ldw1, kTile, k0, st_);
-            dma_kc<kTile, NT>(Bm, a.ldx, srows, k0, st_ + kTile * kBK);
-        },
-        [&](int buf, auto p) {
-            constexpr int P = decltype(p)::value;
-            const uint16_t* ta = smem + buf * STG + (128 * wm) * kBK + lo;
-            const uint16_t* tb = smem + buf * STG + kTile * kBK + (16 * JT * wn) * kBK + lo;
-#pragma unroll
-            for (int j = 0; j < JT; ++j) fb[P][j] = *(const bf16x8*)(tb + j * 16 * kBK);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) fa[i] = *(const bf16x8*)(ta + i * 16 * kBK);
-        },
-        [&](auto p) {
-            constexpr int P = decltype(p)::value;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < JT; ++j) acc[i][j] = mma(fa[i], fb[P][j], acc[i][j]);
-            reads_among_mfma<8 + JT, 8 * JT>();
-        },
-        no_pre);
-
-    // epilogue: lane holds features 128 wm + 16 i + 4 q + r of samples
-    // 16 (JT wn + j) + l16 (tile-local); staged as [sample][feature] rows.
-    // relu'(z1) leaves as bits in the layout of mask_word0, whose lane covers
-    // the 8 sample tiles of a 128-sample half: this wave's JT tiles are the
-    // bits 4 JT (wn % (8 / JT)) .. of each word.
-    const float* bias = a.params + (int64_t)g * a.P + a.off_b1 + f0;
-    uint32_t mbits[8];
-    __syncthreads();  // every wave is done with the last stage
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int f = 128 * wm + 16 * i + 4 * q;
-        float bb[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) bb[r] = bias[f + r];
-        mbits[i] = 0u;
-#pragma unroll
-        for (int j = 0; j < JT; ++j) {
-            const int sl = 16 * (JT * wn + j) + l16;
-            float y[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                // relu as an integer max on the bit pattern (negative values
-                // and -0 become +0), and the mask bit from the result, so no
-                // compare results have to be held
-                const int zb = max(__float_as_int(acc[i][j][r] + bb[r]), 0);
-                y[r] = __int_as_float(zb);
-                mbits[i] |= min((uint32_t)zb, 1u) << (4 * j + r);
-            }
-            *(u32x2*)(smem + stage_off<kTile>(sl, f)) = u32x2{cvt2(y[0], y[1]), cvt2(y[2], y[3])};
-        }
-    }
-    if (!a.fwd_only) {
-        static_assert(JT == 4 || JT == 8, "mask word pieces");
-        // lane t of the word layout: 128-feature half wm, 128-sample half
-        // (JT wn) / 8, this lane's place in the wave
-        const int t = 64 * (wm + 2 * ((JT * wn) / 8)) + l;
-        uint32_t* mw = a.mask + mask_word0(a, g, st, ft, t);
-        if constexpr (JT == 8) {
-            u32x4* mp = (u32x4*)mw;
-            mp[0] = u32x4{mbits[0], mbits[1], mbits[2], mbits[3]};
-            mp[1] = u32x4{mbits[4], mbits[5], mbits[6], mbits[7]};
-        } else {
-            uint16_t* mh = (uint16_t*)mw + (wn & 1);  // low or high half of each word
-#pragma unroll
-            for (int i = 0; i < 8; ++i) mh[2 * i] = (uint16_t)mbits[i];
-        }
-    }
-    __syncthreads();
-    stage_out<kTile, kTile, NT>(smem, a.h1 + ((int64_t)g * B + s0) * H + f0, H, srows);
-}
-
 // ------------------------------------------------- dh1 inside fwd2's workgroup
 // dh1[f][s] = sum_k W2^T[f][k] dz2[s][k] for the H features of this wave's
 // rows ((H / NW) w + 16 i + .., NW waves) and the block's 128 samples, K = H.  The B
 // operand is the dz2 tile staged in LDS ([sample][feature], 16-byte unit u of
 // row s at u ^ (s & 7)); the A operand comes from the W2^T shadow in global
 // memory (L2-resident after the first blocks), 16 bytes per lane, loaded one
-// k-step ahead.  Then dz1 = dh1 relu'(z1) from fwd1's mask bits, the block's
+// k-step ahead.  Then dz1 = dh1 relu'(z1) from the forward's mask bits, the block's
 // db1 sums from dz1 as stored, and dz1 staged and stored as whole rows.
 template <int H, int NW>
 IQLH_DEV const uint16_t* w2t_lane(const BigArgs& a, int g, int wv, int l16, int q) {
@@ -545,26 +426,16 @@ IQLH_DEV void lds_b_product(const uint16_t* At, const uint16_t* smem, f4 (&acc)[
     }
 }
 
-template <int H, int MT, int NW, bool FUSE>
+template <int H, int MT, int NW>
 IQLH_DEV void backward_h1(const BigArgs& a, uint16_t* smem, f4 (&acc)[MT][8], bf16x8 (&fa0)[MT], int g, int blk,
                           int s0, int srows, int wv, int l, int l16, int q, int krot, const uint32_t* smask) {
     // (l16 and q are formed again from the thread index before the epilogue)
     static_assert(MT * 16 * NW == H, "row tiles");
     const uint16_t* At = w2t_lane<H, NW>(a, g, wv, l16, q);
-    // this lane's relu'(z1) words: from the fused forward's LDS copy (FUSE),
-    // else fwd1's words -- tile (s0 / 256, f / 256), lane 64 (wm + 2 wn) + l
-    // with wn = the block's half of its 256-sample tile
+    // this lane's relu'(z1) words, left in LDS by the forward product
     uint32_t mb[MT];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-        if constexpr (FUSE) {
-            mb[i] = smask[i * (64 * NW) + (int)threadIdx.x];
-        } else {
-            const int f = (H / NW) * wv + 16 * i;
-            const int ft = f / kTile, wm = (f % kTile) / 128, word = (f % 128) / 16;
-            mb[i] = a.mask[mask_word0(a, g, s0 / kTile, ft, 64 * (wm + 2 * (blk & 1)) + l) + word];
-        }
-    }
+    for (int i = 0; i < MT; ++i) mb[i] = smask[i * (64 * NW) + (int)threadIdx.x];
     lds_b_product<H, MT>(At, smem, acc, fa0, krot, l16, q);
     __syncthreads();  // every wave is done with the dz2 tile
     // lane coordinates formed again here (opaque_tid): otherwise the compiler
@@ -617,24 +488,27 @@ IQLH_DEV float wave_parts_sum(const float* svp, int sl) {
 }
 
 // --------------------------------------------------------------- fwd2
-// All H features of 128 samples: z2 = W2 h1 + b2 and the loss epilogue.
-// Wave w of NW owns features (H / NW) w .. + H / NW - 1 (MT row tiles of 16).
+// All H features of 128 samples: z1 = W1 s through the ring, h1 =
+// relu(z1 + b1) to LDS, z2 = W2 h1 + b2 from it, and the loss epilogue.
+// Wave w of NW owns features (H / NW) w .. + H / NW - 1 (MT row tiles of 16)
+// of every layer, so the mask bits of relu'(z1) sit in the lanes that form
+// dh1 for the same features and samples.
 // With BWD, the same workgroup then forms dh1 = W2^T dz2 for its samples from
 // the dz2 tile still staged in LDS, and dz1 = dh1 relu'(z1) with the block's
 // db1 sums, so dz2 is never read back from memory for it.
-template <int H, bool BWD, int NW, bool FUSE>
+template <int H, bool BWD, int NW>
 __global__ __launch_bounds__(64 * NW) void big_fwd2_kernel(BigArgs a) {
     extern __shared__ __align__(16) uint16_t smem[];
     constexpr int NT = 64 * NW, MT = H / (16 * NW), NST = 3, STG = (H + kFwd2Samples) * kBK;
     constexpr int LPT = (H + kFwd2Samples) * 4 / NT;
     const int g = blockIdx.y, blk = blockIdx.x;
     const int B = a.B, s0 = blk * kFwd2Samples;
-    // the ring's product: z1 = W1 s (FUSE) or z2 = W2 h1 with h1 from fwd1
-    const uint16_t* A = FUSE ? a.w1s + (int64_t)g * H * a.ldw1 : a.w2s + (int64_t)g * H * H;
-    const int64_t lda = FUSE ? a.ldw1 : H;
-    const uint16_t* Bm = FUSE ? a.x + (int64_t)s0 * a.ldx : a.h1 + ((int64_t)g * B + s0) * H;
-    const int64_t ldb = FUSE ? a.ldx : H;
-    const int nks = FUSE ? a.S / kBK : H / kBK;
+    // the ring's product: z1 = W1 s over the state's k-slices
+    const uint16_t* A = a.w1s + (int64_t)g * H * a.ldw1;
+    const int64_t lda = a.ldw1;
+    const uint16_t* Bm = a.x + (int64_t)s0 * a.ldx;
+    const int64_t ldb = a.ldx;
+    const int nks = a.S / kBK;
     const int srows = B - s0;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lo = kc_lane();
@@ -643,8 +517,8 @@ __global__ __launch_bounds__(64 * NW) void big_fwd2_kernel(BigArgs a) {
     float* sq = svp + NW * kFwd2Samples;                            // [128] q of the block's samples
     float* sb2 = sq + kFwd2Samples;                                 // [H] b2
     float* sw3 = sb2 + H;                                           // [H] w3
-    float* sb1 = sw3 + H;                                           // [H] b1 (FUSE)
-    uint32_t* smask = (uint32_t*)(sb1 + H);                         // [MT][NT] relu'(z1) words (FUSE)
+    float* sb1 = sw3 + H;                                           // [H] b1
+    uint32_t* smask = (uint32_t*)(sb1 + H);                         // [MT][NT] relu'(z1) words
     const float* prm = a.params + (int64_t)g * a.P;
     // q, b2 and w3 to LDS while the first stages are in flight, so that the
     // epilogue reads them without a memory round trip
@@ -654,7 +528,7 @@ __global__ __launch_bounds__(64 * NW) void big_fwd2_kernel(BigArgs a) {
         for (int f = t; f < H; f += NT) {
             sb2[f] = prm[a.off_b2 + f];
             sw3[f] = prm[a.off_w3 + f];
-            if (FUSE) sb1[f] = prm[a.off_b1 + f];
+            sb1[f] = prm[a.off_b1 + f];
         }
         wait_lgkm0();  // the stores are complete before the loop's first barrier
     };
@@ -665,7 +539,7 @@ __global__ __launch_bounds__(64 * NW) void big_fwd2_kernel(BigArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
-    const int krot = k_rotation(H / kBK), krot1 = FUSE ? k_rotation(nks) : krot;
+    const int krot = k_rotation(H / kBK), krot1 = k_rotation(nks);
     auto issue = [&](int s, int buf) {
         uint16_t* st_ = smem + buf * STG;
         const int k0 = ((s + krot1) % nks) * kBK;
@@ -712,7 +586,7 @@ __global__ __launch_bounds__(64 * NW) void big_fwd2_kernel(BigArgs a) {
             pre);
     }
 
-    if constexpr (FUSE) {
+    {
         // lane coordinates formed afresh in each phase (opaque_tid), so that
         // no phase's addresses are held across another phase's loop
         const int ta1 = opaque_tid(), l16a = ta1 & 15, fb0a = (H / NW) * wv + 4 * ((ta1 & 63) >> 4);
@@ -753,7 +627,7 @@ __global__ __launch_bounds__(64 * NW) void big_fwd2_kernel(BigArgs a) {
         if (!a.fwd_only) stage_out<H, kFwd2Samples, NT>(smem, a.h1 + ((int64_t)g * B + s0) * H, H, srows, opaque_tid());
         lds_b_product<H, MT>(A2, smem, acc, fz, krot, l16b, qb);
     }
-    const int l = (FUSE ? opaque_tid() : (int)threadIdx.x) & 63, l16 = l & 15, q = l >> 4;
+    const int l = opaque_tid() & 63, l16 = l & 15, q = l >> 4;
     const int fb0 = (H / NW) * wv + 4 * q;
     // z2 = acc + b2 (formed again in each pass below, so the accumulators
     // are only read); this wave's part of v for each of its 8 samples
@@ -859,7 +733,7 @@ __global__ __launch_bounds__(64 * NW) void big_fwd2_kernel(BigArgs a) {
     if constexpr (BWD) w2t_frags<H, MT>(w2t_lane<H, NW>(a, g, wv, l16, q), krot, fa0);
     __syncthreads();
     stage_out<H, kFwd2Samples, NT>(smem, a.dz2 + ((int64_t)g * B + s0) * H, H, srows);
-    if constexpr (BWD) backward_h1<H, MT, NW, FUSE>(a, smem, acc, fa0, g, blk, s0, srows, wv, l, l16, q, krot, smask);
+    if constexpr (BWD) backward_h1<H, MT, NW>(a, smem, acc, fa0, g, blk, s0, srows, wv, l, l16, q, krot, smask);
 }
 
 // --------------------------------------------------------------- wgrad
@@ -993,10 +867,6 @@ bool iql_big_supported(int dtype, int S, int H) {
 }
 int iql_big_blocks(int B) { return (B + kFwd2Samples - 1) / kFwd2Samples; }
 int iql_big_spart_width(int H) { return spart_w(H); }
-// ReLU mask words: 8 per lane of every fwd1 tile (256 lanes)
-size_t iql_big_mask_words(int G, int B, int H) {
-    return (size_t)G * ((B + kTile - 1) / kTile) * (H / kTile) * kThreads * 8;
-}
 static int big_tiles(int S, int H) {
     const int nth = H / kTile, nts = (S + kTile - 1) / kTile;
     return nth * nth + nth * nts;
@@ -1037,7 +907,7 @@ static hipError_t big_launch(const IqlDims& d, const IqlBuffers& b, const float*
     a.w2s = (const uint16_t*)b.w2s; a.w2ts = (const uint16_t*)b.w2ts;
     a.params = b.params; a.q = q;
     a.h1 = (uint16_t*)b.act_h1; a.dz2 = (uint16_t*)b.act_dz2; a.dz1 = (uint16_t*)b.act_dz1;
-    a.spart = b.big_spart; a.mask = b.big_mask; a.loss_part = b.loss_part; a.out_v = out_v; a.part = b.part;
+    a.spart = b.big_spart; a.loss_part = b.loss_part; a.out_v = out_v; a.part = b.part;
     a.P = d.P; a.Pp = d.Pp;
     a.off_b1 = (int64_t)H * S; a.off_w2 = a.off_b1 + H; a.off_b2 = a.off_w2 + (int64_t)H * H;
     a.off_w3 = a.off_b2 + H; a.off_b3 = a.off_w3 + H;
@@ -1053,32 +923,26 @@ static hipError_t big_launch(const IqlDims& d, const IqlBuffers& b, const float*
 
     static bool attr = false;
     if (!attr) {
-        hipError_t e = allow_lds(big_fwd1_kernel, ring_lds_bytes(kTileStages));
-        if (e == hipSuccess) e = allow_lds(big_wgrad_kernel, ring_lds_bytes(kWgradStages));
-        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<256, false, kFwd2Waves, kFuseF1>, fwd2_lds_bytes<256>());
-        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<512, false, kFwd2Waves, kFuseF1>, fwd2_lds_bytes<512>());
-        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<256, true, kFwd2Waves, kFuseF1>, fwd2_lds_bytes<256>());
-        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<512, true, kFwd2Waves, kFuseF1>, fwd2_lds_bytes<512>());
+        hipError_t e = allow_lds(big_wgrad_kernel, ring_lds_bytes(kWgradStages));
+        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<256, false, kFwd2Waves>, fwd2_lds_bytes<256>());
+        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<512, false, kFwd2Waves>, fwd2_lds_bytes<512>());
+        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<256, true, kFwd2Waves>, fwd2_lds_bytes<256>());
+        if (e == hipSuccess) e = allow_lds(big_fwd2_kernel<512, true, kFwd2Waves>, fwd2_lds_bytes<512>());
         if (e != hipSuccess) return e;
         attr = true;
-    }
-    if (!kFuseF1) {
-        const int nst = (B + kTile - 1) / kTile;
-        const dim3 gt(nst * (H / kTile), G);
-        hipLaunchKernelGGL(big_fwd1_kernel, gt, dim3(64 * kFwd1Waves), ring_lds_bytes(kTileStages), stream, a);
     }
     const dim3 g2(a.nblk, G), t2(64 * kFwd2Waves);
     if (vo) {
         if (H == 512)
-            hipLaunchKernelGGL((big_fwd2_kernel<512, false, kFwd2Waves, kFuseF1>), g2, t2, fwd2_lds_bytes<512>(), stream, a);
+            hipLaunchKernelGGL((big_fwd2_kernel<512, false, kFwd2Waves>), g2, t2, fwd2_lds_bytes<512>(), stream, a);
         else
-            hipLaunchKernelGGL((big_fwd2_kernel<256, false, kFwd2Waves, kFuseF1>), g2, t2, fwd2_lds_bytes<256>(), stream, a);
+            hipLaunchKernelGGL((big_fwd2_kernel<256, false, kFwd2Waves>), g2, t2, fwd2_lds_bytes<256>(), stream, a);
         return hipGetLastError();
     }
     if (H == 512)
-        hipLaunchKernelGGL((big_fwd2_kernel<512, true, kFwd2Waves, kFuseF1>), g2, t2, fwd2_lds_bytes<512>(), stream, a);
+        hipLaunchKernelGGL((big_fwd2_kernel<512, true, kFwd2Waves>), g2, t2, fwd2_lds_bytes<512>(), stream, a);
     else
-        hipLaunchKernelGGL((big_fwd2_kernel<256, true, kFwd2Waves, kFuseF1>), g2, t2, fwd2_lds_bytes<256>(), stream, a);
+        hipLaunchKernelGGL((big_fwd2_kernel<256, true, kFwd2Waves>), g2, t2, fwd2_lds_bytes<256>(), stream, a);
     const dim3 gw(a.nchunk * big_tiles(S, H), G);
     hipLaunchKernelGGL(big_wgrad_kernel, gw, dim3(64 * kWgradWaves), ring_lds_bytes(kWgradStages), stream, a);
     return hipGetLastError();

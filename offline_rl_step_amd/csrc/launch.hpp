@@ -130,7 +130,6 @@ struct IqlBuffers {
     // [G][nblk][iql_big_spart_width(H)], and the ReLU masks of h1 that the
     // first forward product leaves for the first backward one
     float* big_spart;
-    uint32_t* big_mask;
 };
 bool iql_supported(int dtype, int S, int H);
 int iql_tile_samples(int dtype, int S, int H);
@@ -173,7 +172,6 @@ int iql_big_blocks(int B);
 int iql_big_max_chunks(int S, int H);
 int iql_big_chunk(int S, int H, int G, int B);
 int iql_big_spart_width(int H);
-size_t iql_big_mask_words(int G, int B, int H);
 hipError_t launch_iql_big_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float* tau, const void* states,
                                   int64_t ld, const float* q, int B, float* out_v, hipStream_t stream);
 hipError_t launch_iql_target_ema(const IqlDims& d, const IqlBuffers& b, float tau, hipStream_t stream);
