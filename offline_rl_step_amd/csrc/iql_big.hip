@@ -616,16 +616,16 @@ __global__ __launch_bounds__(64 * NW) void big_fwd2_kernel(BigArgs a) {
             }
             smask[i * NT + ta1] = bits;
         }
-        // z2 = W2 h1 from the tile: W2's rows from global memory (the first
-        // k-step's fragments issued before the h1 stores, so that waiting for
-        // them does not wait for the stores), h1 from LDS
+        // z2 = W2 h1 from the tile: W2's rows from global memory, h1 from
+        // LDS; h1 leaves for the weight gradients after the product, so that
+        // no wait for W2's fragments inside it waits for those stores too
         const int ta2 = opaque_tid(), l16b = ta2 & 15, qb = (ta2 & 63) >> 4;
         const uint16_t* A2 = a.w2s + (int64_t)g * H * H + (int64_t)((H / NW) * wv + l16b) * H + 8 * qb;
         bf16x8 fz[MT];
         w2t_frags<H, MT>(A2, krot, fz);
         __syncthreads();
-        if (!a.fwd_only) stage_out<H, kFwd2Samples, NT>(smem, a.h1 + ((int64_t)g * B + s0) * H, H, srows, opaque_tid());
         lds_b_product<H, MT>(A2, smem, acc, fz, krot, l16b, qb);
+        if (!a.fwd_only) stage_out<H, kFwd2Samples, NT>(smem, a.h1 + ((int64_t)g * B + s0) * H, H, srows, opaque_tid());
     }
     const int l = opaque_tid() & 63, l16 = l & 15, q = l >> 4;
     const int fb0 = (H / NW) * wv + 4 * q;
