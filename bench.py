@@ -1096,8 +1096,10 @@ def main():
     src_hash = kernel_source_hash()
     if default:
         kernel = "iql_fused16w_kernel<128,128,xvec>"
+    elif w.H in (256, 512) and w.dtype == "bf16" and w.S % 32 == 0:
+        kernel = "wide forward/backward (big_fwd2, big_wgrad and the policy; events around the launch)"
     elif w.H > 128:
-        kernel = "layered forward/backward (five kernels; events around the group)"
+        kernel = "layered forward/backward (events around the group)"
     else:
         kernel = "fused forward/backward"
     # the roof that bounds this launch: its algorithmic flops over the bytes

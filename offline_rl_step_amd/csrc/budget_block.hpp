@@ -165,35 +165,52 @@ IQLH_DEV void saxpy_block(const SourceSet& s, int64_t n, int vec, float mgn, con
         nrm[j] = sqrtf(c[j]);
         c[j] = j < s.k ? s.alpha[j] * budget_scale(nrm[j], s.frac[j] * mgn) : 0.f;
     }
-    // PIPE: software-pipelined, the next quad's loads (at a clamped index)
-    // issued before this quad's store, so that waiting for them never waits
-    // for the store as well (vmcnt counts both, in order) -- for the
-    // standalone pass, whose threads take many quads; it holds a second set
-    // of source quads, which would lower the occupancy of the merged launch
-    // whose reduction blocks share the kernel.  Same sums either way.
+    // PIPE: software-pipelined, the next quad's loads issued before this
+    // quad's store, so that waiting for them never waits for the store as
+    // well (vmcnt counts both, in order) -- for the standalone pass, whose
+    // threads take many quads; it holds a second set of source quads, which
+    // would lower the occupancy of the merged launch whose reduction blocks
+    // share the kernel.  A thread's last iteration re-reads its own quad
+    // (cached) rather than a common one: the same address from every thread
+    // would queue on one L2 channel.  Same sums either way.
     float acc = 0.f;
-    for (int64_t qd = q0; qd < quads; qd += stride) {
-        const int64_t nx = qd + stride, nc = nx < quads ? nx : quads - 1;
-        f32x4 x[kMaxSources];
-        if constexpr (PIPE) {
+    if constexpr (PIPE) {
+        for (int64_t qd = q0; qd < quads; qd += stride) {
+            const int64_t nx = qd + stride, nc = nx < quads ? nx : qd;
+            f32x4 x[kMaxSources];
 #pragma unroll
             for (int j = 0; j < kMaxSources; ++j)
                 x[j] = j < s.k ? ld4(s.ptr[j], 4 * nc, n, vec4) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        f32x4 g = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < kMaxSources; ++j)
-            if (j < s.k) g += c[j] * pre[j];
-        st4(grad, 4 * qd, n, vec, g);
-        acc = fmaf(g.x, g.x, fmaf(g.y, g.y, fmaf(g.z, g.z, fmaf(g.w, g.w, acc))));
-        if constexpr (PIPE) {
-#pragma unroll
-            for (int j = 0; j < kMaxSources; ++j) pre[j] = x[j];
-        } else {
-            // the next quad's loads after this quad's store
+            f32x4 g = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < kMaxSources; ++j)
-                pre[j] = j < s.k ? ld4(s.ptr[j], 4 * nc, n, vec4) : f32x4{0.f, 0.f, 0.f, 0.f};
+                if (j < s.k) g += c[j] * pre[j];
+            st4(grad, 4 * qd, n, vec, g);
+            acc = fmaf(g.x, g.x, fmaf(g.y, g.y, fmaf(g.z, g.z, fmaf(g.w, g.w, acc))));
+#pragma unroll
+            for (int j = 0; j < kMaxSources; ++j) pre[j] = x[j];
+        }
+    } else {
+        if (q0 < quads) {
+            f32x4 g = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < kMaxSources; ++j)
+                if (j < s.k) g += c[j] * pre[j];
+            st4(grad, 4 * q0, n, vec, g);
+            acc = fmaf(g.x, g.x, fmaf(g.y, g.y, fmaf(g.z, g.z, fmaf(g.w, g.w, acc))));
+        }
+        for (int64_t qd = q0 + stride; qd < quads; qd += stride) {
+            // every source's quad in flight before the first is used
+            f32x4 x[kMaxSources];
+#pragma unroll
+            for (int j = 0; j < kMaxSources; ++j)
+                x[j] = j < s.k ? ld4(s.ptr[j], 4 * qd, n, vec4) : f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 g = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < kMaxSources; ++j)
+                if (j < s.k) g += c[j] * x[j];
+            st4(grad, 4 * qd, n, vec, g);
+            acc = fmaf(g.x, g.x, fmaf(g.y, g.y, fmaf(g.z, g.z, fmaf(g.w, g.w, acc))));
         }
     }
     const float t = block_sum<kBT>(acc, red);
@@ -284,10 +301,10 @@ IQLH_DEV void adam_flat_block(float* __restrict__ params, float* __restrict__ gr
     const float decay = 1.f - hp.lr * hp.weight_decay;
     bool bad = false, bad_state = false;
     // software-pipelined as in saxpy_block: the next quad's state is loaded
-    // (at a clamped index) before this quad's stores
+    // before this quad's stores (the last iteration re-reads its own quad)
     f32x4 cg = pg, cm = pm, cv = pv, cp = pp;
     for (int64_t qd = q0; qd < quads; qd += stride) {
-        const int64_t nx = qd + stride, i1 = 4 * (nx < quads ? nx : quads - 1);
+        const int64_t nx = qd + stride, i1 = 4 * (nx < quads ? nx : qd);
         const f32x4 ng = ld4(grad, i1, n, vec4), nm = ld4(m, i1, n, vec4), nv = ld4(v, i1, n, vec4),
                     np = ld4(params, i1, n, vec4);
         adam_flat_quad(params, grad, m, v, 4 * qd, n, vec, cg * c, cm, cv, cp, bc1, bc2, decay, hp, bad, bad_state);

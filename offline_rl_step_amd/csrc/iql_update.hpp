@@ -188,12 +188,14 @@ IQLH_DEV void iql_adam_block(const IqlDims& d, const IqlBuffers& b, const AdamHy
                                    : ((nrm > hp.max_grad_norm && nrm > 0.f) ? hp.max_grad_norm / nrm : 1.f);
     const float decay = 1.f - hp.lr * hp.weight_decay;
     bool bad = false, bad_state = false;
-    // software-pipelined: the next parameter's state is loaded (at a clamped
-    // index) before this parameter's stores, so waiting for it never waits
-    // for the stores as well (vmcnt counts both, in order)
+    // software-pipelined: the next parameter's state is loaded before this
+    // parameter's stores, so waiting for it never waits for the stores as
+    // well (vmcnt counts both, in order).  The last iteration re-reads the
+    // thread's own element (cached): one common address for every thread
+    // would queue on one L2 channel.
     float cg = pg, cp = pp, cm = pm, cv = pv, ct = pt;
     for (int64_t i = i0; i < P; i += stride) {
-        const int64_t nx = i + stride, j1 = nx < P ? nx : P - 1;
+        const int64_t nx = i + stride, j1 = nx < P ? nx : i;
         const float ng = gr[j1], np = prm[j1], nm = m[j1], nv = v[j1], nt = tg[j1];
         iql_adam_param<T>(i, cg * c, cp, cm, cv, ct, bc1, bc2, decay, hp, H, H2, S, SP, prm, gr, m, v, tg, w1s, w2s,
                           w2ts, bad, bad_state);
