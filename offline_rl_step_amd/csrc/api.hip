@@ -294,7 +294,7 @@ int iql_train_step_aw(iql_handle h, const void* states, const float* q_taken, in
     if (rc) return rc;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
-    if (iql_fused_policy(h->dims, num_actions)) {
+    if (iql_policy_in_launch(h->dims, batch, num_actions, q_all, out_pi)) {
         e = launch_iql_fwd_bwd(h->dims, h->buf, h->cfg.tau, states, h->cfg.states_ld, q_taken, batch, out_v, s,
                                nullptr, nullptr, q_all, num_actions, beta, out_pi);
     } else {

@@ -6,12 +6,13 @@
 // the row maximum subtracted.
 //
 // HBM-bound.  Action counts of 4, 8, 16, 32 or 64 with 16-byte aligned rows
-// take the streaming kernel below (float4 per lane, rows split over lanes).
+// take the streaming form (aw_block.hpp: float4 per lane, rows split over lanes).
 // Any other A: a one-wave workgroup owns 64 consecutive rows (16384 rows give
 // 256 workgroups, one per CU): the [64, A] slab of Q is read once with
 // coalesced loads into LDS (padded to an odd row stride so the per-row reads
 // are bank-conflict free), every group's policy is computed from that one
 // copy, and each result slab is written back with coalesced stores.
+#include "aw_block.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -85,62 +86,15 @@ __global__ __launch_bounds__(kAwRows) void aw_policy_kernel(const float* __restr
     }
 }
 
-// Streaming form for action counts A = 4 LPR with LPR in {1, 2, 4, 8, 16} and
-// 16-byte aligned rows: LPR lanes own one row, one float4 of four actions
-// each, so a wave's load or store of 64 float4 covers 64 / LPR consecutive
-// rows (1 KB contiguous).  The row maximum and sum are xor-shuffles among the
-// row's lanes.  Each lane keeps kAwUnroll rows' loads in flight before it
-// computes, and the grid strides over the rows.
-constexpr int kAwVecThreads = 256, kAwUnroll = 4;
-typedef float f4v __attribute__((ext_vector_type(4)));
+// Streaming form (aw_block.hpp): 256-thread workgroups striding over the
+// rows.
+constexpr int kAwVecThreads = 256;
 
 template <int LPR>
 __global__ __launch_bounds__(kAwVecThreads) void aw_policy_vec_kernel(const float4* __restrict__ q,
                                                                    const float* __restrict__ v, int G, int64_t B,
                                                                    float beta, float4* __restrict__ pi) {
-    constexpr int RPW = kAwVecThreads / LPR;  // rows per workgroup pass
-    const int sub = threadIdx.x % LPR;
-    const int64_t stride = (int64_t)gridDim.x * RPW * kAwUnroll;
-    for (int64_t base = (int64_t)blockIdx.x * RPW * kAwUnroll; base < B; base += stride) {
-        float4 x[kAwUnroll];
-        int64_t row[kAwUnroll];
-#pragma unroll
-        for (int u = 0; u < kAwUnroll; ++u) {
-            row[u] = base + (int64_t)u * RPW + threadIdx.x / LPR;
-            const int64_t rc = row[u] < B ? row[u] : B - 1;
-            x[u] = q[rc * LPR + sub];
-        }
-        for (int g = 0; g < G; ++g) {
-            float vv[kAwUnroll];
-#pragma unroll
-            for (int u = 0; u < kAwUnroll; ++u) vv[u] = v[(int64_t)g * B + (row[u] < B ? row[u] : B - 1)];
-#pragma unroll
-            for (int u = 0; u < kAwUnroll; ++u) {
-                float e[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
-                float mx = -INFINITY;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    e[j] = beta * fminf(fmaxf(e[j] - vv[u], -10.f), 10.f);
-                    mx = fmaxf(mx, e[j]);
-                }
-#pragma unroll
-                for (int o = LPR / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, LPR));
-                float s = 0.f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    e[j] = expf(e[j] - mx);
-                    s += e[j];
-                }
-#pragma unroll
-                for (int o = LPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, LPR);
-                // the policy is this call's output only: non-temporal stores
-                // (measured 5 % faster on working sets beyond the caches)
-                if (row[u] < B)
-                    __builtin_nontemporal_store(f4v{e[0] / s, e[1] / s, e[2] / s, e[3] / s},
-                                                (f4v*)&pi[((int64_t)g * B + row[u]) * LPR + sub]);
-            }
-        }
-    }
+    aw_vec_rows<LPR, kAwVecThreads>(q, v, G, B, beta, pi, blockIdx.x, gridDim.x);
 }
 
 template <int LPR>

@@ -1734,6 +1734,14 @@ bool iql_fused_policy(const IqlDims& d, int A) {
     return !d.layered && A >= 1 && A <= 16 && iql_supported(d.dtype, d.S, d.H);
 }
 
+// The policy runs inside the forward/backward launch: in every fused tile
+// kernel (A <= 16), or in the wide-hidden weight-gradient launch's spare
+// workgroups (A = 4, 8, 16, 32 or 64, 16-byte aligned rows, at least 8 idle
+// compute units).
+bool iql_policy_in_launch(const IqlDims& d, int B, int A, const void* q_all, const void* out_pi) {
+    return iql_fused_policy(d, A) || (d.layered && d.big && iql_big_policy_ok(d, B, A, q_all, out_pi));
+}
+
 // The shapes that run iql_fused16w_kernel (bf16, hidden 128, state <= 128).
 static bool is_fused16w(const IqlDims& d) { return !d.layered && d.dtype == 1 && d.H == 128 && d.S <= 128; }
 bool iql_runs_fused16w(const IqlDims& d) { return is_fused16w(d); }
@@ -1764,7 +1772,9 @@ hipError_t launch_iql_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float
                               const NormsArgs* nrm, uint64_t* stamps) {
     if (d.layered) {
         if (ev0) (void)hipEventRecord(ev0, stream);
-        hipError_t e = d.big ? launch_iql_big_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream)
+        if (out_pi && !d.big) return hipErrorInvalidValue;
+        hipError_t e = d.big ? launch_iql_big_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream, q_all, A, beta,
+                                                      out_pi)
                              : launch_iql_layered_fwd_bwd(d, b, tau, states, ld, q, B, out_v, stream);
         if (ev1 && e == hipSuccess) e = hipEventRecord(ev1, stream);
         return e;

@@ -42,6 +42,7 @@
 // The product orientation is D[feature][sample], so a lane ends with four
 // consecutive features of one sample: bias, ReLU masks and the bf16 stores
 // work on 8-byte runs of a row.
+#include "aw_block.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -347,7 +348,30 @@ struct BigArgs {
     int B, S, H, chunk, nchunk, nblk;
     int fwd_only;  // 1: V (and the bootstrap target) only
     ValueOut vo;
+    // advantage-weighted policy run by the weight-gradient launch's spare
+    // workgroups: grid columns pol_x0 .. pol_x0 + pol_nx - 1 of every group
+    // row; pol_lpr = 0 when the launch does not run it
+    const float4* pol_q;  // [B][A]
+    float4* pol_pi;       // [G][B][A]
+    float pol_beta;
+    int pol_lpr, pol_x0, pol_nx;
 };
+
+// A spare workgroup of the weight-gradient launch: its share of the policy of
+// every group from V, which fwd2 completed before this launch started.
+IQLH_DEV void big_policy_block(const BigArgs& a) {
+    constexpr int NT = 64 * kWgradWaves;
+    const int64_t bid = (int64_t)blockIdx.y * a.pol_nx + ((int)blockIdx.x - a.pol_x0);
+    const int64_t nb = (int64_t)gridDim.y * a.pol_nx;
+    const int G = (int)gridDim.y;
+    switch (a.pol_lpr) {
+        case 1: aw_vec_rows<1, NT>(a.pol_q, a.out_v, G, a.B, a.pol_beta, a.pol_pi, bid, nb); break;
+        case 2: aw_vec_rows<2, NT>(a.pol_q, a.out_v, G, a.B, a.pol_beta, a.pol_pi, bid, nb); break;
+        case 4: aw_vec_rows<4, NT>(a.pol_q, a.out_v, G, a.B, a.pol_beta, a.pol_pi, bid, nb); break;
+        case 8: aw_vec_rows<8, NT>(a.pol_q, a.out_v, G, a.B, a.pol_beta, a.pol_pi, bid, nb); break;
+        default: aw_vec_rows<16, NT>(a.pol_q, a.out_v, G, a.B, a.pol_beta, a.pol_pi, bid, nb); break;
+    }
+}
 
 
 // Workgroup id -> (tile, group): consecutive ids go to different XCDs, so the
@@ -747,6 +771,10 @@ __global__ __launch_bounds__(64 * kWgradWaves) void big_wgrad_kernel(BigArgs a) 
     // the 256 x 256 tile, NC = waves / 2 column groups of JT feature tiles
     constexpr int NT = 64 * kWgradWaves, NC = kWgradWaves / 2, JT = 16 / NC;
     constexpr int NST = kWgradStages, STG = 2 * kBK * kTile;
+    if (a.pol_lpr && (int)blockIdx.x >= a.pol_x0) {  // uniform per workgroup, before any barrier
+        big_policy_block(a);
+        return;
+    }
     const int g = blockIdx.y;
     const int H = a.H, S = a.S, B = a.B;
     const int nth = H / kTile, nts = (S + kTile - 1) / kTile;
@@ -884,22 +912,53 @@ int iql_big_chunk(int S, int H, int G, int B) {
     return c < kFwd2Samples ? kFwd2Samples : c;
 }
 
+struct BigPolicy {
+    const float* q_all;
+    int A;
+    float beta;
+    float* out_pi;
+};
+
 static hipError_t big_launch(const IqlDims& d, const IqlBuffers& b, const float* tau, const void* states, int64_t ld,
-                             const float* q, int B, float* out_v, const ValueOut* vo, hipStream_t stream);
+                             const float* q, int B, float* out_v, const ValueOut* vo, const BigPolicy* pol,
+                             hipStream_t stream);
+
+// Grid columns of the weight-gradient launch that run the policy: the compute
+// units its tiles leave idle (256 - tiles x groups; one workgroup per CU), per
+// group row, in whole multiples of 8 so that the tiles keep their XCD
+// placement, and at least 8; 0 when the policy cannot run there (no streaming
+// form for A, unaligned rows, too few idle CUs).
+static int big_policy_cols(const IqlDims& d, int B, int A, const void* q_all, const void* out_pi) {
+    if (!d.big || B <= 0 || aw_vec_lanes(A) == 0 || (((uintptr_t)q_all | (uintptr_t)out_pi) & 15u)) return 0;
+    const int chunk = iql_big_chunk(d.S, d.H, d.G, B);
+    const int tiles = ((B + chunk - 1) / chunk) * big_tiles(d.S, d.H);
+    const int idle = 256 - tiles * d.G;
+    const int px = idle > 0 ? idle / d.G / 8 * 8 : 0;
+    return px >= 8 ? px : 0;
+}
+
+bool iql_big_policy_ok(const IqlDims& d, int B, int A, const void* q_all, const void* out_pi) {
+    return q_all && out_pi && big_policy_cols(d, B, A, q_all, out_pi) > 0;
+}
 
 hipError_t launch_iql_big_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float* tau, const void* states,
-                                  int64_t ld, const float* q, int B, float* out_v, hipStream_t stream) {
-    return big_launch(d, b, tau, states, ld, q, B, out_v, nullptr, stream);
+                                  int64_t ld, const float* q, int B, float* out_v, hipStream_t stream,
+                                  const float* q_all, int A, float beta, float* out_pi) {
+    if (!out_pi) return big_launch(d, b, tau, states, ld, q, B, out_v, nullptr, nullptr, stream);
+    if (!out_v || !iql_big_policy_ok(d, B, A, q_all, out_pi)) return hipErrorInvalidValue;
+    const BigPolicy pol{q_all, A, beta, out_pi};
+    return big_launch(d, b, tau, states, ld, q, B, out_v, nullptr, &pol, stream);
 }
 
 hipError_t launch_iql_big_forward(const IqlDims& d, const IqlBuffers& b, const void* states, int64_t ld, int B,
                                   const ValueOut& vo, hipStream_t stream) {
     const float tau[2] = {0.f, 0.f};
-    return big_launch(d, b, tau, states, ld, nullptr, B, nullptr, &vo, stream);
+    return big_launch(d, b, tau, states, ld, nullptr, B, nullptr, &vo, nullptr, stream);
 }
 
 static hipError_t big_launch(const IqlDims& d, const IqlBuffers& b, const float* tau, const void* states, int64_t ld,
-                             const float* q, int B, float* out_v, const ValueOut* vo, hipStream_t stream) {
+                             const float* q, int B, float* out_v, const ValueOut* vo, const BigPolicy* pol,
+                             hipStream_t stream) {
     const int G = d.G, S = d.S, H = d.H;
     BigArgs a{};
     a.x = (const uint16_t*)states; a.ldx = ld;
@@ -943,7 +1002,19 @@ static hipError_t big_launch(const IqlDims& d, const IqlBuffers& b, const float*
         hipLaunchKernelGGL((big_fwd2_kernel<512, true, kFwd2Waves>), g2, t2, fwd2_lds_bytes<512>(), stream, a);
     else
         hipLaunchKernelGGL((big_fwd2_kernel<256, true, kFwd2Waves>), g2, t2, fwd2_lds_bytes<256>(), stream, a);
-    const dim3 gw(a.nchunk * big_tiles(S, H), G);
+    const int xw = a.nchunk * big_tiles(S, H);
+    int px = 0;
+    if (pol) {
+        px = big_policy_cols(d, B, pol->A, pol->q_all, pol->out_pi);
+        if (px <= 0) return hipErrorInvalidValue;
+        a.pol_q = (const float4*)pol->q_all;
+        a.pol_pi = (float4*)pol->out_pi;
+        a.pol_beta = pol->beta;
+        a.pol_lpr = aw_vec_lanes(pol->A);
+        a.pol_x0 = xw;
+        a.pol_nx = px;
+    }
+    const dim3 gw(xw + px, G);
     hipLaunchKernelGGL(big_wgrad_kernel, gw, dim3(64 * kWgradWaves), ring_lds_bytes(kWgradStages), stream, a);
     return hipGetLastError();
 }

@@ -127,16 +127,17 @@ struct IqlBuffers {
     void* act_dz1;
     float* act_dv;
     // wide-hidden path: per-128-sample-block sums of db2, dw3, db3, db1
-    // [G][nblk][iql_big_spart_width(H)], and the ReLU masks of h1 that the
-    // first forward product leaves for the first backward one
+    // [G][nblk][iql_big_spart_width(H)]
     float* big_spart;
 };
 bool iql_supported(int dtype, int S, int H);
 int iql_tile_samples(int dtype, int S, int H);
 int iql_reduce_blocks(int64_t P);
 // Fused forward/backward: V(s) and the per-workgroup gradient partials.
-// With out_pi non-null and iql_fused_policy(d, A), the advantage-weighted
-// policy of every group is computed in the same launch from this V.
+// With out_pi non-null and iql_policy_in_launch(d, B, A, q_all, out_pi), the
+// advantage-weighted policy of every group is computed in the same launch
+// from this V (by the fused tile kernels, or by the spare workgroups of the
+// wide-hidden weight-gradient kernel).
 // With `her` (iql_fused_her_ok), the HER rows that form the batch tail from
 // row her_row0 on are relabelled inside the launch instead of read from
 // `states` (group 0 also writes every HER output); with `nrm`
@@ -156,6 +157,7 @@ constexpr int kPhaseStamps = 8;
 // state <= 128), the one that can record phase ends.
 bool iql_runs_fused16w(const IqlDims& d);
 bool iql_fused_policy(const IqlDims& d, int A);
+bool iql_policy_in_launch(const IqlDims& d, int B, int A, const void* q_all, const void* out_pi);
 bool iql_fused_her_ok(const IqlDims& d, const HerArgs& her, const void* states, int64_t ld, int B);
 bool iql_fused_norms_ok(const IqlDims& d, int B, int her_rows, int nb);
 // Fixed-order reduction of the partials of a batch of B rows, clip, Adam.
@@ -172,8 +174,13 @@ int iql_big_blocks(int B);
 int iql_big_max_chunks(int S, int H);
 int iql_big_chunk(int S, int H, int G, int B);
 int iql_big_spart_width(int H);
+// The policy (out_pi non-null) runs in the weight-gradient launch's spare
+// workgroups when iql_big_policy_ok; otherwise hipErrorInvalidValue.
+bool iql_big_policy_ok(const IqlDims& d, int B, int A, const void* q_all, const void* out_pi);
 hipError_t launch_iql_big_fwd_bwd(const IqlDims& d, const IqlBuffers& b, const float* tau, const void* states,
-                                  int64_t ld, const float* q, int B, float* out_v, hipStream_t stream);
+                                  int64_t ld, const float* q, int B, float* out_v, hipStream_t stream,
+                                  const float* q_all = nullptr, int A = 0, float beta = 0.f,
+                                  float* out_pi = nullptr);
 hipError_t launch_iql_target_ema(const IqlDims& d, const IqlBuffers& b, float tau, hipStream_t stream);
 hipError_t launch_iql_layered_forward(const IqlDims& d, const IqlBuffers& b, const void* states, int64_t ld,
                                       int B, const ValueOut& vo, hipStream_t stream);

@@ -161,7 +161,7 @@ hipError_t launch_aux_step(const IqlDims& d, const IqlBuffers& b, const AdamHype
 
     // B: fused forward/backward (+ policy, HER rows, budget norms)
     hipError_t e;
-    const bool fused_pi = q_all && iql_fused_policy(d, A);
+    const bool fused_pi = q_all && out_pi && iql_policy_in_launch(d, B, A, q_all, out_pi);
     hipEvent_t e0 = ev ? ev[2] : nullptr, e1 = ev ? ev[3] : nullptr;
     const HerArgs* hb = her_in_b ? her : nullptr;
     const NormsArgs* nbp = norms_in_b ? &np : nullptr;

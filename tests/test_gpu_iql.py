@@ -394,3 +394,46 @@ def test_train_step_with_policy(m, wname, B, A):
         assert np.all(d <= 1e-5 * np.abs(ref) + 1e-7), f"policy g{gi}: {d.max():.3e}"
     refs = s.oracle_step()
     s.compare_step(refs, s.oracle, 2e-2 if s.bf16 else 1e-4, 1, "train_step_aw")
+
+
+@pytest.mark.parametrize("S,H,G,B,A,oracle_step", [
+    (256, 512, 1, 4096, 16, True),    # 192 gradient tiles: the policy on 64 spare workgroups
+    (64, 256, 2, 1000, 64, True),     # two groups, 16 lanes per row, 112 spare columns per group row
+    (96, 512, 1, 1037, 4, True),      # one lane per row, ragged batch
+    (256, 512, 1, 1000, 9, True),     # no streaming form for 9 actions: the policy after the launch
+    (256, 512, 1, 65536, 16, False),  # the stress shape: 240 tiles, the policy on the 16 idle CUs
+])
+def test_wide_train_step_with_policy(m, S, H, G, B, A, oracle_step):
+    """On the wide-hidden path the policy runs in the weight-gradient launch's
+    spare workgroups (A = 4, 8, 16, 32 or 64 and at least 8 idle compute
+    units), else after the launch.  Either way it equals the standalone
+    policy call on the step's own V bit for bit (the same per-row
+    arithmetic), and the oracle's policy of that V within 1e-5 relative; the
+    step itself still matches the oracle."""
+    import torch
+    from oracle import aw
+    w = synth.shrink(synth.WORKLOADS["stress_b65536_s256_h512_bf16"], S=S, H=H, groups=G,
+                     taus=(0.9, 0.3)[:G], G=8, A=A)
+    s = Setup(m, w, B=B)
+    g = np.random.default_rng(A + B)
+    Q = (g.standard_normal((B, A)) * 2).astype(np.float32)
+    Q[::7, 0] = 1e3  # clamp path
+    tQ = to_dev(Q)
+    pi = torch.full((s.G, B, A), float("nan"), dtype=torch.float32, device=dev())
+    s.tr.train_step_aw(s.tX, s.tq, B, tQ, A, w.beta, pi, s.out_v, s.out_loss, s.out_gn)
+    sync()
+    solo = torch.full((s.G, B, A), float("nan"), dtype=torch.float32, device=dev())
+    m.iql_aw_policy(tQ, s.out_v, s.G, B, A, w.beta, solo)
+    sync()
+    got = host(pi)
+    assert np.array_equal(got.view(np.uint32), host(solo).view(np.uint32)), "policy differs from the standalone call"
+    vg = host(s.out_v)
+    for gi in range(s.G):
+        ref = aw.aw_policy(Q, vg[gi], w.beta)
+        d = np.abs(got[gi] - ref)
+        assert np.all(d <= 1e-5 * np.abs(ref) + 1e-7), f"policy g{gi}: {d.max():.3e}"
+    if oracle_step:
+        refs = s.oracle_step()
+        s.compare_step(refs, s.oracle, 2e-2, 1, "wide train_step_aw")
+    rc, flags = s.tr.status()
+    assert rc == m.OK and flags == 0
